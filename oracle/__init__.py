@@ -1,0 +1,161 @@
+"""CPU oracle for the P2G transfer and its neighbouring steps.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the package smoke check
+and by the benchmark's CPU-baseline leg, never by the library's product path.
+It shares no code with the HIP library (see mpm_oracle.c for the definitions
+and the pages each step follows).
+
+``build()`` compiles mpm_oracle.c with gcc; the wrappers below take numpy
+arrays and return numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mpm_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libmpm_oracle.so")
+_lib = None
+
+I64P = ct.POINTER(ct.c_int64)
+U32P = ct.POINTER(ct.c_uint32)
+I32P = ct.POINTER(ct.c_int32)
+F32P = ct.POINTER(ct.c_float)
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle into oracle/libmpm_oracle.so (plain gcc, -O2,
+    no FMA contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-shared",
+                        "-Wall", "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ct.CDLL(_LIB_PATH)
+        L.oracle_split_far.restype = ct.c_int64
+        L.oracle_split_far.argtypes = [ct.c_int64, ct.c_int32]
+        L.oracle_cic_bounds_ok.restype = ct.c_int
+        L.oracle_cic_bounds_ok.argtypes = [ct.c_int64, ct.c_int64, ct.c_int64]
+        L.oracle_p2g_cic_split.restype = None
+        L.oracle_p2g_cic_split.argtypes = [ct.c_int64, I32P, I32P, I32P, I64P, ct.c_int32, I64P, U32P]
+        L.oracle_p2g_quadratic.restype = None
+        L.oracle_p2g_quadratic.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_int64, F32P, F32P, F32P, F32P,
+                                           I64P, ct.c_double, ct.c_double, ct.c_double, I64P, U32P]
+        L.oracle_p2g_log2_bound.restype = ct.c_double
+        L.oracle_p2g_log2_bound.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_int64,
+                                            ct.c_double, ct.c_double, ct.c_double]
+        L.oracle_grid_update.restype = None
+        L.oracle_grid_update.argtypes = [ct.c_int, ct.c_int, I64P, F32P, ct.c_float, F32P, ct.c_int]
+        L.oracle_g2p.restype = None
+        L.oracle_g2p.argtypes = [ct.c_int, ct.c_int, F32P, ct.c_int64, F32P, F32P, F32P, ct.c_float, U32P]
+        L.oracle_bin.restype = ct.c_int64
+        L.oracle_bin.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_int64, F32P, F32P, F32P, F32P,
+                                 ct.c_double, ct.c_double, ct.c_double, U32P, U32P, I64P]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray, ctype):
+    assert a.flags.c_contiguous
+    return a.ctypes.data_as(ctype)
+
+
+def _order_ptr(order):
+    if order is None:
+        return None, None
+    o = np.ascontiguousarray(order, dtype=np.int64)
+    return o, _p(o, I64P)
+
+
+def split_far(q: int, f: int) -> int:
+    return lib().oracle_split_far(int(q), int(f))
+
+
+def cic_bounds_ok(n: int, max_mass: int, max_speed: int) -> bool:
+    return bool(lib().oracle_cic_bounds_ok(n, max_mass, max_speed))
+
+
+def p2g_cic_split(X, m, vel, cells: int, order=None):
+    """Integer-split cloud-in-cell scatter; returns (grid[3][cells+1][cells+1], status[4])."""
+    X = np.ascontiguousarray(X, dtype=np.int32)
+    m = np.ascontiguousarray(m, dtype=np.int32)
+    vel = np.ascontiguousarray(vel, dtype=np.int32)
+    n = m.shape[0]
+    grid = np.zeros((3, cells + 1, cells + 1), dtype=np.int64)
+    status = np.zeros(4, dtype=np.uint32)
+    o, op = _order_ptr(order)
+    lib().oracle_p2g_cic_split(n, _p(X, I32P), _p(m, I32P), _p(vel, I32P), op, cells, _p(grid, I64P),
+                               _p(status, U32P))
+    return grid, status
+
+
+def _soa(d):
+    return (np.ascontiguousarray(d["x"], dtype=np.float32), np.ascontiguousarray(d["v"], dtype=np.float32),
+            np.ascontiguousarray(d["C"], dtype=np.float32), np.ascontiguousarray(d["m"], dtype=np.float32))
+
+
+def p2g_quadratic(dim: int, n: int, frac_bits: int, particles: dict, ranges, order=None, grid=None):
+    """Fixed-point APIC P2G; returns (grid[1+dim][n]*dim, status[4])."""
+    x, v, C, m = _soa(particles)
+    np_ = m.shape[0]
+    shape = (1 + dim,) + (n,) * dim
+    if grid is None:
+        grid = np.zeros(shape, dtype=np.int64)
+    status = np.zeros(4, dtype=np.uint32)
+    o, op = _order_ptr(order)
+    lib().oracle_p2g_quadratic(dim, n, frac_bits, np_, _p(x, F32P), _p(v, F32P), _p(C, F32P), _p(m, F32P), op,
+                               float(ranges[0]), float(ranges[1]), float(ranges[2]), _p(grid, I64P),
+                               _p(status, U32P))
+    return grid, status
+
+
+def p2g_log2_bound(dim, n, frac_bits, np_, ranges) -> float:
+    return lib().oracle_p2g_log2_bound(dim, n, frac_bits, np_, float(ranges[0]), float(ranges[1]),
+                                       float(ranges[2]))
+
+
+def grid_update(dim: int, n: int, grid: np.ndarray, dt: float, gravity, sticky: int):
+    """Consumes (and zeroes) grid in place; returns vg[dim][n]*dim."""
+    assert grid.dtype == np.int64 and grid.flags.c_contiguous
+    vg = np.zeros((dim,) + (n,) * dim, dtype=np.float32)
+    g = np.zeros(3, dtype=np.float32)
+    g[:dim] = np.asarray(gravity, dtype=np.float32)[:dim]
+    lib().oracle_grid_update(dim, n, _p(grid, I64P), _p(vg, F32P), ct.c_float(dt), _p(g, F32P), sticky)
+    return vg
+
+
+def g2p(dim: int, n: int, vg: np.ndarray, particles: dict, dt: float):
+    """Updates particles['x'], ['v'], ['C'] in place; returns status[4]."""
+    x, v, C, _ = _soa(particles)
+    assert x is particles["x"] and v is particles["v"] and C is particles["C"], "arrays must be float32 C-contiguous"
+    vg = np.ascontiguousarray(vg, dtype=np.float32)
+    status = np.zeros(4, dtype=np.uint32)
+    lib().oracle_g2p(dim, n, _p(vg, F32P), x.shape[1], _p(x, F32P), _p(v, F32P), _p(C, F32P), ct.c_float(dt),
+                     _p(status, U32P))
+    return status
+
+
+def bin_particles(dim: int, n: int, tile: int, particles: dict, ranges):
+    """Counting sort by tile-major cell key; returns (cell_count, cell_start, order)."""
+    x, v, C, m = _soa(particles)
+    np_ = m.shape[0]
+    n_cells = n ** dim
+    count = np.zeros(n_cells, dtype=np.uint32)
+    start = np.zeros(n_cells + 1, dtype=np.uint32)
+    order = np.zeros(max(np_, 1), dtype=np.int64)
+    placed = lib().oracle_bin(dim, n, tile, np_, _p(x, F32P), _p(v, F32P), _p(C, F32P), _p(m, F32P),
+                              float(ranges[0]), float(ranges[1]), float(ranges[2]), _p(count, U32P),
+                              _p(start, U32P), _p(order, I64P))
+    return count, start, order[:placed]

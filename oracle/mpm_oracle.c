@@ -1,0 +1,430 @@
+/*
+ * mpm_oracle.c -- plain, slow, single-threaded CPU oracle for the material
+ * point method's particle-to-grid (P2G) transfer and the three steps around it
+ * (binning, grid update, grid-to-particle).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library's product path may call,
+ * link or load this file; only the tests, the package smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code with the HIP
+ * library: the two are written separately from the same definitions.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no -ffast-math, no
+ * -march=native), so every float operation is one IEEE binary32 operation
+ * rounded to nearest even, in the order written below.
+ *
+ * Sources (pages as titled):
+ *  - "particle to grid transfer in checked integer arithmetic" (integerc.dev),
+ *    sections "integers do not care about order" and "the program": the
+ *    integer split of a quantity between near and far nodes, done along x and
+ *    then along y, and the bounds line run before any scatter.
+ *  - "Implementation -- GPU Optimization & Reference Codebases" (vocaro.com),
+ *    section 1 (the four-phase step reset -> P2G -> grid update -> G2P),
+ *    section 2.1 (fixed-point accumulation, tiles), section 3.1 (APIC
+ *    transfer with the 3x3 quadratic B-spline stencil and affine matrix C),
+ *    section 3.3.1 (rounding, not truncating, fixed-point encode), section 5
+ *    rules 1, 4, 7 and 9 (integer accumulation converted once in the grid
+ *    update; consume-and-zero; gravity owned by the solver; counted
+ *    overflows).
+ *  - "Mass Matrix Assembly on Tensor Cores for Implicit PIC" (arXiv
+ *    2604.19286), section on shape functions: tensor-product B-splines,
+ *    partition of unity, and the rule that places a second-order stencil on
+ *    nodes {j-1, j, j+1} or {j, j+1, j+2} by whether the fractional
+ *    coordinate is below one half.
+ *  - "Particle worlds, part 3" (ericlevin.dev), steps 3 and 4: counting sort
+ *    by cell as histogram, exclusive prefix sum and scatter.
+ *
+ * Readings taken where the pages leave a step open are listed with each
+ * function.  The quadratic B-spline's formula is not legible on the pages
+ * (the equation was lost in extraction); the textbook piecewise form is used:
+ * N(t) = 3/4 - t^2 for |t| < 1/2, (3/2 - |t|)^2 / 2 for 1/2 <= |t| < 3/2,
+ * else 0, which has the support and partition of unity the PIC page states.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* status counters shared by every function that can skip work */
+enum { ST_DOMAIN = 0, ST_RANGE = 1, ST_CLAMP = 2 };
+
+/* ------------------------------------------------------------------------ */
+/* Integer split cloud-in-cell (integer-arithmetic page).                    */
+/* ------------------------------------------------------------------------ */
+
+/* t / 65536 rounded to the nearest integer, ties to the even neighbour,
+ * computed in integers only.  (The page says "rounded once to the nearest
+ * integer" without a tie rule; ties to even is the reading taken.) */
+static int64_t div65536_nearest_even(int64_t t)
+{
+    int64_t fl = t / 65536;
+    if (t % 65536 != 0 && t < 0)
+        fl -= 1;                            /* floor division */
+    int64_t r = t - fl * 65536;             /* 0 <= r < 65536 */
+    if (r > 32768)
+        return fl + 1;
+    if (r == 32768)
+        return fl + (fl & 1);
+    return fl;
+}
+
+/* The far node's share of q at fraction f/65536 toward it. */
+int64_t oracle_split_far(int64_t q, int32_t f)
+{
+    return div65536_nearest_even(q * (int64_t)f);
+}
+
+/* Bounds line: particle count x largest mass x largest speed, and the largest
+ * product q * f formed by a split, must fit a signed 64-bit integer.
+ * Returns 1 when the scatter may run, 0 when it must stop before any work. */
+int oracle_cic_bounds_ok(int64_t n, int64_t max_mass, int64_t max_speed)
+{
+    long double node_bound = (long double)n * (long double)max_mass * (long double)(max_speed > 1 ? max_speed : 1);
+    long double split_bound = (long double)max_mass * (long double)(max_speed > 1 ? max_speed : 1) * 65536.0L;
+    long double lim = 9223372036854775807.0L;
+    return node_bound <= lim && split_bound <= lim;
+}
+
+/*
+ * Scatter n particles (in `order`, or index order when order is NULL) onto a
+ * (cells+1) x (cells+1) node grid.  Positions X[2][n] are in units of 1/65536
+ * of a cell; masses m[n] and velocities vel[2][n] are integers.  The three
+ * quantities q = m, m*vx, m*vy are each split along x between the near node
+ * (cell index) and the far node (index + 1), and each x part is then split
+ * along y the same way.  grid[3][cells+1][cells+1] (x fastest) is
+ * accumulated into.  Particles outside [0, cells) are skipped and counted in
+ * status[0].
+ */
+void oracle_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32_t *vel,
+                          const int64_t *order, int32_t cells, int64_t *grid, uint32_t *status)
+{
+    const int64_t nn = (int64_t)(cells + 1);
+    const int64_t span = (int64_t)cells * 65536;
+    for (int64_t k = 0; k < n; ++k) {
+        int64_t p = order ? order[k] : k;
+        int64_t px = X[p], py = X[n + p];
+        if (px < 0 || px >= span || py < 0 || py >= span) {
+            status[ST_DOMAIN] += 1;
+            continue;
+        }
+        int64_t cx = px / 65536, cy = py / 65536;
+        int32_t fx = (int32_t)(px % 65536), fy = (int32_t)(py % 65536);
+        int64_t q[3];
+        q[0] = m[p];
+        q[1] = (int64_t)m[p] * vel[p];
+        q[2] = (int64_t)m[p] * vel[n + p];
+        for (int c = 0; c < 3; ++c) {
+            int64_t far_x = oracle_split_far(q[c], fx);
+            int64_t near_x = q[c] - far_x;
+            int64_t part[2] = { near_x, far_x };
+            for (int i = 0; i < 2; ++i) {
+                int64_t far_y = oracle_split_far(part[i], fy);
+                int64_t near_y = part[i] - far_y;
+                grid[(c * nn + (cy + 0)) * nn + (cx + i)] += near_y;
+                grid[(c * nn + (cy + 1)) * nn + (cx + i)] += far_y;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quadratic B-spline APIC transfer.                                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Stencil of one particle along one axis, with g = x * n in node units:
+ * base = floor(g - 1/2) (the PIC page's placement rule: nodes {j-1, j, j+1}
+ * when the fraction is below one half, else {j, j+1, j+2}); f = g - base in
+ * [1/2, 3/2) is the distance from the base node; the three weights are the
+ * quadratic B-spline at distances f, f-1, f-2; r[o] = (o - f) * dx is the
+ * offset of node base+o from the particle in domain units.
+ * Returns 0 when base falls outside [0, n-3] (the stencil would leave the
+ * grid) or the coordinate is not finite.
+ */
+static int stencil_1d(float x, int n, int *base, float w[3], float r[3])
+{
+    float g = x * (float)n;
+    float b = floorf(g - 0.5f);
+    if (!(b >= 0.0f && b <= (float)(n - 3)))
+        return 0;
+    float f = g - b;
+    float dx = 1.0f / (float)n;
+    w[0] = 0.5f * ((1.5f - f) * (1.5f - f));
+    w[1] = 0.75f - ((f - 1.0f) * (f - 1.0f));
+    w[2] = 0.5f * ((f - 0.5f) * (f - 0.5f));
+    for (int o = 0; o < 3; ++o)
+        r[o] = ((float)o - f) * dx;
+    *base = (int)b;
+    return 1;
+}
+
+/* Is every attribute inside the declared ranges (the ranges the bounds check
+ * proved safe)?  NaN fails every comparison and is therefore rejected. */
+static int in_ranges(int dim, int64_t np_, int64_t p, const float *v, const float *C, const float *m,
+                     double max_mass, double max_speed, double max_affine)
+{
+    if (!((double)fabsf(m[p]) <= max_mass))
+        return 0;
+    for (int d = 0; d < dim; ++d)
+        if (!((double)fabsf(v[d * np_ + p]) <= max_speed))
+            return 0;
+    for (int k = 0; k < dim * dim; ++k)
+        if (!((double)fabsf(C[k * np_ + p]) <= max_affine))
+            return 0;
+    return 1;
+}
+
+/*
+ * Fixed-point APIC P2G with the quadratic B-spline stencil (3^dim nodes).
+ *
+ * Inputs (component-major): x[dim][np], v[dim][np], C[dim*dim][np] with
+ * C[d*dim+e] the (row d, column e) entry of the affine matrix, m[np].
+ * Output grid[(1+dim)][n^dim] (x fastest; channel 0 mass, channel 1+d
+ * momentum d) is accumulated into.  S = 2^frac_bits.
+ *
+ * Per particle and node (a, b, c) of its stencil, all in float32:
+ *   wmS = (((m * S) * wx[a]) * wy[b]) * wz[c]        (2D: no wz factor)
+ *   u_d = ((v_d + C_d0 * rx[a]) + C_d1 * ry[b]) + C_d2 * rz[c]
+ *   M   += (int64) rint(wmS)
+ *   P_d += (int64) rint(wmS * u_d)
+ * i.e. node mass m w and momentum m w (v + C (x_i - x_p)), scaled by S and
+ * rounded to nearest (ties even) once per contribution.  The association
+ * order above is this library's fixed reading (the pages fix no order); the
+ * sums themselves are integer and so independent of particle order.
+ *
+ * Particles whose stencil leaves the grid are skipped and counted in
+ * status[0]; particles outside the declared ranges are skipped and counted
+ * in status[1] (domain is checked first).
+ */
+void oracle_p2g_quadratic(int dim, int n, int frac_bits, int64_t np_,
+                          const float *x, const float *v, const float *C, const float *m,
+                          const int64_t *order, double max_mass, double max_speed, double max_affine,
+                          int64_t *grid, uint32_t *status)
+{
+    const int64_t nodes = dim == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    const float S = ldexpf(1.0f, frac_bits);
+    for (int64_t k = 0; k < np_; ++k) {
+        int64_t p = order ? order[k] : k;
+        int base[3] = { 0, 0, 0 };
+        float w[3][3] = { { 1, 0, 0 }, { 1, 0, 0 }, { 1, 0, 0 } };
+        float r[3][3] = { { 0, 0, 0 }, { 0, 0, 0 }, { 0, 0, 0 } };
+        int ok = 1;
+        for (int e = 0; e < dim; ++e)
+            ok &= stencil_1d(x[e * np_ + p], n, &base[e], w[e], r[e]);
+        if (!ok) {
+            status[ST_DOMAIN] += 1;
+            continue;
+        }
+        if (!in_ranges(dim, np_, p, v, C, m, max_mass, max_speed, max_affine)) {
+            status[ST_RANGE] += 1;
+            continue;
+        }
+        const float mS = m[p] * S;
+        const int nc = dim == 3 ? 3 : 1;
+        for (int a = 0; a < 3; ++a)
+            for (int b = 0; b < 3; ++b)
+                for (int c = 0; c < nc; ++c) {
+                    float wmS = (mS * w[0][a]) * w[1][b];
+                    if (dim == 3)
+                        wmS = wmS * w[2][c];
+                    int64_t node = dim == 3
+                        ? ((int64_t)(base[2] + c) * n + (base[1] + b)) * n + (base[0] + a)
+                        : (int64_t)(base[1] + b) * n + (base[0] + a);
+                    grid[node] += (int64_t)rintf(wmS);
+                    for (int d = 0; d < dim; ++d) {
+                        const float *Cd = C + (int64_t)d * dim * np_;
+                        float u = (v[d * np_ + p] + Cd[0 * np_ + p] * r[0][a]) + Cd[1 * np_ + p] * r[1][b];
+                        if (dim == 3)
+                            u = u + Cd[2 * np_ + p] * r[2][c];
+                        grid[(int64_t)(1 + d) * nodes + node] += (int64_t)rintf(wmS * u);
+                    }
+                }
+    }
+}
+
+/*
+ * Largest magnitude a single quantised contribution can take under the
+ * declared ranges, in units of the fixed-point quantum:
+ *   S * (3/4)^dim * max_mass * (max_speed + dim * max_affine * (3/2) dx)
+ * (each 1D weight is at most 3/4 and each offset at most 3/2 cells), with a
+ * small allowance for float32 rounding.  A P2G over np particles is safe in
+ * int64 when np times this bound stays below 2^63.  Returns log2 of np times
+ * the bound.
+ */
+double oracle_p2g_log2_bound(int dim, int n, int frac_bits, int64_t np_,
+                             double max_mass, double max_speed, double max_affine)
+{
+    double dx = 1.0 / (double)n;
+    double wmax = dim == 3 ? 0.421875 : 0.5625;
+    double umax = max_speed + dim * max_affine * 1.5 * dx;
+    if (umax < 1.0)
+        umax = 1.0;   /* the mass channel has u = 1 */
+    double q = ldexp(1.0, frac_bits) * wmax * max_mass * umax * (1.0 + 1e-6) + 1.0;
+    return log2((double)(np_ > 0 ? np_ : 1) * q);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Grid update (consume-and-zero) and grid-to-particle gather.               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Per node: velocity v_d = P_d / M computed in double from the integer sums
+ * and rounded once to float (zero where M == 0); where M != 0 the velocity
+ * gains gravity, v_d = v_d + (dt * g_d) with dt * g_d formed once in float;
+ * nodes within `sticky` nodes of any face get v = 0; finally the integer
+ * accumulators are zeroed (each accumulator has exactly one reader, so the
+ * clear rides along with the update).  vg[dim][n^dim] is written.
+ */
+void oracle_grid_update(int dim, int n, int64_t *grid, float *vg, float dt, const float *gravity, int sticky)
+{
+    const int64_t nodes = dim == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    float gdt[3] = { 0, 0, 0 };
+    for (int d = 0; d < dim; ++d)
+        gdt[d] = dt * gravity[d];
+    for (int64_t i = 0; i < nodes; ++i) {
+        int64_t ix = i % n, iy = (i / n) % n, iz = dim == 3 ? i / ((int64_t)n * n) : 0;
+        int64_t M = grid[i];
+        float vel[3] = { 0, 0, 0 };
+        if (M != 0) {
+            for (int d = 0; d < dim; ++d) {
+                vel[d] = (float)((double)grid[(1 + d) * nodes + i] / (double)M);
+                vel[d] = vel[d] + gdt[d];
+            }
+        }
+        int wall = ix < sticky || ix >= n - sticky || iy < sticky || iy >= n - sticky;
+        if (dim == 3)
+            wall = wall || iz < sticky || iz >= n - sticky;
+        for (int d = 0; d < dim; ++d) {
+            vg[d * nodes + i] = wall ? 0.0f : vel[d];
+            grid[(1 + d) * nodes + i] = 0;
+        }
+        grid[i] = 0;
+    }
+}
+
+/*
+ * APIC gather: for each particle, over its stencil nodes in lexicographic
+ * order (a outermost, then b, then c), with w = (wx[a] * wy[b]) * wz[c]:
+ *   wv_d   = w * vg_d(node)
+ *   vnew_d = vnew_d + wv_d                     (from 0)
+ *   B_de   = B_de + wv_d * r_e                 (r_e the node's offset on axis e)
+ * then C = B * (4 / dx^2) (the quadratic B-spline's inertia-like factor
+ * dx^2/4 inverted), v = vnew, x_e = x_e + dt * v_e, and x_e is clamped to
+ * [dx, (n-2) dx] (each clamped particle counted in status[2]).  Particles
+ * whose stencil leaves the grid are left untouched and counted in status[0].
+ */
+void oracle_g2p(int dim, int n, const float *vg, int64_t np_, float *x, float *v, float *C, float dt,
+                uint32_t *status)
+{
+    const int64_t nodes = dim == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    const float dx = 1.0f / (float)n;
+    const float lo = dx, hi = (float)(n - 2) * dx;
+    const float cscale = 4.0f * (float)n * (float)n;
+    for (int64_t p = 0; p < np_; ++p) {
+        int base[3] = { 0, 0, 0 };
+        float w[3][3] = { { 1, 0, 0 }, { 1, 0, 0 }, { 1, 0, 0 } };
+        float r[3][3] = { { 0, 0, 0 }, { 0, 0, 0 }, { 0, 0, 0 } };
+        int ok = 1;
+        for (int e = 0; e < dim; ++e)
+            ok &= stencil_1d(x[e * np_ + p], n, &base[e], w[e], r[e]);
+        if (!ok) {
+            status[ST_DOMAIN] += 1;
+            continue;
+        }
+        float vnew[3] = { 0, 0, 0 };
+        float B[3][3] = { { 0, 0, 0 }, { 0, 0, 0 }, { 0, 0, 0 } };
+        const int nc = dim == 3 ? 3 : 1;
+        for (int a = 0; a < 3; ++a)
+            for (int b = 0; b < 3; ++b)
+                for (int c = 0; c < nc; ++c) {
+                    float wt = w[0][a] * w[1][b];
+                    if (dim == 3)
+                        wt = wt * w[2][c];
+                    int64_t node = dim == 3
+                        ? ((int64_t)(base[2] + c) * n + (base[1] + b)) * n + (base[0] + a)
+                        : (int64_t)(base[1] + b) * n + (base[0] + a);
+                    const float off[3] = { r[0][a], r[1][b], r[2][c] };
+                    for (int d = 0; d < dim; ++d) {
+                        float wv = wt * vg[d * nodes + node];
+                        vnew[d] = vnew[d] + wv;
+                        for (int e = 0; e < dim; ++e)
+                            B[d][e] = B[d][e] + wv * off[e];
+                    }
+                }
+        int clamped = 0;
+        for (int d = 0; d < dim; ++d) {
+            for (int e = 0; e < dim; ++e)
+                C[(int64_t)(d * dim + e) * np_ + p] = B[d][e] * cscale;
+            v[d * np_ + p] = vnew[d];
+            float xn = x[d * np_ + p] + dt * vnew[d];
+            float xc = fminf(fmaxf(xn, lo), hi);
+            clamped |= xc != xn;
+            x[d * np_ + p] = xc;
+        }
+        status[ST_CLAMP] += (uint32_t)clamped;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Counting sort of particles by cell, cells numbered tile by tile.          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Cell key of a particle: its base cell (the stencil's base node, as in
+ * stencil_1d) numbered tile-major: tiles of `tile` cells per axis in
+ * row-major order, then the cells inside a tile in row-major order.
+ * Returns -1 for a particle the transfer would skip (outside the domain or
+ * the declared ranges).
+ */
+static int64_t cell_key(int dim, int n, int tile, int64_t np_, int64_t p, const float *x, const float *v,
+                        const float *C, const float *m, double max_mass, double max_speed, double max_affine)
+{
+    int base[3] = { 0, 0, 0 };
+    float w[3], r[3];
+    for (int e = 0; e < dim; ++e)
+        if (!stencil_1d(x[e * np_ + p], n, &base[e], w, r))
+            return -1;
+    if (!in_ranges(dim, np_, p, v, C, m, max_mass, max_speed, max_affine))
+        return -1;
+    int64_t nt = n / tile;
+    int64_t t = 0, l = 0;
+    for (int e = dim - 1; e >= 0; --e) {
+        t = t * nt + base[e] / tile;
+        l = l * tile + base[e] % tile;
+    }
+    int64_t per_tile = dim == 3 ? (int64_t)tile * tile * tile : (int64_t)tile * tile;
+    return t * per_tile + l;
+}
+
+/*
+ * Histogram of cell keys (cell_count[n_cells]), exclusive prefix sum
+ * (cell_start[n_cells + 1]) and a stable scatter of particle indices into
+ * order[] (particles the transfer would skip are left out).  Returns the
+ * number of particles placed.  n_cells = n^dim.
+ */
+int64_t oracle_bin(int dim, int n, int tile, int64_t np_, const float *x, const float *v, const float *C,
+                   const float *m, double max_mass, double max_speed, double max_affine,
+                   uint32_t *cell_count, uint32_t *cell_start, int64_t *order)
+{
+    const int64_t n_cells = dim == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)(np_ > 0 ? np_ : 1));
+    memset(cell_count, 0, sizeof(uint32_t) * (size_t)n_cells);
+    for (int64_t p = 0; p < np_; ++p) {
+        key[p] = cell_key(dim, n, tile, np_, p, x, v, C, m, max_mass, max_speed, max_affine);
+        if (key[p] >= 0)
+            cell_count[key[p]] += 1;
+    }
+    uint32_t run = 0;
+    for (int64_t c = 0; c < n_cells; ++c) {
+        cell_start[c] = run;
+        run += cell_count[c];
+    }
+    cell_start[n_cells] = run;
+    uint32_t *cursor = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)n_cells);
+    memcpy(cursor, cell_start, sizeof(uint32_t) * (size_t)n_cells);
+    for (int64_t p = 0; p < np_; ++p)
+        if (key[p] >= 0)
+            order[cursor[key[p]]++] = p;
+    free(cursor);
+    free(key);
+    return (int64_t)run;
+}
