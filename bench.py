@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X P2G hot path: one JSON line on stdout.
+
+A step is one pass of the whole hot path over the 16M-particle Gaussian-blob
+workload (256^3 nodes, 4 int64 channels at 2^28): clear the grid, bin the
+particles into 4^3-cell tiles (counting sort), and run the tiled fixed-point
+APIC P2G.  Inputs are resident in HBM before timing starts; two input copies
+(each with its own workspace and grid) alternate between steps so that the
+256 MB last-level cache cannot keep one step's data for the next.
+
+Timing: HIP events recorded on the stream the library launches on (torch's
+current stream), around each stage of each timed step; `value` is particles
+per second of the whole step.  The `roofline` object is for the dominant
+kernel, using algorithmic bytes (particle records read once, touched nodes
+written once) over its average event-measured duration.  `cpu_baseline` is
+the oracle (plain single-threaded C) timed on this host's cores over one
+step of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "P2G particles/sec and achieved HBM GB/s (% of peak), 3D 16M particles, 1 GPU"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="blobs_3d_256")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="particles in the CPU-baseline sample (0: all)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the hot path is measured on "
+              "one GPU's share at its real shape)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import material_point_particle_amd as M
+    from material_point_particle_amd.transfer import DeviceParticles, Transfer
+    from mpm_inputs import WORKLOADS, build
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    M.lib()
+    w = WORKLOADS[args.workload]
+    rng = (w.max_mass, w.max_speed, w.max_affine)
+    t0 = time.time()
+    host = build(w)
+    log(f"inputs {w.name}: {w.n_particles} particles in {time.time() - t0:.1f}s")
+
+    copies = []
+    for _ in range(2):
+        parts = DeviceParticles(host)
+        tr = Transfer(w.dim, w.n, w.frac_bits, rng, parts.n)
+        copies.append((parts, tr))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(k, ev=None):
+        parts, tr = copies[k % 2]
+        if ev:
+            ev[0].record(stream)
+        tr.grid.zero_()
+        if ev:
+            ev[1].record(stream)
+        tr.bin(parts)
+        if ev:
+            ev[2].record(stream)
+        tr.p2g(parts, binned=True)
+        if ev:
+            ev[3].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        step(k, events[k])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in events])
+    clear_ms, bin_ms, p2g_ms = stage.mean(axis=0)
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (clear {clear_ms:.3f}, bin {bin_ms:.3f}, p2g {p2g_ms:.3f})")
+
+    # workload facts for the algorithmic byte counts
+    parts, tr = copies[0]
+    meta = tr.meta()
+    binned = int(meta[2])
+    touched = int((tr.grid != 0).any(dim=0).sum().item())
+    status = tr.status.cpu().numpy().view(np.uint32).tolist()
+    rec_bytes = 4 * (2 * w.dim + w.dim * w.dim + 1)          # x, v, C, m
+    p2g_bytes = binned * rec_bytes + touched * 8 * (1 + w.dim)
+    bin_bytes = binned * (rec_bytes + rec_bytes + 4)           # read particles, write records and the index
+    p2g_gbs = p2g_bytes / (p2g_ms * 1e-3) / 1e9
+    bin_gbs = bin_bytes / (bin_ms * 1e-3) / 1e9
+    stages = {"clear": clear_ms, "bin": bin_ms, "p2g": p2g_ms}
+    dominant = max(stages, key=stages.get)
+    if dominant == "bin":
+        roof = {"kernel": "binning (count + scan + scatter)", "achieved": bin_gbs, "bytes_per_launch": bin_bytes,
+                "ms_per_launch": bin_ms}
+    elif dominant == "clear":
+        nbytes = tr.grid.numel() * 8
+        roof = {"kernel": "grid clear", "achieved": nbytes / (clear_ms * 1e-3) / 1e9, "bytes_per_launch": nbytes,
+                "ms_per_launch": clear_ms}
+    else:
+        roof = {"kernel": "p2g_tiled_kernel<3>", "achieved": p2g_gbs, "bytes_per_launch": p2g_bytes,
+                "ms_per_launch": p2g_ms}
+    roofline = {"bound": "hbm", "achieved": round(roof["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(roof["achieved"] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": roof["kernel"],
+                "bytes_per_launch": int(roof["bytes_per_launch"]), "ms_per_launch": round(roof["ms_per_launch"], 4)}
+
+    value = w.n_particles / (ms_step * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "particles/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32/i64",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.n_particles} particles, 32 Gaussian blobs (sigma 4 cells), "
+                               f"{w.n}^3 nodes, {1 + w.dim} int64 channels at 2^{w.frac_bits}; step = grid clear + "
+                               "binning into 4^3-cell tiles + tiled P2G",
+                   "particles": w.n_particles, "nodes": w.n ** w.dim, "touched_nodes": touched},
+        "roofline": roofline,
+        "breakdown": {
+            "clear_ms": round(clear_ms, 4), "bin_ms": round(bin_ms, 4), "p2g_ms": round(p2g_ms, 4),
+            "p2g_particles_per_s": round(binned / (p2g_ms * 1e-3), 1), "p2g_gbs": round(p2g_gbs, 1),
+            "p2g_frac_hbm": round(p2g_gbs / HBM_PEAK_GBS, 4), "bin_gbs": round(bin_gbs, 1),
+            "p2g_bytes": int(p2g_bytes), "status": status,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        n_s = args.cpu_sample or w.n_particles
+        sample = {k: np.ascontiguousarray(v[..., :n_s]) for k, v in host.items() if k in ("x", "v", "C", "m")}
+        log(f"cpu baseline on {n_s} particles")
+        t = time.perf_counter()
+        grid = np.zeros((1 + w.dim,) + (w.n,) * w.dim, dtype=np.int64)
+        oracle.bin_particles(w.dim, w.n, w.tile, sample, rng)
+        oracle.p2g_quadratic(w.dim, w.n, w.frac_bits, sample, rng, grid=grid)
+        dt = time.perf_counter() - t
+        out["cpu_baseline"] = {"value": round(n_s / dt, 1), "unit": "particles/s", "cores": 1, "kind": "oracle",
+                               "sample": f"one step (grid clear + counting sort + P2G) over the first {n_s} "
+                                         f"particles of {w.name}, single-threaded C oracle, {dt:.2f}s",
+                               "host_cpus": os.cpu_count()}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+/*
+ * mpm.h -- C ABI of libmpm, the MI355X (gfx950) particle-to-grid (P2G) hot
+ * path of the material point method and the steps around it.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device pointers must point to device memory of the
+ *    current HIP device; the caller owns them (the library allocates nothing
+ *    and keeps no per-call state between calls).  Host pointers are read
+ *    before the call returns.
+ *  - Work is enqueued on `stream` and the call returns without waiting; the
+ *    library never synchronises the stream.  Results (and the status
+ *    counters) are valid once the caller's stream has reached that point.
+ *  - The return value reports only errors the host can detect before any
+ *    launch (bad descriptor, NULL or misaligned pointer, workspace too small,
+ *    bounds that would overflow) or a failed launch.  On a non-zero return
+ *    nothing was enqueued, except for MPM_ERR_HIP after a partial launch
+ *    sequence, which leaves outputs unspecified.
+ *  - Conditions met on the device are counted in the caller's status
+ *    counters (uint32_t status[4], zeroed by the caller, accumulated into):
+ *      status[0]  particles skipped because their stencil leaves the grid
+ *                 (or a coordinate is not finite),
+ *      status[1]  particles skipped because mass, velocity or affine entries
+ *                 fall outside the declared ranges the bounds check proved,
+ *      status[2]  particles whose advected position was clamped to the box,
+ *      status[3]  internal consistency faults: an order entry naming no
+ *                 particle, or a binned record outside its tile (skipped;
+ *                 0 in correct use).
+ *    "Implementation -- GPU Optimization & Reference Codebases", section 5
+ *    rules 8 and 9: read back asynchronously, and count what overflows or is
+ *    clamped instead of sanitising silently.
+ *  - Layouts are component-major structure-of-arrays: a per-particle vector
+ *    field of D components over N particles is float[D][N]; the affine
+ *    matrix is float[dim*dim][N] with entry (row d, column e) at
+ *    [(d*dim + e)*N + p].  Grids are int64[channels][n]...[n] with x fastest;
+ *    channel 0 is mass, channel 1+d momentum along axis d.
+ */
+#ifndef MPM_H
+#define MPM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MPM_OK = 0,
+    MPM_ERR_INVALID = -1,   /* bad descriptor, NULL or misaligned pointer, bad size */
+    MPM_ERR_OVERFLOW = -2,  /* the declared ranges could overflow the accumulators */
+    MPM_ERR_DOMAIN = -3,    /* reserved: domain problems are counted on the device */
+    MPM_ERR_WORKSPACE = -4, /* workspace smaller than mpm_workspace_bytes() */
+    MPM_ERR_HIP = -6        /* a HIP call or kernel launch failed */
+} mpm_status;
+
+/* The background grid of the quadratic-stencil transfer.  The domain is the
+ * unit square/cube with n nodes per axis, node i at i/n (dx = 1/n).
+ * n must be a power of two in [8, 1024] (2D) or [8, 512] (3D), so that x*n
+ * and dx are exact in float32.  Fixed-point scale S = 2^frac_bits with
+ * frac_bits in [0, 60].  tile is the binning tile edge in cells and must be 4. */
+typedef struct {
+    int32_t dim;
+    int32_t n;
+    int32_t frac_bits;
+    int32_t tile;
+} mpm_grid_desc;
+
+/* Particle attributes, device pointers, component-major (see above).
+ * C may be NULL for a transfer without the affine term (treated as zero). */
+typedef struct {
+    int64_t n;
+    float *x;     /* [dim][n] positions in the unit domain */
+    float *v;     /* [dim][n] velocities */
+    float *C;     /* [dim*dim][n] affine (APIC) matrices */
+    float *m;     /* [n] masses */
+} mpm_particles;
+
+/* Declared ranges: |m| <= max_mass, |v_d| <= max_speed, |C_de| <= max_affine.
+ * The bounds check proves that no accumulator can overflow for particles in
+ * these ranges; a particle outside them is skipped and counted (status[1]).
+ * "particle to grid transfer in checked integer arithmetic", section "the
+ * program": the bounds line runs before any particle is scattered. */
+typedef struct {
+    double max_mass;
+    double max_speed;
+    double max_affine;
+} mpm_ranges;
+
+/* Offsets (bytes from the workspace base) of the arrays mpm_bin_particles
+ * writes, so that callers and tests can read them.  Counts are the
+ * capacities allocated, not what one call fills. */
+typedef struct {
+    size_t cell_start;      /* uint32 [n_cells + 1] exclusive prefix sum of per-cell counts    */
+    size_t cell_count;      /* uint32 [n_cells]     per-cell particle counts                    */
+    size_t tile_row_start;  /* uint32 [n_tiles + 1] first 64-slot row of each tile              */
+    size_t item_start;      /* uint32 [n_tiles + 1] first P2G work item of each tile            */
+    size_t items;           /* uint32 [2][max_items] (tile, first row) of each work item        */
+    size_t meta;            /* uint32 [16]: [0] items, [1] rows, [2] binned particles, [3] work cursor */
+    size_t key;             /* uint32 [n] cell key of each particle (0xFFFFFFFF when skipped)   */
+    size_t rank;            /* uint32 [n] arrival rank of each particle inside its cell         */
+    size_t order;           /* uint32 [max_slots] slot -> particle index (0xFFFFFFFF: empty)    */
+    size_t sorted;          /* float  [max_slots][n_fields] binned records x, v, C, m, padding  */
+    size_t tile_tmp;        /* uint32 [2][n_tiles] per-tile row and work-item counts (internal) */
+    size_t scan_tmp;        /* uint32 [scan_blocks] prefix-sum block totals (internal)          */
+    int64_t n_cells, n_tiles, max_items, max_slots, n_fields, rows_per_item;
+    size_t total_bytes;
+} mpm_ws_layout;
+
+/* ------------------------------------------------------------------------ */
+
+/* Library version string (static storage). */
+const char *mpm_version(void);
+
+/* Message for a return code (static storage). */
+const char *mpm_strerror(int code);
+
+/* Host-only bounds line, run before any scatter ("particle to grid transfer
+ * in checked integer arithmetic", sections "integers do not care about
+ * order" and "limits").  The largest quantised contribution is
+ *   S * (3/4)^dim * max_mass * max(1, max_speed + dim * max_affine * 1.5 dx)
+ * (each 1D quadratic weight is at most 3/4, each node offset at most 1.5
+ * cells), plus float32 rounding.  Returns MPM_OK when n_particles times that
+ * stays below 2^63 (every int64 node sum completes in any order) and one
+ * P2G work item's worth of it stays below 2^53 (the exact float64 on-chip
+ * partial sums), else MPM_ERR_OVERFLOW.  log2_bound (may be NULL) receives
+ * log2(n_particles * largest contribution). */
+int mpm_check_bounds(const mpm_grid_desc *grid, int64_t n_particles, const mpm_ranges *ranges,
+                     double *log2_bound);
+
+/* Workspace size for binning n_particles on this grid (host-only). */
+int mpm_workspace_bytes(const mpm_grid_desc *grid, int64_t n_particles, size_t *bytes);
+
+/* Offsets of the arrays inside that workspace (host-only). */
+int mpm_workspace_layout(const mpm_grid_desc *grid, int64_t n_particles, mpm_ws_layout *layout);
+
+/* Counting sort of the particles into tiles of 4^dim cells, keyed by the
+ * stencil's base cell and numbered tile by tile ("Particle worlds, part 3",
+ * steps 3-4: histogram, exclusive prefix sum, scatter; "Implementation --
+ * GPU Optimization & Reference Codebases", section 2.1: sort + tile).  The
+ * caller's arrays are not reordered (section 5 rule 2): the workspace
+ * receives the cell histogram and prefix sum, per-tile 64-slot rows, the
+ * P2G work items, a slot -> particle permutation and a binned copy of
+ * x, v, C, m.  Particles whose stencil leaves the grid or whose attributes
+ * leave the declared ranges are not binned and are counted in status[0] and
+ * status[1].  Arrival order inside a cell is not deterministic; the P2G grid
+ * built from the bins is (integer sums commute).
+ * particles, status: device.  ws: device, ws_bytes >= mpm_workspace_bytes().
+ * Errors: MPM_ERR_INVALID, MPM_ERR_WORKSPACE, MPM_ERR_OVERFLOW (bounds),
+ * MPM_ERR_HIP. */
+int mpm_bin_particles(const mpm_grid_desc *grid, const mpm_particles *particles, const mpm_ranges *ranges,
+                      void *ws, size_t ws_bytes, uint32_t *status, hipStream_t stream);
+
+/* Fixed-point APIC P2G with the quadratic B-spline stencil (3^dim nodes per
+ * particle).  For each particle and stencil node, in float32 with one
+ * rounding per operation:
+ *   wmS = (((m * S) * wx[a]) * wy[b]) * wz[c]
+ *   u_d = ((v_d + C_d0 * rx[a]) + C_d1 * ry[b]) + C_d2 * rz[c]
+ *   M  += rint(wmS),  P_d += rint(wmS * u_d)     (round to nearest, ties even)
+ * where g = x*n, base = floor(g - 1/2), f = g - base, the weights are the
+ * quadratic B-spline at distances f, f-1, f-2 and r[o] = (o - f) dx.
+ * Sources: "Implementation -- GPU Optimization & Reference Codebases",
+ * sections 1 (P2G scatter), 2.1 (fixed-point accumulation, shared-memory
+ * tiles, warp-level pre-reduction) and 3.1 (APIC, 3x3 quadratic stencil,
+ * affine matrix C); "Mass Matrix Assembly on Tensor Cores for Implicit
+ * PIC", shape functions (tensor-product B-spline, stencil placement).
+ * Accumulation is in integers, so the grid is identical for every particle
+ * order and every scheduling.
+ *   bins == NULL: one thread per particle of `particles`, 64-bit global
+ *     atomics; skipped particles are counted in status[0]/status[1].
+ *   bins != NULL: the workspace filled by mpm_bin_particles for these
+ *     particles on this grid (particles may be NULL); one wavefront per
+ *     work item of one tile accumulates the tile's node block on chip and
+ *     flushes it with one 64-bit atomic per non-zero node and channel.
+ * grid: device int64[1+dim][n]^dim, accumulated into (zero it first for a
+ * fresh transfer).  The caller must have run mpm_check_bounds on `ranges`;
+ * this call re-checks and refuses with MPM_ERR_OVERFLOW.
+ * Errors: MPM_ERR_INVALID, MPM_ERR_OVERFLOW, MPM_ERR_HIP. */
+int mpm_p2g(const mpm_grid_desc *grid, const mpm_particles *particles, const mpm_ranges *ranges,
+            const void *bins, int64_t *grid_out, uint32_t *status, hipStream_t stream);
+
+/* Integer-split cloud-in-cell scatter in 2D ("particle to grid transfer in
+ * checked integer arithmetic", sections "integers do not care about order"
+ * and "the program").  Positions X[2][n] are int32 in units of 1/65536 of a
+ * cell on a cells x cells grid; m[n] and vel[2][n] are integers.  Each of
+ * q = m, m*vx, m*vy is split along x into far = round(q*fx/65536) (ties to
+ * even) and near = q - far, and each part likewise along y, so the four
+ * shares sum to q exactly.  grid: device int64[3][cells+1][cells+1],
+ * accumulated into.  order (device, may be NULL) gives the visiting order;
+ * the result is the same for every order.  Particles outside the grid are
+ * skipped and counted in status[0].  The bounds line
+ * n * max_mass * max_speed < 2^63 (and max_mass * max_speed * 65536 < 2^63)
+ * is checked on the host with the declared maxima.
+ * Errors: MPM_ERR_INVALID, MPM_ERR_OVERFLOW, MPM_ERR_HIP. */
+int mpm_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32_t *vel, const uint32_t *order,
+                      int32_t cells, int64_t max_mass, int64_t max_speed, int64_t *grid_out, uint32_t *status,
+                      hipStream_t stream);
+
+/* Grid update with consume-and-zero ("Implementation -- GPU Optimization &
+ * Reference Codebases", section 1 four-phase step; section 2.1 and rule 4
+ * of section 5: each accumulator has one reader, which zeroes it; rule 1:
+ * convert the fixed-point sums once, here; rule 7: gravity belongs to the
+ * solver).  Per node: where M != 0, v_d = (float)((double)P_d / (double)M)
+ * then v_d = v_d + (dt * g_d) (the product formed once in float32); where
+ * M == 0, v = 0; nodes within `sticky` nodes of any face get v = 0; then
+ * M and P are set to 0.
+ * grid: device int64[1+dim][n]^dim, read and zeroed.  vg: device
+ * float[dim][n]^dim, written.  gravity: host float[dim].
+ * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
+int mpm_grid_update(const mpm_grid_desc *grid, int64_t *grid_io, float *vg, float dt, const float *gravity,
+                    int32_t sticky, hipStream_t stream);
+
+/* APIC grid-to-particle gather and advection ("Implementation -- GPU
+ * Optimization & Reference Codebases", sections 1 and 3.1).  Per particle,
+ * over its stencil nodes in lexicographic order (x offset outermost), with
+ * w = (wx[a] * wy[b]) * wz[c]:  wv_d = w * vg_d;  v_d += wv_d;
+ * B_de += wv_d * r_e;  then C = B * (4 n^2), x_e += dt * v_e, and x_e is
+ * clamped to [dx, (n-2) dx] (clamped particles counted in status[2]).
+ * Particles whose stencil leaves the grid are left unchanged and counted in
+ * status[0].  particles: device, x, v, C read/written in place (m unused).
+ * vg: device float[dim][n]^dim.
+ * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
+int mpm_g2p(const mpm_grid_desc *grid, const float *vg, const mpm_particles *particles, float dt,
+            uint32_t *status, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MPM_H */

@@ -1,0 +1,14 @@
+"""MI355X (gfx950) particle-to-grid transfer of the material point method.
+
+The compute path is libmpm.so (hand-written HIP kernels behind a C ABI, see
+include/mpm.h); this package holds the HIP sources (csrc/), the build step
+(build.py), the ctypes binding (_lib.py) and a small device-memory driver
+(transfer.py).  PyTorch is used for device memory and streams only.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS, LIB_PATH, MpmError, grid_desc, lib, mpm_bin_particles, mpm_check_bounds, mpm_g2p, mpm_grid_update,
+    mpm_p2g, mpm_p2g_cic_split, mpm_strerror, mpm_version, mpm_workspace_bytes, mpm_workspace_layout, particles,
+    ranges,
+)
+
+__version__ = "0.1.0"

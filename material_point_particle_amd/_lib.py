@@ -1,0 +1,183 @@
+"""ctypes binding of libmpm: the C entry points under the same names.
+
+Argument marshalling only: device tensors are passed as raw pointers and the
+current torch stream as the HIP stream; every step of the transfer runs in
+the library's HIP kernels.  Loading fails loudly when libmpm.so is missing
+(build it with ``python -m material_point_particle_amd.build``); there is no
+CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmpm.so")
+
+MPM_OK = 0
+MPM_ERR_INVALID = -1
+MPM_ERR_OVERFLOW = -2
+MPM_ERR_DOMAIN = -3
+MPM_ERR_WORKSPACE = -4
+MPM_ERR_HIP = -6
+
+
+class MpmError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {mpm_strerror(code)} (code {code})")
+        self.code = code
+
+
+class mpm_grid_desc(ct.Structure):
+    _fields_ = [("dim", ct.c_int32), ("n", ct.c_int32), ("frac_bits", ct.c_int32), ("tile", ct.c_int32)]
+
+
+class mpm_particles(ct.Structure):
+    _fields_ = [("n", ct.c_int64), ("x", ct.c_void_p), ("v", ct.c_void_p), ("C", ct.c_void_p), ("m", ct.c_void_p)]
+
+
+class mpm_ranges(ct.Structure):
+    _fields_ = [("max_mass", ct.c_double), ("max_speed", ct.c_double), ("max_affine", ct.c_double)]
+
+
+class mpm_ws_layout(ct.Structure):
+    _fields_ = [(name, ct.c_size_t) for name in ("cell_start", "cell_count", "tile_row_start", "item_start", "items",
+                                                  "meta", "key", "rank", "order", "sorted", "tile_tmp", "scan_tmp")]
+    _fields_ += [(name, ct.c_int64) for name in ("n_cells", "n_tiles", "max_items", "max_slots", "n_fields",
+                                                  "rows_per_item")]
+    _fields_ += [("total_bytes", ct.c_size_t)]
+
+
+EXPORTS = ("mpm_version", "mpm_strerror", "mpm_check_bounds", "mpm_workspace_bytes", "mpm_workspace_layout",
+           "mpm_bin_particles", "mpm_p2g", "mpm_p2g_cic_split", "mpm_grid_update", "mpm_g2p")
+
+_lib = None
+
+
+def lib() -> ct.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libmpm.so not found at {LIB_PATH}; build it with "
+                               "`python -m material_point_particle_amd.build` (no CPU fallback exists)")
+        L = ct.CDLL(LIB_PATH)
+        P = ct.POINTER
+        L.mpm_version.restype = ct.c_char_p
+        L.mpm_version.argtypes = []
+        L.mpm_strerror.restype = ct.c_char_p
+        L.mpm_strerror.argtypes = [ct.c_int]
+        L.mpm_check_bounds.restype = ct.c_int
+        L.mpm_check_bounds.argtypes = [P(mpm_grid_desc), ct.c_int64, P(mpm_ranges), P(ct.c_double)]
+        L.mpm_workspace_bytes.restype = ct.c_int
+        L.mpm_workspace_bytes.argtypes = [P(mpm_grid_desc), ct.c_int64, P(ct.c_size_t)]
+        L.mpm_workspace_layout.restype = ct.c_int
+        L.mpm_workspace_layout.argtypes = [P(mpm_grid_desc), ct.c_int64, P(mpm_ws_layout)]
+        L.mpm_bin_particles.restype = ct.c_int
+        L.mpm_bin_particles.argtypes = [P(mpm_grid_desc), P(mpm_particles), P(mpm_ranges), ct.c_void_p, ct.c_size_t,
+                                        ct.c_void_p, ct.c_void_p]
+        L.mpm_p2g.restype = ct.c_int
+        L.mpm_p2g.argtypes = [P(mpm_grid_desc), P(mpm_particles), P(mpm_ranges), ct.c_void_p, ct.c_void_p,
+                              ct.c_void_p, ct.c_void_p]
+        L.mpm_p2g_cic_split.restype = ct.c_int
+        L.mpm_p2g_cic_split.argtypes = [ct.c_int64, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int32,
+                                        ct.c_int64, ct.c_int64, ct.c_void_p, ct.c_void_p, ct.c_void_p]
+        L.mpm_grid_update.restype = ct.c_int
+        L.mpm_grid_update.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_float, P(ct.c_float),
+                                      ct.c_int32, ct.c_void_p]
+        L.mpm_g2p.restype = ct.c_int
+        L.mpm_g2p.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_float, ct.c_void_p, ct.c_void_p]
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != MPM_OK:
+        raise MpmError(rc, where)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def grid_desc(dim: int, n: int, frac_bits: int, tile: int = 4) -> mpm_grid_desc:
+    return mpm_grid_desc(dim, n, frac_bits, tile)
+
+
+def ranges(max_mass: float, max_speed: float, max_affine: float) -> mpm_ranges:
+    return mpm_ranges(max_mass, max_speed, max_affine)
+
+
+def particles(n: int, x=None, v=None, C=None, m=None) -> mpm_particles:
+    """Descriptor of component-major device tensors x[dim][n], v[dim][n],
+    C[dim*dim][n], m[n] (float32, contiguous)."""
+    for t in (x, v, C, m):
+        if t is not None:
+            assert t.is_contiguous() and t.dtype.itemsize == 4, "particle arrays must be contiguous float32"
+    return mpm_particles(n, _ptr(x), _ptr(v), _ptr(C), _ptr(m))
+
+
+# ------------------------------------------------------------------ entry points
+
+def mpm_version() -> str:
+    return lib().mpm_version().decode()
+
+
+def mpm_strerror(code: int) -> str:
+    try:
+        return lib().mpm_strerror(code).decode()
+    except RuntimeError:
+        return f"error {code}"
+
+
+def mpm_check_bounds(desc: mpm_grid_desc, n_particles: int, rng: mpm_ranges) -> float:
+    """Returns log2 of the bound; raises MpmError(MPM_ERR_OVERFLOW) when refused."""
+    out = ct.c_double(0.0)
+    _check(lib().mpm_check_bounds(ct.byref(desc), n_particles, ct.byref(rng), ct.byref(out)), "mpm_check_bounds")
+    return out.value
+
+
+def mpm_workspace_bytes(desc: mpm_grid_desc, n_particles: int) -> int:
+    out = ct.c_size_t(0)
+    _check(lib().mpm_workspace_bytes(ct.byref(desc), n_particles, ct.byref(out)), "mpm_workspace_bytes")
+    return out.value
+
+
+def mpm_workspace_layout(desc: mpm_grid_desc, n_particles: int) -> mpm_ws_layout:
+    out = mpm_ws_layout()
+    _check(lib().mpm_workspace_layout(ct.byref(desc), n_particles, ct.byref(out)), "mpm_workspace_layout")
+    return out
+
+
+def mpm_bin_particles(desc, parts: mpm_particles, rng: mpm_ranges, ws, status, stream=None) -> None:
+    _check(lib().mpm_bin_particles(ct.byref(desc), ct.byref(parts), ct.byref(rng), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _ptr(status), _stream(stream)), "mpm_bin_particles")
+
+
+def mpm_p2g(desc, parts: mpm_particles, rng: mpm_ranges, bins, grid, status, stream=None) -> None:
+    _check(lib().mpm_p2g(ct.byref(desc), ct.byref(parts), ct.byref(rng), _ptr(bins), _ptr(grid), _ptr(status),
+                         _stream(stream)), "mpm_p2g")
+
+
+def mpm_p2g_cic_split(X, m, vel, order, cells: int, max_mass: int, max_speed: int, grid, status, stream=None) -> None:
+    _check(lib().mpm_p2g_cic_split(m.numel(), _ptr(X), _ptr(m), _ptr(vel), _ptr(order), cells, max_mass, max_speed,
+                                   _ptr(grid), _ptr(status), _stream(stream)), "mpm_p2g_cic_split")
+
+
+def mpm_grid_update(desc, grid, vg, dt: float, gravity, sticky: int, stream=None) -> None:
+    g = (ct.c_float * 3)(*(list(gravity) + [0.0] * (3 - len(gravity))))
+    _check(lib().mpm_grid_update(ct.byref(desc), _ptr(grid), _ptr(vg), dt, g, sticky, _stream(stream)),
+           "mpm_grid_update")
+
+
+def mpm_g2p(desc, vg, parts: mpm_particles, dt: float, status, stream=None) -> None:
+    _check(lib().mpm_g2p(ct.byref(desc), _ptr(vg), ct.byref(parts), dt, _ptr(status), _stream(stream)), "mpm_g2p")

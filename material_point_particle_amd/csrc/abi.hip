@@ -1,0 +1,320 @@
+// abi.hip -- the extern "C" entry points of libmpm: argument validation, the
+// host-side bounds line, workspace layout, and launches on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "common.hpp"
+
+namespace mpmk {
+
+int device_cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0)
+        return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+        v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+}  // namespace mpmk
+
+namespace {
+
+using namespace mpmk;
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+bool aligned(const void *p, size_t a) { return p != nullptr && ((uintptr_t)p % a) == 0; }
+
+int check_desc(const mpm_grid_desc *g)
+{
+    if (!g || (g->dim != 2 && g->dim != 3))
+        return MPM_ERR_INVALID;
+    const int nmax = g->dim == 3 ? 512 : 1024;
+    if (!is_pow2(g->n) || g->n < 8 || g->n > nmax)
+        return MPM_ERR_INVALID;
+    if (g->frac_bits < 0 || g->frac_bits > 60 || g->tile != kTile)
+        return MPM_ERR_INVALID;
+    return MPM_OK;
+}
+
+int check_ranges(const mpm_ranges *r)
+{
+    if (!r)
+        return MPM_ERR_INVALID;
+    if (!(r->max_mass >= 0.0) || !(r->max_speed >= 0.0) || !(r->max_affine >= 0.0))
+        return MPM_ERR_INVALID;
+    return MPM_OK;
+}
+
+// Largest float not above v (v >= 0), so |x| <= result in float32 decides
+// exactly |x| <= v in real numbers for every float x.
+float floor_to_float(double v)
+{
+    float f = (float)v;
+    if ((double)f > v)
+        f = nextafterf(f, -INFINITY);
+    return f;
+}
+
+RangesF ranges_f(const mpm_ranges *r)
+{
+    RangesF o;
+    o.max_mass = floor_to_float(r->max_mass);
+    o.max_speed = floor_to_float(r->max_speed);
+    o.max_affine = floor_to_float(r->max_affine);
+    return o;
+}
+
+// log2 of the largest quantised contribution under the declared ranges.
+double log2_max_contribution(const mpm_grid_desc *g, const mpm_ranges *r)
+{
+    const double dx = 1.0 / (double)g->n;
+    const double wmax = g->dim == 3 ? 27.0 / 64.0 : 9.0 / 16.0;     // (3/4)^dim
+    double umax = r->max_speed + (double)g->dim * r->max_affine * 1.5 * dx;
+    if (umax < 1.0)
+        umax = 1.0;                                                   // mass channel: u = 1
+    const double q = ldexp(1.0, g->frac_bits) * wmax * r->max_mass * umax * (1.0 + ldexp(1.0, -20)) + 1.0;
+    return log2(q);
+}
+
+struct Layout {
+    mpm_ws_layout l;
+};
+
+int64_t pow_int(int64_t b, int e)
+{
+    int64_t r = 1;
+    for (int i = 0; i < e; ++i)
+        r *= b;
+    return r;
+}
+
+void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
+{
+    memset(o, 0, sizeof(*o));
+    const int64_t n_cells = pow_int(g->n, g->dim);
+    const int64_t n_tiles = pow_int(g->n / kTile, g->dim);
+    const int64_t busy = np < n_tiles ? (np > 0 ? np : 1) : n_tiles;       // tiles that can hold particles
+    const int64_t max_rows = (np + kWave - 1) / kWave + busy;
+    const int64_t max_items = (max_rows + kRowsPerItem - 1) / kRowsPerItem + busy;
+    const int64_t n_fields = g->dim == 3 ? rec_floats<3>() : rec_floats<2>();
+    const int64_t big = n_cells > n_tiles ? n_cells : n_tiles;
+    const int64_t scan_blocks = (big + kScanTileElems - 1) / kScanTileElems + 1;
+    size_t off = 0;
+    auto take = [&off](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return at;
+    };
+    const size_t u4 = sizeof(uint32_t);
+    const int64_t n1 = np > 0 ? np : 1;
+    o->cell_start = take(u4 * (size_t)(n_cells + 1));
+    o->cell_count = take(u4 * (size_t)n_cells);
+    o->tile_row_start = take(u4 * (size_t)(n_tiles + 1));
+    o->item_start = take(u4 * (size_t)(n_tiles + 1));
+    o->items = take(u4 * 2 * (size_t)max_items);
+    o->meta = take(u4 * 16);
+    o->key = take(u4 * (size_t)n1);
+    o->rank = take(u4 * (size_t)n1);
+    o->order = take(u4 * (size_t)(max_rows * kWave));
+    o->sorted = take(sizeof(float) * (size_t)(n_fields * max_rows * kWave));
+    o->tile_tmp = take(u4 * 2 * (size_t)n_tiles);
+    o->scan_tmp = take(u4 * (size_t)scan_blocks);
+    o->n_cells = n_cells;
+    o->n_tiles = n_tiles;
+    o->max_items = max_items;
+    o->max_slots = max_rows * kWave;
+    o->n_fields = n_fields;
+    o->rows_per_item = kRowsPerItem;
+    o->total_bytes = off;
+}
+
+BinView bin_view(void *ws, const mpm_ws_layout &l)
+{
+    char *b = (char *)ws;
+    BinView v;
+    v.cell_start = (uint32_t *)(b + l.cell_start);
+    v.cell_count = (uint32_t *)(b + l.cell_count);
+    v.tile_row_start = (uint32_t *)(b + l.tile_row_start);
+    v.item_start = (uint32_t *)(b + l.item_start);
+    v.items = (uint32_t *)(b + l.items);
+    v.meta = (uint32_t *)(b + l.meta);
+    v.key = (uint32_t *)(b + l.key);
+    v.rank = (uint32_t *)(b + l.rank);
+    v.order = (uint32_t *)(b + l.order);
+    v.sorted = (float *)(b + l.sorted);
+    v.tile_tmp = (uint32_t *)(b + l.tile_tmp);
+    v.scan_tmp = (uint32_t *)(b + l.scan_tmp);
+    v.n_cells = l.n_cells;
+    v.n_tiles = l.n_tiles;
+    v.max_items = l.max_items;
+    v.max_slots = l.max_slots;
+    v.n_fields = l.n_fields;
+    return v;
+}
+
+int check_particles(const mpm_grid_desc *g, const mpm_particles *p, bool need_arrays, bool need_mass)
+{
+    if (!p || p->n < 0 || p->n > (int64_t)0xFFFFFFF0)
+        return MPM_ERR_INVALID;
+    if (!need_arrays || p->n == 0)
+        return MPM_OK;
+    if (!aligned(p->x, 4) || !aligned(p->v, 4))
+        return MPM_ERR_INVALID;
+    if (p->C && !aligned(p->C, 4))
+        return MPM_ERR_INVALID;
+    if (need_mass && !aligned(p->m, 4))
+        return MPM_ERR_INVALID;
+    (void)g;
+    return MPM_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MPM_OK : MPM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *mpm_version(void) { return "libmpm 0.1.0 gfx950"; }
+
+const char *mpm_strerror(int code)
+{
+    switch (code) {
+    case MPM_OK: return "ok";
+    case MPM_ERR_INVALID: return "invalid argument (descriptor, pointer, alignment or size)";
+    case MPM_ERR_OVERFLOW: return "declared ranges could overflow the fixed-point accumulators";
+    case MPM_ERR_DOMAIN: return "particle outside the grid";
+    case MPM_ERR_WORKSPACE: return "workspace too small";
+    case MPM_ERR_HIP: return "HIP runtime or launch failure";
+    default: return "unknown error";
+    }
+}
+
+int mpm_check_bounds(const mpm_grid_desc *grid, int64_t n_particles, const mpm_ranges *ranges, double *log2_bound)
+{
+    int rc;
+    if ((rc = check_desc(grid)) != MPM_OK || (rc = check_ranges(ranges)) != MPM_OK || n_particles < 0)
+        return rc != MPM_OK ? rc : MPM_ERR_INVALID;
+    const double lq = log2_max_contribution(grid, ranges);
+    const double lb = lq + log2((double)(n_particles > 0 ? n_particles : 1));
+    if (log2_bound)
+        *log2_bound = lb;
+    // int64 node sums over all particles; exact float64 partial sums over one
+    // work item (at most kRowsPerItem * 64 particles) on chip.
+    if (!(lb < 62.999) || !(lq + log2((double)(kRowsPerItem * kWave)) < 53.0))
+        return MPM_ERR_OVERFLOW;
+    return MPM_OK;
+}
+
+int mpm_workspace_layout(const mpm_grid_desc *grid, int64_t n_particles, mpm_ws_layout *layout)
+{
+    if (check_desc(grid) != MPM_OK || n_particles < 0 || n_particles > (int64_t)0xFFFFFFF0 || !layout)
+        return MPM_ERR_INVALID;
+    make_layout(grid, n_particles, layout);
+    return MPM_OK;
+}
+
+int mpm_workspace_bytes(const mpm_grid_desc *grid, int64_t n_particles, size_t *bytes)
+{
+    mpm_ws_layout l;
+    const int rc = mpm_workspace_layout(grid, n_particles, &l);
+    if (rc != MPM_OK || !bytes)
+        return rc != MPM_OK ? rc : MPM_ERR_INVALID;
+    *bytes = l.total_bytes;
+    return MPM_OK;
+}
+
+int mpm_bin_particles(const mpm_grid_desc *grid, const mpm_particles *particles, const mpm_ranges *ranges, void *ws,
+                      size_t ws_bytes, uint32_t *status, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_desc(grid)) != MPM_OK || (rc = check_ranges(ranges)) != MPM_OK ||
+        (rc = check_particles(grid, particles, true, true)) != MPM_OK)
+        return rc;
+    if (!aligned(ws, 256) || !aligned(status, 4))
+        return MPM_ERR_INVALID;
+    if ((rc = mpm_check_bounds(grid, particles->n, ranges, nullptr)) != MPM_OK)
+        return rc;
+    mpm_ws_layout l;
+    make_layout(grid, particles->n, &l);
+    if (ws_bytes < l.total_bytes)
+        return MPM_ERR_WORKSPACE;
+    const BinView b = bin_view(ws, l);
+    Fields f{ particles->x, particles->v, particles->C, particles->m, particles->n };
+    return hip_status(launch_bin(grid->dim, grid->n, f, ranges_f(ranges), b, status, stream));
+}
+
+int mpm_p2g(const mpm_grid_desc *grid, const mpm_particles *particles, const mpm_ranges *ranges, const void *bins,
+            int64_t *grid_out, uint32_t *status, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_desc(grid)) != MPM_OK || (rc = check_ranges(ranges)) != MPM_OK ||
+        (rc = check_particles(grid, particles, bins == nullptr, true)) != MPM_OK)
+        return rc;
+    if (!aligned(grid_out, 8) || !aligned(status, 4))
+        return MPM_ERR_INVALID;
+    if ((rc = mpm_check_bounds(grid, particles->n, ranges, nullptr)) != MPM_OK)
+        return rc;
+    if (bins) {
+        if (!aligned(bins, 256))
+            return MPM_ERR_INVALID;
+        mpm_ws_layout l;
+        make_layout(grid, particles->n, &l);
+        return hip_status(launch_p2g_tiled(grid->dim, grid->n, grid->frac_bits, bin_view((void *)bins, l), grid_out,
+                                           status, stream));
+    }
+    Fields f{ particles->x, particles->v, particles->C, particles->m, particles->n };
+    return hip_status(launch_p2g_direct(grid->dim, grid->n, grid->frac_bits, f, nullptr, ranges_f(ranges), grid_out,
+                                        status, stream));
+}
+
+int mpm_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32_t *vel, const uint32_t *order,
+                      int32_t cells, int64_t max_mass, int64_t max_speed, int64_t *grid_out, uint32_t *status,
+                      hipStream_t stream)
+{
+    if (n < 0 || n > (int64_t)0xFFFFFFF0 || cells < 1 || cells > 32767 || max_mass < 0 || max_speed < 0)
+        return MPM_ERR_INVALID;
+    if (!aligned(grid_out, 8) || !aligned(status, 4))
+        return MPM_ERR_INVALID;
+    if (n > 0 && (!aligned(X, 4) || !aligned(m, 4) || !aligned(vel, 4) || (order && !aligned(order, 4))))
+        return MPM_ERR_INVALID;
+    // bounds line: n * max_mass * max_speed and the split products q * f fit int64
+    const long double sp = (long double)(max_speed > 1 ? max_speed : 1);
+    const long double lim = 9223372036854775807.0L;
+    if ((long double)n * (long double)max_mass * sp > lim || (long double)max_mass * sp * 65536.0L > lim)
+        return MPM_ERR_OVERFLOW;
+    return hip_status(launch_p2g_cic_split(n, X, m, vel, order, cells, grid_out, status, stream));
+}
+
+int mpm_grid_update(const mpm_grid_desc *grid, int64_t *grid_io, float *vg, float dt, const float *gravity,
+                    int32_t sticky, hipStream_t stream)
+{
+    if (check_desc(grid) != MPM_OK || !aligned(grid_io, 8) || !aligned(vg, 4) || !gravity || sticky < 0 ||
+        sticky > grid->n / 2)
+        return MPM_ERR_INVALID;
+    float g3[3] = { gravity[0], gravity[1], grid->dim == 3 ? gravity[2] : 0.0f };
+    return hip_status(launch_grid_update(grid->dim, grid->n, grid_io, vg, dt, g3, sticky, stream));
+}
+
+int mpm_g2p(const mpm_grid_desc *grid, const float *vg, const mpm_particles *particles, float dt, uint32_t *status,
+            hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_desc(grid)) != MPM_OK || (rc = check_particles(grid, particles, true, false)) != MPM_OK)
+        return rc;
+    if (!aligned(vg, 4) || !aligned(status, 4) || (particles->n > 0 && !particles->C))
+        return MPM_ERR_INVALID;
+    return hip_status(launch_g2p(grid->dim, grid->n, vg, particles->x, particles->v, particles->C, particles->n, dt,
+                                 status, stream));
+}
+
+}  // extern "C"

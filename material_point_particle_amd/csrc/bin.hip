@@ -1,0 +1,332 @@
+// bin.hip -- counting sort of particles into tiles of 4^dim cells (gfx950).
+//
+// "Particle worlds, part 3" (steps 3 and 4): a histogram of cell numbers, an
+// exclusive prefix sum, and a scatter of each particle to its slot; the
+// implementation page's section 2.1 bins particles into tiles every substep
+// and builds an index table so the particle arrays themselves never move.
+//
+// Passes (all on the caller's stream, no host synchronisation):
+//   1. count    one thread per particle: base cell -> tile-major cell key;
+//               atomic increment of the cell's counter returns the particle's
+//               arrival rank inside the cell.
+//   2. scan     exclusive prefix sum of the cell counters (three phases:
+//               per-block sums, one block scans the sums, per-block rescan).
+//   3. layout   per tile: rows of 64 slots needed, and P2G work items of up to
+//               kRowsPerItem rows; both prefix-summed over tiles.
+//   4. items    per tile: the (tile, first row) of each of its work items.
+//   5. scatter  one thread per particle: its slot in the tile's transposed
+//               row layout; the slot -> particle index and a record of the
+//               particle's fields (x, v, C, m: 64 bytes in 3D) are written
+//               there, so each scattered write is one whole record.
+// Arrival ranks depend on scheduling, so slot contents differ between runs;
+// every slot holds one particle of the right cell, which is all P2G needs.
+#include "common.hpp"
+
+namespace mpmk {
+namespace {
+
+constexpr int kScanBlock = 256;
+constexpr int kScanItems = 16;
+constexpr int kScanTile = kScanBlock * kScanItems;
+
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v)
+{
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t o = __shfl_up(v, d, kWave);
+        if (lane >= d)
+            v += o;
+    }
+    return v;
+}
+
+// Exclusive scan across the block of one value per thread; returns the
+// exclusive prefix and writes the block total to *total.
+template <int BLOCK>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *total)
+{
+    __shared__ uint32_t wsum[BLOCK / kWave];
+    const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+    const uint32_t inc = wave_inclusive_scan(v);
+    if (lane == kWave - 1)
+        wsum[wid] = inc;
+    __syncthreads();
+    if (wid == 0) {
+        uint32_t w = lane < BLOCK / kWave ? wsum[lane] : 0u;
+        const uint32_t winc = wave_inclusive_scan(w);
+        if (lane < BLOCK / kWave)
+            wsum[lane] = winc - w;
+        if (lane == kWave - 1)
+            *total = winc;
+    }
+    __syncthreads();
+    const uint32_t r = wsum[wid] + inc - v;
+    __syncthreads();
+    return r;
+}
+
+__global__ void __launch_bounds__(kScanBlock) scan_reduce_kernel(const uint32_t *__restrict__ in, int64_t len,
+                                                                 uint32_t *__restrict__ partial)
+{
+    const int64_t base = (int64_t)blockIdx.x * kScanTile;
+    uint32_t s = 0;
+    for (int i = threadIdx.x; i < kScanTile; i += kScanBlock) {
+        const int64_t k = base + i;
+        if (k < len)
+            s += in[k];
+    }
+    __shared__ uint32_t tot;
+    (void)block_exclusive_scan<kScanBlock>(s, &tot);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        partial[blockIdx.x] = tot;
+}
+
+// One block: exclusive scan of the per-block sums in place; grand total to *total.
+__global__ void __launch_bounds__(1024) scan_partials_kernel(uint32_t *__restrict__ partial, int64_t nblocks,
+                                                             uint32_t *__restrict__ total)
+{
+    __shared__ uint32_t chunk_total;
+    uint32_t carry = 0;
+    for (int64_t base = 0; base < nblocks; base += 1024) {
+        const int64_t k = base + threadIdx.x;
+        const uint32_t v = k < nblocks ? partial[k] : 0u;
+        const uint32_t ex = block_exclusive_scan<1024>(v, &chunk_total);
+        if (k < nblocks)
+            partial[k] = carry + ex;
+        __syncthreads();
+        carry += chunk_total;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        *total = carry;
+}
+
+__global__ void __launch_bounds__(kScanBlock) scan_final_kernel(const uint32_t *__restrict__ in, int64_t len,
+                                                                const uint32_t *__restrict__ partial,
+                                                                uint32_t *__restrict__ out)
+{
+    const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+    uint32_t v[kScanItems];
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        const int64_t k = base + i;
+        v[i] = k < len ? in[k] : 0u;
+        s += v[i];
+    }
+    __shared__ uint32_t tot;
+    uint32_t run = block_exclusive_scan<kScanBlock>(s, &tot) + partial[blockIdx.x];
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        const int64_t k = base + i;
+        if (k < len)
+            out[k] = run;
+        run += v[i];
+    }
+}
+
+__global__ void fill_u32_kernel(uint32_t *__restrict__ p, int64_t count, uint32_t value)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = value;
+}
+
+// out[0..len] = exclusive prefix sum of in[0..len), out[len] = total.
+// scratch must hold ceil(len / kScanTile) words.
+hipError_t exclusive_scan(const uint32_t *in, int64_t len, uint32_t *out, uint32_t *scratch, hipStream_t s)
+{
+    const int64_t nb = (len + kScanTile - 1) / kScanTile;
+    if (nb == 0) {
+        hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, s, out, (int64_t)1, 0u);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(scan_reduce_kernel, dim3((unsigned)nb), dim3(kScanBlock), 0, s, in, len, scratch);
+    hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(1024), 0, s, scratch, nb, out + len);
+    hipLaunchKernelGGL(scan_final_kernel, dim3((unsigned)nb), dim3(kScanBlock), 0, s, in, len, scratch, out);
+    return hipGetLastError();
+}
+
+// Fill order[0 .. 64 * rows) with kEmpty, rows read from the device.
+__global__ void fill_order_kernel(uint32_t *__restrict__ order, const uint32_t *__restrict__ rows)
+{
+    const int64_t count = (int64_t)(*rows) * kWave;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+        order[i] = kEmpty;
+}
+
+template <int DIM>
+__global__ void __launch_bounds__(256) bin_count_kernel(Fields f, float nf, float dx, float last_base, RangesF r,
+                                                         int ntx, uint32_t *__restrict__ cell_count,
+                                                         uint32_t *__restrict__ key_out,
+                                                         uint32_t *__restrict__ rank_out,
+                                                         uint32_t *__restrict__ status)
+{
+    constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < f.n; p += (int64_t)gridDim.x * blockDim.x) {
+        bool dom = true;
+        int base[DIM];
+#pragma unroll
+        for (int e = 0; e < DIM; ++e) {
+            Axis ax;
+            dom = axis_stencil(f.x[e * f.n + p], nf, dx, last_base, ax) && dom;
+            base[e] = ax.base;
+        }
+        bool rng = fabsf(f.m[p]) <= r.max_mass;
+#pragma unroll
+        for (int e = 0; e < DIM; ++e)
+            rng = rng && fabsf(f.v[e * f.n + p]) <= r.max_speed;
+        if (f.C) {
+#pragma unroll
+            for (int k = 0; k < DIM * DIM; ++k)
+                rng = rng && fabsf(f.C[k * f.n + p]) <= r.max_affine;
+        }
+        rng = rng && dom;
+        wave_count(!dom, &status[0]);
+        wave_count(dom && !rng, &status[1]);
+        uint32_t key = kEmpty, rank = 0;
+        if (rng) {
+            uint32_t t = 0, l = 0;
+#pragma unroll
+            for (int e = DIM - 1; e >= 0; --e) {
+                t = t * (uint32_t)ntx + (uint32_t)(base[e] / kTile);
+                l = l * kTile + (uint32_t)(base[e] % kTile);
+            }
+            key = t * per_tile + l;
+            rank = atomicAdd(&cell_count[key], 1u);
+        }
+        key_out[p] = key;
+        rank_out[p] = rank;
+    }
+}
+
+template <int DIM>
+__global__ void __launch_bounds__(256) tile_layout_kernel(const uint32_t *__restrict__ cell_start, int64_t n_tiles,
+                                                           uint32_t *__restrict__ tile_rows,
+                                                           uint32_t *__restrict__ tile_items)
+{
+    constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n_tiles; t += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t count = cell_start[(t + 1) * per_tile] - cell_start[t * per_tile];
+        const uint32_t rows = (count + kWave - 1) / kWave;
+        tile_rows[t] = rows;
+        tile_items[t] = (rows + kRowsPerItem - 1) / kRowsPerItem;
+    }
+}
+
+__global__ void __launch_bounds__(256) items_kernel(const uint32_t *__restrict__ tile_items,
+                                                     const uint32_t *__restrict__ item_start, int64_t n_tiles,
+                                                     int64_t max_items, uint32_t *__restrict__ items)
+{
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n_tiles; t += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t k = tile_items[t], s0 = item_start[t];
+        for (uint32_t c = 0; c < k; ++c) {
+            items[s0 + c] = (uint32_t)t;
+            items[max_items + s0 + c] = c * kRowsPerItem;
+        }
+    }
+}
+
+__global__ void meta_kernel(const uint32_t *__restrict__ item_start, const uint32_t *__restrict__ tile_row_start,
+                            const uint32_t *__restrict__ cell_start, int64_t n_tiles, int64_t n_cells,
+                            uint32_t *__restrict__ meta)
+{
+    meta[0] = item_start[n_tiles];
+    meta[1] = tile_row_start[n_tiles];
+    meta[2] = cell_start[n_cells];
+    meta[3] = 0u;
+}
+
+template <int DIM>
+__global__ void __launch_bounds__(256) bin_scatter_kernel(Fields f, const uint32_t *__restrict__ key_in,
+                                                           const uint32_t *__restrict__ rank_in,
+                                                           const uint32_t *__restrict__ cell_start,
+                                                           const uint32_t *__restrict__ tile_row_start,
+                                                           uint32_t *__restrict__ order, float *__restrict__ sorted)
+{
+    constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < f.n; p += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t key = key_in[p];
+        if (key == kEmpty)
+            continue;
+        const uint32_t tile = key / per_tile;
+        const uint32_t first = cell_start[(int64_t)tile * per_tile];
+        const uint32_t count = cell_start[(int64_t)(tile + 1) * per_tile] - first;
+        const uint32_t rows = (count + kWave - 1) / kWave;
+        const uint32_t s = cell_start[key] - first + rank_in[p];
+        const int64_t slot = (int64_t)tile_row_start[tile] * kWave + (int64_t)(s % rows) * kWave + s / rows;
+        order[slot] = (uint32_t)p;
+        // one record of kRec floats per slot: x, v, C, m, zero padding
+        float rec[rec_floats<DIM>()];
+        int fi = 0;
+#pragma unroll
+        for (int e = 0; e < DIM; ++e)
+            rec[fi++] = f.x[e * f.n + p];
+#pragma unroll
+        for (int e = 0; e < DIM; ++e)
+            rec[fi++] = f.v[e * f.n + p];
+#pragma unroll
+        for (int k = 0; k < DIM * DIM; ++k)
+            rec[fi++] = f.C ? f.C[k * f.n + p] : 0.0f;
+        rec[fi++] = f.m[p];
+#pragma unroll
+        for (; fi < rec_floats<DIM>(); ++fi)
+            rec[fi] = 0.0f;
+        float4 *dst = reinterpret_cast<float4 *>(sorted + slot * rec_floats<DIM>());
+#pragma unroll
+        for (int q = 0; q < rec_floats<DIM>() / 4; ++q)
+            dst[q] = make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
+    }
+}
+
+int blocks_for(int64_t work, int block)
+{
+    const int64_t want = (work + block - 1) / block;
+    const int64_t cap = (int64_t)device_cu_count() * 32;
+    return (int)(want < 1 ? 1 : (want > cap ? cap : want));
+}
+
+}  // namespace
+
+hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView &b, uint32_t *status, hipStream_t s)
+{
+    const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3);
+    const int ntx = n / kTile;
+    uint32_t *tile_rows = b.tile_tmp, *tile_items = b.tile_tmp + b.n_tiles;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks_for(b.n_cells, 256)), dim3(256), 0, s, b.cell_count, b.n_cells,
+                       0u);
+    if (dim == 3)
+        hipLaunchKernelGGL(bin_count_kernel<3>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, nf, dx, last, r, ntx,
+                           b.cell_count, b.key, b.rank, status);
+    else
+        hipLaunchKernelGGL(bin_count_kernel<2>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, nf, dx, last, r, ntx,
+                           b.cell_count, b.key, b.rank, status);
+    hipError_t e = exclusive_scan(b.cell_count, b.n_cells, b.cell_start, b.scan_tmp, s);
+    if (e != hipSuccess)
+        return e;
+    if (dim == 3)
+        hipLaunchKernelGGL(tile_layout_kernel<3>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, b.cell_start,
+                           b.n_tiles, tile_rows, tile_items);
+    else
+        hipLaunchKernelGGL(tile_layout_kernel<2>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, b.cell_start,
+                           b.n_tiles, tile_rows, tile_items);
+    if ((e = exclusive_scan(tile_rows, b.n_tiles, b.tile_row_start, b.scan_tmp, s)) != hipSuccess)
+        return e;
+    if ((e = exclusive_scan(tile_items, b.n_tiles, b.item_start, b.scan_tmp, s)) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(items_kernel, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_items, b.item_start,
+                       b.n_tiles, b.max_items, b.items);
+    hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(1), 0, s, b.item_start, b.tile_row_start, b.cell_start, b.n_tiles,
+                       b.n_cells, b.meta);
+    hipLaunchKernelGGL(fill_order_kernel, dim3(blocks_for(b.max_slots, 256)), dim3(256), 0, s, b.order, b.meta + 1);
+    if (dim == 3)
+        hipLaunchKernelGGL(bin_scatter_kernel<3>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, b.key, b.rank,
+                           b.cell_start, b.tile_row_start, b.order, b.sorted);
+    else
+        hipLaunchKernelGGL(bin_scatter_kernel<2>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, b.key, b.rank,
+                           b.cell_start, b.tile_row_start, b.order, b.sorted);
+    return hipGetLastError();
+}
+
+}  // namespace mpmk

@@ -1,0 +1,104 @@
+// common.hpp -- device helpers and internal launch interfaces of libmpm.
+//
+// Everything here is gfx950 HIP.  The floating-point expressions below are
+// the library's fixed operation order for the transfer; the build uses
+// -ffp-contract=off and no fast-math, so each operation is one IEEE binary32
+// (or binary64) operation rounded to nearest even, exactly as written.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mpm.h"
+
+namespace mpmk {
+
+constexpr uint32_t kEmpty = 0xFFFFFFFFu;
+constexpr int kWave = 64;
+constexpr int kTile = 4;             // tile edge in cells
+constexpr int kRowsPerItem = 32;     // 64-slot rows per P2G work item (2048 particle slots)
+constexpr int kScanTileElems = 4096; // elements per block of the prefix-sum passes
+
+// One axis of a particle's quadratic B-spline stencil.  With g = x*n in node
+// units, the stencil starts at base = floor(g - 1/2) ("Mass Matrix Assembly on
+// Tensor Cores for Implicit PIC", shape functions: second-order support on
+// {j-1, j, j+1} below a half-cell fraction, {j, j+1, j+2} above); f = g - base
+// lies in [1/2, 3/2); the weights are the quadratic B-spline at distances f,
+// f-1 and f-2, and r[o] = (o - f) dx is node base+o's offset from the particle.
+struct Axis {
+    float w0, w1, w2;
+    float r0, r1, r2;
+    int base;
+};
+
+__device__ __forceinline__ bool axis_stencil(float x, float nf, float dx, float last_base, Axis &s)
+{
+    const float g = x * nf;
+    const float b = floorf(g - 0.5f);
+    const bool ok = (b >= 0.0f) && (b <= last_base);
+    const float f = g - b;
+    const float t0 = 1.5f - f;
+    const float t1 = f - 1.0f;
+    const float t2 = f - 0.5f;
+    s.w0 = 0.5f * (t0 * t0);
+    s.w1 = 0.75f - (t1 * t1);
+    s.w2 = 0.5f * (t2 * t2);
+    s.r0 = (0.0f - f) * dx;
+    s.r1 = (1.0f - f) * dx;
+    s.r2 = (2.0f - f) * dx;
+    s.base = ok ? (int)b : 0;
+    return ok;
+}
+
+// Declared ranges as float32 thresholds.  The host rounds each declared
+// maximum down to the largest float not above it, so |value| <= threshold in
+// float32 decides exactly what |value| <= maximum decides in real numbers.
+// Floats per particle record of the binned copy: x, v, C, m padded to a
+// multiple of four (64 bytes in 3D, 48 in 2D) so records load as float4s.
+template <int DIM>
+__host__ __device__ constexpr int rec_floats() { return ((2 * DIM + DIM * DIM + 1) + 3) / 4 * 4; }
+
+struct RangesF {
+    float max_mass, max_speed, max_affine;
+};
+
+// Count the lanes of the wavefront for which `pred` holds with one atomic.
+__device__ __forceinline__ void wave_count(bool pred, uint32_t *counter)
+{
+    const unsigned long long bits = __ballot(pred);
+    if (bits != 0ull && (threadIdx.x % kWave) == (unsigned)__ffsll((long long)bits) - 1u)
+        atomicAdd(counter, (uint32_t)__popcll(bits));
+}
+
+// ---------------------------------------------------------------------------
+// Internal launch interfaces (host side).  Arguments are validated by the
+// C ABI layer before these are called; each returns hipGetLastError().
+// ---------------------------------------------------------------------------
+struct Fields {           // component-major particle arrays of n particles
+    const float *x, *v, *C, *m;
+    int64_t n;
+};
+
+struct BinView {          // the workspace arrays, as typed device pointers
+    uint32_t *cell_start, *cell_count, *tile_row_start, *item_start, *items, *meta, *key, *rank, *order,
+        *tile_tmp, *scan_tmp;
+    float *sorted;
+    int64_t n_cells, n_tiles, max_items, max_slots, n_fields;
+};
+
+hipError_t launch_p2g_direct(int dim, int n, int frac_bits, const Fields &p, const uint32_t *order, RangesF r,
+                             int64_t *grid, uint32_t *status, hipStream_t s);
+hipError_t launch_p2g_tiled(int dim, int n, int frac_bits, const BinView &b, int64_t *grid, uint32_t *status,
+                            hipStream_t s);
+hipError_t launch_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32_t *vel,
+                                const uint32_t *order, int cells, int64_t *grid, uint32_t *status, hipStream_t s);
+hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView &b, uint32_t *status,
+                      hipStream_t s);
+hipError_t launch_grid_update(int dim, int n, int64_t *grid, float *vg, float dt, const float *gravity,
+                              int sticky, hipStream_t s);
+hipError_t launch_g2p(int dim, int n, const float *vg, float *x, float *v, float *C, int64_t np, float dt,
+                      uint32_t *status, hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace mpmk

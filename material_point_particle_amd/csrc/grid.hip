@@ -1,0 +1,161 @@
+// grid.hip -- grid update (consume-and-zero) and APIC grid-to-particle gather.
+//
+// "Implementation -- GPU Optimization & Reference Codebases": section 1 (the
+// four-phase step; G2P is a contention-free gather), section 2.1 and rule 4 of
+// section 5 (each accumulator has one reader here, so the grid update zeroes
+// it in place and no separate clear pass exists), rule 1 (the fixed-point sums
+// are converted once, in the grid update) and rule 7 (gravity is applied by the
+// solver to the grid velocity).
+#include "common.hpp"
+
+namespace mpmk {
+namespace {
+
+// One thread per node, x fastest, so every access is coalesced.  Per node:
+// v_d = (float)((double)P_d / (double)M) and v_d += dt*g_d where M != 0,
+// v = 0 where M == 0 and within `sticky` nodes of a face; then M = P = 0.
+template <int DIM>
+__global__ void __launch_bounds__(256) grid_update_kernel(int n, int64_t *__restrict__ grid, float *__restrict__ vg,
+                                                          float dt, float g0, float g1, float g2, int sticky)
+{
+    const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    const float gdt[3] = { dt * g0, dt * g1, dt * g2 };
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nodes; i += (int64_t)gridDim.x * blockDim.x) {
+        const int ix = (int)(i % n), iy = (int)((i / n) % n);
+        const int iz = DIM == 3 ? (int)(i / ((int64_t)n * n)) : 0;
+        bool wall = ix < sticky || ix >= n - sticky || iy < sticky || iy >= n - sticky;
+        if (DIM == 3)
+            wall = wall || iz < sticky || iz >= n - sticky;
+        const int64_t M = grid[i];
+#pragma unroll
+        for (int d = 0; d < DIM; ++d) {
+            const int64_t P = grid[(1 + d) * nodes + i];
+            float v = 0.0f;
+            if (M != 0) {
+                v = (float)((double)P / (double)M);
+                v = v + gdt[d];
+            }
+            vg[d * nodes + i] = wall ? 0.0f : v;
+            grid[(1 + d) * nodes + i] = 0;
+        }
+        grid[i] = 0;
+    }
+}
+
+// One thread per particle.  Over the stencil in lexicographic node order (x
+// offset outermost), with w = (wx[a]*wy[b])*wz[c]: wv_d = w*vg_d,
+// v_d += wv_d, B_de += wv_d*r_e; then C = B*(4 n^2), x += dt*v, clamp.
+template <int DIM>
+__global__ void __launch_bounds__(256) g2p_kernel(int n, float nf, float dx, float last_base,
+                                                  const float *__restrict__ vg, float *__restrict__ x,
+                                                  float *__restrict__ v, float *__restrict__ C, int64_t np, float dt,
+                                                  float lo, float hi, float cscale, uint32_t *__restrict__ status)
+{
+    const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
+        Axis ax[DIM];
+        bool ok = true;
+#pragma unroll
+        for (int e = 0; e < DIM; ++e)
+            ok = axis_stencil(x[e * np + p], nf, dx, last_base, ax[e]) && ok;
+        wave_count(!ok, &status[0]);
+        if (!ok)
+            continue;
+        float vn[DIM];
+        float B[DIM][DIM];
+#pragma unroll
+        for (int d = 0; d < DIM; ++d) {
+            vn[d] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < DIM; ++e)
+                B[d][e] = 0.0f;
+        }
+        const float wx[3] = { ax[0].w0, ax[0].w1, ax[0].w2 }, rx[3] = { ax[0].r0, ax[0].r1, ax[0].r2 };
+        const float wy[3] = { ax[1].w0, ax[1].w1, ax[1].w2 }, ry[3] = { ax[1].r0, ax[1].r1, ax[1].r2 };
+        float wz[3] = { 1.0f, 0.0f, 0.0f }, rz[3] = { 0.0f, 0.0f, 0.0f };
+        int bz = 0;
+        if constexpr (DIM == 3) {
+            wz[0] = ax[2].w0; wz[1] = ax[2].w1; wz[2] = ax[2].w2;
+            rz[0] = ax[2].r0; rz[1] = ax[2].r1; rz[2] = ax[2].r2;
+            bz = ax[2].base;
+        }
+        const int nc = DIM == 3 ? 3 : 1;
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+            for (int b = 0; b < 3; ++b)
+#pragma unroll
+                for (int c = 0; c < nc; ++c) {
+                    float w = wx[a] * wy[b];
+                    if constexpr (DIM == 3)
+                        w = w * wz[c];
+                    const int64_t node = DIM == 3
+                        ? ((int64_t)(bz + c) * n + (ax[1].base + b)) * n + (ax[0].base + a)
+                        : (int64_t)(ax[1].base + b) * n + (ax[0].base + a);
+                    const float off[3] = { rx[a], ry[b], rz[c] };
+#pragma unroll
+                    for (int d = 0; d < DIM; ++d) {
+                        const float wv = w * vg[d * nodes + node];
+                        vn[d] = vn[d] + wv;
+#pragma unroll
+                        for (int e = 0; e < DIM; ++e)
+                            B[d][e] = B[d][e] + wv * off[e];
+                    }
+                }
+        bool clamped = false;
+#pragma unroll
+        for (int d = 0; d < DIM; ++d) {
+#pragma unroll
+            for (int e = 0; e < DIM; ++e)
+                C[(int64_t)(d * DIM + e) * np + p] = B[d][e] * cscale;
+            v[d * np + p] = vn[d];
+            const float xn = x[d * np + p] + dt * vn[d];
+            const float xc = fminf(fmaxf(xn, lo), hi);
+            clamped = clamped || (xc != xn);
+            x[d * np + p] = xc;
+        }
+        wave_count(clamped, &status[2]);
+    }
+}
+
+int blocks_for(int64_t work, int block)
+{
+    const int64_t want = (work + block - 1) / block;
+    const int64_t cap = (int64_t)device_cu_count() * 32;
+    return (int)(want < 1 ? 1 : (want > cap ? cap : want));
+}
+
+}  // namespace
+
+hipError_t launch_grid_update(int dim, int n, int64_t *grid, float *vg, float dt, const float *gravity, int sticky,
+                              hipStream_t s)
+{
+    const int64_t nodes = dim == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    const float g0 = gravity[0], g1 = gravity[1], g2 = dim == 3 ? gravity[2] : 0.0f;
+    if (dim == 3)
+        hipLaunchKernelGGL(grid_update_kernel<3>, dim3(blocks_for(nodes, 256)), dim3(256), 0, s, n, grid, vg, dt, g0,
+                           g1, g2, sticky);
+    else
+        hipLaunchKernelGGL(grid_update_kernel<2>, dim3(blocks_for(nodes, 256)), dim3(256), 0, s, n, grid, vg, dt, g0,
+                           g1, g2, sticky);
+    return hipGetLastError();
+}
+
+hipError_t launch_g2p(int dim, int n, const float *vg, float *x, float *v, float *C, int64_t np, float dt,
+                      uint32_t *status, hipStream_t s)
+{
+    if (np == 0)
+        return hipSuccess;
+    const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3);
+    const float lo = dx, hi = (float)(n - 2) * dx;
+    const float cscale = 4.0f * (float)n * (float)n;
+    if (dim == 3)
+        hipLaunchKernelGGL(g2p_kernel<3>, dim3(blocks_for(np, 256)), dim3(256), 0, s, n, nf, dx, last, vg, x, v, C, np,
+                           dt, lo, hi, cscale, status);
+    else
+        hipLaunchKernelGGL(g2p_kernel<2>, dim3(blocks_for(np, 256)), dim3(256), 0, s, n, nf, dx, last, vg, x, v, C, np,
+                           dt, lo, hi, cscale, status);
+    return hipGetLastError();
+}
+
+}  // namespace mpmk

@@ -1,0 +1,460 @@
+// p2g.hip -- particle-to-grid scatter kernels for gfx950.
+//
+// The transfer ("Implementation -- GPU Optimization & Reference Codebases",
+// sections 1, 2.1 and 3.1): every particle deposits mass m w and APIC momentum
+// m w (v + C (x_i - x_p)) on the 3^dim nodes of its quadratic B-spline
+// stencil; each contribution is scaled by S = 2^k and rounded to an integer
+// once, so node sums are integer sums and the grid does not depend on the
+// order in which particles arrive.
+//
+// Fixed operation order per particle and node (a, b, c), float32:
+//   wmS = (((m*S) * wx[a]) * wy[b]) * wz[c]
+//   u_d = ((v_d + C_d0*rx[a]) + C_d1*ry[b]) + C_d2*rz[c]
+//   M += rint(wmS);  P_d += rint(wmS * u_d)
+// The kernels hoist the per-(a), per-(a,b) and per-(c) partial products; the
+// hoisted values are the same operations on the same operands, so every
+// contribution has the same bits as the per-node form.
+#include "common.hpp"
+
+namespace mpmk {
+namespace {
+
+template <int DIM>
+struct Particle {
+    float x[DIM], v[DIM], C[DIM * DIM], m;
+};
+
+template <int DIM>
+__device__ __forceinline__ bool in_ranges(const Particle<DIM> &p, RangesF r)
+{
+    bool ok = fabsf(p.m) <= r.max_mass;
+#pragma unroll
+    for (int d = 0; d < DIM; ++d)
+        ok = ok && (fabsf(p.v[d]) <= r.max_speed);
+#pragma unroll
+    for (int k = 0; k < DIM * DIM; ++k)
+        ok = ok && (fabsf(p.C[k]) <= r.max_affine);
+    return ok;
+}
+
+// Per-particle factors shared by the stencil's nodes.
+template <int DIM>
+struct Hoisted {
+    float mwxy[3][3];          // ((m*S)*wx[a])*wy[b]
+    float t2[DIM][3][3];       // (v_d + C_d0*rx[a]) + C_d1*ry[b]
+    float wz[3];
+    float cz[DIM][3];          // C_d2*rz[c]
+    int base[DIM];
+};
+
+template <int DIM>
+__device__ __forceinline__ bool hoist(const Particle<DIM> &p, float nf, float dx, float last_base, float S,
+                                      Hoisted<DIM> &h)
+{
+    Axis ax[DIM];
+    bool ok = true;
+#pragma unroll
+    for (int e = 0; e < DIM; ++e) {
+        ok = axis_stencil(p.x[e], nf, dx, last_base, ax[e]) && ok;
+        h.base[e] = ax[e].base;
+    }
+    const float mS = p.m * S;
+    const float wx[3] = { ax[0].w0, ax[0].w1, ax[0].w2 };
+    const float wy[3] = { ax[1].w0, ax[1].w1, ax[1].w2 };
+    const float rx[3] = { ax[0].r0, ax[0].r1, ax[0].r2 };
+    const float ry[3] = { ax[1].r0, ax[1].r1, ax[1].r2 };
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        const float mwx = mS * wx[a];
+#pragma unroll
+        for (int b = 0; b < 3; ++b)
+            h.mwxy[a][b] = mwx * wy[b];
+    }
+#pragma unroll
+    for (int d = 0; d < DIM; ++d) {
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            const float t1 = p.v[d] + p.C[d * DIM + 0] * rx[a];
+#pragma unroll
+            for (int b = 0; b < 3; ++b)
+                h.t2[d][a][b] = t1 + p.C[d * DIM + 1] * ry[b];
+        }
+    }
+    if constexpr (DIM == 3) {
+        const float rz[3] = { ax[2].r0, ax[2].r1, ax[2].r2 };
+        h.wz[0] = ax[2].w0;
+        h.wz[1] = ax[2].w1;
+        h.wz[2] = ax[2].w2;
+#pragma unroll
+        for (int d = 0; d < DIM; ++d)
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+                h.cz[d][c] = p.C[d * DIM + 2] * rz[c];
+    }
+    return ok;
+}
+
+template <int DIM>
+__device__ __forceinline__ void load_particle(const Fields &f, int64_t i, Particle<DIM> &p)
+{
+#pragma unroll
+    for (int e = 0; e < DIM; ++e) {
+        p.x[e] = f.x[e * f.n + i];
+        p.v[e] = f.v[e * f.n + i];
+    }
+#pragma unroll
+    for (int k = 0; k < DIM * DIM; ++k)
+        p.C[k] = f.C ? f.C[k * f.n + i] : 0.0f;
+    p.m = f.m[i];
+}
+
+__device__ __forceinline__ void atomic_add_i64(int64_t *addr, int64_t v)
+{
+    atomicAdd(reinterpret_cast<unsigned long long *>(addr), (unsigned long long)v);
+}
+
+// ---------------------------------------------------------------------------
+// Direct path: one thread per particle, 64-bit global atomics per
+// contribution.  No binning needed; the baseline the tiled path is measured
+// against and the path for unbinned particle sets.
+// ---------------------------------------------------------------------------
+template <int DIM>
+__global__ void __launch_bounds__(256) p2g_direct_kernel(Fields f, const uint32_t *__restrict__ order, int n,
+                                                          float nf, float dx, float last_base, float S, RangesF r,
+                                                          int64_t *__restrict__ grid, uint32_t *__restrict__ status)
+{
+    const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < f.n;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = order ? (int64_t)order[k] : k;
+        if (i >= f.n) {                  // an order entry that names no particle
+            atomicAdd(&status[3], 1u);
+            continue;
+        }
+        Particle<DIM> p;
+        load_particle<DIM>(f, i, p);
+        Hoisted<DIM> h;
+        const bool dom = hoist<DIM>(p, nf, dx, last_base, S, h);
+        const bool rng = dom && in_ranges<DIM>(p, r);
+        wave_count(!dom, &status[0]);
+        wave_count(dom && !rng, &status[1]);
+        if (!rng)
+            continue;
+        const int nc = DIM == 3 ? 3 : 1;
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+            for (int b = 0; b < 3; ++b)
+#pragma unroll
+                for (int c = 0; c < nc; ++c) {
+                    float wmS = h.mwxy[a][b];
+                    int64_t node;
+                    if constexpr (DIM == 3) {
+                        wmS = wmS * h.wz[c];
+                        node = ((int64_t)(h.base[2] + c) * n + (h.base[1] + b)) * n + (h.base[0] + a);
+                    } else {
+                        node = (int64_t)(h.base[1] + b) * n + (h.base[0] + a);
+                    }
+                    atomic_add_i64(&grid[node], (int64_t)rintf(wmS));
+#pragma unroll
+                    for (int d = 0; d < DIM; ++d) {
+                        float u = h.t2[d][a][b];
+                        if constexpr (DIM == 3)
+                            u = u + h.cz[d][c];
+                        atomic_add_i64(&grid[(1 + d) * nodes + node], (int64_t)rintf(wmS * u));
+                    }
+                }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled path.  The bins hold, per tile of 4^dim cells, the tile's particles
+// sorted by cell and laid out in rows of 64 slots "transposed": the particle
+// at cell-sorted position s of a tile with R rows sits in row s % R, lane
+// s / R.  A wavefront takes one work item (a range of rows of one tile), so
+// its 64 lanes hold particles that are R apart in cell order -- mostly in
+// different cells, hence mostly writing different node addresses at the same
+// instruction -- while each slot holds one particle record (x, v, C, m: 64
+// bytes in 3D), so a row is 4 KB of contiguous memory read by one wavefront.
+//
+// The tile's node block ((4+2)^dim nodes, 1+dim channels) lives in LDS as
+// float64.  Every contribution is an integer below 2^53 in magnitude and the
+// bounds check keeps every partial sum of one work item below 2^53, so each
+// LDS add is exact and the block holds the exact integer sums in any order.
+// After the item the block is flushed with one 64-bit global atomic per
+// non-zero node and channel ("Implementation -- GPU Optimization & Reference
+// Codebases", section 2.1: stage a tile of the grid on chip, accumulate
+// there, flush once).
+// ---------------------------------------------------------------------------
+template <int DIM>
+struct TileShape {
+    static constexpr int side = kTile + 2;
+    static constexpr int nodes = DIM == 3 ? side * side * side : side * side;
+    static constexpr int cells = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
+    static constexpr int ch = 1 + DIM;
+};
+
+struct TiledArgs {
+    const float *sorted;
+    const uint32_t *cell_start, *tile_row_start, *items, *meta;
+    uint32_t *cursor;
+    int64_t max_items;
+    int n, ntx;
+    float nf, dx, last_base, S;
+    int64_t *grid;
+    uint32_t *status;
+};
+
+__global__ void reset_cursor_kernel(uint32_t *cursor) { *cursor = 0u; }
+
+template <int DIM>
+__global__ void __launch_bounds__(kWave) p2g_tiled_kernel(TiledArgs a)
+{
+    using TS = TileShape<DIM>;
+    __shared__ double acc[TS::ch * TS::nodes];
+    __shared__ uint32_t item_sh;
+    const int lane = threadIdx.x;
+    const uint32_t n_items = a.meta[0];
+    const int64_t nodes = DIM == 3 ? (int64_t)a.n * a.n * a.n : (int64_t)a.n * a.n;
+
+    for (;;) {
+        if (lane == 0)
+            item_sh = atomicAdd(a.cursor, 1u);
+        __syncthreads();
+        const uint32_t item = item_sh;
+        __syncthreads();
+        if (item >= n_items)
+            break;
+        const uint32_t tile = a.items[item];
+        const uint32_t row0 = a.items[a.max_items + item];
+        const uint32_t first = a.cell_start[(int64_t)tile * TS::cells];
+        const uint32_t count = a.cell_start[(int64_t)(tile + 1) * TS::cells] - first;
+        const uint32_t rows = (count + kWave - 1) / kWave;
+        const uint32_t row1 = min(rows, row0 + (uint32_t)kRowsPerItem);
+        const int64_t slot0 = (int64_t)a.tile_row_start[tile] * kWave;
+        int torg[3] = { 0, 0, 0 };
+        {
+            uint32_t t = tile;
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                torg[e] = (int)(t % (uint32_t)a.ntx) * kTile;
+                t /= (uint32_t)a.ntx;
+            }
+        }
+        for (int i = lane; i < TS::ch * TS::nodes; i += kWave)
+            acc[i] = 0.0;
+        __syncthreads();
+
+        for (uint32_t j = row0; j < row1; ++j) {
+            const uint32_t s = (uint32_t)lane * rows + j;     // cell-sorted position of this lane's particle
+            if (s >= count)
+                continue;
+            const int64_t slot = slot0 + (int64_t)j * kWave + lane;
+            Particle<DIM> p;
+            {
+                constexpr int R = rec_floats<DIM>();
+                const float4 *src = reinterpret_cast<const float4 *>(a.sorted + slot * R);
+                float rec[R];
+#pragma unroll
+                for (int q = 0; q < R / 4; ++q) {
+                    const float4 t = src[q];
+                    rec[4 * q] = t.x;
+                    rec[4 * q + 1] = t.y;
+                    rec[4 * q + 2] = t.z;
+                    rec[4 * q + 3] = t.w;
+                }
+                int fi = 0;
+#pragma unroll
+                for (int e = 0; e < DIM; ++e)
+                    p.x[e] = rec[fi++];
+#pragma unroll
+                for (int e = 0; e < DIM; ++e)
+                    p.v[e] = rec[fi++];
+#pragma unroll
+                for (int k = 0; k < DIM * DIM; ++k)
+                    p.C[k] = rec[fi++];
+                p.m = rec[fi];
+            }
+            Hoisted<DIM> h;
+            hoist<DIM>(p, a.nf, a.dx, a.last_base, a.S, h);   // binned particles are in the domain
+            bool inside = true;
+#pragma unroll
+            for (int e = 0; e < DIM; ++e)
+                inside = inside && (unsigned)(h.base[e] - torg[e]) < (unsigned)kTile;
+            if (!inside) {               // a record that does not belong to this tile: never expected
+                atomicAdd(&a.status[3], 1u);
+                continue;
+            }
+            int lb;
+            if constexpr (DIM == 3)
+                lb = ((h.base[2] - torg[2]) * TS::side + (h.base[1] - torg[1])) * TS::side + (h.base[0] - torg[0]);
+            else
+                lb = (h.base[1] - torg[1]) * TS::side + (h.base[0] - torg[0]);
+            const int nc = DIM == 3 ? 3 : 1;
+#pragma unroll
+            for (int aa = 0; aa < 3; ++aa)
+#pragma unroll
+                for (int b = 0; b < 3; ++b)
+#pragma unroll
+                    for (int c = 0; c < nc; ++c) {
+                        const int off = DIM == 3 ? (c * TS::side + b) * TS::side + aa : b * TS::side + aa;
+                        float wmS = h.mwxy[aa][b];
+                        if constexpr (DIM == 3)
+                            wmS = wmS * h.wz[c];
+                        atomicAdd(&acc[lb + off], (double)rintf(wmS));
+#pragma unroll
+                        for (int d = 0; d < DIM; ++d) {
+                            float u = h.t2[d][aa][b];
+                            if constexpr (DIM == 3)
+                                u = u + h.cz[d][c];
+                            atomicAdd(&acc[(1 + d) * TS::nodes + lb + off], (double)rintf(wmS * u));
+                        }
+                    }
+        }
+        __syncthreads();
+        for (int i = lane; i < TS::ch * TS::nodes; i += kWave) {
+            const double val = acc[i];
+            if (val == 0.0)
+                continue;
+            const int ch = i / TS::nodes;
+            int rem = i - ch * TS::nodes;
+            int gx, gy, gz = 0;
+            gx = torg[0] + rem % TS::side;
+            rem /= TS::side;
+            gy = torg[1] + rem % TS::side;
+            if constexpr (DIM == 3)
+                gz = torg[2] + rem / TS::side;
+            if (gx >= a.n || gy >= a.n || gz >= a.n)
+                continue;
+            const int64_t node = DIM == 3 ? ((int64_t)gz * a.n + gy) * a.n + gx : (int64_t)gy * a.n + gx;
+            atomic_add_i64(&a.grid[ch * nodes + node], (int64_t)val);
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Integer-split cloud-in-cell ("particle to grid transfer in checked integer
+// arithmetic"): for q in {m, m*vx, m*vy}, far = round(q*fx / 2^16) with ties
+// to even, near = q - far; each part is split along y the same way.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t round_shift16_even(int64_t t)
+{
+    const int64_t fl = t >> 16;            // floor(t / 65536): arithmetic shift
+    const int64_t r = t & 0xFFFF;          // t - 65536*fl, in [0, 65536)
+    return fl + ((r > 0x8000) | ((r == 0x8000) & (fl & 1)));
+}
+
+__global__ void __launch_bounds__(256) p2g_cic_split_kernel(int64_t n, const int32_t *__restrict__ X,
+                                                             const int32_t *__restrict__ m,
+                                                             const int32_t *__restrict__ vel,
+                                                             const uint32_t *__restrict__ order, int cells,
+                                                             int64_t *__restrict__ grid, uint32_t *__restrict__ status)
+{
+    const int64_t nn = cells + 1;
+    const int64_t span = (int64_t)cells << 16;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p = order ? (int64_t)order[k] : k;
+        if (p >= n) {                    // an order entry that names no particle
+            atomicAdd(&status[3], 1u);
+            continue;
+        }
+        const int64_t px = X[p], py = X[n + p];
+        const bool ok = px >= 0 && px < span && py >= 0 && py < span;
+        wave_count(!ok, &status[0]);
+        if (!ok)
+            continue;
+        const int64_t cx = px >> 16, cy = py >> 16;
+        const int64_t fx = px & 0xFFFF, fy = py & 0xFFFF;
+        const int64_t q[3] = { (int64_t)m[p], (int64_t)m[p] * vel[p], (int64_t)m[p] * vel[n + p] };
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            const int64_t qx1 = round_shift16_even(q[c] * fx);
+            const int64_t qx0 = q[c] - qx1;
+            const int64_t q01 = round_shift16_even(qx0 * fy);
+            const int64_t q11 = round_shift16_even(qx1 * fy);
+            int64_t *g = grid + c * nn * nn;
+            atomic_add_i64(&g[cy * nn + cx], qx0 - q01);
+            atomic_add_i64(&g[(cy + 1) * nn + cx], q01);
+            atomic_add_i64(&g[cy * nn + cx + 1], qx1 - q11);
+            atomic_add_i64(&g[(cy + 1) * nn + cx + 1], q11);
+        }
+    }
+}
+
+int grid_blocks(int64_t work, int block)
+{
+    const int64_t want = (work + block - 1) / block;
+    const int64_t cap = (int64_t)device_cu_count() * 32;
+    return (int)(want < 1 ? 1 : (want > cap ? cap : want));
+}
+
+}  // namespace
+
+hipError_t launch_p2g_direct(int dim, int n, int frac_bits, const Fields &p, const uint32_t *order, RangesF r,
+                             int64_t *grid, uint32_t *status, hipStream_t s)
+{
+    if (p.n == 0)
+        return hipSuccess;
+    const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3), S = ldexpf(1.0f, frac_bits);
+    const int blocks = grid_blocks(p.n, 256);
+    if (dim == 3)
+        hipLaunchKernelGGL(p2g_direct_kernel<3>, dim3(blocks), dim3(256), 0, s, p, order, n, nf, dx, last, S, r,
+                           grid, status);
+    else
+        hipLaunchKernelGGL(p2g_direct_kernel<2>, dim3(blocks), dim3(256), 0, s, p, order, n, nf, dx, last, S, r,
+                           grid, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_p2g_tiled(int dim, int n, int frac_bits, const BinView &b, int64_t *grid, uint32_t *status,
+                            hipStream_t s)
+{
+    TiledArgs a;
+    a.sorted = b.sorted;
+    a.cell_start = b.cell_start;
+    a.tile_row_start = b.tile_row_start;
+    a.items = b.items;
+    a.meta = b.meta;
+    a.cursor = b.meta + 3;
+    a.max_items = b.max_items;
+    a.n = n;
+    a.ntx = n / kTile;
+    a.nf = (float)n;
+    a.dx = 1.0f / (float)n;
+    a.last_base = (float)(n - 3);
+    a.S = ldexpf(1.0f, frac_bits);
+    a.grid = grid;
+    a.status = status;
+    hipLaunchKernelGGL(reset_cursor_kernel, dim3(1), dim3(1), 0, s, a.cursor);
+    int per_cu = 0;
+    hipError_t e;
+    if (dim == 3)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, p2g_tiled_kernel<3>, kWave, 0);
+    else
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, p2g_tiled_kernel<2>, kWave, 0);
+    if (e != hipSuccess)
+        return e;
+    int64_t blocks = (int64_t)device_cu_count() * (per_cu > 0 ? per_cu : 1);
+    if (blocks > b.max_items)
+        blocks = b.max_items;
+    if (blocks < 1)
+        blocks = 1;
+    if (dim == 3)
+        hipLaunchKernelGGL(p2g_tiled_kernel<3>, dim3((unsigned)blocks), dim3(kWave), 0, s, a);
+    else
+        hipLaunchKernelGGL(p2g_tiled_kernel<2>, dim3((unsigned)blocks), dim3(kWave), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32_t *vel,
+                                const uint32_t *order, int cells, int64_t *grid, uint32_t *status, hipStream_t s)
+{
+    if (n == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(p2g_cic_split_kernel, dim3(grid_blocks(n, 256)), dim3(256), 0, s, n, X, m, vel, order, cells,
+                       grid, status);
+    return hipGetLastError();
+}
+
+}  // namespace mpmk

@@ -1,0 +1,75 @@
+"""Device-memory driver around the C ABI: owns torch-allocated buffers and
+calls the library's entry points on the current torch stream.
+
+Every step of the transfer runs in libmpm's HIP kernels; this module only
+allocates memory, copies host arrays to the device and passes pointers.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class DeviceParticles:
+    """Component-major float32 particle arrays on the device."""
+
+    def __init__(self, host: dict, device="cuda"):
+        self.x = to_device(host["x"], device)
+        self.v = to_device(host["v"], device)
+        self.C = to_device(host["C"], device)
+        self.m = to_device(host["m"], device)
+        self.n = int(self.m.shape[0])
+
+    def desc(self) -> L.mpm_particles:
+        return L.particles(self.n, self.x, self.v, self.C, self.m)
+
+    def host(self) -> dict:
+        return {k: getattr(self, k).cpu().numpy() for k in ("x", "v", "C", "m")}
+
+
+class Transfer:
+    """One grid (dim, n, 2^frac_bits) with its binning workspace, int64
+    accumulators, velocity grid and status counters."""
+
+    def __init__(self, dim: int, n: int, frac_bits: int, ranges, n_particles: int, device="cuda"):
+        self.dim, self.n, self.frac_bits = dim, n, frac_bits
+        self.desc = L.grid_desc(dim, n, frac_bits)
+        self.ranges = L.ranges(*ranges)
+        self.n_particles = n_particles
+        self.log2_bound = L.mpm_check_bounds(self.desc, n_particles, self.ranges)
+        self.layout = L.mpm_workspace_layout(self.desc, n_particles)
+        nbytes = self.layout.total_bytes
+        self.ws = torch.empty((nbytes + 7) // 8, dtype=torch.int64, device=device)
+        self.grid = torch.zeros((1 + dim,) + (n,) * dim, dtype=torch.int64, device=device)
+        self.vg = torch.zeros((dim,) + (n,) * dim, dtype=torch.float32, device=device)
+        self.status = torch.zeros(4, dtype=torch.int32, device=device)
+
+    # -- steps -------------------------------------------------------------
+    def bin(self, parts: DeviceParticles) -> None:
+        L.mpm_bin_particles(self.desc, parts.desc(), self.ranges, self.ws, self.status)
+
+    def p2g(self, parts: DeviceParticles, binned: bool = True, grid: torch.Tensor | None = None) -> torch.Tensor:
+        g = self.grid if grid is None else grid
+        L.mpm_p2g(self.desc, parts.desc(), self.ranges, self.ws if binned else None, g, self.status)
+        return g
+
+    def grid_update(self, dt: float, gravity, sticky: int) -> torch.Tensor:
+        L.mpm_grid_update(self.desc, self.grid, self.vg, dt, gravity, sticky)
+        return self.vg
+
+    def g2p(self, parts: DeviceParticles, dt: float) -> None:
+        L.mpm_g2p(self.desc, self.vg, parts.desc(), dt, self.status)
+
+    # -- workspace views (for tests and reports) ----------------------------
+    def ws_u32(self, field: str, count: int) -> torch.Tensor:
+        off = getattr(self.layout, field)
+        return self.ws.view(torch.int32)[off // 4: off // 4 + count]
+
+    def meta(self) -> np.ndarray:
+        return self.ws_u32("meta", 16).cpu().numpy().view(np.uint32)

@@ -1,0 +1,117 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point
+include/mpm.h declares, and its host-side logic (bounds line, workspace
+layout, argument validation) behaves as documented.  No kernel is launched:
+every call here returns before touching the device."""
+import ctypes as ct
+import math
+import os
+import re
+
+import pytest
+
+import material_point_particle_amd as M
+from material_point_particle_amd import _lib as L
+from mpm_inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_entry_points():
+    text = open(os.path.join(ROOT, "include", "mpm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mpm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    names = declared_entry_points()
+    assert set(names) == set(L.EXPORTS), names
+    lib = M.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+        assert ct.cast(getattr(lib, name), ct.c_void_p).value
+
+
+def test_version_and_errors():
+    assert "gfx950" in M.mpm_version()
+    for code in (0, -1, -2, -3, -4, -6):
+        assert M.mpm_strerror(code)
+    assert "unknown" in M.mpm_strerror(12345)
+
+
+@pytest.mark.parametrize("name", ["pile_2d", "dam_3d_128", "blobs_3d_256", "dam_3d_256"])
+def test_bounds_accept_the_workloads_and_agree_with_the_oracle(oracle_lib, name):
+    w = WORKLOADS[name]
+    r = (w.max_mass, w.max_speed, w.max_affine)
+    lb = M.mpm_check_bounds(M.grid_desc(w.dim, w.n, w.frac_bits), w.n_particles, M.ranges(*r))
+    assert lb < 63
+    assert math.isclose(lb, oracle_lib.p2g_log2_bound(w.dim, w.n, w.frac_bits, w.n_particles, r), abs_tol=1e-3)
+
+
+def test_bounds_refuse_overflowing_ranges():
+    with pytest.raises(M.MpmError) as e:
+        M.mpm_check_bounds(M.grid_desc(3, 256, 40), 1 << 24, M.ranges(2.0, 8.0, 0.5))
+    assert e.value.code == L.MPM_ERR_OVERFLOW
+    # one work item of 2048 particles must stay below 2^53 on chip
+    with pytest.raises(M.MpmError):
+        M.mpm_check_bounds(M.grid_desc(3, 64, 50), 1, M.ranges(1.0, 1.0, 0.0))
+
+
+def test_descriptor_validation():
+    r = M.ranges(1.0, 1.0, 1.0)
+    for bad in [(4, 64, 32), (3, 100, 32), (3, 4, 32), (3, 1024, 32), (2, 64, 61), (2, 64, -1)]:
+        with pytest.raises(M.MpmError) as e:
+            M.mpm_check_bounds(M.grid_desc(*bad), 10, r)
+        assert e.value.code == L.MPM_ERR_INVALID
+    with pytest.raises(M.MpmError):
+        M.mpm_check_bounds(M.grid_desc(3, 64, 32, tile=8), 10, r)
+    with pytest.raises(M.MpmError):
+        M.mpm_check_bounds(M.grid_desc(3, 64, 32), 10, M.ranges(float("nan"), 1.0, 1.0))
+
+
+def test_workspace_layout_is_disjoint_and_aligned():
+    for dim, n, N in [(2, 64, 3500), (3, 128, 1 << 20), (3, 256, 1 << 24), (3, 8, 0), (2, 8, 1)]:
+        d = M.grid_desc(dim, n, 20)
+        lay = M.mpm_workspace_layout(d, N)
+        assert M.mpm_workspace_bytes(d, N) == lay.total_bytes
+        assert lay.n_cells == n ** dim and lay.n_tiles == (n // 4) ** dim
+        assert lay.n_fields == {2: 12, 3: 16}[dim]     # x, v, C, m padded to a multiple of 4 floats
+        assert lay.max_slots % 64 == 0 and lay.max_slots >= N
+        spans = sorted([
+            (lay.cell_start, 4 * (lay.n_cells + 1)), (lay.cell_count, 4 * lay.n_cells),
+            (lay.tile_row_start, 4 * (lay.n_tiles + 1)), (lay.item_start, 4 * (lay.n_tiles + 1)),
+            (lay.items, 8 * lay.max_items), (lay.meta, 64), (lay.key, 4 * max(N, 1)), (lay.rank, 4 * max(N, 1)),
+            (lay.order, 4 * lay.max_slots), (lay.sorted, 4 * lay.n_fields * lay.max_slots),
+            (lay.tile_tmp, 8 * lay.n_tiles)])
+        for (a, la), (b, _) in zip(spans, spans[1:]):
+            assert a % 256 == 0 and a + la <= b
+        assert spans[-1][0] + spans[-1][1] <= lay.total_bytes
+
+
+def test_entry_points_reject_bad_arguments_before_any_launch():
+    lib = M.lib()
+    d = M.grid_desc(3, 64, 32)
+    r = M.ranges(1.0, 1.0, 1.0)
+    p = L.mpm_particles(10, None, None, None, None)
+    status = ct.c_void_p(256)
+    grid = ct.c_void_p(4096)
+    assert lib.mpm_p2g(ct.byref(d), ct.byref(p), ct.byref(r), None, grid, status, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_p2g(None, ct.byref(p), ct.byref(r), None, grid, status, None) == L.MPM_ERR_INVALID
+    misaligned = ct.c_void_p(4099)
+    p2 = L.mpm_particles(10, 4096, 4096, 4096, 4096)
+    assert lib.mpm_p2g(ct.byref(d), ct.byref(p2), ct.byref(r), None, misaligned, status, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_bin_particles(ct.byref(d), ct.byref(p2), ct.byref(r), ct.c_void_p(4096), 16, status,
+                                 None) == L.MPM_ERR_WORKSPACE
+    assert lib.mpm_bin_particles(ct.byref(d), ct.byref(p2), ct.byref(r), ct.c_void_p(4100), 1 << 30, status,
+                                 None) == L.MPM_ERR_INVALID
+    big = L.mpm_ranges(1e30, 1e30, 1e30)
+    assert lib.mpm_p2g(ct.byref(d), ct.byref(p2), ct.byref(big), None, grid, status, None) == L.MPM_ERR_OVERFLOW
+    assert lib.mpm_p2g_cic_split(256, None, None, None, None, 8, 1000, 1000, grid, status, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_p2g_cic_split(1 << 40, 4096, 4096, 4096, None, 8, 1 << 20, 1 << 20, grid, status,
+                                 None) == L.MPM_ERR_INVALID
+    assert lib.mpm_p2g_cic_split(1 << 30, 4096, 4096, 4096, None, 8, 1 << 20, 1 << 20, grid, status,
+                                 None) == L.MPM_ERR_OVERFLOW
+    g = (ct.c_float * 3)(0, -9.8, 0)
+    assert lib.mpm_grid_update(ct.byref(d), grid, ct.c_void_p(4096), 1e-4, g, 100, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_update(ct.byref(d), grid, ct.c_void_p(4096), 1e-4, None, 2, None) == L.MPM_ERR_INVALID
+    p3 = L.mpm_particles(10, 4096, 4096, None, 4096)
+    assert lib.mpm_g2p(ct.byref(d), ct.c_void_p(4096), ct.byref(p3), 1e-4, status, None) == L.MPM_ERR_INVALID

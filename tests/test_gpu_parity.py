@@ -1,0 +1,398 @@
+"""GPU parity: libmpm's HIP kernels, called through the C ABI, against the CPU
+oracle on the same seeded inputs.  Integer and fixed-point grids must match
+bit for bit; the grid must also be identical for every particle order and on
+repeated runs."""
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+from mpm_inputs import WORKLOADS, build, scaled
+from mpm_inputs import generators as G
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print("[gpu-test]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def mpm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import material_point_particle_amd as M
+    M.lib()
+    return M
+
+
+def ranges_of(w):
+    return (w.max_mass, w.max_speed, w.max_affine)
+
+
+def u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def gpu_p2g(mpm, w, host, binned, order=None, repeats=1):
+    from material_point_particle_amd.transfer import DeviceParticles, Transfer
+    if order is not None:
+        host = {k: np.ascontiguousarray(v[..., order]) for k, v in host.items()}
+    parts = DeviceParticles(host)
+    tr = Transfer(w.dim, w.n, w.frac_bits, ranges_of(w), parts.n)
+    grids = []
+    for _ in range(repeats):
+        tr.grid.zero_()
+        tr.status.zero_()
+        if binned:
+            tr.bin(parts)
+        tr.p2g(parts, binned=binned)
+        torch.cuda.synchronize()
+        grids.append(tr.grid.cpu().numpy())
+    return grids, u32(tr.status), tr
+
+
+def assert_same(a, b, what):
+    if not np.array_equal(a, b):
+        diff = np.argwhere(a != b)
+        i = tuple(diff[0])
+        raise AssertionError(f"{what}: {len(diff)} entries differ; first at {i}: gpu {a[i]} oracle {b[i]}")
+
+
+# ------------------------------------------------------------ integer split
+
+def test_cic_split_bit_exact_in_every_order(mpm, oracle_lib):
+    w = WORKLOADS["cic_split_2d"]
+    d = build(w)
+    ref, ref_status = oracle_lib.p2g_cic_split(d["X"], d["m"], d["vel"], w.n)
+    X, m, vel = (torch.from_numpy(d[k]).cuda() for k in ("X", "m", "vel"))
+    N = w.n_particles
+    orders = [None] + [G.affine_order(N, a, 13) for a in range(1, 256, 2)]
+    orders += [np.arange(N)[::-1].copy()] + [G.permutation(w.seed ^ 0x5F5F, s, N) for s in range(3)]
+    say("cic_split orders", len(orders))
+    grid = torch.zeros((3, 9, 9), dtype=torch.int64, device="cuda")
+    status = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for o in orders:
+        grid.zero_()
+        status.zero_()
+        ot = None if o is None else torch.from_numpy(o.astype(np.int32)).cuda()
+        mpm.mpm_p2g_cic_split(X, m, vel, ot, w.n, int(w.max_mass), int(w.max_speed), grid, status)
+        torch.cuda.synchronize()
+        assert_same(grid.cpu().numpy(), ref, "cic grid")
+        assert u32(status).tolist() == ref_status.tolist()
+
+
+def test_cic_split_edge_cases(mpm, oracle_lib):
+    w = WORKLOADS["cic_split_2d"]
+    d = build(w)
+    X = d["X"].copy()
+    X[0, 3] = -1
+    X[1, 4] = 8 * 65536
+    X[0, 5] = 8 * 65536 - 1                 # last sub-cell position: kept
+    X[:, 6] = [3 * 65536 + 32768, 5 * 65536 + 32768]   # ties in both axes
+    ref, ref_status = oracle_lib.p2g_cic_split(X, d["m"], d["vel"], w.n)
+    grid = torch.zeros((3, 9, 9), dtype=torch.int64, device="cuda")
+    status = torch.zeros(4, dtype=torch.int32, device="cuda")
+    say("cic_split edge cases")
+    mpm.mpm_p2g_cic_split(torch.from_numpy(X).cuda(), torch.from_numpy(d["m"]).cuda(),
+                          torch.from_numpy(d["vel"]).cuda(), None, w.n, 1000, 1000, grid, status)
+    torch.cuda.synchronize()
+    assert_same(grid.cpu().numpy(), ref, "cic edge grid")
+    assert u32(status).tolist() == ref_status.tolist() == [2, 0, 0, 0]
+    # empty particle set: no launch, grid untouched
+    grid.zero_()
+    e32 = torch.zeros((2, 0), dtype=torch.int32, device="cuda")
+    mpm.mpm_p2g_cic_split(e32, torch.zeros(0, dtype=torch.int32, device="cuda"), e32, None, w.n, 1000, 1000, grid,
+                          status)
+    torch.cuda.synchronize()
+    assert int(grid.abs().sum()) == 0
+
+
+# ------------------------------------------------------------ quadratic P2G
+
+CASES = [("pile_2d", None), ("dam_3d_128", 1 << 16), ("blobs_3d_256", 1 << 18)]
+
+
+@pytest.mark.parametrize("name,count", CASES)
+@pytest.mark.parametrize("binned", [False, True])
+def test_p2g_bit_exact(mpm, oracle_lib, name, count, binned):
+    w = WORKLOADS[name] if count is None else scaled(WORKLOADS[name], count)
+    host = build(w)
+    say("p2g", w.name, "binned" if binned else "direct", w.n_particles)
+    ref, ref_status = oracle_lib.p2g_quadratic(w.dim, w.n, w.frac_bits, host, ranges_of(w))
+    grids, status, _ = gpu_p2g(mpm, w, host, binned, repeats=2)
+    for g in grids:
+        assert_same(g, ref, f"{w.name} grid")
+    assert status.tolist() == ref_status.tolist()
+
+
+@pytest.mark.parametrize("name,count", CASES)
+def test_p2g_identical_in_every_particle_order(mpm, name, count):
+    w = WORKLOADS[name] if count is None else scaled(WORKLOADS[name], count)
+    host = build(w)
+    N = w.n_particles
+    say("order invariance", w.name)
+    base, _, _ = gpu_p2g(mpm, w, host, True)
+    for order in [np.arange(N)[::-1].copy()] + [G.permutation(w.seed ^ 0x5F5F, s, N) for s in range(3)]:
+        for binned in (True, False):
+            g, _, _ = gpu_p2g(mpm, w, host, binned, order=order, repeats=2)
+            for gi in g:
+                assert_same(gi, base[0], f"{w.name} shuffled")
+
+
+def test_p2g_skips_match_oracle(mpm, oracle_lib):
+    w = WORKLOADS["pile_2d"]
+    host = build(w)
+    q = {k: v.copy() for k, v in host.items()}
+    q["x"][0, 5] = 0.0
+    q["x"][1, 6] = np.nan
+    q["x"][0, 7] = (w.n - 2.0) / w.n
+    q["x"][1, 11] = 1.5 / w.n                     # base 1
+    q["x"][0, 12] = 0.5 / w.n                     # base exactly 0: kept
+    q["v"][1, 8] = 100.0
+    q["C"][3, 9] = -5.0
+    q["m"][10] = np.inf
+    ref, ref_status = oracle_lib.p2g_quadratic(w.dim, w.n, w.frac_bits, q, ranges_of(w))
+    assert ref_status.tolist() == [2, 3, 0, 0]
+    for binned in (False, True):
+        say("skips", "binned" if binned else "direct")
+        g, status, _ = gpu_p2g(mpm, w, q, binned)
+        assert_same(g[0], ref, "grid with skipped particles")
+        assert status.tolist() == ref_status.tolist()
+
+
+def _cloud_in_cells(dim, n, cells_and_counts, seed):
+    """Particles placed uniformly inside given base cells (cell -> count), with
+    random velocity and affine matrix."""
+    xs = []
+    for k, (cell, cnt) in enumerate(cells_and_counts):
+        u = G.uniform01(seed, 100 + k, dim * cnt).reshape(dim, cnt)
+        g = np.array(cell, dtype=np.float64)[:, None] + 0.5 + u * 0.999   # base = cell
+        xs.append(g / n)
+    x = np.concatenate(xs, axis=1)
+    N = x.shape[1]
+    f = G.particle_fields(seed, N, dim, (0.5, 2.0), 1.0, 0.5)
+    return {"x": np.ascontiguousarray(x.astype(np.float32)), **f}
+
+
+@pytest.mark.parametrize("layout", ["ragged_tiles", "one_dense_cell", "tile_corners"])
+def test_p2g_ragged_and_dense_tiles(mpm, oracle_lib, layout):
+    dim, n, k = 3, 32, 32
+    if layout == "ragged_tiles":
+        # tiles with 1, 63, 64, 65, 2047, 2048, 2049 and 4097 particles (rows and work-item boundaries)
+        spec = [((1, 1, 1), 1), ((5, 1, 1), 63), ((9, 1, 1), 64), ((13, 2, 3), 65), ((1, 5, 1), 2047),
+                ((5, 5, 5), 2048), ((9, 9, 9), 2049), ((13, 13, 13), 4097)]
+    elif layout == "one_dense_cell":
+        spec = [((17, 17, 17), 9000)]
+    else:
+        # the first and last valid base cells on every axis, and cells on tile edges
+        spec = [((0, 0, 0), 7), ((n - 3, n - 3, n - 3), 9), ((3, 4, 7), 33), ((4, 3, 8), 31), ((n - 3, 0, 11), 5)]
+    host = _cloud_in_cells(dim, n, spec, 0xED6E)
+    w = WORKLOADS["dam_3d_128"]
+    w = scaled(w, host["m"].shape[0], n=n)
+    from dataclasses import replace
+    w = replace(w, frac_bits=k, max_mass=2.0, max_speed=8.0, max_affine=4.0)
+    ref, ref_status = oracle_lib.p2g_quadratic(dim, n, k, host, ranges_of(w))
+    assert ref_status.tolist() == [0, 0, 0, 0]
+    for binned in (True, False):
+        say("ragged", layout, "binned" if binned else "direct")
+        g, status, _ = gpu_p2g(mpm, w, host, binned)
+        assert_same(g[0], ref, layout)
+        assert status.tolist() == [0, 0, 0, 0]
+
+
+def test_p2g_empty_and_single_particle(mpm, oracle_lib):
+    from dataclasses import replace
+    w = replace(WORKLOADS["dam_3d_128"], n=16, n_particles=0, name="empty")
+    host = {"x": np.zeros((3, 0), np.float32), "v": np.zeros((3, 0), np.float32),
+            "C": np.zeros((9, 0), np.float32), "m": np.zeros(0, np.float32)}
+    for binned in (False, True):
+        say("empty", binned)
+        g, status, _ = gpu_p2g(mpm, w, host, binned)
+        assert int(np.abs(g[0]).sum()) == 0 and status.tolist() == [0, 0, 0, 0]
+    one = {"x": np.array([[0.3], [0.41], [0.77]], np.float32), "v": np.array([[0.1], [-0.2], [0.3]], np.float32),
+           "C": np.arange(9, dtype=np.float32).reshape(9, 1) * 0.01, "m": np.array([1.0], np.float32)}
+    w1 = replace(w, n_particles=1)
+    ref, _ = oracle_lib.p2g_quadratic(3, 16, w1.frac_bits, one, ranges_of(w1))
+    for binned in (False, True):
+        say("single", binned)
+        g, status, _ = gpu_p2g(mpm, w1, one, binned)
+        assert_same(g[0], ref, "single particle")
+
+
+# ------------------------------------------------------------------ binning
+
+@pytest.mark.parametrize("name,count", [("pile_2d", None), ("dam_3d_128", 1 << 16), ("blobs_3d_256", 1 << 18)])
+def test_binning_matches_oracle(mpm, oracle_lib, name, count):
+    w = WORKLOADS[name] if count is None else scaled(WORKLOADS[name], count)
+    host = build(w)
+    say("binning", w.name)
+    cnt, start, order = oracle_lib.bin_particles(w.dim, w.n, w.tile, host, ranges_of(w))
+    _, _, tr = gpu_p2g(mpm, w, host, True)
+    lay = tr.layout
+    gcount = u32(tr.ws_u32("cell_count", lay.n_cells))
+    gstart = u32(tr.ws_u32("cell_start", lay.n_cells + 1))
+    assert_same(gcount, cnt, "cell counts")
+    assert_same(gstart, start, "cell starts")
+    meta = tr.meta()
+    rows_total, items = int(meta[1]), int(meta[0])
+    assert int(meta[2]) == len(order)
+    trs = u32(tr.ws_u32("tile_row_start", lay.n_tiles + 1))
+    gorder = u32(tr.ws_u32("order", lay.max_slots))[: rows_total * 64]
+    per = 4 ** w.dim
+    tile_count = start[per::per].astype(np.int64) - start[:-1:per].astype(np.int64)
+    rows = (tile_count + 63) // 64
+    assert np.array_equal(np.diff(trs.astype(np.int64)), rows) and int(trs[-1]) == rows_total
+    assert items == int(np.sum((rows + 31) // 32))
+    # rebuild each tile's cell-sorted sequence from the transposed rows and
+    # compare cell by cell with the oracle's (as sets: arrival order is free)
+    seen = np.zeros(w.n_particles, np.int64)
+    for t in np.nonzero(tile_count)[0]:
+        R, P = int(rows[t]), int(tile_count[t])
+        block = gorder[int(trs[t]) * 64:(int(trs[t]) + R) * 64].reshape(R, 64)     # [row][lane]
+        seq = block.T.reshape(-1)[:P]                                               # s = lane*R + row
+        assert np.all(block.T.reshape(-1)[P:] == 0xFFFFFFFF)
+        c0 = t * per
+        for c in range(c0, c0 + per):
+            a, b = int(start[c]) - int(start[c0]), int(start[c + 1]) - int(start[c0])
+            assert np.array_equal(np.sort(seq[a:b]), np.sort(order[start[c]:start[c + 1]]))
+        seen[seq] += 1
+    assert np.all(seen[order] == 1) and seen.sum() == len(order)
+    # the binned copy holds each slot's particle
+    sorted_f = tr.ws.view(torch.float32)[lay.sorted // 4: lay.sorted // 4 + lay.n_fields * lay.max_slots]
+    sorted_f = sorted_f.view(lay.max_slots, lay.n_fields)[: rows_total * 64].cpu().numpy()
+    valid = gorder != 0xFFFFFFFF
+    src = np.concatenate([host["x"], host["v"], host["C"], host["m"][None]])
+    nf = src.shape[0]
+    assert np.array_equal(sorted_f[valid, :nf].T, src[:, gorder[valid]])
+
+
+# ------------------------------------------------------ grid update + gather
+
+def test_grid_update_and_g2p_bit_exact(mpm, oracle_lib):
+    from material_point_particle_amd.transfer import DeviceParticles, Transfer
+    w = scaled(WORKLOADS["dam_3d_256"], 1 << 16, n=64)
+    host = build(w)
+    ex = w.extra
+    grid, _ = oracle_lib.p2g_quadratic(w.dim, w.n, w.frac_bits, host, ranges_of(w))
+    tr = Transfer(w.dim, w.n, w.frac_bits, ranges_of(w), w.n_particles)
+    tr.grid.copy_(torch.from_numpy(grid))
+    say("grid update")
+    tr.grid_update(ex["dt"], ex["gravity"], ex["sticky"])
+    g_ref = grid.copy()
+    vg_ref = oracle_lib.grid_update(w.dim, w.n, g_ref, ex["dt"], ex["gravity"], ex["sticky"])
+    torch.cuda.synchronize()
+    assert_same(tr.vg.cpu().numpy(), vg_ref, "grid velocity")
+    assert int(tr.grid.abs().sum()) == 0
+    parts = DeviceParticles(host)
+    say("g2p")
+    tr.status.zero_()
+    tr.g2p(parts, ex["dt"])
+    ref = {k: v.copy() for k, v in host.items()}
+    st = oracle_lib.g2p(w.dim, w.n, vg_ref, ref, ex["dt"])
+    torch.cuda.synchronize()
+    got = parts.host()
+    for k in ("x", "v", "C"):
+        assert_same(got[k], ref[k], f"g2p {k}")
+    assert u32(tr.status).tolist() == st.tolist()
+
+
+def _oracle_substep(w, host, grid_shape):
+    """One oracle substep; returns (P2G grid, particle arrays after)."""
+    import oracle
+    ex = w.extra
+    grid, st = oracle.p2g_quadratic(w.dim, w.n, w.frac_bits, host, ranges_of(w))
+    g_after = grid.copy()
+    vg = oracle.grid_update(w.dim, w.n, g_after, ex["dt"], ex["gravity"], ex["sticky"])
+    out = {k: v.copy() for k, v in host.items()}
+    oracle.g2p(w.dim, w.n, vg, out, ex["dt"])
+    return grid, out
+
+
+def _run_substeps(mpm, w, host, checkpoints, binned=True):
+    """GPU substeps; at each checkpoint substep k (1-based) records the state
+    before the substep, the P2G grid of the substep and the state after."""
+    from material_point_particle_amd.transfer import DeviceParticles, Transfer
+    ex = w.extra
+    parts = DeviceParticles(host)
+    tr = Transfer(w.dim, w.n, w.frac_bits, ranges_of(w), parts.n)
+    rec = {}
+    for k in range(1, ex["substeps"] + 1):
+        before = parts.host() if k in checkpoints else None
+        if binned:
+            tr.bin(parts)
+        tr.p2g(parts, binned=binned)
+        if k in checkpoints:
+            torch.cuda.synchronize()
+            g = tr.grid.cpu().numpy()
+        tr.grid_update(ex["dt"], ex["gravity"], ex["sticky"])
+        tr.g2p(parts, ex["dt"])
+        if k in checkpoints:
+            torch.cuda.synchronize()
+            rec[k] = (before, g, parts.host())
+            say("substep", k)
+    return rec, u32(tr.status)
+
+
+def test_substeps_lockstep_with_oracle_small(mpm, oracle_lib):
+    """Dam-break recipe on 64^3 nodes, 2^16 particles, 100 substeps: the GPU
+    and the oracle each run their own trajectory; at every 10th substep the
+    P2G grid and the particle state must be identical."""
+    w = scaled(WORKLOADS["dam_3d_256"], 1 << 16, n=64)
+    host = build(w)
+    checkpoints = set(range(10, 101, 10))
+    say("lockstep small")
+    rec, _ = _run_substeps(mpm, w, host, checkpoints)
+    state = {k: v.copy() for k, v in host.items()}
+    for k in range(1, w.extra["substeps"] + 1):
+        grid, state = _oracle_substep(w, state, None)
+        if k in checkpoints:
+            _, g_gpu, after = rec[k]
+            assert_same(g_gpu, grid, f"substep {k} grid")
+            for key in ("x", "v", "C"):
+                assert_same(after[key], state[key], f"substep {k} {key}")
+
+
+@pytest.mark.timeout(900)
+def test_substeps_full_size_checked_every_ten(mpm, oracle_lib):
+    """The full 8M-particle, 256^3 dam-break loop: at substeps 10, 20, ..., 100
+    the oracle recomputes that substep from the GPU's state before it; the
+    P2G grid and the state after must be identical."""
+    w = WORKLOADS["dam_3d_256"]
+    host = build(w)
+    checkpoints = set(range(10, 101, 10))
+    say("lockstep full size")
+    rec, status = _run_substeps(mpm, w, host, checkpoints)
+    assert status.tolist()[:2] == [0, 0]
+
+    def check(k):
+        before, g_gpu, after = rec[k]
+        grid, out = _oracle_substep(w, before, None)
+        ok = np.array_equal(g_gpu, grid) and all(np.array_equal(after[key], out[key]) for key in ("x", "v", "C"))
+        return k, ok
+
+    with ThreadPoolExecutor(max_workers=10) as ex:
+        results = dict(ex.map(check, sorted(checkpoints)))
+    assert all(results.values()), results
+
+
+@pytest.mark.timeout(600)
+def test_full_size_blobs_bit_exact(mpm, oracle_lib):
+    """16M particles in 32 Gaussian blobs on 256^3 nodes at 2^28 -- the
+    benchmark's workload and launch configuration -- against the full oracle
+    grid, and identical after a shuffle of the particle arrays."""
+    w = WORKLOADS["blobs_3d_256"]
+    host = build(w)
+    say("full-size blobs: oracle")
+    ref, ref_status = oracle_lib.p2g_quadratic(w.dim, w.n, w.frac_bits, host, ranges_of(w))
+    say("full-size blobs: gpu")
+    grids, status, _ = gpu_p2g(mpm, w, host, True, repeats=2)
+    for g in grids:
+        assert_same(g, ref, "blobs full grid")
+    assert status.tolist() == ref_status.tolist()
+    say("full-size blobs: shuffled")
+    g2, _, _ = gpu_p2g(mpm, w, host, True, order=G.permutation(w.seed ^ 0x5F5F, 0, w.n_particles))
+    assert_same(g2[0], ref, "blobs shuffled")
