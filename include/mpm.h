@@ -91,12 +91,14 @@ typedef struct {
  * writes, so that callers and tests can read them.  Counts are the
  * capacities allocated, not what one call fills. */
 typedef struct {
-    size_t cell_start;      /* uint32 [n_cells + 1] exclusive prefix sum of per-cell counts    */
+    size_t cell_start;      /* uint32 [n_cells + 1] exclusive prefix sum of per-cell counts,
+                                        each rounded up to a multiple of 4 (record groups) */
     size_t cell_count;      /* uint32 [n_cells]     per-cell particle counts                    */
-    size_t tile_row_start;  /* uint32 [n_tiles + 1] first 64-slot row of each tile              */
+    size_t tile_row_start;  /* uint32 [n_tiles + 1] first 256-slot row of each tile             */
     size_t item_start;      /* uint32 [n_tiles + 1] first P2G work item of each tile            */
     size_t items;           /* uint32 [2][max_items] (tile, first row) of each work item        */
-    size_t meta;            /* uint32 [16]: [0] items, [1] rows, [2] binned particles, [3] work cursor */
+    size_t meta;            /* uint32 [16]: [0] items, [1] rows, [2] binned particles,
+                                        [3] P2G work cursor, [4] record slots incl. pads */
     size_t key;             /* uint32 [n] cell key of each particle (0xFFFFFFFF when skipped)   */
     size_t rank;            /* uint32 [n] arrival rank of each particle inside its cell         */
     size_t order;           /* uint32 [max_slots] slot -> particle index (0xFFFFFFFF: empty)    */
@@ -139,12 +141,16 @@ int mpm_workspace_layout(const mpm_grid_desc *grid, int64_t n_particles, mpm_ws_
  * steps 3-4: histogram, exclusive prefix sum, scatter; "Implementation --
  * GPU Optimization & Reference Codebases", section 2.1: sort + tile).  The
  * caller's arrays are not reordered (section 5 rule 2): the workspace
- * receives the cell histogram and prefix sum, per-tile 64-slot rows, the
- * P2G work items, a slot -> particle permutation and a binned copy of
- * x, v, C, m.  Particles whose stencil leaves the grid or whose attributes
- * leave the declared ranges are not binned and are counted in status[0] and
- * status[1].  Arrival order inside a cell is not deterministic; the P2G grid
- * built from the bins is (integer sums commute).
+ * receives the cell histogram and prefix sum, per-tile rows, the P2G work
+ * items, a slot -> particle permutation and a binned copy of x, v, C, m:
+ * 64-byte records (48 in 2D), each cell padded with zero-mass records to a
+ * multiple of 4, in groups of 4 same-cell records, one group per lane of a
+ * 256-slot row.  Particles whose stencil leaves the grid are not binned and
+ * are counted in status[0]; particles whose attributes leave the declared
+ * ranges are binned as zero-mass records (they contribute nothing, exactly
+ * as if skipped) and counted in status[1].  Arrival order inside a cell is
+ * not deterministic; the P2G grid built from the bins is (integer sums
+ * commute).
  * particles, status: device.  ws: device, ws_bytes >= mpm_workspace_bytes().
  * Errors: MPM_ERR_INVALID, MPM_ERR_WORKSPACE, MPM_ERR_OVERFLOW (bounds),
  * MPM_ERR_HIP. */

@@ -104,7 +104,10 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     const int64_t n_cells = pow_int(g->n, g->dim);
     const int64_t n_tiles = pow_int(g->n / kTile, g->dim);
     const int64_t busy = np < n_tiles ? (np > 0 ? np : 1) : n_tiles;       // tiles that can hold particles
-    const int64_t max_rows = (np + kWave - 1) / kWave + busy;
+    // every non-empty cell adds at most kGroup-1 pad records, every non-empty
+    // tile at most one partly filled row
+    const int64_t busy_cells = np < n_cells ? np : n_cells;
+    const int64_t max_rows = (np + (kGroup - 1) * busy_cells + kRowSlots - 1) / kRowSlots + busy;
     const int64_t max_items = (max_rows + kRowsPerItem - 1) / kRowsPerItem + busy;
     const int64_t n_fields = g->dim == 3 ? rec_floats<3>() : rec_floats<2>();
     const int64_t big = n_cells > n_tiles ? n_cells : n_tiles;
@@ -125,14 +128,14 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     o->meta = take(u4 * 16);
     o->key = take(u4 * (size_t)n1);
     o->rank = take(u4 * (size_t)n1);
-    o->order = take(u4 * (size_t)(max_rows * kWave));
-    o->sorted = take(sizeof(float) * (size_t)(n_fields * max_rows * kWave));
+    o->order = take(u4 * (size_t)(max_rows * kRowSlots));
+    o->sorted = take(sizeof(float) * (size_t)(n_fields * max_rows * kRowSlots));
     o->tile_tmp = take(u4 * 2 * (size_t)n_tiles);
     o->scan_tmp = take(u4 * (size_t)scan_blocks);
     o->n_cells = n_cells;
     o->n_tiles = n_tiles;
     o->max_items = max_items;
-    o->max_slots = max_rows * kWave;
+    o->max_slots = max_rows * kRowSlots;
     o->n_fields = n_fields;
     o->rows_per_item = kRowsPerItem;
     o->total_bytes = off;
@@ -209,8 +212,8 @@ int mpm_check_bounds(const mpm_grid_desc *grid, int64_t n_particles, const mpm_r
     if (log2_bound)
         *log2_bound = lb;
     // int64 node sums over all particles; exact float64 partial sums over one
-    // work item (at most kRowsPerItem * 64 particles) on chip.
-    if (!(lb < 62.999) || !(lq + log2((double)(kRowsPerItem * kWave)) < 53.0))
+    // work item (at most kRowsPerItem * kRowSlots particles) on chip.
+    if (!(lb < 62.999) || !(lq + log2((double)(kRowsPerItem * kRowSlots)) < 53.0))
         return MPM_ERR_OVERFLOW;
     return MPM_OK;
 }

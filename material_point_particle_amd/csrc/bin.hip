@@ -9,17 +9,21 @@
 //   1. count    one thread per particle: base cell -> tile-major cell key;
 //               atomic increment of the cell's counter returns the particle's
 //               arrival rank inside the cell.
-//   2. scan     exclusive prefix sum of the cell counters (three phases:
-//               per-block sums, one block scans the sums, per-block rescan).
-//   3. layout   per tile: rows of 64 slots needed, and P2G work items of up to
+//   2. scan     exclusive prefix sum of the cell counters, each rounded up to
+//               a multiple of kGroup (three phases: per-block sums, one block
+//               scans the sums, per-block rescan).
+//   3. layout   per tile: rows of kRowSlots record slots (one group of kGroup
+//               same-cell records per lane) and P2G work items of up to
 //               kRowsPerItem rows; both prefix-summed over tiles.
 //   4. items    per tile: the (tile, first row) of each of its work items.
-//   5. scatter  one thread per particle: its slot in the tile's transposed
-//               row layout; the slot -> particle index and a record of the
-//               particle's fields (x, v, C, m: 64 bytes in 3D) are written
-//               there, so each scattered write is one whole record.
+//   5. scatter  one thread per particle: its slot in the tile's grouped,
+//               transposed layout (group g of a tile with R rows sits in lane
+//               g / R of row g % R); the slot -> particle index and a record of
+//               the particle's fields (x, v, C, m: 64 bytes in 3D) are written
+//               there, so each scattered write is one whole record.  Cells are
+//               padded to whole groups with zero-mass records.
 // Arrival ranks depend on scheduling, so slot contents differ between runs;
-// every slot holds one particle of the right cell, which is all P2G needs.
+// every group holds kGroup records of one cell, which is all P2G needs.
 #include "common.hpp"
 
 namespace mpmk {
@@ -66,6 +70,15 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *t
     return r;
 }
 
+// The scans read each counter rounded up to a multiple of ROUND (1 or kGroup).
+template <int ROUND>
+__device__ __forceinline__ uint32_t scan_load(const uint32_t *in, int64_t k)
+{
+    const uint32_t v = in[k];
+    return ROUND == 1 ? v : (v + (ROUND - 1)) / ROUND * ROUND;
+}
+
+template <int ROUND>
 __global__ void __launch_bounds__(kScanBlock) scan_reduce_kernel(const uint32_t *__restrict__ in, int64_t len,
                                                                  uint32_t *__restrict__ partial)
 {
@@ -74,7 +87,7 @@ __global__ void __launch_bounds__(kScanBlock) scan_reduce_kernel(const uint32_t 
     for (int i = threadIdx.x; i < kScanTile; i += kScanBlock) {
         const int64_t k = base + i;
         if (k < len)
-            s += in[k];
+            s += scan_load<ROUND>(in, k);
     }
     __shared__ uint32_t tot;
     (void)block_exclusive_scan<kScanBlock>(s, &tot);
@@ -103,6 +116,7 @@ __global__ void __launch_bounds__(1024) scan_partials_kernel(uint32_t *__restric
         *total = carry;
 }
 
+template <int ROUND>
 __global__ void __launch_bounds__(kScanBlock) scan_final_kernel(const uint32_t *__restrict__ in, int64_t len,
                                                                 const uint32_t *__restrict__ partial,
                                                                 uint32_t *__restrict__ out)
@@ -113,7 +127,7 @@ __global__ void __launch_bounds__(kScanBlock) scan_final_kernel(const uint32_t *
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
         const int64_t k = base + i;
-        v[i] = k < len ? in[k] : 0u;
+        v[i] = k < len ? scan_load<ROUND>(in, k) : 0u;
         s += v[i];
     }
     __shared__ uint32_t tot;
@@ -133,8 +147,9 @@ __global__ void fill_u32_kernel(uint32_t *__restrict__ p, int64_t count, uint32_
         p[i] = value;
 }
 
-// out[0..len] = exclusive prefix sum of in[0..len), out[len] = total.
-// scratch must hold ceil(len / kScanTile) words.
+// out[0..len] = exclusive prefix sum of in[0..len) (each value rounded up to a
+// multiple of ROUND), out[len] = total.  scratch holds ceil(len / kScanTile) words.
+template <int ROUND>
 hipError_t exclusive_scan(const uint32_t *in, int64_t len, uint32_t *out, uint32_t *scratch, hipStream_t s)
 {
     const int64_t nb = (len + kScanTile - 1) / kScanTile;
@@ -142,26 +157,29 @@ hipError_t exclusive_scan(const uint32_t *in, int64_t len, uint32_t *out, uint32
         hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, s, out, (int64_t)1, 0u);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(scan_reduce_kernel, dim3((unsigned)nb), dim3(kScanBlock), 0, s, in, len, scratch);
+    hipLaunchKernelGGL(scan_reduce_kernel<ROUND>, dim3((unsigned)nb), dim3(kScanBlock), 0, s, in, len, scratch);
     hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(1024), 0, s, scratch, nb, out + len);
-    hipLaunchKernelGGL(scan_final_kernel, dim3((unsigned)nb), dim3(kScanBlock), 0, s, in, len, scratch, out);
+    hipLaunchKernelGGL(scan_final_kernel<ROUND>, dim3((unsigned)nb), dim3(kScanBlock), 0, s, in, len, scratch, out);
     return hipGetLastError();
 }
 
-// Fill order[0 .. 64 * rows) with kEmpty, rows read from the device.
+// Fill order[0 .. kRowSlots * rows) with kEmpty, rows read from the device.
 __global__ void fill_order_kernel(uint32_t *__restrict__ order, const uint32_t *__restrict__ rows)
 {
-    const int64_t count = (int64_t)(*rows) * kWave;
+    const int64_t count = (int64_t)(*rows) * kRowSlots;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
         order[i] = kEmpty;
 }
 
+// Pass 1: cell key from the position only; particles whose stencil leaves the
+// grid are counted and not binned.  The attribute range check happens in the
+// scatter pass, which reads the attributes anyway.
 template <int DIM>
-__global__ void __launch_bounds__(256) bin_count_kernel(Fields f, float nf, float dx, float last_base, RangesF r,
-                                                         int ntx, uint32_t *__restrict__ cell_count,
+__global__ void __launch_bounds__(256) bin_count_kernel(Fields f, float nf, float dx, float last_base, int ntx,
+                                                         uint32_t *__restrict__ cell_count,
                                                          uint32_t *__restrict__ key_out,
                                                          uint32_t *__restrict__ rank_out,
-                                                         uint32_t *__restrict__ status)
+                                                         uint32_t *__restrict__ status, uint32_t *__restrict__ meta)
 {
     constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < f.n; p += (int64_t)gridDim.x * blockDim.x) {
@@ -173,20 +191,10 @@ __global__ void __launch_bounds__(256) bin_count_kernel(Fields f, float nf, floa
             dom = axis_stencil(f.x[e * f.n + p], nf, dx, last_base, ax) && dom;
             base[e] = ax.base;
         }
-        bool rng = fabsf(f.m[p]) <= r.max_mass;
-#pragma unroll
-        for (int e = 0; e < DIM; ++e)
-            rng = rng && fabsf(f.v[e * f.n + p]) <= r.max_speed;
-        if (f.C) {
-#pragma unroll
-            for (int k = 0; k < DIM * DIM; ++k)
-                rng = rng && fabsf(f.C[k * f.n + p]) <= r.max_affine;
-        }
-        rng = rng && dom;
         wave_count(!dom, &status[0]);
-        wave_count(dom && !rng, &status[1]);
+        wave_count(dom, &meta[2]);
         uint32_t key = kEmpty, rank = 0;
-        if (rng) {
+        if (dom) {
             uint32_t t = 0, l = 0;
 #pragma unroll
             for (int e = DIM - 1; e >= 0; --e) {
@@ -201,6 +209,8 @@ __global__ void __launch_bounds__(256) bin_count_kernel(Fields f, float nf, floa
     }
 }
 
+// Pass 3: per tile, rows of kRowSlots record slots (one group of kGroup
+// records per lane) and the number of P2G work items.
 template <int DIM>
 __global__ void __launch_bounds__(256) tile_layout_kernel(const uint32_t *__restrict__ cell_start, int64_t n_tiles,
                                                            uint32_t *__restrict__ tile_rows,
@@ -208,8 +218,8 @@ __global__ void __launch_bounds__(256) tile_layout_kernel(const uint32_t *__rest
 {
     constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n_tiles; t += (int64_t)gridDim.x * blockDim.x) {
-        const uint32_t count = cell_start[(t + 1) * per_tile] - cell_start[t * per_tile];
-        const uint32_t rows = (count + kWave - 1) / kWave;
+        const uint32_t padded = cell_start[(t + 1) * per_tile] - cell_start[t * per_tile];
+        const uint32_t rows = (padded + kRowSlots - 1) / kRowSlots;
         tile_rows[t] = rows;
         tile_items[t] = (rows + kRowsPerItem - 1) / kRowsPerItem;
     }
@@ -234,49 +244,97 @@ __global__ void meta_kernel(const uint32_t *__restrict__ item_start, const uint3
 {
     meta[0] = item_start[n_tiles];
     meta[1] = tile_row_start[n_tiles];
-    meta[2] = cell_start[n_cells];
     meta[3] = 0u;
+    meta[4] = cell_start[n_cells];
 }
 
+// Record slot of padded cell-sorted position s in a tile with `rows` rows:
+// group g = s / kGroup sits in lane g / rows of row g % rows, element s % kGroup.
+__device__ __forceinline__ int64_t slot_of(uint32_t row_start, uint32_t rows, uint32_t s)
+{
+    const uint32_t g = s / kGroup;
+    return ((int64_t)row_start + g % rows) * kRowSlots + (int64_t)(s % kGroup) * kWave + g / rows;
+}
+
+// Pass 5: place each binned particle's record.  The last arrival of a cell
+// whose count is not a multiple of kGroup also writes the cell's pad records:
+// its own position with zero mass, velocity and affine matrix, which the
+// transfer turns into exact zero contributions.  Particles outside the
+// declared ranges are counted and written the same way (they contribute
+// nothing, as if skipped).
 template <int DIM>
-__global__ void __launch_bounds__(256) bin_scatter_kernel(Fields f, const uint32_t *__restrict__ key_in,
+__global__ void __launch_bounds__(256) bin_scatter_kernel(Fields f, RangesF r, const uint32_t *__restrict__ key_in,
                                                            const uint32_t *__restrict__ rank_in,
+                                                           const uint32_t *__restrict__ cell_count,
                                                            const uint32_t *__restrict__ cell_start,
                                                            const uint32_t *__restrict__ tile_row_start,
-                                                           uint32_t *__restrict__ order, float *__restrict__ sorted)
+                                                           uint32_t *__restrict__ order, float *__restrict__ sorted,
+                                                           uint32_t *__restrict__ status)
 {
     constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
+    constexpr int R = rec_floats<DIM>();
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < f.n; p += (int64_t)gridDim.x * blockDim.x) {
         const uint32_t key = key_in[p];
-        if (key == kEmpty)
+        const bool binned = key != kEmpty;
+        float rec[R];
+        bool rng = false;
+        uint32_t tile = 0, first = 0, rows = 1, s = 0, rank = 0, count = 0;
+        if (binned) {
+            tile = key / per_tile;
+            first = cell_start[(int64_t)tile * per_tile];
+            rows = (cell_start[(int64_t)(tile + 1) * per_tile] - first + kRowSlots - 1) / kRowSlots;
+            rank = rank_in[p];
+            count = cell_count[key];
+            s = cell_start[key] - first + rank;
+            int fi = 0;
+#pragma unroll
+            for (int e = 0; e < DIM; ++e)
+                rec[fi++] = f.x[e * f.n + p];
+            rng = fabsf(f.m[p]) <= r.max_mass;
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                rec[fi] = f.v[e * f.n + p];
+                rng = rng && fabsf(rec[fi]) <= r.max_speed;
+                ++fi;
+            }
+#pragma unroll
+            for (int k = 0; k < DIM * DIM; ++k) {
+                rec[fi] = f.C ? f.C[k * f.n + p] : 0.0f;
+                rng = rng && fabsf(rec[fi]) <= r.max_affine;
+                ++fi;
+            }
+            rec[fi++] = f.m[p];
+#pragma unroll
+            for (; fi < R; ++fi)
+                rec[fi] = 0.0f;
+            if (!rng) {
+#pragma unroll
+                for (int k = DIM; k < R; ++k)
+                    rec[k] = 0.0f;
+            }
+        }
+        wave_count(binned && !rng, &status[1]);
+        if (!binned)
             continue;
-        const uint32_t tile = key / per_tile;
-        const uint32_t first = cell_start[(int64_t)tile * per_tile];
-        const uint32_t count = cell_start[(int64_t)(tile + 1) * per_tile] - first;
-        const uint32_t rows = (count + kWave - 1) / kWave;
-        const uint32_t s = cell_start[key] - first + rank_in[p];
-        const int64_t slot = (int64_t)tile_row_start[tile] * kWave + (int64_t)(s % rows) * kWave + s / rows;
+        const uint32_t row_start = tile_row_start[tile];
+        int64_t slot = slot_of(row_start, rows, s);
         order[slot] = (uint32_t)p;
-        // one record of kRec floats per slot: x, v, C, m, zero padding
-        float rec[rec_floats<DIM>()];
-        int fi = 0;
+        float4 *dst = reinterpret_cast<float4 *>(sorted + slot * R);
 #pragma unroll
-        for (int e = 0; e < DIM; ++e)
-            rec[fi++] = f.x[e * f.n + p];
-#pragma unroll
-        for (int e = 0; e < DIM; ++e)
-            rec[fi++] = f.v[e * f.n + p];
-#pragma unroll
-        for (int k = 0; k < DIM * DIM; ++k)
-            rec[fi++] = f.C ? f.C[k * f.n + p] : 0.0f;
-        rec[fi++] = f.m[p];
-#pragma unroll
-        for (; fi < rec_floats<DIM>(); ++fi)
-            rec[fi] = 0.0f;
-        float4 *dst = reinterpret_cast<float4 *>(sorted + slot * rec_floats<DIM>());
-#pragma unroll
-        for (int q = 0; q < rec_floats<DIM>() / 4; ++q)
+        for (int q = 0; q < R / 4; ++q)
             dst[q] = make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
+        if (rank + 1 == count && count % kGroup != 0) {
+#pragma unroll
+            for (int k = DIM; k < R; ++k)
+                rec[k] = 0.0f;
+            for (uint32_t pad = s + 1; pad < s + 1 + (kGroup - count % kGroup); ++pad) {
+                slot = slot_of(row_start, rows, pad);
+                dst = reinterpret_cast<float4 *>(sorted + slot * R);
+#pragma unroll
+                for (int q = 0; q < R / 4; ++q)
+                    dst[q] = make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
+            }
+        }
     }
 }
 
@@ -296,13 +354,14 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
     uint32_t *tile_rows = b.tile_tmp, *tile_items = b.tile_tmp + b.n_tiles;
     hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks_for(b.n_cells, 256)), dim3(256), 0, s, b.cell_count, b.n_cells,
                        0u);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, s, b.meta, (int64_t)16, 0u);
     if (dim == 3)
-        hipLaunchKernelGGL(bin_count_kernel<3>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, nf, dx, last, r, ntx,
-                           b.cell_count, b.key, b.rank, status);
+        hipLaunchKernelGGL(bin_count_kernel<3>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, nf, dx, last, ntx,
+                           b.cell_count, b.key, b.rank, status, b.meta);
     else
-        hipLaunchKernelGGL(bin_count_kernel<2>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, nf, dx, last, r, ntx,
-                           b.cell_count, b.key, b.rank, status);
-    hipError_t e = exclusive_scan(b.cell_count, b.n_cells, b.cell_start, b.scan_tmp, s);
+        hipLaunchKernelGGL(bin_count_kernel<2>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, nf, dx, last, ntx,
+                           b.cell_count, b.key, b.rank, status, b.meta);
+    hipError_t e = exclusive_scan<kGroup>(b.cell_count, b.n_cells, b.cell_start, b.scan_tmp, s);
     if (e != hipSuccess)
         return e;
     if (dim == 3)
@@ -311,9 +370,9 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
     else
         hipLaunchKernelGGL(tile_layout_kernel<2>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, b.cell_start,
                            b.n_tiles, tile_rows, tile_items);
-    if ((e = exclusive_scan(tile_rows, b.n_tiles, b.tile_row_start, b.scan_tmp, s)) != hipSuccess)
+    if ((e = exclusive_scan<1>(tile_rows, b.n_tiles, b.tile_row_start, b.scan_tmp, s)) != hipSuccess)
         return e;
-    if ((e = exclusive_scan(tile_items, b.n_tiles, b.item_start, b.scan_tmp, s)) != hipSuccess)
+    if ((e = exclusive_scan<1>(tile_items, b.n_tiles, b.item_start, b.scan_tmp, s)) != hipSuccess)
         return e;
     hipLaunchKernelGGL(items_kernel, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_items, b.item_start,
                        b.n_tiles, b.max_items, b.items);
@@ -321,11 +380,11 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
                        b.n_cells, b.meta);
     hipLaunchKernelGGL(fill_order_kernel, dim3(blocks_for(b.max_slots, 256)), dim3(256), 0, s, b.order, b.meta + 1);
     if (dim == 3)
-        hipLaunchKernelGGL(bin_scatter_kernel<3>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, b.key, b.rank,
-                           b.cell_start, b.tile_row_start, b.order, b.sorted);
+        hipLaunchKernelGGL(bin_scatter_kernel<3>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, r, b.key, b.rank,
+                           b.cell_count, b.cell_start, b.tile_row_start, b.order, b.sorted, status);
     else
-        hipLaunchKernelGGL(bin_scatter_kernel<2>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, b.key, b.rank,
-                           b.cell_start, b.tile_row_start, b.order, b.sorted);
+        hipLaunchKernelGGL(bin_scatter_kernel<2>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, r, b.key, b.rank,
+                           b.cell_count, b.cell_start, b.tile_row_start, b.order, b.sorted, status);
     return hipGetLastError();
 }
 

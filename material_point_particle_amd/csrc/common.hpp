@@ -16,7 +16,9 @@ namespace mpmk {
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
 constexpr int kWave = 64;
 constexpr int kTile = 4;             // tile edge in cells
-constexpr int kRowsPerItem = 32;     // 64-slot rows per P2G work item (2048 particle slots)
+constexpr int kGroup = 4;            // records per group: one cell's particles, four at a time
+constexpr int kRowSlots = kWave * kGroup;  // a row: one group per lane (256 record slots)
+constexpr int kRowsPerItem = 16;     // rows per P2G work item (4096 record slots)
 constexpr int kScanTileElems = 4096; // elements per block of the prefix-sum passes
 
 // One axis of a particle's quadratic B-spline stencil.  With g = x*n in node

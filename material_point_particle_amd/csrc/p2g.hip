@@ -169,22 +169,29 @@ __global__ void __launch_bounds__(256) p2g_direct_kernel(Fields f, const uint32_
 
 // ---------------------------------------------------------------------------
 // Tiled path.  The bins hold, per tile of 4^dim cells, the tile's particles
-// sorted by cell and laid out in rows of 64 slots "transposed": the particle
-// at cell-sorted position s of a tile with R rows sits in row s % R, lane
-// s / R.  A wavefront takes one work item (a range of rows of one tile), so
-// its 64 lanes hold particles that are R apart in cell order -- mostly in
-// different cells, hence mostly writing different node addresses at the same
-// instruction -- while each slot holds one particle record (x, v, C, m: 64
-// bytes in 3D), so a row is 4 KB of contiguous memory read by one wavefront.
+// sorted by cell, each cell padded with zero-mass records to whole groups of
+// kGroup records, and the groups laid out "transposed": group g of a tile with
+// R rows sits in lane g / R of row g % R, its kGroup records in four
+// consecutive 64-record sub-rows.  A wavefront takes one work item (a range of
+// rows of one tile): every lane holds kGroup particles of one cell, and the 64
+// lanes are R groups apart in cell order, so they are mostly in different
+// cells and write different node addresses at the same instruction.  Each
+// record is 64 bytes (x, v, C, m in 3D), so a sub-row is 4 KB of contiguous
+// memory read by one wavefront.
+//
+// Per lane and stencil node, the group's kGroup quantised contributions are
+// summed in float64 registers and added to the on-chip node block with one LDS
+// atomic, a quarter of the atomics of one add per particle (the implementation
+// page's section 2.1 pre-reduces same-node contributions before one atomic).
 //
 // The tile's node block ((4+2)^dim nodes, 1+dim channels) lives in LDS as
 // float64.  Every contribution is an integer below 2^53 in magnitude and the
 // bounds check keeps every partial sum of one work item below 2^53, so each
-// LDS add is exact and the block holds the exact integer sums in any order.
-// After the item the block is flushed with one 64-bit global atomic per
-// non-zero node and channel ("Implementation -- GPU Optimization & Reference
-// Codebases", section 2.1: stage a tile of the grid on chip, accumulate
-// there, flush once).
+// add is exact and the block holds the exact integer sums in any order.  After
+// the item the block is flushed with one 64-bit global atomic per non-zero
+// node and channel ("Implementation -- GPU Optimization & Reference
+// Codebases", section 2.1: stage a tile of the grid on chip, accumulate there,
+// flush once).
 // ---------------------------------------------------------------------------
 template <int DIM>
 struct TileShape {
@@ -193,6 +200,59 @@ struct TileShape {
     static constexpr int cells = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
     static constexpr int ch = 1 + DIM;
 };
+
+// Per-particle factors of the grouped kernel (the per-(a,b) products are
+// formed inside the node loop to keep kGroup particles' state in registers).
+template <int DIM>
+struct GroupHoist {
+    float mwx[3];              // (m*S)*wx[a]
+    float wy[3];
+    float wz[3];
+    float t1[DIM][3];          // v_d + C_d0*rx[a]
+    float cy[DIM][3];          // C_d1*ry[b]
+    float cz[DIM][3];          // C_d2*rz[c]
+    int base[DIM];
+};
+
+template <int DIM>
+__device__ __forceinline__ void group_hoist(const float *rec, float nf, float dx, float last_base, float S,
+                                            GroupHoist<DIM> &h)
+{
+    Axis ax[DIM];
+#pragma unroll
+    for (int e = 0; e < DIM; ++e) {
+        axis_stencil(rec[e], nf, dx, last_base, ax[e]);
+        h.base[e] = ax[e].base;
+    }
+    const float *v = rec + DIM, *C = rec + 2 * DIM, m = rec[2 * DIM + DIM * DIM];
+    const float mS = m * S;
+    const float wx[3] = { ax[0].w0, ax[0].w1, ax[0].w2 }, rx[3] = { ax[0].r0, ax[0].r1, ax[0].r2 };
+    const float ry[3] = { ax[1].r0, ax[1].r1, ax[1].r2 };
+    h.wy[0] = ax[1].w0;
+    h.wy[1] = ax[1].w1;
+    h.wy[2] = ax[1].w2;
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+        h.mwx[a] = mS * wx[a];
+#pragma unroll
+    for (int d = 0; d < DIM; ++d)
+#pragma unroll
+        for (int o = 0; o < 3; ++o) {
+            h.t1[d][o] = v[d] + C[d * DIM + 0] * rx[o];
+            h.cy[d][o] = C[d * DIM + 1] * ry[o];
+        }
+    if constexpr (DIM == 3) {
+        const float rz[3] = { ax[2].r0, ax[2].r1, ax[2].r2 };
+        h.wz[0] = ax[2].w0;
+        h.wz[1] = ax[2].w1;
+        h.wz[2] = ax[2].w2;
+#pragma unroll
+        for (int d = 0; d < DIM; ++d)
+#pragma unroll
+            for (int o = 0; o < 3; ++o)
+                h.cz[d][o] = C[d * DIM + 2] * rz[o];
+    }
+}
 
 struct TiledArgs {
     const float *sorted;
@@ -211,6 +271,8 @@ template <int DIM>
 __global__ void __launch_bounds__(kWave) p2g_tiled_kernel(TiledArgs a)
 {
     using TS = TileShape<DIM>;
+    constexpr int R = rec_floats<DIM>();
+    constexpr int G = kGroup;
     __shared__ double acc[TS::ch * TS::nodes];
     __shared__ uint32_t item_sh;
     const int lane = threadIdx.x;
@@ -228,10 +290,10 @@ __global__ void __launch_bounds__(kWave) p2g_tiled_kernel(TiledArgs a)
         const uint32_t tile = a.items[item];
         const uint32_t row0 = a.items[a.max_items + item];
         const uint32_t first = a.cell_start[(int64_t)tile * TS::cells];
-        const uint32_t count = a.cell_start[(int64_t)(tile + 1) * TS::cells] - first;
-        const uint32_t rows = (count + kWave - 1) / kWave;
+        const uint32_t groups = (a.cell_start[(int64_t)(tile + 1) * TS::cells] - first) / G;
+        const uint32_t rows = (groups + kWave - 1) / kWave;
         const uint32_t row1 = min(rows, row0 + (uint32_t)kRowsPerItem);
-        const int64_t slot0 = (int64_t)a.tile_row_start[tile] * kWave;
+        const int64_t row_base = (int64_t)a.tile_row_start[tile];
         int torg[3] = { 0, 0, 0 };
         {
             uint32_t t = tile;
@@ -246,14 +308,13 @@ __global__ void __launch_bounds__(kWave) p2g_tiled_kernel(TiledArgs a)
         __syncthreads();
 
         for (uint32_t j = row0; j < row1; ++j) {
-            const uint32_t s = (uint32_t)lane * rows + j;     // cell-sorted position of this lane's particle
-            if (s >= count)
+            if ((uint32_t)lane * rows + j >= groups)        // this lane's group index: lane * rows + j
                 continue;
-            const int64_t slot = slot0 + (int64_t)j * kWave + lane;
-            Particle<DIM> p;
-            {
-                constexpr int R = rec_floats<DIM>();
-                const float4 *src = reinterpret_cast<const float4 *>(a.sorted + slot * R);
+            const int64_t slot0 = (row_base + j) * kRowSlots + lane;
+            GroupHoist<DIM> h[G];
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
+                const float4 *src = reinterpret_cast<const float4 *>(a.sorted + (slot0 + k * kWave) * R);
                 float rec[R];
 #pragma unroll
                 for (int q = 0; q < R / 4; ++q) {
@@ -263,53 +324,66 @@ __global__ void __launch_bounds__(kWave) p2g_tiled_kernel(TiledArgs a)
                     rec[4 * q + 2] = t.z;
                     rec[4 * q + 3] = t.w;
                 }
-                int fi = 0;
-#pragma unroll
-                for (int e = 0; e < DIM; ++e)
-                    p.x[e] = rec[fi++];
-#pragma unroll
-                for (int e = 0; e < DIM; ++e)
-                    p.v[e] = rec[fi++];
-#pragma unroll
-                for (int k = 0; k < DIM * DIM; ++k)
-                    p.C[k] = rec[fi++];
-                p.m = rec[fi];
+                group_hoist<DIM>(rec, a.nf, a.dx, a.last_base, a.S, h[k]);
             }
-            Hoisted<DIM> h;
-            hoist<DIM>(p, a.nf, a.dx, a.last_base, a.S, h);   // binned particles are in the domain
-            bool inside = true;
+            // every record of the group is in one cell of this tile (binning's
+            // invariant); a group that breaks it is counted and skipped
+            bool ok = true;
 #pragma unroll
-            for (int e = 0; e < DIM; ++e)
-                inside = inside && (unsigned)(h.base[e] - torg[e]) < (unsigned)kTile;
-            if (!inside) {               // a record that does not belong to this tile: never expected
+            for (int e = 0; e < DIM; ++e) {
+                ok = ok && (unsigned)(h[0].base[e] - torg[e]) < (unsigned)kTile;
+#pragma unroll
+                for (int k = 1; k < G; ++k)
+                    ok = ok && h[k].base[e] == h[0].base[e];
+            }
+            if (!ok) {
                 atomicAdd(&a.status[3], 1u);
                 continue;
             }
             int lb;
             if constexpr (DIM == 3)
-                lb = ((h.base[2] - torg[2]) * TS::side + (h.base[1] - torg[1])) * TS::side + (h.base[0] - torg[0]);
+                lb = ((h[0].base[2] - torg[2]) * TS::side + (h[0].base[1] - torg[1])) * TS::side +
+                     (h[0].base[0] - torg[0]);
             else
-                lb = (h.base[1] - torg[1]) * TS::side + (h.base[0] - torg[0]);
+                lb = (h[0].base[1] - torg[1]) * TS::side + (h[0].base[0] - torg[0]);
             const int nc = DIM == 3 ? 3 : 1;
 #pragma unroll
             for (int aa = 0; aa < 3; ++aa)
 #pragma unroll
-                for (int b = 0; b < 3; ++b)
+                for (int b = 0; b < 3; ++b) {
+                    float mwxy[G], t2[G][DIM];
+#pragma unroll
+                    for (int k = 0; k < G; ++k) {
+                        mwxy[k] = h[k].mwx[aa] * h[k].wy[b];
+#pragma unroll
+                        for (int d = 0; d < DIM; ++d)
+                            t2[k][d] = h[k].t1[d][aa] + h[k].cy[d][b];
+                    }
 #pragma unroll
                     for (int c = 0; c < nc; ++c) {
                         const int off = DIM == 3 ? (c * TS::side + b) * TS::side + aa : b * TS::side + aa;
-                        float wmS = h.mwxy[aa][b];
-                        if constexpr (DIM == 3)
-                            wmS = wmS * h.wz[c];
-                        atomicAdd(&acc[lb + off], (double)rintf(wmS));
+                        float wmS[G];
+                        double sum;
+#pragma unroll
+                        for (int k = 0; k < G; ++k) {
+                            wmS[k] = DIM == 3 ? mwxy[k] * h[k].wz[c] : mwxy[k];
+                            const double q = (double)rintf(wmS[k]);
+                            sum = k == 0 ? q : sum + q;
+                        }
+                        atomicAdd(&acc[lb + off], sum);
 #pragma unroll
                         for (int d = 0; d < DIM; ++d) {
-                            float u = h.t2[d][aa][b];
-                            if constexpr (DIM == 3)
-                                u = u + h.cz[d][c];
-                            atomicAdd(&acc[(1 + d) * TS::nodes + lb + off], (double)rintf(wmS * u));
+                            double ps;
+#pragma unroll
+                            for (int k = 0; k < G; ++k) {
+                                const float u = DIM == 3 ? t2[k][d] + h[k].cz[d][c] : t2[k][d];
+                                const double q = (double)rintf(wmS[k] * u);
+                                ps = k == 0 ? q : ps + q;
+                            }
+                            atomicAdd(&acc[(1 + d) * TS::nodes + lb + off], ps);
                         }
                     }
+                }
         }
         __syncthreads();
         for (int i = lane; i < TS::ch * TS::nodes; i += kWave) {

@@ -236,38 +236,48 @@ def test_binning_matches_oracle(mpm, oracle_lib, name, count):
     gcount = u32(tr.ws_u32("cell_count", lay.n_cells))
     gstart = u32(tr.ws_u32("cell_start", lay.n_cells + 1))
     assert_same(gcount, cnt, "cell counts")
-    assert_same(gstart, start, "cell starts")
+    # the library's cell starts are the prefix sums of counts padded to whole groups of 4 records
+    padded = (cnt.astype(np.int64) + 3) // 4 * 4
+    assert_same(gstart.astype(np.int64), np.concatenate([[0], np.cumsum(padded)]), "padded cell starts")
     meta = tr.meta()
     rows_total, items = int(meta[1]), int(meta[0])
-    assert int(meta[2]) == len(order)
-    trs = u32(tr.ws_u32("tile_row_start", lay.n_tiles + 1))
-    gorder = u32(tr.ws_u32("order", lay.max_slots))[: rows_total * 64]
+    assert int(meta[2]) == len(order) and int(meta[4]) == int(padded.sum())
+    trs = u32(tr.ws_u32("tile_row_start", lay.n_tiles + 1)).astype(np.int64)
+    gorder = u32(tr.ws_u32("order", lay.max_slots))[: rows_total * 256]
     per = 4 ** w.dim
-    tile_count = start[per::per].astype(np.int64) - start[:-1:per].astype(np.int64)
-    rows = (tile_count + 63) // 64
-    assert np.array_equal(np.diff(trs.astype(np.int64)), rows) and int(trs[-1]) == rows_total
-    assert items == int(np.sum((rows + 31) // 32))
-    # rebuild each tile's cell-sorted sequence from the transposed rows and
-    # compare cell by cell with the oracle's (as sets: arrival order is free)
-    seen = np.zeros(w.n_particles, np.int64)
-    for t in np.nonzero(tile_count)[0]:
-        R, P = int(rows[t]), int(tile_count[t])
-        block = gorder[int(trs[t]) * 64:(int(trs[t]) + R) * 64].reshape(R, 64)     # [row][lane]
-        seq = block.T.reshape(-1)[:P]                                               # s = lane*R + row
-        assert np.all(block.T.reshape(-1)[P:] == 0xFFFFFFFF)
-        c0 = t * per
-        for c in range(c0, c0 + per):
-            a, b = int(start[c]) - int(start[c0]), int(start[c + 1]) - int(start[c0])
-            assert np.array_equal(np.sort(seq[a:b]), np.sort(order[start[c]:start[c + 1]]))
-        seen[seq] += 1
-    assert np.all(seen[order] == 1) and seen.sum() == len(order)
-    # the binned copy holds each slot's particle
+    gs = gstart.astype(np.int64)
+    tile_pad = gs[per::per] - gs[:-1:per]
+    groups = tile_pad // 4
+    rows = (groups + 63) // 64
+    assert np.array_equal(np.diff(trs), rows) and int(trs[-1]) == rows_total
+    assert items == int(np.sum((rows + 15) // 16))
     sorted_f = tr.ws.view(torch.float32)[lay.sorted // 4: lay.sorted // 4 + lay.n_fields * lay.max_slots]
-    sorted_f = sorted_f.view(lay.max_slots, lay.n_fields)[: rows_total * 64].cpu().numpy()
-    valid = gorder != 0xFFFFFFFF
+    rec = sorted_f.view(lay.max_slots, lay.n_fields)[: rows_total * 256].cpu().numpy()
     src = np.concatenate([host["x"], host["v"], host["C"], host["m"][None]])
     nf = src.shape[0]
-    assert np.array_equal(sorted_f[valid, :nf].T, src[:, gorder[valid]])
+    seen = np.zeros(w.n_particles, np.int64)
+    for t in np.nonzero(tile_pad)[0]:
+        R = int(rows[t])
+        s_pos = np.arange(int(tile_pad[t]))
+        g = s_pos // 4
+        slot = (trs[t] + g % R) * 256 + (s_pos % 4) * 64 + g // R
+        seq = gorder[slot]                                   # padded cell-sorted sequence of the tile
+        c0 = t * per
+        for c in range(c0, c0 + per):
+            a = int(gs[c] - gs[c0])
+            n_c = int(cnt[c])
+            got = seq[a:a + n_c]
+            assert np.array_equal(np.sort(got), np.sort(order[start[c]:start[c + 1]]))
+            pads = slot[a + n_c:int(gs[c + 1] - gs[c0])]
+            assert np.all(gorder[pads] == 0xFFFFFFFF)
+            if len(pads):
+                pr = rec[pads]                               # zero mass, velocity and affine matrix
+                assert np.all(pr[:, w.dim:nf] == 0)
+                assert np.any(np.all(src[:w.dim, got].T[:, None, :] == pr[None, :, :w.dim], axis=2), axis=0).all()
+        seen[seq[seq != 0xFFFFFFFF]] += 1
+    assert np.all(seen[order] == 1) and seen.sum() == len(order)
+    valid = gorder != 0xFFFFFFFF
+    assert np.array_equal(rec[valid, :nf].T, src[:, gorder[valid]])
 
 
 # ------------------------------------------------------ grid update + gather
