@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--workload", default="blobs_3d_256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="particles in the CPU-baseline sample (0: all)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -108,6 +110,13 @@ def main():
     stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in events])
     clear_ms, bin_ms, p2g_ms = stage.mean(axis=0)
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (clear {clear_ms:.3f}, bin {bin_ms:.3f}, p2g {p2g_ms:.3f})")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)                      # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
 
     # workload facts for the algorithmic byte counts
     parts, tr = copies[0]

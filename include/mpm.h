@@ -101,10 +101,11 @@ typedef struct {
                                         [3] P2G work cursor, [4] record slots incl. pads */
     size_t key;             /* uint32 [n] cell key of each particle (0xFFFFFFFF when skipped)   */
     size_t rank;            /* uint32 [n] arrival rank of each particle inside its cell         */
-    size_t order;           /* uint32 [max_slots] slot -> particle index (0xFFFFFFFF: empty)    */
+    size_t slot;            /* uint32 [n] record slot of each particle (0xFFFFFFFF: not binned) */
     size_t sorted;          /* float  [max_slots][n_fields] binned records x, v, C, m, padding  */
     size_t tile_tmp;        /* uint32 [2][n_tiles] per-tile row and work-item counts (internal) */
     size_t scan_tmp;        /* uint32 [scan_blocks] prefix-sum block totals (internal)          */
+    size_t tile_info;       /* uint32 [n_tiles][4]: padded first position, rows, first row, 0  */
     int64_t n_cells, n_tiles, max_items, max_slots, n_fields, rows_per_item;
     size_t total_bytes;
 } mpm_ws_layout;
@@ -142,7 +143,7 @@ int mpm_workspace_layout(const mpm_grid_desc *grid, int64_t n_particles, mpm_ws_
  * GPU Optimization & Reference Codebases", section 2.1: sort + tile).  The
  * caller's arrays are not reordered (section 5 rule 2): the workspace
  * receives the cell histogram and prefix sum, per-tile rows, the P2G work
- * items, a slot -> particle permutation and a binned copy of x, v, C, m:
+ * items, each particle's record slot and a binned copy of x, v, C, m:
  * 64-byte records (48 in 2D), each cell padded with zero-mass records to a
  * multiple of 4, in groups of 4 same-cell records, one group per lane of a
  * 256-slot row.  Particles whose stencil leaves the grid are not binned and

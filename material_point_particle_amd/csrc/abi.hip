@@ -128,10 +128,11 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     o->meta = take(u4 * 16);
     o->key = take(u4 * (size_t)n1);
     o->rank = take(u4 * (size_t)n1);
-    o->order = take(u4 * (size_t)(max_rows * kRowSlots));
+    o->slot = take(u4 * (size_t)n1);
     o->sorted = take(sizeof(float) * (size_t)(n_fields * max_rows * kRowSlots));
     o->tile_tmp = take(u4 * 2 * (size_t)n_tiles);
     o->scan_tmp = take(u4 * (size_t)scan_blocks);
+    o->tile_info = take(u4 * 4 * (size_t)n_tiles);
     o->n_cells = n_cells;
     o->n_tiles = n_tiles;
     o->max_items = max_items;
@@ -153,10 +154,11 @@ BinView bin_view(void *ws, const mpm_ws_layout &l)
     v.meta = (uint32_t *)(b + l.meta);
     v.key = (uint32_t *)(b + l.key);
     v.rank = (uint32_t *)(b + l.rank);
-    v.order = (uint32_t *)(b + l.order);
+    v.slot = (uint32_t *)(b + l.slot);
     v.sorted = (float *)(b + l.sorted);
     v.tile_tmp = (uint32_t *)(b + l.tile_tmp);
     v.scan_tmp = (uint32_t *)(b + l.scan_tmp);
+    v.tile_info = (uint32_t *)(b + l.tile_info);
     v.n_cells = l.n_cells;
     v.n_tiles = l.n_tiles;
     v.max_items = l.max_items;

@@ -15,13 +15,15 @@
 //   3. layout   per tile: rows of kRowSlots record slots (one group of kGroup
 //               same-cell records per lane) and P2G work items of up to
 //               kRowsPerItem rows; both prefix-summed over tiles.
-//   4. items    per tile: the (tile, first row) of each of its work items.
+//   4. items    per tile: the (tile, first row) of each of its work items, and
+//               a compact (first position, rows, first row) record per tile.
 //   5. scatter  one thread per particle: its slot in the tile's grouped,
 //               transposed layout (group g of a tile with R rows sits in lane
-//               g / R of row g % R); the slot -> particle index and a record of
+//               g / R of row g % R); the particle's slot and a record of
 //               the particle's fields (x, v, C, m: 64 bytes in 3D) are written
-//               there, so each scattered write is one whole record.  Cells are
-//               padded to whole groups with zero-mass records.
+//               there, so each scattered write is one whole record.
+//   6. pad      one thread per cell: zero-mass records complete the cell's
+//               last group.
 // Arrival ranks depend on scheduling, so slot contents differ between runs;
 // every group holds kGroup records of one cell, which is all P2G needs.
 #include "common.hpp"
@@ -122,22 +124,54 @@ __global__ void __launch_bounds__(kScanBlock) scan_final_kernel(const uint32_t *
                                                                 uint32_t *__restrict__ out)
 {
     const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+    const bool full = (int64_t)(blockIdx.x + 1) * kScanTile <= len;   // uniform across the block
     uint32_t v[kScanItems];
     uint32_t s = 0;
+    if (full) {                      // 16 consecutive words per thread as four 16-byte loads
+        const uint4 *src = reinterpret_cast<const uint4 *>(in + base);
 #pragma unroll
-    for (int i = 0; i < kScanItems; ++i) {
-        const int64_t k = base + i;
-        v[i] = k < len ? scan_load<ROUND>(in, k) : 0u;
-        s += v[i];
+        for (int q = 0; q < kScanItems / 4; ++q) {
+            const uint4 t = src[q];
+            v[4 * q] = t.x;
+            v[4 * q + 1] = t.y;
+            v[4 * q + 2] = t.z;
+            v[4 * q + 3] = t.w;
+        }
+#pragma unroll
+        for (int i = 0; i < kScanItems; ++i) {
+            if (ROUND != 1)
+                v[i] = (v[i] + (ROUND - 1)) / ROUND * ROUND;
+            s += v[i];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kScanItems; ++i) {
+            const int64_t k = base + i;
+            v[i] = k < len ? scan_load<ROUND>(in, k) : 0u;
+            s += v[i];
+        }
     }
     __shared__ uint32_t tot;
     uint32_t run = block_exclusive_scan<kScanBlock>(s, &tot) + partial[blockIdx.x];
+    if (full) {
+        uint32_t o[kScanItems];
 #pragma unroll
-    for (int i = 0; i < kScanItems; ++i) {
-        const int64_t k = base + i;
-        if (k < len)
-            out[k] = run;
-        run += v[i];
+        for (int i = 0; i < kScanItems; ++i) {
+            o[i] = run;
+            run += v[i];
+        }
+        uint4 *dst = reinterpret_cast<uint4 *>(out + base);
+#pragma unroll
+        for (int q = 0; q < kScanItems / 4; ++q)
+            dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kScanItems; ++i) {
+            const int64_t k = base + i;
+            if (k < len)
+                out[k] = run;
+            run += v[i];
+        }
     }
 }
 
@@ -163,26 +197,30 @@ hipError_t exclusive_scan(const uint32_t *in, int64_t len, uint32_t *out, uint32
     return hipGetLastError();
 }
 
-// Fill order[0 .. kRowSlots * rows) with kEmpty, rows read from the device.
-__global__ void fill_order_kernel(uint32_t *__restrict__ order, const uint32_t *__restrict__ rows)
-{
-    const int64_t count = (int64_t)(*rows) * kRowSlots;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
-        order[i] = kEmpty;
-}
-
 // Pass 1: cell key from the position only; particles whose stencil leaves the
 // grid are counted and not binned.  The attribute range check happens in the
 // scatter pass, which reads the attributes anyway.
+//
+// Blocks visit 256-particle chunks in the order chunk = (i * stride) mod
+// chunks (stride a prime not dividing the chunk count), so the blocks that
+// run at the same time hold particles from all over the caller's array.
+// Input arrays often list particles region by region (a generator filling one
+// blob or block after another); visiting them in order would aim every
+// concurrent atomic at the few cells of one region and serialise them.
 template <int DIM>
 __global__ void __launch_bounds__(256) bin_count_kernel(Fields f, float nf, float dx, float last_base, int ntx,
                                                          uint32_t *__restrict__ cell_count,
                                                          uint32_t *__restrict__ key_out,
                                                          uint32_t *__restrict__ rank_out,
-                                                         uint32_t *__restrict__ status, uint32_t *__restrict__ meta)
+                                                         uint32_t *__restrict__ status, uint32_t *__restrict__ meta,
+                                                         int64_t chunks, int64_t stride)
 {
     constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
-    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < f.n; p += (int64_t)gridDim.x * blockDim.x) {
+    uint32_t binned = 0;
+    for (int64_t i = blockIdx.x; i < chunks; i += gridDim.x) {
+        const int64_t p = ((i * stride) % chunks) * 256 + threadIdx.x;
+        if (p >= f.n)
+            continue;
         bool dom = true;
         int base[DIM];
 #pragma unroll
@@ -192,7 +230,7 @@ __global__ void __launch_bounds__(256) bin_count_kernel(Fields f, float nf, floa
             base[e] = ax.base;
         }
         wave_count(!dom, &status[0]);
-        wave_count(dom, &meta[2]);
+        binned += dom ? 1u : 0u;
         uint32_t key = kEmpty, rank = 0;
         if (dom) {
             uint32_t t = 0, l = 0;
@@ -207,6 +245,12 @@ __global__ void __launch_bounds__(256) bin_count_kernel(Fields f, float nf, floa
         key_out[p] = key;
         rank_out[p] = rank;
     }
+    // one atomic per block for the binned-particle total (a per-wave atomic on
+    // one address from every wave of the grid would serialise)
+    __shared__ uint32_t total;
+    (void)block_exclusive_scan<256>(binned, &total);
+    if (threadIdx.x == 0 && total != 0u)
+        atomicAdd(&meta[2], total);
 }
 
 // Pass 3: per tile, rows of kRowSlots record slots (one group of kGroup
@@ -225,16 +269,25 @@ __global__ void __launch_bounds__(256) tile_layout_kernel(const uint32_t *__rest
     }
 }
 
-__global__ void __launch_bounds__(256) items_kernel(const uint32_t *__restrict__ tile_items,
-                                                     const uint32_t *__restrict__ item_start, int64_t n_tiles,
-                                                     int64_t max_items, uint32_t *__restrict__ items)
+// Pass 4: the work items of each tile, and a compact per-tile record
+// (padded first position, rows, first row) for the scatter pass.
+template <int DIM>
+__global__ void __launch_bounds__(256) items_kernel(const uint32_t *__restrict__ tile_rows,
+                                                     const uint32_t *__restrict__ tile_items,
+                                                     const uint32_t *__restrict__ item_start,
+                                                     const uint32_t *__restrict__ tile_row_start,
+                                                     const uint32_t *__restrict__ cell_start, int64_t n_tiles,
+                                                     int64_t max_items, uint32_t *__restrict__ items,
+                                                     uint4 *__restrict__ tile_info)
 {
+    constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n_tiles; t += (int64_t)gridDim.x * blockDim.x) {
         const uint32_t k = tile_items[t], s0 = item_start[t];
         for (uint32_t c = 0; c < k; ++c) {
             items[s0 + c] = (uint32_t)t;
             items[max_items + s0 + c] = c * kRowsPerItem;
         }
+        tile_info[t] = make_uint4(cell_start[t * per_tile], tile_rows[t], tile_row_start[t], 0u);
     }
 }
 
@@ -256,20 +309,16 @@ __device__ __forceinline__ int64_t slot_of(uint32_t row_start, uint32_t rows, ui
     return ((int64_t)row_start + g % rows) * kRowSlots + (int64_t)(s % kGroup) * kWave + g / rows;
 }
 
-// Pass 5: place each binned particle's record.  The last arrival of a cell
-// whose count is not a multiple of kGroup also writes the cell's pad records:
-// its own position with zero mass, velocity and affine matrix, which the
-// transfer turns into exact zero contributions.  Particles outside the
-// declared ranges are counted and written the same way (they contribute
-// nothing, as if skipped).
+// Pass 5: place each binned particle's record.  Particles outside the
+// declared ranges are counted and written with zero mass, velocity and affine
+// matrix: they contribute nothing, as if skipped.
 template <int DIM>
 __global__ void __launch_bounds__(256) bin_scatter_kernel(Fields f, RangesF r, const uint32_t *__restrict__ key_in,
                                                            const uint32_t *__restrict__ rank_in,
-                                                           const uint32_t *__restrict__ cell_count,
                                                            const uint32_t *__restrict__ cell_start,
-                                                           const uint32_t *__restrict__ tile_row_start,
-                                                           uint32_t *__restrict__ order, float *__restrict__ sorted,
-                                                           uint32_t *__restrict__ status)
+                                                           const uint4 *__restrict__ tile_info,
+                                                           uint32_t *__restrict__ slot_out,
+                                                           float *__restrict__ sorted, uint32_t *__restrict__ status)
 {
     constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
     constexpr int R = rec_floats<DIM>();
@@ -278,14 +327,7 @@ __global__ void __launch_bounds__(256) bin_scatter_kernel(Fields f, RangesF r, c
         const bool binned = key != kEmpty;
         float rec[R];
         bool rng = false;
-        uint32_t tile = 0, first = 0, rows = 1, s = 0, rank = 0, count = 0;
         if (binned) {
-            tile = key / per_tile;
-            first = cell_start[(int64_t)tile * per_tile];
-            rows = (cell_start[(int64_t)(tile + 1) * per_tile] - first + kRowSlots - 1) / kRowSlots;
-            rank = rank_in[p];
-            count = cell_count[key];
-            s = cell_start[key] - first + rank;
             int fi = 0;
 #pragma unroll
             for (int e = 0; e < DIM; ++e)
@@ -314,28 +356,71 @@ __global__ void __launch_bounds__(256) bin_scatter_kernel(Fields f, RangesF r, c
             }
         }
         wave_count(binned && !rng, &status[1]);
-        if (!binned)
+        if (!binned) {
+            slot_out[p] = kEmpty;
             continue;
-        const uint32_t row_start = tile_row_start[tile];
-        int64_t slot = slot_of(row_start, rows, s);
-        order[slot] = (uint32_t)p;
+        }
+        const uint4 ti = tile_info[key / per_tile];           // (first, rows, row_start, -)
+        const uint32_t s = cell_start[key] - ti.x + rank_in[p];
+        const int64_t slot = slot_of(ti.z, ti.y, s);
+        slot_out[p] = (uint32_t)slot;
         float4 *dst = reinterpret_cast<float4 *>(sorted + slot * R);
 #pragma unroll
         for (int q = 0; q < R / 4; ++q)
             dst[q] = make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
-        if (rank + 1 == count && count % kGroup != 0) {
+    }
+}
+
+// Pass 6: pad records.  A cell whose count is not a multiple of kGroup gets
+// zero-mass records at its centre (g = base + 1 on every axis, which lies in
+// the same base cell) in its remaining group positions; the transfer turns
+// them into exact zero contributions.
+template <int DIM>
+__global__ void __launch_bounds__(256) bin_pad_kernel(const uint32_t *__restrict__ cell_count,
+                                                       const uint32_t *__restrict__ cell_start,
+                                                       const uint4 *__restrict__ tile_info, int64_t n_cells, int ntx,
+                                                       float inv_n, float *__restrict__ sorted)
+{
+    constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
+    constexpr int R = rec_floats<DIM>();
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n_cells; c += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t count = cell_count[c];
+        const uint32_t rem = count % kGroup;
+        if (rem == 0)
+            continue;
+        const uint32_t tile = (uint32_t)(c / per_tile), local = (uint32_t)(c % per_tile);
+        const uint4 ti = tile_info[tile];
+        float rec[R];
 #pragma unroll
-            for (int k = DIM; k < R; ++k)
-                rec[k] = 0.0f;
-            for (uint32_t pad = s + 1; pad < s + 1 + (kGroup - count % kGroup); ++pad) {
-                slot = slot_of(row_start, rows, pad);
-                dst = reinterpret_cast<float4 *>(sorted + slot * R);
+        for (int k = 0; k < R; ++k)
+            rec[k] = 0.0f;
+        uint32_t t = tile, l = local;
 #pragma unroll
-                for (int q = 0; q < R / 4; ++q)
-                    dst[q] = make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
-            }
+        for (int e = 0; e < DIM; ++e) {
+            const uint32_t base = (t % (uint32_t)ntx) * kTile + l % kTile;
+            rec[e] = (float)(base + 1) * inv_n;
+            t /= (uint32_t)ntx;
+            l /= kTile;
+        }
+        const uint32_t s0 = cell_start[c] - ti.x + count;
+        for (uint32_t s = s0; s < s0 + (kGroup - rem); ++s) {
+            float4 *dst = reinterpret_cast<float4 *>(sorted + slot_of(ti.z, ti.y, s) * R);
+#pragma unroll
+            for (int q = 0; q < R / 4; ++q)
+                dst[q] = make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
         }
     }
+}
+
+// A prime step that does not divide `chunks`, so i -> (i * step) mod chunks
+// is a permutation of the chunks.
+int64_t chunk_stride(int64_t chunks)
+{
+    const int64_t primes[] = { 7919, 104729, 1299709, 15485863 };
+    for (int64_t q : primes)
+        if (chunks % q != 0)
+            return q % (chunks > 0 ? chunks : 1) == 0 ? 1 : q;
+    return 1;
 }
 
 int blocks_for(int64_t work, int block)
@@ -355,12 +440,14 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
     hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks_for(b.n_cells, 256)), dim3(256), 0, s, b.cell_count, b.n_cells,
                        0u);
     hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, s, b.meta, (int64_t)16, 0u);
+    const int64_t chunks = (p.n + 255) / 256;
+    const int64_t stride = chunk_stride(chunks);
     if (dim == 3)
         hipLaunchKernelGGL(bin_count_kernel<3>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, nf, dx, last, ntx,
-                           b.cell_count, b.key, b.rank, status, b.meta);
+                           b.cell_count, b.key, b.rank, status, b.meta, chunks, stride);
     else
         hipLaunchKernelGGL(bin_count_kernel<2>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, nf, dx, last, ntx,
-                           b.cell_count, b.key, b.rank, status, b.meta);
+                           b.cell_count, b.key, b.rank, status, b.meta, chunks, stride);
     hipError_t e = exclusive_scan<kGroup>(b.cell_count, b.n_cells, b.cell_start, b.scan_tmp, s);
     if (e != hipSuccess)
         return e;
@@ -374,17 +461,26 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
         return e;
     if ((e = exclusive_scan<1>(tile_items, b.n_tiles, b.item_start, b.scan_tmp, s)) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(items_kernel, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_items, b.item_start,
-                       b.n_tiles, b.max_items, b.items);
+    uint4 *tile_info = reinterpret_cast<uint4 *>(b.tile_info);
+    if (dim == 3)
+        hipLaunchKernelGGL(items_kernel<3>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_rows, tile_items,
+                           b.item_start, b.tile_row_start, b.cell_start, b.n_tiles, b.max_items, b.items, tile_info);
+    else
+        hipLaunchKernelGGL(items_kernel<2>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_rows, tile_items,
+                           b.item_start, b.tile_row_start, b.cell_start, b.n_tiles, b.max_items, b.items, tile_info);
     hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(1), 0, s, b.item_start, b.tile_row_start, b.cell_start, b.n_tiles,
                        b.n_cells, b.meta);
-    hipLaunchKernelGGL(fill_order_kernel, dim3(blocks_for(b.max_slots, 256)), dim3(256), 0, s, b.order, b.meta + 1);
-    if (dim == 3)
+    if (dim == 3) {
         hipLaunchKernelGGL(bin_scatter_kernel<3>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, r, b.key, b.rank,
-                           b.cell_count, b.cell_start, b.tile_row_start, b.order, b.sorted, status);
-    else
+                           b.cell_start, tile_info, b.slot, b.sorted, status);
+        hipLaunchKernelGGL(bin_pad_kernel<3>, dim3(blocks_for(b.n_cells, 256)), dim3(256), 0, s, b.cell_count,
+                           b.cell_start, tile_info, b.n_cells, ntx, 1.0f / (float)n, b.sorted);
+    } else {
         hipLaunchKernelGGL(bin_scatter_kernel<2>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, r, b.key, b.rank,
-                           b.cell_count, b.cell_start, b.tile_row_start, b.order, b.sorted, status);
+                           b.cell_start, tile_info, b.slot, b.sorted, status);
+        hipLaunchKernelGGL(bin_pad_kernel<2>, dim3(blocks_for(b.n_cells, 256)), dim3(256), 0, s, b.cell_count,
+                           b.cell_start, tile_info, b.n_cells, ntx, 1.0f / (float)n, b.sorted);
+    }
     return hipGetLastError();
 }
 

@@ -82,8 +82,8 @@ struct Fields {           // component-major particle arrays of n particles
 };
 
 struct BinView {          // the workspace arrays, as typed device pointers
-    uint32_t *cell_start, *cell_count, *tile_row_start, *item_start, *items, *meta, *key, *rank, *order,
-        *tile_tmp, *scan_tmp;
+    uint32_t *cell_start, *cell_count, *tile_row_start, *item_start, *items, *meta, *key, *rank, *slot,
+        *tile_tmp, *scan_tmp, *tile_info;
     float *sorted;
     int64_t n_cells, n_tiles, max_items, max_slots, n_fields;
 };

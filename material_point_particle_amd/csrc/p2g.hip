@@ -307,25 +307,41 @@ __global__ void __launch_bounds__(kWave) p2g_tiled_kernel(TiledArgs a)
             acc[i] = 0.0;
         __syncthreads();
 
-        for (uint32_t j = row0; j < row1; ++j) {
-            if ((uint32_t)lane * rows + j >= groups)        // this lane's group index: lane * rows + j
-                continue;
+        // Records of the next row are loaded right after the current row's
+        // are hoisted, so the loads overlap the node loop.  Rows below `rows`
+        // lie inside the tile's allocation, so the loads are in bounds even
+        // for lanes whose group index is past the tile's last group.
+        float4 buf[G][R / 4];
+        auto load_row = [&](uint32_t j) {
             const int64_t slot0 = (row_base + j) * kRowSlots + lane;
-            GroupHoist<DIM> h[G];
 #pragma unroll
             for (int k = 0; k < G; ++k) {
                 const float4 *src = reinterpret_cast<const float4 *>(a.sorted + (slot0 + k * kWave) * R);
+#pragma unroll
+                for (int q = 0; q < R / 4; ++q)
+                    buf[k][q] = src[q];
+            }
+        };
+        if (row0 < row1)
+            load_row(row0);
+        for (uint32_t j = row0; j < row1; ++j) {
+            GroupHoist<DIM> h[G];
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
                 float rec[R];
 #pragma unroll
                 for (int q = 0; q < R / 4; ++q) {
-                    const float4 t = src[q];
-                    rec[4 * q] = t.x;
-                    rec[4 * q + 1] = t.y;
-                    rec[4 * q + 2] = t.z;
-                    rec[4 * q + 3] = t.w;
+                    rec[4 * q] = buf[k][q].x;
+                    rec[4 * q + 1] = buf[k][q].y;
+                    rec[4 * q + 2] = buf[k][q].z;
+                    rec[4 * q + 3] = buf[k][q].w;
                 }
                 group_hoist<DIM>(rec, a.nf, a.dx, a.last_base, a.S, h[k]);
             }
+            if (j + 1 < row1)
+                load_row(j + 1);
+            if ((uint32_t)lane * rows + j >= groups)        // this lane's group index: lane * rows + j
+                continue;
             // every record of the group is in one cell of this tile (binning's
             // invariant); a group that breaks it is counted and skipped
             bool ok = true;

@@ -75,13 +75,13 @@ def test_workspace_layout_is_disjoint_and_aligned():
         assert M.mpm_workspace_bytes(d, N) == lay.total_bytes
         assert lay.n_cells == n ** dim and lay.n_tiles == (n // 4) ** dim
         assert lay.n_fields == {2: 12, 3: 16}[dim]     # x, v, C, m padded to a multiple of 4 floats
-        assert lay.max_slots % 64 == 0 and lay.max_slots >= N
+        assert lay.max_slots % 256 == 0 and lay.max_slots >= N
         spans = sorted([
             (lay.cell_start, 4 * (lay.n_cells + 1)), (lay.cell_count, 4 * lay.n_cells),
             (lay.tile_row_start, 4 * (lay.n_tiles + 1)), (lay.item_start, 4 * (lay.n_tiles + 1)),
             (lay.items, 8 * lay.max_items), (lay.meta, 64), (lay.key, 4 * max(N, 1)), (lay.rank, 4 * max(N, 1)),
-            (lay.order, 4 * lay.max_slots), (lay.sorted, 4 * lay.n_fields * lay.max_slots),
-            (lay.tile_tmp, 8 * lay.n_tiles)])
+            (lay.slot, 4 * max(N, 1)), (lay.sorted, 4 * lay.n_fields * lay.max_slots),
+            (lay.tile_tmp, 8 * lay.n_tiles), (lay.tile_info, 16 * lay.n_tiles)])
         for (a, la), (b, _) in zip(spans, spans[1:]):
             assert a % 256 == 0 and a + la <= b
         assert spans[-1][0] + spans[-1][1] <= lay.total_bytes

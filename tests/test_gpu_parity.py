@@ -243,7 +243,14 @@ def test_binning_matches_oracle(mpm, oracle_lib, name, count):
     rows_total, items = int(meta[1]), int(meta[0])
     assert int(meta[2]) == len(order) and int(meta[4]) == int(padded.sum())
     trs = u32(tr.ws_u32("tile_row_start", lay.n_tiles + 1)).astype(np.int64)
-    gorder = u32(tr.ws_u32("order", lay.max_slots))[: rows_total * 256]
+    slot_of = u32(tr.ws_u32("slot", w.n_particles)).astype(np.int64)
+    assert np.all(slot_of[order] != 0xFFFFFFFF)
+    gorder = np.full(rows_total * 256, 0xFFFFFFFF, dtype=np.int64)   # slot -> particle
+    binned_idx = np.nonzero(slot_of != 0xFFFFFFFF)[0]
+    assert np.array_equal(np.sort(binned_idx), np.sort(order))
+    assert np.all(slot_of[binned_idx] < rows_total * 256)
+    gorder[slot_of[binned_idx]] = binned_idx
+    assert len(np.unique(slot_of[binned_idx])) == len(binned_idx)
     per = 4 ** w.dim
     gs = gstart.astype(np.int64)
     tile_pad = gs[per::per] - gs[:-1:per]
@@ -273,7 +280,12 @@ def test_binning_matches_oracle(mpm, oracle_lib, name, count):
             if len(pads):
                 pr = rec[pads]                               # zero mass, velocity and affine matrix
                 assert np.all(pr[:, w.dim:nf] == 0)
-                assert np.any(np.all(src[:w.dim, got].T[:, None, :] == pr[None, :, :w.dim], axis=2), axis=0).all()
+                tile_id, local, centre = int(t), c - c0, []
+                for e in range(w.dim):                       # pads sit at the cell centre, g = base + 1
+                    centre.append(((tile_id % (w.n // 4)) * 4 + local % 4 + 1) / w.n)
+                    tile_id //= w.n // 4
+                    local //= 4
+                assert np.all(pr[:, :w.dim] == np.array(centre, np.float32)[None, :])
         seen[seq[seq != 0xFFFFFFFF]] += 1
     assert np.all(seen[order] == 1) and seen.sum() == len(order)
     valid = gorder != 0xFFFFFFFF
