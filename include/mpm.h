@@ -95,17 +95,21 @@ typedef struct {
                                         each rounded up to a multiple of 4 (record groups) */
     size_t cell_count;      /* uint32 [n_cells]     per-cell particle counts                    */
     size_t tile_row_start;  /* uint32 [n_tiles + 1] first 256-slot row of each tile             */
-    size_t item_start;      /* uint32 [n_tiles + 1] first P2G work item of each tile            */
-    size_t items;           /* uint32 [2][max_items] (tile, first row) of each work item        */
+    size_t item_start;      /* uint32 [n_tiles + 1] first full P2G work item of each tile       */
+    size_t items;           /* uint32 [max_items][4] work items: tile, first row | end row << 16,
+                                        groups of the tile, first row of the tile; handed
+                                        out alternately the largest and smallest remaining */
     size_t meta;            /* uint32 [16]: [0] items, [1] rows, [2] binned particles,
                                         [3] P2G work cursor, [4] record slots incl. pads */
     size_t key;             /* uint32 [n] cell key of each particle (0xFFFFFFFF when skipped)   */
     size_t rank;            /* uint32 [n] arrival rank of each particle inside its cell         */
     size_t slot;            /* uint32 [n] record slot of each particle (0xFFFFFFFF: not binned) */
     size_t sorted;          /* float  [max_slots][n_fields] binned records x, v, C, m, padding  */
-    size_t tile_tmp;        /* uint32 [2][n_tiles] per-tile row and work-item counts (internal) */
+    size_t tile_tmp;        /* uint32 [3][n_tiles] per-tile rows, full items, partial item (internal) */
     size_t scan_tmp;        /* uint32 [scan_blocks] prefix-sum block totals (internal)          */
     size_t tile_info;       /* uint32 [n_tiles][4]: padded first position, rows, first row, 0  */
+    size_t item_hist;       /* uint32 [15][ceil(n_tiles/256)] partial-item sizes per block (internal) */
+    size_t item_hist_start; /* uint32 prefix sum of item_hist (internal)                          */
     int64_t n_cells, n_tiles, max_items, max_slots, n_fields, rows_per_item;
     size_t total_bytes;
 } mpm_ws_layout;
@@ -138,7 +142,8 @@ int mpm_workspace_bytes(const mpm_grid_desc *grid, int64_t n_particles, size_t *
 int mpm_workspace_layout(const mpm_grid_desc *grid, int64_t n_particles, mpm_ws_layout *layout);
 
 /* Counting sort of the particles into tiles of 4^dim cells, keyed by the
- * stencil's base cell and numbered tile by tile ("Particle worlds, part 3",
+ * stencil's base cell and numbered tile by tile (inside a 3D tile x fastest,
+ * then z, then y) ("Particle worlds, part 3",
  * steps 3-4: histogram, exclusive prefix sum, scatter; "Implementation --
  * GPU Optimization & Reference Codebases", section 2.1: sort + tile).  The
  * caller's arrays are not reordered (section 5 rule 2): the workspace

@@ -110,7 +110,7 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     const int64_t max_rows = (np + (kGroup - 1) * busy_cells + kRowSlots - 1) / kRowSlots + busy;
     const int64_t max_items = (max_rows + kRowsPerItem - 1) / kRowsPerItem + busy;
     const int64_t n_fields = g->dim == 3 ? rec_floats<3>() : rec_floats<2>();
-    const int64_t big = n_cells > n_tiles ? n_cells : n_tiles;
+    const int64_t big = n_cells > n_tiles ? n_cells : n_tiles;   // (the item histogram is shorter than n_tiles)
     const int64_t scan_blocks = (big + kScanTileElems - 1) / kScanTileElems + 1;
     size_t off = 0;
     auto take = [&off](size_t bytes) {
@@ -124,15 +124,18 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     o->cell_count = take(u4 * (size_t)n_cells);
     o->tile_row_start = take(u4 * (size_t)(n_tiles + 1));
     o->item_start = take(u4 * (size_t)(n_tiles + 1));
-    o->items = take(u4 * 2 * (size_t)max_items);
+    o->items = take(u4 * 4 * (size_t)max_items);
     o->meta = take(u4 * 16);
     o->key = take(u4 * (size_t)n1);
     o->rank = take(u4 * (size_t)n1);
     o->slot = take(u4 * (size_t)n1);
     o->sorted = take(sizeof(float) * (size_t)(n_fields * max_rows * kRowSlots));
-    o->tile_tmp = take(u4 * 2 * (size_t)n_tiles);
+    o->tile_tmp = take(u4 * 3 * (size_t)n_tiles);
     o->scan_tmp = take(u4 * (size_t)scan_blocks);
     o->tile_info = take(u4 * 4 * (size_t)n_tiles);
+    const int64_t hist_len = (kRowsPerItem - 1) * ((n_tiles + 255) / 256);
+    o->item_hist = take(u4 * (size_t)hist_len);
+    o->item_hist_start = take(u4 * (size_t)(hist_len + 1));
     o->n_cells = n_cells;
     o->n_tiles = n_tiles;
     o->max_items = max_items;
@@ -159,6 +162,8 @@ BinView bin_view(void *ws, const mpm_ws_layout &l)
     v.tile_tmp = (uint32_t *)(b + l.tile_tmp);
     v.scan_tmp = (uint32_t *)(b + l.scan_tmp);
     v.tile_info = (uint32_t *)(b + l.tile_info);
+    v.item_hist = (uint32_t *)(b + l.item_hist);
+    v.item_hist_start = (uint32_t *)(b + l.item_hist_start);
     v.n_cells = l.n_cells;
     v.n_tiles = l.n_tiles;
     v.max_items = l.max_items;

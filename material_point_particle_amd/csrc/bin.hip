@@ -13,10 +13,13 @@
 //               a multiple of kGroup (three phases: per-block sums, one block
 //               scans the sums, per-block rescan).
 //   3. layout   per tile: rows of kRowSlots record slots (one group of kGroup
-//               same-cell records per lane) and P2G work items of up to
-//               kRowsPerItem rows; both prefix-summed over tiles.
-//   4. items    per tile: the (tile, first row) of each of its work items, and
-//               a compact (first position, rows, first row) record per tile.
+//               same-cell records per lane), full P2G work items of
+//               kRowsPerItem rows and a partial last item; rows and full items
+//               prefix-summed over tiles, partial items counting-sorted by
+//               size (largest first).
+//   4. items    the (tile, first row) of every work item, alternately from the
+//               large and the small end of the size order; and a compact
+//               (first position, rows, first row) record per tile.
 //   5. scatter  one thread per particle: its slot in the tile's grouped,
 //               transposed layout (group g of a tile with R rows sits in lane
 //               g / R of row g % R); the particle's slot and a record of
@@ -197,7 +200,8 @@ hipError_t exclusive_scan(const uint32_t *in, int64_t len, uint32_t *out, uint32
     return hipGetLastError();
 }
 
-// Pass 1: cell key from the position only; particles whose stencil leaves the
+// Pass 1: cell key (tile, then the cell's local number, see tile_local) from
+// the position only; particles whose stencil leaves the
 // grid are counted and not binned.  The attribute range check happens in the
 // scatter pass, which reads the attributes anyway.
 //
@@ -233,13 +237,13 @@ __global__ void __launch_bounds__(256) bin_count_kernel(Fields f, float nf, floa
         binned += dom ? 1u : 0u;
         uint32_t key = kEmpty, rank = 0;
         if (dom) {
-            uint32_t t = 0, l = 0;
+            uint32_t t = 0, l[DIM];
 #pragma unroll
             for (int e = DIM - 1; e >= 0; --e) {
                 t = t * (uint32_t)ntx + (uint32_t)(base[e] / kTile);
-                l = l * kTile + (uint32_t)(base[e] % kTile);
+                l[e] = (uint32_t)(base[e] % kTile);
             }
-            key = t * per_tile + l;
+            key = t * per_tile + tile_local<DIM>(l);
             rank = atomicAdd(&cell_count[key], 1u);
         }
         key_out[p] = key;
@@ -254,48 +258,89 @@ __global__ void __launch_bounds__(256) bin_count_kernel(Fields f, float nf, floa
 }
 
 // Pass 3: per tile, rows of kRowSlots record slots (one group of kGroup
-// records per lane) and the number of P2G work items.
+// records per lane), its number of full work items (kRowsPerItem rows each)
+// and the size of its last, partial item.  P2G hands items out dynamically;
+// the items are ordered by size (all full items, then the partial items by
+// decreasing size) and handed out alternately from both ends of that order
+// (see items_kernel).  The partial sizes are counting-sorted: one block of 256 tiles counts them per
+// size in LDS (the returned count is the tile's rank within the block) and
+// writes its histogram, size-major, for a prefix sum.  One thread per tile.
 template <int DIM>
 __global__ void __launch_bounds__(256) tile_layout_kernel(const uint32_t *__restrict__ cell_start, int64_t n_tiles,
                                                            uint32_t *__restrict__ tile_rows,
-                                                           uint32_t *__restrict__ tile_items)
+                                                           uint32_t *__restrict__ tile_full,
+                                                           uint32_t *__restrict__ tile_part,
+                                                           uint32_t *__restrict__ item_hist)
 {
     constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n_tiles; t += (int64_t)gridDim.x * blockDim.x) {
+    __shared__ uint32_t hist[kRowsPerItem];
+    if (threadIdx.x < kRowsPerItem)
+        hist[threadIdx.x] = 0u;
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t part = 0, rank = 0;
+    if (t < n_tiles) {
         const uint32_t padded = cell_start[(t + 1) * per_tile] - cell_start[t * per_tile];
         const uint32_t rows = (padded + kRowSlots - 1) / kRowSlots;
+        part = rows % kRowsPerItem;
         tile_rows[t] = rows;
-        tile_items[t] = (rows + kRowsPerItem - 1) / kRowsPerItem;
+        tile_full[t] = rows / kRowsPerItem;
+        if (part != 0u)
+            rank = atomicAdd(&hist[part], 1u);
+        tile_part[t] = (part << 16) | rank;
     }
+    __syncthreads();
+    // row (kRowsPerItem - 1 - size) of the size-major histogram: largest size first
+    if (threadIdx.x >= 1 && threadIdx.x < kRowsPerItem)
+        item_hist[(int64_t)(kRowsPerItem - 1 - threadIdx.x) * gridDim.x + blockIdx.x] = hist[threadIdx.x];
 }
 
 // Pass 4: the work items of each tile, and a compact per-tile record
 // (padded first position, rows, first row) for the scatter pass.
 template <int DIM>
 __global__ void __launch_bounds__(256) items_kernel(const uint32_t *__restrict__ tile_rows,
-                                                     const uint32_t *__restrict__ tile_items,
-                                                     const uint32_t *__restrict__ item_start,
+                                                     const uint32_t *__restrict__ tile_full,
+                                                     const uint32_t *__restrict__ tile_part,
+                                                     const uint32_t *__restrict__ full_start,
+                                                     const uint32_t *__restrict__ hist_start,
                                                      const uint32_t *__restrict__ tile_row_start,
                                                      const uint32_t *__restrict__ cell_start, int64_t n_tiles,
-                                                     int64_t max_items, uint32_t *__restrict__ items,
+                                                     int64_t layout_blocks, uint4 *__restrict__ items,
                                                      uint4 *__restrict__ tile_info)
 {
     constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
+    const uint32_t n_full = full_start[n_tiles];
+    const uint32_t total = n_full + hist_start[(int64_t)(kRowsPerItem - 1) * layout_blocks];
+    // p is an item's position in the size-sorted list; the items are handed
+    // out alternately from its two ends (largest, smallest, second largest,
+    // ...), so long and short items run side by side on every CU and the last
+    // items handed out are short.
+    auto place = [&](uint32_t p) { return p < (total + 1) / 2 ? 2 * p : 2 * (total - 1 - p) + 1; };
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n_tiles; t += (int64_t)gridDim.x * blockDim.x) {
-        const uint32_t k = tile_items[t], s0 = item_start[t];
-        for (uint32_t c = 0; c < k; ++c) {
-            items[s0 + c] = (uint32_t)t;
-            items[max_items + s0 + c] = c * kRowsPerItem;
+        // one 16-byte record per item: tile, first row | end row << 16,
+        // groups of the tile, first row of the tile in the binned copy
+        const uint32_t k = tile_full[t], s0 = full_start[t], rows = tile_rows[t];
+        const uint32_t groups = (cell_start[(t + 1) * per_tile] - cell_start[t * per_tile]) / kGroup;
+        const uint32_t base = tile_row_start[t];
+        for (uint32_t c = 0; c < k; ++c)
+            items[place(s0 + c)] = make_uint4((uint32_t)t, (c * kRowsPerItem) | ((c + 1) * kRowsPerItem << 16),
+                                              groups, base);
+        const uint32_t part = tile_part[t] >> 16;
+        if (part != 0u) {
+            const uint32_t q = place(n_full + hist_start[(int64_t)(kRowsPerItem - 1 - part) * layout_blocks + t / 256] +
+                                     (tile_part[t] & 0xFFFFu));
+            items[q] = make_uint4((uint32_t)t, (k * kRowsPerItem) | (rows << 16), groups, base);
         }
         tile_info[t] = make_uint4(cell_start[t * per_tile], tile_rows[t], tile_row_start[t], 0u);
     }
 }
 
-__global__ void meta_kernel(const uint32_t *__restrict__ item_start, const uint32_t *__restrict__ tile_row_start,
+__global__ void meta_kernel(const uint32_t *__restrict__ full_start, const uint32_t *__restrict__ hist_start,
+                            int64_t hist_len, const uint32_t *__restrict__ tile_row_start,
                             const uint32_t *__restrict__ cell_start, int64_t n_tiles, int64_t n_cells,
                             uint32_t *__restrict__ meta)
 {
-    meta[0] = item_start[n_tiles];
+    meta[0] = full_start[n_tiles] + hist_start[hist_len];
     meta[1] = tile_row_start[n_tiles];
     meta[3] = 0u;
     meta[4] = cell_start[n_cells];
@@ -394,13 +439,13 @@ __global__ void __launch_bounds__(256) bin_pad_kernel(const uint32_t *__restrict
 #pragma unroll
         for (int k = 0; k < R; ++k)
             rec[k] = 0.0f;
-        uint32_t t = tile, l = local;
+        uint32_t t = tile, l[DIM];
+        tile_local_inverse<DIM>(local, l);
 #pragma unroll
         for (int e = 0; e < DIM; ++e) {
-            const uint32_t base = (t % (uint32_t)ntx) * kTile + l % kTile;
+            const uint32_t base = (t % (uint32_t)ntx) * kTile + l[e];
             rec[e] = (float)(base + 1) * inv_n;
             t /= (uint32_t)ntx;
-            l /= kTile;
         }
         const uint32_t s0 = cell_start[c] - ti.x + count;
         for (uint32_t s = s0; s < s0 + (kGroup - rem); ++s) {
@@ -451,25 +496,32 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
     hipError_t e = exclusive_scan<kGroup>(b.cell_count, b.n_cells, b.cell_start, b.scan_tmp, s);
     if (e != hipSuccess)
         return e;
+    const int64_t lblocks = (b.n_tiles + 255) / 256;
+    uint32_t *tile_part = b.tile_tmp + 2 * b.n_tiles;
+    const int64_t hist_len = (kRowsPerItem - 1) * lblocks;
     if (dim == 3)
-        hipLaunchKernelGGL(tile_layout_kernel<3>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, b.cell_start,
-                           b.n_tiles, tile_rows, tile_items);
+        hipLaunchKernelGGL(tile_layout_kernel<3>, dim3((unsigned)lblocks), dim3(256), 0, s, b.cell_start, b.n_tiles,
+                           tile_rows, tile_items, tile_part, b.item_hist);
     else
-        hipLaunchKernelGGL(tile_layout_kernel<2>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, b.cell_start,
-                           b.n_tiles, tile_rows, tile_items);
+        hipLaunchKernelGGL(tile_layout_kernel<2>, dim3((unsigned)lblocks), dim3(256), 0, s, b.cell_start, b.n_tiles,
+                           tile_rows, tile_items, tile_part, b.item_hist);
     if ((e = exclusive_scan<1>(tile_rows, b.n_tiles, b.tile_row_start, b.scan_tmp, s)) != hipSuccess)
         return e;
     if ((e = exclusive_scan<1>(tile_items, b.n_tiles, b.item_start, b.scan_tmp, s)) != hipSuccess)
         return e;
+    if ((e = exclusive_scan<1>(b.item_hist, hist_len, b.item_hist_start, b.scan_tmp, s)) != hipSuccess)
+        return e;
     uint4 *tile_info = reinterpret_cast<uint4 *>(b.tile_info);
     if (dim == 3)
         hipLaunchKernelGGL(items_kernel<3>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_rows, tile_items,
-                           b.item_start, b.tile_row_start, b.cell_start, b.n_tiles, b.max_items, b.items, tile_info);
+                           tile_part, b.item_start, b.item_hist_start, b.tile_row_start, b.cell_start, b.n_tiles,
+                           lblocks, reinterpret_cast<uint4 *>(b.items), tile_info);
     else
         hipLaunchKernelGGL(items_kernel<2>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_rows, tile_items,
-                           b.item_start, b.tile_row_start, b.cell_start, b.n_tiles, b.max_items, b.items, tile_info);
-    hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(1), 0, s, b.item_start, b.tile_row_start, b.cell_start, b.n_tiles,
-                       b.n_cells, b.meta);
+                           tile_part, b.item_start, b.item_hist_start, b.tile_row_start, b.cell_start, b.n_tiles,
+                           lblocks, reinterpret_cast<uint4 *>(b.items), tile_info);
+    hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(1), 0, s, b.item_start, b.item_hist_start, hist_len,
+                       b.tile_row_start, b.cell_start, b.n_tiles, b.n_cells, b.meta);
     if (dim == 3) {
         hipLaunchKernelGGL(bin_scatter_kernel<3>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, r, b.key, b.rank,
                            b.cell_start, tile_info, b.slot, b.sorted, status);

@@ -60,6 +60,33 @@ __device__ __forceinline__ bool axis_stencil(float x, float nf, float dx, float 
 template <int DIM>
 __host__ __device__ constexpr int rec_floats() { return ((2 * DIM + DIM * DIM + 1) + 3) / 4 * 4; }
 
+// Local number of a cell inside its tile.  In 3D the cells are numbered x
+// fastest, then z, then y: with the binned layout a dense tile puts cell l on
+// lane ~l, and with this order the 64 lanes' node addresses in the 6x6x6 LDS
+// block (x, y, z strides 1, 6, 36) fall in distinct LDS banks, so the
+// stencil's LDS atomics run without bank conflicts (row-major order costs
+// twice as long per instruction on gfx950).  2D tiles are row-major.
+template <int DIM>
+__host__ __device__ __forceinline__ uint32_t tile_local(const uint32_t l[DIM])
+{
+    if constexpr (DIM == 3)
+        return l[0] + kTile * l[2] + kTile * kTile * l[1];
+    else
+        return l[0] + kTile * l[1];
+}
+
+template <int DIM>
+__host__ __device__ __forceinline__ void tile_local_inverse(uint32_t local, uint32_t l[DIM])
+{
+    l[0] = local % kTile;
+    if constexpr (DIM == 3) {
+        l[2] = (local / kTile) % kTile;
+        l[1] = local / (kTile * kTile);
+    } else {
+        l[1] = local / kTile;
+    }
+}
+
 struct RangesF {
     float max_mass, max_speed, max_affine;
 };
@@ -83,7 +110,7 @@ struct Fields {           // component-major particle arrays of n particles
 
 struct BinView {          // the workspace arrays, as typed device pointers
     uint32_t *cell_start, *cell_count, *tile_row_start, *item_start, *items, *meta, *key, *rank, *slot,
-        *tile_tmp, *scan_tmp, *tile_info;
+        *tile_tmp, *scan_tmp, *tile_info, *item_hist, *item_hist_start;
     float *sorted;
     int64_t n_cells, n_tiles, max_items, max_slots, n_fields;
 };

@@ -256,9 +256,8 @@ __device__ __forceinline__ void group_hoist(const float *rec, float nf, float dx
 
 struct TiledArgs {
     const float *sorted;
-    const uint32_t *cell_start, *tile_row_start, *items, *meta;
+    const uint32_t *items, *meta;
     uint32_t *cursor;
-    int64_t max_items;
     int n, ntx;
     float nf, dx, last_base, S;
     int64_t *grid;
@@ -268,32 +267,53 @@ struct TiledArgs {
 __global__ void reset_cursor_kernel(uint32_t *cursor) { *cursor = 0u; }
 
 template <int DIM>
-__global__ void __launch_bounds__(kWave) p2g_tiled_kernel(TiledArgs a)
+__global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+p2g_tiled_kernel(TiledArgs a)
 {
     using TS = TileShape<DIM>;
     constexpr int R = rec_floats<DIM>();
     constexpr int G = kGroup;
+    constexpr int kFlush = (TS::nodes + kWave - 1) / kWave;      // node-block entries per lane
     __shared__ double acc[TS::ch * TS::nodes];
-    __shared__ uint32_t item_sh;
     const int lane = threadIdx.x;
     const uint32_t n_items = a.meta[0];
     const int64_t nodes = DIM == 3 ? (int64_t)a.n * a.n * a.n : (int64_t)a.n * a.n;
 
+    // The block's local coordinates of the nodes this lane flushes (node
+    // lane + 64*m of the block), fixed for every item.
+    int fx[kFlush], fy[kFlush], fz[kFlush];
+#pragma unroll
+    for (int m = 0; m < kFlush; ++m) {
+        const int i = lane + kWave * m;
+        fx[m] = i % TS::side;
+        fy[m] = (i / TS::side) % TS::side;
+        fz[m] = DIM == 3 ? i / (TS::side * TS::side) : 0;
+    }
+    for (int i = lane; i < TS::ch * TS::nodes; i += kWave)
+        acc[i] = 0.0;
+    __syncthreads();
+
+    // Lane 0 fetches the next item index as soon as an item starts, and the
+    // next item's record is loaded before the current item's flush, so
+    // neither round trip stalls the wave between items.
+    const uint4 *items = reinterpret_cast<const uint4 *>(a.items);
+    uint32_t next = 0;
+    if (lane == 0)
+        next = atomicAdd(a.cursor, 1u);
+    uint32_t item = __builtin_amdgcn_readfirstlane(next);
+    uint4 rec_item = make_uint4(0u, 0u, 0u, 0u);
+    if (item < n_items)
+        rec_item = items[item];
     for (;;) {
-        if (lane == 0)
-            item_sh = atomicAdd(a.cursor, 1u);
-        __syncthreads();
-        const uint32_t item = item_sh;
-        __syncthreads();
         if (item >= n_items)
             break;
-        const uint32_t tile = a.items[item];
-        const uint32_t row0 = a.items[a.max_items + item];
-        const uint32_t first = a.cell_start[(int64_t)tile * TS::cells];
-        const uint32_t groups = (a.cell_start[(int64_t)(tile + 1) * TS::cells] - first) / G;
+        if (lane == 0)
+            next = atomicAdd(a.cursor, 1u);
+        const uint32_t tile = rec_item.x;
+        const uint32_t row0 = rec_item.y & 0xFFFFu, row1 = rec_item.y >> 16;
+        const uint32_t groups = rec_item.z;
         const uint32_t rows = (groups + kWave - 1) / kWave;
-        const uint32_t row1 = min(rows, row0 + (uint32_t)kRowsPerItem);
-        const int64_t row_base = (int64_t)a.tile_row_start[tile];
+        const int64_t row_base = (int64_t)rec_item.w;
         int torg[3] = { 0, 0, 0 };
         {
             uint32_t t = tile;
@@ -303,43 +323,23 @@ __global__ void __launch_bounds__(kWave) p2g_tiled_kernel(TiledArgs a)
                 t /= (uint32_t)a.ntx;
             }
         }
-        for (int i = lane; i < TS::ch * TS::nodes; i += kWave)
-            acc[i] = 0.0;
-        __syncthreads();
-
-        // Records of the next row are loaded right after the current row's
-        // are hoisted, so the loads overlap the node loop.  Rows below `rows`
-        // lie inside the tile's allocation, so the loads are in bounds even
-        // for lanes whose group index is past the tile's last group.
-        float4 buf[G][R / 4];
-        auto load_row = [&](uint32_t j) {
-            const int64_t slot0 = (row_base + j) * kRowSlots + lane;
-#pragma unroll
-            for (int k = 0; k < G; ++k) {
-                const float4 *src = reinterpret_cast<const float4 *>(a.sorted + (slot0 + k * kWave) * R);
-#pragma unroll
-                for (int q = 0; q < R / 4; ++q)
-                    buf[k][q] = src[q];
-            }
-        };
-        if (row0 < row1)
-            load_row(row0);
         for (uint32_t j = row0; j < row1; ++j) {
+            const int64_t slot0 = (row_base + j) * kRowSlots + lane;
             GroupHoist<DIM> h[G];
 #pragma unroll
             for (int k = 0; k < G; ++k) {
+                const float4 *src = reinterpret_cast<const float4 *>(a.sorted + (slot0 + k * kWave) * R);
                 float rec[R];
 #pragma unroll
                 for (int q = 0; q < R / 4; ++q) {
-                    rec[4 * q] = buf[k][q].x;
-                    rec[4 * q + 1] = buf[k][q].y;
-                    rec[4 * q + 2] = buf[k][q].z;
-                    rec[4 * q + 3] = buf[k][q].w;
+                    const float4 t = src[q];
+                    rec[4 * q] = t.x;
+                    rec[4 * q + 1] = t.y;
+                    rec[4 * q + 2] = t.z;
+                    rec[4 * q + 3] = t.w;
                 }
                 group_hoist<DIM>(rec, a.nf, a.dx, a.last_base, a.S, h[k]);
             }
-            if (j + 1 < row1)
-                load_row(j + 1);
             if ((uint32_t)lane * rows + j >= groups)        // this lane's group index: lane * rows + j
                 continue;
             // every record of the group is in one cell of this tile (binning's
@@ -378,46 +378,61 @@ __global__ void __launch_bounds__(kWave) p2g_tiled_kernel(TiledArgs a)
 #pragma unroll
                     for (int c = 0; c < nc; ++c) {
                         const int off = DIM == 3 ? (c * TS::side + b) * TS::side + aa : b * TS::side + aa;
-                        float wmS[G];
-                        double sum;
+                        // The node's (1+DIM) x G contributions are independent until
+                        // the per-channel sums; they are written phase by phase
+                        // (products, rounding, widening, sums) so that the chains
+                        // interleave instead of running back to back.
+                        float wmS[G], val[1 + DIM][G];
 #pragma unroll
                         for (int k = 0; k < G; ++k) {
                             wmS[k] = DIM == 3 ? mwxy[k] * h[k].wz[c] : mwxy[k];
-                            const double q = (double)rintf(wmS[k]);
-                            sum = k == 0 ? q : sum + q;
+                            val[0][k] = wmS[k];
                         }
-                        atomicAdd(&acc[lb + off], sum);
 #pragma unroll
-                        for (int d = 0; d < DIM; ++d) {
-                            double ps;
+                        for (int d = 0; d < DIM; ++d)
 #pragma unroll
                             for (int k = 0; k < G; ++k) {
                                 const float u = DIM == 3 ? t2[k][d] + h[k].cz[d][c] : t2[k][d];
-                                const double q = (double)rintf(wmS[k] * u);
-                                ps = k == 0 ? q : ps + q;
+                                val[1 + d][k] = wmS[k] * u;
                             }
-                            atomicAdd(&acc[(1 + d) * TS::nodes + lb + off], ps);
+                        double q[1 + DIM][G];
+#pragma unroll
+                        for (int ch = 0; ch < 1 + DIM; ++ch)
+#pragma unroll
+                            for (int k = 0; k < G; ++k)
+                                q[ch][k] = (double)rintf(val[ch][k]);
+#pragma unroll
+                        for (int ch = 0; ch < 1 + DIM; ++ch) {
+                            double sum = q[ch][0];
+#pragma unroll
+                            for (int k = 1; k < G; ++k)
+                                sum = sum + q[ch][k];
+                            atomicAdd(&acc[ch * TS::nodes + lb + off], sum);
                         }
                     }
                 }
         }
         __syncthreads();
-        for (int i = lane; i < TS::ch * TS::nodes; i += kWave) {
-            const double val = acc[i];
-            if (val == 0.0)
+        item = __builtin_amdgcn_readfirstlane(next);
+        if (item < n_items)
+            rec_item = items[item];
+        // Flush: every non-zero node sum goes to the grid with one 64-bit
+        // atomic, and the block is left zeroed for the next item.
+#pragma unroll
+        for (int m = 0; m < kFlush; ++m) {
+            const int i = lane + kWave * m;
+            if (i >= TS::nodes)
                 continue;
-            const int ch = i / TS::nodes;
-            int rem = i - ch * TS::nodes;
-            int gx, gy, gz = 0;
-            gx = torg[0] + rem % TS::side;
-            rem /= TS::side;
-            gy = torg[1] + rem % TS::side;
-            if constexpr (DIM == 3)
-                gz = torg[2] + rem / TS::side;
-            if (gx >= a.n || gy >= a.n || gz >= a.n)
-                continue;
+            const int gx = torg[0] + fx[m], gy = torg[1] + fy[m], gz = torg[2] + fz[m];
+            const bool in_grid = gx < a.n && gy < a.n && gz < a.n;
             const int64_t node = DIM == 3 ? ((int64_t)gz * a.n + gy) * a.n + gx : (int64_t)gy * a.n + gx;
-            atomic_add_i64(&a.grid[ch * nodes + node], (int64_t)val);
+#pragma unroll
+            for (int ch = 0; ch < TS::ch; ++ch) {
+                const double val = acc[ch * TS::nodes + i];
+                acc[ch * TS::nodes + i] = 0.0;
+                if (val != 0.0 && in_grid)
+                    atomic_add_i64(&a.grid[ch * nodes + node], (int64_t)val);
+            }
         }
         __syncthreads();
     }
@@ -502,12 +517,9 @@ hipError_t launch_p2g_tiled(int dim, int n, int frac_bits, const BinView &b, int
 {
     TiledArgs a;
     a.sorted = b.sorted;
-    a.cell_start = b.cell_start;
-    a.tile_row_start = b.tile_row_start;
     a.items = b.items;
     a.meta = b.meta;
     a.cursor = b.meta + 3;
-    a.max_items = b.max_items;
     a.n = n;
     a.ntx = n / kTile;
     a.nf = (float)n;

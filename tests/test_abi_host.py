@@ -81,7 +81,8 @@ def test_workspace_layout_is_disjoint_and_aligned():
             (lay.tile_row_start, 4 * (lay.n_tiles + 1)), (lay.item_start, 4 * (lay.n_tiles + 1)),
             (lay.items, 8 * lay.max_items), (lay.meta, 64), (lay.key, 4 * max(N, 1)), (lay.rank, 4 * max(N, 1)),
             (lay.slot, 4 * max(N, 1)), (lay.sorted, 4 * lay.n_fields * lay.max_slots),
-            (lay.tile_tmp, 8 * lay.n_tiles), (lay.tile_info, 16 * lay.n_tiles)])
+            (lay.tile_tmp, 12 * lay.n_tiles), (lay.tile_info, 16 * lay.n_tiles),
+            (lay.item_hist, 60 * ((lay.n_tiles + 255) // 256)), (lay.item_hist_start, 4 * (15 * ((lay.n_tiles + 255) // 256) + 1))])
         for (a, la), (b, _) in zip(spans, spans[1:]):
             assert a % 256 == 0 and a + la <= b
         assert spans[-1][0] + spans[-1][1] <= lay.total_bytes

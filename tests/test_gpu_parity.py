@@ -235,14 +235,22 @@ def test_binning_matches_oracle(mpm, oracle_lib, name, count):
     lay = tr.layout
     gcount = u32(tr.ws_u32("cell_count", lay.n_cells))
     gstart = u32(tr.ws_u32("cell_start", lay.n_cells + 1))
-    assert_same(gcount, cnt, "cell counts")
+    per = 4 ** w.dim
+    # the library numbers the cells of a 3D tile x fastest, then z, then y; the
+    # oracle row-major: map library keys to oracle keys before comparing
+    local = np.arange(per)
+    lx, ly, lz = local % 4, (local // 16) if w.dim == 3 else local // 4, (local // 4) % 4
+    oracle_local = lx + 4 * ly + 16 * lz if w.dim == 3 else local
+    to_oracle = (np.arange(lay.n_cells) // per) * per + oracle_local[np.arange(lay.n_cells) % per]
+    assert_same(gcount, cnt[to_oracle], "cell counts")
     # the library's cell starts are the prefix sums of counts padded to whole groups of 4 records
-    padded = (cnt.astype(np.int64) + 3) // 4 * 4
+    padded = (gcount.astype(np.int64) + 3) // 4 * 4
     assert_same(gstart.astype(np.int64), np.concatenate([[0], np.cumsum(padded)]), "padded cell starts")
     meta = tr.meta()
     rows_total, items = int(meta[1]), int(meta[0])
     assert int(meta[2]) == len(order) and int(meta[4]) == int(padded.sum())
     trs = u32(tr.ws_u32("tile_row_start", lay.n_tiles + 1)).astype(np.int64)
+    ostart = start.astype(np.int64)
     slot_of = u32(tr.ws_u32("slot", w.n_particles)).astype(np.int64)
     assert np.all(slot_of[order] != 0xFFFFFFFF)
     gorder = np.full(rows_total * 256, 0xFFFFFFFF, dtype=np.int64)   # slot -> particle
@@ -251,13 +259,25 @@ def test_binning_matches_oracle(mpm, oracle_lib, name, count):
     assert np.all(slot_of[binned_idx] < rows_total * 256)
     gorder[slot_of[binned_idx]] = binned_idx
     assert len(np.unique(slot_of[binned_idx])) == len(binned_idx)
-    per = 4 ** w.dim
     gs = gstart.astype(np.int64)
     tile_pad = gs[per::per] - gs[:-1:per]
     groups = tile_pad // 4
     rows = (groups + 63) // 64
     assert np.array_equal(np.diff(trs), rows) and int(trs[-1]) == rows_total
     assert items == int(np.sum((rows + 15) // 16))
+    # work items: every (tile, first row) exactly once, handed out alternately from the
+    # large and the small end of the size order
+    it = u32(tr.ws_u32("items", 4 * lay.max_items)).astype(np.int64).reshape(-1, 4)[:items]
+    it_tile, it_row, it_end = it[:, 0], it[:, 1] & 0xFFFF, it[:, 1] >> 16
+    want = sorted((int(t), int(r0)) for t in np.nonzero(rows)[0] for r0 in range(0, int(rows[t]), 16))
+    assert sorted(zip(it_tile.tolist(), it_row.tolist())) == want
+    assert np.array_equal(it_end, np.minimum(it_row + 16, rows[it_tile]))
+    assert np.array_equal(it[:, 2], groups[it_tile]) and np.array_equal(it[:, 3], trs[it_tile])
+    size = it_end - it_row
+    big, small = size[0::2], size[1::2]
+    assert np.all(np.diff(big) <= 0) and np.all(np.diff(small) >= 0)
+    if len(small):
+        assert big[-1] >= small[-1]
     sorted_f = tr.ws.view(torch.float32)[lay.sorted // 4: lay.sorted // 4 + lay.n_fields * lay.max_slots]
     rec = sorted_f.view(lay.max_slots, lay.n_fields)[: rows_total * 256].cpu().numpy()
     src = np.concatenate([host["x"], host["v"], host["C"], host["m"][None]])
@@ -272,19 +292,19 @@ def test_binning_matches_oracle(mpm, oracle_lib, name, count):
         c0 = t * per
         for c in range(c0, c0 + per):
             a = int(gs[c] - gs[c0])
-            n_c = int(cnt[c])
+            n_c = int(gcount[c])
+            oc = int(to_oracle[c])
             got = seq[a:a + n_c]
-            assert np.array_equal(np.sort(got), np.sort(order[start[c]:start[c + 1]]))
+            assert np.array_equal(np.sort(got), np.sort(order[ostart[oc]:ostart[oc + 1]]))
             pads = slot[a + n_c:int(gs[c + 1] - gs[c0])]
             assert np.all(gorder[pads] == 0xFFFFFFFF)
             if len(pads):
                 pr = rec[pads]                               # zero mass, velocity and affine matrix
                 assert np.all(pr[:, w.dim:nf] == 0)
-                tile_id, local, centre = int(t), c - c0, []
+                tile_id, loc, centre = int(t), [int(lx[c - c0]), int(ly[c - c0]), int(lz[c - c0])], []
                 for e in range(w.dim):                       # pads sit at the cell centre, g = base + 1
-                    centre.append(((tile_id % (w.n // 4)) * 4 + local % 4 + 1) / w.n)
+                    centre.append(((tile_id % (w.n // 4)) * 4 + loc[e] + 1) / w.n)
                     tile_id //= w.n // 4
-                    local //= 4
                 assert np.all(pr[:, :w.dim] == np.array(centre, np.float32)[None, :])
         seen[seq[seq != 0xFFFFFFFF]] += 1
     assert np.all(seen[order] == 1) and seen.sum() == len(order)
