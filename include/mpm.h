@@ -91,23 +91,27 @@ typedef struct {
  * writes, so that callers and tests can read them.  Counts are the
  * capacities allocated, not what one call fills. */
 typedef struct {
-    size_t cell_start;      /* uint32 [n_cells + 1] exclusive prefix sum of per-cell counts,
-                                        each rounded up to a multiple of 4 (record groups) */
-    size_t cell_count;      /* uint32 [n_cells]     per-cell particle counts                    */
-    size_t tile_row_start;  /* uint32 [n_tiles + 1] first 256-slot row of each tile             */
+    size_t tile_count;      /* uint32 [n_tiles]     binned particles per tile                    */
+    size_t tile_start;      /* uint32 [n_tiles + 1] first record of each tile (exclusive prefix sum) */
+    size_t tile_row_start;  /* uint32 [n_tiles + 1] first row of group entries of each tile      */
     size_t item_start;      /* uint32 [n_tiles + 1] first full P2G work item of each tile       */
     size_t items;           /* uint32 [max_items][4] work items: tile, first row | end row << 16,
-                                        groups of the tile, first row of the tile; handed
-                                        out alternately the largest and smallest remaining */
+                                        group bound of the tile, first row of the tile;
+                                        handed out alternately the largest and smallest
+                                        remaining */
     size_t meta;            /* uint32 [16]: [0] items, [1] rows, [2] binned particles,
-                                        [3] P2G work cursor, [4] record slots incl. pads */
-    size_t key;             /* uint32 [n] cell key of each particle (0xFFFFFFFF when skipped)   */
-    size_t rank;            /* uint32 [n] arrival rank of each particle inside its cell         */
-    size_t slot;            /* uint32 [n] record slot of each particle (0xFFFFFFFF: not binned) */
-    size_t sorted;          /* float  [max_slots][n_fields] binned records x, v, C, m, padding  */
+                                        [3] P2G work cursor, [4] group entries (rows * 256) */
+    size_t rank;            /* uint32 [n] rank of each particle inside its tile (internal)      */
+    size_t slot;            /* uint32 [n] record index of each particle (0xFFFFFFFF: not binned) */
+    size_t cell_key;        /* uint8  [n] local cell number of each record, in record order      */
+    size_t perm;            /* uint32 [max_slots] group entries: rows of 64 lanes x 4 entries; an
+                                        entry is a record index, with bit 31 set when it
+                                        completes a cell's last group (read with zero mass);
+                                        0xFFFFFFFF in a group's first entry: no group      */
+    size_t sorted;          /* float  [n][n_fields] binned records x, v, C, m (+ padding floats),
+                                        tile by tile                                       */
     size_t tile_tmp;        /* uint32 [3][n_tiles] per-tile rows, full items, partial item (internal) */
     size_t scan_tmp;        /* uint32 [scan_blocks] prefix-sum block totals (internal)          */
-    size_t tile_info;       /* uint32 [n_tiles][4]: padded first position, rows, first row, 0  */
     size_t item_hist;       /* uint32 [15][ceil(n_tiles/256)] partial-item sizes per block (internal) */
     size_t item_hist_start; /* uint32 prefix sum of item_hist (internal)                          */
     int64_t n_cells, n_tiles, max_items, max_slots, n_fields, rows_per_item;
@@ -141,17 +145,17 @@ int mpm_workspace_bytes(const mpm_grid_desc *grid, int64_t n_particles, size_t *
 /* Offsets of the arrays inside that workspace (host-only). */
 int mpm_workspace_layout(const mpm_grid_desc *grid, int64_t n_particles, mpm_ws_layout *layout);
 
-/* Counting sort of the particles into tiles of 4^dim cells, keyed by the
- * stencil's base cell and numbered tile by tile (inside a 3D tile x fastest,
- * then z, then y) ("Particle worlds, part 3",
- * steps 3-4: histogram, exclusive prefix sum, scatter; "Implementation --
- * GPU Optimization & Reference Codebases", section 2.1: sort + tile).  The
- * caller's arrays are not reordered (section 5 rule 2): the workspace
- * receives the cell histogram and prefix sum, per-tile rows, the P2G work
- * items, each particle's record slot and a binned copy of x, v, C, m:
- * 64-byte records (48 in 2D), each cell padded with zero-mass records to a
- * multiple of 4, in groups of 4 same-cell records, one group per lane of a
- * 256-slot row.  Particles whose stencil leaves the grid are not binned and
+/* Counting sort of the particles into tiles of 4^dim cells by the stencil's
+ * base cell ("Particle worlds, part 3", steps 3-4: histogram, exclusive
+ * prefix sum, scatter; "Implementation -- GPU Optimization & Reference
+ * Codebases", section 2.1: sort + tile).  The caller's arrays are not
+ * reordered (section 5 rule 2): the workspace receives the tile histogram
+ * and prefix sum, each particle's record index, a binned copy of x, v, C, m
+ * (64-byte records, 48 in 2D) tile by tile, and for each tile its records
+ * sorted by cell (inside a 3D tile cells are numbered x fastest, then z,
+ * then y) as groups of 4 same-cell entries, each cell completed to a
+ * multiple of 4 by pad entries, one group per lane of a 256-entry row; and
+ * the P2G work items.  Particles whose stencil leaves the grid are not binned and
  * are counted in status[0]; particles whose attributes leave the declared
  * ranges are binned as zero-mass records (they contribute nothing, exactly
  * as if skipped) and counted in status[1].  Arrival order inside a cell is

@@ -30,6 +30,9 @@ namespace {
 
 using namespace mpmk;
 
+// Binned group entries hold a record index below 2^31 (bit 31 flags pads).
+constexpr int64_t kMaxParticles = 0x7FFFFFF0;
+
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
 bool aligned(const void *p, size_t a) { return p != nullptr && ((uintptr_t)p % a) == 0; }
@@ -104,14 +107,18 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     const int64_t n_cells = pow_int(g->n, g->dim);
     const int64_t n_tiles = pow_int(g->n / kTile, g->dim);
     const int64_t busy = np < n_tiles ? (np > 0 ? np : 1) : n_tiles;       // tiles that can hold particles
-    // every non-empty cell adds at most kGroup-1 pad records, every non-empty
-    // tile at most one partly filled row
-    const int64_t busy_cells = np < n_cells ? np : n_cells;
-    const int64_t max_rows = (np + (kGroup - 1) * busy_cells + kRowSlots - 1) / kRowSlots + busy;
-    const int64_t max_items = (max_rows + kRowsPerItem - 1) / kRowsPerItem + busy;
+    // work items: every non-empty tile's records cut into slices, all full
+    // but the last; each item's occupied cells (at most min(records, cells))
+    // add at most kGroup-1 pad entries each, and each item at most one partly
+    // filled row
+    const int64_t slice = g->dim == 3 ? slice_records<3>() : slice_records<2>();
+    const int64_t cells = g->dim == 3 ? cells_per_tile<3>() : cells_per_tile<2>();
+    const int64_t max_items = np / slice + busy;
+    const int64_t pads = (kGroup - 1) * (np < cells * max_items ? np : cells * max_items);
+    const int64_t max_rows = (np + pads + kRowSlots - 1) / kRowSlots + max_items;
     const int64_t n_fields = g->dim == 3 ? rec_floats<3>() : rec_floats<2>();
-    const int64_t big = n_cells > n_tiles ? n_cells : n_tiles;   // (the item histogram is shorter than n_tiles)
-    const int64_t scan_blocks = (big + kScanTileElems - 1) / kScanTileElems + 1;
+    // (the item histogram is shorter than n_tiles)
+    const int64_t scan_blocks = (n_tiles + kScanTileElems - 1) / kScanTileElems + 1;
     size_t off = 0;
     auto take = [&off](size_t bytes) {
         const size_t at = off;
@@ -120,20 +127,20 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     };
     const size_t u4 = sizeof(uint32_t);
     const int64_t n1 = np > 0 ? np : 1;
-    o->cell_start = take(u4 * (size_t)(n_cells + 1));
-    o->cell_count = take(u4 * (size_t)n_cells);
+    o->tile_count = take(u4 * (size_t)n_tiles);
+    o->tile_start = take(u4 * (size_t)(n_tiles + 1));
     o->tile_row_start = take(u4 * (size_t)(n_tiles + 1));
     o->item_start = take(u4 * (size_t)(n_tiles + 1));
     o->items = take(u4 * 4 * (size_t)max_items);
     o->meta = take(u4 * 16);
-    o->key = take(u4 * (size_t)n1);
     o->rank = take(u4 * (size_t)n1);
     o->slot = take(u4 * (size_t)n1);
-    o->sorted = take(sizeof(float) * (size_t)(n_fields * max_rows * kRowSlots));
+    o->cell_key = take((size_t)n1);
+    o->perm = take(u4 * (size_t)(max_rows * kRowSlots));
+    o->sorted = take(sizeof(float) * (size_t)(n_fields * n1));
     o->tile_tmp = take(u4 * 3 * (size_t)n_tiles);
     o->scan_tmp = take(u4 * (size_t)scan_blocks);
-    o->tile_info = take(u4 * 4 * (size_t)n_tiles);
-    const int64_t hist_len = (kRowsPerItem - 1) * ((n_tiles + 255) / 256);
+    const int64_t hist_len = kRowsPerItem * ((n_tiles + 255) / 256);
     o->item_hist = take(u4 * (size_t)hist_len);
     o->item_hist_start = take(u4 * (size_t)(hist_len + 1));
     o->n_cells = n_cells;
@@ -149,19 +156,19 @@ BinView bin_view(void *ws, const mpm_ws_layout &l)
 {
     char *b = (char *)ws;
     BinView v;
-    v.cell_start = (uint32_t *)(b + l.cell_start);
-    v.cell_count = (uint32_t *)(b + l.cell_count);
+    v.tile_count = (uint32_t *)(b + l.tile_count);
+    v.tile_start = (uint32_t *)(b + l.tile_start);
     v.tile_row_start = (uint32_t *)(b + l.tile_row_start);
     v.item_start = (uint32_t *)(b + l.item_start);
     v.items = (uint32_t *)(b + l.items);
     v.meta = (uint32_t *)(b + l.meta);
-    v.key = (uint32_t *)(b + l.key);
     v.rank = (uint32_t *)(b + l.rank);
     v.slot = (uint32_t *)(b + l.slot);
+    v.cell_key = (uint8_t *)(b + l.cell_key);
+    v.perm = (uint32_t *)(b + l.perm);
     v.sorted = (float *)(b + l.sorted);
     v.tile_tmp = (uint32_t *)(b + l.tile_tmp);
     v.scan_tmp = (uint32_t *)(b + l.scan_tmp);
-    v.tile_info = (uint32_t *)(b + l.tile_info);
     v.item_hist = (uint32_t *)(b + l.item_hist);
     v.item_hist_start = (uint32_t *)(b + l.item_hist_start);
     v.n_cells = l.n_cells;
@@ -174,7 +181,7 @@ BinView bin_view(void *ws, const mpm_ws_layout &l)
 
 int check_particles(const mpm_grid_desc *g, const mpm_particles *p, bool need_arrays, bool need_mass)
 {
-    if (!p || p->n < 0 || p->n > (int64_t)0xFFFFFFF0)
+    if (!p || p->n < 0 || p->n > kMaxParticles)
         return MPM_ERR_INVALID;
     if (!need_arrays || p->n == 0)
         return MPM_OK;
@@ -227,7 +234,7 @@ int mpm_check_bounds(const mpm_grid_desc *grid, int64_t n_particles, const mpm_r
 
 int mpm_workspace_layout(const mpm_grid_desc *grid, int64_t n_particles, mpm_ws_layout *layout)
 {
-    if (check_desc(grid) != MPM_OK || n_particles < 0 || n_particles > (int64_t)0xFFFFFFF0 || !layout)
+    if (check_desc(grid) != MPM_OK || n_particles < 0 || n_particles > kMaxParticles || !layout)
         return MPM_ERR_INVALID;
     make_layout(grid, n_particles, layout);
     return MPM_OK;

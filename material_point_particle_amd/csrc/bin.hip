@@ -1,34 +1,44 @@
 // bin.hip -- counting sort of particles into tiles of 4^dim cells (gfx950).
 //
-// "Particle worlds, part 3" (steps 3 and 4): a histogram of cell numbers, an
-// exclusive prefix sum, and a scatter of each particle to its slot; the
+// "Particle worlds, part 3" (steps 3 and 4): a histogram of keys, an
+// exclusive prefix sum, and a scatter of each particle to its place; the
 // implementation page's section 2.1 bins particles into tiles every substep
 // and builds an index table so the particle arrays themselves never move.
+// Here the sort is two-level: particles are counting-sorted by tile, and the
+// cells inside each tile are sorted on chip.
 //
 // Passes (all on the caller's stream, no host synchronisation):
-//   1. count    one thread per particle: base cell -> tile-major cell key;
-//               atomic increment of the cell's counter returns the particle's
-//               arrival rank inside the cell.
-//   2. scan     exclusive prefix sum of the cell counters, each rounded up to
-//               a multiple of kGroup (three phases: per-block sums, one block
-//               scans the sums, per-block rescan).
-//   3. layout   per tile: rows of kRowSlots record slots (one group of kGroup
-//               same-cell records per lane), full P2G work items of
-//               kRowsPerItem rows and a partial last item; rows and full items
-//               prefix-summed over tiles, partial items counting-sorted by
-//               size (largest first).
-//   4. items    the (tile, first row) of every work item, alternately from the
-//               large and the small end of the size order; and a compact
-//               (first position, rows, first row) record per tile.
-//   5. scatter  one thread per particle: its slot in the tile's grouped,
-//               transposed layout (group g of a tile with R rows sits in lane
-//               g / R of row g % R); the particle's slot and a record of
-//               the particle's fields (x, v, C, m: 64 bytes in 3D) are written
-//               there, so each scattered write is one whole record.
-//   6. pad      one thread per cell: zero-mass records complete the cell's
-//               last group.
-// Arrival ranks depend on scheduling, so slot contents differ between runs;
-// every group holds kGroup records of one cell, which is all P2G needs.
+//   1. count    blocks of up to 65,536 consecutive particles (a chunk): each
+//               particle's base cell gives its tile; an LDS hash table counts
+//               the chunk's particles per tile, then one global atomic per
+//               (chunk, tile) reserves the chunk's run inside the tile, so a
+//               particle's rank in its tile is its run's base plus its rank
+//               in the chunk.
+//   2. scan     exclusive prefix sum of the tile counts: each tile's first
+//               record.
+//   3. layout   each tile's records are cut into slices of at most
+//               slice_records(), one P2G work item each, whose groups of
+//               kGroup same-cell entries fill at most kRowsPerItem rows of
+//               kRowSlots entries (one group per lane; the rows are sized from
+//               the slice's count alone, an upper bound on its padded groups);
+//               rows and full slices prefix-summed over tiles, partial slices
+//               counting-sorted by rows.
+//   4. items    the 16-byte record of every work item, alternately from the
+//               large and the small end of the size order.
+//   5. scatter  the same chunks as pass 1: each particle's 64-byte record
+//               (x, v, C, m in 3D) goes to its tile's record range at its
+//               rank, with the cell's local number beside it.  A chunk's
+//               particles of one tile land in one contiguous run.
+//   6. groups   one block per work item: the slice's records are
+//               counting-sorted by cell in LDS and their indices written as
+//               group entries in the item's rows, transposed (group g of an
+//               item with R rows sits in lane g / R of row g % R); entries
+//               that complete a cell's last group name one of the cell's
+//               records with the pad flag (P2G reads it with zero mass),
+//               groups past the last are marked empty.
+// Arrival ranks depend on scheduling, so record order inside a tile differs
+// between runs; every group holds kGroup entries of one cell, which is all
+// P2G needs.
 #include "common.hpp"
 
 namespace mpmk {
@@ -200,256 +210,321 @@ hipError_t exclusive_scan(const uint32_t *in, int64_t len, uint32_t *out, uint32
     return hipGetLastError();
 }
 
-// Pass 1: cell key (tile, then the cell's local number, see tile_local) from
-// the position only; particles whose stencil leaves the
-// grid are counted and not binned.  The attribute range check happens in the
-// scatter pass, which reads the attributes anyway.
-//
-// Blocks visit 256-particle chunks in the order chunk = (i * stride) mod
-// chunks (stride a prime not dividing the chunk count), so the blocks that
-// run at the same time hold particles from all over the caller's array.
-// Input arrays often list particles region by region (a generator filling one
-// blob or block after another); visiting them in order would aim every
-// concurrent atomic at the few cells of one region and serialise them.
+// Passes 1 and 5 visit the same chunks of kBinThreads * per consecutive
+// particles (per <= kMaxPer, chosen per launch so that every CU gets chunks),
+// one block per chunk.
+constexpr int kBinThreads = 1024;
+constexpr int kMaxPer = 64;                          // a chunk holds at most 65,536 particles
+constexpr int kHashBits = 11;
+constexpr int kHashSlots = 1 << kHashBits;           // tiles per chunk counted in LDS
+constexpr int kMaxProbes = 64;
+constexpr uint32_t kLocalRank = 0x80000000u;         // rank_out holds (slot << 16) | rank in the chunk
+static_assert(kBinThreads * kMaxPer <= 65536, "a rank inside the chunk must fit 16 bits");
+
+// Tile and local cell number (see tile_local) of the particle's base cell;
+// false when its stencil leaves the grid.
 template <int DIM>
-__global__ void __launch_bounds__(256) bin_count_kernel(Fields f, float nf, float dx, float last_base, int ntx,
-                                                         uint32_t *__restrict__ cell_count,
-                                                         uint32_t *__restrict__ key_out,
-                                                         uint32_t *__restrict__ rank_out,
-                                                         uint32_t *__restrict__ status, uint32_t *__restrict__ meta,
-                                                         int64_t chunks, int64_t stride)
+__device__ __forceinline__ bool particle_cell(const float *x, float nf, float dx, float last_base, int ntx,
+                                              uint32_t &tile, uint32_t &local)
 {
-    constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
+    bool dom = true;
+    int base[DIM];
+#pragma unroll
+    for (int e = 0; e < DIM; ++e) {
+        Axis ax;
+        dom = axis_stencil(x[e], nf, dx, last_base, ax) && dom;
+        base[e] = ax.base;
+    }
+    uint32_t t = 0, l[DIM];
+#pragma unroll
+    for (int e = DIM - 1; e >= 0; --e) {
+        t = t * (uint32_t)ntx + (uint32_t)(base[e] / kTile);
+        l[e] = (uint32_t)(base[e] % kTile);
+    }
+    tile = t;
+    local = tile_local<DIM>(l);
+    return dom;
+}
+
+// Pass 1.  Particles whose stencil leaves the grid are counted (status[0])
+// and not binned; the attribute range check happens in pass 5, which reads
+// the attributes anyway.  An LDS hash table counts the chunk's particles per
+// tile; after the chunk, one global atomic per table entry reserves the
+// chunk's run inside the tile, and each particle's rank becomes the run's
+// base plus its rank in the chunk.  A particle whose tile finds no table
+// entry within kMaxProbes probes takes a rank of its own with a global atomic.
+// Input that lists particles region by region (as generators and simulations
+// usually leave it) touches few tiles per chunk, so the global atomics number
+// a few hundred per chunk, and each tile's records from one chunk form one
+// contiguous run for pass 5 to write.  Inside a run the records keep their
+// arrival order, so records written close together in time are neighbours in
+// memory.
+template <int DIM>
+__global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, float nf, float dx, float last_base,
+                                                                      int ntx, int64_t chunks, int per,
+                                                                      uint32_t *__restrict__ tile_count,
+                                                                      uint32_t *__restrict__ rank_out,
+                                                                      uint32_t *__restrict__ status,
+                                                                      uint32_t *__restrict__ meta)
+{
+    __shared__ uint32_t hkey[kHashSlots];
+    __shared__ uint32_t hval[kHashSlots];     // count in the chunk, then the chunk's base in the tile
+    for (int e = threadIdx.x; e < kHashSlots; e += kBinThreads) {
+        hkey[e] = kEmpty;
+        hval[e] = 0u;
+    }
+    __syncthreads();
     uint32_t binned = 0;
-    for (int64_t i = blockIdx.x; i < chunks; i += gridDim.x) {
-        const int64_t p = ((i * stride) % chunks) * 256 + threadIdx.x;
-        if (p >= f.n)
-            continue;
-        bool dom = true;
-        int base[DIM];
+    const int64_t chunk = (int64_t)kBinThreads * per;
+    for (int64_t c = blockIdx.x; c < chunks; c += gridDim.x) {
+        const int64_t p0 = c * chunk + threadIdx.x;
+        for (int k0 = 0; k0 < per; k0 += 4) {
+            float xs[4][DIM];
 #pragma unroll
-        for (int e = 0; e < DIM; ++e) {
-            Axis ax;
-            dom = axis_stencil(f.x[e * f.n + p], nf, dx, last_base, ax) && dom;
-            base[e] = ax.base;
-        }
-        wave_count(!dom, &status[0]);
-        binned += dom ? 1u : 0u;
-        uint32_t key = kEmpty, rank = 0;
-        if (dom) {
-            uint32_t t = 0, l[DIM];
+            for (int j = 0; j < 4; ++j) {
+                const int64_t p = p0 + (int64_t)(k0 + j) * kBinThreads;
 #pragma unroll
-            for (int e = DIM - 1; e >= 0; --e) {
-                t = t * (uint32_t)ntx + (uint32_t)(base[e] / kTile);
-                l[e] = (uint32_t)(base[e] % kTile);
+                for (int e = 0; e < DIM; ++e)
+                    xs[j][e] = (k0 + j < per && p < f.n) ? f.x[e * f.n + p] : 0.0f;
             }
-            key = t * per_tile + tile_local<DIM>(l);
-            rank = atomicAdd(&cell_count[key], 1u);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t p = p0 + (int64_t)(k0 + j) * kBinThreads;
+                const bool live = k0 + j < per && p < f.n;
+                uint32_t t = 0, l = 0;
+                const bool dom = live && particle_cell<DIM>(xs[j], nf, dx, last_base, ntx, t, l);
+                wave_count(live && !dom, &status[0]);
+                if (!live)
+                    continue;
+                uint32_t v = 0u;
+                if (dom) {
+                    uint32_t h = (t * 0x9E3779B1u) >> (32 - kHashBits);
+                    bool found = false;
+                    for (int probe = 0; probe < kMaxProbes; ++probe) {
+                        const uint32_t old = atomicCAS(&hkey[h], kEmpty, t);
+                        if (old == kEmpty || old == t) {
+                            found = true;
+                            break;
+                        }
+                        h = (h + 1u) & (kHashSlots - 1);
+                    }
+                    v = found ? kLocalRank | (h << 16) | atomicAdd(&hval[h], 1u) : atomicAdd(&tile_count[t], 1u);
+                    ++binned;
+                }
+                rank_out[p] = v;
+            }
         }
-        key_out[p] = key;
-        rank_out[p] = rank;
+        __syncthreads();
+        for (int e = threadIdx.x; e < kHashSlots; e += kBinThreads) {
+            const uint32_t key = hkey[e];
+            if (key != kEmpty)
+                hval[e] = atomicAdd(&tile_count[key], hval[e]);
+        }
+        __syncthreads();
+        for (int k = 0; k < per; ++k) {            // the thread's own writes above: no fence needed
+            const int64_t p = p0 + (int64_t)k * kBinThreads;
+            if (p >= f.n)
+                break;
+            const uint32_t v = rank_out[p];
+            if (v & kLocalRank)
+                rank_out[p] = hval[(v >> 16) & (kHashSlots - 1)] + (v & 0xFFFFu);
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < kHashSlots; e += kBinThreads) {
+            hkey[e] = kEmpty;
+            hval[e] = 0u;
+        }
+        __syncthreads();
     }
     // one atomic per block for the binned-particle total (a per-wave atomic on
     // one address from every wave of the grid would serialise)
     __shared__ uint32_t total;
-    (void)block_exclusive_scan<256>(binned, &total);
+    (void)block_exclusive_scan<kBinThreads>(binned, &total);
     if (threadIdx.x == 0 && total != 0u)
         atomicAdd(&meta[2], total);
 }
 
-// Pass 3: per tile, rows of kRowSlots record slots (one group of kGroup
-// records per lane), its number of full work items (kRowsPerItem rows each)
-// and the size of its last, partial item.  P2G hands items out dynamically;
-// the items are ordered by size (all full items, then the partial items by
-// decreasing size) and handed out alternately from both ends of that order
-// (see items_kernel).  The partial sizes are counting-sorted: one block of 256 tiles counts them per
-// size in LDS (the returned count is the tile's rank within the block) and
-// writes its histogram, size-major, for a prefix sum.  One thread per tile.
+// Pass 3: each tile's records are cut into slices of slice_records() (the
+// last one shorter), one P2G work item each; a slice's groups fill at most
+// kRowsPerItem rows.  Per tile: its rows, its full slices and the rows of
+// its last, partial slice.  P2G hands items out dynamically; the items are
+// ordered by size (all full slices, then the partial slices by decreasing
+// rows) and handed out alternately from both ends of that order (see
+// items_kernel).  The partial slices are counting-sorted by rows: one block of
+// 256 tiles counts them per row count in LDS (the returned count is the
+// tile's rank within the block) and writes its histogram, size-major, for a
+// prefix sum.  One thread per tile.
 template <int DIM>
-__global__ void __launch_bounds__(256) tile_layout_kernel(const uint32_t *__restrict__ cell_start, int64_t n_tiles,
+__global__ void __launch_bounds__(256) tile_layout_kernel(const uint32_t *__restrict__ tile_count, int64_t n_tiles,
                                                            uint32_t *__restrict__ tile_rows,
                                                            uint32_t *__restrict__ tile_full,
                                                            uint32_t *__restrict__ tile_part,
                                                            uint32_t *__restrict__ item_hist)
 {
-    constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
-    __shared__ uint32_t hist[kRowsPerItem];
-    if (threadIdx.x < kRowsPerItem)
+    constexpr uint32_t S = slice_records<DIM>();
+    __shared__ uint32_t hist[kRowsPerItem + 1];
+    if (threadIdx.x <= kRowsPerItem)
         hist[threadIdx.x] = 0u;
     __syncthreads();
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    uint32_t part = 0, rank = 0;
     if (t < n_tiles) {
-        const uint32_t padded = cell_start[(t + 1) * per_tile] - cell_start[t * per_tile];
-        const uint32_t rows = (padded + kRowSlots - 1) / kRowSlots;
-        part = rows % kRowsPerItem;
-        tile_rows[t] = rows;
-        tile_full[t] = rows / kRowsPerItem;
+        const uint32_t c = tile_count[t];
+        const uint32_t full = c / S, rem = c % S;
+        const uint32_t part = rem != 0u ? rows_bound<DIM>(rem) : 0u;      // 1 .. kRowsPerItem
+        uint32_t rank = 0;
+        tile_rows[t] = full * kRowsPerItem + part;
+        tile_full[t] = full;
         if (part != 0u)
             rank = atomicAdd(&hist[part], 1u);
         tile_part[t] = (part << 16) | rank;
     }
     __syncthreads();
-    // row (kRowsPerItem - 1 - size) of the size-major histogram: largest size first
-    if (threadIdx.x >= 1 && threadIdx.x < kRowsPerItem)
-        item_hist[(int64_t)(kRowsPerItem - 1 - threadIdx.x) * gridDim.x + blockIdx.x] = hist[threadIdx.x];
+    // row (kRowsPerItem - rows) of the size-major histogram: largest first
+    if (threadIdx.x >= 1 && threadIdx.x <= kRowsPerItem)
+        item_hist[(int64_t)(kRowsPerItem - threadIdx.x) * gridDim.x + blockIdx.x] = hist[threadIdx.x];
 }
 
-// Pass 4: the work items of each tile, and a compact per-tile record
-// (padded first position, rows, first row) for the scatter pass.
+// Pass 4: the work items of each tile.  One 16-byte record per item: tile,
+// first record, records, first row of its group entries.
 template <int DIM>
-__global__ void __launch_bounds__(256) items_kernel(const uint32_t *__restrict__ tile_rows,
-                                                     const uint32_t *__restrict__ tile_full,
+__global__ void __launch_bounds__(256) items_kernel(const uint32_t *__restrict__ tile_full,
                                                      const uint32_t *__restrict__ tile_part,
                                                      const uint32_t *__restrict__ full_start,
                                                      const uint32_t *__restrict__ hist_start,
                                                      const uint32_t *__restrict__ tile_row_start,
-                                                     const uint32_t *__restrict__ cell_start, int64_t n_tiles,
-                                                     int64_t layout_blocks, uint4 *__restrict__ items,
-                                                     uint4 *__restrict__ tile_info)
+                                                     const uint32_t *__restrict__ tile_start, int64_t n_tiles,
+                                                     int64_t layout_blocks, uint4 *__restrict__ items)
 {
-    constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
+    constexpr uint32_t S = slice_records<DIM>();
     const uint32_t n_full = full_start[n_tiles];
-    const uint32_t total = n_full + hist_start[(int64_t)(kRowsPerItem - 1) * layout_blocks];
+    const uint32_t total = n_full + hist_start[(int64_t)kRowsPerItem * layout_blocks];
     // p is an item's position in the size-sorted list; the items are handed
     // out alternately from its two ends (largest, smallest, second largest,
     // ...), so long and short items run side by side on every CU and the last
     // items handed out are short.
     auto place = [&](uint32_t p) { return p < (total + 1) / 2 ? 2 * p : 2 * (total - 1 - p) + 1; };
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n_tiles; t += (int64_t)gridDim.x * blockDim.x) {
-        // one 16-byte record per item: tile, first row | end row << 16,
-        // groups of the tile, first row of the tile in the binned copy
-        const uint32_t k = tile_full[t], s0 = full_start[t], rows = tile_rows[t];
-        const uint32_t groups = (cell_start[(t + 1) * per_tile] - cell_start[t * per_tile]) / kGroup;
+        const uint32_t k = tile_full[t], s0 = full_start[t];
+        const uint32_t c0 = tile_start[t], count = tile_start[t + 1] - c0;
         const uint32_t base = tile_row_start[t];
         for (uint32_t c = 0; c < k; ++c)
-            items[place(s0 + c)] = make_uint4((uint32_t)t, (c * kRowsPerItem) | ((c + 1) * kRowsPerItem << 16),
-                                              groups, base);
+            items[place(s0 + c)] = make_uint4((uint32_t)t, c0 + c * S, S, base + c * kRowsPerItem);
         const uint32_t part = tile_part[t] >> 16;
         if (part != 0u) {
-            const uint32_t q = place(n_full + hist_start[(int64_t)(kRowsPerItem - 1 - part) * layout_blocks + t / 256] +
+            const uint32_t q = place(n_full + hist_start[(int64_t)(kRowsPerItem - part) * layout_blocks + t / 256] +
                                      (tile_part[t] & 0xFFFFu));
-            items[q] = make_uint4((uint32_t)t, (k * kRowsPerItem) | (rows << 16), groups, base);
+            items[q] = make_uint4((uint32_t)t, c0 + k * S, count - k * S, base + k * kRowsPerItem);
         }
-        tile_info[t] = make_uint4(cell_start[t * per_tile], tile_rows[t], tile_row_start[t], 0u);
     }
 }
 
 __global__ void meta_kernel(const uint32_t *__restrict__ full_start, const uint32_t *__restrict__ hist_start,
-                            int64_t hist_len, const uint32_t *__restrict__ tile_row_start,
-                            const uint32_t *__restrict__ cell_start, int64_t n_tiles, int64_t n_cells,
+                            int64_t hist_len, const uint32_t *__restrict__ tile_row_start, int64_t n_tiles,
                             uint32_t *__restrict__ meta)
 {
     meta[0] = full_start[n_tiles] + hist_start[hist_len];
     meta[1] = tile_row_start[n_tiles];
     meta[3] = 0u;
-    meta[4] = cell_start[n_cells];
+    meta[4] = tile_row_start[n_tiles] * (uint32_t)kRowSlots;
 }
 
-// Record slot of padded cell-sorted position s in a tile with `rows` rows:
-// group g = s / kGroup sits in lane g / rows of row g % rows, element s % kGroup.
-__device__ __forceinline__ int64_t slot_of(uint32_t row_start, uint32_t rows, uint32_t s)
-{
-    const uint32_t g = s / kGroup;
-    return ((int64_t)row_start + g % rows) * kRowSlots + (int64_t)(s % kGroup) * kWave + g / rows;
-}
-
-// Pass 5: place each binned particle's record.  Particles outside the
-// declared ranges are counted and written with zero mass, velocity and affine
-// matrix: they contribute nothing, as if skipped.
+// Pass 5: each binned particle's record at its tile's first record plus its
+// rank.  Particles outside the declared ranges are counted and written with
+// zero mass, velocity and affine matrix: they contribute nothing, as if
+// skipped.  Each thread loads two particles before writing either, so that
+// twice the loads are in flight.  Every lane of a wavefront runs the same
+// number of iterations, so all of them reach write_records's exchanges.
 template <int DIM>
-__global__ void __launch_bounds__(256) bin_scatter_kernel(Fields f, RangesF r, const uint32_t *__restrict__ key_in,
-                                                           const uint32_t *__restrict__ rank_in,
-                                                           const uint32_t *__restrict__ cell_start,
-                                                           const uint4 *__restrict__ tile_info,
-                                                           uint32_t *__restrict__ slot_out,
-                                                           float *__restrict__ sorted, uint32_t *__restrict__ status)
+__device__ __forceinline__ void load_record(const Fields &f, int64_t p, float *rec)
 {
-    constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
     constexpr int R = rec_floats<DIM>();
-    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < f.n; p += (int64_t)gridDim.x * blockDim.x) {
-        const uint32_t key = key_in[p];
-        const bool binned = key != kEmpty;
-        float rec[R];
-        bool rng = false;
-        if (binned) {
-            int fi = 0;
+    int fi = 0;
 #pragma unroll
-            for (int e = 0; e < DIM; ++e)
-                rec[fi++] = f.x[e * f.n + p];
-            rng = fabsf(f.m[p]) <= r.max_mass;
+    for (int e = 0; e < DIM; ++e)
+        rec[fi++] = f.x[e * f.n + p];
 #pragma unroll
-            for (int e = 0; e < DIM; ++e) {
-                rec[fi] = f.v[e * f.n + p];
-                rng = rng && fabsf(rec[fi]) <= r.max_speed;
-                ++fi;
-            }
+    for (int e = 0; e < DIM; ++e)
+        rec[fi++] = f.v[e * f.n + p];
 #pragma unroll
-            for (int k = 0; k < DIM * DIM; ++k) {
-                rec[fi] = f.C ? f.C[k * f.n + p] : 0.0f;
-                rng = rng && fabsf(rec[fi]) <= r.max_affine;
-                ++fi;
-            }
-            rec[fi++] = f.m[p];
+    for (int q = 0; q < DIM * DIM; ++q)
+        rec[fi++] = f.C ? f.C[q * f.n + p] : 0.0f;
+    rec[fi++] = f.m[p];
 #pragma unroll
-            for (; fi < R; ++fi)
-                rec[fi] = 0.0f;
-            if (!rng) {
-#pragma unroll
-                for (int k = DIM; k < R; ++k)
-                    rec[k] = 0.0f;
-            }
-        }
-        wave_count(binned && !rng, &status[1]);
-        if (!binned) {
-            slot_out[p] = kEmpty;
-            continue;
-        }
-        const uint4 ti = tile_info[key / per_tile];           // (first, rows, row_start, -)
-        const uint32_t s = cell_start[key] - ti.x + rank_in[p];
-        const int64_t slot = slot_of(ti.z, ti.y, s);
-        slot_out[p] = (uint32_t)slot;
-        float4 *dst = reinterpret_cast<float4 *>(sorted + slot * R);
-#pragma unroll
-        for (int q = 0; q < R / 4; ++q)
-            dst[q] = make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
+    for (; fi < R; ++fi)
+        rec[fi] = 0.0f;
+}
+
+// Range check and destination of one loaded record: its index in the binned
+// copy, or kEmpty when the particle is not binned.
+template <int DIM>
+__device__ __forceinline__ uint32_t place_record(const Fields &f, RangesF r, float nf, float dx, float last_base,
+                                                 int ntx, int64_t p, float *rec,
+                                                 const uint32_t *__restrict__ rank_in,
+                                                 const uint32_t *__restrict__ tile_start,
+                                                 uint32_t *__restrict__ slot_out, uint8_t *__restrict__ cell_key,
+                                                 uint32_t *__restrict__ status)
+{
+    constexpr int R = rec_floats<DIM>();
+    uint32_t t, l;
+    if (!particle_cell<DIM>(rec, nf, dx, last_base, ntx, t, l)) {
+        slot_out[p] = kEmpty;
+        return kEmpty;
     }
+    bool rng = fabsf(rec[2 * DIM + DIM * DIM]) <= r.max_mass;
+#pragma unroll
+    for (int e = 0; e < DIM; ++e)
+        rng = rng && fabsf(rec[DIM + e]) <= r.max_speed;
+#pragma unroll
+    for (int q = 0; q < DIM * DIM; ++q)
+        rng = rng && fabsf(rec[2 * DIM + q]) <= r.max_affine;
+    wave_count(!rng, &status[1]);
+    if (!rng) {
+#pragma unroll
+        for (int q = DIM; q < R; ++q)
+            rec[q] = 0.0f;
+    }
+    const uint32_t pos = tile_start[t] + rank_in[p];
+    slot_out[p] = pos;
+    cell_key[pos] = (uint8_t)l;
+    return pos;
 }
 
-// Pass 6: pad records.  A cell whose count is not a multiple of kGroup gets
-// zero-mass records at its centre (g = base + 1 on every axis, which lies in
-// the same base cell) in its remaining group positions; the transfer turns
-// them into exact zero contributions.
+// Writes the wavefront's 64 records (one per lane, destination pos or kEmpty).
+// In 3D a record is four 16-byte pieces; the records pass through LDS so that
+// the four lanes of a quad write one record's pieces with one instruction:
+// each store covers 16 whole 64-byte records instead of one piece of 64
+// records, a quarter of the memory requests.
 template <int DIM>
-__global__ void __launch_bounds__(256) bin_pad_kernel(const uint32_t *__restrict__ cell_count,
-                                                       const uint32_t *__restrict__ cell_start,
-                                                       const uint4 *__restrict__ tile_info, int64_t n_cells, int ntx,
-                                                       float inv_n, float *__restrict__ sorted)
+__device__ __forceinline__ void write_records(const float *rec, uint32_t pos, float4 *stage, uint32_t *spos,
+                                              float *__restrict__ sorted)
 {
-    constexpr int per_tile = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
     constexpr int R = rec_floats<DIM>();
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n_cells; c += (int64_t)gridDim.x * blockDim.x) {
-        const uint32_t count = cell_count[c];
-        const uint32_t rem = count % kGroup;
-        if (rem == 0)
-            continue;
-        const uint32_t tile = (uint32_t)(c / per_tile), local = (uint32_t)(c % per_tile);
-        const uint4 ti = tile_info[tile];
-        float rec[R];
+    const int lane = threadIdx.x % kWave;
+    if constexpr (DIM == 3) {
+        static_assert(R == 16, "a 3D record is four float4 pieces");
 #pragma unroll
-        for (int k = 0; k < R; ++k)
-            rec[k] = 0.0f;
-        uint32_t t = tile, l[DIM];
-        tile_local_inverse<DIM>(local, l);
+        for (int q = 0; q < 4; ++q)
+            stage[lane * 4 + q] = make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
+        spos[lane] = pos;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int e = 0; e < DIM; ++e) {
-            const uint32_t base = (t % (uint32_t)ntx) * kTile + l[e];
-            rec[e] = (float)(base + 1) * inv_n;
-            t /= (uint32_t)ntx;
+        for (int i = 0; i < 4; ++i) {
+            const int src = 16 * i + (lane >> 2), piece = lane & 3;
+            const uint32_t d = spos[src];
+            const float4 v = stage[src * 4 + piece];
+            if (d != kEmpty)
+                reinterpret_cast<float4 *>(sorted + (int64_t)d * R)[piece] = v;
         }
-        const uint32_t s0 = cell_start[c] - ti.x + count;
-        for (uint32_t s = s0; s < s0 + (kGroup - rem); ++s) {
-            float4 *dst = reinterpret_cast<float4 *>(sorted + slot_of(ti.z, ti.y, s) * R);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+        (void)stage;
+        (void)spos;
+        if (pos != kEmpty) {
+            float4 *dst = reinterpret_cast<float4 *>(sorted + (int64_t)pos * R);
 #pragma unroll
             for (int q = 0; q < R / 4; ++q)
                 dst[q] = make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
@@ -457,15 +532,125 @@ __global__ void __launch_bounds__(256) bin_pad_kernel(const uint32_t *__restrict
     }
 }
 
-// A prime step that does not divide `chunks`, so i -> (i * step) mod chunks
-// is a permutation of the chunks.
-int64_t chunk_stride(int64_t chunks)
+template <int DIM>
+__global__ void __launch_bounds__(kBinThreads) bin_scatter_kernel(Fields f, RangesF r, float nf, float dx,
+                                                                   float last_base, int ntx, int64_t chunks, int per,
+                                                                   const uint32_t *__restrict__ rank_in,
+                                                                   const uint32_t *__restrict__ tile_start,
+                                                                   uint32_t *__restrict__ slot_out,
+                                                                   uint8_t *__restrict__ cell_key,
+                                                                   float *__restrict__ sorted,
+                                                                   uint32_t *__restrict__ status)
 {
-    const int64_t primes[] = { 7919, 104729, 1299709, 15485863 };
-    for (int64_t q : primes)
-        if (chunks % q != 0)
-            return q % (chunks > 0 ? chunks : 1) == 0 ? 1 : q;
-    return 1;
+    constexpr int R = rec_floats<DIM>();
+    constexpr int kWaves = kBinThreads / kWave;
+    __shared__ float4 stage[DIM == 3 ? kWaves * kWave * 4 : 1];
+    __shared__ uint32_t spos[DIM == 3 ? kWaves * kWave : 1];
+    const int w = threadIdx.x / kWave;
+    float4 *my_stage = DIM == 3 ? stage + w * kWave * 4 : stage;
+    uint32_t *my_spos = DIM == 3 ? spos + w * kWave : spos;
+    const int64_t chunk = (int64_t)kBinThreads * per;
+    for (int64_t c = blockIdx.x; c < chunks; c += gridDim.x) {
+        for (int k = 0; k < per; k += 2) {              // uniform trip count: every lane reaches the exchanges
+            const int64_t pa = c * chunk + (int64_t)k * kBinThreads + threadIdx.x;
+            const int64_t pb = pa + kBinThreads;
+            const bool la = pa < f.n, lb = k + 1 < per && pb < f.n;
+            float ra[R], rb[R];
+            if (la)
+                load_record<DIM>(f, pa, ra);
+            if (lb)
+                load_record<DIM>(f, pb, rb);
+            uint32_t da = kEmpty, db = kEmpty;
+            if (la)
+                da = place_record<DIM>(f, r, nf, dx, last_base, ntx, pa, ra, rank_in, tile_start, slot_out, cell_key,
+                                       status);
+            if (lb)
+                db = place_record<DIM>(f, r, nf, dx, last_base, ntx, pb, rb, rank_in, tile_start, slot_out, cell_key,
+                                       status);
+            write_records<DIM>(ra, da, my_stage, my_spos, sorted);
+            write_records<DIM>(rb, db, my_stage, my_spos, sorted);
+        }
+    }
+}
+
+// Entry index of padded cell-sorted position s in an item whose rows start
+// at row0 and number `rows`: group g = s / kGroup sits in lane g / rows of row
+// g % rows, entry s % kGroup.
+__device__ __forceinline__ int64_t entry_of(int64_t row0, uint32_t rows, uint32_t s)
+{
+    const uint32_t g = s / kGroup;
+    return ((row0 + g % rows) * kWave + g / rows) * kGroup + s % kGroup;
+}
+
+// Pass 6: one block per work item (a slice of at most slice_records() records
+// of one tile).  The cells' counts come from an LDS histogram of the slice's
+// cell keys; a wave prefix sum of the counts rounded up to whole groups gives
+// each cell's first padded position; a second sweep places every record (LDS
+// cursor per cell), and the record placed first in a cell also fills the
+// cell's pad entries.  Groups between the last one and the bound are marked
+// empty.  The keys stay in registers between the sweeps.
+constexpr int kGroupThreads = 256;
+
+template <int DIM>
+__global__ void __launch_bounds__(kGroupThreads) bin_groups_kernel(const uint4 *__restrict__ items,
+                                                                    const uint32_t *__restrict__ meta,
+                                                                    const uint8_t *__restrict__ cell_key,
+                                                                    uint32_t *__restrict__ perm)
+{
+    static_assert(cells_per_tile<DIM>() <= (uint32_t)kWave, "one lane per cell of a tile");
+    constexpr int kKeys = (int)((slice_records<DIM>() + kGroupThreads - 1) / kGroupThreads);
+    __shared__ uint32_t cnt[kWave], start[kWave], cur[kWave];
+    const int tid = threadIdx.x;
+    const uint32_t n_items = meta[0];
+    for (uint32_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+        const uint4 item = items[it];
+        const uint32_t first = item.y, count = item.z;
+        const int64_t row0 = item.w;
+        const uint32_t rows = rows_bound<DIM>(count);
+        uint32_t l[kKeys];
+#pragma unroll
+        for (int k = 0; k < kKeys; ++k) {
+            const uint32_t i = k * kGroupThreads + tid;
+            l[k] = i < count ? (uint32_t)cell_key[first + i] : kEmpty;
+        }
+        if (tid < kWave)
+            cnt[tid] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kKeys; ++k)
+            if (l[k] != kEmpty)
+                atomicAdd(&cnt[l[k]], 1u);
+        __syncthreads();
+        if (tid < kWave) {
+            const uint32_t padded = (cnt[tid] + kGroup - 1) / kGroup * kGroup;
+            const uint32_t inc = wave_inclusive_scan(padded);
+            start[tid] = inc - padded;
+            cur[tid] = inc - padded;
+            const uint32_t bound = groups_bound<DIM>(count);
+            for (uint32_t g = __shfl(inc, kWave - 1, kWave) / kGroup + tid; g < bound; g += kWave)
+                perm[entry_of(row0, rows, g * kGroup)] = kEmpty;
+        }
+        __syncthreads();
+        uint32_t pos[kKeys];
+#pragma unroll
+        for (int k = 0; k < kKeys; ++k)
+            pos[k] = l[k] != kEmpty ? atomicAdd(&cur[l[k]], 1u) : 0u;
+#pragma unroll
+        for (int k = 0; k < kKeys; ++k) {
+            if (l[k] == kEmpty)
+                continue;
+            const uint32_t rec = first + k * kGroupThreads + tid;
+            perm[entry_of(row0, rows, pos[k])] = rec;
+            const uint32_t s0 = start[l[k]];
+            if (pos[k] == s0) {                      // the cell's first position: fill its pads
+                const uint32_t n_l = cnt[l[k]];
+                const uint32_t padded = (n_l + kGroup - 1) / kGroup * kGroup;
+                for (uint32_t q = s0 + n_l; q < s0 + padded; ++q)
+                    perm[entry_of(row0, rows, q)] = kPadFlag | rec;
+            }
+        }
+        __syncthreads();
+    }
 }
 
 int blocks_for(int64_t work, int block)
@@ -481,29 +666,33 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
 {
     const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3);
     const int ntx = n / kTile;
-    uint32_t *tile_rows = b.tile_tmp, *tile_items = b.tile_tmp + b.n_tiles;
-    hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks_for(b.n_cells, 256)), dim3(256), 0, s, b.cell_count, b.n_cells,
+    uint32_t *tile_rows = b.tile_tmp, *tile_items = b.tile_tmp + b.n_tiles, *tile_part = b.tile_tmp + 2 * b.n_tiles;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, b.tile_count, b.n_tiles,
                        0u);
     hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, s, b.meta, (int64_t)16, 0u);
-    const int64_t chunks = (p.n + 255) / 256;
-    const int64_t stride = chunk_stride(chunks);
-    if (dim == 3)
-        hipLaunchKernelGGL(bin_count_kernel<3>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, nf, dx, last, ntx,
-                           b.cell_count, b.key, b.rank, status, b.meta, chunks, stride);
-    else
-        hipLaunchKernelGGL(bin_count_kernel<2>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, nf, dx, last, ntx,
-                           b.cell_count, b.key, b.rank, status, b.meta, chunks, stride);
-    hipError_t e = exclusive_scan<kGroup>(b.cell_count, b.n_cells, b.cell_start, b.scan_tmp, s);
+    // particles per thread of a chunk: enough chunks for every CU, at most kMaxPer
+    int64_t per = (p.n + (int64_t)kBinThreads * device_cu_count() - 1) / ((int64_t)kBinThreads * device_cu_count());
+    per = per < 4 ? 4 : (per > kMaxPer ? kMaxPer : per);
+    const int64_t chunks = (p.n + kBinThreads * per - 1) / (kBinThreads * per);
+    const unsigned cblocks = (unsigned)(chunks < (int64_t)device_cu_count() * 2 ? chunks : device_cu_count() * 2);
+    if (chunks > 0) {
+        if (dim == 3)
+            hipLaunchKernelGGL(bin_tile_count_kernel<3>, dim3(cblocks), dim3(kBinThreads), 0, s, p, nf, dx, last, ntx,
+                               chunks, (int)per, b.tile_count, b.rank, status, b.meta);
+        else
+            hipLaunchKernelGGL(bin_tile_count_kernel<2>, dim3(cblocks), dim3(kBinThreads), 0, s, p, nf, dx, last, ntx,
+                               chunks, (int)per, b.tile_count, b.rank, status, b.meta);
+    }
+    hipError_t e = exclusive_scan<1>(b.tile_count, b.n_tiles, b.tile_start, b.scan_tmp, s);
     if (e != hipSuccess)
         return e;
     const int64_t lblocks = (b.n_tiles + 255) / 256;
-    uint32_t *tile_part = b.tile_tmp + 2 * b.n_tiles;
-    const int64_t hist_len = (kRowsPerItem - 1) * lblocks;
+    const int64_t hist_len = kRowsPerItem * lblocks;
     if (dim == 3)
-        hipLaunchKernelGGL(tile_layout_kernel<3>, dim3((unsigned)lblocks), dim3(256), 0, s, b.cell_start, b.n_tiles,
+        hipLaunchKernelGGL(tile_layout_kernel<3>, dim3((unsigned)lblocks), dim3(256), 0, s, b.tile_count, b.n_tiles,
                            tile_rows, tile_items, tile_part, b.item_hist);
     else
-        hipLaunchKernelGGL(tile_layout_kernel<2>, dim3((unsigned)lblocks), dim3(256), 0, s, b.cell_start, b.n_tiles,
+        hipLaunchKernelGGL(tile_layout_kernel<2>, dim3((unsigned)lblocks), dim3(256), 0, s, b.tile_count, b.n_tiles,
                            tile_rows, tile_items, tile_part, b.item_hist);
     if ((e = exclusive_scan<1>(tile_rows, b.n_tiles, b.tile_row_start, b.scan_tmp, s)) != hipSuccess)
         return e;
@@ -511,27 +700,29 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
         return e;
     if ((e = exclusive_scan<1>(b.item_hist, hist_len, b.item_hist_start, b.scan_tmp, s)) != hipSuccess)
         return e;
-    uint4 *tile_info = reinterpret_cast<uint4 *>(b.tile_info);
+    uint4 *items = reinterpret_cast<uint4 *>(b.items);
     if (dim == 3)
-        hipLaunchKernelGGL(items_kernel<3>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_rows, tile_items,
-                           tile_part, b.item_start, b.item_hist_start, b.tile_row_start, b.cell_start, b.n_tiles,
-                           lblocks, reinterpret_cast<uint4 *>(b.items), tile_info);
+        hipLaunchKernelGGL(items_kernel<3>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_items, tile_part,
+                           b.item_start, b.item_hist_start, b.tile_row_start, b.tile_start, b.n_tiles, lblocks, items);
     else
-        hipLaunchKernelGGL(items_kernel<2>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_rows, tile_items,
-                           tile_part, b.item_start, b.item_hist_start, b.tile_row_start, b.cell_start, b.n_tiles,
-                           lblocks, reinterpret_cast<uint4 *>(b.items), tile_info);
+        hipLaunchKernelGGL(items_kernel<2>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_items, tile_part,
+                           b.item_start, b.item_hist_start, b.tile_row_start, b.tile_start, b.n_tiles, lblocks, items);
     hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(1), 0, s, b.item_start, b.item_hist_start, hist_len,
-                       b.tile_row_start, b.cell_start, b.n_tiles, b.n_cells, b.meta);
+                       b.tile_row_start, b.n_tiles, b.meta);
+    const unsigned sblocks = (unsigned)(chunks < (int64_t)device_cu_count() * 8 ? chunks : device_cu_count() * 8);
+    const unsigned gblocks = (unsigned)blocks_for(b.max_items, 1);      // one block per item, capped
     if (dim == 3) {
-        hipLaunchKernelGGL(bin_scatter_kernel<3>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, r, b.key, b.rank,
-                           b.cell_start, tile_info, b.slot, b.sorted, status);
-        hipLaunchKernelGGL(bin_pad_kernel<3>, dim3(blocks_for(b.n_cells, 256)), dim3(256), 0, s, b.cell_count,
-                           b.cell_start, tile_info, b.n_cells, ntx, 1.0f / (float)n, b.sorted);
+        if (chunks > 0)
+            hipLaunchKernelGGL(bin_scatter_kernel<3>, dim3(sblocks), dim3(kBinThreads), 0, s, p, r, nf, dx, last, ntx,
+                               chunks, (int)per, b.rank, b.tile_start, b.slot, b.cell_key, b.sorted, status);
+        hipLaunchKernelGGL(bin_groups_kernel<3>, dim3(gblocks), dim3(kGroupThreads), 0, s, items, b.meta, b.cell_key,
+                           b.perm);
     } else {
-        hipLaunchKernelGGL(bin_scatter_kernel<2>, dim3(blocks_for(p.n, 256)), dim3(256), 0, s, p, r, b.key, b.rank,
-                           b.cell_start, tile_info, b.slot, b.sorted, status);
-        hipLaunchKernelGGL(bin_pad_kernel<2>, dim3(blocks_for(b.n_cells, 256)), dim3(256), 0, s, b.cell_count,
-                           b.cell_start, tile_info, b.n_cells, ntx, 1.0f / (float)n, b.sorted);
+        if (chunks > 0)
+            hipLaunchKernelGGL(bin_scatter_kernel<2>, dim3(sblocks), dim3(kBinThreads), 0, s, p, r, nf, dx, last, ntx,
+                               chunks, (int)per, b.rank, b.tile_start, b.slot, b.cell_key, b.sorted, status);
+        hipLaunchKernelGGL(bin_groups_kernel<2>, dim3(gblocks), dim3(kGroupThreads), 0, s, items, b.meta, b.cell_key,
+                           b.perm);
     }
     return hipGetLastError();
 }

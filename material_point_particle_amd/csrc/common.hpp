@@ -14,11 +14,12 @@
 namespace mpmk {
 
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
+constexpr uint32_t kPadFlag = 0x80000000u;  // group entry that completes a cell's last group
 constexpr int kWave = 64;
 constexpr int kTile = 4;             // tile edge in cells
 constexpr int kGroup = 4;            // records per group: one cell's particles, four at a time
-constexpr int kRowSlots = kWave * kGroup;  // a row: one group per lane (256 record slots)
-constexpr int kRowsPerItem = 16;     // rows per P2G work item (4096 record slots)
+constexpr int kRowSlots = kWave * kGroup;  // a row: one group per lane (256 group entries)
+constexpr int kRowsPerItem = 16;     // most rows of one P2G work item (4096 group entries)
 constexpr int kScanTileElems = 4096; // elements per block of the prefix-sum passes
 
 // One axis of a particle's quadratic B-spline stencil.  With g = x*n in node
@@ -87,6 +88,35 @@ __host__ __device__ __forceinline__ void tile_local_inverse(uint32_t local, uint
     }
 }
 
+template <int DIM>
+__host__ __device__ constexpr uint32_t cells_per_tile() { return DIM == 3 ? kTile * kTile * kTile : kTile * kTile; }
+
+// Upper bound on the groups of kGroup same-cell entries formed from `count`
+// records of one tile: each occupied cell adds at most kGroup-1 pad entries
+// and at most min(count, cells) cells are occupied.  The bound depends on the
+// count alone, so rows are laid out before the cells are sorted.
+template <int DIM>
+__host__ __device__ inline uint32_t groups_bound(uint32_t count)
+{
+    const uint64_t occupied = count < cells_per_tile<DIM>() ? count : cells_per_tile<DIM>();
+    return (uint32_t)(((uint64_t)count + (kGroup - 1) * occupied) / kGroup);
+}
+
+template <int DIM>
+__host__ __device__ inline uint32_t rows_bound(uint32_t count)
+{
+    return (groups_bound<DIM>(count) + kWave - 1) / kWave;
+}
+
+// Records per P2G work item: a tile's records are cut into slices of this
+// many (the last one shorter); a full slice's groups fill exactly
+// kRowsPerItem rows at the bound.
+template <int DIM>
+__host__ __device__ constexpr uint32_t slice_records()
+{
+    return kRowsPerItem * kRowSlots - (kGroup - 1) * cells_per_tile<DIM>();
+}
+
 struct RangesF {
     float max_mass, max_speed, max_affine;
 };
@@ -109,8 +139,9 @@ struct Fields {           // component-major particle arrays of n particles
 };
 
 struct BinView {          // the workspace arrays, as typed device pointers
-    uint32_t *cell_start, *cell_count, *tile_row_start, *item_start, *items, *meta, *key, *rank, *slot,
-        *tile_tmp, *scan_tmp, *tile_info, *item_hist, *item_hist_start;
+    uint32_t *tile_count, *tile_start, *tile_row_start, *item_start, *items, *meta, *rank, *slot, *perm,
+        *tile_tmp, *scan_tmp, *item_hist, *item_hist_start;
+    uint8_t *cell_key;
     float *sorted;
     int64_t n_cells, n_tiles, max_items, max_slots, n_fields;
 };

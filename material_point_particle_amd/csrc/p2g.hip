@@ -168,16 +168,18 @@ __global__ void __launch_bounds__(256) p2g_direct_kernel(Fields f, const uint32_
 }
 
 // ---------------------------------------------------------------------------
-// Tiled path.  The bins hold, per tile of 4^dim cells, the tile's particles
-// sorted by cell, each cell padded with zero-mass records to whole groups of
-// kGroup records, and the groups laid out "transposed": group g of a tile with
-// R rows sits in lane g / R of row g % R, its kGroup records in four
-// consecutive 64-record sub-rows.  A wavefront takes one work item (a range of
-// rows of one tile): every lane holds kGroup particles of one cell, and the 64
-// lanes are R groups apart in cell order, so they are mostly in different
-// cells and write different node addresses at the same instruction.  Each
-// record is 64 bytes (x, v, C, m in 3D), so a sub-row is 4 KB of contiguous
-// memory read by one wavefront.
+// Tiled path.  The bins hold each tile's particle records (64 bytes: x, v, C,
+// m in 3D) in one contiguous range, cut into slices of at most
+// slice_records(), one work item each, and per item rows of group entries:
+// the slice's records sorted by cell, each cell completed to whole groups of
+// kGroup entries (a completing entry names one of the cell's records with the
+// pad flag, read with zero mass), and the groups laid out "transposed": group
+// g of an item with R rows sits in lane g / R of row g % R, its kGroup entries
+// as one 16-byte word.  A wavefront takes one item: every lane holds kGroup
+// particles of one cell, and the 64 lanes are R groups apart in cell order, so
+// they are mostly in different cells and write different node addresses at
+// the same instruction.  A row's entries are 1 KB of contiguous memory; the
+// records they name lie in the slice's contiguous range.
 //
 // Per lane and stencil node, the group's kGroup quantised contributions are
 // summed in float64 registers and added to the on-chip node block with one LDS
@@ -256,7 +258,7 @@ __device__ __forceinline__ void group_hoist(const float *rec, float nf, float dx
 
 struct TiledArgs {
     const float *sorted;
-    const uint32_t *items, *meta;
+    const uint32_t *perm, *items, *meta;
     uint32_t *cursor;
     int n, ntx;
     float nf, dx, last_base, S;
@@ -309,9 +311,9 @@ p2g_tiled_kernel(TiledArgs a)
             break;
         if (lane == 0)
             next = atomicAdd(a.cursor, 1u);
+        // item: tile, first record, records, first row of its group entries
         const uint32_t tile = rec_item.x;
-        const uint32_t row0 = rec_item.y & 0xFFFFu, row1 = rec_item.y >> 16;
-        const uint32_t groups = rec_item.z;
+        const uint32_t groups = groups_bound<DIM>(rec_item.z);
         const uint32_t rows = (groups + kWave - 1) / kWave;
         const int64_t row_base = (int64_t)rec_item.w;
         int torg[3] = { 0, 0, 0 };
@@ -323,12 +325,27 @@ p2g_tiled_kernel(TiledArgs a)
                 t /= (uint32_t)a.ntx;
             }
         }
-        for (uint32_t j = row0; j < row1; ++j) {
-            const int64_t slot0 = (row_base + j) * kRowSlots + lane;
+        static_assert(kGroup == 4, "a group's entries load as one uint4");
+        const uint4 *entries = reinterpret_cast<const uint4 *>(a.perm);
+        // this lane's group in row j is group lane * rows + j of the tile; the
+        // next row's entries are loaded one row ahead
+        uint4 ent_next = make_uint4(kEmpty, kEmpty, kEmpty, kEmpty);
+        if ((uint32_t)lane * rows < groups)
+            ent_next = entries[row_base * kWave + lane];
+        for (uint32_t j = 0; j < rows; ++j) {
+            const uint4 ent = ent_next;
+            if (j + 1 < rows && (uint32_t)lane * rows + j + 1 < groups)
+                ent_next = entries[(row_base + j + 1) * kWave + lane];
+            // this lane's entries; kEmpty where the lane holds no group
+            const bool live = (uint32_t)lane * rows + j < groups && ent.x != kEmpty;
+            const uint32_t e4[G] = { live ? ent.x : kEmpty, live ? ent.y : kEmpty, live ? ent.z : kEmpty,
+                                     live ? ent.w : kEmpty };
+            if (!live)
+                continue;
             GroupHoist<DIM> h[G];
 #pragma unroll
             for (int k = 0; k < G; ++k) {
-                const float4 *src = reinterpret_cast<const float4 *>(a.sorted + (slot0 + k * kWave) * R);
+                const float4 *src = reinterpret_cast<const float4 *>(a.sorted + (int64_t)(e4[k] & ~kPadFlag) * R);
                 float rec[R];
 #pragma unroll
                 for (int q = 0; q < R / 4; ++q) {
@@ -338,10 +355,10 @@ p2g_tiled_kernel(TiledArgs a)
                     rec[4 * q + 2] = t.z;
                     rec[4 * q + 3] = t.w;
                 }
+                if (e4[k] & kPadFlag)                        // completes the cell's group: zero mass
+                    rec[2 * DIM + DIM * DIM] = 0.0f;
                 group_hoist<DIM>(rec, a.nf, a.dx, a.last_base, a.S, h[k]);
             }
-            if ((uint32_t)lane * rows + j >= groups)        // this lane's group index: lane * rows + j
-                continue;
             // every record of the group is in one cell of this tile (binning's
             // invariant); a group that breaks it is counted and skipped
             bool ok = true;
@@ -517,6 +534,7 @@ hipError_t launch_p2g_tiled(int dim, int n, int frac_bits, const BinView &b, int
 {
     TiledArgs a;
     a.sorted = b.sorted;
+    a.perm = b.perm;
     a.items = b.items;
     a.meta = b.meta;
     a.cursor = b.meta + 3;

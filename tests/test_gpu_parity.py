@@ -233,83 +233,100 @@ def test_binning_matches_oracle(mpm, oracle_lib, name, count):
     cnt, start, order = oracle_lib.bin_particles(w.dim, w.n, w.tile, host, ranges_of(w))
     _, _, tr = gpu_p2g(mpm, w, host, True)
     lay = tr.layout
-    gcount = u32(tr.ws_u32("cell_count", lay.n_cells))
-    gstart = u32(tr.ws_u32("cell_start", lay.n_cells + 1))
-    per = 4 ** w.dim
+    N, per = w.n_particles, 4 ** w.dim
     # the library numbers the cells of a 3D tile x fastest, then z, then y; the
-    # oracle row-major: map library keys to oracle keys before comparing
+    # oracle row-major: lib_of_oracle maps an oracle local number to the library's
     local = np.arange(per)
     lx, ly, lz = local % 4, (local // 16) if w.dim == 3 else local // 4, (local // 4) % 4
     oracle_local = lx + 4 * ly + 16 * lz if w.dim == 3 else local
-    to_oracle = (np.arange(lay.n_cells) // per) * per + oracle_local[np.arange(lay.n_cells) % per]
-    assert_same(gcount, cnt[to_oracle], "cell counts")
-    # the library's cell starts are the prefix sums of counts padded to whole groups of 4 records
-    padded = (gcount.astype(np.int64) + 3) // 4 * 4
-    assert_same(gstart.astype(np.int64), np.concatenate([[0], np.cumsum(padded)]), "padded cell starts")
+    lib_of_oracle = np.empty(per, np.int64)
+    lib_of_oracle[oracle_local] = local
+    # each binned particle's oracle cell key, tile and library-local cell
+    pkey = np.full(N, -1, np.int64)
+    pkey[order] = np.repeat(np.arange(lay.n_cells), cnt.astype(np.int64))
+    ptile, plocal = pkey // per, lib_of_oracle[pkey % per]
+    # tile histogram and prefix sum: bit-exact against the oracle's cell counts
+    ocount = cnt.astype(np.int64).reshape(-1, per).sum(axis=1)
+    tcount = u32(tr.ws_u32("tile_count", lay.n_tiles)).astype(np.int64)
+    tstart = u32(tr.ws_u32("tile_start", lay.n_tiles + 1)).astype(np.int64)
+    assert_same(tcount, ocount, "tile counts")
+    assert_same(tstart, np.concatenate([[0], np.cumsum(ocount)]), "tile starts")
     meta = tr.meta()
     rows_total, items = int(meta[1]), int(meta[0])
-    assert int(meta[2]) == len(order) and int(meta[4]) == int(padded.sum())
-    trs = u32(tr.ws_u32("tile_row_start", lay.n_tiles + 1)).astype(np.int64)
-    ostart = start.astype(np.int64)
-    slot_of = u32(tr.ws_u32("slot", w.n_particles)).astype(np.int64)
-    assert np.all(slot_of[order] != 0xFFFFFFFF)
-    gorder = np.full(rows_total * 256, 0xFFFFFFFF, dtype=np.int64)   # slot -> particle
+    assert int(meta[2]) == len(order) and int(meta[4]) == rows_total * 256
+    # record index of every binned particle: inside its tile's range, each index once
+    slot_of = u32(tr.ws_u32("slot", N)).astype(np.int64)
     binned_idx = np.nonzero(slot_of != 0xFFFFFFFF)[0]
-    assert np.array_equal(np.sort(binned_idx), np.sort(order))
-    assert np.all(slot_of[binned_idx] < rows_total * 256)
-    gorder[slot_of[binned_idx]] = binned_idx
-    assert len(np.unique(slot_of[binned_idx])) == len(binned_idx)
-    gs = gstart.astype(np.int64)
-    tile_pad = gs[per::per] - gs[:-1:per]
-    groups = tile_pad // 4
-    rows = (groups + 63) // 64
+    assert np.array_equal(binned_idx, np.sort(order))
+    sl = slot_of[order]
+    assert np.all(sl >= tstart[ptile[order]]) and np.all(sl < tstart[ptile[order]] + tcount[ptile[order]])
+    assert len(np.unique(sl)) == len(order)
+    # records and their cell keys
+    nb = len(order)
+    sorted_f = tr.ws.view(torch.float32)[lay.sorted // 4: lay.sorted // 4 + lay.n_fields * max(nb, 1)]
+    rec = sorted_f.view(-1, lay.n_fields)[:nb].cpu().numpy()
+    src = np.concatenate([host["x"], host["v"], host["C"], host["m"][None]])
+    nf = src.shape[0]
+    assert np.array_equal(rec[sl, :nf].T, src[:, order])
+    ck = tr.ws.view(torch.uint8)[lay.cell_key: lay.cell_key + nb].cpu().numpy().astype(np.int64)
+    assert np.array_equal(ck[sl], plocal[order])
+    rec_local = ck                                            # local cell of each record index
+    # work items: each tile's records cut into slices of S records (the last one
+    # shorter); a slice's rows come from its count alone, an upper bound on its
+    # padded groups
+    S = 16 * 256 - 3 * per
+
+    def bound(c):
+        return (c + 3 * np.minimum(c, per)) // 4
+
+    full, rem = tcount // S, tcount % S
+    rows = full * 16 + np.where(rem > 0, (bound(rem) + 63) // 64, 0)
+    trs = u32(tr.ws_u32("tile_row_start", lay.n_tiles + 1)).astype(np.int64)
     assert np.array_equal(np.diff(trs), rows) and int(trs[-1]) == rows_total
-    assert items == int(np.sum((rows + 15) // 16))
-    # work items: every (tile, first row) exactly once, handed out alternately from the
-    # large and the small end of the size order
+    assert items == int(full.sum() + (rem > 0).sum())
     it = u32(tr.ws_u32("items", 4 * lay.max_items)).astype(np.int64).reshape(-1, 4)[:items]
-    it_tile, it_row, it_end = it[:, 0], it[:, 1] & 0xFFFF, it[:, 1] >> 16
-    want = sorted((int(t), int(r0)) for t in np.nonzero(rows)[0] for r0 in range(0, int(rows[t]), 16))
-    assert sorted(zip(it_tile.tolist(), it_row.tolist())) == want
-    assert np.array_equal(it_end, np.minimum(it_row + 16, rows[it_tile]))
-    assert np.array_equal(it[:, 2], groups[it_tile]) and np.array_equal(it[:, 3], trs[it_tile])
-    size = it_end - it_row
+    want = []
+    for t in np.nonzero(tcount)[0]:
+        for c in range(int(full[t])):
+            want.append((int(t), int(tstart[t]) + c * S, S, int(trs[t]) + 16 * c))
+        if rem[t]:
+            want.append((int(t), int(tstart[t] + full[t] * S), int(rem[t]), int(trs[t] + 16 * full[t])))
+    assert sorted(map(tuple, it.tolist())) == sorted(want)
+    # handed out alternately from the large and the small end of the size order
+    size = (bound(it[:, 2]) + 63) // 64
     big, small = size[0::2], size[1::2]
     assert np.all(np.diff(big) <= 0) and np.all(np.diff(small) >= 0)
     if len(small):
         assert big[-1] >= small[-1]
-    sorted_f = tr.ws.view(torch.float32)[lay.sorted // 4: lay.sorted // 4 + lay.n_fields * lay.max_slots]
-    rec = sorted_f.view(lay.max_slots, lay.n_fields)[: rows_total * 256].cpu().numpy()
-    src = np.concatenate([host["x"], host["v"], host["C"], host["m"][None]])
-    nf = src.shape[0]
-    seen = np.zeros(w.n_particles, np.int64)
-    for t in np.nonzero(tile_pad)[0]:
-        R = int(rows[t])
-        s_pos = np.arange(int(tile_pad[t]))
-        g = s_pos // 4
-        slot = (trs[t] + g % R) * 256 + (s_pos % 4) * 64 + g // R
-        seq = gorder[slot]                                   # padded cell-sorted sequence of the tile
-        c0 = t * per
-        for c in range(c0, c0 + per):
-            a = int(gs[c] - gs[c0])
-            n_c = int(gcount[c])
-            oc = int(to_oracle[c])
-            got = seq[a:a + n_c]
-            assert np.array_equal(np.sort(got), np.sort(order[ostart[oc]:ostart[oc + 1]]))
-            pads = slot[a + n_c:int(gs[c + 1] - gs[c0])]
-            assert np.all(gorder[pads] == 0xFFFFFFFF)
-            if len(pads):
-                pr = rec[pads]                               # zero mass, velocity and affine matrix
-                assert np.all(pr[:, w.dim:nf] == 0)
-                tile_id, loc, centre = int(t), [int(lx[c - c0]), int(ly[c - c0]), int(lz[c - c0])], []
-                for e in range(w.dim):                       # pads sit at the cell centre, g = base + 1
-                    centre.append(((tile_id % (w.n // 4)) * 4 + loc[e] + 1) / w.n)
-                    tile_id //= w.n // 4
-                assert np.all(pr[:, :w.dim] == np.array(centre, np.float32)[None, :])
-        seen[seq[seq != 0xFFFFFFFF]] += 1
-    assert np.all(seen[order] == 1) and seen.sum() == len(order)
-    valid = gorder != 0xFFFFFFFF
-    assert np.array_equal(rec[valid, :nf].T, src[:, gorder[valid]])
+    # group entries of every item: the slice's records sorted by cell, each cell
+    # completed to whole groups of 4 by pad entries naming one of its records
+    perm = u32(tr.ws_u32("perm", rows_total * 256)).astype(np.int64).reshape(rows_total, 64, 4)
+    for t, first, cnt_i, row0 in it.tolist():
+        R = int((bound(cnt_i) + 63) // 64)
+        gb = int(bound(cnt_i))
+        g = np.arange(gb)
+        ent = perm[row0 + g % R, g // R, :]
+        live = ent[:, 0] != 0xFFFFFFFF
+        ga = int(live.sum())
+        assert np.all(live[:ga]), "empty groups only after the last group"
+        ent = ent[:ga]
+        pad = (ent & 0x80000000) != 0
+        idx = ent & 0x7FFFFFFF
+        assert not np.any(pad[:, 0]), "a group starts with a record"
+        assert np.all((idx >= first) & (idx < first + cnt_i))
+        assert np.array_equal(np.sort(idx[~pad]), np.arange(first, first + cnt_i))
+        cells = rec_local[idx]
+        assert np.all(cells == cells[:, :1]), "one cell per group"
+        gcell = cells[:, 0]
+        assert np.all(np.diff(gcell) >= 0), "groups in cell order"
+        want_c = np.bincount(rec_local[first:first + cnt_i], minlength=per)
+        assert np.array_equal(np.bincount(gcell.repeat(4)[~pad.ravel()], minlength=per), want_c)
+        assert np.array_equal(np.bincount(gcell.repeat(4)[pad.ravel()], minlength=per), (-want_c) % 4)
+        assert ga == int(((want_c + 3) // 4).sum())
+        # pads fill only the tail of a cell's last group
+        last_of_cell = np.r_[gcell[1:] != gcell[:-1], True]
+        assert not np.any(pad[~last_of_cell])
+        assert np.all(np.diff(pad[last_of_cell].astype(np.int8), axis=1) >= 0)
 
 
 # ------------------------------------------------------ grid update + gather
