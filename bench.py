@@ -54,6 +54,74 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def measure_substeps(args, torch, w, build, DeviceParticles, Transfer):
+    """The full MPM substep on the 8M-particle dam-break workload (256^3 nodes,
+    2^32): binning, tiled P2G, grid update (consume-and-zero, gravity, sticky
+    walls) and APIC G2P with advection, substep after substep on the evolving
+    state, timed per stage with HIP events on the library's stream."""
+    host = build(w)
+    ex = w.extra
+    parts = DeviceParticles(host)
+    del host
+    tr = Transfer(w.dim, w.n, w.frac_bits, (w.max_mass, w.max_speed, w.max_affine), parts.n)
+    stream = torch.cuda.current_stream()
+
+    def substep(ev=None):
+        if ev:
+            ev[0].record(stream)
+        tr.bin(parts)
+        if ev:
+            ev[1].record(stream)
+        tr.p2g(parts, binned=True)
+        if ev:
+            ev[2].record(stream)
+        tr.grid_update(ex["dt"], ex["gravity"], ex["sticky"])
+        if ev:
+            ev[3].record(stream)
+        tr.g2p(parts, ex["dt"])
+        if ev:
+            ev[4].record(stream)
+
+    for _ in range(3):
+        substep()
+    torch.cuda.synchronize()
+    k = args.substeps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(k)]
+    for i in range(k):
+        substep(events[i])
+    torch.cuda.synchronize()
+    st = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events]).mean(axis=0)
+    ms = float(st.sum())
+    bin_ms, p2g_ms, upd_ms, g2p_ms = (float(v) for v in st)
+    nodes = w.n ** w.dim
+    touched = int((tr.vg != 0).any(dim=0).sum().item())
+    upd_bytes = nodes * (8 * (1 + w.dim) * 2 + 4 * w.dim)                # read and zero M, P; write v
+    g2p_bytes = parts.n * (4 * w.dim + 4 * (2 * w.dim + w.dim * w.dim)) + touched * 4 * w.dim
+    meta = tr.meta()
+    rec_bytes = 4 * (2 * w.dim + w.dim * w.dim + 1)
+    p2g_bytes = int(meta[2]) * rec_bytes + int((tr.grid != 0).any(dim=0).sum().item()) * 8 * (1 + w.dim)
+    status = tr.status.cpu().numpy().view(np.uint32).tolist()
+    log(f"substeps: {ms:.3f} ms (bin {bin_ms:.3f}, p2g {p2g_ms:.3f}, grid update {upd_ms:.3f}, g2p {g2p_ms:.3f})")
+
+    def gbs(b, t):
+        return round(b / (t * 1e-3) / 1e9, 1)
+
+    return {
+        "workload": f"{w.name}: {parts.n} particles, dam-break block, {w.n}^3 nodes, {1 + w.dim} int64 channels at "
+                    f"2^{w.frac_bits}, dt {ex['dt']}, gravity {ex['gravity'][1]}, sticky band {ex['sticky']}",
+        "substeps": k, "ms_per_substep": round(ms, 4), "particles_per_s": round(parts.n / (ms * 1e-3), 1),
+        "stages_ms": {"bin": round(bin_ms, 4), "p2g": round(p2g_ms, 4), "grid_update": round(upd_ms, 4),
+                      "g2p": round(g2p_ms, 4)},
+        "grid_update": {"bound": "hbm", "bytes": upd_bytes, "achieved_gbs": gbs(upd_bytes, upd_ms),
+                        "frac": round(gbs(upd_bytes, upd_ms) / HBM_PEAK_GBS, 4)},
+        "g2p": {"bound": "hbm", "bytes": g2p_bytes, "achieved_gbs": gbs(g2p_bytes, g2p_ms),
+                "frac": round(gbs(g2p_bytes, g2p_ms) / HBM_PEAK_GBS, 4)},
+        "p2g": {"bound": "hbm", "bytes": p2g_bytes, "achieved_gbs": gbs(p2g_bytes, p2g_ms),
+                "frac": round(gbs(p2g_bytes, p2g_ms) / HBM_PEAK_GBS, 4)},
+        "status": status,
+    }
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -64,6 +132,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=0, help="particles in the CPU-baseline sample (0: all)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--no-substep", action="store_true",
+                    help="skip the full-substep measurement (binning, P2G, grid update, G2P) on the dam-break workload")
+    ap.add_argument("--substeps", type=int, default=20, help="timed substeps of the full-substep measurement")
     return ap.parse_args()
 
 
@@ -186,6 +257,11 @@ def main():
             "p2g_bytes": int(p2g_bytes), "status": status,
         },
     }
+
+    if not args.no_substep:
+        del copies, parts, tr
+        torch.cuda.empty_cache()
+        out["substep"] = measure_substeps(args, torch, WORKLOADS["dam_3d_256"], build, DeviceParticles, Transfer)
 
     if not args.no_cpu_baseline:
         import oracle
