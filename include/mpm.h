@@ -93,12 +93,14 @@ typedef struct {
 typedef struct {
     size_t tile_count;      /* uint32 [n_tiles]     binned particles per tile                    */
     size_t tile_start;      /* uint32 [n_tiles + 1] first record of each tile (exclusive prefix sum) */
+    size_t tile_active;     /* uint8  [n_tiles] written by mpm_grid_update when given the bins: 1
+                                        for the node tiles that P2G from these bins can reach */
     size_t tile_row_start;  /* uint32 [n_tiles + 1] first row of group entries of each tile      */
     size_t item_start;      /* uint32 [n_tiles + 1] first full P2G work item of each tile       */
-    size_t items;           /* uint32 [max_items][4] work items: tile, first row | end row << 16,
-                                        group bound of the tile, first row of the tile;
-                                        handed out alternately the largest and smallest
-                                        remaining */
+    size_t items;           /* uint32 [max_items][4] work items: tile, first record, records (a
+                                        slice of at most rows_per_item rows' worth of a tile's
+                                        records), first row of its group entries; handed out
+                                        alternately the largest and smallest remaining     */
     size_t meta;            /* uint32 [16]: [0] items, [1] rows, [2] binned particles,
                                         [3] P2G work cursor, [4] group entries (rows * 256) */
     size_t rank;            /* uint32 [n] rank of each particle inside its tile (internal)      */
@@ -112,7 +114,7 @@ typedef struct {
                                         tile by tile                                       */
     size_t tile_tmp;        /* uint32 [3][n_tiles] per-tile rows, full items, partial item (internal) */
     size_t scan_tmp;        /* uint32 [scan_blocks] prefix-sum block totals (internal)          */
-    size_t item_hist;       /* uint32 [15][ceil(n_tiles/256)] partial-item sizes per block (internal) */
+    size_t item_hist;       /* uint32 [rows_per_item][ceil(n_tiles/256)] partial-slice rows per block (internal) */
     size_t item_hist_start; /* uint32 prefix sum of item_hist (internal)                          */
     int64_t n_cells, n_tiles, max_items, max_slots, n_fields, rows_per_item;
     size_t total_bytes;
@@ -220,11 +222,20 @@ int mpm_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32
  * then v_d = v_d + (dt * g_d) (the product formed once in float32); where
  * M == 0, v = 0; nodes within `sticky` nodes of any face get v = 0; then
  * M and P are set to 0.
+ * bins == NULL: every node.  bins != NULL: the workspace of the
+ * mpm_bin_particles call whose P2G filled the grid (same grid descriptor);
+ * only the nodes of 4^dim-node tiles that this P2G can reach (tiles whose
+ * own or lower-neighbour cell tiles hold binned particles) are updated, and
+ * vg elsewhere is left as it was.  Every other accumulator is already zero
+ * when the grid was zero before that P2G, and G2P of the same particles reads
+ * vg only at reachable nodes, so a substep loop gives the same particles as
+ * with every node updated.  The call writes the tile_active flags of the
+ * workspace.
  * grid: device int64[1+dim][n]^dim, read and zeroed.  vg: device
  * float[dim][n]^dim, written.  gravity: host float[dim].
  * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
-int mpm_grid_update(const mpm_grid_desc *grid, int64_t *grid_io, float *vg, float dt, const float *gravity,
-                    int32_t sticky, hipStream_t stream);
+int mpm_grid_update(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, float *vg, float dt,
+                    const float *gravity, int32_t sticky, hipStream_t stream);
 
 /* APIC grid-to-particle gather and advection ("Implementation -- GPU
  * Optimization & Reference Codebases", sections 1 and 3.1).  Per particle,

@@ -41,7 +41,8 @@ class mpm_ranges(ct.Structure):
 
 
 class mpm_ws_layout(ct.Structure):
-    _fields_ = [(name, ct.c_size_t) for name in ("tile_count", "tile_start", "tile_row_start", "item_start", "items",
+    _fields_ = [(name, ct.c_size_t) for name in ("tile_count", "tile_start", "tile_active", "tile_row_start",
+                                                  "item_start", "items",
                                                   "meta", "rank", "slot", "cell_key", "perm", "sorted", "tile_tmp",
                                                   "scan_tmp", "item_hist", "item_hist_start")]
     _fields_ += [(name, ct.c_int64) for name in ("n_cells", "n_tiles", "max_items", "max_slots", "n_fields",
@@ -84,8 +85,8 @@ def lib() -> ct.CDLL:
         L.mpm_p2g_cic_split.argtypes = [ct.c_int64, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int32,
                                         ct.c_int64, ct.c_int64, ct.c_void_p, ct.c_void_p, ct.c_void_p]
         L.mpm_grid_update.restype = ct.c_int
-        L.mpm_grid_update.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_float, P(ct.c_float),
-                                      ct.c_int32, ct.c_void_p]
+        L.mpm_grid_update.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_float,
+                                      P(ct.c_float), ct.c_int32, ct.c_void_p]
         L.mpm_g2p.restype = ct.c_int
         L.mpm_g2p.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_float, ct.c_void_p, ct.c_void_p]
         _lib = L
@@ -174,9 +175,9 @@ def mpm_p2g_cic_split(X, m, vel, order, cells: int, max_mass: int, max_speed: in
                                    _ptr(grid), _ptr(status), _stream(stream)), "mpm_p2g_cic_split")
 
 
-def mpm_grid_update(desc, grid, vg, dt: float, gravity, sticky: int, stream=None) -> None:
+def mpm_grid_update(desc, bins, grid, vg, dt: float, gravity, sticky: int, stream=None) -> None:
     g = (ct.c_float * 3)(*(list(gravity) + [0.0] * (3 - len(gravity))))
-    _check(lib().mpm_grid_update(ct.byref(desc), _ptr(grid), _ptr(vg), dt, g, sticky, _stream(stream)),
+    _check(lib().mpm_grid_update(ct.byref(desc), _ptr(bins), _ptr(grid), _ptr(vg), dt, g, sticky, _stream(stream)),
            "mpm_grid_update")
 
 

@@ -129,6 +129,7 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     const int64_t n1 = np > 0 ? np : 1;
     o->tile_count = take(u4 * (size_t)n_tiles);
     o->tile_start = take(u4 * (size_t)(n_tiles + 1));
+    o->tile_active = take((size_t)n_tiles);          // (offsets up to here do not depend on np)
     o->tile_row_start = take(u4 * (size_t)(n_tiles + 1));
     o->item_start = take(u4 * (size_t)(n_tiles + 1));
     o->items = take(u4 * 4 * (size_t)max_items);
@@ -168,6 +169,7 @@ BinView bin_view(void *ws, const mpm_ws_layout &l)
     v.perm = (uint32_t *)(b + l.perm);
     v.sorted = (float *)(b + l.sorted);
     v.tile_tmp = (uint32_t *)(b + l.tile_tmp);
+    v.tile_active = (uint8_t *)(b + l.tile_active);
     v.scan_tmp = (uint32_t *)(b + l.scan_tmp);
     v.item_hist = (uint32_t *)(b + l.item_hist);
     v.item_hist_start = (uint32_t *)(b + l.item_hist_start);
@@ -312,14 +314,19 @@ int mpm_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32
     return hip_status(launch_p2g_cic_split(n, X, m, vel, order, cells, grid_out, status, stream));
 }
 
-int mpm_grid_update(const mpm_grid_desc *grid, int64_t *grid_io, float *vg, float dt, const float *gravity,
-                    int32_t sticky, hipStream_t stream)
+int mpm_grid_update(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, float *vg, float dt,
+                    const float *gravity, int32_t sticky, hipStream_t stream)
 {
     if (check_desc(grid) != MPM_OK || !aligned(grid_io, 8) || !aligned(vg, 4) || !gravity || sticky < 0 ||
-        sticky > grid->n / 2)
+        sticky > grid->n / 2 || (bins && !aligned(bins, 256)))
         return MPM_ERR_INVALID;
     float g3[3] = { gravity[0], gravity[1], grid->dim == 3 ? gravity[2] : 0.0f };
-    return hip_status(launch_grid_update(grid->dim, grid->n, grid_io, vg, dt, g3, sticky, stream));
+    if (!bins)
+        return hip_status(launch_grid_update(grid->dim, grid->n, grid_io, vg, dt, g3, sticky, nullptr, stream));
+    mpm_ws_layout l;
+    make_layout(grid, 0, &l);         // tile_count and tile_active come first: their offsets do not depend on n
+    const BinView v = bin_view(bins, l);
+    return hip_status(launch_grid_update(grid->dim, grid->n, grid_io, vg, dt, g3, sticky, &v, stream));
 }
 
 int mpm_g2p(const mpm_grid_desc *grid, const float *vg, const mpm_particles *particles, float dt, uint32_t *status,

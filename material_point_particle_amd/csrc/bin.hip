@@ -493,7 +493,9 @@ __device__ __forceinline__ uint32_t place_record(const Fields &f, RangesF r, flo
 // In 3D a record is four 16-byte pieces; the records pass through LDS so that
 // the four lanes of a quad write one record's pieces with one instruction:
 // each store covers 16 whole 64-byte records instead of one piece of 64
-// records, a quarter of the memory requests.
+// records, a quarter of the memory requests.  Piece q of lane L's record sits
+// in slot (q + L + L / 4) mod 4 of its 64 bytes, so that eight consecutive
+// lanes' 16-byte accesses fall in distinct LDS banks on both sides.
 template <int DIM>
 __device__ __forceinline__ void write_records(const float *rec, uint32_t pos, float4 *stage, uint32_t *spos,
                                               float *__restrict__ sorted)
@@ -504,7 +506,8 @@ __device__ __forceinline__ void write_records(const float *rec, uint32_t pos, fl
         static_assert(R == 16, "a 3D record is four float4 pieces");
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            stage[lane * 4 + q] = make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
+            stage[lane * 4 + ((q + lane + (lane >> 2)) & 3)] =
+                make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
         spos[lane] = pos;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -513,7 +516,7 @@ __device__ __forceinline__ void write_records(const float *rec, uint32_t pos, fl
         for (int i = 0; i < 4; ++i) {
             const int src = 16 * i + (lane >> 2), piece = lane & 3;
             const uint32_t d = spos[src];
-            const float4 v = stage[src * 4 + piece];
+            const float4 v = stage[src * 4 + ((piece + src + (src >> 2)) & 3)];
             if (d != kEmpty)
                 reinterpret_cast<float4 *>(sorted + (int64_t)d * R)[piece] = v;
         }

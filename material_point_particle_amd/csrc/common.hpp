@@ -141,7 +141,7 @@ struct Fields {           // component-major particle arrays of n particles
 struct BinView {          // the workspace arrays, as typed device pointers
     uint32_t *tile_count, *tile_start, *tile_row_start, *item_start, *items, *meta, *rank, *slot, *perm,
         *tile_tmp, *scan_tmp, *item_hist, *item_hist_start;
-    uint8_t *cell_key;
+    uint8_t *cell_key, *tile_active;
     float *sorted;
     int64_t n_cells, n_tiles, max_items, max_slots, n_fields;
 };
@@ -155,7 +155,7 @@ hipError_t launch_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, c
 hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView &b, uint32_t *status,
                       hipStream_t s);
 hipError_t launch_grid_update(int dim, int n, int64_t *grid, float *vg, float dt, const float *gravity,
-                              int sticky, hipStream_t s);
+                              int sticky, const BinView *bins, hipStream_t s);
 hipError_t launch_g2p(int dim, int n, const float *vg, float *x, float *v, float *C, int64_t np, float dt,
                       uint32_t *status, hipStream_t s);
 

@@ -11,18 +11,43 @@
 namespace mpmk {
 namespace {
 
+// Node tile t (the 4^dim nodes whose indices divided by 4 give t) can receive
+// deposits from the node blocks of cell tiles t - e, e in {0,1}^dim: a block
+// covers the 6 nodes from its tile's first node on each axis.
+template <int DIM>
+__global__ void __launch_bounds__(256) active_tiles_kernel(const uint32_t *__restrict__ tile_count, int ntx,
+                                                           int64_t n_tiles, uint8_t *__restrict__ active)
+{
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n_tiles; t += (int64_t)gridDim.x * blockDim.x) {
+        const int tx = (int)(t % ntx), ty = (int)((t / ntx) % ntx), tz = DIM == 3 ? (int)(t / ((int64_t)ntx * ntx)) : 0;
+        bool act = false;
+#pragma unroll
+        for (int e = 0; e < (1 << DIM); ++e) {
+            const int sx = tx - (e & 1), sy = ty - ((e >> 1) & 1), sz = DIM == 3 ? tz - (e >> 2) : 0;
+            if (sx >= 0 && sy >= 0 && sz >= 0)
+                act = act || tile_count[((int64_t)sz * ntx + sy) * ntx + sx] != 0u;
+        }
+        active[t] = act ? 1 : 0;
+    }
+}
+
 // One thread per node, x fastest, so every access is coalesced.  Per node:
 // v_d = (float)((double)P_d / (double)M) and v_d += dt*g_d where M != 0,
 // v = 0 where M == 0 and within `sticky` nodes of a face; then M = P = 0.
+// With `active`, nodes of inactive node tiles are skipped.
 template <int DIM>
 __global__ void __launch_bounds__(256) grid_update_kernel(int n, int64_t *__restrict__ grid, float *__restrict__ vg,
-                                                          float dt, float g0, float g1, float g2, int sticky)
+                                                          float dt, float g0, float g1, float g2, int sticky,
+                                                          const uint8_t *__restrict__ active)
 {
     const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    const int ntx = n / kTile;
     const float gdt[3] = { dt * g0, dt * g1, dt * g2 };
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nodes; i += (int64_t)gridDim.x * blockDim.x) {
         const int ix = (int)(i % n), iy = (int)((i / n) % n);
         const int iz = DIM == 3 ? (int)(i / ((int64_t)n * n)) : 0;
+        if (active && !active[((int64_t)(iz / kTile) * ntx + iy / kTile) * ntx + ix / kTile])
+            continue;
         bool wall = ix < sticky || ix >= n - sticky || iy < sticky || iy >= n - sticky;
         if (DIM == 3)
             wall = wall || iz < sticky || iz >= n - sticky;
@@ -128,16 +153,27 @@ int blocks_for(int64_t work, int block)
 }  // namespace
 
 hipError_t launch_grid_update(int dim, int n, int64_t *grid, float *vg, float dt, const float *gravity, int sticky,
-                              hipStream_t s)
+                              const BinView *bins, hipStream_t s)
 {
     const int64_t nodes = dim == 3 ? (int64_t)n * n * n : (int64_t)n * n;
     const float g0 = gravity[0], g1 = gravity[1], g2 = dim == 3 ? gravity[2] : 0.0f;
+    const uint8_t *active = nullptr;
+    if (bins) {
+        const int ntx = n / kTile;
+        if (dim == 3)
+            hipLaunchKernelGGL(active_tiles_kernel<3>, dim3(blocks_for(bins->n_tiles, 256)), dim3(256), 0, s,
+                               bins->tile_count, ntx, bins->n_tiles, bins->tile_active);
+        else
+            hipLaunchKernelGGL(active_tiles_kernel<2>, dim3(blocks_for(bins->n_tiles, 256)), dim3(256), 0, s,
+                               bins->tile_count, ntx, bins->n_tiles, bins->tile_active);
+        active = bins->tile_active;
+    }
     if (dim == 3)
         hipLaunchKernelGGL(grid_update_kernel<3>, dim3(blocks_for(nodes, 256)), dim3(256), 0, s, n, grid, vg, dt, g0,
-                           g1, g2, sticky);
+                           g1, g2, sticky, active);
     else
         hipLaunchKernelGGL(grid_update_kernel<2>, dim3(blocks_for(nodes, 256)), dim3(256), 0, s, n, grid, vg, dt, g0,
-                           g1, g2, sticky);
+                           g1, g2, sticky, active);
     return hipGetLastError();
 }
 

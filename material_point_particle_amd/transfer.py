@@ -59,8 +59,10 @@ class Transfer:
         L.mpm_p2g(self.desc, parts.desc(), self.ranges, self.ws if binned else None, g, self.status)
         return g
 
-    def grid_update(self, dt: float, gravity, sticky: int) -> torch.Tensor:
-        L.mpm_grid_update(self.desc, self.grid, self.vg, dt, gravity, sticky)
+    def grid_update(self, dt: float, gravity, sticky: int, active: bool = False) -> torch.Tensor:
+        """active: update only the node tiles the last binned P2G can reach
+        (the workspace must hold that binning)."""
+        L.mpm_grid_update(self.desc, self.ws if active else None, self.grid, self.vg, dt, gravity, sticky)
         return self.vg
 
     def g2p(self, parts: DeviceParticles, dt: float) -> None:

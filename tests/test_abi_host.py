@@ -77,15 +77,28 @@ def test_workspace_layout_is_disjoint_and_aligned():
         assert lay.n_fields == {2: 12, 3: 16}[dim]     # x, v, C, m padded to a multiple of 4 floats
         assert lay.max_slots % 256 == 0 and lay.max_slots >= N
         spans = sorted([
-            (lay.tile_count, 4 * lay.n_tiles), (lay.tile_start, 4 * (lay.n_tiles + 1)),
+            (lay.tile_count, 4 * lay.n_tiles), (lay.tile_start, 4 * (lay.n_tiles + 1)), (lay.tile_active, lay.n_tiles),
             (lay.tile_row_start, 4 * (lay.n_tiles + 1)), (lay.item_start, 4 * (lay.n_tiles + 1)),
             (lay.items, 16 * lay.max_items), (lay.meta, 64), (lay.rank, 4 * max(N, 1)), (lay.slot, 4 * max(N, 1)),
             (lay.cell_key, max(N, 1)), (lay.perm, 4 * lay.max_slots), (lay.sorted, 4 * lay.n_fields * max(N, 1)),
             (lay.tile_tmp, 12 * lay.n_tiles),
-            (lay.item_hist, 60 * ((lay.n_tiles + 255) // 256)), (lay.item_hist_start, 4 * (15 * ((lay.n_tiles + 255) // 256) + 1))])
+            (lay.item_hist, 4 * lay.rows_per_item * ((lay.n_tiles + 255) // 256)),
+            (lay.item_hist_start, 4 * (lay.rows_per_item * ((lay.n_tiles + 255) // 256) + 1))])
         for (a, la), (b, _) in zip(spans, spans[1:]):
             assert a % 256 == 0 and a + la <= b
         assert spans[-1][0] + spans[-1][1] <= lay.total_bytes
+
+
+def test_tile_arrays_sit_at_offsets_independent_of_the_particle_count():
+    # mpm_grid_update finds tile_count and tile_active in a workspace without
+    # knowing the particle count it was sized for
+    for dim, n in [(2, 64), (3, 256)]:
+        d = M.grid_desc(dim, n, 20)
+        base = M.mpm_workspace_layout(d, 0)
+        for N in (1, 3500, 1 << 20):
+            lay = M.mpm_workspace_layout(d, N)
+            assert (lay.tile_count, lay.tile_start, lay.tile_active) == (base.tile_count, base.tile_start,
+                                                                         base.tile_active)
 
 
 def test_entry_points_reject_bad_arguments_before_any_launch():
@@ -112,7 +125,9 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert lib.mpm_p2g_cic_split(1 << 30, 4096, 4096, 4096, None, 8, 1 << 20, 1 << 20, grid, status,
                                  None) == L.MPM_ERR_OVERFLOW
     g = (ct.c_float * 3)(0, -9.8, 0)
-    assert lib.mpm_grid_update(ct.byref(d), grid, ct.c_void_p(4096), 1e-4, g, 100, None) == L.MPM_ERR_INVALID
-    assert lib.mpm_grid_update(ct.byref(d), grid, ct.c_void_p(4096), 1e-4, None, 2, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_update(ct.byref(d), None, grid, ct.c_void_p(4096), 1e-4, g, 100, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_update(ct.byref(d), None, grid, ct.c_void_p(4096), 1e-4, None, 2, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_update(ct.byref(d), ct.c_void_p(4100), grid, ct.c_void_p(4096), 1e-4, g, 2,
+                               None) == L.MPM_ERR_INVALID
     p3 = L.mpm_particles(10, 4096, 4096, None, 4096)
     assert lib.mpm_g2p(ct.byref(d), ct.c_void_p(4096), ct.byref(p3), 1e-4, status, None) == L.MPM_ERR_INVALID

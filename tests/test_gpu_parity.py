@@ -373,7 +373,8 @@ def _oracle_substep(w, host, grid_shape):
 
 def _run_substeps(mpm, w, host, checkpoints, binned=True):
     """GPU substeps; at each checkpoint substep k (1-based) records the state
-    before the substep, the P2G grid of the substep and the state after."""
+    before the substep, the P2G grid of the substep and the state after.
+    With binning, the grid update is restricted to the reachable node tiles."""
     from material_point_particle_amd.transfer import DeviceParticles, Transfer
     ex = w.extra
     parts = DeviceParticles(host)
@@ -387,13 +388,51 @@ def _run_substeps(mpm, w, host, checkpoints, binned=True):
         if k in checkpoints:
             torch.cuda.synchronize()
             g = tr.grid.cpu().numpy()
-        tr.grid_update(ex["dt"], ex["gravity"], ex["sticky"])
+        tr.grid_update(ex["dt"], ex["gravity"], ex["sticky"], active=binned)
         tr.g2p(parts, ex["dt"])
         if k in checkpoints:
             torch.cuda.synchronize()
             rec[k] = (before, g, parts.host())
             say("substep", k)
     return rec, u32(tr.status)
+
+
+def test_active_grid_update_matches_dense_on_reachable_nodes(mpm, oracle_lib):
+    """The grid update restricted to the node tiles that the binned P2G can
+    reach: bit-exact against the oracle's dense update there, vg untouched
+    elsewhere, every accumulator zero afterwards, and every node P2G touched
+    inside a reachable tile."""
+    from material_point_particle_amd.transfer import DeviceParticles, Transfer
+    w = scaled(WORKLOADS["dam_3d_256"], 1 << 16, n=64)
+    host = build(w)
+    ex = w.extra
+    parts = DeviceParticles(host)
+    tr = Transfer(w.dim, w.n, w.frac_bits, ranges_of(w), parts.n)
+    tr.bin(parts)
+    tr.p2g(parts, binned=True)
+    torch.cuda.synchronize()
+    grid0 = tr.grid.cpu().numpy()
+    tr.vg.fill_(12345.0)
+    say("active grid update")
+    tr.grid_update(ex["dt"], ex["gravity"], ex["sticky"], active=True)
+    torch.cuda.synchronize()
+    lay = tr.layout
+    vg_ref = oracle_lib.grid_update(w.dim, w.n, grid0.copy(), ex["dt"], ex["gravity"], ex["sticky"])
+    nt = w.n // 4
+    tcount = u32(tr.ws_u32("tile_count", lay.n_tiles)).reshape(nt, nt, nt) != 0       # [tz][ty][tx]
+    want = np.zeros_like(tcount)
+    for dz in (0, 1):
+        for dy in (0, 1):
+            for dx in (0, 1):
+                want[dz:, dy:, dx:] |= tcount[:nt - dz, :nt - dy, :nt - dx]
+    act = tr.ws.view(torch.uint8)[lay.tile_active: lay.tile_active + lay.n_tiles].cpu().numpy().reshape(nt, nt, nt)
+    assert np.array_equal(act != 0, want)
+    node_act = np.repeat(np.repeat(np.repeat(want, 4, 0), 4, 1), 4, 2)                  # [z][y][x] per node
+    assert not np.any((grid0 != 0).any(axis=0) & ~node_act), "a deposit outside the reachable tiles"
+    vg = tr.vg.cpu().numpy()
+    assert np.array_equal(vg[:, node_act], vg_ref[:, node_act])
+    assert np.all(vg[:, ~node_act] == 12345.0)
+    assert int(tr.grid.abs().sum()) == 0
 
 
 def test_substeps_lockstep_with_oracle_small(mpm, oracle_lib):
