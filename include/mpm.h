@@ -95,28 +95,22 @@ typedef struct {
     size_t tile_start;      /* uint32 [n_tiles + 1] first record of each tile (exclusive prefix sum) */
     size_t tile_active;     /* uint8  [n_tiles] written by mpm_grid_update when given the bins: 1
                                         for the node tiles that P2G from these bins can reach */
-    size_t tile_row_start;  /* uint32 [n_tiles + 1] first row of group entries of each tile      */
     size_t item_start;      /* uint32 [n_tiles + 1] first full P2G work item of each tile       */
     size_t items;           /* uint32 [max_items][4] work items: tile, first record, records (a
                                         slice of at most rows_per_item rows' worth of a tile's
-                                        records), first row of its group entries; handed out
-                                        alternately the largest and smallest remaining     */
-    size_t meta;            /* uint32 [16]: [0] items, [1] rows, [2] binned particles,
-                                        [3] P2G work cursor, [4] group entries (rows * 256) */
+                                        records), 0; handed out alternately the largest and
+                                        smallest remaining                                 */
+    size_t meta;            /* uint32 [16]: [0] items, [2] binned particles, [3] P2G work cursor */
     size_t rank;            /* uint32 [n] rank of each particle inside its tile (internal)      */
     size_t slot;            /* uint32 [n] record index of each particle (0xFFFFFFFF: not binned) */
     size_t cell_key;        /* uint8  [n] local cell number of each record, in record order      */
-    size_t perm;            /* uint32 [max_slots] group entries: rows of 64 lanes x 4 entries; an
-                                        entry is a record index, with bit 31 set when it
-                                        completes a cell's last group (read with zero mass);
-                                        0xFFFFFFFF in a group's first entry: no group      */
     size_t sorted;          /* float  [n][n_fields] binned records x, v, C, m (+ padding floats),
                                         tile by tile                                       */
-    size_t tile_tmp;        /* uint32 [3][n_tiles] per-tile rows, full items, partial item (internal) */
+    size_t tile_tmp;        /* uint32 [2][n_tiles] per-tile full slices, partial slice (internal) */
     size_t scan_tmp;        /* uint32 [scan_blocks] prefix-sum block totals (internal)          */
     size_t item_hist;       /* uint32 [rows_per_item][ceil(n_tiles/256)] partial-slice rows per block (internal) */
     size_t item_hist_start; /* uint32 prefix sum of item_hist (internal)                          */
-    int64_t n_cells, n_tiles, max_items, max_slots, n_fields, rows_per_item;
+    int64_t n_cells, n_tiles, max_items, n_fields, rows_per_item;
     size_t total_bytes;
 } mpm_ws_layout;
 
@@ -153,14 +147,14 @@ int mpm_workspace_layout(const mpm_grid_desc *grid, int64_t n_particles, mpm_ws_
  * Codebases", section 2.1: sort + tile).  The caller's arrays are not
  * reordered (section 5 rule 2): the workspace receives the tile histogram
  * and prefix sum, each particle's record index, a binned copy of x, v, C, m
- * (64-byte records, 48 in 2D) tile by tile, and for each tile its records
- * sorted by cell (inside a 3D tile cells are numbered x fastest, then z,
- * then y) as groups of 4 same-cell entries, each cell completed to a
- * multiple of 4 by pad entries, one group per lane of a 256-entry row; and
- * the P2G work items.  Particles whose stencil leaves the grid are not binned and
+ * (64-byte records, 48 in 2D) tile by tile with each record's local cell
+ * number (inside a 3D tile cells are numbered x fastest, then z, then y), and
+ * the P2G work items: slices of each tile's records, which mpm_p2g sorts by
+ * cell on chip.
+ * Particles whose stencil leaves the grid are not binned and
  * are counted in status[0]; particles whose attributes leave the declared
  * ranges are binned as zero-mass records (they contribute nothing, exactly
- * as if skipped) and counted in status[1].  Arrival order inside a cell is
+ * as if skipped) and counted in status[1].  Arrival order inside a tile is
  * not deterministic; the P2G grid built from the bins is (integer sums
  * commute).
  * particles, status: device.  ws: device, ws_bytes >= mpm_workspace_bytes().
@@ -188,8 +182,10 @@ int mpm_bin_particles(const mpm_grid_desc *grid, const mpm_particles *particles,
  *     atomics; skipped particles are counted in status[0]/status[1].
  *   bins != NULL: the workspace filled by mpm_bin_particles for these
  *     particles on this grid (particles may be NULL); one wavefront per
- *     work item of one tile accumulates the tile's node block on chip and
- *     flushes it with one 64-bit atomic per non-zero node and channel.
+ *     work item (a slice of one tile's records) sorts the slice by cell in
+ *     LDS, sums each 4 same-cell particles' contributions in registers,
+ *     accumulates the tile's node block on chip and flushes it with one
+ *     64-bit atomic per non-zero node and channel.
  * grid: device int64[1+dim][n]^dim, accumulated into (zero it first for a
  * fresh transfer).  The caller must have run mpm_check_bounds on `ranges`;
  * this call re-checks and refuses with MPM_ERR_OVERFLOW.

@@ -30,8 +30,8 @@ namespace {
 
 using namespace mpmk;
 
-// Binned group entries hold a record index below 2^31 (bit 31 flags pads).
-constexpr int64_t kMaxParticles = 0x7FFFFFF0;
+// Record indices and tile ranks are uint32.
+constexpr int64_t kMaxParticles = 0xFFFFFFF0;
 
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
@@ -108,14 +108,9 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     const int64_t n_tiles = pow_int(g->n / kTile, g->dim);
     const int64_t busy = np < n_tiles ? (np > 0 ? np : 1) : n_tiles;       // tiles that can hold particles
     // work items: every non-empty tile's records cut into slices, all full
-    // but the last; each item's occupied cells (at most min(records, cells))
-    // add at most kGroup-1 pad entries each, and each item at most one partly
-    // filled row
+    // but the last
     const int64_t slice = g->dim == 3 ? slice_records<3>() : slice_records<2>();
-    const int64_t cells = g->dim == 3 ? cells_per_tile<3>() : cells_per_tile<2>();
     const int64_t max_items = np / slice + busy;
-    const int64_t pads = (kGroup - 1) * (np < cells * max_items ? np : cells * max_items);
-    const int64_t max_rows = (np + pads + kRowSlots - 1) / kRowSlots + max_items;
     const int64_t n_fields = g->dim == 3 ? rec_floats<3>() : rec_floats<2>();
     // (the item histogram is shorter than n_tiles)
     const int64_t scan_blocks = (n_tiles + kScanTileElems - 1) / kScanTileElems + 1;
@@ -130,16 +125,14 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     o->tile_count = take(u4 * (size_t)n_tiles);
     o->tile_start = take(u4 * (size_t)(n_tiles + 1));
     o->tile_active = take((size_t)n_tiles);          // (offsets up to here do not depend on np)
-    o->tile_row_start = take(u4 * (size_t)(n_tiles + 1));
     o->item_start = take(u4 * (size_t)(n_tiles + 1));
     o->items = take(u4 * 4 * (size_t)max_items);
     o->meta = take(u4 * 16);
     o->rank = take(u4 * (size_t)n1);
     o->slot = take(u4 * (size_t)n1);
     o->cell_key = take((size_t)n1);
-    o->perm = take(u4 * (size_t)(max_rows * kRowSlots));
     o->sorted = take(sizeof(float) * (size_t)(n_fields * n1));
-    o->tile_tmp = take(u4 * 3 * (size_t)n_tiles);
+    o->tile_tmp = take(u4 * 2 * (size_t)n_tiles);
     o->scan_tmp = take(u4 * (size_t)scan_blocks);
     const int64_t hist_len = kRowsPerItem * ((n_tiles + 255) / 256);
     o->item_hist = take(u4 * (size_t)hist_len);
@@ -147,7 +140,6 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     o->n_cells = n_cells;
     o->n_tiles = n_tiles;
     o->max_items = max_items;
-    o->max_slots = max_rows * kRowSlots;
     o->n_fields = n_fields;
     o->rows_per_item = kRowsPerItem;
     o->total_bytes = off;
@@ -159,14 +151,12 @@ BinView bin_view(void *ws, const mpm_ws_layout &l)
     BinView v;
     v.tile_count = (uint32_t *)(b + l.tile_count);
     v.tile_start = (uint32_t *)(b + l.tile_start);
-    v.tile_row_start = (uint32_t *)(b + l.tile_row_start);
     v.item_start = (uint32_t *)(b + l.item_start);
     v.items = (uint32_t *)(b + l.items);
     v.meta = (uint32_t *)(b + l.meta);
     v.rank = (uint32_t *)(b + l.rank);
     v.slot = (uint32_t *)(b + l.slot);
     v.cell_key = (uint8_t *)(b + l.cell_key);
-    v.perm = (uint32_t *)(b + l.perm);
     v.sorted = (float *)(b + l.sorted);
     v.tile_tmp = (uint32_t *)(b + l.tile_tmp);
     v.tile_active = (uint8_t *)(b + l.tile_active);
@@ -176,7 +166,6 @@ BinView bin_view(void *ws, const mpm_ws_layout &l)
     v.n_cells = l.n_cells;
     v.n_tiles = l.n_tiles;
     v.max_items = l.max_items;
-    v.max_slots = l.max_slots;
     v.n_fields = l.n_fields;
     return v;
 }

@@ -4,8 +4,8 @@
 // exclusive prefix sum, and a scatter of each particle to its place; the
 // implementation page's section 2.1 bins particles into tiles every substep
 // and builds an index table so the particle arrays themselves never move.
-// Here the sort is two-level: particles are counting-sorted by tile, and the
-// cells inside each tile are sorted on chip.
+// Here the particles are counting-sorted by tile; P2G sorts the cells of each
+// work item on chip.
 //
 // Passes (all on the caller's stream, no host synchronisation):
 //   1. count    blocks of up to 65,536 consecutive particles (a chunk): each
@@ -17,28 +17,17 @@
 //   2. scan     exclusive prefix sum of the tile counts: each tile's first
 //               record.
 //   3. layout   each tile's records are cut into slices of at most
-//               slice_records(), one P2G work item each, whose groups of
-//               kGroup same-cell entries fill at most kRowsPerItem rows of
-//               kRowSlots entries (one group per lane; the rows are sized from
-//               the slice's count alone, an upper bound on its padded groups);
-//               rows and full slices prefix-summed over tiles, partial slices
-//               counting-sorted by rows.
+//               slice_records(), one P2G work item each; full slices counted
+//               and prefix-summed over tiles, partial slices counting-sorted
+//               by the rows their groups need.
 //   4. items    the 16-byte record of every work item, alternately from the
 //               large and the small end of the size order.
 //   5. scatter  the same chunks as pass 1: each particle's 64-byte record
 //               (x, v, C, m in 3D) goes to its tile's record range at its
 //               rank, with the cell's local number beside it.  A chunk's
 //               particles of one tile land in one contiguous run.
-//   6. groups   one block per work item: the slice's records are
-//               counting-sorted by cell in LDS and their indices written as
-//               group entries in the item's rows, transposed (group g of an
-//               item with R rows sits in lane g / R of row g % R); entries
-//               that complete a cell's last group name one of the cell's
-//               records with the pad flag (P2G reads it with zero mass),
-//               groups past the last are marked empty.
 // Arrival ranks depend on scheduling, so record order inside a tile differs
-// between runs; every group holds kGroup entries of one cell, which is all
-// P2G needs.
+// between runs; P2G's grid does not depend on it.
 #include "common.hpp"
 
 namespace mpmk {
@@ -47,18 +36,6 @@ namespace {
 constexpr int kScanBlock = 256;
 constexpr int kScanItems = 16;
 constexpr int kScanTile = kScanBlock * kScanItems;
-
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v)
-{
-    const int lane = threadIdx.x % kWave;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t o = __shfl_up(v, d, kWave);
-        if (lane >= d)
-            v += o;
-    }
-    return v;
-}
 
 // Exclusive scan across the block of one value per thread; returns the
 // exclusive prefix and writes the block total to *total.
@@ -346,8 +323,8 @@ __global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, f
 
 // Pass 3: each tile's records are cut into slices of slice_records() (the
 // last one shorter), one P2G work item each; a slice's groups fill at most
-// kRowsPerItem rows.  Per tile: its rows, its full slices and the rows of
-// its last, partial slice.  P2G hands items out dynamically; the items are
+// kRowsPerItem rows.  Per tile: its full slices and the rows of its last,
+// partial slice.  P2G hands items out dynamically; the items are
 // ordered by size (all full slices, then the partial slices by decreasing
 // rows) and handed out alternately from both ends of that order (see
 // items_kernel).  The partial slices are counting-sorted by rows: one block of
@@ -356,7 +333,6 @@ __global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, f
 // prefix sum.  One thread per tile.
 template <int DIM>
 __global__ void __launch_bounds__(256) tile_layout_kernel(const uint32_t *__restrict__ tile_count, int64_t n_tiles,
-                                                           uint32_t *__restrict__ tile_rows,
                                                            uint32_t *__restrict__ tile_full,
                                                            uint32_t *__restrict__ tile_part,
                                                            uint32_t *__restrict__ item_hist)
@@ -372,7 +348,6 @@ __global__ void __launch_bounds__(256) tile_layout_kernel(const uint32_t *__rest
         const uint32_t full = c / S, rem = c % S;
         const uint32_t part = rem != 0u ? rows_bound<DIM>(rem) : 0u;      // 1 .. kRowsPerItem
         uint32_t rank = 0;
-        tile_rows[t] = full * kRowsPerItem + part;
         tile_full[t] = full;
         if (part != 0u)
             rank = atomicAdd(&hist[part], 1u);
@@ -385,13 +360,12 @@ __global__ void __launch_bounds__(256) tile_layout_kernel(const uint32_t *__rest
 }
 
 // Pass 4: the work items of each tile.  One 16-byte record per item: tile,
-// first record, records, first row of its group entries.
+// first record, records, 0.
 template <int DIM>
 __global__ void __launch_bounds__(256) items_kernel(const uint32_t *__restrict__ tile_full,
                                                      const uint32_t *__restrict__ tile_part,
                                                      const uint32_t *__restrict__ full_start,
                                                      const uint32_t *__restrict__ hist_start,
-                                                     const uint32_t *__restrict__ tile_row_start,
                                                      const uint32_t *__restrict__ tile_start, int64_t n_tiles,
                                                      int64_t layout_blocks, uint4 *__restrict__ items)
 {
@@ -406,26 +380,24 @@ __global__ void __launch_bounds__(256) items_kernel(const uint32_t *__restrict__
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n_tiles; t += (int64_t)gridDim.x * blockDim.x) {
         const uint32_t k = tile_full[t], s0 = full_start[t];
         const uint32_t c0 = tile_start[t], count = tile_start[t + 1] - c0;
-        const uint32_t base = tile_row_start[t];
         for (uint32_t c = 0; c < k; ++c)
-            items[place(s0 + c)] = make_uint4((uint32_t)t, c0 + c * S, S, base + c * kRowsPerItem);
+            items[place(s0 + c)] = make_uint4((uint32_t)t, c0 + c * S, S, 0u);
         const uint32_t part = tile_part[t] >> 16;
         if (part != 0u) {
             const uint32_t q = place(n_full + hist_start[(int64_t)(kRowsPerItem - part) * layout_blocks + t / 256] +
                                      (tile_part[t] & 0xFFFFu));
-            items[q] = make_uint4((uint32_t)t, c0 + k * S, count - k * S, base + k * kRowsPerItem);
+            items[q] = make_uint4((uint32_t)t, c0 + k * S, count - k * S, 0u);
         }
     }
 }
 
+// meta: [0] work items, [3] P2G's work cursor ([2], the binned particles, is
+// added to by pass 1).
 __global__ void meta_kernel(const uint32_t *__restrict__ full_start, const uint32_t *__restrict__ hist_start,
-                            int64_t hist_len, const uint32_t *__restrict__ tile_row_start, int64_t n_tiles,
-                            uint32_t *__restrict__ meta)
+                            int64_t hist_len, int64_t n_tiles, uint32_t *__restrict__ meta)
 {
     meta[0] = full_start[n_tiles] + hist_start[hist_len];
-    meta[1] = tile_row_start[n_tiles];
     meta[3] = 0u;
-    meta[4] = tile_row_start[n_tiles] * (uint32_t)kRowSlots;
 }
 
 // Pass 5: each binned particle's record at its tile's first record plus its
@@ -576,86 +548,6 @@ __global__ void __launch_bounds__(kBinThreads) bin_scatter_kernel(Fields f, Rang
     }
 }
 
-// Entry index of padded cell-sorted position s in an item whose rows start
-// at row0 and number `rows`: group g = s / kGroup sits in lane g / rows of row
-// g % rows, entry s % kGroup.
-__device__ __forceinline__ int64_t entry_of(int64_t row0, uint32_t rows, uint32_t s)
-{
-    const uint32_t g = s / kGroup;
-    return ((row0 + g % rows) * kWave + g / rows) * kGroup + s % kGroup;
-}
-
-// Pass 6: one block per work item (a slice of at most slice_records() records
-// of one tile).  The cells' counts come from an LDS histogram of the slice's
-// cell keys; a wave prefix sum of the counts rounded up to whole groups gives
-// each cell's first padded position; a second sweep places every record (LDS
-// cursor per cell), and the record placed first in a cell also fills the
-// cell's pad entries.  Groups between the last one and the bound are marked
-// empty.  The keys stay in registers between the sweeps.
-constexpr int kGroupThreads = 256;
-
-template <int DIM>
-__global__ void __launch_bounds__(kGroupThreads) bin_groups_kernel(const uint4 *__restrict__ items,
-                                                                    const uint32_t *__restrict__ meta,
-                                                                    const uint8_t *__restrict__ cell_key,
-                                                                    uint32_t *__restrict__ perm)
-{
-    static_assert(cells_per_tile<DIM>() <= (uint32_t)kWave, "one lane per cell of a tile");
-    constexpr int kKeys = (int)((slice_records<DIM>() + kGroupThreads - 1) / kGroupThreads);
-    __shared__ uint32_t cnt[kWave], start[kWave], cur[kWave];
-    const int tid = threadIdx.x;
-    const uint32_t n_items = meta[0];
-    for (uint32_t it = blockIdx.x; it < n_items; it += gridDim.x) {
-        const uint4 item = items[it];
-        const uint32_t first = item.y, count = item.z;
-        const int64_t row0 = item.w;
-        const uint32_t rows = rows_bound<DIM>(count);
-        uint32_t l[kKeys];
-#pragma unroll
-        for (int k = 0; k < kKeys; ++k) {
-            const uint32_t i = k * kGroupThreads + tid;
-            l[k] = i < count ? (uint32_t)cell_key[first + i] : kEmpty;
-        }
-        if (tid < kWave)
-            cnt[tid] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < kKeys; ++k)
-            if (l[k] != kEmpty)
-                atomicAdd(&cnt[l[k]], 1u);
-        __syncthreads();
-        if (tid < kWave) {
-            const uint32_t padded = (cnt[tid] + kGroup - 1) / kGroup * kGroup;
-            const uint32_t inc = wave_inclusive_scan(padded);
-            start[tid] = inc - padded;
-            cur[tid] = inc - padded;
-            const uint32_t bound = groups_bound<DIM>(count);
-            for (uint32_t g = __shfl(inc, kWave - 1, kWave) / kGroup + tid; g < bound; g += kWave)
-                perm[entry_of(row0, rows, g * kGroup)] = kEmpty;
-        }
-        __syncthreads();
-        uint32_t pos[kKeys];
-#pragma unroll
-        for (int k = 0; k < kKeys; ++k)
-            pos[k] = l[k] != kEmpty ? atomicAdd(&cur[l[k]], 1u) : 0u;
-#pragma unroll
-        for (int k = 0; k < kKeys; ++k) {
-            if (l[k] == kEmpty)
-                continue;
-            const uint32_t rec = first + k * kGroupThreads + tid;
-            perm[entry_of(row0, rows, pos[k])] = rec;
-            const uint32_t s0 = start[l[k]];
-            if (pos[k] == s0) {                      // the cell's first position: fill its pads
-                const uint32_t n_l = cnt[l[k]];
-                const uint32_t padded = (n_l + kGroup - 1) / kGroup * kGroup;
-                for (uint32_t q = s0 + n_l; q < s0 + padded; ++q)
-                    perm[entry_of(row0, rows, q)] = kPadFlag | rec;
-            }
-        }
-        __syncthreads();
-    }
-}
-
 int blocks_for(int64_t work, int block)
 {
     const int64_t want = (work + block - 1) / block;
@@ -669,12 +561,13 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
 {
     const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3);
     const int ntx = n / kTile;
-    uint32_t *tile_rows = b.tile_tmp, *tile_items = b.tile_tmp + b.n_tiles, *tile_part = b.tile_tmp + 2 * b.n_tiles;
+    uint32_t *tile_items = b.tile_tmp, *tile_part = b.tile_tmp + b.n_tiles;
     hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, b.tile_count, b.n_tiles,
                        0u);
     hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, s, b.meta, (int64_t)16, 0u);
-    // particles per thread of a chunk: enough chunks for every CU, at most kMaxPer
-    int64_t per = (p.n + (int64_t)kBinThreads * device_cu_count() - 1) / ((int64_t)kBinThreads * device_cu_count());
+    // particles per thread of a chunk: enough chunks for two blocks per CU, at most kMaxPer
+    const int64_t span = (int64_t)kBinThreads * device_cu_count() * 2;
+    int64_t per = (p.n + span - 1) / span;
     per = per < 4 ? 4 : (per > kMaxPer ? kMaxPer : per);
     const int64_t chunks = (p.n + kBinThreads * per - 1) / (kBinThreads * per);
     const unsigned cblocks = (unsigned)(chunks < (int64_t)device_cu_count() * 2 ? chunks : device_cu_count() * 2);
@@ -693,12 +586,10 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
     const int64_t hist_len = kRowsPerItem * lblocks;
     if (dim == 3)
         hipLaunchKernelGGL(tile_layout_kernel<3>, dim3((unsigned)lblocks), dim3(256), 0, s, b.tile_count, b.n_tiles,
-                           tile_rows, tile_items, tile_part, b.item_hist);
+                           tile_items, tile_part, b.item_hist);
     else
         hipLaunchKernelGGL(tile_layout_kernel<2>, dim3((unsigned)lblocks), dim3(256), 0, s, b.tile_count, b.n_tiles,
-                           tile_rows, tile_items, tile_part, b.item_hist);
-    if ((e = exclusive_scan<1>(tile_rows, b.n_tiles, b.tile_row_start, b.scan_tmp, s)) != hipSuccess)
-        return e;
+                           tile_items, tile_part, b.item_hist);
     if ((e = exclusive_scan<1>(tile_items, b.n_tiles, b.item_start, b.scan_tmp, s)) != hipSuccess)
         return e;
     if ((e = exclusive_scan<1>(b.item_hist, hist_len, b.item_hist_start, b.scan_tmp, s)) != hipSuccess)
@@ -706,26 +597,20 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
     uint4 *items = reinterpret_cast<uint4 *>(b.items);
     if (dim == 3)
         hipLaunchKernelGGL(items_kernel<3>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_items, tile_part,
-                           b.item_start, b.item_hist_start, b.tile_row_start, b.tile_start, b.n_tiles, lblocks, items);
+                           b.item_start, b.item_hist_start, b.tile_start, b.n_tiles, lblocks, items);
     else
         hipLaunchKernelGGL(items_kernel<2>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_items, tile_part,
-                           b.item_start, b.item_hist_start, b.tile_row_start, b.tile_start, b.n_tiles, lblocks, items);
-    hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(1), 0, s, b.item_start, b.item_hist_start, hist_len,
-                       b.tile_row_start, b.n_tiles, b.meta);
+                           b.item_start, b.item_hist_start, b.tile_start, b.n_tiles, lblocks, items);
+    hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(1), 0, s, b.item_start, b.item_hist_start, hist_len, b.n_tiles,
+                       b.meta);
     const unsigned sblocks = (unsigned)(chunks < (int64_t)device_cu_count() * 8 ? chunks : device_cu_count() * 8);
-    const unsigned gblocks = (unsigned)blocks_for(b.max_items, 1);      // one block per item, capped
-    if (dim == 3) {
-        if (chunks > 0)
+    if (chunks > 0) {
+        if (dim == 3)
             hipLaunchKernelGGL(bin_scatter_kernel<3>, dim3(sblocks), dim3(kBinThreads), 0, s, p, r, nf, dx, last, ntx,
                                chunks, (int)per, b.rank, b.tile_start, b.slot, b.cell_key, b.sorted, status);
-        hipLaunchKernelGGL(bin_groups_kernel<3>, dim3(gblocks), dim3(kGroupThreads), 0, s, items, b.meta, b.cell_key,
-                           b.perm);
-    } else {
-        if (chunks > 0)
+        else
             hipLaunchKernelGGL(bin_scatter_kernel<2>, dim3(sblocks), dim3(kBinThreads), 0, s, p, r, nf, dx, last, ntx,
                                chunks, (int)per, b.rank, b.tile_start, b.slot, b.cell_key, b.sorted, status);
-        hipLaunchKernelGGL(bin_groups_kernel<2>, dim3(gblocks), dim3(kGroupThreads), 0, s, items, b.meta, b.cell_key,
-                           b.perm);
     }
     return hipGetLastError();
 }

@@ -14,7 +14,6 @@
 namespace mpmk {
 
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
-constexpr uint32_t kPadFlag = 0x80000000u;  // group entry that completes a cell's last group
 constexpr int kWave = 64;
 constexpr int kTile = 4;             // tile edge in cells
 constexpr int kGroup = 4;            // records per group: one cell's particles, four at a time
@@ -121,6 +120,19 @@ struct RangesF {
     float max_mass, max_speed, max_affine;
 };
 
+// Inclusive prefix sum of v over the lanes of the wavefront.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v)
+{
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t o = __shfl_up(v, d, kWave);
+        if (lane >= d)
+            v += o;
+    }
+    return v;
+}
+
 // Count the lanes of the wavefront for which `pred` holds with one atomic.
 __device__ __forceinline__ void wave_count(bool pred, uint32_t *counter)
 {
@@ -139,11 +151,11 @@ struct Fields {           // component-major particle arrays of n particles
 };
 
 struct BinView {          // the workspace arrays, as typed device pointers
-    uint32_t *tile_count, *tile_start, *tile_row_start, *item_start, *items, *meta, *rank, *slot, *perm,
-        *tile_tmp, *scan_tmp, *item_hist, *item_hist_start;
+    uint32_t *tile_count, *tile_start, *item_start, *items, *meta, *rank, *slot, *tile_tmp, *scan_tmp, *item_hist,
+        *item_hist_start;
     uint8_t *cell_key, *tile_active;
     float *sorted;
-    int64_t n_cells, n_tiles, max_items, max_slots, n_fields;
+    int64_t n_cells, n_tiles, max_items, n_fields;
 };
 
 hipError_t launch_p2g_direct(int dim, int n, int frac_bits, const Fields &p, const uint32_t *order, RangesF r,

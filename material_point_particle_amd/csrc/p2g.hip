@@ -169,17 +169,16 @@ __global__ void __launch_bounds__(256) p2g_direct_kernel(Fields f, const uint32_
 
 // ---------------------------------------------------------------------------
 // Tiled path.  The bins hold each tile's particle records (64 bytes: x, v, C,
-// m in 3D) in one contiguous range, cut into slices of at most
-// slice_records(), one work item each, and per item rows of group entries:
-// the slice's records sorted by cell, each cell completed to whole groups of
-// kGroup entries (a completing entry names one of the cell's records with the
-// pad flag, read with zero mass), and the groups laid out "transposed": group
-// g of an item with R rows sits in lane g / R of row g % R, its kGroup entries
-// as one 16-byte word.  A wavefront takes one item: every lane holds kGroup
-// particles of one cell, and the 64 lanes are R groups apart in cell order, so
-// they are mostly in different cells and write different node addresses at
-// the same instruction.  A row's entries are 1 KB of contiguous memory; the
-// records they name lie in the slice's contiguous range.
+// m in 3D) in one contiguous range with each record's cell key beside it, cut
+// into slices of at most slice_records(), one work item each.  A wavefront
+// takes one item and first sorts the slice by cell in LDS into rows of group
+// entries: each cell completed to whole groups of kGroup entries (a
+// completing entry names one of the cell's records, read with zero mass), and
+// the groups laid out "transposed": group g of an item with R rows sits in
+// lane g / R of row g % R.  Every lane then holds kGroup particles of one
+// cell, and the 64 lanes are R groups apart in cell order, so they are mostly
+// in different cells and write different node addresses at the same
+// instruction.  The records a row names lie in the slice's contiguous range.
 //
 // Per lane and stencil node, the group's kGroup quantised contributions are
 // summed in float64 registers and added to the on-chip node block with one LDS
@@ -258,7 +257,8 @@ __device__ __forceinline__ void group_hoist(const float *rec, float nf, float dx
 
 struct TiledArgs {
     const float *sorted;
-    const uint32_t *perm, *items, *meta;
+    const uint8_t *cell_key;
+    const uint32_t *items, *meta;
     uint32_t *cursor;
     int n, ntx;
     float nf, dx, last_base, S;
@@ -267,6 +267,88 @@ struct TiledArgs {
 };
 
 __global__ void reset_cursor_kernel(uint32_t *cursor) { *cursor = 0u; }
+
+// Group entries of the item being processed, in LDS: a record's offset in the
+// slice, with kPad16 set when the entry only completes its cell's last group
+// (read with zero mass); kEmpty16 in a group's first entry where the lane
+// holds no group.
+constexpr uint16_t kPad16 = 0x8000u;
+constexpr uint16_t kEmpty16 = 0xFFFFu;
+constexpr int kSortKeys = 16;                 // cell keys per lane per memory round trip
+
+// Entry index of padded cell-sorted position s in an item with `rows` rows:
+// group g = s / kGroup sits in lane g / rows of row g % rows, entry s % kGroup.
+// magic = ceil(2^32 / rows) for rows > 1 (exact for g < 2^24).
+__device__ __forceinline__ uint32_t entry16(uint32_t s, uint32_t rows, uint32_t magic)
+{
+    const uint32_t g = s / kGroup;
+    const uint32_t q = rows == 1u ? g : __umulhi(g, magic);
+    return ((g - q * rows) * kWave + q) * kGroup + s % kGroup;
+}
+
+// Counting sort of the item's records by cell into its rows of group
+// entries ("Particle worlds, part 3", steps 3-4, on chip): an LDS histogram of
+// the slice's cell keys, a wave prefix sum of the counts rounded up to whole
+// groups (each cell's first padded position), then every record placed
+// through an LDS cursor per cell; the record placed first in its cell also
+// writes the cell's pad entries.  One wavefront; `keys` are the slice's cell
+// keys.
+template <int DIM>
+__device__ __forceinline__ void sort_item(const uint8_t *__restrict__ keys, uint32_t count, uint32_t groups,
+                                          uint32_t rows, uint16_t *ent, uint32_t *cnt, uint32_t *cur,
+                                          uint32_t *cstart, int lane)
+{
+    const uint32_t magic = rows > 1u ? 0xFFFFFFFFu / rows + 1u : 0u;
+    cnt[lane] = 0u;
+    __syncthreads();
+    for (uint32_t base = 0; base < count; base += kWave * kSortKeys) {
+        uint32_t l[kSortKeys];
+#pragma unroll
+        for (int k = 0; k < kSortKeys; ++k) {
+            const uint32_t i = base + k * kWave + lane;
+            l[k] = i < count ? (uint32_t)keys[i] : kEmpty;
+        }
+#pragma unroll
+        for (int k = 0; k < kSortKeys; ++k)
+            if (l[k] != kEmpty)
+                atomicAdd(&cnt[l[k]], 1u);
+    }
+    __syncthreads();
+    const uint32_t n_l = cnt[lane];
+    const uint32_t padded = (n_l + kGroup - 1) / kGroup * kGroup;
+    const uint32_t inc = wave_inclusive_scan(padded);
+    cstart[lane] = inc - padded;
+    cur[lane] = inc - padded;
+    for (uint32_t g = __shfl(inc, kWave - 1, kWave) / kGroup + lane; g < groups; g += kWave)
+        ent[entry16(g * kGroup, rows, magic)] = kEmpty16;
+    __syncthreads();
+    for (uint32_t base = 0; base < count; base += kWave * kSortKeys) {
+        uint32_t l[kSortKeys];
+#pragma unroll
+        for (int k = 0; k < kSortKeys; ++k) {
+            const uint32_t i = base + k * kWave + lane;
+            l[k] = i < count ? (uint32_t)keys[i] : kEmpty;
+        }
+        uint32_t pos[kSortKeys];
+#pragma unroll
+        for (int k = 0; k < kSortKeys; ++k)
+            pos[k] = l[k] != kEmpty ? atomicAdd(&cur[l[k]], 1u) : 0u;
+#pragma unroll
+        for (int k = 0; k < kSortKeys; ++k) {
+            if (l[k] == kEmpty)
+                continue;
+            const uint32_t i = base + k * kWave + lane;
+            ent[entry16(pos[k], rows, magic)] = (uint16_t)i;
+            const uint32_t s0 = cstart[l[k]];
+            if (pos[k] == s0) {                          // the cell's first position: fill its pads
+                const uint32_t c = cnt[l[k]];
+                for (uint32_t q = s0 + c; q < s0 + (c + kGroup - 1) / kGroup * kGroup; ++q)
+                    ent[entry16(q, rows, magic)] = (uint16_t)(kPad16 | i);
+            }
+        }
+    }
+    __syncthreads();
+}
 
 template <int DIM>
 __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -277,6 +359,10 @@ p2g_tiled_kernel(TiledArgs a)
     constexpr int G = kGroup;
     constexpr int kFlush = (TS::nodes + kWave - 1) / kWave;      // node-block entries per lane
     __shared__ double acc[TS::ch * TS::nodes];
+    __shared__ __align__(16) uint16_t ent[kRowsPerItem * kRowSlots];
+    __shared__ uint32_t cnt[kWave], cur[kWave], cstart[kWave];
+    static_assert(slice_records<DIM>() < kPad16, "a slice offset must leave the pad bit free");
+    static_assert(cells_per_tile<DIM>() <= (uint32_t)kWave, "one lane per cell of a tile");
     const int lane = threadIdx.x;
     const uint32_t n_items = a.meta[0];
     const int64_t nodes = DIM == 3 ? (int64_t)a.n * a.n * a.n : (int64_t)a.n * a.n;
@@ -311,11 +397,10 @@ p2g_tiled_kernel(TiledArgs a)
             break;
         if (lane == 0)
             next = atomicAdd(a.cursor, 1u);
-        // item: tile, first record, records, first row of its group entries
-        const uint32_t tile = rec_item.x;
-        const uint32_t groups = groups_bound<DIM>(rec_item.z);
+        // item: tile, first record, records (one slice of the tile)
+        const uint32_t tile = rec_item.x, first = rec_item.y, count = rec_item.z;
+        const uint32_t groups = groups_bound<DIM>(count);
         const uint32_t rows = (groups + kWave - 1) / kWave;
-        const int64_t row_base = (int64_t)rec_item.w;
         int torg[3] = { 0, 0, 0 };
         {
             uint32_t t = tile;
@@ -325,27 +410,21 @@ p2g_tiled_kernel(TiledArgs a)
                 t /= (uint32_t)a.ntx;
             }
         }
-        static_assert(kGroup == 4, "a group's entries load as one uint4");
-        const uint4 *entries = reinterpret_cast<const uint4 *>(a.perm);
-        // this lane's group in row j is group lane * rows + j of the tile; the
-        // next row's entries are loaded one row ahead
-        uint4 ent_next = make_uint4(kEmpty, kEmpty, kEmpty, kEmpty);
-        if ((uint32_t)lane * rows < groups)
-            ent_next = entries[row_base * kWave + lane];
+        sort_item<DIM>(a.cell_key + first, count, groups, rows, ent, cnt, cur, cstart, lane);
+        static_assert(kGroup == 4, "a group's entries load as one 8-byte word");
         for (uint32_t j = 0; j < rows; ++j) {
-            const uint4 ent = ent_next;
-            if (j + 1 < rows && (uint32_t)lane * rows + j + 1 < groups)
-                ent_next = entries[(row_base + j + 1) * kWave + lane];
-            // this lane's entries; kEmpty where the lane holds no group
-            const bool live = (uint32_t)lane * rows + j < groups && ent.x != kEmpty;
-            const uint32_t e4[G] = { live ? ent.x : kEmpty, live ? ent.y : kEmpty, live ? ent.z : kEmpty,
-                                     live ? ent.w : kEmpty };
-            if (!live)
+            // this lane's group in row j is group lane * rows + j of the item
+            if ((uint32_t)lane * rows + j >= groups)
+                continue;
+            const uint2 w2 = *reinterpret_cast<const uint2 *>(&ent[(j * kWave + lane) * kGroup]);
+            const uint32_t e4[G] = { w2.x & 0xFFFFu, w2.x >> 16, w2.y & 0xFFFFu, w2.y >> 16 };
+            if (e4[0] == kEmpty16)
                 continue;
             GroupHoist<DIM> h[G];
 #pragma unroll
             for (int k = 0; k < G; ++k) {
-                const float4 *src = reinterpret_cast<const float4 *>(a.sorted + (int64_t)(e4[k] & ~kPadFlag) * R);
+                const float4 *src =
+                    reinterpret_cast<const float4 *>(a.sorted + (int64_t)(first + (e4[k] & ~(uint32_t)kPad16)) * R);
                 float rec[R];
 #pragma unroll
                 for (int q = 0; q < R / 4; ++q) {
@@ -355,7 +434,7 @@ p2g_tiled_kernel(TiledArgs a)
                     rec[4 * q + 2] = t.z;
                     rec[4 * q + 3] = t.w;
                 }
-                if (e4[k] & kPadFlag)                        // completes the cell's group: zero mass
+                if (e4[k] & kPad16)                          // completes the cell's group: zero mass
                     rec[2 * DIM + DIM * DIM] = 0.0f;
                 group_hoist<DIM>(rec, a.nf, a.dx, a.last_base, a.S, h[k]);
             }
@@ -534,7 +613,7 @@ hipError_t launch_p2g_tiled(int dim, int n, int frac_bits, const BinView &b, int
 {
     TiledArgs a;
     a.sorted = b.sorted;
-    a.perm = b.perm;
+    a.cell_key = b.cell_key;
     a.items = b.items;
     a.meta = b.meta;
     a.cursor = b.meta + 3;

@@ -75,13 +75,12 @@ def test_workspace_layout_is_disjoint_and_aligned():
         assert M.mpm_workspace_bytes(d, N) == lay.total_bytes
         assert lay.n_cells == n ** dim and lay.n_tiles == (n // 4) ** dim
         assert lay.n_fields == {2: 12, 3: 16}[dim]     # x, v, C, m padded to a multiple of 4 floats
-        assert lay.max_slots % 256 == 0 and lay.max_slots >= N
         spans = sorted([
             (lay.tile_count, 4 * lay.n_tiles), (lay.tile_start, 4 * (lay.n_tiles + 1)), (lay.tile_active, lay.n_tiles),
-            (lay.tile_row_start, 4 * (lay.n_tiles + 1)), (lay.item_start, 4 * (lay.n_tiles + 1)),
+            (lay.item_start, 4 * (lay.n_tiles + 1)),
             (lay.items, 16 * lay.max_items), (lay.meta, 64), (lay.rank, 4 * max(N, 1)), (lay.slot, 4 * max(N, 1)),
-            (lay.cell_key, max(N, 1)), (lay.perm, 4 * lay.max_slots), (lay.sorted, 4 * lay.n_fields * max(N, 1)),
-            (lay.tile_tmp, 12 * lay.n_tiles),
+            (lay.cell_key, max(N, 1)), (lay.sorted, 4 * lay.n_fields * max(N, 1)),
+            (lay.tile_tmp, 8 * lay.n_tiles),
             (lay.item_hist, 4 * lay.rows_per_item * ((lay.n_tiles + 255) // 256)),
             (lay.item_hist_start, 4 * (lay.rows_per_item * ((lay.n_tiles + 255) // 256) + 1))])
         for (a, la), (b, _) in zip(spans, spans[1:]):

