@@ -95,7 +95,6 @@ typedef struct {
     size_t tile_start;      /* uint32 [n_tiles + 1] first record of each tile (exclusive prefix sum) */
     size_t tile_active;     /* uint8  [n_tiles] written by mpm_grid_update when given the bins: 1
                                         for the node tiles that P2G from these bins can reach */
-    size_t item_start;      /* uint32 [n_tiles + 1] first full P2G work item of each tile       */
     size_t items;           /* uint32 [max_items][4] work items: tile, first record, records (a
                                         slice of at most rows_per_item rows' worth of a tile's
                                         records), 0; handed out alternately the largest and
@@ -106,10 +105,8 @@ typedef struct {
     size_t cell_key;        /* uint8  [n] local cell number of each record, in record order      */
     size_t sorted;          /* float  [n][n_fields] binned records x, v, C, m (+ padding floats),
                                         tile by tile                                       */
-    size_t tile_tmp;        /* uint32 [2][n_tiles] per-tile full slices, partial slice (internal) */
-    size_t scan_tmp;        /* uint32 [scan_blocks] prefix-sum block totals (internal)          */
-    size_t item_hist;       /* uint32 [rows_per_item][ceil(n_tiles/256)] partial-slice rows per block (internal) */
-    size_t item_hist_start; /* uint32 prefix sum of item_hist (internal)                          */
+    size_t scan_tmp;        /* uint32 [ceil(n_tiles/4096)][2 + rows_per_item] per-block sums of the
+                                        work-item plan (internal)                          */
     int64_t n_cells, n_tiles, max_items, n_fields, rows_per_item;
     size_t total_bytes;
 } mpm_ws_layout;

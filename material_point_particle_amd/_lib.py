@@ -41,9 +41,8 @@ class mpm_ranges(ct.Structure):
 
 
 class mpm_ws_layout(ct.Structure):
-    _fields_ = [(name, ct.c_size_t) for name in ("tile_count", "tile_start", "tile_active", "item_start", "items",
-                                                  "meta", "rank", "slot", "cell_key", "sorted", "tile_tmp",
-                                                  "scan_tmp", "item_hist", "item_hist_start")]
+    _fields_ = [(name, ct.c_size_t) for name in ("tile_count", "tile_start", "tile_active", "items", "meta", "rank",
+                                                  "slot", "cell_key", "sorted", "scan_tmp")]
     _fields_ += [(name, ct.c_int64) for name in ("n_cells", "n_tiles", "max_items", "n_fields", "rows_per_item")]
     _fields_ += [("total_bytes", ct.c_size_t)]
 

@@ -112,8 +112,7 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     const int64_t slice = g->dim == 3 ? slice_records<3>() : slice_records<2>();
     const int64_t max_items = np / slice + busy;
     const int64_t n_fields = g->dim == 3 ? rec_floats<3>() : rec_floats<2>();
-    // (the item histogram is shorter than n_tiles)
-    const int64_t scan_blocks = (n_tiles + kScanTileElems - 1) / kScanTileElems + 1;
+    const int64_t plan_blocks = (n_tiles + kPlanTiles - 1) / kPlanTiles;
     size_t off = 0;
     auto take = [&off](size_t bytes) {
         const size_t at = off;
@@ -125,18 +124,13 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     o->tile_count = take(u4 * (size_t)n_tiles);
     o->tile_start = take(u4 * (size_t)(n_tiles + 1));
     o->tile_active = take((size_t)n_tiles);          // (offsets up to here do not depend on np)
-    o->item_start = take(u4 * (size_t)(n_tiles + 1));
     o->items = take(u4 * 4 * (size_t)max_items);
     o->meta = take(u4 * 16);
     o->rank = take(u4 * (size_t)n1);
     o->slot = take(u4 * (size_t)n1);
     o->cell_key = take((size_t)n1);
     o->sorted = take(sizeof(float) * (size_t)(n_fields * n1));
-    o->tile_tmp = take(u4 * 2 * (size_t)n_tiles);
-    o->scan_tmp = take(u4 * (size_t)scan_blocks);
-    const int64_t hist_len = kRowsPerItem * ((n_tiles + 255) / 256);
-    o->item_hist = take(u4 * (size_t)hist_len);
-    o->item_hist_start = take(u4 * (size_t)(hist_len + 1));
+    o->scan_tmp = take(u4 * (size_t)(kPlanStride * plan_blocks));
     o->n_cells = n_cells;
     o->n_tiles = n_tiles;
     o->max_items = max_items;
@@ -151,18 +145,14 @@ BinView bin_view(void *ws, const mpm_ws_layout &l)
     BinView v;
     v.tile_count = (uint32_t *)(b + l.tile_count);
     v.tile_start = (uint32_t *)(b + l.tile_start);
-    v.item_start = (uint32_t *)(b + l.item_start);
     v.items = (uint32_t *)(b + l.items);
     v.meta = (uint32_t *)(b + l.meta);
     v.rank = (uint32_t *)(b + l.rank);
     v.slot = (uint32_t *)(b + l.slot);
     v.cell_key = (uint8_t *)(b + l.cell_key);
     v.sorted = (float *)(b + l.sorted);
-    v.tile_tmp = (uint32_t *)(b + l.tile_tmp);
     v.tile_active = (uint8_t *)(b + l.tile_active);
     v.scan_tmp = (uint32_t *)(b + l.scan_tmp);
-    v.item_hist = (uint32_t *)(b + l.item_hist);
-    v.item_hist_start = (uint32_t *)(b + l.item_hist_start);
     v.n_cells = l.n_cells;
     v.n_tiles = l.n_tiles;
     v.max_items = l.max_items;

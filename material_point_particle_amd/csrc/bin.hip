@@ -14,14 +14,11 @@
 //               (chunk, tile) reserves the chunk's run inside the tile, so a
 //               particle's rank in its tile is its run's base plus its rank
 //               in the chunk.
-//   2. scan     exclusive prefix sum of the tile counts: each tile's first
-//               record.
-//   3. layout   each tile's records are cut into slices of at most
-//               slice_records(), one P2G work item each; full slices counted
-//               and prefix-summed over tiles, partial slices counting-sorted
-//               by the rows their groups need.
-//   4. items    the 16-byte record of every work item, alternately from the
-//               large and the small end of the size order.
+//   2-4. plan   each tile's first record (prefix sum of the counts) and its
+//               work items: the tile's records cut into slices of at most
+//               slice_records(), listed by size (full slices, then partial
+//               slices counting-sorted by the rows their groups need) and
+//               handed out alternately from the two ends of that list.
 //   5. scatter  the same chunks as pass 1: each particle's 64-byte record
 //               (x, v, C, m in 3D) goes to its tile's record range at its
 //               rank, with the cell's local number beside it.  A chunk's
@@ -33,9 +30,6 @@
 namespace mpmk {
 namespace {
 
-constexpr int kScanBlock = 256;
-constexpr int kScanItems = 16;
-constexpr int kScanTile = kScanBlock * kScanItems;
 
 // Exclusive scan across the block of one value per thread; returns the
 // exclusive prefix and writes the block total to *total.
@@ -62,136 +56,21 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *t
     return r;
 }
 
-// The scans read each counter rounded up to a multiple of ROUND (1 or kGroup).
-template <int ROUND>
-__device__ __forceinline__ uint32_t scan_load(const uint32_t *in, int64_t k)
+__global__ void fill2_u32_kernel(uint32_t *__restrict__ p, int64_t np, uint32_t *__restrict__ q, int64_t nq)
 {
-    const uint32_t v = in[k];
-    return ROUND == 1 ? v : (v + (ROUND - 1)) / ROUND * ROUND;
-}
-
-template <int ROUND>
-__global__ void __launch_bounds__(kScanBlock) scan_reduce_kernel(const uint32_t *__restrict__ in, int64_t len,
-                                                                 uint32_t *__restrict__ partial)
-{
-    const int64_t base = (int64_t)blockIdx.x * kScanTile;
-    uint32_t s = 0;
-    for (int i = threadIdx.x; i < kScanTile; i += kScanBlock) {
-        const int64_t k = base + i;
-        if (k < len)
-            s += scan_load<ROUND>(in, k);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < np + nq; i += (int64_t)gridDim.x * blockDim.x) {
+        if (i < np)
+            p[i] = 0u;
+        else
+            q[i - np] = 0u;
     }
-    __shared__ uint32_t tot;
-    (void)block_exclusive_scan<kScanBlock>(s, &tot);
-    __syncthreads();
-    if (threadIdx.x == 0)
-        partial[blockIdx.x] = tot;
-}
-
-// One block: exclusive scan of the per-block sums in place; grand total to *total.
-__global__ void __launch_bounds__(1024) scan_partials_kernel(uint32_t *__restrict__ partial, int64_t nblocks,
-                                                             uint32_t *__restrict__ total)
-{
-    __shared__ uint32_t chunk_total;
-    uint32_t carry = 0;
-    for (int64_t base = 0; base < nblocks; base += 1024) {
-        const int64_t k = base + threadIdx.x;
-        const uint32_t v = k < nblocks ? partial[k] : 0u;
-        const uint32_t ex = block_exclusive_scan<1024>(v, &chunk_total);
-        if (k < nblocks)
-            partial[k] = carry + ex;
-        __syncthreads();
-        carry += chunk_total;
-        __syncthreads();
-    }
-    if (threadIdx.x == 0)
-        *total = carry;
-}
-
-template <int ROUND>
-__global__ void __launch_bounds__(kScanBlock) scan_final_kernel(const uint32_t *__restrict__ in, int64_t len,
-                                                                const uint32_t *__restrict__ partial,
-                                                                uint32_t *__restrict__ out)
-{
-    const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
-    const bool full = (int64_t)(blockIdx.x + 1) * kScanTile <= len;   // uniform across the block
-    uint32_t v[kScanItems];
-    uint32_t s = 0;
-    if (full) {                      // 16 consecutive words per thread as four 16-byte loads
-        const uint4 *src = reinterpret_cast<const uint4 *>(in + base);
-#pragma unroll
-        for (int q = 0; q < kScanItems / 4; ++q) {
-            const uint4 t = src[q];
-            v[4 * q] = t.x;
-            v[4 * q + 1] = t.y;
-            v[4 * q + 2] = t.z;
-            v[4 * q + 3] = t.w;
-        }
-#pragma unroll
-        for (int i = 0; i < kScanItems; ++i) {
-            if (ROUND != 1)
-                v[i] = (v[i] + (ROUND - 1)) / ROUND * ROUND;
-            s += v[i];
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kScanItems; ++i) {
-            const int64_t k = base + i;
-            v[i] = k < len ? scan_load<ROUND>(in, k) : 0u;
-            s += v[i];
-        }
-    }
-    __shared__ uint32_t tot;
-    uint32_t run = block_exclusive_scan<kScanBlock>(s, &tot) + partial[blockIdx.x];
-    if (full) {
-        uint32_t o[kScanItems];
-#pragma unroll
-        for (int i = 0; i < kScanItems; ++i) {
-            o[i] = run;
-            run += v[i];
-        }
-        uint4 *dst = reinterpret_cast<uint4 *>(out + base);
-#pragma unroll
-        for (int q = 0; q < kScanItems / 4; ++q)
-            dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < kScanItems; ++i) {
-            const int64_t k = base + i;
-            if (k < len)
-                out[k] = run;
-            run += v[i];
-        }
-    }
-}
-
-__global__ void fill_u32_kernel(uint32_t *__restrict__ p, int64_t count, uint32_t value)
-{
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = value;
-}
-
-// out[0..len] = exclusive prefix sum of in[0..len) (each value rounded up to a
-// multiple of ROUND), out[len] = total.  scratch holds ceil(len / kScanTile) words.
-template <int ROUND>
-hipError_t exclusive_scan(const uint32_t *in, int64_t len, uint32_t *out, uint32_t *scratch, hipStream_t s)
-{
-    const int64_t nb = (len + kScanTile - 1) / kScanTile;
-    if (nb == 0) {
-        hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, s, out, (int64_t)1, 0u);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL(scan_reduce_kernel<ROUND>, dim3((unsigned)nb), dim3(kScanBlock), 0, s, in, len, scratch);
-    hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(1024), 0, s, scratch, nb, out + len);
-    hipLaunchKernelGGL(scan_final_kernel<ROUND>, dim3((unsigned)nb), dim3(kScanBlock), 0, s, in, len, scratch, out);
-    return hipGetLastError();
 }
 
 // Passes 1 and 5 visit the same chunks of kBinThreads * per consecutive
 // particles (per <= kMaxPer, chosen per launch so that every CU gets chunks),
 // one block per chunk.
 constexpr int kBinThreads = 1024;
-constexpr int kMaxPer = 64;                          // a chunk holds at most 65,536 particles
+constexpr int kMaxPer = 32;                          // a chunk holds at most 32,768 particles
 constexpr int kHashBits = 11;
 constexpr int kHashSlots = 1 << kHashBits;           // tiles per chunk counted in LDS
 constexpr int kMaxProbes = 64;
@@ -255,7 +134,14 @@ __global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, f
     const int64_t chunk = (int64_t)kBinThreads * per;
     for (int64_t c = blockIdx.x; c < chunks; c += gridDim.x) {
         const int64_t p0 = c * chunk + threadIdx.x;
-        for (int k0 = 0; k0 < per; k0 += 4) {
+        // per particle k of this thread: kLocalRank | slot << 16 | rank in the
+        // chunk, a final rank, or 0 when not binned; kept in registers until the
+        // chunk's runs are placed
+        uint32_t v[kMaxPer];
+#pragma unroll
+        for (int k0 = 0; k0 < kMaxPer; k0 += 4) {
+            if (k0 >= per)
+                break;
             float xs[4][DIM];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -271,9 +157,7 @@ __global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, f
                 uint32_t t = 0, l = 0;
                 const bool dom = live && particle_cell<DIM>(xs[j], nf, dx, last_base, ntx, t, l);
                 wave_count(live && !dom, &status[0]);
-                if (!live)
-                    continue;
-                uint32_t v = 0u;
+                v[k0 + j] = 0u;
                 if (dom) {
                     uint32_t h = (t * 0x9E3779B1u) >> (32 - kHashBits);
                     bool found = false;
@@ -285,10 +169,9 @@ __global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, f
                         }
                         h = (h + 1u) & (kHashSlots - 1);
                     }
-                    v = found ? kLocalRank | (h << 16) | atomicAdd(&hval[h], 1u) : atomicAdd(&tile_count[t], 1u);
+                    v[k0 + j] = found ? kLocalRank | (h << 16) | atomicAdd(&hval[h], 1u) : atomicAdd(&tile_count[t], 1u);
                     ++binned;
                 }
-                rank_out[p] = v;
             }
         }
         __syncthreads();
@@ -298,13 +181,12 @@ __global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, f
                 hval[e] = atomicAdd(&tile_count[key], hval[e]);
         }
         __syncthreads();
-        for (int k = 0; k < per; ++k) {            // the thread's own writes above: no fence needed
+#pragma unroll
+        for (int k = 0; k < kMaxPer; ++k) {
             const int64_t p = p0 + (int64_t)k * kBinThreads;
-            if (p >= f.n)
+            if (k >= per || p >= f.n)
                 break;
-            const uint32_t v = rank_out[p];
-            if (v & kLocalRank)
-                rank_out[p] = hval[(v >> 16) & (kHashSlots - 1)] + (v & 0xFFFFu);
+            rank_out[p] = (v[k] & kLocalRank) ? hval[(v[k] >> 16) & (kHashSlots - 1)] + (v[k] & 0xFFFFu) : v[k];
         }
         __syncthreads();
         for (int e = threadIdx.x; e < kHashSlots; e += kBinThreads) {
@@ -321,83 +203,157 @@ __global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, f
         atomicAdd(&meta[2], total);
 }
 
-// Pass 3: each tile's records are cut into slices of slice_records() (the
-// last one shorter), one P2G work item each; a slice's groups fill at most
-// kRowsPerItem rows.  Per tile: its full slices and the rows of its last,
-// partial slice.  P2G hands items out dynamically; the items are
-// ordered by size (all full slices, then the partial slices by decreasing
-// rows) and handed out alternately from both ends of that order (see
-// items_kernel).  The partial slices are counting-sorted by rows: one block of
-// 256 tiles counts them per row count in LDS (the returned count is the
-// tile's rank within the block) and writes its histogram, size-major, for a
-// prefix sum.  One thread per tile.
+// Passes 2-4: the work-item plan.  Each tile's records are cut into slices
+// of slice_records() (the last one shorter), one P2G work item each.  Per
+// tile: its first record (prefix sum of the counts), its full slices and the
+// rows its last, partial slice needs.  The items are listed by size (all full
+// slices, then the partial slices by decreasing rows, counting-sorted by
+// class) and handed out alternately from both ends of that list (largest,
+// smallest, second largest, ...), so long and short items run side by side on
+// every CU and the last items handed out are short.  Blocks of kPlanTiles
+// tiles: pass 2 writes each block's sums and class counts, pass 3 (one block)
+// prefix-sums them, pass 4 writes the tile starts and the items.
+constexpr int kPlanBlock = 256;
+constexpr int kPlanPer = kPlanTiles / kPlanBlock;   // tiles per thread
+
+// Full slices and class of a tile's last, partial slice: class r holds the
+// partial slices of kRowsPerItem - r rows; kRowsPerItem means none.
 template <int DIM>
-__global__ void __launch_bounds__(256) tile_layout_kernel(const uint32_t *__restrict__ tile_count, int64_t n_tiles,
-                                                           uint32_t *__restrict__ tile_full,
-                                                           uint32_t *__restrict__ tile_part,
-                                                           uint32_t *__restrict__ item_hist)
+__device__ __forceinline__ void tile_slices(uint32_t count, uint32_t &full, uint32_t &cls)
 {
     constexpr uint32_t S = slice_records<DIM>();
-    __shared__ uint32_t hist[kRowsPerItem + 1];
-    if (threadIdx.x <= kRowsPerItem)
+    full = count / S;
+    const uint32_t rem = count % S;
+    cls = rem != 0u ? kRowsPerItem - rows_bound<DIM>(rem) : (uint32_t)kRowsPerItem;
+}
+
+template <int DIM>
+__global__ void __launch_bounds__(kPlanBlock) plan_reduce_kernel(const uint32_t *__restrict__ tile_count,
+                                                                 int64_t n_tiles, uint32_t *__restrict__ part)
+{
+    __shared__ uint32_t hist[kRowsPerItem];
+    __shared__ uint32_t tot;
+    if (threadIdx.x < kRowsPerItem)
         hist[threadIdx.x] = 0u;
     __syncthreads();
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t < n_tiles) {
-        const uint32_t c = tile_count[t];
-        const uint32_t full = c / S, rem = c % S;
-        const uint32_t part = rem != 0u ? rows_bound<DIM>(rem) : 0u;      // 1 .. kRowsPerItem
-        uint32_t rank = 0;
-        tile_full[t] = full;
-        if (part != 0u)
-            rank = atomicAdd(&hist[part], 1u);
-        tile_part[t] = (part << 16) | rank;
-    }
-    __syncthreads();
-    // row (kRowsPerItem - rows) of the size-major histogram: largest first
-    if (threadIdx.x >= 1 && threadIdx.x <= kRowsPerItem)
-        item_hist[(int64_t)(kRowsPerItem - threadIdx.x) * gridDim.x + blockIdx.x] = hist[threadIdx.x];
-}
-
-// Pass 4: the work items of each tile.  One 16-byte record per item: tile,
-// first record, records, 0.
-template <int DIM>
-__global__ void __launch_bounds__(256) items_kernel(const uint32_t *__restrict__ tile_full,
-                                                     const uint32_t *__restrict__ tile_part,
-                                                     const uint32_t *__restrict__ full_start,
-                                                     const uint32_t *__restrict__ hist_start,
-                                                     const uint32_t *__restrict__ tile_start, int64_t n_tiles,
-                                                     int64_t layout_blocks, uint4 *__restrict__ items)
-{
-    constexpr uint32_t S = slice_records<DIM>();
-    const uint32_t n_full = full_start[n_tiles];
-    const uint32_t total = n_full + hist_start[(int64_t)kRowsPerItem * layout_blocks];
-    // p is an item's position in the size-sorted list; the items are handed
-    // out alternately from its two ends (largest, smallest, second largest,
-    // ...), so long and short items run side by side on every CU and the last
-    // items handed out are short.
-    auto place = [&](uint32_t p) { return p < (total + 1) / 2 ? 2 * p : 2 * (total - 1 - p) + 1; };
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n_tiles; t += (int64_t)gridDim.x * blockDim.x) {
-        const uint32_t k = tile_full[t], s0 = full_start[t];
-        const uint32_t c0 = tile_start[t], count = tile_start[t + 1] - c0;
-        for (uint32_t c = 0; c < k; ++c)
-            items[place(s0 + c)] = make_uint4((uint32_t)t, c0 + c * S, S, 0u);
-        const uint32_t part = tile_part[t] >> 16;
-        if (part != 0u) {
-            const uint32_t q = place(n_full + hist_start[(int64_t)(kRowsPerItem - part) * layout_blocks + t / 256] +
-                                     (tile_part[t] & 0xFFFFu));
-            items[q] = make_uint4((uint32_t)t, c0 + k * S, count - k * S, 0u);
+    const int64_t base = (int64_t)blockIdx.x * kPlanTiles + (int64_t)threadIdx.x * kPlanPer;
+    uint32_t sc = 0, sf = 0;
+#pragma unroll
+    for (int i = 0; i < kPlanPer; ++i) {
+        const int64_t t = base + i;
+        if (t < n_tiles) {
+            const uint32_t c = tile_count[t];
+            uint32_t full, cls;
+            tile_slices<DIM>(c, full, cls);
+            sc += c;
+            sf += full;
+            if (cls < (uint32_t)kRowsPerItem)
+                atomicAdd(&hist[cls], 1u);
         }
     }
+    uint32_t *out = part + (int64_t)blockIdx.x * kPlanStride;
+    (void)block_exclusive_scan<kPlanBlock>(sc, &tot);
+    if (threadIdx.x == 0)
+        out[0] = tot;
+    __syncthreads();
+    (void)block_exclusive_scan<kPlanBlock>(sf, &tot);
+    if (threadIdx.x == 0)
+        out[1] = tot;
+    if (threadIdx.x < kRowsPerItem)
+        out[2 + threadIdx.x] = hist[threadIdx.x];
 }
 
-// meta: [0] work items, [3] P2G's work cursor ([2], the binned particles, is
-// added to by pass 1).
-__global__ void meta_kernel(const uint32_t *__restrict__ full_start, const uint32_t *__restrict__ hist_start,
-                            int64_t hist_len, int64_t n_tiles, uint32_t *__restrict__ meta)
+// One block: each field of the per-block records prefix-summed over the
+// blocks, in place (one wavefront per field): [0] first record, [1] first
+// full slice, [2 + r] first item of class r (the classes follow all full
+// slices, in class order).  Writes the total record count after the tile
+// starts, the item count to meta[0], and resets P2G's work cursor.
+__global__ void __launch_bounds__(1024) plan_partials_kernel(uint32_t *__restrict__ part, int64_t nblocks,
+                                                             uint32_t *__restrict__ tile_start_end,
+                                                             uint32_t *__restrict__ meta)
 {
-    meta[0] = full_start[n_tiles] + hist_start[hist_len];
-    meta[3] = 0u;
+    constexpr int kWaves = 1024 / kWave;
+    __shared__ uint32_t ftot[kPlanStride];
+    __shared__ uint32_t cbase[kRowsPerItem];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    for (int f = wave; f < kPlanStride; f += kWaves) {
+        uint32_t carry = 0;
+        for (int64_t base = 0; base < nblocks; base += kWave) {
+            const int64_t k = base + lane;
+            const uint32_t v = k < nblocks ? part[k * kPlanStride + f] : 0u;
+            const uint32_t inc = wave_inclusive_scan(v);
+            if (k < nblocks)
+                part[k * kPlanStride + f] = carry + inc - v;
+            carry += __shfl(inc, kWave - 1, kWave);
+        }
+        if (lane == 0)
+            ftot[f] = carry;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const uint32_t v = lane < kRowsPerItem ? ftot[2 + lane] : 0u;
+        const uint32_t inc = wave_inclusive_scan(v);
+        if (lane < kRowsPerItem)
+            cbase[lane] = ftot[1] + inc - v;
+        if (lane == kWave - 1) {
+            *tile_start_end = ftot[0];
+            meta[0] = ftot[1] + inc;
+            meta[3] = 0u;
+        }
+    }
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < nblocks * kRowsPerItem; i += 1024) {
+        const int64_t k = i / kRowsPerItem;
+        const int r = (int)(i % kRowsPerItem);
+        part[k * kPlanStride + 2 + r] += cbase[r];
+    }
+}
+
+template <int DIM>
+__global__ void __launch_bounds__(kPlanBlock) plan_final_kernel(const uint32_t *__restrict__ tile_count,
+                                                                int64_t n_tiles, const uint32_t *__restrict__ part,
+                                                                const uint32_t *__restrict__ meta,
+                                                                uint32_t *__restrict__ tile_start,
+                                                                uint4 *__restrict__ items)
+{
+    constexpr uint32_t S = slice_records<DIM>();
+    __shared__ uint32_t cls_next[kRowsPerItem];
+    __shared__ uint32_t tot;
+    const uint32_t *in = part + (int64_t)blockIdx.x * kPlanStride;
+    if (threadIdx.x < kRowsPerItem)
+        cls_next[threadIdx.x] = in[2 + threadIdx.x];
+    const int64_t base = (int64_t)blockIdx.x * kPlanTiles + (int64_t)threadIdx.x * kPlanPer;
+    uint32_t c[kPlanPer];
+    uint32_t sc = 0, sf = 0;
+#pragma unroll
+    for (int i = 0; i < kPlanPer; ++i) {
+        const int64_t t = base + i;
+        c[i] = t < n_tiles ? tile_count[t] : 0u;
+        uint32_t full, cls;
+        tile_slices<DIM>(c[i], full, cls);
+        sc += c[i];
+        sf += full;
+    }
+    uint32_t rec0 = in[0] + block_exclusive_scan<kPlanBlock>(sc, &tot);
+    uint32_t item0 = in[1] + block_exclusive_scan<kPlanBlock>(sf, &tot);
+    __syncthreads();                                 // cls_next visible
+    const uint32_t total = meta[0];
+    auto place = [&](uint32_t q) { return q < (total + 1) / 2 ? 2 * q : 2 * (total - 1 - q) + 1; };
+#pragma unroll
+    for (int i = 0; i < kPlanPer; ++i) {
+        const int64_t t = base + i;
+        if (t >= n_tiles)
+            break;
+        tile_start[t] = rec0;
+        uint32_t full, cls;
+        tile_slices<DIM>(c[i], full, cls);
+        for (uint32_t k = 0; k < full; ++k)
+            items[place(item0 + k)] = make_uint4((uint32_t)t, rec0 + k * S, S, 0u);
+        if (cls < (uint32_t)kRowsPerItem)
+            items[place(atomicAdd(&cls_next[cls], 1u))] = make_uint4((uint32_t)t, rec0 + full * S, c[i] - full * S, 0u);
+        item0 += full;
+        rec0 += c[i];
+    }
 }
 
 // Pass 5: each binned particle's record at its tile's first record plus its
@@ -561,10 +517,8 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
 {
     const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3);
     const int ntx = n / kTile;
-    uint32_t *tile_items = b.tile_tmp, *tile_part = b.tile_tmp + b.n_tiles;
-    hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, b.tile_count, b.n_tiles,
-                       0u);
-    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, s, b.meta, (int64_t)16, 0u);
+    hipLaunchKernelGGL(fill2_u32_kernel, dim3(blocks_for(b.n_tiles + 16, 256)), dim3(256), 0, s, b.tile_count,
+                       b.n_tiles, b.meta, (int64_t)16);
     // particles per thread of a chunk: enough chunks for two blocks per CU, at most kMaxPer
     const int64_t span = (int64_t)kBinThreads * device_cu_count() * 2;
     int64_t per = (p.n + span - 1) / span;
@@ -579,30 +533,23 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
             hipLaunchKernelGGL(bin_tile_count_kernel<2>, dim3(cblocks), dim3(kBinThreads), 0, s, p, nf, dx, last, ntx,
                                chunks, (int)per, b.tile_count, b.rank, status, b.meta);
     }
-    hipError_t e = exclusive_scan<1>(b.tile_count, b.n_tiles, b.tile_start, b.scan_tmp, s);
-    if (e != hipSuccess)
-        return e;
-    const int64_t lblocks = (b.n_tiles + 255) / 256;
-    const int64_t hist_len = kRowsPerItem * lblocks;
-    if (dim == 3)
-        hipLaunchKernelGGL(tile_layout_kernel<3>, dim3((unsigned)lblocks), dim3(256), 0, s, b.tile_count, b.n_tiles,
-                           tile_items, tile_part, b.item_hist);
-    else
-        hipLaunchKernelGGL(tile_layout_kernel<2>, dim3((unsigned)lblocks), dim3(256), 0, s, b.tile_count, b.n_tiles,
-                           tile_items, tile_part, b.item_hist);
-    if ((e = exclusive_scan<1>(tile_items, b.n_tiles, b.item_start, b.scan_tmp, s)) != hipSuccess)
-        return e;
-    if ((e = exclusive_scan<1>(b.item_hist, hist_len, b.item_hist_start, b.scan_tmp, s)) != hipSuccess)
-        return e;
+    const int64_t pblocks = (b.n_tiles + kPlanTiles - 1) / kPlanTiles;
     uint4 *items = reinterpret_cast<uint4 *>(b.items);
-    if (dim == 3)
-        hipLaunchKernelGGL(items_kernel<3>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_items, tile_part,
-                           b.item_start, b.item_hist_start, b.tile_start, b.n_tiles, lblocks, items);
-    else
-        hipLaunchKernelGGL(items_kernel<2>, dim3(blocks_for(b.n_tiles, 256)), dim3(256), 0, s, tile_items, tile_part,
-                           b.item_start, b.item_hist_start, b.tile_start, b.n_tiles, lblocks, items);
-    hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(1), 0, s, b.item_start, b.item_hist_start, hist_len, b.n_tiles,
-                       b.meta);
+    if (dim == 3) {
+        hipLaunchKernelGGL(plan_reduce_kernel<3>, dim3((unsigned)pblocks), dim3(kPlanBlock), 0, s, b.tile_count,
+                           b.n_tiles, b.scan_tmp);
+        hipLaunchKernelGGL(plan_partials_kernel, dim3(1), dim3(1024), 0, s, b.scan_tmp, pblocks,
+                           b.tile_start + b.n_tiles, b.meta);
+        hipLaunchKernelGGL(plan_final_kernel<3>, dim3((unsigned)pblocks), dim3(kPlanBlock), 0, s, b.tile_count,
+                           b.n_tiles, b.scan_tmp, b.meta, b.tile_start, items);
+    } else {
+        hipLaunchKernelGGL(plan_reduce_kernel<2>, dim3((unsigned)pblocks), dim3(kPlanBlock), 0, s, b.tile_count,
+                           b.n_tiles, b.scan_tmp);
+        hipLaunchKernelGGL(plan_partials_kernel, dim3(1), dim3(1024), 0, s, b.scan_tmp, pblocks,
+                           b.tile_start + b.n_tiles, b.meta);
+        hipLaunchKernelGGL(plan_final_kernel<2>, dim3((unsigned)pblocks), dim3(kPlanBlock), 0, s, b.tile_count,
+                           b.n_tiles, b.scan_tmp, b.meta, b.tile_start, items);
+    }
     const unsigned sblocks = (unsigned)(chunks < (int64_t)device_cu_count() * 8 ? chunks : device_cu_count() * 8);
     if (chunks > 0) {
         if (dim == 3)

@@ -19,7 +19,8 @@ constexpr int kTile = 4;             // tile edge in cells
 constexpr int kGroup = 4;            // records per group: one cell's particles, four at a time
 constexpr int kRowSlots = kWave * kGroup;  // a row: one group per lane (256 group entries)
 constexpr int kRowsPerItem = 16;     // most rows of one P2G work item (4096 group entries)
-constexpr int kScanTileElems = 4096; // elements per block of the prefix-sum passes
+constexpr int kPlanTiles = 4096;     // tiles per block of binning's work-item plan
+constexpr int kPlanStride = 2 + kRowsPerItem;  // words per plan block: records, full slices, slices per class
 
 // One axis of a particle's quadratic B-spline stencil.  With g = x*n in node
 // units, the stencil starts at base = floor(g - 1/2) ("Mass Matrix Assembly on
@@ -151,8 +152,7 @@ struct Fields {           // component-major particle arrays of n particles
 };
 
 struct BinView {          // the workspace arrays, as typed device pointers
-    uint32_t *tile_count, *tile_start, *item_start, *items, *meta, *rank, *slot, *tile_tmp, *scan_tmp, *item_hist,
-        *item_hist_start;
+    uint32_t *tile_count, *tile_start, *items, *meta, *rank, *slot, *scan_tmp;
     uint8_t *cell_key, *tile_active;
     float *sorted;
     int64_t n_cells, n_tiles, max_items, n_fields;

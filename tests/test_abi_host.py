@@ -77,12 +77,9 @@ def test_workspace_layout_is_disjoint_and_aligned():
         assert lay.n_fields == {2: 12, 3: 16}[dim]     # x, v, C, m padded to a multiple of 4 floats
         spans = sorted([
             (lay.tile_count, 4 * lay.n_tiles), (lay.tile_start, 4 * (lay.n_tiles + 1)), (lay.tile_active, lay.n_tiles),
-            (lay.item_start, 4 * (lay.n_tiles + 1)),
             (lay.items, 16 * lay.max_items), (lay.meta, 64), (lay.rank, 4 * max(N, 1)), (lay.slot, 4 * max(N, 1)),
             (lay.cell_key, max(N, 1)), (lay.sorted, 4 * lay.n_fields * max(N, 1)),
-            (lay.tile_tmp, 8 * lay.n_tiles),
-            (lay.item_hist, 4 * lay.rows_per_item * ((lay.n_tiles + 255) // 256)),
-            (lay.item_hist_start, 4 * (lay.rows_per_item * ((lay.n_tiles + 255) // 256) + 1))])
+            (lay.scan_tmp, 4 * (2 + lay.rows_per_item) * ((lay.n_tiles + 4095) // 4096))])
         for (a, la), (b, _) in zip(spans, spans[1:]):
             assert a % 256 == 0 and a + la <= b
         assert spans[-1][0] + spans[-1][1] <= lay.total_bytes
