@@ -233,8 +233,11 @@ int mpm_grid_update(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, flo
 /* APIC grid-to-particle gather and advection ("Implementation -- GPU
  * Optimization & Reference Codebases", sections 1 and 3.1).  Per particle,
  * over its stencil nodes in lexicographic order (x offset outermost), with
- * w = (wx[a] * wy[b]) * wz[c]:  wv_d = w * vg_d;  v_d += wv_d;
- * B_de += wv_d * r_e;  then C = B * (4 n^2), x_e += dt * v_e, and x_e is
+ * w = (wx[a] * wy[b]) * wz[c] and wv_d = w * vg_d, the per-axis offset sums
+ * S_de[o] += wv_d (o the node's offset along axis e); then
+ * v_d = (S_d0[0] + S_d0[1]) + S_d0[2],
+ * B_de = (r_e[0] S_de[0] + r_e[1] S_de[1]) + r_e[2] S_de[2],
+ * C = B * (4 n^2), x_e += dt * v_e, and x_e is
  * clamped to [dx, (n-2) dx] (clamped particles counted in status[2]).
  * Particles whose stencil leaves the grid are left unchanged and counted in
  * status[0].  particles: device, x, v, C read/written in place (m unused).

@@ -40,13 +40,13 @@ __global__ void __launch_bounds__(256) grid_update_kernel(int n, int64_t *__rest
                                                           float dt, float g0, float g1, float g2, int sticky,
                                                           const uint8_t *__restrict__ active)
 {
+    const int sh = 31 - __builtin_clz(n);                     // n is a power of two
     const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
-    const int ntx = n / kTile;
     const float gdt[3] = { dt * g0, dt * g1, dt * g2 };
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nodes; i += (int64_t)gridDim.x * blockDim.x) {
-        const int ix = (int)(i % n), iy = (int)((i / n) % n);
-        const int iz = DIM == 3 ? (int)(i / ((int64_t)n * n)) : 0;
-        if (active && !active[((int64_t)(iz / kTile) * ntx + iy / kTile) * ntx + ix / kTile])
+        const int ix = (int)(i & (n - 1)), iy = (int)((i >> sh) & (n - 1));
+        const int iz = DIM == 3 ? (int)(i >> (2 * sh)) : 0;
+        if (active && !active[(((int64_t)(iz >> 2) << (2 * sh - 4)) | ((int64_t)(iy >> 2) << (sh - 2))) | (ix >> 2)])
             continue;
         bool wall = ix < sticky || ix >= n - sticky || iy < sticky || iy >= n - sticky;
         if (DIM == 3)
@@ -68,8 +68,10 @@ __global__ void __launch_bounds__(256) grid_update_kernel(int n, int64_t *__rest
 }
 
 // One thread per particle.  Over the stencil in lexicographic node order (x
-// offset outermost), with w = (wx[a]*wy[b])*wz[c]: wv_d = w*vg_d,
-// v_d += wv_d, B_de += wv_d*r_e; then C = B*(4 n^2), x += dt*v, clamp.
+// offset outermost), with w = (wx[a]*wy[b])*wz[c] and wv_d = w*vg_d, the
+// per-axis offset sums S[d][e][o] += wv_d; then v_d = sum_o S[d][0][o] and
+// B_de = sum_o r_e[o] S[d][e][o] (in offset order), C = B*(4 n^2), x += dt*v,
+// clamp.
 template <int DIM>
 __global__ void __launch_bounds__(256) g2p_kernel(int n, float nf, float dx, float last_base,
                                                   const float *__restrict__ vg, float *__restrict__ x,
@@ -86,15 +88,17 @@ __global__ void __launch_bounds__(256) g2p_kernel(int n, float nf, float dx, flo
         wave_count(!ok, &status[0]);
         if (!ok)
             continue;
-        float vn[DIM];
-        float B[DIM][DIM];
+        // S[d][e][o]: sum of w * vg_d over the stencil nodes at offset o along
+        // axis e, in lexicographic node order; v and B follow from it because
+        // r_e depends on the offset along axis e only.
+        float S[DIM][DIM][3];
 #pragma unroll
-        for (int d = 0; d < DIM; ++d) {
-            vn[d] = 0.0f;
+        for (int d = 0; d < DIM; ++d)
 #pragma unroll
             for (int e = 0; e < DIM; ++e)
-                B[d][e] = 0.0f;
-        }
+#pragma unroll
+                for (int o = 0; o < 3; ++o)
+                    S[d][e][o] = 0.0f;
         const float wx[3] = { ax[0].w0, ax[0].w1, ax[0].w2 }, rx[3] = { ax[0].r0, ax[0].r1, ax[0].r2 };
         const float wy[3] = { ax[1].w0, ax[1].w1, ax[1].w2 }, ry[3] = { ax[1].r0, ax[1].r1, ax[1].r2 };
         float wz[3] = { 1.0f, 0.0f, 0.0f }, rz[3] = { 0.0f, 0.0f, 0.0f };
@@ -117,16 +121,25 @@ __global__ void __launch_bounds__(256) g2p_kernel(int n, float nf, float dx, flo
                     const int64_t node = DIM == 3
                         ? ((int64_t)(bz + c) * n + (ax[1].base + b)) * n + (ax[0].base + a)
                         : (int64_t)(ax[1].base + b) * n + (ax[0].base + a);
-                    const float off[3] = { rx[a], ry[b], rz[c] };
+                    const int o[3] = { a, b, c };
 #pragma unroll
                     for (int d = 0; d < DIM; ++d) {
                         const float wv = w * vg[d * nodes + node];
-                        vn[d] = vn[d] + wv;
 #pragma unroll
                         for (int e = 0; e < DIM; ++e)
-                            B[d][e] = B[d][e] + wv * off[e];
+                            S[d][e][o[e]] = S[d][e][o[e]] + wv;
                     }
                 }
+        const float *rr[3] = { rx, ry, rz };
+        float vn[DIM];
+        float B[DIM][DIM];
+#pragma unroll
+        for (int d = 0; d < DIM; ++d) {
+            vn[d] = (S[d][0][0] + S[d][0][1]) + S[d][0][2];
+#pragma unroll
+            for (int e = 0; e < DIM; ++e)
+                B[d][e] = (rr[e][0] * S[d][e][0] + rr[e][1] * S[d][e][1]) + rr[e][2] * S[d][e][2];
+        }
         bool clamped = false;
 #pragma unroll
         for (int d = 0; d < DIM; ++d) {

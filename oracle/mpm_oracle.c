@@ -302,12 +302,15 @@ void oracle_grid_update(int dim, int n, int64_t *grid, float *vg, float dt, cons
 }
 
 /*
- * APIC gather: for each particle, over its stencil nodes in lexicographic
- * order (a outermost, then b, then c), with w = (wx[a] * wy[b]) * wz[c]:
- *   wv_d   = w * vg_d(node)
- *   vnew_d = vnew_d + wv_d                     (from 0)
- *   B_de   = B_de + wv_d * r_e                 (r_e the node's offset on axis e)
- * then C = B * (4 / dx^2) (the quadratic B-spline's inertia-like factor
+ * APIC gather: v = sum w vg and B = sum (w vg) r^T over the stencil.  For each
+ * particle, over its stencil nodes in lexicographic order (a outermost, then
+ * b, then c), with w = (wx[a] * wy[b]) * wz[c]:
+ *   wv_d        = w * vg_d(node)
+ *   S[d][e][o] += wv_d     for each axis e, o the node's offset on axis e (from 0)
+ * then vnew_d = (S[d][0][0] + S[d][0][1]) + S[d][0][2] and
+ *   B_de = (r_e[0] * S[d][e][0] + r_e[1] * S[d][e][1]) + r_e[2] * S[d][e][2],
+ * the same sums grouped by the offset along one axis (r_e depends on that
+ * offset only); then C = B * (4 / dx^2) (the quadratic B-spline's inertia-like factor
  * dx^2/4 inverted), v = vnew, x_e = x_e + dt * v_e, and x_e is clamped to
  * [dx, (n-2) dx] (each clamped particle counted in status[2]).  Particles
  * whose stencil leaves the grid are left untouched and counted in status[0].
@@ -330,6 +333,12 @@ void oracle_g2p(int dim, int n, const float *vg, int64_t np_, float *x, float *v
             status[ST_DOMAIN] += 1;
             continue;
         }
+        /* S[d][e][o]: the sum of w * vg_d over the stencil nodes at offset o
+         * along axis e, accumulated in lexicographic node order.  Since r_e
+         * depends on the offset along axis e only, the sums over the stencil
+         * v_d = sum w vg_d and B_de = sum (w vg_d) r_e are sum_o S[d][e][o] and
+         * sum_o r_e[o] S[d][e][o]. */
+        float S[3][3][3] = { { { 0 } } };
         float vnew[3] = { 0, 0, 0 };
         float B[3][3] = { { 0, 0, 0 }, { 0, 0, 0 }, { 0, 0, 0 } };
         const int nc = dim == 3 ? 3 : 1;
@@ -342,14 +351,18 @@ void oracle_g2p(int dim, int n, const float *vg, int64_t np_, float *x, float *v
                     int64_t node = dim == 3
                         ? ((int64_t)(base[2] + c) * n + (base[1] + b)) * n + (base[0] + a)
                         : (int64_t)(base[1] + b) * n + (base[0] + a);
-                    const float off[3] = { r[0][a], r[1][b], r[2][c] };
+                    const int o[3] = { a, b, c };
                     for (int d = 0; d < dim; ++d) {
                         float wv = wt * vg[d * nodes + node];
-                        vnew[d] = vnew[d] + wv;
                         for (int e = 0; e < dim; ++e)
-                            B[d][e] = B[d][e] + wv * off[e];
+                            S[d][e][o[e]] = S[d][e][o[e]] + wv;
                     }
                 }
+        for (int d = 0; d < dim; ++d) {
+            vnew[d] = (S[d][0][0] + S[d][0][1]) + S[d][0][2];
+            for (int e = 0; e < dim; ++e)
+                B[d][e] = (r[e][0] * S[d][e][0] + r[e][1] * S[d][e][1]) + r[e][2] * S[d][e][2];
+        }
         int clamped = 0;
         for (int d = 0; d < dim; ++d) {
             for (int e = 0; e < dim; ++e)
