@@ -96,7 +96,7 @@ __host__ __device__ constexpr uint32_t cells_per_tile() { return DIM == 3 ? kTil
 // and at most min(count, cells) cells are occupied.  The bound depends on the
 // count alone, so rows are laid out before the cells are sorted.
 template <int DIM>
-__host__ __device__ inline uint32_t groups_bound(uint32_t count)
+__host__ __device__ constexpr uint32_t groups_bound(uint32_t count)
 {
     const uint64_t occupied = count < cells_per_tile<DIM>() ? count : cells_per_tile<DIM>();
     return (uint32_t)(((uint64_t)count + (kGroup - 1) * occupied) / kGroup);

@@ -270,11 +270,9 @@ __global__ void reset_cursor_kernel(uint32_t *cursor) { *cursor = 0u; }
 
 // Group entries of the item being processed, in LDS: a record's offset in the
 // slice, with kPad16 set when the entry only completes its cell's last group
-// (read with zero mass); kEmpty16 in a group's first entry where the lane
-// holds no group.
+// (read with zero mass).
 constexpr uint16_t kPad16 = 0x8000u;
-constexpr uint16_t kEmpty16 = 0xFFFFu;
-constexpr int kSortKeys = 16;                 // cell keys per lane per memory round trip
+constexpr int kKeyWords = 16;                 // words of four cell keys per lane: a whole slice
 
 // Entry index of padded cell-sorted position s in an item with `rows` rows:
 // group g = s / kGroup sits in lane g / rows of row g % rows, entry s % kGroup.
@@ -287,67 +285,94 @@ __device__ __forceinline__ uint32_t entry16(uint32_t s, uint32_t rows, uint32_t 
 }
 
 // Counting sort of the item's records by cell into its rows of group
-// entries ("Particle worlds, part 3", steps 3-4, on chip): an LDS histogram of
-// the slice's cell keys, a wave prefix sum of the counts rounded up to whole
-// groups (each cell's first padded position), then every record placed
-// through an LDS cursor per cell; the record placed first in its cell also
-// writes the cell's pad entries.  One wavefront; `keys` are the slice's cell
-// keys.
-template <int DIM>
-__device__ __forceinline__ void sort_item(const uint8_t *__restrict__ keys, uint32_t count, uint32_t groups,
-                                          uint32_t rows, uint16_t *ent, uint32_t *cnt, uint32_t *cur,
-                                          uint32_t *cstart, int lane)
+// entries ("Particle worlds, part 3", steps 3-4, on chip).  The slice's cell
+// keys are read once, four to a word, and kept in registers.  One returning
+// LDS atomic per key on its cell's counter gives both the histogram and the
+// key's rank among its cell's keys, and every key also leaves its record's
+// offset in its cell's representative slot (any one of them survives).  A
+// wave prefix sum of the counts rounded up to whole groups gives each cell's
+// first padded position; the cell's lane writes its pad entries (naming the
+// representative record), and every record is placed at its cell's start plus
+// its rank.  Every position below the padded total is written once, so the
+// item's groups are exactly the first total / kGroup.  Positions past the
+// slice's keys in a word that holds some take their atomics and
+// representative writes on a spare slot of their own lane (kWave + lane) and
+// their entry writes on a spare entry, so that inside each round of words
+// the code has no branches and the LDS operations of many keys are in
+// flight at once.  One wavefront.  `keys` holds
+// the cell key of record `first` + i at byte i; its allocation extends to a
+// multiple of 4 bytes past the last key.  Returns the number of groups; rows =
+// ceil(groups / 64).
+constexpr uint32_t kTrashEntry = kRowsPerItem * kRowSlots; // spare group entry
+
+__device__ __forceinline__ uint32_t sort_item(const uint8_t *__restrict__ keys, uint32_t first, uint32_t count,
+                                              uint16_t *ent, uint32_t *cnt, uint32_t *cstart, uint32_t *rep,
+                                              int lane, uint32_t &rows_out)
 {
-    const uint32_t magic = rows > 1u ? 0xFFFFFFFFu / rows + 1u : 0u;
+    const uint32_t off = first & 3u;
+    const uint32_t *words = reinterpret_cast<const uint32_t *>(keys + (first - off));
+    const uint32_t n_words = (off + count + 3u) / 4u;
+    const uint32_t last_word = n_words - 1u;
+    const int rounds = (int)((n_words + kWave - 1) / kWave);   // rounds of one word per lane
     cnt[lane] = 0u;
+    cnt[kWave + lane] = 0u;
+    uint32_t kw[kKeyWords];
+#pragma unroll
+    for (int k = 0; k < kKeyWords; ++k) {
+        const uint32_t i = (uint32_t)(k * kWave + lane);
+        kw[k] = k < rounds ? words[i < last_word ? i : last_word] : 0u;
+    }
     __syncthreads();
-    for (uint32_t base = 0; base < count; base += kWave * kSortKeys) {
-        uint32_t l[kSortKeys];
+    // rank of key (k, b) among its cell's keys (spare slots: meaningless); the
+    // results are only read after the barrier, so the atomics queue up
+    uint32_t rk[kKeyWords][4];
 #pragma unroll
-        for (int k = 0; k < kSortKeys; ++k) {
-            const uint32_t i = base + k * kWave + lane;
-            l[k] = i < count ? (uint32_t)keys[i] : kEmpty;
+    for (int k = 0; k < kKeyWords; ++k) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            rk[k][b] = 0u;
+        if (k >= rounds)
+            continue;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t s = 4u * (uint32_t)(k * kWave + lane) + (uint32_t)b - off;
+            const uint32_t key = s < count ? (kw[k] >> (8 * b)) & 0xFFu : kWave + (uint32_t)lane;
+            rk[k][b] = atomicAdd(&cnt[key], 1u);
+            rep[key] = s;
         }
-#pragma unroll
-        for (int k = 0; k < kSortKeys; ++k)
-            if (l[k] != kEmpty)
-                atomicAdd(&cnt[l[k]], 1u);
     }
     __syncthreads();
     const uint32_t n_l = cnt[lane];
     const uint32_t padded = (n_l + kGroup - 1) / kGroup * kGroup;
     const uint32_t inc = wave_inclusive_scan(padded);
-    cstart[lane] = inc - padded;
-    cur[lane] = inc - padded;
-    for (uint32_t g = __shfl(inc, kWave - 1, kWave) / kGroup + lane; g < groups; g += kWave)
-        ent[entry16(g * kGroup, rows, magic)] = kEmpty16;
+    const uint32_t groups = (uint32_t)__shfl((int)inc, kWave - 1, kWave) / kGroup;
+    const uint32_t rows = (groups + kWave - 1) / kWave;
+    const uint32_t magic = rows > 1u ? 0xFFFFFFFFu / rows + 1u : 0u;
+    const uint32_t c0 = inc - padded;
+    cstart[lane] = c0;
+    for (uint32_t q = c0 + n_l; q < inc; ++q)                  // this lane's cell's pads
+        ent[entry16(q, rows, magic)] = (uint16_t)(kPad16 | rep[lane]);
     __syncthreads();
-    for (uint32_t base = 0; base < count; base += kWave * kSortKeys) {
-        uint32_t l[kSortKeys];
 #pragma unroll
-        for (int k = 0; k < kSortKeys; ++k) {
-            const uint32_t i = base + k * kWave + lane;
-            l[k] = i < count ? (uint32_t)keys[i] : kEmpty;
+    for (int k = 0; k < kKeyWords; ++k) {
+        if (k >= rounds)
+            continue;
+        uint32_t c4[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t s = 4u * (uint32_t)(k * kWave + lane) + (uint32_t)b - off;
+            c4[b] = cstart[s < count ? (kw[k] >> (8 * b)) & 0xFFu : kWave + (uint32_t)lane];
         }
-        uint32_t pos[kSortKeys];
 #pragma unroll
-        for (int k = 0; k < kSortKeys; ++k)
-            pos[k] = l[k] != kEmpty ? atomicAdd(&cur[l[k]], 1u) : 0u;
-#pragma unroll
-        for (int k = 0; k < kSortKeys; ++k) {
-            if (l[k] == kEmpty)
-                continue;
-            const uint32_t i = base + k * kWave + lane;
-            ent[entry16(pos[k], rows, magic)] = (uint16_t)i;
-            const uint32_t s0 = cstart[l[k]];
-            if (pos[k] == s0) {                          // the cell's first position: fill its pads
-                const uint32_t c = cnt[l[k]];
-                for (uint32_t q = s0 + c; q < s0 + (c + kGroup - 1) / kGroup * kGroup; ++q)
-                    ent[entry16(q, rows, magic)] = (uint16_t)(kPad16 | i);
-            }
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t s = 4u * (uint32_t)(k * kWave + lane) + (uint32_t)b - off;
+            const uint32_t e = entry16(c4[b] + rk[k][b], rows, magic);
+            ent[s < count ? e : kTrashEntry] = (uint16_t)s;
         }
     }
     __syncthreads();
+    rows_out = rows;
+    return groups;
 }
 
 template <int DIM>
@@ -359,9 +384,12 @@ p2g_tiled_kernel(TiledArgs a)
     constexpr int G = kGroup;
     constexpr int kFlush = (TS::nodes + kWave - 1) / kWave;      // node-block entries per lane
     __shared__ double acc[TS::ch * TS::nodes];
-    __shared__ __align__(16) uint16_t ent[kRowsPerItem * kRowSlots];
-    __shared__ uint32_t cnt[kWave], cur[kWave], cstart[kWave];
+    __shared__ __align__(16) uint16_t ent[kRowsPerItem * kRowSlots + 4];
+    __shared__ uint32_t cnt[2 * kWave], cstart[2 * kWave], rep[2 * kWave];   // [kWave, 2 kWave): spare slots
     static_assert(slice_records<DIM>() < kPad16, "a slice offset must leave the pad bit free");
+    static_assert((slice_records<DIM>() + 6) / 4 <= (uint32_t)(kWave * kKeyWords), "a slice's keys fit the key words");
+    static_assert(groups_bound<DIM>(slice_records<DIM>()) <= (uint32_t)(kRowsPerItem * kWave),
+                  "a slice's groups fit the entry rows");
     static_assert(cells_per_tile<DIM>() <= (uint32_t)kWave, "one lane per cell of a tile");
     const int lane = threadIdx.x;
     const uint32_t n_items = a.meta[0];
@@ -399,8 +427,6 @@ p2g_tiled_kernel(TiledArgs a)
             next = atomicAdd(a.cursor, 1u);
         // item: tile, first record, records (one slice of the tile)
         const uint32_t tile = rec_item.x, first = rec_item.y, count = rec_item.z;
-        const uint32_t groups = groups_bound<DIM>(count);
-        const uint32_t rows = (groups + kWave - 1) / kWave;
         int torg[3] = { 0, 0, 0 };
         {
             uint32_t t = tile;
@@ -410,7 +436,8 @@ p2g_tiled_kernel(TiledArgs a)
                 t /= (uint32_t)a.ntx;
             }
         }
-        sort_item<DIM>(a.cell_key + first, count, groups, rows, ent, cnt, cur, cstart, lane);
+        uint32_t rows;
+        const uint32_t groups = sort_item(a.cell_key, first, count, ent, cnt, cstart, rep, lane, rows);
         static_assert(kGroup == 4, "a group's entries load as one 8-byte word");
         for (uint32_t j = 0; j < rows; ++j) {
             // this lane's group in row j is group lane * rows + j of the item
@@ -418,8 +445,6 @@ p2g_tiled_kernel(TiledArgs a)
                 continue;
             const uint2 w2 = *reinterpret_cast<const uint2 *>(&ent[(j * kWave + lane) * kGroup]);
             const uint32_t e4[G] = { w2.x & 0xFFFFu, w2.x >> 16, w2.y & 0xFFFFu, w2.y >> 16 };
-            if (e4[0] == kEmpty16)
-                continue;
             GroupHoist<DIM> h[G];
 #pragma unroll
             for (int k = 0; k < G; ++k) {
@@ -499,10 +524,8 @@ p2g_tiled_kernel(TiledArgs a)
                                 q[ch][k] = (double)rintf(val[ch][k]);
 #pragma unroll
                         for (int ch = 0; ch < 1 + DIM; ++ch) {
-                            double sum = q[ch][0];
-#pragma unroll
-                            for (int k = 1; k < G; ++k)
-                                sum = sum + q[ch][k];
+                            // exact integer adds: a pairwise tree gives the same sum
+                            const double sum = (q[ch][0] + q[ch][1]) + (q[ch][2] + q[ch][3]);
                             atomicAdd(&acc[ch * TS::nodes + lb + off], sum);
                         }
                     }
