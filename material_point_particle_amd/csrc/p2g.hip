@@ -270,59 +270,59 @@ __global__ void reset_cursor_kernel(uint32_t *cursor) { *cursor = 0u; }
 
 // Group entries of the item being processed, in LDS: a record's offset in the
 // slice, with kPad16 set when the entry only completes its cell's last group
-// (read with zero mass).
+// (read with zero mass).  Group P of an item sits in lane P % 64 of row P / 64,
+// its kGroup entries at ent[kGroup * P ...].
 constexpr uint16_t kPad16 = 0x8000u;
 constexpr int kKeyWords = 16;                 // words of four cell keys per lane: a whole slice
+constexpr uint32_t kMaxGroups = kRowsPerItem * kWave;
+constexpr uint32_t kTrashEntry = kMaxGroups * kGroup;      // spare group entry
 
-// Entry index of padded cell-sorted position s in an item with `rows` rows:
-// group g = s / kGroup sits in lane g / rows of row g % rows, entry s % kGroup.
-// magic = ceil(2^32 / rows) for rows > 1 (exact for g < 2^24).
-__device__ __forceinline__ uint32_t entry16(uint32_t s, uint32_t rows, uint32_t magic)
-{
-    const uint32_t g = s / kGroup;
-    const uint32_t q = rows == 1u ? g : __umulhi(g, magic);
-    return ((g - q * rows) * kWave + q) * kGroup + s % kGroup;
-}
-
-// Counting sort of the item's records by cell into its rows of group
-// entries ("Particle worlds, part 3", steps 3-4, on chip).  The slice's cell
-// keys are read once, four to a word, and kept in registers.  One returning
-// LDS atomic per key on its cell's counter gives both the histogram and the
-// key's rank among its cell's keys, and every key also leaves its record's
-// offset in its cell's representative slot (any one of them survives).  A
-// wave prefix sum of the counts rounded up to whole groups gives each cell's
-// first padded position; the cell's lane writes its pad entries (naming the
-// representative record), and every record is placed at its cell's start plus
-// its rank.  Every position below the padded total is written once, so the
-// item's groups are exactly the first total / kGroup.  Positions past the
-// slice's keys in a word that holds some take their atomics and
-// representative writes on a spare slot of their own lane (kWave + lane) and
-// their entry writes on a spare entry, so that inside each round of words
-// the code has no branches and the LDS operations of many keys are in
-// flight at once.  One wavefront.  `keys` holds
-// the cell key of record `first` + i at byte i; its allocation extends to a
-// multiple of 4 bytes past the last key.  Returns the number of groups; rows =
-// ceil(groups / 64).
-constexpr uint32_t kTrashEntry = kRowsPerItem * kRowSlots; // spare group entry
-
-__device__ __forceinline__ uint32_t sort_item(const uint8_t *__restrict__ keys, uint32_t first, uint32_t count,
-                                              uint16_t *ent, uint32_t *cnt, uint32_t *cstart, uint32_t *rep,
-                                              int lane, uint32_t &rows_out)
+// Counting sort of the item's records by cell into groups ("Particle worlds,
+// part 3", steps 3-4, on chip).  The slice's cell keys are read once, four to
+// a word, and kept in registers.  One returning LDS atomic per key on its
+// cell's counter gives both the histogram and the key's rank among its cell's
+// keys, and every key also leaves its record's offset in its cell's
+// representative slot (any one of them survives).  Cell c holds
+// g_c = ceil(n_c / kGroup) groups; group k of cell c (records kGroup k ..
+// kGroup k + kGroup - 1 by rank, the last one completed with pad entries that
+// name the representative record) is placed level by level: all cells' groups
+// 0 in cell order, then all groups 1, and so on, so that the 64 lanes of a row
+// hold groups of 64 different cells wherever the level is wide enough (they
+// then add to different LDS nodes, and with cells numbered x, z, y a full
+// level's lanes hit distinct banks).  gpos[cg_c + k] is that place, cg_c the
+// cell's first group in cell order.  Positions past the slice's keys in a word
+// that holds some take their atomics and representative writes on a spare
+// slot of their own lane (kWave + lane) and their entry writes on a spare
+// entry, so that inside each round of words the code has no branches and the
+// LDS operations of many keys are in flight at once.  One wavefront.  The
+// keys are read by load_keys: the cell key of record `first` + i is byte i of
+// the key array, whose allocation extends to a multiple of 4 bytes past the
+// last key.  Returns the number of groups (at most kMaxGroups for a slice of
+// at most slice_records()).
+__device__ __forceinline__ void load_keys(const uint8_t *__restrict__ keys, uint32_t first, uint32_t count, int lane,
+                                          uint32_t kw[kKeyWords])
 {
     const uint32_t off = first & 3u;
     const uint32_t *words = reinterpret_cast<const uint32_t *>(keys + (first - off));
     const uint32_t n_words = (off + count + 3u) / 4u;
     const uint32_t last_word = n_words - 1u;
-    const int rounds = (int)((n_words + kWave - 1) / kWave);   // rounds of one word per lane
-    cnt[lane] = 0u;
-    cnt[kWave + lane] = 0u;
-    uint32_t kw[kKeyWords];
+    const int rounds = (int)((n_words + kWave - 1) / kWave);
 #pragma unroll
     for (int k = 0; k < kKeyWords; ++k) {
         const uint32_t i = (uint32_t)(k * kWave + lane);
         kw[k] = k < rounds ? words[i < last_word ? i : last_word] : 0u;
     }
-    __syncthreads();
+}
+
+// `kw` holds the slice's keys as load_keys left them; cnt must be zero on
+// entry (all 2 kWave slots), and the call leaves it so for the next item.
+__device__ __forceinline__ uint32_t sort_item(const uint32_t kw[kKeyWords], uint32_t first, uint32_t count,
+                                              uint16_t *ent, uint16_t *gpos, uint32_t *cnt, uint32_t *cgs,
+                                              uint32_t *rep, int lane)
+{
+    const uint32_t off = first & 3u;
+    const uint32_t n_words = (off + count + 3u) / 4u;
+    const int rounds = (int)((n_words + kWave - 1) / kWave);   // rounds of one word per lane
     // rank of key (k, b) among its cell's keys (spare slots: meaningless); the
     // results are only read after the barrier, so the atomics queue up
     uint32_t rk[kKeyWords][4];
@@ -343,35 +343,52 @@ __device__ __forceinline__ uint32_t sort_item(const uint8_t *__restrict__ keys, 
     }
     __syncthreads();
     const uint32_t n_l = cnt[lane];
-    const uint32_t padded = (n_l + kGroup - 1) / kGroup * kGroup;
-    const uint32_t inc = wave_inclusive_scan(padded);
-    const uint32_t groups = (uint32_t)__shfl((int)inc, kWave - 1, kWave) / kGroup;
-    const uint32_t rows = (groups + kWave - 1) / kWave;
-    const uint32_t magic = rows > 1u ? 0xFFFFFFFFu / rows + 1u : 0u;
-    const uint32_t c0 = inc - padded;
-    cstart[lane] = c0;
-    for (uint32_t q = c0 + n_l; q < inc; ++q)                  // this lane's cell's pads
-        ent[entry16(q, rows, magic)] = (uint16_t)(kPad16 | rep[lane]);
+    const uint32_t g_l = (n_l + kGroup - 1) / kGroup;
+    cnt[lane] = 0u;                                            // ready for the next item
+    cnt[kWave + lane] = 0u;
+    const uint32_t inc = wave_inclusive_scan(g_l);
+    const uint32_t groups = (uint32_t)__shfl((int)inc, kWave - 1, kWave);
+    const uint32_t cg = inc - g_l;
+    cgs[lane] = cg;
+    // level by level: this lane's cell takes the next free places of every
+    // level it reaches, in cell order among that level's cells
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t level_start = 0;
+    for (uint32_t k = 0;; ++k) {
+        const bool active = g_l > k;
+        const uint64_t m = __ballot(active);
+        if (m == 0ull)
+            break;
+        if (active)
+            gpos[cg + k] = (uint16_t)(level_start + (uint32_t)__popcll(m & below));
+        level_start += (uint32_t)__popcll(m);
+    }
+    // this lane's cell's pads complete its last group
+    for (uint32_t q = n_l; q < kGroup * g_l; ++q)
+        ent[kGroup * (uint32_t)gpos[cg + q / kGroup] + q % kGroup] = (uint16_t)(kPad16 | rep[lane]);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kKeyWords; ++k) {
         if (k >= rounds)
             continue;
-        uint32_t c4[4];
+        uint32_t g4[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const uint32_t s = 4u * (uint32_t)(k * kWave + lane) + (uint32_t)b - off;
-            c4[b] = cstart[s < count ? (kw[k] >> (8 * b)) & 0xFFu : kWave + (uint32_t)lane];
+            g4[b] = s < count ? cgs[(kw[k] >> (8 * b)) & 0xFFu] + rk[k][b] / kGroup : 0u;
         }
+        uint32_t p4[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            p4[b] = gpos[g4[b]];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const uint32_t s = 4u * (uint32_t)(k * kWave + lane) + (uint32_t)b - off;
-            const uint32_t e = entry16(c4[b] + rk[k][b], rows, magic);
+            const uint32_t e = kGroup * p4[b] + rk[k][b] % kGroup;
             ent[s < count ? e : kTrashEntry] = (uint16_t)s;
         }
     }
     __syncthreads();
-    rows_out = rows;
     return groups;
 }
 
@@ -384,12 +401,12 @@ p2g_tiled_kernel(TiledArgs a)
     constexpr int G = kGroup;
     constexpr int kFlush = (TS::nodes + kWave - 1) / kWave;      // node-block entries per lane
     __shared__ double acc[TS::ch * TS::nodes];
-    __shared__ __align__(16) uint16_t ent[kRowsPerItem * kRowSlots + 4];
-    __shared__ uint32_t cnt[2 * kWave], cstart[2 * kWave], rep[2 * kWave];   // [kWave, 2 kWave): spare slots
+    __shared__ __align__(16) uint16_t ent[kMaxGroups * kGroup + 4];
+    __shared__ uint16_t gpos[kMaxGroups];
+    __shared__ uint32_t cnt[2 * kWave], cgs[kWave], rep[2 * kWave];   // [kWave, 2 kWave): spare slots
     static_assert(slice_records<DIM>() < kPad16, "a slice offset must leave the pad bit free");
     static_assert((slice_records<DIM>() + 6) / 4 <= (uint32_t)(kWave * kKeyWords), "a slice's keys fit the key words");
-    static_assert(groups_bound<DIM>(slice_records<DIM>()) <= (uint32_t)(kRowsPerItem * kWave),
-                  "a slice's groups fit the entry rows");
+    static_assert(groups_bound<DIM>(slice_records<DIM>()) <= kMaxGroups, "a slice's groups fit the entry rows");
     static_assert(cells_per_tile<DIM>() <= (uint32_t)kWave, "one lane per cell of a tile");
     const int lane = threadIdx.x;
     const uint32_t n_items = a.meta[0];
@@ -407,19 +424,25 @@ p2g_tiled_kernel(TiledArgs a)
     }
     for (int i = lane; i < TS::ch * TS::nodes; i += kWave)
         acc[i] = 0.0;
+    cnt[lane] = 0u;
+    cnt[kWave + lane] = 0u;
     __syncthreads();
 
-    // Lane 0 fetches the next item index as soon as an item starts, and the
-    // next item's record is loaded before the current item's flush, so
-    // neither round trip stalls the wave between items.
+    // Lane 0 fetches the next item index as soon as an item starts; the next
+    // item's record is loaded during the current item's rows and its cell keys
+    // during the current item's flush, so no round trip stalls the wave
+    // between items.
     const uint4 *items = reinterpret_cast<const uint4 *>(a.items);
     uint32_t next = 0;
     if (lane == 0)
         next = atomicAdd(a.cursor, 1u);
     uint32_t item = __builtin_amdgcn_readfirstlane(next);
     uint4 rec_item = make_uint4(0u, 0u, 0u, 0u);
-    if (item < n_items)
+    uint32_t kw[kKeyWords];
+    if (item < n_items) {
         rec_item = items[item];
+        load_keys(a.cell_key, rec_item.y, rec_item.z, lane, kw);
+    }
     for (;;) {
         if (item >= n_items)
             break;
@@ -436,12 +459,16 @@ p2g_tiled_kernel(TiledArgs a)
                 t /= (uint32_t)a.ntx;
             }
         }
-        uint32_t rows;
-        const uint32_t groups = sort_item(a.cell_key, first, count, ent, cnt, cstart, rep, lane, rows);
+        const uint32_t groups = sort_item(kw, first, count, ent, gpos, cnt, cgs, rep, lane);
+        const uint32_t rows = (groups + kWave - 1) / kWave;
+        const uint32_t item_next = __builtin_amdgcn_readfirstlane(next);
+        uint4 rec_next = make_uint4(0u, 0u, 0u, 0u);
+        if (item_next < n_items)
+            rec_next = items[item_next];
         static_assert(kGroup == 4, "a group's entries load as one 8-byte word");
         for (uint32_t j = 0; j < rows; ++j) {
-            // this lane's group in row j is group lane * rows + j of the item
-            if ((uint32_t)lane * rows + j >= groups)
+            // this lane's group in row j is group 64 j + lane of the item
+            if (j * kWave + (uint32_t)lane >= groups)
                 continue;
             const uint2 w2 = *reinterpret_cast<const uint2 *>(&ent[(j * kWave + lane) * kGroup]);
             const uint32_t e4[G] = { w2.x & 0xFFFFu, w2.x >> 16, w2.y & 0xFFFFu, w2.y >> 16 };
@@ -532,9 +559,10 @@ p2g_tiled_kernel(TiledArgs a)
                 }
         }
         __syncthreads();
-        item = __builtin_amdgcn_readfirstlane(next);
+        item = item_next;
+        rec_item = rec_next;
         if (item < n_items)
-            rec_item = items[item];
+            load_keys(a.cell_key, rec_item.y, rec_item.z, lane, kw);
         // Flush: every non-zero node sum goes to the grid with one 64-bit
         // atomic, and the block is left zeroed for the next item.
 #pragma unroll
