@@ -93,8 +93,9 @@ typedef struct {
 typedef struct {
     size_t tile_count;      /* uint32 [n_tiles]     binned particles per tile                    */
     size_t tile_start;      /* uint32 [n_tiles + 1] first record of each tile (exclusive prefix sum) */
-    size_t tile_active;     /* uint8  [n_tiles] written by mpm_grid_update when given the bins: 1
-                                        for the node tiles that P2G from these bins can reach */
+    size_t tile_active;     /* uint8  [n_tiles] written by mpm_grid_update and mpm_grid_clear when
+                                        given the bins: 1 for the node tiles that P2G from these
+                                        bins can reach */
     size_t items;           /* uint32 [max_items][4] work items: tile, first record, records (a
                                         slice of at most rows_per_item rows' worth of a tile's
                                         records), 0; handed out alternately the largest and
@@ -229,6 +230,19 @@ int mpm_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32
  * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
 int mpm_grid_update(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, float *vg, float dt,
                     const float *gravity, int32_t sticky, hipStream_t stream);
+
+/* Accumulator reset before a P2G ("Implementation -- GPU Optimization &
+ * Reference Codebases", section 2.1 and rule 4 of section 5: accumulators
+ * must start each step at zero; sparse grids reset only the blocks in use).
+ * bins == NULL: every channel of every node is set to 0.  bins != NULL: the
+ * workspace of the mpm_bin_particles call whose P2G last added to this grid
+ * (same grid descriptor); only the nodes of the 4^dim-node tiles that this
+ * P2G could reach are zeroed (the set mpm_grid_update restricts itself to),
+ * which zeroes the whole grid when it was zero before that P2G.  The call
+ * writes the tile_active flags of the workspace.
+ * grid: device int64[1+dim][n]^dim, written.
+ * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
+int mpm_grid_clear(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, hipStream_t stream);
 
 /* APIC grid-to-particle gather and advection ("Implementation -- GPU
  * Optimization & Reference Codebases", sections 1 and 3.1).  Per particle,

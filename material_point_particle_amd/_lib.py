@@ -48,7 +48,7 @@ class mpm_ws_layout(ct.Structure):
 
 
 EXPORTS = ("mpm_version", "mpm_strerror", "mpm_check_bounds", "mpm_workspace_bytes", "mpm_workspace_layout",
-           "mpm_bin_particles", "mpm_p2g", "mpm_p2g_cic_split", "mpm_grid_update", "mpm_g2p")
+           "mpm_bin_particles", "mpm_p2g", "mpm_p2g_cic_split", "mpm_grid_update", "mpm_grid_clear", "mpm_g2p")
 
 _lib = None
 
@@ -84,6 +84,8 @@ def lib() -> ct.CDLL:
         L.mpm_grid_update.restype = ct.c_int
         L.mpm_grid_update.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_float,
                                       P(ct.c_float), ct.c_int32, ct.c_void_p]
+        L.mpm_grid_clear.restype = ct.c_int
+        L.mpm_grid_clear.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p]
         L.mpm_g2p.restype = ct.c_int
         L.mpm_g2p.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_float, ct.c_void_p, ct.c_void_p]
         _lib = L
@@ -176,6 +178,10 @@ def mpm_grid_update(desc, bins, grid, vg, dt: float, gravity, sticky: int, strea
     g = (ct.c_float * 3)(*(list(gravity) + [0.0] * (3 - len(gravity))))
     _check(lib().mpm_grid_update(ct.byref(desc), _ptr(bins), _ptr(grid), _ptr(vg), dt, g, sticky, _stream(stream)),
            "mpm_grid_update")
+
+
+def mpm_grid_clear(desc, bins, grid, stream=None) -> None:
+    _check(lib().mpm_grid_clear(ct.byref(desc), _ptr(bins), _ptr(grid), _stream(stream)), "mpm_grid_clear")
 
 
 def mpm_g2p(desc, vg, parts: mpm_particles, dt: float, status, stream=None) -> None:

@@ -308,6 +308,18 @@ int mpm_grid_update(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, flo
     return hip_status(launch_grid_update(grid->dim, grid->n, grid_io, vg, dt, g3, sticky, &v, stream));
 }
 
+int mpm_grid_clear(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, hipStream_t stream)
+{
+    if (check_desc(grid) != MPM_OK || !aligned(grid_io, 8) || (bins && !aligned(bins, 256)))
+        return MPM_ERR_INVALID;
+    if (!bins)
+        return hip_status(launch_grid_clear(grid->dim, grid->n, grid_io, nullptr, stream));
+    mpm_ws_layout l;
+    make_layout(grid, 0, &l);         // tile_count and tile_active come first: their offsets do not depend on n
+    const BinView v = bin_view(bins, l);
+    return hip_status(launch_grid_clear(grid->dim, grid->n, grid_io, &v, stream));
+}
+
 int mpm_g2p(const mpm_grid_desc *grid, const float *vg, const mpm_particles *particles, float dt, uint32_t *status,
             hipStream_t stream)
 {

@@ -31,40 +31,80 @@ __global__ void __launch_bounds__(256) active_tiles_kernel(const uint32_t *__res
     }
 }
 
-// One thread per node, x fastest, so every access is coalesced.  Per node:
-// v_d = (float)((double)P_d / (double)M) and v_d += dt*g_d where M != 0,
-// v = 0 where M == 0 and within `sticky` nodes of a face; then M = P = 0.
-// With `active`, nodes of inactive node tiles are skipped.
-template <int DIM>
-__global__ void __launch_bounds__(256) grid_update_kernel(int n, int64_t *__restrict__ grid, float *__restrict__ vg,
-                                                          float dt, float g0, float g1, float g2, int sticky,
-                                                          const uint8_t *__restrict__ active)
+// One thread per run of 4 x-consecutive nodes (one row of a node tile), x
+// fastest, so that every thread moves 32-byte pieces and a wavefront's
+// accesses are contiguous.  With `active`, runs in inactive node tiles are
+// skipped.  OP 0 zeroes the nodes in every channel.  OP 1 is the grid update:
+// per node v_d = (float)((double)P_d / (double)M) then v_d += dt*g_d where
+// M != 0, v = 0 where M == 0 and within `sticky` nodes of a face; then
+// M = P = 0 (P is not read where the run's four M are all zero).
+template <int DIM, int OP>
+__global__ void __launch_bounds__(256) node_rows_kernel(int n, const uint8_t *__restrict__ active,
+                                                        int64_t *__restrict__ grid, float *__restrict__ vg, float dt,
+                                                        float g0, float g1, float g2, int sticky)
 {
-    const int sh = 31 - __builtin_clz(n);                     // n is a power of two
+    const int sh = 31 - __builtin_clz(n);                     // n is a power of two, at least 8
     const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    const int64_t runs = nodes / kTile;
     const float gdt[3] = { dt * g0, dt * g1, dt * g2 };
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nodes; i += (int64_t)gridDim.x * blockDim.x) {
-        const int ix = (int)(i & (n - 1)), iy = (int)((i >> sh) & (n - 1));
-        const int iz = DIM == 3 ? (int)(i >> (2 * sh)) : 0;
-        if (active && !active[(((int64_t)(iz >> 2) << (2 * sh - 4)) | ((int64_t)(iy >> 2) << (sh - 2))) | (ix >> 2)])
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < runs; r += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i0 = r * kTile;
+        const int ix0 = (int)(i0 & (n - 1)), iy = (int)((i0 >> sh) & (n - 1));
+        const int iz = DIM == 3 ? (int)(i0 >> (2 * sh)) : 0;
+        if (active && !active[(((int64_t)(iz >> 2) << (2 * sh - 4)) | ((int64_t)(iy >> 2) << (sh - 2))) | (ix0 >> 2)])
             continue;
-        bool wall = ix < sticky || ix >= n - sticky || iy < sticky || iy >= n - sticky;
-        if (DIM == 3)
-            wall = wall || iz < sticky || iz >= n - sticky;
-        const int64_t M = grid[i];
+        if (OP == 0) {
 #pragma unroll
-        for (int d = 0; d < DIM; ++d) {
-            const int64_t P = grid[(1 + d) * nodes + i];
-            float v = 0.0f;
-            if (M != 0) {
-                v = (float)((double)P / (double)M);
-                v = v + gdt[d];
+            for (int ch = 0; ch < 1 + DIM; ++ch) {
+                longlong2 *q = reinterpret_cast<longlong2 *>(grid + ch * nodes + i0);
+                q[0] = make_longlong2(0, 0);
+                q[1] = make_longlong2(0, 0);
             }
-            vg[d * nodes + i] = wall ? 0.0f : v;
-            grid[(1 + d) * nodes + i] = 0;
+        } else {
+            bool wall_row = iy < sticky || iy >= n - sticky;
+            if (DIM == 3)
+                wall_row = wall_row || iz < sticky || iz >= n - sticky;
+            longlong2 *Mq = reinterpret_cast<longlong2 *>(grid + i0);
+            const longlong2 m01 = Mq[0], m23 = Mq[1];
+            const int64_t M[4] = { m01.x, m01.y, m23.x, m23.y };
+            const bool any = (M[0] | M[1] | M[2] | M[3]) != 0;
+#pragma unroll
+            for (int d = 0; d < DIM; ++d) {
+                longlong2 *Pq = reinterpret_cast<longlong2 *>(grid + (1 + d) * nodes + i0);
+                int64_t P[4] = { 0, 0, 0, 0 };
+                if (any) {
+                    const longlong2 p01 = Pq[0], p23 = Pq[1];
+                    P[0] = p01.x;
+                    P[1] = p01.y;
+                    P[2] = p23.x;
+                    P[3] = p23.y;
+                }
+                float v[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    float vk = 0.0f;
+                    if (M[k] != 0) {
+                        vk = (float)((double)P[k] / (double)M[k]);
+                        vk = vk + gdt[d];
+                    }
+                    const bool wall = wall_row || ix0 + k < sticky || ix0 + k >= n - sticky;
+                    v[k] = wall ? 0.0f : vk;
+                }
+                *reinterpret_cast<float4 *>(vg + d * nodes + i0) = make_float4(v[0], v[1], v[2], v[3]);
+                Pq[0] = make_longlong2(0, 0);
+                Pq[1] = make_longlong2(0, 0);
+            }
+            Mq[0] = make_longlong2(0, 0);
+            Mq[1] = make_longlong2(0, 0);
         }
-        grid[i] = 0;
     }
+}
+
+// Zeroes every channel of every node.
+__global__ void __launch_bounds__(256) clear_kernel(int64_t *__restrict__ grid, int64_t count)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+        grid[i] = 0;
 }
 
 // One thread per particle.  Over the stencil in lexicographic node order (x
@@ -165,28 +205,57 @@ int blocks_for(int64_t work, int block)
 
 }  // namespace
 
+namespace {
+
+// Flags of the node tiles the binned particles can reach, in bins->tile_active.
+void mark_active(int dim, int n, const BinView *bins, hipStream_t s)
+{
+    const int ntx = n / kTile;
+    if (dim == 3)
+        hipLaunchKernelGGL(active_tiles_kernel<3>, dim3(blocks_for(bins->n_tiles, 256)), dim3(256), 0, s,
+                           bins->tile_count, ntx, bins->n_tiles, bins->tile_active);
+    else
+        hipLaunchKernelGGL(active_tiles_kernel<2>, dim3(blocks_for(bins->n_tiles, 256)), dim3(256), 0, s,
+                           bins->tile_count, ntx, bins->n_tiles, bins->tile_active);
+}
+
+template <int OP>
+void node_rows(int dim, int n, const uint8_t *active, int64_t *grid, float *vg, float dt, const float *g, int sticky,
+               hipStream_t s)
+{
+    const int64_t runs = (dim == 3 ? (int64_t)n * n * n : (int64_t)n * n) / kTile;
+    const unsigned blocks = (unsigned)blocks_for(runs, 256);
+    if (dim == 3)
+        hipLaunchKernelGGL((node_rows_kernel<3, OP>), dim3(blocks), dim3(256), 0, s, n, active, grid, vg, dt, g[0],
+                           g[1], g[2], sticky);
+    else
+        hipLaunchKernelGGL((node_rows_kernel<2, OP>), dim3(blocks), dim3(256), 0, s, n, active, grid, vg, dt, g[0],
+                           g[1], g[2], sticky);
+}
+
+}  // namespace
+
 hipError_t launch_grid_update(int dim, int n, int64_t *grid, float *vg, float dt, const float *gravity, int sticky,
                               const BinView *bins, hipStream_t s)
 {
+    const float g[3] = { gravity[0], gravity[1], dim == 3 ? gravity[2] : 0.0f };
+    if (bins)
+        mark_active(dim, n, bins, s);
+    node_rows<1>(dim, n, bins ? bins->tile_active : nullptr, grid, vg, dt, g, sticky, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_grid_clear(int dim, int n, int64_t *grid, const BinView *bins, hipStream_t s)
+{
     const int64_t nodes = dim == 3 ? (int64_t)n * n * n : (int64_t)n * n;
-    const float g0 = gravity[0], g1 = gravity[1], g2 = dim == 3 ? gravity[2] : 0.0f;
-    const uint8_t *active = nullptr;
     if (bins) {
-        const int ntx = n / kTile;
-        if (dim == 3)
-            hipLaunchKernelGGL(active_tiles_kernel<3>, dim3(blocks_for(bins->n_tiles, 256)), dim3(256), 0, s,
-                               bins->tile_count, ntx, bins->n_tiles, bins->tile_active);
-        else
-            hipLaunchKernelGGL(active_tiles_kernel<2>, dim3(blocks_for(bins->n_tiles, 256)), dim3(256), 0, s,
-                               bins->tile_count, ntx, bins->n_tiles, bins->tile_active);
-        active = bins->tile_active;
+        const float g[3] = { 0.0f, 0.0f, 0.0f };
+        mark_active(dim, n, bins, s);
+        node_rows<0>(dim, n, bins->tile_active, grid, nullptr, 0.0f, g, 0, s);
+    } else {
+        hipLaunchKernelGGL(clear_kernel, dim3(blocks_for((1 + dim) * nodes, 256)), dim3(256), 0, s, grid,
+                           (int64_t)(1 + dim) * nodes);
     }
-    if (dim == 3)
-        hipLaunchKernelGGL(grid_update_kernel<3>, dim3(blocks_for(nodes, 256)), dim3(256), 0, s, n, grid, vg, dt, g0,
-                           g1, g2, sticky, active);
-    else
-        hipLaunchKernelGGL(grid_update_kernel<2>, dim3(blocks_for(nodes, 256)), dim3(256), 0, s, n, grid, vg, dt, g0,
-                           g1, g2, sticky, active);
     return hipGetLastError();
 }
 

@@ -65,6 +65,11 @@ class Transfer:
         L.mpm_grid_update(self.desc, self.ws if active else None, self.grid, self.vg, dt, gravity, sticky)
         return self.vg
 
+    def clear(self, active: bool = False) -> None:
+        """Zero the grid; active: only the node tiles the last binned P2G can
+        reach (the workspace must hold that binning)."""
+        L.mpm_grid_clear(self.desc, self.ws if active else None, self.grid)
+
     def g2p(self, parts: DeviceParticles, dt: float) -> None:
         L.mpm_g2p(self.desc, self.vg, parts.desc(), dt, self.status)
 

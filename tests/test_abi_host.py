@@ -125,5 +125,8 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert lib.mpm_grid_update(ct.byref(d), None, grid, ct.c_void_p(4096), 1e-4, None, 2, None) == L.MPM_ERR_INVALID
     assert lib.mpm_grid_update(ct.byref(d), ct.c_void_p(4100), grid, ct.c_void_p(4096), 1e-4, g, 2,
                                None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_clear(ct.byref(d), None, ct.c_void_p(4100), None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_clear(ct.byref(d), ct.c_void_p(4100), grid, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_clear(None, None, grid, None) == L.MPM_ERR_INVALID
     p3 = L.mpm_particles(10, 4096, 4096, None, 4096)
     assert lib.mpm_g2p(ct.byref(d), ct.c_void_p(4096), ct.byref(p3), 1e-4, status, None) == L.MPM_ERR_INVALID

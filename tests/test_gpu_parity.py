@@ -402,6 +402,67 @@ def test_active_grid_update_matches_dense_on_reachable_nodes(mpm, oracle_lib):
     assert int(tr.grid.abs().sum()) == 0
 
 
+def reachable_nodes(tr, dim, n):
+    """Per-node mask of the node tiles a binned P2G can reach: a tile whose own
+    or lower-neighbour cell tile holds binned particles."""
+    nt = n // 4
+    lay = tr.layout
+    tcount = u32(tr.ws_u32("tile_count", lay.n_tiles)).reshape((nt,) * dim) != 0
+    want = np.zeros_like(tcount)
+    for e in range(1 << dim):
+        sl_dst = tuple(slice((e >> a) & 1, None) for a in range(dim))
+        sl_src = tuple(slice(0, nt - ((e >> a) & 1)) for a in range(dim))
+        want[sl_dst] |= tcount[sl_src]
+    node = want
+    for a in range(dim):
+        node = np.repeat(node, 4, axis=a)
+    return want, node
+
+
+@pytest.mark.parametrize("name,count", [("pile_2d", None), ("blobs_3d_256", 1 << 16)])
+def test_restricted_clear_and_update_on_reachable_tiles(mpm, oracle_lib, name, count):
+    """mpm_grid_clear and mpm_grid_update with the bins touch exactly the node
+    tiles the binned P2G can reach: the clear zeroes them and leaves every
+    other node as it was; the update matches the oracle's dense update there
+    (bit-exact), leaves vg elsewhere and zeroes the accumulators."""
+    from material_point_particle_amd.transfer import DeviceParticles, Transfer
+    w = WORKLOADS[name] if count is None else scaled(WORKLOADS[name], count)
+    host = build(w)
+    parts = DeviceParticles(host)
+    tr = Transfer(w.dim, w.n, w.frac_bits, ranges_of(w), parts.n)
+    tr.bin(parts)
+    tr.p2g(parts, binned=True)
+    torch.cuda.synchronize()
+    grid0 = tr.grid.cpu().numpy()
+    want, node_act = reachable_nodes(tr, w.dim, w.n)
+    assert not np.any((grid0 != 0).any(axis=0) & ~node_act), "a deposit outside the reachable tiles"
+    say("restricted clear", w.name)
+    sentinel = torch.from_numpy(np.where(node_act[None], grid0, 7)).to(tr.grid.device)
+    tr.grid.copy_(sentinel)
+    tr.clear(active=True)
+    torch.cuda.synchronize()
+    lay = tr.layout
+    act = tr.ws.view(torch.uint8)[lay.tile_active: lay.tile_active + lay.n_tiles].cpu().numpy()
+    assert np.array_equal(act.reshape(want.shape) != 0, want)
+    after = tr.grid.cpu().numpy()
+    assert np.all(after[:, node_act] == 0)
+    assert np.all(after[:, ~node_act] == 7)
+    tr.clear()
+    torch.cuda.synchronize()
+    assert int(tr.grid.abs().sum()) == 0
+    say("restricted update", w.name)
+    tr.grid.copy_(torch.from_numpy(grid0).to(tr.grid.device))
+    tr.vg.fill_(12345.0)
+    dt, gravity, sticky = 1e-4, [0.0, -9.8, 0.0][:w.dim], 2
+    tr.grid_update(dt, gravity, sticky, active=True)
+    torch.cuda.synchronize()
+    vg_ref = oracle_lib.grid_update(w.dim, w.n, grid0.copy(), dt, gravity, sticky)
+    vg = tr.vg.cpu().numpy()
+    assert np.array_equal(vg[:, node_act], vg_ref[:, node_act])
+    assert np.all(vg[:, ~node_act] == 12345.0)
+    assert int(tr.grid.abs().sum()) == 0
+
+
 def test_substeps_lockstep_with_oracle_small(mpm, oracle_lib):
     """Dam-break recipe on 64^3 nodes, 2^16 particles, 100 substeps: the GPU
     and the oracle each run their own trajectory; at every 10th substep the
