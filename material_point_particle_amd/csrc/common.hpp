@@ -18,7 +18,7 @@ constexpr int kWave = 64;
 constexpr int kTile = 4;             // tile edge in cells
 constexpr int kGroup = 4;            // records per group: one cell's particles, four at a time
 constexpr int kRowSlots = kWave * kGroup;  // a row: one group per lane (256 group entries)
-constexpr int kRowsPerItem = 16;     // most rows of one P2G work item (4096 group entries)
+constexpr int kRowsPerItem = 8;      // most rows of one P2G work item (2048 group entries)
 constexpr int kPlanTiles = 4096;     // tiles per block of binning's work-item plan
 constexpr int kPlanStride = 2 + kRowsPerItem;  // words per plan block: records, full slices, slices per class
 

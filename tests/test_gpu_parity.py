@@ -182,9 +182,11 @@ def _cloud_in_cells(dim, n, cells_and_counts, seed):
 def test_p2g_ragged_and_dense_tiles(mpm, oracle_lib, layout):
     dim, n, k = 3, 32, 32
     if layout == "ragged_tiles":
-        # tiles with 1, 63, 64, 65, 2047, 2048, 2049 and 4097 particles (rows and work-item boundaries)
+        # tiles with 1, 63, 64, 65, 2047, 2048, 2049 and 4097 particles (row boundaries), and 1855, 1856,
+        # 1857 and 3713 (a work item holds at most 8 rows: 8 * 256 - 3 * 64 = 1856 records in 3D)
         spec = [((1, 1, 1), 1), ((5, 1, 1), 63), ((9, 1, 1), 64), ((13, 2, 3), 65), ((1, 5, 1), 2047),
-                ((5, 5, 5), 2048), ((9, 9, 9), 2049), ((13, 13, 13), 4097)]
+                ((5, 5, 5), 2048), ((9, 9, 9), 2049), ((13, 13, 13), 4097), ((17, 1, 1), 1855),
+                ((21, 1, 1), 1856), ((25, 1, 1), 1857), ((17, 5, 1), 3713)]
     elif layout == "one_dense_cell":
         spec = [((17, 17, 17), 9000)]
     else:
