@@ -361,7 +361,12 @@ __global__ void __launch_bounds__(kPlanBlock) plan_final_kernel(const uint32_t *
 // zero mass, velocity and affine matrix: they contribute nothing, as if
 // skipped.  Each thread loads two particles before writing either, so that
 // twice the loads are in flight.  Every lane of a wavefront runs the same
-// number of iterations, so all of them reach write_records's exchanges.
+// number of iterations, so all of them reach write_records's exchanges.  The
+// streams read or written once (particle fields, ranks, slots, records) carry
+// the nontemporal hint, which leaves the L2 to the one-byte cell keys: those
+// land scattered and are merged into whole lines there (measured: 0.80 ->
+// 0.75 ms for the 16M-particle blob binning; the keys themselves with the hint
+// take 1.2 ms).
 template <int DIM>
 __device__ __forceinline__ void load_record(const Fields &f, int64_t p, float *rec)
 {
@@ -369,14 +374,14 @@ __device__ __forceinline__ void load_record(const Fields &f, int64_t p, float *r
     int fi = 0;
 #pragma unroll
     for (int e = 0; e < DIM; ++e)
-        rec[fi++] = f.x[e * f.n + p];
+        rec[fi++] = __builtin_nontemporal_load(&f.x[e * f.n + p]);
 #pragma unroll
     for (int e = 0; e < DIM; ++e)
-        rec[fi++] = f.v[e * f.n + p];
+        rec[fi++] = __builtin_nontemporal_load(&f.v[e * f.n + p]);
 #pragma unroll
     for (int q = 0; q < DIM * DIM; ++q)
-        rec[fi++] = f.C ? f.C[q * f.n + p] : 0.0f;
-    rec[fi++] = f.m[p];
+        rec[fi++] = f.C ? __builtin_nontemporal_load(&f.C[q * f.n + p]) : 0.0f;
+    rec[fi++] = __builtin_nontemporal_load(&f.m[p]);
 #pragma unroll
     for (; fi < R; ++fi)
         rec[fi] = 0.0f;
@@ -411,11 +416,13 @@ __device__ __forceinline__ uint32_t place_record(const Fields &f, RangesF r, flo
         for (int q = DIM; q < R; ++q)
             rec[q] = 0.0f;
     }
-    const uint32_t pos = tile_start[t] + rank_in[p];
-    slot_out[p] = pos;
+    const uint32_t pos = tile_start[t] + __builtin_nontemporal_load(&rank_in[p]);
+    __builtin_nontemporal_store(pos, &slot_out[p]);
     cell_key[pos] = (uint8_t)l;
     return pos;
 }
+
+typedef float v4nt __attribute__((ext_vector_type(4)));
 
 // Writes the wavefront's 64 records (one per lane, destination pos or kEmpty).
 // In 3D a record is four 16-byte pieces; the records pass through LDS so that
@@ -446,7 +453,7 @@ __device__ __forceinline__ void write_records(const float *rec, uint32_t pos, fl
             const uint32_t d = spos[src];
             const float4 v = stage[src * 4 + ((piece + src + (src >> 2)) & 3)];
             if (d != kEmpty)
-                reinterpret_cast<float4 *>(sorted + (int64_t)d * R)[piece] = v;
+                __builtin_nontemporal_store(v4nt{ v.x, v.y, v.z, v.w }, reinterpret_cast<v4nt *>(sorted + (int64_t)d * R) + piece);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -455,10 +462,10 @@ __device__ __forceinline__ void write_records(const float *rec, uint32_t pos, fl
         (void)stage;
         (void)spos;
         if (pos != kEmpty) {
-            float4 *dst = reinterpret_cast<float4 *>(sorted + (int64_t)pos * R);
+            v4nt *dst = reinterpret_cast<v4nt *>(sorted + (int64_t)pos * R);
 #pragma unroll
             for (int q = 0; q < R / 4; ++q)
-                dst[q] = make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
+                __builtin_nontemporal_store(v4nt{ rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3] }, dst + q);
         }
     }
 }
