@@ -273,7 +273,7 @@ __global__ void reset_cursor_kernel(uint32_t *cursor) { *cursor = 0u; }
 // (read with zero mass).  Group P of an item sits in lane P % 64 of row P / 64,
 // its kGroup entries at ent[kGroup * P ...].
 constexpr uint16_t kPad16 = 0x8000u;
-constexpr int kKeyWords = 16;                 // words of four cell keys per lane: a whole slice
+constexpr int kKeyWords = 8;                  // words of four cell keys per lane: a whole slice
 constexpr uint32_t kMaxGroups = kRowsPerItem * kWave;
 constexpr uint32_t kTrashEntry = kMaxGroups * kGroup;      // spare group entry
 
