@@ -61,6 +61,9 @@ def lib():
         L.oracle_g2p.restype = None
         L.oracle_g2p.argtypes = [ct.c_int, ct.c_int, F32P, ct.c_int64, F32P, F32P, F32P, ct.c_float, U32P]
         L.oracle_bin.restype = ct.c_int64
+        L.oracle_neohookean_affine.argtypes = [ct.c_int, ct.c_int, ct.c_int64, F32P, F32P, F32P, F32P, ct.c_float,
+                                               ct.c_float, ct.c_float, F32P, U32P]
+        L.oracle_update_F.argtypes = [ct.c_int, ct.c_int64, F32P, F32P, ct.c_float]
         L.oracle_bin.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_int64, F32P, F32P, F32P, F32P,
                                  ct.c_double, ct.c_double, ct.c_double, U32P, U32P, I64P]
         _lib = L
@@ -145,6 +148,26 @@ def g2p(dim: int, n: int, vg: np.ndarray, particles: dict, dt: float):
     lib().oracle_g2p(dim, n, _p(vg, F32P), x.shape[1], _p(x, F32P), _p(v, F32P), _p(C, F32P), ct.c_float(dt),
                      _p(status, U32P))
     return status
+
+
+def neohookean_affine(dim: int, n: int, particles: dict, F: np.ndarray, vol0: np.ndarray, dt: float, mu: float,
+                      lam: float):
+    """MLS-MPM affine matrix with the Neo-Hookean stress term; returns (C'[dim*dim][np], status[4])."""
+    _, _, C, m = _soa(particles)
+    F = np.ascontiguousarray(F, dtype=np.float32)
+    vol0 = np.ascontiguousarray(vol0, dtype=np.float32)
+    out = np.empty_like(C)
+    status = np.zeros(4, dtype=np.uint32)
+    lib().oracle_neohookean_affine(dim, n, m.shape[0], _p(F, F32P), _p(C, F32P), _p(m, F32P), _p(vol0, F32P),
+                                   ct.c_float(dt), ct.c_float(mu), ct.c_float(lam), _p(out, F32P), _p(status, U32P))
+    return out, status
+
+
+def update_F(dim: int, C: np.ndarray, F: np.ndarray, dt: float) -> None:
+    """F <- (I + dt C) F in place (F float32 C-contiguous [dim*dim][np])."""
+    C = np.ascontiguousarray(C, dtype=np.float32)
+    assert F.dtype == np.float32 and F.flags.c_contiguous
+    lib().oracle_update_F(dim, F.shape[1], _p(C, F32P), _p(F, F32P), ct.c_float(dt))
 
 
 def bin_particles(dim: int, n: int, tile: int, particles: dict, ranges):

@@ -20,7 +20,9 @@
  *  - "Implementation -- GPU Optimization & Reference Codebases" (vocaro.com),
  *    section 1 (the four-phase step reset -> P2G -> grid update -> G2P),
  *    section 2.1 (fixed-point accumulation, tiles), section 3.1 (APIC
- *    transfer with the 3x3 quadratic B-spline stencil and affine matrix C),
+ *    transfer with the 3x3 quadratic B-spline stencil and affine matrix C;
+ *    part 2 of the guide described there: the Neo-Hookean stress and the
+ *    deformation gradient),
  *    section 3.3.1 (rounding, not truncating, fixed-point encode), section 5
  *    rules 1, 4, 7 and 9 (integer accumulation converted once in the grid
  *    update; consume-and-zero; gravity owned by the solver; counted
@@ -374,6 +376,108 @@ void oracle_g2p(int dim, int n, const float *vg, int64_t np_, float *x, float *v
             x[d * np_ + p] = xc;
         }
         status[ST_CLAMP] += (uint32_t)clamped;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* MLS-MPM stress term of a Neo-Hookean solid.                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * "Implementation -- GPU Optimization & Reference Codebases", section 3.1,
+ * part 2 of the guide: with J = det F and F^-T = (F^T)^-1,
+ *   P = mu (F - F^-T) + lambda log(J) F^-T,   sigma = (1/J) P F^T.
+ * In the MLS-MPM transfer the stress enters the affine term (reading 17): a
+ * particle adds w_i (m v + Q (x_i - x_p)) to node i with
+ * Q = m C - dt vol sigma D^-1, where D^-1 = 4 / dx^2 = 4 n^2 for the
+ * quadratic B-spline (the inverse of sum_i w_i r_i r_i^T) and
+ * vol sigma = vol0 J sigma = vol0 P F^T (vol0 the particle's initial volume).
+ * Divided by m, the APIC P2G arithmetic is unchanged when its affine matrix is
+ *   C' = C - k (P F^T),   k = dt vol0 4 n^2 / m.
+ * Everything is float64 in the order written; each C' entry is rounded to
+ * float32 once.  F^-T is the cofactor matrix over J.  Particles with
+ * det F <= 0 (inverted) or m == 0 keep C' = C; the inverted ones are counted
+ * in status[0].  F and C are component-major: entry (d, e) at [(d dim + e) np].
+ */
+void oracle_neohookean_affine(int dim, int n, int64_t np_, const float *F, const float *C, const float *m,
+                              const float *vol0, float dt, float mu, float lambda, float *Cout, uint32_t *status)
+{
+    const double scale = 4.0 * (double)n * (double)n;
+    for (int64_t p = 0; p < np_; ++p) {
+        double f[3][3] = { { 0 } }, cof[3][3] = { { 0 } };
+        for (int d = 0; d < dim; ++d)
+            for (int e = 0; e < dim; ++e) {
+                f[d][e] = (double)F[(int64_t)(d * dim + e) * np_ + p];
+                Cout[(int64_t)(d * dim + e) * np_ + p] = C[(int64_t)(d * dim + e) * np_ + p];
+            }
+        double J;
+        if (dim == 3) {
+            cof[0][0] = f[1][1] * f[2][2] - f[1][2] * f[2][1];
+            cof[0][1] = f[1][2] * f[2][0] - f[1][0] * f[2][2];
+            cof[0][2] = f[1][0] * f[2][1] - f[1][1] * f[2][0];
+            cof[1][0] = f[0][2] * f[2][1] - f[0][1] * f[2][2];
+            cof[1][1] = f[0][0] * f[2][2] - f[0][2] * f[2][0];
+            cof[1][2] = f[0][1] * f[2][0] - f[0][0] * f[2][1];
+            cof[2][0] = f[0][1] * f[1][2] - f[0][2] * f[1][1];
+            cof[2][1] = f[0][2] * f[1][0] - f[0][0] * f[1][2];
+            cof[2][2] = f[0][0] * f[1][1] - f[0][1] * f[1][0];
+            J = (f[0][0] * cof[0][0] + f[0][1] * cof[0][1]) + f[0][2] * cof[0][2];
+        } else {
+            cof[0][0] = f[1][1];
+            cof[0][1] = -f[1][0];
+            cof[1][0] = -f[0][1];
+            cof[1][1] = f[0][0];
+            J = f[0][0] * f[1][1] - f[0][1] * f[1][0];
+        }
+        if (!(J > 0.0)) {
+            status[ST_DOMAIN] += 1;
+            continue;
+        }
+        if (m[p] == 0.0f)
+            continue;
+        const double llj = (double)lambda * log(J);
+        double P[3][3];
+        for (int d = 0; d < dim; ++d)
+            for (int e = 0; e < dim; ++e) {
+                const double fit = cof[d][e] / J;                       /* (F^-T)_de */
+                P[d][e] = (double)mu * (f[d][e] - fit) + llj * fit;
+            }
+        const double k = (((double)dt * (double)vol0[p]) * scale) / (double)m[p];
+        for (int d = 0; d < dim; ++d)
+            for (int e = 0; e < dim; ++e) {
+                double tau = 0.0;                                       /* (P F^T)_de */
+                for (int q = 0; q < dim; ++q)
+                    tau = tau + P[d][q] * f[e][q];
+                const int64_t i = (int64_t)(d * dim + e) * np_ + p;
+                Cout[i] = (float)((double)C[i] - k * tau);
+            }
+    }
+}
+
+/*
+ * Deformation gradient update after G2P (the same part of the guide):
+ * F <- (I + dt C) F with C the particle's new affine matrix, in float32:
+ * G_dq = [d == q] + dt C_dq, then F'_de = sum_q G_dq F_qe in order q = 0, 1, 2.
+ */
+void oracle_update_F(int dim, int64_t np_, const float *C, float *F, float dt)
+{
+    for (int64_t p = 0; p < np_; ++p) {
+        float G[3][3], f[3][3], out[3][3];
+        for (int d = 0; d < dim; ++d)
+            for (int q = 0; q < dim; ++q) {
+                G[d][q] = (d == q ? 1.0f : 0.0f) + dt * C[(int64_t)(d * dim + q) * np_ + p];
+                f[d][q] = F[(int64_t)(d * dim + q) * np_ + p];
+            }
+        for (int d = 0; d < dim; ++d)
+            for (int e = 0; e < dim; ++e) {
+                float t = G[d][0] * f[0][e];
+                for (int q = 1; q < dim; ++q)
+                    t = t + G[d][q] * f[q][e];
+                out[d][e] = t;
+            }
+        for (int d = 0; d < dim; ++d)
+            for (int e = 0; e < dim; ++e)
+                F[(int64_t)(d * dim + e) * np_ + p] = out[d][e];
     }
 }
 
