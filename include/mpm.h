@@ -260,6 +260,35 @@ int mpm_grid_clear(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, hipS
 int mpm_g2p(const mpm_grid_desc *grid, const float *vg, const mpm_particles *particles, float dt,
             uint32_t *status, hipStream_t stream);
 
+/* MLS-MPM stress term of a Neo-Hookean solid ("Implementation -- GPU
+ * Optimization & Reference Codebases", section 3.1, part 2 of the guide
+ * described there: P = mu (F - F^-T) + lambda log(J) F^-T, J = det F,
+ * sigma = P F^T / J).  The stress enters P2G through the affine term
+ * Q = m C - dt vol sigma 4 n^2 (vol sigma = vol0 P F^T); divided by m, the
+ * APIC P2G is unchanged when its affine matrix is
+ *   C' = C - (dt vol0 4 n^2 / m) P F^T,
+ * which this call writes to C_out, for binning and P2G to read in place of C.
+ * Per particle in float64 in this order: the cofactor matrix cof of F (F^-T =
+ * cof / J), J = (F00 cof00 + F01 cof01) + F02 cof02 (2D: F00 F11 - F01 F10),
+ * P_de = mu (F_de - cof_de / J) + (lambda log J) (cof_de / J),
+ * tau_de = sum_q P_dq F_eq, k = ((dt vol0) 4 n^2) / m, C'_de = C_de - k tau_de
+ * rounded to float32 once.  Particles with det F <= 0 (counted in status[0])
+ * or m == 0 get C' = C.
+ * particles: device; C and m read (x, v unused).  F: device float[dim*dim][n]
+ * component-major like C.  vol0: device float[n], initial volumes.  C_out:
+ * device float[dim*dim][n], written (may not alias C).
+ * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
+int mpm_neohookean_affine(const mpm_grid_desc *grid, const mpm_particles *particles, const float *F, const float *vol0,
+                          float dt, float mu, float lambda, float *C_out, uint32_t *status, hipStream_t stream);
+
+/* Deformation gradient update after G2P (the same part of the guide):
+ * F <- (I + dt C) F with C the particles' new affine matrices, in float32:
+ * G_dq = [d == q] + dt C_dq, F'_de = (G_d0 F_0e + G_d1 F_1e) + G_d2 F_2e.
+ * particles: device, C read.  F: device float[dim*dim][n], read and written.
+ * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
+int mpm_update_deformation(const mpm_grid_desc *grid, const mpm_particles *particles, float *F, float dt,
+                           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,7 +48,8 @@ class mpm_ws_layout(ct.Structure):
 
 
 EXPORTS = ("mpm_version", "mpm_strerror", "mpm_check_bounds", "mpm_workspace_bytes", "mpm_workspace_layout",
-           "mpm_bin_particles", "mpm_p2g", "mpm_p2g_cic_split", "mpm_grid_update", "mpm_grid_clear", "mpm_g2p")
+           "mpm_bin_particles", "mpm_p2g", "mpm_p2g_cic_split", "mpm_grid_update", "mpm_grid_clear", "mpm_g2p",
+           "mpm_neohookean_affine", "mpm_update_deformation")
 
 _lib = None
 
@@ -88,6 +89,11 @@ def lib() -> ct.CDLL:
         L.mpm_grid_clear.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p]
         L.mpm_g2p.restype = ct.c_int
         L.mpm_g2p.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_float, ct.c_void_p, ct.c_void_p]
+        L.mpm_neohookean_affine.restype = ct.c_int
+        L.mpm_neohookean_affine.argtypes = [P(mpm_grid_desc), P(mpm_particles), ct.c_void_p, ct.c_void_p, ct.c_float,
+                                            ct.c_float, ct.c_float, ct.c_void_p, ct.c_void_p, ct.c_void_p]
+        L.mpm_update_deformation.restype = ct.c_int
+        L.mpm_update_deformation.argtypes = [P(mpm_grid_desc), P(mpm_particles), ct.c_void_p, ct.c_float, ct.c_void_p]
         _lib = L
     return _lib
 
@@ -186,3 +192,14 @@ def mpm_grid_clear(desc, bins, grid, stream=None) -> None:
 
 def mpm_g2p(desc, vg, parts: mpm_particles, dt: float, status, stream=None) -> None:
     _check(lib().mpm_g2p(ct.byref(desc), _ptr(vg), ct.byref(parts), dt, _ptr(status), _stream(stream)), "mpm_g2p")
+
+
+def mpm_neohookean_affine(desc, parts: mpm_particles, F, vol0, dt: float, mu: float, lam: float, C_out, status,
+                          stream=None) -> None:
+    _check(lib().mpm_neohookean_affine(ct.byref(desc), ct.byref(parts), _ptr(F), _ptr(vol0), dt, mu, lam, _ptr(C_out),
+                                       _ptr(status), _stream(stream)), "mpm_neohookean_affine")
+
+
+def mpm_update_deformation(desc, parts: mpm_particles, F, dt: float, stream=None) -> None:
+    _check(lib().mpm_update_deformation(ct.byref(desc), ct.byref(parts), _ptr(F), dt, _stream(stream)),
+           "mpm_update_deformation")

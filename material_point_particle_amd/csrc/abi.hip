@@ -320,6 +320,31 @@ int mpm_grid_clear(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, hipS
     return hip_status(launch_grid_clear(grid->dim, grid->n, grid_io, &v, stream));
 }
 
+int mpm_neohookean_affine(const mpm_grid_desc *grid, const mpm_particles *particles, const float *F, const float *vol0,
+                          float dt, float mu, float lambda, float *C_out, uint32_t *status, hipStream_t stream)
+{
+    if (check_desc(grid) != MPM_OK || !particles || particles->n < 0 || particles->n > kMaxParticles)
+        return MPM_ERR_INVALID;
+    const int64_t np = particles->n;
+    if (np > 0 && (!particles->C || !particles->m || !F || !vol0 || !C_out || !aligned(particles->C, 4) ||
+                   !aligned(particles->m, 4) || !aligned(F, 4) || !aligned(vol0, 4) || !aligned(C_out, 4)))
+        return MPM_ERR_INVALID;
+    if (!aligned(status, 4) || !(dt >= 0.0f) || !(mu >= 0.0f) || !(lambda >= 0.0f))
+        return MPM_ERR_INVALID;
+    return hip_status(launch_neohookean_affine(grid->dim, grid->n, np, F, particles->C, particles->m, vol0, dt, mu,
+                                               lambda, C_out, status, stream));
+}
+
+int mpm_update_deformation(const mpm_grid_desc *grid, const mpm_particles *particles, float *F, float dt,
+                           hipStream_t stream)
+{
+    if (check_desc(grid) != MPM_OK || !particles || particles->n < 0 || particles->n > kMaxParticles)
+        return MPM_ERR_INVALID;
+    if (particles->n > 0 && (!particles->C || !F || !aligned(particles->C, 4) || !aligned(F, 4)))
+        return MPM_ERR_INVALID;
+    return hip_status(launch_update_F(grid->dim, particles->n, particles->C, F, dt, stream));
+}
+
 int mpm_g2p(const mpm_grid_desc *grid, const float *vg, const mpm_particles *particles, float dt, uint32_t *status,
             hipStream_t stream)
 {

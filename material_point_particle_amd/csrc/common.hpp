@@ -169,6 +169,10 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
 hipError_t launch_grid_update(int dim, int n, int64_t *grid, float *vg, float dt, const float *gravity,
                               int sticky, const BinView *bins, hipStream_t s);
 hipError_t launch_grid_clear(int dim, int n, int64_t *grid, const BinView *bins, hipStream_t s);
+hipError_t launch_neohookean_affine(int dim, int n, int64_t np, const float *F, const float *C, const float *m,
+                                    const float *vol0, float dt, float mu, float lambda, float *Cout,
+                                    uint32_t *status, hipStream_t s);
+hipError_t launch_update_F(int dim, int64_t np, const float *C, float *F, float dt, hipStream_t s);
 hipError_t launch_g2p(int dim, int n, const float *vg, float *x, float *v, float *C, int64_t np, float dt,
                       uint32_t *status, hipStream_t s);
 

@@ -33,6 +33,42 @@ class DeviceParticles:
         return {k: getattr(self, k).cpu().numpy() for k in ("x", "v", "C", "m")}
 
 
+class ElasticParticles(DeviceParticles):
+    """Particles of a Neo-Hookean solid: the APIC state plus the deformation
+    gradient F[dim*dim][n] (component-major, like C), the initial volumes and
+    a buffer for the stressed affine matrix C' that binning and P2G read."""
+
+    def __init__(self, host: dict, F: np.ndarray, vol0: np.ndarray, device="cuda"):
+        super().__init__(host, device)
+        self.F = to_device(np.asarray(F, dtype=np.float32), device)
+        self.vol0 = to_device(np.asarray(vol0, dtype=np.float32), device)
+        self.C_aff = torch.empty_like(self.C)
+
+    def affine(self) -> "StressedView":
+        """The particles as P2G sees them after stress(): C replaced by C'."""
+        return StressedView(self)
+
+    def stress(self, tr: "Transfer", dt: float, mu: float, lam: float) -> None:
+        L.mpm_neohookean_affine(tr.desc, self.desc(), self.F, self.vol0, dt, mu, lam, self.C_aff, tr.status)
+
+    def update_F(self, tr: "Transfer", dt: float) -> None:
+        L.mpm_update_deformation(tr.desc, self.desc(), self.F, dt)
+
+    def host(self) -> dict:
+        h = super().host()
+        h["F"] = self.F.cpu().numpy()
+        return h
+
+
+class StressedView:
+    def __init__(self, parts: ElasticParticles):
+        self.p = parts
+        self.n = parts.n
+
+    def desc(self) -> L.mpm_particles:
+        return L.particles(self.n, self.p.x, self.p.v, self.p.C_aff, self.p.m)
+
+
 class Transfer:
     """One grid (dim, n, 2^frac_bits) with its binning workspace, int64
     accumulators, velocity grid and status counters."""

@@ -189,6 +189,23 @@ def dam_break_3d(seed: int, n_particles: int, n: int) -> np.ndarray:
     return g / n
 
 
+def jelly_block_3d(seed: int, n_particles: int, n: int) -> np.ndarray:
+    """An elastic cube resting just above the floor: 8 particles per cell on a
+    jittered 2x2x2 sub-lattice, the cube side s cells with 8 s^3 = n_particles
+    (n_particles must be 8 times a cube), centred in x and z, its bottom at
+    y = 3 cells.  Returns x [3][N] in the unit domain."""
+    s = round((n_particles / 8) ** (1.0 / 3.0))
+    assert 8 * s ** 3 == n_particles and s + 6 <= n
+    lo = [(n - s) // 2, 3, (n - s) // 2]
+    k = np.arange(n_particles, dtype=np.int64)
+    sub = [k % (2 * s), (k // (2 * s)) % (2 * s), k // (4 * s * s)]        # x fastest, then y, then z
+    g = np.empty((3, n_particles), dtype=np.float64)
+    for ax in range(3):
+        jit = (uniform01(seed, 60 + ax, n_particles) - 0.5) * 0.25      # +-1/8 cell
+        g[ax] = lo[ax] + (sub[ax] + 0.5) * 0.5 + jit
+    return g / n
+
+
 def gaussian_blobs_3d(seed: int, n_particles: int, n: int, n_blobs: int = 32,
                       sigma_cells: float = 4.0) -> np.ndarray:
     """n_blobs isotropic Gaussian blobs (sigma in cells) with seeded centres

@@ -77,6 +77,16 @@ WORKLOADS = {
         max_mass=1.0, max_speed=2.0, max_affine=1000.0, seed=_seed(5),
         extra={"dt": 1e-4, "gravity": (0.0, -9.8, 0.0), "sticky": 2, "substeps": 100,
                "check_every": 10}),
+    # Elastic (Neo-Hookean) cube thrown at the floor: the MLS-MPM stress term
+    # on top of the APIC transfer, 64^3 nodes.  rho = m / vol0 = 8 / dx^3; with
+    # mu = lambda = 1e9 the wave speed sqrt((lambda + 2 mu) / rho) ~ 38 keeps
+    # c dt / dx ~ 0.24.
+    "jelly_3d_64": Workload(
+        name="jelly_3d_64", kind="quadratic", dim=3, n=64, n_particles=8 * 16 ** 3, frac_bits=28,
+        placement="jelly", mass=1.0, v_sigma=0.05, c_sigma=0.0,
+        max_mass=1.0, max_speed=50.0, max_affine=1.0e4, seed=_seed(6),
+        extra={"dt": 1e-4, "gravity": (0.0, -9.8, 0.0), "sticky": 2, "substeps": 60, "check_every": 10,
+               "mu": 1.0e9, "lam": 1.0e9, "v0": (0.0, -3.0, 0.0)}),
 }
 
 
@@ -97,6 +107,8 @@ def build(w: Workload) -> dict:
         x = G.dam_break_3d(w.seed, w.n_particles, w.n)
     elif w.placement == "blobs":
         x = G.gaussian_blobs_3d(w.seed, w.n_particles, w.n)
+    elif w.placement == "jelly":
+        x = G.jelly_block_3d(w.seed, w.n_particles, w.n)
     elif w.placement == "uniform":
         x = 2.0 / w.n + G.uniform01(w.seed, 90, w.dim * w.n_particles).reshape(w.dim, -1) * ((w.n - 4.0) / w.n)
     else:
@@ -106,4 +118,9 @@ def build(w: Workload) -> dict:
     if w.dim == 3 and w.placement == "dam":
         dx = 1.0 / w.n
         out["vol"] = np.full(w.n_particles, dx ** 3 / 8.0, dtype=np.float32)
+    if w.placement == "jelly":
+        dx = 1.0 / w.n
+        out["vol"] = np.full(w.n_particles, dx ** 3 / 8.0, dtype=np.float32)
+        out["F"] = np.ascontiguousarray(np.tile(np.eye(3, dtype=np.float32).reshape(9, 1), (1, w.n_particles)))
+        out["v"] = np.ascontiguousarray(out["v"] + np.asarray(w.extra["v0"], np.float32)[:, None])
     return out

@@ -130,3 +130,12 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert lib.mpm_grid_clear(None, None, grid, None) == L.MPM_ERR_INVALID
     p3 = L.mpm_particles(10, 4096, 4096, None, 4096)
     assert lib.mpm_g2p(ct.byref(d), ct.c_void_p(4096), ct.byref(p3), 1e-4, status, None) == L.MPM_ERR_INVALID
+    p4 = L.mpm_particles(10, 4096, 4096, 4096, 4096)
+    ok = (ct.c_void_p(4096), ct.c_void_p(4096), 1e-4, 1e5, 1e5, ct.c_void_p(4096), status)
+    assert lib.mpm_neohookean_affine(ct.byref(d), ct.byref(p3), *ok, None) == L.MPM_ERR_INVALID     # no C
+    assert lib.mpm_neohookean_affine(ct.byref(d), ct.byref(p4), None, *ok[1:], None) == L.MPM_ERR_INVALID
+    assert lib.mpm_neohookean_affine(ct.byref(d), ct.byref(p4), *ok[:3], -1.0, *ok[4:], None) == L.MPM_ERR_INVALID
+    assert lib.mpm_neohookean_affine(ct.byref(d), ct.byref(p4), ct.c_void_p(4098), *ok[1:], None) == L.MPM_ERR_INVALID
+    assert lib.mpm_neohookean_affine(None, ct.byref(p4), *ok, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_update_deformation(ct.byref(d), ct.byref(p3), ct.c_void_p(4096), 1e-4, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_update_deformation(ct.byref(d), ct.byref(p4), None, 1e-4, None) == L.MPM_ERR_INVALID

@@ -1,0 +1,155 @@
+"""GPU parity of the MLS-MPM stress term (Neo-Hookean solid) and the
+deformation-gradient update against the oracle, through the C ABI.
+
+The stress is formed in float64 with the same operation order on both sides;
+the only operation whose last bit may differ between the host's and the
+device's math library is the float64 log, so C' may differ from the oracle by
+at most one float32 ulp, in a vanishing fraction of entries.  Everything else
+(the F update, and P2G, grid update and G2P given the same C') is bit-exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from mpm_inputs import WORKLOADS, build
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-test]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def mpm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import material_point_particle_amd as M
+    M.lib()
+    return M
+
+
+def ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    ia = a.astype(np.float32).view(np.int32).astype(np.int64)
+    ib = b.astype(np.float32).view(np.int32).astype(np.int64)
+    ia = np.where(ia < 0, -(ia & 0x7FFFFFFF), ia)
+    ib = np.where(ib < 0, -(ib & 0x7FFFFFFF), ib)
+    return np.abs(ia - ib)
+
+
+def assert_close_ulp(gpu, ref, what, max_frac=1e-4):
+    d = ulp_diff(gpu, ref)
+    assert d.max() <= 1, f"{what}: {d.max()} ulp apart"
+    assert np.count_nonzero(d) <= max(1, int(max_frac * d.size)), f"{what}: {np.count_nonzero(d)} entries 1 ulp apart"
+
+
+def random_solid(dim, np_, seed, inverted=0):
+    rng = np.random.default_rng(seed)
+    F = (np.eye(dim).reshape(dim * dim, 1) + 0.2 * rng.standard_normal((dim * dim, np_))).astype(np.float32)
+    if inverted:
+        F[0, :inverted] = -np.abs(F[0, :inverted]) - 2.0      # det < 0 for the first few (dominant -F00)
+        for q in range(1, dim):
+            F[q * dim + q, :inverted] = 1.0
+            F[q, :inverted] = 0.0
+            F[q * dim, :inverted] = 0.0
+    host = {"x": rng.uniform(0.2, 0.8, (dim, np_)).astype(np.float32),
+            "v": rng.standard_normal((dim, np_)).astype(np.float32),
+            "C": rng.standard_normal((dim * dim, np_)).astype(np.float32),
+            "m": rng.uniform(0.5, 2.0, np_).astype(np.float32)}
+    host["m"][-3:] = 0.0
+    vol0 = rng.uniform(0.5, 2.0, np_).astype(np.float32) * 1e-6
+    return host, F, vol0
+
+
+@pytest.mark.parametrize("dim", [2, 3])
+def test_neohookean_affine_matches_oracle(mpm, oracle_lib, dim):
+    from material_point_particle_amd.transfer import ElasticParticles, Transfer
+    np_ = 100_003
+    host, F, vol0 = random_solid(dim, np_, 21 + dim, inverted=17)
+    dt, mu, lam = 1e-4, 2.0e8, 3.0e8
+    n = 64
+    say("neohookean affine", dim, np_)
+    ref, ref_st = oracle_lib.neohookean_affine(dim, n, host, F, vol0, dt, mu, lam)
+    parts = ElasticParticles(host, F, vol0)
+    tr = Transfer(dim, n, 24, (2.0, 10.0, 1e6), np_)
+    parts.stress(tr, dt, mu, lam)
+    torch.cuda.synchronize()
+    got = parts.C_aff.cpu().numpy()
+    assert_close_ulp(got, ref, "C'")
+    assert tr.status.cpu().numpy().view(np.uint32).tolist() == ref_st.tolist()
+    assert ref_st[0] >= 17                      # the 17 built inverted, and any the random draw inverted
+    # inverted and massless particles keep C exactly
+    assert np.array_equal(got[:, :17], host["C"][:, :17]) and np.array_equal(got[:, -3:], host["C"][:, -3:])
+
+
+@pytest.mark.parametrize("dim", [2, 3])
+def test_update_F_bit_exact(mpm, oracle_lib, dim):
+    from material_point_particle_amd.transfer import ElasticParticles, Transfer
+    np_ = 65_537
+    host, F, vol0 = random_solid(dim, np_, 31 + dim)
+    ref = F.copy()
+    oracle_lib.update_F(dim, host["C"], ref, 1e-3)
+    parts = ElasticParticles(host, F, vol0)
+    tr = Transfer(dim, 32, 24, (2.0, 10.0, 10.0), np_)
+    say("update F", dim)
+    parts.update_F(tr, 1e-3)
+    torch.cuda.synchronize()
+    assert np.array_equal(parts.F.cpu().numpy(), ref)
+
+
+def test_elastic_substeps_match_oracle(mpm, oracle_lib):
+    """An elastic cube thrown at the floor (32,768 particles, 64^3 nodes): the
+    substep stress -> bin -> P2G (with C') -> restricted grid update -> G2P ->
+    F update on the GPU.  At every 10th substep the oracle recomputes that
+    substep from the GPU's state before it: C' within one ulp (float64 log);
+    given the GPU's C', the P2G grid, the particle state and F bit-exact."""
+    from material_point_particle_amd.transfer import ElasticParticles, Transfer
+    w = WORKLOADS["jelly_3d_64"]
+    ex = w.extra
+    host = build(w)
+    parts = ElasticParticles(host, host["F"], host["vol"])
+    rng = (w.max_mass, w.max_speed, w.max_affine)
+    tr = Transfer(w.dim, w.n, w.frac_bits, rng, parts.n)
+    checked = 0
+    for k in range(1, ex["substeps"] + 1):
+        check = k % ex["check_every"] == 0
+        if check:
+            torch.cuda.synchronize()
+            before = parts.host()
+        parts.stress(tr, ex["dt"], ex["mu"], ex["lam"])
+        tr.bin(parts.affine())
+        tr.p2g(parts.affine(), binned=True)
+        if check:
+            torch.cuda.synchronize()
+            c_aff = parts.C_aff.cpu().numpy()
+            grid = tr.grid.cpu().numpy()
+        tr.grid_update(ex["dt"], ex["gravity"], ex["sticky"], active=True)
+        tr.g2p(parts, ex["dt"])
+        parts.update_F(tr, ex["dt"])
+        if not check:
+            continue
+        torch.cuda.synchronize()
+        after = parts.host()
+        say("elastic substep", k)
+        ref_c, _ = oracle_lib.neohookean_affine(3, w.n, before, before["F"], host["vol"], ex["dt"], ex["mu"],
+                                                ex["lam"])
+        assert_close_ulp(c_aff, ref_c, f"C' at substep {k}")
+        st = {"x": before["x"].copy(), "v": before["v"].copy(), "C": c_aff.copy(), "m": before["m"].copy()}
+        g_ref, s_ref = oracle_lib.p2g_quadratic(3, w.n, w.frac_bits, st, rng)
+        assert np.array_equal(grid, g_ref), f"P2G grid at substep {k}"
+        assert s_ref.tolist() == [0, 0, 0, 0]
+        vg = oracle_lib.grid_update(3, w.n, g_ref, ex["dt"], ex["gravity"], ex["sticky"])
+        st["C"] = before["C"].copy()
+        oracle_lib.g2p(3, w.n, vg, st, ex["dt"])
+        F_ref = before["F"].copy()
+        oracle_lib.update_F(3, st["C"], F_ref, ex["dt"])
+        for key in ("x", "v", "C"):
+            assert np.array_equal(after[key], st[key]), f"{key} at substep {k}"
+        assert np.array_equal(after["F"], F_ref), f"F at substep {k}"
+        checked += 1
+    assert checked == ex["substeps"] // ex["check_every"]
+    # the cube has hit the floor and is deforming: some particles are compressed
+    J = np.linalg.det(parts.F.cpu().numpy().reshape(3, 3, -1).transpose(2, 0, 1))
+    assert J.min() < 0.999 and np.all(J > 0)
