@@ -136,6 +136,67 @@ def measure_substeps(args, torch, w, build, DeviceParticles, Transfer):
     }
 
 
+def measure_elastic(args, torch, w, build, Transfer):
+    """The elastic substep (MLS-MPM with the Neo-Hookean stress term) on the
+    8M-particle jelly cube at 256^3 nodes: stressed affine matrix, binning,
+    P2G, restricted grid update, G2P and the deformation-gradient update,
+    substep after substep on the evolving state, timed per stage with HIP
+    events.  Algorithmic bytes of the two elementwise passes: the stress reads
+    F, C, m, vol0 and writes C' (116 B per particle); the F update reads C, F
+    and writes F (108 B per particle)."""
+    from material_point_particle_amd.transfer import ElasticParticles
+    host = build(w)
+    ex = w.extra
+    parts = ElasticParticles(host, host["F"], host["vol"])
+    del host
+    tr = Transfer(w.dim, w.n, w.frac_bits, (w.max_mass, w.max_speed, w.max_affine), parts.n)
+    stream = torch.cuda.current_stream()
+
+    def substep(ev=None):
+        steps = (lambda: parts.stress(tr, ex["dt"], ex["mu"], ex["lam"]),
+                 lambda: tr.bin(parts.affine()),
+                 lambda: tr.p2g(parts.affine(), binned=True),
+                 lambda: tr.grid_update(ex["dt"], ex["gravity"], ex["sticky"], active=True),
+                 lambda: tr.g2p(parts, ex["dt"]),
+                 lambda: parts.update_F(tr, ex["dt"]))
+        for i, f in enumerate(steps):
+            if ev:
+                ev[i].record(stream)
+            f()
+        if ev:
+            ev[len(steps)].record(stream)
+
+    for _ in range(3):
+        substep()
+    torch.cuda.synchronize()
+    k = args.substeps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(k)]
+    for i in range(k):
+        substep(events[i])
+    torch.cuda.synchronize()
+    st = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(6)] for e in events]).mean(axis=0)
+    ms = float(st.sum())
+    names = ("stress", "bin", "p2g", "grid_update", "g2p", "update_F")
+    status = tr.status.cpu().numpy().view(np.uint32).tolist()
+    log(f"elastic substeps: {ms:.3f} ms (" + ", ".join(f"{n} {t:.3f}" for n, t in zip(names, st)) + ")")
+
+    def gbs(b, t):
+        return round(b / (t * 1e-3) / 1e9, 1)
+
+    s_bytes, f_bytes = parts.n * 116, parts.n * 108
+    return {
+        "workload": f"{w.name}: {parts.n} particles, Neo-Hookean cube (mu {ex['mu']:g}, lambda {ex['lam']:g}) "
+                    f"thrown at the floor, {w.n}^3 nodes, 2^{w.frac_bits}, dt {ex['dt']}",
+        "substeps": k, "ms_per_substep": round(ms, 4), "particles_per_s": round(parts.n / (ms * 1e-3), 1),
+        "stages_ms": {n: round(float(t), 4) for n, t in zip(names, st)},
+        "stress": {"bound": "hbm", "bytes": s_bytes, "achieved_gbs": gbs(s_bytes, st[0]),
+                   "frac": round(gbs(s_bytes, st[0]) / HBM_PEAK_GBS, 4)},
+        "update_F": {"bound": "hbm", "bytes": f_bytes, "achieved_gbs": gbs(f_bytes, st[5]),
+                     "frac": round(gbs(f_bytes, st[5]) / HBM_PEAK_GBS, 4)},
+        "status": status,
+    }
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +212,10 @@ def parse():
     ap.add_argument("--substeps", type=int, default=20, help="timed substeps of the full-substep measurement")
     ap.add_argument("--only-substep", action="store_true",
                     help="run only the full-substep measurement (for profiling it alone); prints its object")
+    ap.add_argument("--no-elastic", action="store_true",
+                    help="skip the elastic-substep measurement (Neo-Hookean stress term) on the jelly cube")
+    ap.add_argument("--only-elastic", action="store_true",
+                    help="run only the elastic-substep measurement; prints its object")
     return ap.parse_args()
 
 
@@ -171,6 +236,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     M.lib()
+    if args.only_elastic:
+        print(json.dumps({"elastic": measure_elastic(args, torch, WORKLOADS["jelly_3d_256"], build, Transfer)}),
+              flush=True)
+        return
     if args.only_substep:
         print(json.dumps({"substep": measure_substeps(args, torch, WORKLOADS["dam_3d_256"], build, DeviceParticles,
                                                       Transfer)}), flush=True)
@@ -284,6 +353,12 @@ def main():
         del copies, parts, tr
         torch.cuda.empty_cache()
         out["substep"] = measure_substeps(args, torch, WORKLOADS["dam_3d_256"], build, DeviceParticles, Transfer)
+        torch.cuda.empty_cache()
+    if not args.no_elastic:
+        if args.no_substep:
+            del copies, parts, tr
+            torch.cuda.empty_cache()
+        out["elastic"] = measure_elastic(args, torch, WORKLOADS["jelly_3d_256"], build, Transfer)
 
     if not args.no_cpu_baseline:
         import oracle

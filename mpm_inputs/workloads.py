@@ -87,6 +87,14 @@ WORKLOADS = {
         max_mass=1.0, max_speed=50.0, max_affine=1.0e4, seed=_seed(6),
         extra={"dt": 1e-4, "gravity": (0.0, -9.8, 0.0), "sticky": 2, "substeps": 60, "check_every": 10,
                "mu": 1.0e9, "lam": 1.0e9, "v0": (0.0, -3.0, 0.0)}),
+    # The same elastic cube at 256^3 nodes, side 100 cells (8M particles);
+    # mu = lambda = 4e9 keeps c dt / dx ~ 0.24 at rho = 8 / dx^3.
+    "jelly_3d_256": Workload(
+        name="jelly_3d_256", kind="quadratic", dim=3, n=256, n_particles=8 * 100 ** 3, frac_bits=28,
+        placement="jelly", mass=1.0, v_sigma=0.05, c_sigma=0.0,
+        max_mass=1.0, max_speed=50.0, max_affine=1.0e4, seed=_seed(7),
+        extra={"dt": 1e-4, "gravity": (0.0, -9.8, 0.0), "sticky": 2, "substeps": 60, "check_every": 10,
+               "mu": 4.0e9, "lam": 4.0e9, "v0": (0.0, -3.0, 0.0)}),
 }
 
 
