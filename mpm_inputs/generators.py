@@ -143,6 +143,20 @@ def integer_cloud(seed: int, n: int = 256, cells: int = 8, frac_bits: int = 16,
     }
 
 
+def integer_cloud_quadratic(seed: int, n_particles: int, n: int, dim: int, max_mass: int, max_speed: int,
+                            max_affine: int) -> dict:
+    """Integer particles for the integer-split quadratic transfer: positions in
+    units of 2^-16 cell uniform over [2, n-2) cells per axis, masses 1..max_mass,
+    velocity components in [-max_speed, max_speed] and affine entries (velocity
+    per cell) in [-max_affine, max_affine]."""
+    X = np.stack([uniform_int(seed, 70 + e, n_particles, 2 << 16, ((n - 2) << 16) - 1) for e in range(dim)])
+    m = uniform_int(seed, 75, n_particles, 1, max_mass)
+    v = np.stack([uniform_int(seed, 76 + e, n_particles, -max_speed, max_speed) for e in range(dim)])
+    C = np.stack([uniform_int(seed, 80 + q, n_particles, -max_affine, max_affine) for q in range(dim * dim)])
+    return {"X": np.ascontiguousarray(X.astype(np.int32)), "m": np.ascontiguousarray(m.astype(np.int64)),
+            "v": np.ascontiguousarray(v.astype(np.int64)), "C": np.ascontiguousarray(C.astype(np.int64))}
+
+
 # ---------------------------------------------------------------------------
 # Particle placements for the quadratic-stencil workloads.  Positions are in
 # the unit domain with n nodes per axis, node i at i/n; "g" below is a

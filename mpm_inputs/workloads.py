@@ -19,7 +19,7 @@ from . import generators as G
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "cic_split" or "quadratic"
+    kind: str                 # "cic_split", "quadratic" or "isplit"
     dim: int
     n: int                    # nodes per axis (quadratic); cells per axis (cic_split)
     n_particles: int
@@ -95,6 +95,14 @@ WORKLOADS = {
         max_mass=1.0, max_speed=50.0, max_affine=1.0e4, seed=_seed(7),
         extra={"dt": 1e-4, "gravity": (0.0, -9.8, 0.0), "sticky": 2, "substeps": 60, "check_every": 10,
                "mu": 4.0e9, "lam": 4.0e9, "v0": (0.0, -3.0, 0.0)}),
+    # Integer-split quadratic APIC transfer (exact conservation): integer
+    # positions (2^-16 cell), masses, velocities and affine entries.
+    "isplit_2d_64": Workload(
+        name="isplit_2d_64", kind="isplit", dim=2, n=64, n_particles=3500, frac_bits=0,
+        max_mass=1000, max_speed=1000, max_affine=1000, seed=_seed(8)),
+    "isplit_3d_128": Workload(
+        name="isplit_3d_128", kind="isplit", dim=3, n=128, n_particles=1 << 20, frac_bits=0,
+        max_mass=1000, max_speed=1000, max_affine=1000, seed=_seed(9)),
 }
 
 
@@ -106,6 +114,9 @@ def scaled(w: Workload, n_particles: int, n: int | None = None) -> Workload:
 
 def build(w: Workload) -> dict:
     """Materialise the workload's arrays (numpy, host memory)."""
+    if w.kind == "isplit":
+        return G.integer_cloud_quadratic(w.seed, w.n_particles, w.n, w.dim, int(w.max_mass), int(w.max_speed),
+                                         int(w.max_affine))
     if w.kind == "cic_split":
         return G.integer_cloud(w.seed, n=w.n_particles, cells=w.n, frac_bits=w.frac_bits,
                                max_mass=int(w.max_mass), max_speed=int(w.max_speed))

@@ -61,6 +61,9 @@ def lib():
         L.oracle_g2p.restype = None
         L.oracle_g2p.argtypes = [ct.c_int, ct.c_int, F32P, ct.c_int64, F32P, F32P, F32P, ct.c_float, U32P]
         L.oracle_bin.restype = ct.c_int64
+        L.oracle_p2g_isplit.argtypes = [ct.c_int, ct.c_int, ct.c_int64, I32P, I64P, I64P, I64P, I64P, I64P, U32P]
+        L.oracle_isplit_bounds_ok.restype = ct.c_int
+        L.oracle_isplit_bounds_ok.argtypes = [ct.c_int, ct.c_int64, ct.c_int64, ct.c_int64, ct.c_int64]
         L.oracle_neohookean_affine.argtypes = [ct.c_int, ct.c_int, ct.c_int64, F32P, F32P, F32P, F32P, ct.c_float,
                                                ct.c_float, ct.c_float, F32P, U32P]
         L.oracle_update_F.argtypes = [ct.c_int, ct.c_int64, F32P, F32P, ct.c_float]
@@ -148,6 +151,27 @@ def g2p(dim: int, n: int, vg: np.ndarray, particles: dict, dt: float):
     lib().oracle_g2p(dim, n, _p(vg, F32P), x.shape[1], _p(x, F32P), _p(v, F32P), _p(C, F32P), ct.c_float(dt),
                      _p(status, U32P))
     return status
+
+
+def p2g_isplit(dim: int, n: int, particles: dict, order=None, grid=None):
+    """Integer-split quadratic APIC transfer; particles: X int32 [dim][np] (2^-16 cell), m int64 [np],
+    v int64 [dim][np], C int64 [dim*dim][np].  Returns (grid int64 [1+dim][n]*dim, status[4])."""
+    X = np.ascontiguousarray(particles["X"], dtype=np.int32)
+    m = np.ascontiguousarray(particles["m"], dtype=np.int64)
+    v = np.ascontiguousarray(particles["v"], dtype=np.int64)
+    C = np.ascontiguousarray(particles["C"], dtype=np.int64)
+    np_ = m.shape[0]
+    if grid is None:
+        grid = np.zeros((1 + dim,) + (n,) * dim, dtype=np.int64)
+    status = np.zeros(4, dtype=np.uint32)
+    o, op = _order_ptr(order)
+    lib().oracle_p2g_isplit(dim, n, np_, _p(X, I32P), _p(m, I64P), _p(v, I64P), _p(C, I64P), op, _p(grid, I64P),
+                            _p(status, U32P))
+    return grid, status
+
+
+def isplit_bounds_ok(dim: int, np_: int, max_mass: int, max_speed: int, max_affine: int) -> bool:
+    return bool(lib().oracle_isplit_bounds_ok(dim, np_, max_mass, max_speed, max_affine))
 
 
 def neohookean_affine(dim: int, n: int, particles: dict, F: np.ndarray, vol0: np.ndarray, dt: float, mu: float,

@@ -129,6 +129,150 @@ void oracle_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const i
 }
 
 /* ------------------------------------------------------------------------ */
+/* Integer-split quadratic APIC transfer.                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The integer page's split carried to the quadratic B-spline and the affine
+ * term (its "what is not claimed" section: both would be more splits of the
+ * same kind; reading 18).  Positions are integers in units of 2^-16 cell; along
+ * one axis the base node is floor(g - 1/2) and F = X - 2^16 base is the
+ * distance from it, in [2^15, 3 2^15).  The quadratic B-spline weights are
+ * then exact dyadic rationals over 2^33:
+ *   W0 = (3 2^15 - F)^2,  W2 = (F - 2^15)^2,  W1 = 2^33 - W0 - W2.
+ * A quantity q is split over the three nodes by rounding the two outer shares
+ * (nearest, ties even) and giving the middle node the rest, so the shares sum
+ * to q exactly.  The affine term needs the first-moment weights
+ * u_o = w_o (o - f), which sum to zero: U0 = -W0 F and U2 = W2 (2^17 - F) over
+ * 2^49, the outer shares rounded, the middle share minus their sum, so the
+ * shares sum to exactly zero.
+ */
+
+/* t / 2^k rounded to nearest, ties to the even neighbour (128-bit t). */
+static int64_t rhe_shift128(__int128 t, int k)
+{
+    __int128 fl = t >> k;                       /* arithmetic shift: floor */
+    __int128 r = t - fl * ((__int128)1 << k);   /* 0 <= r < 2^k */
+    __int128 half = (__int128)1 << (k - 1);
+    if (r > half || (r == half && (fl & 1) != 0))
+        fl += 1;
+    return (int64_t)fl;
+}
+
+/* kind 0: the weights w; kind 1: the first-moment weights u. */
+static void split_1d(int64_t q, int64_t F, int kind, int64_t s[3])
+{
+    const __int128 W0 = (__int128)(3 * 32768 - F) * (3 * 32768 - F);
+    const __int128 W2 = (__int128)(F - 32768) * (F - 32768);
+    if (kind == 0) {
+        s[0] = rhe_shift128((__int128)q * W0, 33);
+        s[2] = rhe_shift128((__int128)q * W2, 33);
+        s[1] = q - s[0] - s[2];
+    } else {
+        s[0] = rhe_shift128((__int128)q * (-W0 * F), 49);
+        s[2] = rhe_shift128((__int128)q * (W2 * (131072 - F)), 49);
+        s[1] = -s[0] - s[2];
+    }
+}
+
+/* Tensor split of q over the 3^dim stencil: along x, then each x share along
+ * y, then each of those along z; kinds[e] picks w or u on axis e.  out is
+ * indexed [a][b][c] as out[(a * 3 + b) * 3 + c] (2D: c = 0). */
+static void split_tensor(int dim, int64_t q, const int64_t F[3], const int kinds[3], int64_t out[27])
+{
+    int64_t sx[3];
+    split_1d(q, F[0], kinds[0], sx);
+    for (int a = 0; a < 3; ++a) {
+        int64_t sy[3];
+        split_1d(sx[a], F[1], kinds[1], sy);
+        for (int b = 0; b < 3; ++b) {
+            if (dim == 3) {
+                int64_t sz[3];
+                split_1d(sy[b], F[2], kinds[2], sz);
+                for (int c = 0; c < 3; ++c)
+                    out[(a * 3 + b) * 3 + c] = sz[c];
+            } else {
+                out[(a * 3 + b) * 3] = sy[b];
+            }
+        }
+    }
+}
+
+/*
+ * Scatter np particles (in `order`, or index order) onto the int64 grid
+ * [1+dim][n]^dim (x fastest).  X[dim][np]: positions in 2^-16 cell; m[np],
+ * v[dim][np], C[dim*dim][np]: integers, C_de in velocity per cell, so that a
+ * particle's exact contribution to node i is m w_i (v + C (i - g)) with the
+ * offset in cells.  Mass: the tensor split of m.  Momentum d: the tensor split
+ * of m v_d, plus for every axis e the tensor split of m C_de with the
+ * first-moment weights on axis e (and the weights on the others).  Node totals
+ * equal particle totals exactly: sum M = sum m, sum P_d = sum m v_d.
+ * Particles whose stencil leaves the grid are skipped and counted in
+ * status[0].
+ */
+void oracle_p2g_isplit(int dim, int n, int64_t np_, const int32_t *X, const int64_t *m, const int64_t *v,
+                       const int64_t *C, const int64_t *order, int64_t *grid, uint32_t *status)
+{
+    const int64_t nodes = dim == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    const int nc = dim == 3 ? 3 : 1;
+    for (int64_t k = 0; k < np_; ++k) {
+        const int64_t p = order ? order[k] : k;
+        int64_t base[3] = { 0, 0, 0 }, F[3] = { 65536, 65536, 65536 };
+        int ok = 1;
+        for (int e = 0; e < dim; ++e) {
+            const int64_t x = X[e * np_ + p];
+            int64_t t = x - 32768, b = t / 65536;
+            if (t % 65536 != 0 && t < 0)
+                b -= 1;                                 /* floor */
+            base[e] = b;
+            F[e] = x - b * 65536;
+            ok &= b >= 0 && b <= n - 3;
+        }
+        if (!ok) {
+            status[ST_DOMAIN] += 1;
+            continue;
+        }
+        int64_t share[1 + 3][27];
+        memset(share, 0, sizeof(share));
+        const int w_only[3] = { 0, 0, 0 };
+        split_tensor(dim, m[p], F, w_only, share[0]);
+        for (int d = 0; d < dim; ++d) {
+            int64_t part[27];
+            split_tensor(dim, m[p] * v[d * np_ + p], F, w_only, part);
+            for (int i = 0; i < 27; ++i)
+                share[1 + d][i] += part[i];
+            for (int e = 0; e < dim; ++e) {
+                int kinds[3] = { 0, 0, 0 };
+                kinds[e] = 1;
+                split_tensor(dim, m[p] * C[(int64_t)(d * dim + e) * np_ + p], F, kinds, part);
+                for (int i = 0; i < 27; ++i)
+                    share[1 + d][i] += part[i];
+            }
+        }
+        for (int a = 0; a < 3; ++a)
+            for (int b = 0; b < 3; ++b)
+                for (int c = 0; c < nc; ++c) {
+                    const int64_t node = dim == 3
+                        ? ((base[2] + c) * n + (base[1] + b)) * n + (base[0] + a)
+                        : (base[1] + b) * n + (base[0] + a);
+                    for (int ch = 0; ch <= dim; ++ch)
+                        grid[ch * nodes + node] += share[ch][(a * 3 + b) * 3 + c];
+                }
+    }
+}
+
+/* Bounds line of the integer-split transfer: every split product fits the
+ * 128-bit intermediate by construction; the node sums fit int64 when
+ * np * max_mass * (max_speed + dim * max_affine * 3/2 + 1) < 2^62 (each share's
+ * magnitude is at most its quantity's, plus the rounding).  1: may run. */
+int oracle_isplit_bounds_ok(int dim, int64_t np_, int64_t max_mass, int64_t max_speed, int64_t max_affine)
+{
+    long double b = (long double)np_ * (long double)max_mass *
+                    ((long double)max_speed + (long double)dim * (long double)max_affine * 1.5L + 1.0L);
+    return b < 4611686018427387904.0L;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Quadratic B-spline APIC transfer.                                         */
 /* ------------------------------------------------------------------------ */
 
