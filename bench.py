@@ -197,6 +197,52 @@ def measure_elastic(args, torch, w, build, Transfer):
     }
 
 
+def measure_isplit(args, torch, w, build):
+    """The integer-split quadratic APIC transfer (exact conservation) on
+    1,048,576 integer particles at 128^3 nodes: the mpm_p2g_isplit kernel alone,
+    timed per launch with HIP events, accumulating into one grid.  Per particle
+    it reads 116 B (X int32 x3, m, v x3, C x9 int64) and makes 27 x 4 int64
+    atomic adds (shares of 0 are skipped)."""
+    import material_point_particle_amd as M
+    host = build(w)
+    dev = torch.device("cuda", 0)
+    X = torch.from_numpy(host["X"]).to(dev)
+    m = torch.from_numpy(host["m"]).to(dev)
+    v = torch.from_numpy(host["v"]).to(dev)
+    C = torch.from_numpy(host["C"]).to(dev)
+    grid = torch.zeros((1 + w.dim,) + (w.n,) * w.dim, dtype=torch.int64, device=dev)
+    status = torch.zeros(4, dtype=torch.int32, device=dev)
+    rng = (int(w.max_mass), int(w.max_speed), int(w.max_affine))
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        M.mpm_p2g_isplit(w.dim, w.n, X, m, v, C, None, *rng, grid, status)     # on the current stream
+
+    for _ in range(2):
+        launch()
+    torch.cuda.synchronize()
+    k = max(5, args.substeps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+    ev[0].record(stream)
+    for i in range(k):
+        launch()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(k)]))
+    np_ = w.n_particles
+    atomics = np_ * 27 * (1 + w.dim)
+    rd = np_ * 116
+    log(f"isplit: {ms:.3f} ms per launch, {np_ / (ms * 1e-3) / 1e9:.2f} G particles/s")
+    return {
+        "workload": f"{w.name}: {np_} integer particles uniform over {w.n}^3 nodes, |m|,|v|,|C| <= "
+                    f"{rng[0]}, 2^-16 cell positions",
+        "launches": k, "ms_per_launch": round(ms, 4), "particles_per_s": round(np_ / (ms * 1e-3), 1),
+        "atomics_per_launch": atomics, "atomics_per_s": round(atomics / (ms * 1e-3), 1),
+        "read_bytes_per_launch": rd, "read_gbs": round(rd / (ms * 1e-3) / 1e9, 1),
+        "status": status.cpu().numpy().view(np.uint32).tolist(),
+    }
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,6 +262,10 @@ def parse():
                     help="skip the elastic-substep measurement (Neo-Hookean stress term) on the jelly cube")
     ap.add_argument("--only-elastic", action="store_true",
                     help="run only the elastic-substep measurement; prints its object")
+    ap.add_argument("--no-isplit", action="store_true",
+                    help="skip the integer-split quadratic transfer measurement")
+    ap.add_argument("--only-isplit", action="store_true",
+                    help="run only the integer-split quadratic transfer measurement; prints its object")
     return ap.parse_args()
 
 
@@ -236,6 +286,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     M.lib()
+    if args.only_isplit:
+        print(json.dumps({"isplit": measure_isplit(args, torch, WORKLOADS["isplit_3d_128"], build)}), flush=True)
+        return
     if args.only_elastic:
         print(json.dumps({"elastic": measure_elastic(args, torch, WORKLOADS["jelly_3d_256"], build, Transfer)}),
               flush=True)
@@ -359,6 +412,12 @@ def main():
             del copies, parts, tr
             torch.cuda.empty_cache()
         out["elastic"] = measure_elastic(args, torch, WORKLOADS["jelly_3d_256"], build, Transfer)
+        torch.cuda.empty_cache()
+    if not args.no_isplit:
+        if args.no_substep and args.no_elastic:
+            del copies, parts, tr
+            torch.cuda.empty_cache()
+        out["isplit"] = measure_isplit(args, torch, WORKLOADS["isplit_3d_128"], build)
 
     if not args.no_cpu_baseline:
         import oracle

@@ -208,6 +208,38 @@ int mpm_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32
                       int32_t cells, int64_t max_mass, int64_t max_speed, int64_t *grid_out, uint32_t *status,
                       hipStream_t stream);
 
+/* Integer-split quadratic APIC transfer ("particle to grid transfer in
+ * checked integer arithmetic", sections "integers do not care about order"
+ * and "what is not claimed", which names quadratic weights and the affine
+ * term as further splits of the kind the page gives for cloud-in-cell).
+ * Positions X[dim][np] are int32 in units of 1/65536 of a cell (node i at
+ * i * 65536); m[np], v[dim][np] and C[dim*dim][np] (C_de = C[d*dim+e],
+ * velocity per cell) are int64.  With base = floor(x/65536 - 1/2) and
+ * F = x - 65536 base per axis, the quadratic B-spline weights are
+ * w_0 = (98304 - F)^2 / 2^33, w_2 = (F - 32768)^2 / 2^33, w_1 = 1 - w_0 - w_2
+ * and the first moments u_o = w_o (o - F/65536) are u_0 = -(98304 - F)^2 F /
+ * 2^49, u_2 = (F - 32768)^2 (131072 - F) / 2^49, u_1 = -u_0 - u_2.  A quantity
+ * q is split along an axis into round(q c_0), q minus both outer shares (w)
+ * or minus their sum (u), round(q c_2), rounding to nearest with ties to
+ * even from the exact 128-bit product; the 3^dim shares are the split along
+ * x, then y, then z.  Channel 0 gets the split of m; channel 1+d the split of
+ * m v_d plus, for each axis e, the split of m C_de with the first moments on
+ * axis e.  Node totals equal particle totals exactly (sum M = sum m,
+ * sum P_d = sum m v_d), and the grid is identical for every order.
+ * grid: device int64[1+dim][n]^dim (x fastest), accumulated into.  order
+ * (device uint32[np], may be NULL) gives the visiting order.  Particles with
+ * a node outside [0, n) are skipped and counted in status[0]; particles with
+ * |m| > max_mass, |v_d| > max_speed or |C_de| > max_affine are skipped and
+ * counted in status[1]; order entries >= np in status[3].  The bounds line
+ * np * max_mass * (max_speed + dim * max_affine * 3/2 + 1) < 2^62 is checked
+ * on the host (MPM_ERR_OVERFLOW).  All pointers are device memory owned by
+ * the caller; the call is asynchronous on `stream`.
+ * Errors: MPM_ERR_INVALID (dim not 2 or 3, n outside [3, 32767], negative
+ * maxima, misaligned pointers), MPM_ERR_OVERFLOW, MPM_ERR_HIP. */
+int mpm_p2g_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
+                   const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed, int64_t max_affine,
+                   int64_t *grid_out, uint32_t *status, hipStream_t stream);
+
 /* Grid update with consume-and-zero ("Implementation -- GPU Optimization &
  * Reference Codebases", section 1 four-phase step; section 2.1 and rule 4
  * of section 5: each accumulator has one reader, which zeroes it; rule 1:

@@ -48,8 +48,8 @@ class mpm_ws_layout(ct.Structure):
 
 
 EXPORTS = ("mpm_version", "mpm_strerror", "mpm_check_bounds", "mpm_workspace_bytes", "mpm_workspace_layout",
-           "mpm_bin_particles", "mpm_p2g", "mpm_p2g_cic_split", "mpm_grid_update", "mpm_grid_clear", "mpm_g2p",
-           "mpm_neohookean_affine", "mpm_update_deformation")
+           "mpm_bin_particles", "mpm_p2g", "mpm_p2g_cic_split", "mpm_p2g_isplit", "mpm_grid_update", "mpm_grid_clear",
+           "mpm_g2p", "mpm_neohookean_affine", "mpm_update_deformation")
 
 _lib = None
 
@@ -82,6 +82,10 @@ def lib() -> ct.CDLL:
         L.mpm_p2g_cic_split.restype = ct.c_int
         L.mpm_p2g_cic_split.argtypes = [ct.c_int64, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int32,
                                         ct.c_int64, ct.c_int64, ct.c_void_p, ct.c_void_p, ct.c_void_p]
+        L.mpm_p2g_isplit.restype = ct.c_int
+        L.mpm_p2g_isplit.argtypes = [ct.c_int32, ct.c_int32, ct.c_int64, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                     ct.c_void_p, ct.c_void_p, ct.c_int64, ct.c_int64, ct.c_int64, ct.c_void_p,
+                                     ct.c_void_p, ct.c_void_p]
         L.mpm_grid_update.restype = ct.c_int
         L.mpm_grid_update.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_float,
                                       P(ct.c_float), ct.c_int32, ct.c_void_p]
@@ -178,6 +182,12 @@ def mpm_p2g(desc, parts: mpm_particles, rng: mpm_ranges, bins, grid, status, str
 def mpm_p2g_cic_split(X, m, vel, order, cells: int, max_mass: int, max_speed: int, grid, status, stream=None) -> None:
     _check(lib().mpm_p2g_cic_split(m.numel(), _ptr(X), _ptr(m), _ptr(vel), _ptr(order), cells, max_mass, max_speed,
                                    _ptr(grid), _ptr(status), _stream(stream)), "mpm_p2g_cic_split")
+
+
+def mpm_p2g_isplit(dim: int, n: int, X, m, v, C, order, max_mass: int, max_speed: int, max_affine: int, grid,
+                   status, stream=None) -> None:
+    _check(lib().mpm_p2g_isplit(dim, n, m.numel(), _ptr(X), _ptr(m), _ptr(v), _ptr(C), _ptr(order), max_mass,
+                                max_speed, max_affine, _ptr(grid), _ptr(status), _stream(stream)), "mpm_p2g_isplit")
 
 
 def mpm_grid_update(desc, bins, grid, vg, dt: float, gravity, sticky: int, stream=None) -> None:

@@ -293,6 +293,32 @@ int mpm_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32
     return hip_status(launch_p2g_cic_split(n, X, m, vel, order, cells, grid_out, status, stream));
 }
 
+int mpm_p2g_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
+                   const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed, int64_t max_affine,
+                   int64_t *grid_out, uint32_t *status, hipStream_t stream)
+{
+    if ((dim != 2 && dim != 3) || n < 3 || n > 32767 || np < 0 || np > (int64_t)0xFFFFFFF0 || max_mass < 0 ||
+        max_speed < 0 || max_affine < 0)
+        return MPM_ERR_INVALID;
+    if (!aligned(grid_out, 8) || !aligned(status, 4))
+        return MPM_ERR_INVALID;
+    if (np > 0 && (!aligned(X, 4) || !aligned(m, 8) || !aligned(v, 8) || !aligned(C, 8) ||
+                   (order && !aligned(order, 4))))
+        return MPM_ERR_INVALID;
+    // bounds line: every node total, and every product m v_d and m C_de, fits
+    // int64 when np * max_mass * (max_speed + dim * max_affine * 3/2 + 1) < 2^62
+    // (first-moment shares of one quantity sum to at most half of it in
+    // magnitude, doubled by the middle share, plus one unit of rounding each)
+    const long double line = (long double)np * (long double)max_mass *
+                             ((long double)max_speed + (long double)dim * (long double)max_affine * 1.5L + 1.0L);
+    const long double one = (long double)max_mass *
+                            ((long double)max_speed + (long double)dim * (long double)max_affine * 1.5L + 1.0L);
+    if (line >= 4611686018427387904.0L || one >= 4611686018427387904.0L)
+        return MPM_ERR_OVERFLOW;
+    return hip_status(launch_p2g_isplit(dim, n, np, X, m, v, C, order, max_mass, max_speed, max_affine, grid_out,
+                                        status, stream));
+}
+
 int mpm_grid_update(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, float *vg, float dt,
                     const float *gravity, int32_t sticky, hipStream_t stream)
 {

@@ -120,6 +120,19 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
                                  None) == L.MPM_ERR_INVALID
     assert lib.mpm_p2g_cic_split(1 << 30, 4096, 4096, 4096, None, 8, 1 << 20, 1 << 20, grid, status,
                                  None) == L.MPM_ERR_OVERFLOW
+    A = ct.c_void_p(4096)
+    assert lib.mpm_p2g_isplit(3, 64, 10, None, A, A, A, None, 1000, 1000, 1000, grid, status, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_p2g_isplit(3, 64, 10, A, ct.c_void_p(4100), A, A, None, 1000, 1000, 1000, grid, status,
+                              None) == L.MPM_ERR_INVALID
+    assert lib.mpm_p2g_isplit(4, 64, 10, A, A, A, A, None, 1000, 1000, 1000, grid, status, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_p2g_isplit(3, 2, 10, A, A, A, A, None, 1000, 1000, 1000, grid, status, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_p2g_isplit(3, 64, 10, A, A, A, A, None, -1, 1000, 1000, grid, status, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_p2g_isplit(3, 64, 10, A, A, A, A, ct.c_void_p(4098), 1000, 1000, 1000, grid, status,
+                              None) == L.MPM_ERR_INVALID
+    assert lib.mpm_p2g_isplit(3, 64, 1 << 30, A, A, A, A, None, 1 << 20, 1 << 20, 1 << 20, grid, status,
+                              None) == L.MPM_ERR_OVERFLOW
+    assert lib.mpm_p2g_isplit(3, 64, 1, A, A, A, A, None, 1 << 40, 1 << 20, 1 << 20, grid, status,
+                              None) == L.MPM_ERR_OVERFLOW
     g = (ct.c_float * 3)(0, -9.8, 0)
     assert lib.mpm_grid_update(ct.byref(d), None, grid, ct.c_void_p(4096), 1e-4, g, 100, None) == L.MPM_ERR_INVALID
     assert lib.mpm_grid_update(ct.byref(d), None, grid, ct.c_void_p(4096), 1e-4, None, 2, None) == L.MPM_ERR_INVALID
