@@ -199,10 +199,11 @@ def measure_elastic(args, torch, w, build, Transfer):
 
 def measure_isplit(args, torch, w, build):
     """The integer-split quadratic APIC transfer (exact conservation) on
-    1,048,576 integer particles at 128^3 nodes: the mpm_p2g_isplit kernel alone,
-    timed per launch with HIP events, accumulating into one grid.  Per particle
-    it reads 116 B (X int32 x3, m, v x3, C x9 int64) and makes 27 x 4 int64
-    atomic adds (shares of 0 are skipped)."""
+    1,048,576 integer particles at 128^3 nodes, one mpm_p2g_isplit call per
+    launch accumulating into one grid, timed with HIP events: the tiled path
+    (counting sort into 8^3-cell tiles, on-chip node blocks) and the direct
+    path (27 x 4 int64 global atomics per particle).  Per particle a call
+    reads 116 B (X int32 x3, m, v x3, C x9 int64)."""
     import material_point_particle_amd as M
     host = build(w)
     dev = torch.device("cuda", 0)
@@ -212,33 +213,38 @@ def measure_isplit(args, torch, w, build):
     C = torch.from_numpy(host["C"]).to(dev)
     grid = torch.zeros((1 + w.dim,) + (w.n,) * w.dim, dtype=torch.int64, device=dev)
     status = torch.zeros(4, dtype=torch.int32, device=dev)
+    ws = torch.empty(M.mpm_isplit_workspace_bytes(w.dim, w.n, w.n_particles), dtype=torch.uint8, device=dev)
     rng = (int(w.max_mass), int(w.max_speed), int(w.max_affine))
     stream = torch.cuda.current_stream()
-
-    def launch():
-        M.mpm_p2g_isplit(w.dim, w.n, X, m, v, C, None, *rng, grid, status)     # on the current stream
-
-    for _ in range(2):
-        launch()
-    torch.cuda.synchronize()
-    k = max(5, args.substeps)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
-    ev[0].record(stream)
-    for i in range(k):
-        launch()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(k)]))
     np_ = w.n_particles
+
+    def timed(workspace, k):
+        def launch():
+            M.mpm_p2g_isplit(w.dim, w.n, X, m, v, C, None, *rng, grid, status, workspace=workspace)
+        for _ in range(2):
+            launch()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+        ev[0].record(stream)
+        for i in range(k):
+            launch()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(k)]))
+
+    k = max(5, args.substeps)
+    ms_t = timed(ws, k)
+    ms_d = timed(None, 5)
     atomics = np_ * 27 * (1 + w.dim)
     rd = np_ * 116
-    log(f"isplit: {ms:.3f} ms per launch, {np_ / (ms * 1e-3) / 1e9:.2f} G particles/s")
+    log(f"isplit: tiled {ms_t:.3f} ms, direct {ms_d:.3f} ms per call ({np_ / (ms_t * 1e-3) / 1e9:.2f} G particles/s)")
     return {
         "workload": f"{w.name}: {np_} integer particles uniform over {w.n}^3 nodes, |m|,|v|,|C| <= "
                     f"{rng[0]}, 2^-16 cell positions",
-        "launches": k, "ms_per_launch": round(ms, 4), "particles_per_s": round(np_ / (ms * 1e-3), 1),
-        "atomics_per_launch": atomics, "atomics_per_s": round(atomics / (ms * 1e-3), 1),
-        "read_bytes_per_launch": rd, "read_gbs": round(rd / (ms * 1e-3) / 1e9, 1),
+        "calls": k, "ms_per_call": round(ms_t, 4), "particles_per_s": round(np_ / (ms_t * 1e-3), 1),
+        "read_bytes_per_call": rd, "read_gbs": round(rd / (ms_t * 1e-3) / 1e9, 1),
+        "direct": {"ms_per_call": round(ms_d, 4), "particles_per_s": round(np_ / (ms_d * 1e-3), 1),
+                   "atomics_per_call": atomics, "atomics_per_s": round(atomics / (ms_d * 1e-3), 1)},
         "status": status.cpu().numpy().view(np.uint32).tolist(),
     }
 

@@ -232,13 +232,28 @@ int mpm_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32
  * |m| > max_mass, |v_d| > max_speed or |C_de| > max_affine are skipped and
  * counted in status[1]; order entries >= np in status[3].  The bounds line
  * np * max_mass * (max_speed + dim * max_affine * 3/2 + 1) < 2^62 is checked
- * on the host (MPM_ERR_OVERFLOW).  All pointers are device memory owned by
- * the caller; the call is asynchronous on `stream`.
+ * on the host (MPM_ERR_OVERFLOW).
+ * workspace == NULL: one thread per particle adds each share with a 64-bit
+ * global atomic.  workspace != NULL (device, 256-byte aligned, at least
+ * mpm_isplit_workspace_bytes): particle indices are counting-sorted into
+ * 8^dim-cell tiles and each slice of up to 2048 particles of a tile
+ * accumulates its 10^dim-node block on chip before one atomic per non-zero
+ * node and channel.  Both give the same grid.  The workspace is scratch,
+ * overwritten by each call; calls sharing one workspace must not overlap.
+ * All pointers are device memory owned by the caller; the call is
+ * asynchronous on `stream`.
  * Errors: MPM_ERR_INVALID (dim not 2 or 3, n outside [3, 32767], negative
- * maxima, misaligned pointers), MPM_ERR_OVERFLOW, MPM_ERR_HIP. */
+ * maxima, misaligned pointers), MPM_ERR_WORKSPACE, MPM_ERR_OVERFLOW,
+ * MPM_ERR_HIP. */
 int mpm_p2g_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
                    const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed, int64_t max_affine,
-                   int64_t *grid_out, uint32_t *status, hipStream_t stream);
+                   void *workspace, size_t workspace_bytes, int64_t *grid_out, uint32_t *status, hipStream_t stream);
+
+/* Bytes of the workspace mpm_p2g_isplit's tiled path needs for np particles
+ * on n^dim nodes (tile counts and starts, each visited particle's rank and
+ * the tile-ordered particle indices).  Host only.
+ * Errors: MPM_ERR_INVALID. */
+int mpm_isplit_workspace_bytes(int32_t dim, int32_t n, int64_t np, size_t *bytes);
 
 /* Grid update with consume-and-zero ("Implementation -- GPU Optimization &
  * Reference Codebases", section 1 four-phase step; section 2.1 and rule 4

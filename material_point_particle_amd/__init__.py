@@ -7,8 +7,8 @@ include/mpm.h); this package holds the HIP sources (csrc/), the build step
 """
 from ._lib import (  # noqa: F401
     EXPORTS, LIB_PATH, MpmError, grid_desc, lib, mpm_bin_particles, mpm_check_bounds, mpm_g2p, mpm_grid_update,
-    mpm_p2g, mpm_p2g_cic_split, mpm_p2g_isplit, mpm_strerror, mpm_version, mpm_workspace_bytes,
-    mpm_workspace_layout, particles, ranges,
+    mpm_isplit_workspace_bytes, mpm_p2g, mpm_p2g_cic_split, mpm_p2g_isplit, mpm_strerror, mpm_version,
+    mpm_workspace_bytes, mpm_workspace_layout, particles, ranges,
 )
 
 __version__ = "0.1.0"

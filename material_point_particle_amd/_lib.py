@@ -48,8 +48,8 @@ class mpm_ws_layout(ct.Structure):
 
 
 EXPORTS = ("mpm_version", "mpm_strerror", "mpm_check_bounds", "mpm_workspace_bytes", "mpm_workspace_layout",
-           "mpm_bin_particles", "mpm_p2g", "mpm_p2g_cic_split", "mpm_p2g_isplit", "mpm_grid_update", "mpm_grid_clear",
-           "mpm_g2p", "mpm_neohookean_affine", "mpm_update_deformation")
+           "mpm_bin_particles", "mpm_p2g", "mpm_p2g_cic_split", "mpm_p2g_isplit", "mpm_isplit_workspace_bytes",
+           "mpm_grid_update", "mpm_grid_clear", "mpm_g2p", "mpm_neohookean_affine", "mpm_update_deformation")
 
 _lib = None
 
@@ -85,7 +85,9 @@ def lib() -> ct.CDLL:
         L.mpm_p2g_isplit.restype = ct.c_int
         L.mpm_p2g_isplit.argtypes = [ct.c_int32, ct.c_int32, ct.c_int64, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                      ct.c_void_p, ct.c_void_p, ct.c_int64, ct.c_int64, ct.c_int64, ct.c_void_p,
-                                     ct.c_void_p, ct.c_void_p]
+                                     ct.c_size_t, ct.c_void_p, ct.c_void_p, ct.c_void_p]
+        L.mpm_isplit_workspace_bytes.restype = ct.c_int
+        L.mpm_isplit_workspace_bytes.argtypes = [ct.c_int32, ct.c_int32, ct.c_int64, P(ct.c_size_t)]
         L.mpm_grid_update.restype = ct.c_int
         L.mpm_grid_update.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_float,
                                       P(ct.c_float), ct.c_int32, ct.c_void_p]
@@ -184,10 +186,18 @@ def mpm_p2g_cic_split(X, m, vel, order, cells: int, max_mass: int, max_speed: in
                                    _ptr(grid), _ptr(status), _stream(stream)), "mpm_p2g_cic_split")
 
 
+def mpm_isplit_workspace_bytes(dim: int, n: int, np_: int) -> int:
+    b = ct.c_size_t(0)
+    _check(lib().mpm_isplit_workspace_bytes(dim, n, np_, ct.byref(b)), "mpm_isplit_workspace_bytes")
+    return b.value
+
+
 def mpm_p2g_isplit(dim: int, n: int, X, m, v, C, order, max_mass: int, max_speed: int, max_affine: int, grid,
-                   status, stream=None) -> None:
+                   status, workspace=None, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mpm_p2g_isplit(dim, n, m.numel(), _ptr(X), _ptr(m), _ptr(v), _ptr(C), _ptr(order), max_mass,
-                                max_speed, max_affine, _ptr(grid), _ptr(status), _stream(stream)), "mpm_p2g_isplit")
+                                max_speed, max_affine, _ptr(workspace), ws_bytes, _ptr(grid), _ptr(status),
+                                _stream(stream)), "mpm_p2g_isplit")
 
 
 def mpm_grid_update(desc, bins, grid, vg, dt: float, gravity, sticky: int, stream=None) -> None:

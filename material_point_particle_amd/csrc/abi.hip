@@ -293,9 +293,17 @@ int mpm_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32
     return hip_status(launch_p2g_cic_split(n, X, m, vel, order, cells, grid_out, status, stream));
 }
 
+int mpm_isplit_workspace_bytes(int32_t dim, int32_t n, int64_t np, size_t *bytes)
+{
+    if ((dim != 2 && dim != 3) || n < 3 || n > 32767 || np < 0 || np > (int64_t)0xFFFFFFF0 || !bytes)
+        return MPM_ERR_INVALID;
+    *bytes = isplit_layout(dim, n, np).total;
+    return MPM_OK;
+}
+
 int mpm_p2g_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
                    const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed, int64_t max_affine,
-                   int64_t *grid_out, uint32_t *status, hipStream_t stream)
+                   void *workspace, size_t workspace_bytes, int64_t *grid_out, uint32_t *status, hipStream_t stream)
 {
     if ((dim != 2 && dim != 3) || n < 3 || n > 32767 || np < 0 || np > (int64_t)0xFFFFFFF0 || max_mass < 0 ||
         max_speed < 0 || max_affine < 0)
@@ -315,6 +323,14 @@ int mpm_p2g_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const i
                             ((long double)max_speed + (long double)dim * (long double)max_affine * 1.5L + 1.0L);
     if (line >= 4611686018427387904.0L || one >= 4611686018427387904.0L)
         return MPM_ERR_OVERFLOW;
+    if (workspace) {
+        if (!aligned(workspace, 256))
+            return MPM_ERR_INVALID;
+        if (workspace_bytes < isplit_layout(dim, n, np).total)
+            return MPM_ERR_WORKSPACE;
+        return hip_status(launch_p2g_isplit_tiled(dim, n, np, X, m, v, C, order, max_mass, max_speed, max_affine,
+                                                  workspace, grid_out, status, stream));
+    }
     return hip_status(launch_p2g_isplit(dim, n, np, X, m, v, C, order, max_mass, max_speed, max_affine, grid_out,
                                         status, stream));
 }

@@ -167,6 +167,14 @@ hipError_t launch_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, c
 hipError_t launch_p2g_isplit(int dim, int n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
                              const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed,
                              int64_t max_affine, int64_t *grid, uint32_t *status, hipStream_t s);
+struct IsplitLayout {      // byte offsets into the integer-split workspace
+    size_t count, start, partial, meta, rank, perm, total;
+    int64_t tiles_x, tiles, scan_blocks;
+};
+IsplitLayout isplit_layout(int dim, int n, int64_t np);
+hipError_t launch_p2g_isplit_tiled(int dim, int n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
+                                   const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed,
+                                   int64_t max_affine, void *ws, int64_t *grid, uint32_t *status, hipStream_t s);
 hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView &b, uint32_t *status,
                       hipStream_t s);
 hipError_t launch_grid_update(int dim, int n, int64_t *grid, float *vg, float dt, const float *gravity,

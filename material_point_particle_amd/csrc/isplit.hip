@@ -25,9 +25,16 @@
 // of m; channel 1 + d is the split of m v_d plus, for every axis e, the split
 // of m C_de with the first moments on axis e and the weights on the others.
 //
-// One thread per particle; its 3^dim shares of one channel are formed in
-// registers and added with one 64-bit global atomic each.  Integer atomics
-// commute, so the grid is bit-identical in every order and every launch.
+// Two paths, both exact: integer additions commute, so the grid is
+// bit-identical in every order, every launch and every path.
+//  - direct: one thread per particle; its 3^dim shares of one channel are
+//    formed in registers and added with one 64-bit global atomic each
+//    (27 x 4 random atomics per particle in 3D);
+//  - tiled: a counting sort of particle indices into 8^dim-cell tiles, then
+//    one workgroup per slice of a tile accumulates the tile's 10^dim-node
+//    block on chip with 64-bit LDS atomics and flushes it with one global
+//    atomic per non-zero node and channel, consecutive lanes on consecutive
+//    x nodes.
 #include "common.hpp"
 
 namespace mpmk {
@@ -124,6 +131,72 @@ __device__ __forceinline__ void flush(int64_t *g, const int64_t (&acc)[DIM == 3 
             }
 }
 
+// Stencil of one particle: base node and split coefficients per axis;
+// false when a stencil node leaves [0, n).
+template <int DIM>
+__device__ __forceinline__ bool stencil(const int32_t *__restrict__ X, int64_t np, int64_t p, int n,
+                                        int64_t (&base)[DIM], AxisCoef (&ax)[DIM])
+{
+    bool inside = true;
+#pragma unroll
+    for (int e = 0; e < DIM; ++e) {
+        const int64_t x = X[(int64_t)e * np + p];
+        base[e] = (x - 32768) >> 16;                     // floor((x - 2^15) / 2^16)
+        inside &= base[e] >= 0 && base[e] <= n - 3;
+        ax[e] = axis_coef(x - (base[e] << 16));
+    }
+    return inside;
+}
+
+// Loads m, v, C of particle p; false when one leaves the declared ranges.
+template <int DIM>
+__device__ __forceinline__ bool load_quantities(const int64_t *__restrict__ m, const int64_t *__restrict__ v,
+                                                const int64_t *__restrict__ C, int64_t np, int64_t p,
+                                                int64_t max_mass, int64_t max_speed, int64_t max_affine,
+                                                int64_t &mp, int64_t (&vp)[DIM], int64_t (&cp)[DIM][DIM])
+{
+    mp = m[p];
+    bool in_range = mp >= -max_mass && mp <= max_mass;
+#pragma unroll
+    for (int d = 0; d < DIM; ++d) {
+        vp[d] = v[(int64_t)d * np + p];
+        in_range &= vp[d] >= -max_speed && vp[d] <= max_speed;
+#pragma unroll
+        for (int e = 0; e < DIM; ++e) {
+            cp[d][e] = C[(int64_t)(d * DIM + e) * np + p];
+            in_range &= cp[d][e] >= -max_affine && cp[d][e] <= max_affine;
+        }
+    }
+    return in_range;
+}
+
+// All channels of one particle: sink(channel, acc) receives the 3^dim shares
+// of each channel in turn.
+template <int DIM, class Sink>
+__device__ __forceinline__ void particle_shares(const AxisCoef (&ax)[DIM], int64_t mp, const int64_t (&vp)[DIM],
+                                                const int64_t (&cp)[DIM][DIM], Sink &&sink)
+{
+    constexpr int K = DIM == 3 ? 27 : 9;
+    int64_t acc[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+        acc[i] = 0;
+    tensor_add<DIM, 0, 0, 0>(mp, ax, acc);
+    sink(0, acc);
+#pragma unroll 1
+    for (int d = 0; d < DIM; ++d) {
+#pragma unroll
+        for (int i = 0; i < K; ++i)
+            acc[i] = 0;
+        tensor_add<DIM, 0, 0, 0>(mp * vp[d], ax, acc);
+        tensor_add<DIM, 1, 0, 0>(mp * cp[d][0], ax, acc);
+        tensor_add<DIM, 0, 1, 0>(mp * cp[d][1], ax, acc);
+        if constexpr (DIM == 3)
+            tensor_add<DIM, 0, 0, 1>(mp * cp[d][2], ax, acc);
+        sink(1 + d, acc);
+    }
+}
+
 template <int DIM>
 __global__ void __launch_bounds__(256) isplit_kernel(int64_t np, int n, const int32_t *__restrict__ X,
                                                      const int64_t *__restrict__ m, const int64_t *__restrict__ v,
@@ -132,7 +205,6 @@ __global__ void __launch_bounds__(256) isplit_kernel(int64_t np, int n, const in
                                                      int64_t max_speed, int64_t max_affine,
                                                      int64_t *__restrict__ grid, uint32_t *__restrict__ status)
 {
-    constexpr int K = DIM == 3 ? 27 : 9;
     const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
     for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < np; k += (int64_t)gridDim.x * blockDim.x) {
         const int64_t p = order ? (int64_t)order[k] : k;
@@ -142,54 +214,374 @@ __global__ void __launch_bounds__(256) isplit_kernel(int64_t np, int n, const in
         }
         int64_t base[DIM];
         AxisCoef ax[DIM];
-        bool inside = true;
-#pragma unroll
-        for (int e = 0; e < DIM; ++e) {
-            const int64_t x = X[(int64_t)e * np + p];
-            base[e] = (x - 32768) >> 16;                 // floor((x - 2^15) / 2^16)
-            inside &= base[e] >= 0 && base[e] <= n - 3;
-            ax[e] = axis_coef(x - (base[e] << 16));
-        }
-        const int64_t mp = m[p];
-        bool in_range = mp >= -max_mass && mp <= max_mass;
-        int64_t vp[DIM], cp[DIM][DIM];
-#pragma unroll
-        for (int d = 0; d < DIM; ++d) {
-            vp[d] = v[(int64_t)d * np + p];
-            in_range &= vp[d] >= -max_speed && vp[d] <= max_speed;
-#pragma unroll
-            for (int e = 0; e < DIM; ++e) {
-                cp[d][e] = C[(int64_t)(d * DIM + e) * np + p];
-                in_range &= cp[d][e] >= -max_affine && cp[d][e] <= max_affine;
-            }
-        }
+        const bool inside = stencil<DIM>(X, np, p, n, base, ax);
+        int64_t mp, vp[DIM], cp[DIM][DIM];
+        const bool in_range = load_quantities<DIM>(m, v, C, np, p, max_mass, max_speed, max_affine, mp, vp, cp);
         wave_count(!inside, &status[0]);
         wave_count(inside && !in_range, &status[1]);
         if (!inside || !in_range)
             continue;
-
-        int64_t acc[K];
-#pragma unroll
-        for (int i = 0; i < K; ++i)
-            acc[i] = 0;
-        tensor_add<DIM, 0, 0, 0>(mp, ax, acc);
-        flush<DIM>(grid, acc, base, n);
-#pragma unroll 1
-        for (int d = 0; d < DIM; ++d) {
-#pragma unroll
-            for (int i = 0; i < K; ++i)
-                acc[i] = 0;
-            tensor_add<DIM, 0, 0, 0>(mp * vp[d], ax, acc);
-            tensor_add<DIM, 1, 0, 0>(mp * cp[d][0], ax, acc);
-            tensor_add<DIM, 0, 1, 0>(mp * cp[d][1], ax, acc);
-            if constexpr (DIM == 3)
-                tensor_add<DIM, 0, 0, 1>(mp * cp[d][2], ax, acc);
-            flush<DIM>(grid + (1 + d) * nodes, acc, base, n);
-        }
+        particle_shares<DIM>(ax, mp, vp, cp, [&](int ch, const int64_t(&acc)[DIM == 3 ? 27 : 9]) {
+            flush<DIM>(grid + ch * nodes, acc, base, n);
+        });
     }
 }
 
+// ---------------------------------------------------------------------------
+// Tiled path.
+// ---------------------------------------------------------------------------
+constexpr int kIsTile = 8;                 // cells per tile edge
+constexpr int kIsBlock = kIsTile + 2;      // nodes per block edge: bases t0..t0+7 reach t0..t0+9
+constexpr int kIsChunk = 2048;             // particles per work item
+constexpr int kIsThreads = 256;
+constexpr int kScanPer = 4;                // scan entries per thread
+constexpr int kScanBlock = kIsThreads * kScanPer;
+
+template <int DIM>
+__device__ __forceinline__ int64_t tile_of(const int64_t (&base)[DIM], int64_t tx)
+{
+    int64_t t = 0;
+#pragma unroll
+    for (int e = DIM - 1; e >= 0; --e)
+        t = t * tx + base[e] / kIsTile;
+    return t;
+}
+
+__global__ void __launch_bounds__(256) is_zero_kernel(uint32_t *__restrict__ a, int64_t count)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+        a[i] = 0u;
+}
+
+// Tile of every visited particle; its rank among the tile's particles comes
+// from the returning atomic on the tile count.  Particles whose stencil
+// leaves the grid get rank ~0 and are counted; the range check is the
+// accumulating kernel's.
+template <int DIM>
+__global__ void __launch_bounds__(256) is_count_kernel(int64_t np, int n, int64_t tx, const int32_t *__restrict__ X,
+                                                       const uint32_t *__restrict__ order,
+                                                       uint32_t *__restrict__ count, uint32_t *__restrict__ rank,
+                                                       uint32_t *__restrict__ status)
+{
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < np; k += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p = order ? (int64_t)order[k] : k;
+        uint32_t r = ~0u;
+        bool inside = false;
+        if (p >= np) {
+            atomicAdd(&status[3], 1u);
+            inside = true;               // not a stencil fault
+        } else {
+            int64_t base[DIM];
+            AxisCoef ax[DIM];
+            inside = stencil<DIM>(X, np, p, n, base, ax);
+            if (inside)
+                r = atomicAdd(&count[tile_of<DIM>(base, tx)], 1u);
+        }
+        wave_count(!inside, &status[0]);
+        rank[k] = r;
+    }
+}
+
+// Packed scan entry of tile t: work items in the high word, particles in the
+// low word (totals stay below 2^32, so neither half carries into the other).
+__device__ __forceinline__ uint64_t packed_entry(const uint32_t *__restrict__ count, int64_t t, int64_t tiles)
+{
+    if (t >= tiles)
+        return 0ull;
+    const uint64_t c = count[t];
+    return (((c + kIsChunk - 1) / kIsChunk) << 32) | c;
+}
+
+// Exclusive scan of 256 threads' values; returns the block total in *total.
+__device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t x, uint64_t *lds_waves, uint64_t *total)
+{
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    uint64_t inc = x;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint64_t o = __shfl_up(inc, d, kWave);
+        if (lane >= d)
+            inc += o;
+    }
+    if (lane == kWave - 1)
+        lds_waves[wave] = inc;
+    __syncthreads();
+    uint64_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kIsThreads / kWave; ++w) {
+        const uint64_t s = lds_waves[w];
+        before += w < wave ? s : 0ull;
+        all += s;
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - x;
+}
+
+__global__ void __launch_bounds__(kIsThreads) is_scan_partial_kernel(const uint32_t *__restrict__ count, int64_t tiles,
+                                                                     uint64_t *__restrict__ partial)
+{
+    __shared__ uint64_t lw[kIsThreads / kWave];
+    const int64_t t0 = (int64_t)blockIdx.x * kScanBlock + threadIdx.x * kScanPer;
+    uint64_t s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i)
+        s += packed_entry(count, t0 + i, tiles);
+    uint64_t total;
+    block_exclusive_scan(s, lw, &total);
+    if (threadIdx.x == 0)
+        partial[blockIdx.x] = total;
+}
+
+// One workgroup: exclusive scan of the block totals in place; meta[0] = the
+// grand total (items << 32 | particles).
+__global__ void __launch_bounds__(kIsThreads) is_scan_top_kernel(uint64_t *__restrict__ partial, int64_t blocks,
+                                                                 uint64_t *__restrict__ meta)
+{
+    __shared__ uint64_t lw[kIsThreads / kWave];
+    uint64_t carry = 0;
+    for (int64_t b0 = 0; b0 < blocks; b0 += kIsThreads) {
+        const int64_t b = b0 + threadIdx.x;
+        const uint64_t x = b < blocks ? partial[b] : 0ull;
+        uint64_t total;
+        const uint64_t ex = block_exclusive_scan(x, lw, &total);
+        if (b < blocks)
+            partial[b] = carry + ex;
+        carry += total;
+    }
+    if (threadIdx.x == 0)
+        meta[0] = carry;
+}
+
+__global__ void __launch_bounds__(kIsThreads) is_scan_final_kernel(const uint32_t *__restrict__ count, int64_t tiles,
+                                                                   const uint64_t *__restrict__ partial,
+                                                                   uint64_t *__restrict__ start)
+{
+    __shared__ uint64_t lw[kIsThreads / kWave];
+    const int64_t t0 = (int64_t)blockIdx.x * kScanBlock + threadIdx.x * kScanPer;
+    uint64_t e[kScanPer], s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+        e[i] = packed_entry(count, t0 + i, tiles);
+        s += e[i];
+    }
+    uint64_t total;
+    uint64_t run = partial[blockIdx.x] + block_exclusive_scan(s, lw, &total);
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+        if (t0 + i < tiles)
+            start[t0 + i] = run;
+        run += e[i];
+    }
+}
+
+template <int DIM>
+__global__ void __launch_bounds__(256) is_scatter_kernel(int64_t np, int n, int64_t tx, const int32_t *__restrict__ X,
+                                                         const uint32_t *__restrict__ order,
+                                                         const uint32_t *__restrict__ rank,
+                                                         const uint64_t *__restrict__ start,
+                                                         uint32_t *__restrict__ perm)
+{
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < np; k += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t r = rank[k];
+        if (r == ~0u)
+            continue;
+        const int64_t p = order ? (int64_t)order[k] : k;
+        int64_t base[DIM];
+        AxisCoef ax[DIM];
+        stencil<DIM>(X, np, p, n, base, ax);
+        perm[(start[tile_of<DIM>(base, tx)] & 0xFFFFFFFFull) + r] = (uint32_t)p;
+    }
+}
+
+// Work item i -> the tile whose items contain it: the last tile whose first
+// item is <= i (an empty tile shares its first item with the next tile, so
+// the last such tile is never empty).
+__device__ __forceinline__ int64_t item_tile(const uint64_t *__restrict__ start, int64_t tiles, uint64_t i)
+{
+    int64_t lo = 0, hi = tiles;          // first tile with first item > i lies in (lo, hi]
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) / 2;
+        if ((start[mid] >> 32) <= i)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+template <int DIM>
+__global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n, int64_t tx, int64_t tiles,
+                                                              const int32_t *__restrict__ X,
+                                                              const int64_t *__restrict__ m,
+                                                              const int64_t *__restrict__ v,
+                                                              const int64_t *__restrict__ C,
+                                                              const uint32_t *__restrict__ count,
+                                                              const uint64_t *__restrict__ start,
+                                                              const uint32_t *__restrict__ perm,
+                                                              const uint64_t *__restrict__ meta, int64_t max_mass,
+                                                              int64_t max_speed, int64_t max_affine,
+                                                              int64_t *__restrict__ grid,
+                                                              uint32_t *__restrict__ status)
+{
+    constexpr int B = kIsBlock;
+    constexpr int plane = DIM == 3 ? B * B * B : B * B;
+    constexpr int entries = (1 + DIM) * plane;
+    __shared__ unsigned long long block[entries];
+    const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    const uint64_t items = meta[0] >> 32;
+    for (uint64_t i = blockIdx.x; i < items; i += gridDim.x) {
+        const int64_t t = item_tile(start, tiles, i);
+        const uint64_t s = start[t];
+        const int64_t lo = (int64_t)(s & 0xFFFFFFFFull) + (int64_t)(i - (s >> 32)) * kIsChunk;
+        const int64_t end_t = (int64_t)(s & 0xFFFFFFFFull) + count[t];
+        const int64_t hi = lo + kIsChunk < end_t ? lo + kIsChunk : end_t;
+        int64_t origin[DIM];
+        {
+            int64_t r = t;
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                origin[e] = (r % tx) * kIsTile;
+                r /= tx;
+            }
+        }
+        for (int e = threadIdx.x; e < entries; e += kIsThreads)
+            block[e] = 0ull;
+        __syncthreads();
+        for (int64_t j = lo + threadIdx.x; j < hi; j += kIsThreads) {
+            const int64_t p = perm[j];
+            int64_t base[DIM];
+            AxisCoef ax[DIM];
+            stencil<DIM>(X, np, p, n, base, ax);
+            int64_t mp, vp[DIM], cp[DIM][DIM];
+            const bool in_range = load_quantities<DIM>(m, v, C, np, p, max_mass, max_speed, max_affine, mp, vp, cp);
+            wave_count(!in_range, &status[1]);
+            if (!in_range)
+                continue;
+            int lb[DIM];
+#pragma unroll
+            for (int e = 0; e < DIM; ++e)
+                lb[e] = (int)(base[e] - origin[e]);
+            particle_shares<DIM>(ax, mp, vp, cp, [&](int ch, const int64_t(&acc)[DIM == 3 ? 27 : 9]) {
+#pragma unroll
+                for (int a = 0; a < 3; ++a)
+#pragma unroll
+                    for (int b = 0; b < 3; ++b)
+#pragma unroll
+                        for (int c = 0; c < (DIM == 3 ? 3 : 1); ++c) {
+                            int idx;
+                            int64_t sh;
+                            if constexpr (DIM == 3) {
+                                idx = ((ch * B + lb[2] + c) * B + lb[1] + b) * B + lb[0] + a;
+                                sh = acc[(a * 3 + b) * 3 + c];
+                            } else {
+                                idx = (ch * B + lb[1] + b) * B + lb[0] + a;
+                                sh = acc[a * 3 + b];
+                            }
+                            if (sh != 0)
+                                atomicAdd(&block[idx], (unsigned long long)sh);
+                        }
+            });
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < entries; e += kIsThreads) {
+            const unsigned long long val = block[e];
+            if (val == 0ull)
+                continue;
+            const int ch = e / plane;
+            int r = e - ch * plane;
+            const int lx = r % B;
+            r /= B;
+            int64_t node;
+            bool ok;
+            if constexpr (DIM == 3) {
+                const int ly = r % B, lz = r / B;
+                const int64_t x = origin[0] + lx, y = origin[1] + ly, z = origin[2] + lz;
+                ok = x < n && y < n && z < n;
+                node = (z * n + y) * n + x;
+            } else {
+                const int64_t x = origin[0] + lx, y = origin[1] + r;
+                ok = x < n && y < n;
+                node = y * n + x;
+            }
+            if (ok)
+                atomicAdd(reinterpret_cast<unsigned long long *>(&grid[ch * nodes + node]), val);
+        }
+        __syncthreads();
+    }
+}
+
+int64_t is_blocks(int64_t work, int64_t cap_per_cu)
+{
+    const int64_t want = (work + 255) / 256, cap = (int64_t)device_cu_count() * cap_per_cu;
+    return want < 1 ? 1 : (want > cap ? cap : want);
+}
+
 }  // namespace
+
+IsplitLayout isplit_layout(int dim, int n, int64_t np)
+{
+    IsplitLayout l{};
+    l.tiles_x = (n - 2 + kIsTile - 1) / kIsTile;           // bases 0..n-3
+    l.tiles = dim == 3 ? l.tiles_x * l.tiles_x * l.tiles_x : l.tiles_x * l.tiles_x;
+    l.scan_blocks = (l.tiles + kScanBlock - 1) / kScanBlock;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return at;
+    };
+    l.count = take(sizeof(uint32_t) * (size_t)l.tiles);
+    l.start = take(sizeof(uint64_t) * (size_t)l.tiles);
+    l.partial = take(sizeof(uint64_t) * (size_t)l.scan_blocks);
+    l.meta = take(sizeof(uint64_t) * 2);
+    l.rank = take(sizeof(uint32_t) * (size_t)(np > 0 ? np : 1));
+    l.perm = take(sizeof(uint32_t) * (size_t)(np > 0 ? np : 1));
+    l.total = off;
+    return l;
+}
+
+hipError_t launch_p2g_isplit_tiled(int dim, int n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
+                                   const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed,
+                                   int64_t max_affine, void *ws, int64_t *grid, uint32_t *status, hipStream_t s)
+{
+    if (np == 0)
+        return hipSuccess;
+    const IsplitLayout l = isplit_layout(dim, n, np);
+    char *w = static_cast<char *>(ws);
+    uint32_t *count = reinterpret_cast<uint32_t *>(w + l.count);
+    uint64_t *start = reinterpret_cast<uint64_t *>(w + l.start);
+    uint64_t *partial = reinterpret_cast<uint64_t *>(w + l.partial);
+    uint64_t *meta = reinterpret_cast<uint64_t *>(w + l.meta);
+    uint32_t *rank = reinterpret_cast<uint32_t *>(w + l.rank);
+    uint32_t *perm = reinterpret_cast<uint32_t *>(w + l.perm);
+    const dim3 blk(kIsThreads);
+    hipLaunchKernelGGL(is_zero_kernel, dim3((unsigned)is_blocks(l.tiles, 16)), blk, 0, s, count, l.tiles);
+    const unsigned pb = (unsigned)is_blocks(np, 32);
+    if (dim == 3)
+        hipLaunchKernelGGL(is_count_kernel<3>, dim3(pb), blk, 0, s, np, n, l.tiles_x, X, order, count, rank, status);
+    else
+        hipLaunchKernelGGL(is_count_kernel<2>, dim3(pb), blk, 0, s, np, n, l.tiles_x, X, order, count, rank, status);
+    hipLaunchKernelGGL(is_scan_partial_kernel, dim3((unsigned)l.scan_blocks), blk, 0, s, count, l.tiles, partial);
+    hipLaunchKernelGGL(is_scan_top_kernel, dim3(1), blk, 0, s, partial, l.scan_blocks, meta);
+    hipLaunchKernelGGL(is_scan_final_kernel, dim3((unsigned)l.scan_blocks), blk, 0, s, count, l.tiles, partial,
+                       start);
+    if (dim == 3)
+        hipLaunchKernelGGL(is_scatter_kernel<3>, dim3(pb), blk, 0, s, np, n, l.tiles_x, X, order, rank, start, perm);
+    else
+        hipLaunchKernelGGL(is_scatter_kernel<2>, dim3(pb), blk, 0, s, np, n, l.tiles_x, X, order, rank, start, perm);
+    // items <= tiles + np / kIsChunk; persistent workgroups stride over them
+    const int64_t max_items = l.tiles + np / kIsChunk + 1;
+    const int64_t cap = (int64_t)device_cu_count() * 4;
+    const unsigned tb = (unsigned)(max_items < cap ? max_items : cap);
+    if (dim == 3)
+        hipLaunchKernelGGL(is_tiled_kernel<3>, dim3(tb), blk, 0, s, np, n, l.tiles_x, l.tiles, X, m, v, C, count,
+                           start, perm, meta, max_mass, max_speed, max_affine, grid, status);
+    else
+        hipLaunchKernelGGL(is_tiled_kernel<2>, dim3(tb), blk, 0, s, np, n, l.tiles_x, l.tiles, X, m, v, C, count,
+                           start, perm, meta, max_mass, max_speed, max_affine, grid, status);
+    return hipGetLastError();
+}
 
 hipError_t launch_p2g_isplit(int dim, int n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
                              const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed,

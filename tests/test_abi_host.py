@@ -85,6 +85,20 @@ def test_workspace_layout_is_disjoint_and_aligned():
         assert spans[-1][0] + spans[-1][1] <= lay.total_bytes
 
 
+def test_isplit_workspace_size():
+    # tile counts and starts (8^dim-cell tiles over the n - 2 base nodes per
+    # axis), plus a rank and an index per visited particle, in 256-byte sections
+    def r(b):
+        return (b + 255) // 256 * 256
+    for dim, n, N in [(3, 128, 1 << 20), (2, 64, 3500), (3, 10, 1), (2, 2048, 0)]:
+        t = ((n - 2 + 7) // 8) ** dim
+        blocks = (t + 1023) // 1024
+        want = r(4 * t) + r(8 * t) + r(8 * blocks) + r(16) + 2 * r(4 * max(N, 1))
+        assert M.mpm_isplit_workspace_bytes(dim, n, N) == want
+    with pytest.raises(M.MpmError):
+        M.mpm_isplit_workspace_bytes(3, 2, 10)
+
+
 def test_tile_arrays_sit_at_offsets_independent_of_the_particle_count():
     # mpm_grid_update finds tile_count and tile_active in a workspace without
     # knowing the particle count it was sized for
@@ -121,18 +135,21 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert lib.mpm_p2g_cic_split(1 << 30, 4096, 4096, 4096, None, 8, 1 << 20, 1 << 20, grid, status,
                                  None) == L.MPM_ERR_OVERFLOW
     A = ct.c_void_p(4096)
-    assert lib.mpm_p2g_isplit(3, 64, 10, None, A, A, A, None, 1000, 1000, 1000, grid, status, None) == L.MPM_ERR_INVALID
-    assert lib.mpm_p2g_isplit(3, 64, 10, A, ct.c_void_p(4100), A, A, None, 1000, 1000, 1000, grid, status,
-                              None) == L.MPM_ERR_INVALID
-    assert lib.mpm_p2g_isplit(4, 64, 10, A, A, A, A, None, 1000, 1000, 1000, grid, status, None) == L.MPM_ERR_INVALID
-    assert lib.mpm_p2g_isplit(3, 2, 10, A, A, A, A, None, 1000, 1000, 1000, grid, status, None) == L.MPM_ERR_INVALID
-    assert lib.mpm_p2g_isplit(3, 64, 10, A, A, A, A, None, -1, 1000, 1000, grid, status, None) == L.MPM_ERR_INVALID
-    assert lib.mpm_p2g_isplit(3, 64, 10, A, A, A, A, ct.c_void_p(4098), 1000, 1000, 1000, grid, status,
-                              None) == L.MPM_ERR_INVALID
-    assert lib.mpm_p2g_isplit(3, 64, 1 << 30, A, A, A, A, None, 1 << 20, 1 << 20, 1 << 20, grid, status,
-                              None) == L.MPM_ERR_OVERFLOW
-    assert lib.mpm_p2g_isplit(3, 64, 1, A, A, A, A, None, 1 << 40, 1 << 20, 1 << 20, grid, status,
-                              None) == L.MPM_ERR_OVERFLOW
+    W = (ct.c_void_p(1 << 20), 1 << 30)
+
+    def isplit(dim, n, np_, X, m, v, C, order, mm, ms, ma, ws=(None, 0)):
+        return lib.mpm_p2g_isplit(dim, n, np_, X, m, v, C, order, mm, ms, ma, *ws, grid, status, None)
+    assert isplit(3, 64, 10, None, A, A, A, None, 1000, 1000, 1000) == L.MPM_ERR_INVALID
+    assert isplit(3, 64, 10, A, ct.c_void_p(4100), A, A, None, 1000, 1000, 1000) == L.MPM_ERR_INVALID
+    assert isplit(4, 64, 10, A, A, A, A, None, 1000, 1000, 1000) == L.MPM_ERR_INVALID
+    assert isplit(3, 2, 10, A, A, A, A, None, 1000, 1000, 1000) == L.MPM_ERR_INVALID
+    assert isplit(3, 64, 10, A, A, A, A, None, -1, 1000, 1000) == L.MPM_ERR_INVALID
+    assert isplit(3, 64, 10, A, A, A, A, ct.c_void_p(4098), 1000, 1000, 1000) == L.MPM_ERR_INVALID
+    assert isplit(3, 64, 1 << 30, A, A, A, A, None, 1 << 20, 1 << 20, 1 << 20) == L.MPM_ERR_OVERFLOW
+    assert isplit(3, 64, 1, A, A, A, A, None, 1 << 40, 1 << 20, 1 << 20) == L.MPM_ERR_OVERFLOW
+    assert isplit(3, 64, 10, A, A, A, A, None, 1000, 1000, 1000, (ct.c_void_p(4360), 1 << 30)) == L.MPM_ERR_INVALID
+    need = M.mpm_isplit_workspace_bytes(3, 64, 10)
+    assert isplit(3, 64, 10, A, A, A, A, None, 1000, 1000, 1000, (W[0], need - 1)) == L.MPM_ERR_WORKSPACE
     g = (ct.c_float * 3)(0, -9.8, 0)
     assert lib.mpm_grid_update(ct.byref(d), None, grid, ct.c_void_p(4096), 1e-4, g, 100, None) == L.MPM_ERR_INVALID
     assert lib.mpm_grid_update(ct.byref(d), None, grid, ct.c_void_p(4096), 1e-4, None, 2, None) == L.MPM_ERR_INVALID

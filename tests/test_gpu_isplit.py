@@ -1,12 +1,14 @@
 """GPU parity of the integer-split quadratic APIC transfer against the oracle,
 through the C ABI: integer arithmetic, so bit-exact grids and equal status
-counters, in every visiting order.
+counters, in every visiting order, on both paths (direct: global atomics per
+share; tiled: counting sort into tiles and on-chip node blocks).
 
 Cases: the 2D workload (3,500 particles, 64^2 nodes); a ragged 3D cloud at
 wide value ranges (large products near the rounding edges); the 3D workload at
 full size (1,048,576 particles, 128^3 nodes) in the launch the benchmark
 times; reversed and shuffled orders; positions on the tie and node
-boundaries; particles outside the grid or the declared ranges; an empty call.
+boundaries; particles outside the grid or the declared ranges; one tile
+holding many work items; sparse tiles on a large 2D grid; an empty call.
 """
 import sys
 
@@ -33,7 +35,10 @@ def mpm():
     return M
 
 
-def run_gpu(M, dim, n, h, ranges, order=None, grid=None):
+PATHS = ["direct", "tiled"]
+
+
+def run_gpu(M, dim, n, h, ranges, order=None, grid=None, path="tiled"):
     dev = torch.device("cuda", 0)
     X = torch.from_numpy(np.ascontiguousarray(h["X"], np.int32)).to(dev)
     m = torch.from_numpy(np.ascontiguousarray(h["m"], np.int64)).to(dev)
@@ -43,30 +48,35 @@ def run_gpu(M, dim, n, h, ranges, order=None, grid=None):
     g = torch.zeros((1 + dim,) + (n,) * dim, dtype=torch.int64, device=dev) if grid is None else \
         torch.from_numpy(grid.copy()).to(dev)
     st = torch.zeros(4, dtype=torch.int32, device=dev)
-    M.mpm_p2g_isplit(dim, n, X, m, v, C, o, *ranges, g, st)
+    ws = None
+    if path == "tiled":
+        ws = torch.empty(M.mpm_isplit_workspace_bytes(dim, n, m.numel()), dtype=torch.uint8, device=dev)
+    M.mpm_p2g_isplit(dim, n, X, m, v, C, o, *ranges, g, st, workspace=ws)
     torch.cuda.synchronize()
     return g.cpu().numpy(), st.cpu().numpy().view(np.uint32)
 
 
-def test_2d_workload_bit_exact(mpm, oracle_lib):
+@pytest.mark.parametrize("path", PATHS)
+def test_2d_workload_bit_exact(mpm, oracle_lib, path):
     w = WORKLOADS["isplit_2d_64"]
     h = build(w)
-    say("isplit 2D", w.n_particles)
+    say("isplit 2D", w.n_particles, path)
     rng = (int(w.max_mass), int(w.max_speed), int(w.max_affine))
-    g, st = run_gpu(mpm, 2, w.n, h, rng)
+    g, st = run_gpu(mpm, 2, w.n, h, rng, path=path)
     ref, rst = oracle_lib.p2g_isplit(2, w.n, h)
     assert np.array_equal(g, ref)
     assert st.tolist() == rst.tolist() == [0, 0, 0, 0]
 
 
-def test_3d_wide_ranges_ragged_bit_exact(mpm, oracle_lib):
+@pytest.mark.parametrize("path", PATHS)
+def test_3d_wide_ranges_ragged_bit_exact(mpm, oracle_lib, path):
     """20,011 particles with masses, velocities and affine entries up to 2^20:
     products up to 2^40 split with 49-bit coefficients (128-bit products)."""
     big = 1 << 20
     h = G.integer_cloud_quadratic(0x3D1, 20011, 32, 3, big, big, big)
     assert oracle_lib.isplit_bounds_ok(3, 20011, big, big, big)
-    say("isplit 3D wide")
-    g, st = run_gpu(mpm, 3, 32, h, (big, big, big))
+    say("isplit 3D wide", path)
+    g, st = run_gpu(mpm, 3, 32, h, (big, big, big), path=path)
     ref, rst = oracle_lib.p2g_isplit(3, 32, h)
     assert np.array_equal(g, ref)
     assert st.tolist() == rst.tolist() == [0, 0, 0, 0]
@@ -77,14 +87,15 @@ def test_3d_full_size_bit_exact_and_conserving(mpm, oracle_lib):
     w = WORKLOADS["isplit_3d_128"]
     h = build(w)
     rng = (int(w.max_mass), int(w.max_speed), int(w.max_affine))
-    say("isplit 3D full", w.n_particles)
-    g, st = run_gpu(mpm, 3, w.n, h, rng)
-    assert st.tolist() == [0, 0, 0, 0]
-    assert int(g[0].sum()) == int(h["m"].sum())
-    for d in range(3):
-        assert int(g[1 + d].sum()) == int((h["m"] * h["v"][d]).sum())
     ref, _ = oracle_lib.p2g_isplit(3, w.n, h)
-    assert np.array_equal(g, ref)
+    for path in PATHS:
+        say("isplit 3D full", w.n_particles, path)
+        g, st = run_gpu(mpm, 3, w.n, h, rng, path=path)
+        assert st.tolist() == [0, 0, 0, 0]
+        assert int(g[0].sum()) == int(h["m"].sum())
+        for d in range(3):
+            assert int(g[1 + d].sum()) == int((h["m"] * h["v"][d]).sum())
+        assert np.array_equal(g, ref), path
 
 
 @pytest.mark.parametrize("dim", [2, 3])
@@ -94,15 +105,17 @@ def test_every_order_gives_the_same_grid(mpm, oracle_lib, dim):
     h = G.integer_cloud_quadratic(0x0D + dim, np_, n, dim, 1000, 1000, 1000)
     say("isplit orders", dim)
     base, _ = run_gpu(mpm, dim, n, h, (1000, 1000, 1000))
-    for order in (np.arange(np_)[::-1].copy(), G.permutation(11, 3, np_)):
-        g, st = run_gpu(mpm, dim, n, h, (1000, 1000, 1000), order=order)
-        assert np.array_equal(g, base) and st.tolist() == [0, 0, 0, 0]
+    for path in PATHS:
+        for order in (np.arange(np_)[::-1].copy(), G.permutation(11, 3, np_)):
+            g, st = run_gpu(mpm, dim, n, h, (1000, 1000, 1000), order=order, path=path)
+            assert np.array_equal(g, base) and st.tolist() == [0, 0, 0, 0]
     ref, _ = oracle_lib.p2g_isplit(dim, n, h, order=G.permutation(11, 3, np_))
     assert np.array_equal(base, ref)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("dim", [2, 3])
-def test_boundaries_skips_and_accumulation(mpm, oracle_lib, dim):
+def test_boundaries_skips_and_accumulation(mpm, oracle_lib, dim, path):
     """Positions on nodes (F = 2^16), on ties (F = 2^15), at the first and last
     in-domain positions and just outside; particles over the declared ranges;
     accumulation into a non-zero grid."""
@@ -123,8 +136,8 @@ def test_boundaries_skips_and_accumulation(mpm, oracle_lib, dim):
     ok = inside.copy()
     ok[[200, 201, 202]] = False
     prior = np.arange(np.prod((1 + dim,) + (n,) * dim), dtype=np.int64).reshape((1 + dim,) + (n,) * dim) * 7 - 11
-    say("isplit boundaries", dim)
-    g, st = run_gpu(mpm, dim, n, h, (500, 500, 500), grid=prior)
+    say("isplit boundaries", dim, path)
+    g, st = run_gpu(mpm, dim, n, h, (500, 500, 500), grid=prior, path=path)
     sub = {k: np.ascontiguousarray(a[..., ok]) for k, a in h.items()}
     ref, rst = oracle_lib.p2g_isplit(dim, n, sub, grid=prior.copy())
     assert np.array_equal(g, ref)
@@ -132,13 +145,36 @@ def test_boundaries_skips_and_accumulation(mpm, oracle_lib, dim):
     assert st.tolist() == [2, 3, 0, 0]
 
 
-def test_empty_call_leaves_the_grid(mpm):
+def test_one_tile_many_items_and_sparse_tiles(mpm, oracle_lib):
+    """9,001 particles inside one 8^3-cell tile (five work items) plus a
+    scatter over the rest of the grid; and a 2D cloud of 5,000 particles over
+    a 2,048^2-node grid (65,536 tiles, most of them empty)."""
+    n = 40
+    h = G.integer_cloud_quadratic(0x71, 12000, n, 3, 1000, 1000, 1000)
+    lo, span = (16 << 16) + (1 << 15), 8 << 16               # bases 16..23: one tile
+    for e in range(3):
+        h["X"][e, :9001] = lo + (h["X"][e, :9001].astype(np.int64) * 7919) % span
+    say("isplit one tile")
+    g, st = run_gpu(mpm, 3, n, h, (1000, 1000, 1000))
+    ref, _ = oracle_lib.p2g_isplit(3, n, h)
+    assert np.array_equal(g, ref) and st.tolist() == [0, 0, 0, 0]
+    h2 = G.integer_cloud_quadratic(0x72, 5000, 2048, 2, 1000, 1000, 1000)
+    say("isplit sparse 2D")
+    g2, st2 = run_gpu(mpm, 2, 2048, h2, (1000, 1000, 1000))
+    ref2, _ = oracle_lib.p2g_isplit(2, 2048, h2)
+    assert np.array_equal(g2, ref2) and st2.tolist() == [0, 0, 0, 0]
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_empty_call_leaves_the_grid(mpm, path):
     dev = torch.device("cuda", 0)
     e32 = torch.zeros((3, 0), dtype=torch.int32, device=dev)
     e64 = torch.zeros(0, dtype=torch.int64, device=dev)
     g = torch.full((4, 8, 8, 8), 5, dtype=torch.int64, device=dev)
     st = torch.zeros(4, dtype=torch.int32, device=dev)
+    ws = torch.empty(mpm.mpm_isplit_workspace_bytes(3, 8, 0), dtype=torch.uint8, device=dev) if path == "tiled" \
+        else None
     mpm.mpm_p2g_isplit(3, 8, e32, e64, torch.zeros((3, 0), dtype=torch.int64, device=dev),
-                       torch.zeros((9, 0), dtype=torch.int64, device=dev), None, 10, 10, 10, g, st)
+                       torch.zeros((9, 0), dtype=torch.int64, device=dev), None, 10, 10, 10, g, st, workspace=ws)
     torch.cuda.synchronize()
     assert bool((g == 5).all()) and st.cpu().tolist() == [0, 0, 0, 0]
