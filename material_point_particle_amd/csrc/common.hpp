@@ -169,7 +169,8 @@ hipError_t launch_p2g_isplit(int dim, int n, int64_t np, const int32_t *X, const
                              int64_t max_affine, int64_t *grid, uint32_t *status, hipStream_t s);
 struct IsplitLayout {      // byte offsets into the integer-split workspace
     size_t count, start, partial, meta, rank, perm, total;
-    int64_t tiles_x, tiles, scan_blocks;
+    int64_t tiles_x, tiles, entries, scan_blocks;
+    int slot_shift;       // 2^slot_shift counters per tile
 };
 IsplitLayout isplit_layout(int dim, int n, int64_t np);
 hipError_t launch_p2g_isplit_tiled(int dim, int n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,

@@ -67,11 +67,45 @@ __device__ __forceinline__ int64_t round_shift(__int128 t)
     return fl + (int64_t)((r > half) | ((r == half) & ((uint64_t)fl & 1ull)));
 }
 
-// Split q along one axis: KIND 0 with the weights, KIND 1 with the first moments.
-template <int KIND>
+// round-half-even(q c / 2^K) for |q| < 2^31, |c| < 2^49 and 31 < K < 50,
+// with c = c_hi 2^31 + c_lo (0 <= c_lo < 2^31): two signed 32 x 32 -> 64-bit
+// multiply-adds.  u = q c_lo + 2^(K-1) and w = q c_hi + floor(u / 2^31) give
+// q c + 2^(K-1) = 2^31 w + (u mod 2^31), so floor((q c + 2^(K-1)) / 2^K) =
+// floor(w / 2^(K-31)) (round half up); on an exact tie (both remainders zero)
+// an odd result steps down to the even neighbour.
+template <int K>
+__device__ __forceinline__ int64_t mul_round_narrow(int32_t q, int64_t c)
+{
+    const int32_t c_lo = (int32_t)(c & 0x7FFFFFFFll), c_hi = (int32_t)(c >> 31);
+    // the offset's value is hidden from the optimiser: with it known, the
+    // remainder test below is rewritten as a separate low-word multiply
+    int64_t half = 1ll << (K - 1);
+    asm("" : "+s"(half));
+    const int64_t u = (int64_t)q * c_lo + half;
+    const int64_t w = (int64_t)q * c_hi + (u >> 31);
+    const int64_t r = w >> (K - 31);
+    const int64_t tie = (int64_t)(((w & ((1ll << (K - 31)) - 1)) == 0) & ((u & 0x7FFFFFFFll) == 0));
+    return r - (tie & r & 1);
+}
+
+// Split q along one axis: KIND 0 with the weights, KIND 1 with the first
+// moments.  NARROW: |q| < 2^31 (guaranteed by the declared ranges), products
+// from two 32-bit multiply-adds; otherwise full 128-bit products.
+template <int KIND, bool NARROW>
 __device__ __forceinline__ void split1(int64_t q, const AxisCoef &c, int64_t s[3])
 {
-    if constexpr (KIND == 0) {
+    if constexpr (NARROW) {
+        const int32_t q32 = (int32_t)q;
+        if constexpr (KIND == 0) {
+            s[0] = mul_round_narrow<33>(q32, c.w0);
+            s[2] = mul_round_narrow<33>(q32, c.w2);
+            s[1] = q - s[0] - s[2];
+        } else {
+            s[0] = mul_round_narrow<49>(q32, c.u0);
+            s[2] = mul_round_narrow<49>(q32, c.u2);
+            s[1] = -s[0] - s[2];
+        }
+    } else if constexpr (KIND == 0) {
         s[0] = round_shift<33>((__int128)q * c.w0);
         s[2] = round_shift<33>((__int128)q * c.w2);
         s[1] = q - s[0] - s[2];
@@ -84,20 +118,20 @@ __device__ __forceinline__ void split1(int64_t q, const AxisCoef &c, int64_t s[3
 
 // acc[(a * 3 + b) * 3 + c] (2D: acc[a * 3 + b]) += the tensor split of q,
 // along x with KX, then y with KY, then z with KZ.
-template <int DIM, int KX, int KY, int KZ>
+template <int DIM, bool NARROW, int KX, int KY, int KZ>
 __device__ __forceinline__ void tensor_add(int64_t q, const AxisCoef (&ax)[DIM], int64_t (&acc)[DIM == 3 ? 27 : 9])
 {
     int64_t sx[3];
-    split1<KX>(q, ax[0], sx);
+    split1<KX, NARROW>(q, ax[0], sx);
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
         int64_t sy[3];
-        split1<KY>(sx[a], ax[1], sy);
+        split1<KY, NARROW>(sx[a], ax[1], sy);
 #pragma unroll
         for (int b = 0; b < 3; ++b) {
             if constexpr (DIM == 3) {
                 int64_t sz[3];
-                split1<KZ>(sy[b], ax[2], sz);
+                split1<KZ, NARROW>(sy[b], ax[2], sz);
 #pragma unroll
                 for (int c = 0; c < 3; ++c)
                     acc[(a * 3 + b) * 3 + c] += sz[c];
@@ -172,7 +206,7 @@ __device__ __forceinline__ bool load_quantities(const int64_t *__restrict__ m, c
 
 // All channels of one particle: sink(channel, acc) receives the 3^dim shares
 // of each channel in turn.
-template <int DIM, class Sink>
+template <int DIM, bool NARROW, class Sink>
 __device__ __forceinline__ void particle_shares(const AxisCoef (&ax)[DIM], int64_t mp, const int64_t (&vp)[DIM],
                                                 const int64_t (&cp)[DIM][DIM], Sink &&sink)
 {
@@ -181,23 +215,23 @@ __device__ __forceinline__ void particle_shares(const AxisCoef (&ax)[DIM], int64
 #pragma unroll
     for (int i = 0; i < K; ++i)
         acc[i] = 0;
-    tensor_add<DIM, 0, 0, 0>(mp, ax, acc);
+    tensor_add<DIM, NARROW, 0, 0, 0>(mp, ax, acc);
     sink(0, acc);
 #pragma unroll 1
     for (int d = 0; d < DIM; ++d) {
 #pragma unroll
         for (int i = 0; i < K; ++i)
             acc[i] = 0;
-        tensor_add<DIM, 0, 0, 0>(mp * vp[d], ax, acc);
-        tensor_add<DIM, 1, 0, 0>(mp * cp[d][0], ax, acc);
-        tensor_add<DIM, 0, 1, 0>(mp * cp[d][1], ax, acc);
+        tensor_add<DIM, NARROW, 0, 0, 0>(mp * vp[d], ax, acc);
+        tensor_add<DIM, NARROW, 1, 0, 0>(mp * cp[d][0], ax, acc);
+        tensor_add<DIM, NARROW, 0, 1, 0>(mp * cp[d][1], ax, acc);
         if constexpr (DIM == 3)
-            tensor_add<DIM, 0, 0, 1>(mp * cp[d][2], ax, acc);
+            tensor_add<DIM, NARROW, 0, 0, 1>(mp * cp[d][2], ax, acc);
         sink(1 + d, acc);
     }
 }
 
-template <int DIM>
+template <int DIM, bool NARROW>
 __global__ void __launch_bounds__(256) isplit_kernel(int64_t np, int n, const int32_t *__restrict__ X,
                                                      const int64_t *__restrict__ m, const int64_t *__restrict__ v,
                                                      const int64_t *__restrict__ C,
@@ -221,7 +255,7 @@ __global__ void __launch_bounds__(256) isplit_kernel(int64_t np, int n, const in
         wave_count(inside && !in_range, &status[1]);
         if (!inside || !in_range)
             continue;
-        particle_shares<DIM>(ax, mp, vp, cp, [&](int ch, const int64_t(&acc)[DIM == 3 ? 27 : 9]) {
+        particle_shares<DIM, NARROW>(ax, mp, vp, cp, [&](int ch, const int64_t(&acc)[DIM == 3 ? 27 : 9]) {
             flush<DIM>(grid + ch * nodes, acc, base, n);
         });
     }
@@ -253,16 +287,20 @@ __global__ void __launch_bounds__(256) is_zero_kernel(uint32_t *__restrict__ a, 
         a[i] = 0u;
 }
 
-// Tile of every visited particle; its rank among the tile's particles comes
-// from the returning atomic on the tile count.  Particles whose stencil
-// leaves the grid get rank ~0 and are counted; the range check is the
-// accumulating kernel's.
+// Tile of every visited particle; its rank among the particles of its
+// counter comes from the returning atomic on that counter.  Each tile has
+// 2^sshift counters (slots), laid out tile-major; visit k uses slot
+// (k / 256) mod 2^sshift, which spreads the atomics on one tile over several
+// addresses.  Particles whose stencil leaves the grid get rank ~0 and are
+// counted; the range check is the accumulating kernel's.
 template <int DIM>
-__global__ void __launch_bounds__(256) is_count_kernel(int64_t np, int n, int64_t tx, const int32_t *__restrict__ X,
+__global__ void __launch_bounds__(256) is_count_kernel(int64_t np, int n, int64_t tx, int sshift,
+                                                       const int32_t *__restrict__ X,
                                                        const uint32_t *__restrict__ order,
                                                        uint32_t *__restrict__ count, uint32_t *__restrict__ rank,
                                                        uint32_t *__restrict__ status)
 {
+    const int64_t smask = (1ll << sshift) - 1;
     for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < np; k += (int64_t)gridDim.x * blockDim.x) {
         const int64_t p = order ? (int64_t)order[k] : k;
         uint32_t r = ~0u;
@@ -275,21 +313,38 @@ __global__ void __launch_bounds__(256) is_count_kernel(int64_t np, int n, int64_
             AxisCoef ax[DIM];
             inside = stencil<DIM>(X, np, p, n, base, ax);
             if (inside)
-                r = atomicAdd(&count[tile_of<DIM>(base, tx)], 1u);
+                r = atomicAdd(&count[(tile_of<DIM>(base, tx) << sshift) | ((k >> 8) & smask)], 1u);
         }
         wave_count(!inside, &status[0]);
         rank[k] = r;
     }
 }
 
-// Packed scan entry of tile t: work items in the high word, particles in the
-// low word (totals stay below 2^32, so neither half carries into the other).
-__device__ __forceinline__ uint64_t packed_entry(const uint32_t *__restrict__ count, int64_t t, int64_t tiles)
+// Particles of tile t: the sum of its slot counters.
+__device__ __forceinline__ uint64_t tile_total(const uint32_t *__restrict__ count, int64_t t, int sshift)
 {
-    if (t >= tiles)
+    uint64_t c = 0;
+    for (int q = 0; q < (1 << sshift); ++q)
+        c += count[(t << sshift) + q];
+    return c;
+}
+
+// Packed scan entry e (tile e >> sshift, slot e mod 2^sshift): particles of
+// the slot in the low word; on the tile's last slot, the tile's work items in
+// the high word.  Totals stay below 2^32, so neither half carries into the
+// other; the exclusive scan at a tile's first slot holds the items and
+// particles of all tiles before it.
+__device__ __forceinline__ uint64_t packed_entry(const uint32_t *__restrict__ count, int64_t e, int64_t entries,
+                                                 int sshift)
+{
+    if (e >= entries)
         return 0ull;
-    const uint64_t c = count[t];
-    return (((c + kIsChunk - 1) / kIsChunk) << 32) | c;
+    const uint64_t c = count[e];
+    const int64_t smask = (1ll << sshift) - 1;
+    if ((e & smask) != smask)
+        return c;
+    const uint64_t total = tile_total(count, e >> sshift, sshift);
+    return (((total + kIsChunk - 1) / kIsChunk) << 32) | c;
 }
 
 // Exclusive scan of 256 threads' values; returns the block total in *total.
@@ -318,7 +373,8 @@ __device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t x, uint64_t *l
     return before + inc - x;
 }
 
-__global__ void __launch_bounds__(kIsThreads) is_scan_partial_kernel(const uint32_t *__restrict__ count, int64_t tiles,
+__global__ void __launch_bounds__(kIsThreads) is_scan_partial_kernel(const uint32_t *__restrict__ count,
+                                                                     int64_t entries, int sshift,
                                                                      uint64_t *__restrict__ partial)
 {
     __shared__ uint64_t lw[kIsThreads / kWave];
@@ -326,7 +382,7 @@ __global__ void __launch_bounds__(kIsThreads) is_scan_partial_kernel(const uint3
     uint64_t s = 0;
 #pragma unroll
     for (int i = 0; i < kScanPer; ++i)
-        s += packed_entry(count, t0 + i, tiles);
+        s += packed_entry(count, t0 + i, entries, sshift);
     uint64_t total;
     block_exclusive_scan(s, lw, &total);
     if (threadIdx.x == 0)
@@ -353,7 +409,8 @@ __global__ void __launch_bounds__(kIsThreads) is_scan_top_kernel(uint64_t *__res
         meta[0] = carry;
 }
 
-__global__ void __launch_bounds__(kIsThreads) is_scan_final_kernel(const uint32_t *__restrict__ count, int64_t tiles,
+__global__ void __launch_bounds__(kIsThreads) is_scan_final_kernel(const uint32_t *__restrict__ count,
+                                                                   int64_t entries, int sshift,
                                                                    const uint64_t *__restrict__ partial,
                                                                    uint64_t *__restrict__ start)
 {
@@ -362,21 +419,22 @@ __global__ void __launch_bounds__(kIsThreads) is_scan_final_kernel(const uint32_
     uint64_t e[kScanPer], s = 0;
 #pragma unroll
     for (int i = 0; i < kScanPer; ++i) {
-        e[i] = packed_entry(count, t0 + i, tiles);
+        e[i] = packed_entry(count, t0 + i, entries, sshift);
         s += e[i];
     }
     uint64_t total;
     uint64_t run = partial[blockIdx.x] + block_exclusive_scan(s, lw, &total);
 #pragma unroll
     for (int i = 0; i < kScanPer; ++i) {
-        if (t0 + i < tiles)
+        if (t0 + i < entries)
             start[t0 + i] = run;
         run += e[i];
     }
 }
 
 template <int DIM>
-__global__ void __launch_bounds__(256) is_scatter_kernel(int64_t np, int n, int64_t tx, const int32_t *__restrict__ X,
+__global__ void __launch_bounds__(256) is_scatter_kernel(int64_t np, int n, int64_t tx, int sshift,
+                                                         const int32_t *__restrict__ X,
                                                          const uint32_t *__restrict__ order,
                                                          const uint32_t *__restrict__ rank,
                                                          const uint64_t *__restrict__ start,
@@ -390,19 +448,21 @@ __global__ void __launch_bounds__(256) is_scatter_kernel(int64_t np, int n, int6
         int64_t base[DIM];
         AxisCoef ax[DIM];
         stencil<DIM>(X, np, p, n, base, ax);
-        perm[(start[tile_of<DIM>(base, tx)] & 0xFFFFFFFFull) + r] = (uint32_t)p;
+        const int64_t e = (tile_of<DIM>(base, tx) << sshift) | ((k >> 8) & ((1ll << sshift) - 1));
+        perm[(start[e] & 0xFFFFFFFFull) + r] = (uint32_t)p;
     }
 }
 
 // Work item i -> the tile whose items contain it: the last tile whose first
 // item is <= i (an empty tile shares its first item with the next tile, so
 // the last such tile is never empty).
-__device__ __forceinline__ int64_t item_tile(const uint64_t *__restrict__ start, int64_t tiles, uint64_t i)
+__device__ __forceinline__ int64_t item_tile(const uint64_t *__restrict__ start, int64_t tiles, int sshift,
+                                             uint64_t i)
 {
     int64_t lo = 0, hi = tiles;          // first tile with first item > i lies in (lo, hi]
     while (hi - lo > 1) {
         const int64_t mid = (lo + hi) / 2;
-        if ((start[mid] >> 32) <= i)
+        if ((start[mid << sshift] >> 32) <= i)
             lo = mid;
         else
             hi = mid;
@@ -410,8 +470,8 @@ __device__ __forceinline__ int64_t item_tile(const uint64_t *__restrict__ start,
     return lo;
 }
 
-template <int DIM>
-__global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n, int64_t tx, int64_t tiles,
+template <int DIM, bool NARROW>
+__global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n, int64_t tx, int64_t tiles, int sshift,
                                                               const int32_t *__restrict__ X,
                                                               const int64_t *__restrict__ m,
                                                               const int64_t *__restrict__ v,
@@ -431,10 +491,10 @@ __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n,
     const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
     const uint64_t items = meta[0] >> 32;
     for (uint64_t i = blockIdx.x; i < items; i += gridDim.x) {
-        const int64_t t = item_tile(start, tiles, i);
-        const uint64_t s = start[t];
+        const int64_t t = item_tile(start, tiles, sshift, i);
+        const uint64_t s = start[t << sshift];
         const int64_t lo = (int64_t)(s & 0xFFFFFFFFull) + (int64_t)(i - (s >> 32)) * kIsChunk;
-        const int64_t end_t = (int64_t)(s & 0xFFFFFFFFull) + count[t];
+        const int64_t end_t = (int64_t)(s & 0xFFFFFFFFull) + (int64_t)tile_total(count, t, sshift);
         const int64_t hi = lo + kIsChunk < end_t ? lo + kIsChunk : end_t;
         int64_t origin[DIM];
         {
@@ -462,7 +522,7 @@ __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n,
 #pragma unroll
             for (int e = 0; e < DIM; ++e)
                 lb[e] = (int)(base[e] - origin[e]);
-            particle_shares<DIM>(ax, mp, vp, cp, [&](int ch, const int64_t(&acc)[DIM == 3 ? 27 : 9]) {
+            particle_shares<DIM, NARROW>(ax, mp, vp, cp, [&](int ch, const int64_t(&acc)[DIM == 3 ? 27 : 9]) {
 #pragma unroll
                 for (int a = 0; a < 3; ++a)
 #pragma unroll
@@ -511,6 +571,19 @@ __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n,
     }
 }
 
+// Narrow splits need every split quantity below 2^31 in magnitude: the first
+// splits take m, m v_d and m C_de, and each split's shares exceed its
+// quantity by at most one, so max_mass * max(1, max_speed, max_affine) + 3
+// below 2^31 suffices (particles beyond the declared ranges are skipped).
+template <int DIM, class Launch, class K>
+void pick_width(int64_t max_mass, int64_t max_speed, int64_t max_affine, Launch &&launch, K narrow, K wide)
+{
+    int64_t f = max_speed > max_affine ? max_speed : max_affine;
+    f = f > 1 ? f : 1;
+    const __int128 q = (__int128)max_mass * f + 3;
+    launch(q < ((__int128)1 << 31) ? narrow : wide);
+}
+
 int64_t is_blocks(int64_t work, int64_t cap_per_cu)
 {
     const int64_t want = (work + 255) / 256, cap = (int64_t)device_cu_count() * cap_per_cu;
@@ -524,15 +597,19 @@ IsplitLayout isplit_layout(int dim, int n, int64_t np)
     IsplitLayout l{};
     l.tiles_x = (n - 2 + kIsTile - 1) / kIsTile;           // bases 0..n-3
     l.tiles = dim == 3 ? l.tiles_x * l.tiles_x * l.tiles_x : l.tiles_x * l.tiles_x;
-    l.scan_blocks = (l.tiles + kScanBlock - 1) / kScanBlock;
+    l.slot_shift = 3;                                      // up to 8 counters per tile, at most 2^22 in all
+    while (l.slot_shift > 0 && (l.tiles << l.slot_shift) > (1ll << 22))
+        --l.slot_shift;
+    l.entries = l.tiles << l.slot_shift;
+    l.scan_blocks = (l.entries + kScanBlock - 1) / kScanBlock;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
         off += (bytes + 255) & ~(size_t)255;
         return at;
     };
-    l.count = take(sizeof(uint32_t) * (size_t)l.tiles);
-    l.start = take(sizeof(uint64_t) * (size_t)l.tiles);
+    l.count = take(sizeof(uint32_t) * (size_t)l.entries);
+    l.start = take(sizeof(uint64_t) * (size_t)l.entries);
     l.partial = take(sizeof(uint64_t) * (size_t)l.scan_blocks);
     l.meta = take(sizeof(uint64_t) * 2);
     l.rank = take(sizeof(uint32_t) * (size_t)(np > 0 ? np : 1));
@@ -556,30 +633,40 @@ hipError_t launch_p2g_isplit_tiled(int dim, int n, int64_t np, const int32_t *X,
     uint32_t *rank = reinterpret_cast<uint32_t *>(w + l.rank);
     uint32_t *perm = reinterpret_cast<uint32_t *>(w + l.perm);
     const dim3 blk(kIsThreads);
-    hipLaunchKernelGGL(is_zero_kernel, dim3((unsigned)is_blocks(l.tiles, 16)), blk, 0, s, count, l.tiles);
+    const int sh = l.slot_shift;
+    hipLaunchKernelGGL(is_zero_kernel, dim3((unsigned)is_blocks(l.entries, 16)), blk, 0, s, count, l.entries);
     const unsigned pb = (unsigned)is_blocks(np, 32);
     if (dim == 3)
-        hipLaunchKernelGGL(is_count_kernel<3>, dim3(pb), blk, 0, s, np, n, l.tiles_x, X, order, count, rank, status);
+        hipLaunchKernelGGL(is_count_kernel<3>, dim3(pb), blk, 0, s, np, n, l.tiles_x, sh, X, order, count, rank,
+                           status);
     else
-        hipLaunchKernelGGL(is_count_kernel<2>, dim3(pb), blk, 0, s, np, n, l.tiles_x, X, order, count, rank, status);
-    hipLaunchKernelGGL(is_scan_partial_kernel, dim3((unsigned)l.scan_blocks), blk, 0, s, count, l.tiles, partial);
+        hipLaunchKernelGGL(is_count_kernel<2>, dim3(pb), blk, 0, s, np, n, l.tiles_x, sh, X, order, count, rank,
+                           status);
+    hipLaunchKernelGGL(is_scan_partial_kernel, dim3((unsigned)l.scan_blocks), blk, 0, s, count, l.entries, sh,
+                       partial);
     hipLaunchKernelGGL(is_scan_top_kernel, dim3(1), blk, 0, s, partial, l.scan_blocks, meta);
-    hipLaunchKernelGGL(is_scan_final_kernel, dim3((unsigned)l.scan_blocks), blk, 0, s, count, l.tiles, partial,
+    hipLaunchKernelGGL(is_scan_final_kernel, dim3((unsigned)l.scan_blocks), blk, 0, s, count, l.entries, sh, partial,
                        start);
     if (dim == 3)
-        hipLaunchKernelGGL(is_scatter_kernel<3>, dim3(pb), blk, 0, s, np, n, l.tiles_x, X, order, rank, start, perm);
+        hipLaunchKernelGGL(is_scatter_kernel<3>, dim3(pb), blk, 0, s, np, n, l.tiles_x, sh, X, order, rank, start,
+                           perm);
     else
-        hipLaunchKernelGGL(is_scatter_kernel<2>, dim3(pb), blk, 0, s, np, n, l.tiles_x, X, order, rank, start, perm);
+        hipLaunchKernelGGL(is_scatter_kernel<2>, dim3(pb), blk, 0, s, np, n, l.tiles_x, sh, X, order, rank, start,
+                           perm);
     // items <= tiles + np / kIsChunk; persistent workgroups stride over them
     const int64_t max_items = l.tiles + np / kIsChunk + 1;
     const int64_t cap = (int64_t)device_cu_count() * 4;
     const unsigned tb = (unsigned)(max_items < cap ? max_items : cap);
-    if (dim == 3)
-        hipLaunchKernelGGL(is_tiled_kernel<3>, dim3(tb), blk, 0, s, np, n, l.tiles_x, l.tiles, X, m, v, C, count,
-                           start, perm, meta, max_mass, max_speed, max_affine, grid, status);
+if (dim == 3)
+        pick_width<3>(max_mass, max_speed, max_affine, [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3(tb), blk, 0, s, np, n, l.tiles_x, l.tiles, sh, X, m, v, C, count, start,
+                               perm, meta, max_mass, max_speed, max_affine, grid, status);
+        }, is_tiled_kernel<3, true>, is_tiled_kernel<3, false>);
     else
-        hipLaunchKernelGGL(is_tiled_kernel<2>, dim3(tb), blk, 0, s, np, n, l.tiles_x, l.tiles, X, m, v, C, count,
-                           start, perm, meta, max_mass, max_speed, max_affine, grid, status);
+        pick_width<2>(max_mass, max_speed, max_affine, [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3(tb), blk, 0, s, np, n, l.tiles_x, l.tiles, sh, X, m, v, C, count, start,
+                               perm, meta, max_mass, max_speed, max_affine, grid, status);
+        }, is_tiled_kernel<2, true>, is_tiled_kernel<2, false>);
     return hipGetLastError();
 }
 
@@ -591,12 +678,14 @@ hipError_t launch_p2g_isplit(int dim, int n, int64_t np, const int32_t *X, const
         return hipSuccess;
     const int64_t want = (np + 255) / 256, cap = (int64_t)device_cu_count() * 32;
     const int blocks = (int)(want > cap ? cap : want);
+    auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, np, n, X, m, v, C, order, max_mass, max_speed,
+                           max_affine, grid, status);
+    };
     if (dim == 3)
-        hipLaunchKernelGGL(isplit_kernel<3>, dim3(blocks), dim3(256), 0, s, np, n, X, m, v, C, order, max_mass,
-                           max_speed, max_affine, grid, status);
+        pick_width<3>(max_mass, max_speed, max_affine, launch, isplit_kernel<3, true>, isplit_kernel<3, false>);
     else
-        hipLaunchKernelGGL(isplit_kernel<2>, dim3(blocks), dim3(256), 0, s, np, n, X, m, v, C, order, max_mass,
-                           max_speed, max_affine, grid, status);
+        pick_width<2>(max_mass, max_speed, max_affine, launch, isplit_kernel<2, true>, isplit_kernel<2, false>);
     return hipGetLastError();
 }
 

@@ -86,14 +86,19 @@ def test_workspace_layout_is_disjoint_and_aligned():
 
 
 def test_isplit_workspace_size():
-    # tile counts and starts (8^dim-cell tiles over the n - 2 base nodes per
-    # axis), plus a rank and an index per visited particle, in 256-byte sections
+    # tile counters and starts (8^dim-cell tiles over the n - 2 base nodes per
+    # axis; up to 8 counters per tile, at most 2^22 in all), plus a rank and an
+    # index per visited particle, in 256-byte sections
     def r(b):
         return (b + 255) // 256 * 256
-    for dim, n, N in [(3, 128, 1 << 20), (2, 64, 3500), (3, 10, 1), (2, 2048, 0)]:
+    for dim, n, N in [(3, 128, 1 << 20), (2, 64, 3500), (3, 10, 1), (2, 2048, 0), (3, 1024, 5), (2, 32767, 7)]:
         t = ((n - 2 + 7) // 8) ** dim
-        blocks = (t + 1023) // 1024
-        want = r(4 * t) + r(8 * t) + r(8 * blocks) + r(16) + 2 * r(4 * max(N, 1))
+        slots = 8
+        while slots > 1 and t * slots > 1 << 22:
+            slots //= 2
+        e = t * slots
+        blocks = (e + 1023) // 1024
+        want = r(4 * e) + r(8 * e) + r(8 * blocks) + r(16) + 2 * r(4 * max(N, 1))
         assert M.mpm_isplit_workspace_bytes(dim, n, N) == want
     with pytest.raises(M.MpmError):
         M.mpm_isplit_workspace_bytes(3, 2, 10)

@@ -83,6 +83,31 @@ def test_3d_wide_ranges_ragged_bit_exact(mpm, oracle_lib, path):
     assert int(g[0].sum()) == int(h["m"].sum())
 
 
+@pytest.mark.parametrize("path", PATHS)
+def test_narrow_limit_signs_and_ties(mpm, oracle_lib, path):
+    """Declared maxima at the edge of the 32-bit product path (46,340 each:
+    m v up to 2^31 - 88,048), values at the extremes with both signs
+    (negative masses included), positions on ties and nodes; and the same
+    cloud with maxima one step wider, which takes the 128-bit path."""
+    lim = 46340
+    h = G.integer_cloud_quadratic(0x6A, 9001, 24, 3, lim, lim, lim)
+    rng = np.random.default_rng(5)
+    for key in ("m", "v", "C"):
+        a = h[key]
+        pick = rng.random(a.shape) < 0.3
+        a[pick] = np.where(rng.random(a.shape) < 0.5, lim, -lim)[pick]
+    h["m"][::7] *= -1
+    h["X"][0, :500] = (h["X"][0, :500] & ~0xFFFF) | 0x8000           # ties on x
+    h["X"][1, 500:1000] &= ~0xFFFF                                    # on nodes in y
+    assert int(np.abs(h["m"]).max()) == lim
+    ref, rst = oracle_lib.p2g_isplit(3, 24, h)
+    assert rst.tolist() == [0, 0, 0, 0]
+    for maxima in ((lim, lim, lim), (lim + 1, lim + 1, lim + 1)):
+        say("isplit narrow limit", path, maxima[0])
+        g, st = run_gpu(mpm, 3, 24, h, maxima, path=path)
+        assert np.array_equal(g, ref) and st.tolist() == [0, 0, 0, 0]
+
+
 def test_3d_full_size_bit_exact_and_conserving(mpm, oracle_lib):
     w = WORKLOADS["isplit_3d_128"]
     h = build(w)
