@@ -1,0 +1,127 @@
+"""GPU parity at the size limits the C ABI accepts, against the oracle.
+
+- The largest grids of the quadratic path (512^3 nodes in 3D, 1024^2 in 2D):
+  binning, tiled and direct P2G, the grid update restricted to the reachable
+  node tiles and G2P, bit-exact, with particles spread over every valid base
+  cell and packed into the first and last ones (the highest tile, node and
+  channel offsets the kernels form).
+- The integer-split transfer on its smallest grid (n = 3: one base node per
+  axis) and on grids whose last 8-cell tile is partial, both paths.
+"""
+import sys
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from mpm_inputs import WORKLOADS, scaled
+from mpm_inputs import generators as G
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-test]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def mpm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import material_point_particle_amd as M
+    M.lib()
+    return M
+
+
+def spread_cloud(dim, n, count, edge_count, seed):
+    """count particles uniform over every valid base cell (node coordinate in
+    [1/2, n - 3/2)), plus edge_count in each of the first and last base cells."""
+    u = G.uniform01(seed, 1, dim * count).reshape(dim, count)
+    g = 0.5 + u * (n - 2) * 0.99999
+    lo = 0.5 + G.uniform01(seed, 2, dim * edge_count).reshape(dim, edge_count) * 0.999
+    hi = (n - 2.5) + G.uniform01(seed, 3, dim * edge_count).reshape(dim, edge_count) * 0.999
+    x = (np.concatenate([g, lo, hi], axis=1) / n).astype(np.float32)
+    N = x.shape[1]
+    f = G.particle_fields(seed, N, dim, (0.5, 2.0), 1.0, 0.5)
+    return {"x": np.ascontiguousarray(x), **f}
+
+
+def assert_same(a, b, what):
+    if not np.array_equal(a, b):
+        diff = np.argwhere(a != b)
+        i = tuple(diff[0])
+        raise AssertionError(f"{what}: {len(diff)} entries differ; first at {i}: gpu {a[i]} oracle {b[i]}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dim,n,count", [(3, 512, 200_000), (2, 1024, 100_000)])
+def test_largest_grid_chain_bit_exact(mpm, oracle_lib, dim, n, count):
+    from material_point_particle_amd.transfer import DeviceParticles, Transfer
+    host = spread_cloud(dim, n, count, 2_000, 0x1A26 + dim)
+    base = WORKLOADS["dam_3d_256"] if dim == 3 else WORKLOADS["pile_2d"]
+    w = replace(scaled(base, host["m"].shape[0], n=n), frac_bits=30, max_mass=2.0, max_speed=8.0, max_affine=4.0)
+    ex = WORKLOADS["dam_3d_256"].extra
+    rng = (w.max_mass, w.max_speed, w.max_affine)
+    g_x = host["x"].astype(np.float64) * n
+    assert g_x.min() >= 0.5 and g_x.max() < n - 1.5
+    say("largest grid: oracle", dim, n)
+    ref, ref_st = oracle_lib.p2g_quadratic(dim, n, w.frac_bits, host, rng)
+    assert ref_st.tolist() == [0, 0, 0, 0]
+    parts = DeviceParticles(host)
+    tr = Transfer(dim, n, w.frac_bits, rng, parts.n)
+    say("largest grid: direct P2G", dim, n)
+    tr.grid.zero_()
+    tr.p2g(parts, binned=False)
+    torch.cuda.synchronize()
+    assert_same(tr.grid.cpu().numpy(), ref, "direct P2G")
+    say("largest grid: binned P2G", dim, n)
+    tr.grid.zero_()
+    tr.bin(parts)
+    tr.p2g(parts, binned=True)
+    torch.cuda.synchronize()
+    assert_same(tr.grid.cpu().numpy(), ref, "tiled P2G")
+    assert tr.status.cpu().numpy().view(np.uint32).tolist() == [0, 0, 0, 0]
+    say("largest grid: update + G2P", dim, n)
+    gravity = ex["gravity"][:dim]
+    tr.grid_update(ex["dt"], gravity, ex["sticky"], active=True)
+    tr.g2p(parts, ex["dt"])
+    torch.cuda.synchronize()
+    vg_ref = oracle_lib.grid_update(dim, n, ref, ex["dt"], gravity, ex["sticky"])
+    del ref
+    out = {k: v.copy() for k, v in host.items()}
+    st = oracle_lib.g2p(dim, n, vg_ref, out, ex["dt"])
+    got = parts.host()
+    for k in ("x", "v", "C"):
+        assert_same(got[k], out[k], f"G2P {k}")
+    assert tr.status.cpu().numpy().view(np.uint32).tolist() == st.tolist()
+
+
+@pytest.mark.parametrize("dim,n", [(2, 3), (3, 3), (2, 13), (3, 21)])
+def test_isplit_smallest_and_ragged_tile_grids(mpm, oracle_lib, dim, n):
+    dev = torch.device("cuda", 0)
+    np_ = 5000
+    if n == 3:
+        # the only base node is 0: positions in [1/2, 3/2) cells
+        X = (32768 + G.uniform_int(0x33, 7 + dim, dim * np_, 0, 65535)).reshape(dim, np_).astype(np.int32)
+        h = G.integer_cloud_quadratic(0x33, np_, 8, dim, 1000, 1000, 1000)
+        h["X"] = np.ascontiguousarray(X)
+    else:
+        h = G.integer_cloud_quadratic(0x34 + n, np_, n, dim, 1000, 1000, 1000)
+    ref, rst = oracle_lib.p2g_isplit(dim, n, h)
+    assert rst.tolist() == [0, 0, 0, 0]
+    for path in ("direct", "tiled"):
+        X = torch.from_numpy(h["X"]).to(dev)
+        m = torch.from_numpy(h["m"]).to(dev)
+        v = torch.from_numpy(h["v"]).to(dev)
+        C = torch.from_numpy(h["C"]).to(dev)
+        g = torch.zeros((1 + dim,) + (n,) * dim, dtype=torch.int64, device=dev)
+        st = torch.zeros(4, dtype=torch.int32, device=dev)
+        ws = None
+        if path == "tiled":
+            ws = torch.empty(mpm.mpm_isplit_workspace_bytes(dim, n, np_), dtype=torch.uint8, device=dev)
+        say("isplit limits", dim, n, path)
+        mpm.mpm_p2g_isplit(dim, n, X, m, v, C, None, 1000, 1000, 1000, g, st, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(g.cpu().numpy(), ref), path
+        assert st.cpu().numpy().view(np.uint32).tolist() == [0, 0, 0, 0]
