@@ -16,7 +16,9 @@
  *  - "particle to grid transfer in checked integer arithmetic" (integerc.dev),
  *    sections "integers do not care about order" and "the program": the
  *    integer split of a quantity between near and far nodes, done along x and
- *    then along y, and the bounds line run before any scatter.
+ *    then along y, and the bounds line run before any scatter; section "what
+ *    is not claimed": quadratic weights and the affine term as further splits
+ *    of the same kind (the integer-split quadratic APIC transfer below).
  *  - "Implementation -- GPU Optimization & Reference Codebases" (vocaro.com),
  *    section 1 (the four-phase step reset -> P2G -> grid update -> G2P),
  *    section 2.1 (fixed-point accumulation, tiles), section 3.1 (APIC
