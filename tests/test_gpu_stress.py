@@ -153,3 +153,57 @@ def test_elastic_substeps_match_oracle(mpm, oracle_lib):
     # the cube has hit the floor and is deforming: some particles are compressed
     J = np.linalg.det(parts.F.cpu().numpy().reshape(3, 3, -1).transpose(2, 0, 1))
     assert J.min() < 0.999 and np.all(J > 0)
+
+
+@pytest.mark.timeout(900)
+def test_elastic_full_size_checked_substeps(mpm, oracle_lib):
+    """The benchmark's elastic workload at full size (8M-particle jelly cube,
+    256^3 nodes): 12 substeps on the GPU; substeps 6 and 12 are recomputed by
+    the oracle from the GPU state before them: C' within one float32 ulp, and
+    given the GPU's C', the P2G grid, the particles and F bit-exact."""
+    from material_point_particle_amd.transfer import ElasticParticles, Transfer
+    w = WORKLOADS["jelly_3d_256"]
+    ex = w.extra
+    host = build(w)
+    vol = host["vol"]
+    parts = ElasticParticles(host, host["F"], vol)
+    del host
+    rng = (w.max_mass, w.max_speed, w.max_affine)
+    tr = Transfer(w.dim, w.n, w.frac_bits, rng, parts.n)
+    for k in range(1, 13):
+        check = k in (6, 12)
+        if check:
+            torch.cuda.synchronize()
+            before = parts.host()
+        parts.stress(tr, ex["dt"], ex["mu"], ex["lam"])
+        tr.bin(parts.affine())
+        tr.p2g(parts.affine(), binned=True)
+        if check:
+            torch.cuda.synchronize()
+            c_aff = parts.C_aff.cpu().numpy()
+            grid = tr.grid.cpu().numpy()
+        tr.grid_update(ex["dt"], ex["gravity"], ex["sticky"], active=True)
+        tr.g2p(parts, ex["dt"])
+        parts.update_F(tr, ex["dt"])
+        if not check:
+            continue
+        torch.cuda.synchronize()
+        after = parts.host()
+        say("elastic full size, substep", k)
+        ref_c, _ = oracle_lib.neohookean_affine(3, w.n, before, before["F"], vol, ex["dt"], ex["mu"], ex["lam"])
+        assert_close_ulp(c_aff, ref_c, f"C' at substep {k}")
+        del ref_c
+        st = {"x": before["x"], "v": before["v"], "C": c_aff, "m": before["m"]}
+        g_ref, s_ref = oracle_lib.p2g_quadratic(3, w.n, w.frac_bits, st, rng)
+        assert np.array_equal(grid, g_ref), f"P2G grid at substep {k}"
+        assert s_ref.tolist() == [0, 0, 0, 0]
+        del grid
+        vg = oracle_lib.grid_update(3, w.n, g_ref, ex["dt"], ex["gravity"], ex["sticky"])
+        del g_ref
+        st = {"x": before["x"].copy(), "v": before["v"].copy(), "C": before["C"].copy(), "m": before["m"]}
+        oracle_lib.g2p(3, w.n, vg, st, ex["dt"])
+        F_ref = before["F"].copy()
+        oracle_lib.update_F(3, st["C"], F_ref, ex["dt"])
+        for key in ("x", "v", "C"):
+            assert np.array_equal(after[key], st[key]), f"{key} at substep {k}"
+        assert np.array_equal(after["F"], F_ref), f"F at substep {k}"
