@@ -255,6 +255,64 @@ int mpm_p2g_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const i
  * Errors: MPM_ERR_INVALID. */
 int mpm_isplit_workspace_bytes(int32_t dim, int32_t n, int64_t np, size_t *bytes);
 
+/* ---- Resident substep: the particle state kept in the binned records ----
+ *
+ * "Implementation -- GPU Optimization & Reference Codebases", section 2.1:
+ * one kernel per tile slice applies the grid update while it loads the
+ * tile's node block with its halo, gathers and advects the slice's
+ * particles, and scatters them into the next grid through the on-chip block.
+ * The state lives in the workspace between substeps; a substep reads grid k
+ * and writes grid k+1 (two grid buffers used in turn, each with a byte per
+ * 4^dim-node tile that flags the node tiles written into it), and the grid
+ * just read is cleared afterwards.  Results are identical to the separate
+ * steps (binning, mpm_p2g, mpm_grid_update, mpm_g2p).  A loop:
+ *
+ *   mpm_bin_resident(ws <- particles); mpm_g2p2g(grid_in = NULL -> A, flags A)
+ *   per substep: mpm_g2p2g(A -> B, flags B); mpm_grid_clear_tiles(A, flags A);
+ *                swap A and B
+ *   to re-bin (particles drift out of their tiles) or to read the state:
+ *                mpm_gather_records(ws -> particles), then mpm_bin_resident
+ */
+
+/* Binning as mpm_bin_particles, keeping every record as it is (no range
+ * check: mpm_g2p2g checks the declared ranges at every deposit).  Particles
+ * whose stencil leaves the grid are not binned and are counted in status[0].
+ * particles, status: device.  ws: device, 256-byte aligned, ws_bytes >=
+ * mpm_workspace_bytes(n).  Errors: MPM_ERR_INVALID, MPM_ERR_WORKSPACE,
+ * MPM_ERR_HIP. */
+int mpm_bin_resident(const mpm_grid_desc *grid, const mpm_particles *particles, void *ws, size_t ws_bytes,
+                     uint32_t *status, hipStream_t stream);
+
+/* One fused substep over the records of a resident binning of n_particles.
+ * grid_in != NULL: the grid update of grid_in (as mpm_grid_update: v = P/M
+ * + dt g, sticky walls, M = 0 -> 0) feeds the APIC gather and advection of
+ * every record (as mpm_g2p, clamps counted in status[2]), written back in
+ * place; then the updated records are deposited into grid_out (as mpm_p2g,
+ * with the declared ranges checked here: records outside them add nothing
+ * and are counted in status[1]).  grid_in is only read.  grid_in == NULL: the
+ * records are deposited as they are.  Records that left their tile since the
+ * binning deposit with global atomics, so the result does not depend on
+ * when the caller re-bins.  grid_out must be zero on entry; every node tile
+ * it writes is flagged (set to 1) in tiles_out, uint8[(n/4)^dim], for
+ * mpm_grid_clear_tiles.  All pointers device; grid_in and grid_out distinct.
+ * Errors: MPM_ERR_INVALID, MPM_ERR_OVERFLOW (bounds for n_particles and the
+ * ranges, as mpm_check_bounds), MPM_ERR_HIP. */
+int mpm_g2p2g(const mpm_grid_desc *grid, const mpm_ranges *ranges, void *ws, int64_t n_particles,
+              const int64_t *grid_in, int64_t *grid_out, uint8_t *tiles_out, float dt, const float *gravity,
+              int32_t sticky, uint32_t *status, hipStream_t stream);
+
+/* Zeroes every node of the node tiles flagged in tiles (uint8[(n/4)^dim]),
+ * in every channel of grid, then clears the flags.  Errors: MPM_ERR_INVALID,
+ * MPM_ERR_HIP. */
+int mpm_grid_clear_tiles(const mpm_grid_desc *grid, int64_t *grid_io, uint8_t *tiles, hipStream_t stream);
+
+/* Copies x, v and C of every binned particle from its record back to the
+ * caller's arrays (particles->n must be the count the workspace was binned
+ * with; m and particles that were not binned are left as they are).
+ * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
+int mpm_gather_records(const mpm_grid_desc *grid, const void *ws, const mpm_particles *particles,
+                       hipStream_t stream);
+
 /* Grid update with consume-and-zero ("Implementation -- GPU Optimization &
  * Reference Codebases", section 1 four-phase step; section 2.1 and rule 4
  * of section 5: each accumulator has one reader, which zeroes it; rule 1:

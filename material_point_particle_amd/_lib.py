@@ -49,7 +49,8 @@ class mpm_ws_layout(ct.Structure):
 
 EXPORTS = ("mpm_version", "mpm_strerror", "mpm_check_bounds", "mpm_workspace_bytes", "mpm_workspace_layout",
            "mpm_bin_particles", "mpm_p2g", "mpm_p2g_cic_split", "mpm_p2g_isplit", "mpm_isplit_workspace_bytes",
-           "mpm_grid_update", "mpm_grid_clear", "mpm_g2p", "mpm_neohookean_affine", "mpm_update_deformation")
+           "mpm_grid_update", "mpm_grid_clear", "mpm_g2p", "mpm_neohookean_affine", "mpm_update_deformation",
+           "mpm_bin_resident", "mpm_g2p2g", "mpm_grid_clear_tiles", "mpm_gather_records")
 
 _lib = None
 
@@ -100,6 +101,16 @@ def lib() -> ct.CDLL:
                                             ct.c_float, ct.c_float, ct.c_void_p, ct.c_void_p, ct.c_void_p]
         L.mpm_update_deformation.restype = ct.c_int
         L.mpm_update_deformation.argtypes = [P(mpm_grid_desc), P(mpm_particles), ct.c_void_p, ct.c_float, ct.c_void_p]
+        L.mpm_bin_resident.restype = ct.c_int
+        L.mpm_bin_resident.argtypes = [P(mpm_grid_desc), P(mpm_particles), ct.c_void_p, ct.c_size_t, ct.c_void_p,
+                                       ct.c_void_p]
+        L.mpm_g2p2g.restype = ct.c_int
+        L.mpm_g2p2g.argtypes = [P(mpm_grid_desc), P(mpm_ranges), ct.c_void_p, ct.c_int64, ct.c_void_p, ct.c_void_p,
+                                ct.c_void_p, ct.c_float, P(ct.c_float), ct.c_int32, ct.c_void_p, ct.c_void_p]
+        L.mpm_grid_clear_tiles.restype = ct.c_int
+        L.mpm_grid_clear_tiles.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p]
+        L.mpm_gather_records.restype = ct.c_int
+        L.mpm_gather_records.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_void_p]
         _lib = L
     return _lib
 
@@ -198,6 +209,28 @@ def mpm_p2g_isplit(dim: int, n: int, X, m, v, C, order, max_mass: int, max_speed
     _check(lib().mpm_p2g_isplit(dim, n, m.numel(), _ptr(X), _ptr(m), _ptr(v), _ptr(C), _ptr(order), max_mass,
                                 max_speed, max_affine, _ptr(workspace), ws_bytes, _ptr(grid), _ptr(status),
                                 _stream(stream)), "mpm_p2g_isplit")
+
+
+def mpm_bin_resident(desc, parts: mpm_particles, ws, status, stream=None) -> None:
+    _check(lib().mpm_bin_resident(ct.byref(desc), ct.byref(parts), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _ptr(status), _stream(stream)), "mpm_bin_resident")
+
+
+def mpm_g2p2g(desc, rng: mpm_ranges, ws, n_particles: int, grid_in, grid_out, tiles_out, dt: float, gravity,
+              sticky: int, status, stream=None) -> None:
+    g = (ct.c_float * 3)(*(list(gravity) + [0.0] * (3 - len(gravity))))
+    _check(lib().mpm_g2p2g(ct.byref(desc), ct.byref(rng), _ptr(ws), n_particles, _ptr(grid_in), _ptr(grid_out),
+                           _ptr(tiles_out), dt, g, sticky, _ptr(status), _stream(stream)), "mpm_g2p2g")
+
+
+def mpm_grid_clear_tiles(desc, grid, tiles, stream=None) -> None:
+    _check(lib().mpm_grid_clear_tiles(ct.byref(desc), _ptr(grid), _ptr(tiles), _stream(stream)),
+           "mpm_grid_clear_tiles")
+
+
+def mpm_gather_records(desc, ws, parts: mpm_particles, stream=None) -> None:
+    _check(lib().mpm_gather_records(ct.byref(desc), _ptr(ws), ct.byref(parts), _stream(stream)),
+           "mpm_gather_records")
 
 
 def mpm_grid_update(desc, bins, grid, vg, dt: float, gravity, sticky: int, stream=None) -> None:

@@ -251,6 +251,66 @@ int mpm_bin_particles(const mpm_grid_desc *grid, const mpm_particles *particles,
     return hip_status(launch_bin(grid->dim, grid->n, f, ranges_f(ranges), b, status, stream));
 }
 
+int mpm_bin_resident(const mpm_grid_desc *grid, const mpm_particles *particles, void *ws, size_t ws_bytes,
+                     uint32_t *status, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_desc(grid)) != MPM_OK || (rc = check_particles(grid, particles, true, true)) != MPM_OK)
+        return rc;
+    if (!aligned(ws, 256) || !aligned(status, 4))
+        return MPM_ERR_INVALID;
+    mpm_ws_layout l;
+    make_layout(grid, particles->n, &l);
+    if (ws_bytes < l.total_bytes)
+        return MPM_ERR_WORKSPACE;
+    const BinView b = bin_view(ws, l);
+    Fields f{ particles->x, particles->v, particles->C, particles->m, particles->n };
+    const RangesF none{ 0.0f, 0.0f, 0.0f };
+    return hip_status(launch_bin(grid->dim, grid->n, f, none, b, status, stream, true));
+}
+
+int mpm_g2p2g(const mpm_grid_desc *grid, const mpm_ranges *ranges, void *ws, int64_t n_particles,
+              const int64_t *grid_in, int64_t *grid_out, uint8_t *tiles_out, float dt, const float *gravity,
+              int32_t sticky, uint32_t *status, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_desc(grid)) != MPM_OK || (rc = check_ranges(ranges)) != MPM_OK)
+        return rc;
+    if (n_particles < 0 || n_particles > kMaxParticles || !aligned(ws, 256) || !aligned(grid_out, 8) ||
+        !aligned(tiles_out, 4) || !aligned(status, 4) || (grid_in && !aligned(grid_in, 8)) || grid_in == grid_out)
+        return MPM_ERR_INVALID;
+    if (grid_in && (!gravity || sticky < 0 || sticky > grid->n / 2 || !(dt >= 0.0f)))
+        return MPM_ERR_INVALID;
+    if ((rc = mpm_check_bounds(grid, n_particles, ranges, nullptr)) != MPM_OK)
+        return rc;
+    mpm_ws_layout l;
+    make_layout(grid, n_particles, &l);
+    const float g3[3] = { gravity ? gravity[0] : 0.0f, gravity ? gravity[1] : 0.0f,
+                          gravity && grid->dim == 3 ? gravity[2] : 0.0f };
+    return hip_status(launch_g2p2g(grid->dim, grid->n, grid->frac_bits, bin_view(ws, l), ranges_f(ranges), grid_in,
+                                   grid_out, tiles_out, dt, g3, sticky, status, stream));
+}
+
+int mpm_grid_clear_tiles(const mpm_grid_desc *grid, int64_t *grid_io, uint8_t *tiles, hipStream_t stream)
+{
+    if (check_desc(grid) != MPM_OK || !aligned(grid_io, 8) || !aligned(tiles, 4))
+        return MPM_ERR_INVALID;
+    return hip_status(launch_grid_clear_tiles(grid->dim, grid->n, grid_io, tiles, stream));
+}
+
+int mpm_gather_records(const mpm_grid_desc *grid, const void *ws, const mpm_particles *particles, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_desc(grid)) != MPM_OK || (rc = check_particles(grid, particles, true, false)) != MPM_OK)
+        return rc;
+    if (!aligned(ws, 256) || (particles->n > 0 && !particles->C))
+        return MPM_ERR_INVALID;
+    mpm_ws_layout l;
+    make_layout(grid, particles->n, &l);
+    return hip_status(launch_gather_records(grid->dim, particles->n, bin_view((void *)ws, l), particles->x,
+                                            particles->v, particles->C, stream));
+}
+
 int mpm_p2g(const mpm_grid_desc *grid, const mpm_particles *particles, const mpm_ranges *ranges, const void *bins,
             int64_t *grid_out, uint32_t *status, hipStream_t stream)
 {

@@ -388,8 +388,9 @@ __device__ __forceinline__ void load_record(const Fields &f, int64_t p, float *r
 }
 
 // Range check and destination of one loaded record: its index in the binned
-// copy, or kEmpty when the particle is not binned.
-template <int DIM>
+// copy, or kEmpty when the particle is not binned.  KEEP: no range check (the
+// record is copied as it is; the fused substep checks the ranges itself).
+template <int DIM, bool KEEP>
 __device__ __forceinline__ uint32_t place_record(const Fields &f, RangesF r, float nf, float dx, float last_base,
                                                  int ntx, int64_t p, float *rec,
                                                  const uint32_t *__restrict__ rank_in,
@@ -403,18 +404,20 @@ __device__ __forceinline__ uint32_t place_record(const Fields &f, RangesF r, flo
         slot_out[p] = kEmpty;
         return kEmpty;
     }
-    bool rng = fabsf(rec[2 * DIM + DIM * DIM]) <= r.max_mass;
+    if constexpr (!KEEP) {
+        bool rng = fabsf(rec[2 * DIM + DIM * DIM]) <= r.max_mass;
 #pragma unroll
-    for (int e = 0; e < DIM; ++e)
-        rng = rng && fabsf(rec[DIM + e]) <= r.max_speed;
+        for (int e = 0; e < DIM; ++e)
+            rng = rng && fabsf(rec[DIM + e]) <= r.max_speed;
 #pragma unroll
-    for (int q = 0; q < DIM * DIM; ++q)
-        rng = rng && fabsf(rec[2 * DIM + q]) <= r.max_affine;
-    wave_count(!rng, &status[1]);
-    if (!rng) {
+        for (int q = 0; q < DIM * DIM; ++q)
+            rng = rng && fabsf(rec[2 * DIM + q]) <= r.max_affine;
+        wave_count(!rng, &status[1]);
+        if (!rng) {
 #pragma unroll
-        for (int q = DIM; q < R; ++q)
-            rec[q] = 0.0f;
+            for (int q = DIM; q < R; ++q)
+                rec[q] = 0.0f;
+        }
     }
     const uint32_t pos = tile_start[t] + __builtin_nontemporal_load(&rank_in[p]);
     __builtin_nontemporal_store(pos, &slot_out[p]);
@@ -470,7 +473,7 @@ __device__ __forceinline__ void write_records(const float *rec, uint32_t pos, fl
     }
 }
 
-template <int DIM>
+template <int DIM, bool KEEP>
 __global__ void __launch_bounds__(kBinThreads) bin_scatter_kernel(Fields f, RangesF r, float nf, float dx,
                                                                    float last_base, int ntx, int64_t chunks, int per,
                                                                    const uint32_t *__restrict__ rank_in,
@@ -500,10 +503,10 @@ __global__ void __launch_bounds__(kBinThreads) bin_scatter_kernel(Fields f, Rang
                 load_record<DIM>(f, pb, rb);
             uint32_t da = kEmpty, db = kEmpty;
             if (la)
-                da = place_record<DIM>(f, r, nf, dx, last_base, ntx, pa, ra, rank_in, tile_start, slot_out, cell_key,
+                da = place_record<DIM, KEEP>(f, r, nf, dx, last_base, ntx, pa, ra, rank_in, tile_start, slot_out, cell_key,
                                        status);
             if (lb)
-                db = place_record<DIM>(f, r, nf, dx, last_base, ntx, pb, rb, rank_in, tile_start, slot_out, cell_key,
+                db = place_record<DIM, KEEP>(f, r, nf, dx, last_base, ntx, pb, rb, rank_in, tile_start, slot_out, cell_key,
                                        status);
             write_records<DIM>(ra, da, my_stage, my_spos, sorted);
             write_records<DIM>(rb, db, my_stage, my_spos, sorted);
@@ -520,7 +523,8 @@ int blocks_for(int64_t work, int block)
 
 }  // namespace
 
-hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView &b, uint32_t *status, hipStream_t s)
+hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView &b, uint32_t *status, hipStream_t s,
+                      bool keep)
 {
     const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3);
     const int ntx = n / kTile;
@@ -558,14 +562,66 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
                            b.n_tiles, b.scan_tmp, b.meta, b.tile_start, items);
     }
     const unsigned sblocks = (unsigned)(chunks < (int64_t)device_cu_count() * 8 ? chunks : device_cu_count() * 8);
+    auto scatter = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(sblocks), dim3(kBinThreads), 0, s, p, r, nf, dx, last, ntx, chunks, (int)per,
+                           b.rank, b.tile_start, b.slot, b.cell_key, b.sorted, status);
+    };
     if (chunks > 0) {
         if (dim == 3)
-            hipLaunchKernelGGL(bin_scatter_kernel<3>, dim3(sblocks), dim3(kBinThreads), 0, s, p, r, nf, dx, last, ntx,
-                               chunks, (int)per, b.rank, b.tile_start, b.slot, b.cell_key, b.sorted, status);
+            keep ? scatter(bin_scatter_kernel<3, true>) : scatter(bin_scatter_kernel<3, false>);
         else
-            hipLaunchKernelGGL(bin_scatter_kernel<2>, dim3(sblocks), dim3(kBinThreads), 0, s, p, r, nf, dx, last, ntx,
-                               chunks, (int)per, b.rank, b.tile_start, b.slot, b.cell_key, b.sorted, status);
+            keep ? scatter(bin_scatter_kernel<2, true>) : scatter(bin_scatter_kernel<2, false>);
     }
+    return hipGetLastError();
+}
+
+namespace {
+
+// Copies each binned particle's x, v and C from its record back to the
+// caller's component-major arrays (m is never changed by a substep).
+template <int DIM>
+__global__ void __launch_bounds__(256) gather_records_kernel(int64_t np, const uint32_t *__restrict__ slot,
+                                                             const float *__restrict__ sorted, float *__restrict__ x,
+                                                             float *__restrict__ v, float *__restrict__ C)
+{
+    constexpr int R = rec_floats<DIM>();
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t r = slot[p];
+        if (r == kEmpty)
+            continue;
+        const float4 *src = reinterpret_cast<const float4 *>(sorted + (int64_t)r * R);
+        float rec[R];
+#pragma unroll
+        for (int q = 0; q < R / 4; ++q) {
+            const float4 t = src[q];
+            rec[4 * q] = t.x;
+            rec[4 * q + 1] = t.y;
+            rec[4 * q + 2] = t.z;
+            rec[4 * q + 3] = t.w;
+        }
+#pragma unroll
+        for (int d = 0; d < DIM; ++d) {
+            x[d * np + p] = rec[d];
+            v[d * np + p] = rec[DIM + d];
+        }
+#pragma unroll
+        for (int q = 0; q < DIM * DIM; ++q)
+            C[q * np + p] = rec[2 * DIM + q];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gather_records(int dim, int64_t np, const BinView &b, float *x, float *v, float *C, hipStream_t s)
+{
+    if (np == 0)
+        return hipSuccess;
+    if (dim == 3)
+        hipLaunchKernelGGL(gather_records_kernel<3>, dim3(blocks_for(np, 256)), dim3(256), 0, s, np, b.slot, b.sorted,
+                           x, v, C);
+    else
+        hipLaunchKernelGGL(gather_records_kernel<2>, dim3(blocks_for(np, 256)), dim3(256), 0, s, np, b.slot, b.sorted,
+                           x, v, C);
     return hipGetLastError();
 }
 

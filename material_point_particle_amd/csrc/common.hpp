@@ -53,6 +53,83 @@ __device__ __forceinline__ bool axis_stencil(float x, float nf, float dx, float 
     return ok;
 }
 
+// Grid update of one node ("Implementation -- GPU Optimization & Reference
+// Codebases", section 5 rules 1 and 7): where M != 0, v = (float)((double)P /
+// (double)M) and then v + dt*g (gdt, formed once in float32); v = 0 where
+// M == 0 and on the sticky walls.
+__device__ __forceinline__ float node_velocity(int64_t M, int64_t P, float gdt, bool wall)
+{
+    float v = 0.0f;
+    if (M != 0) {
+        v = (float)((double)P / (double)M);
+        v = v + gdt;
+    }
+    return wall ? 0.0f : v;
+}
+
+// APIC gather and advection of one particle (grid-to-particle).  Over the
+// stencil in lexicographic node order (x offset outermost), with
+// w = (wx[a]*wy[b])*wz[c] and wv_d = w*vel(a, b, c, d), the per-axis offset
+// sums S[d][e][o] += wv_d; then v_d = sum_o S[d][0][o] and
+// B_de = sum_o r_e[o] S[d][e][o] (in offset order), C = B*cscale,
+// x_d + dt*v_d clamped to [lo, hi].  Returns whether a coordinate was clamped.
+template <int DIM, class Vel>
+__device__ __forceinline__ bool g2p_particle(const Axis (&ax)[DIM], const float (&x)[DIM], Vel &&vel, float dt,
+                                             float lo, float hi, float cscale, float (&vn)[DIM],
+                                             float (&Cn)[DIM * DIM], float (&xn)[DIM])
+{
+    // S[d][e][o]: sum of w * vg_d over the stencil nodes at offset o along
+    // axis e, in lexicographic node order; v and B follow from it because
+    // r_e depends on the offset along axis e only.
+    float S[DIM][DIM][3];
+#pragma unroll
+    for (int d = 0; d < DIM; ++d)
+#pragma unroll
+        for (int e = 0; e < DIM; ++e)
+#pragma unroll
+            for (int o = 0; o < 3; ++o)
+                S[d][e][o] = 0.0f;
+    const float wx[3] = { ax[0].w0, ax[0].w1, ax[0].w2 }, rx[3] = { ax[0].r0, ax[0].r1, ax[0].r2 };
+    const float wy[3] = { ax[1].w0, ax[1].w1, ax[1].w2 }, ry[3] = { ax[1].r0, ax[1].r1, ax[1].r2 };
+    float wz[3] = { 1.0f, 0.0f, 0.0f }, rz[3] = { 0.0f, 0.0f, 0.0f };
+    if constexpr (DIM == 3) {
+        wz[0] = ax[2].w0; wz[1] = ax[2].w1; wz[2] = ax[2].w2;
+        rz[0] = ax[2].r0; rz[1] = ax[2].r1; rz[2] = ax[2].r2;
+    }
+    const int nc = DIM == 3 ? 3 : 1;
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int b = 0; b < 3; ++b)
+#pragma unroll
+            for (int c = 0; c < nc; ++c) {
+                float w = wx[a] * wy[b];
+                if constexpr (DIM == 3)
+                    w = w * wz[c];
+                const int o[3] = { a, b, c };
+#pragma unroll
+                for (int d = 0; d < DIM; ++d) {
+                    const float wv = w * vel(a, b, c, d);
+#pragma unroll
+                    for (int e = 0; e < DIM; ++e)
+                        S[d][e][o[e]] = S[d][e][o[e]] + wv;
+                }
+            }
+    const float *rr[3] = { rx, ry, rz };
+    bool clamped = false;
+#pragma unroll
+    for (int d = 0; d < DIM; ++d) {
+        vn[d] = (S[d][0][0] + S[d][0][1]) + S[d][0][2];
+#pragma unroll
+        for (int e = 0; e < DIM; ++e)
+            Cn[d * DIM + e] = ((rr[e][0] * S[d][e][0] + rr[e][1] * S[d][e][1]) + rr[e][2] * S[d][e][2]) * cscale;
+        const float xa = x[d] + dt * vn[d];
+        xn[d] = fminf(fmaxf(xa, lo), hi);
+        clamped = clamped || (xn[d] != xa);
+    }
+    return clamped;
+}
+
 // Declared ranges as float32 thresholds.  The host rounds each declared
 // maximum down to the largest float not above it, so |value| <= threshold in
 // float32 decides exactly what |value| <= maximum decides in real numbers.
@@ -162,6 +239,9 @@ hipError_t launch_p2g_direct(int dim, int n, int frac_bits, const Fields &p, con
                              int64_t *grid, uint32_t *status, hipStream_t s);
 hipError_t launch_p2g_tiled(int dim, int n, int frac_bits, const BinView &b, int64_t *grid, uint32_t *status,
                             hipStream_t s);
+hipError_t launch_g2p2g(int dim, int n, int frac_bits, const BinView &b, RangesF r, const int64_t *grid_in,
+                        int64_t *grid_out, uint8_t *tiles_out, float dt, const float *gravity, int sticky,
+                        uint32_t *status, hipStream_t s);
 hipError_t launch_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32_t *vel,
                                 const uint32_t *order, int cells, int64_t *grid, uint32_t *status, hipStream_t s);
 hipError_t launch_p2g_isplit(int dim, int n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
@@ -177,10 +257,12 @@ hipError_t launch_p2g_isplit_tiled(int dim, int n, int64_t np, const int32_t *X,
                                    const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed,
                                    int64_t max_affine, void *ws, int64_t *grid, uint32_t *status, hipStream_t s);
 hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView &b, uint32_t *status,
-                      hipStream_t s);
+                      hipStream_t s, bool keep = false);
+hipError_t launch_gather_records(int dim, int64_t np, const BinView &b, float *x, float *v, float *C, hipStream_t s);
 hipError_t launch_grid_update(int dim, int n, int64_t *grid, float *vg, float dt, const float *gravity,
                               int sticky, const BinView *bins, hipStream_t s);
 hipError_t launch_grid_clear(int dim, int n, int64_t *grid, const BinView *bins, hipStream_t s);
+hipError_t launch_grid_clear_tiles(int dim, int n, int64_t *grid, uint8_t *tiles, hipStream_t s);
 hipError_t launch_neohookean_affine(int dim, int n, int64_t np, const float *F, const float *C, const float *m,
                                     const float *vol0, float dt, float mu, float lambda, float *Cout,
                                     uint32_t *status, hipStream_t s);

@@ -81,15 +81,8 @@ __global__ void __launch_bounds__(256) node_rows_kernel(int n, const uint8_t *__
                 }
                 float v[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    float vk = 0.0f;
-                    if (M[k] != 0) {
-                        vk = (float)((double)P[k] / (double)M[k]);
-                        vk = vk + gdt[d];
-                    }
-                    const bool wall = wall_row || ix0 + k < sticky || ix0 + k >= n - sticky;
-                    v[k] = wall ? 0.0f : vk;
-                }
+                for (int k = 0; k < 4; ++k)
+                    v[k] = node_velocity(M[k], P[k], gdt[d], wall_row || ix0 + k < sticky || ix0 + k >= n - sticky);
                 *reinterpret_cast<float4 *>(vg + d * nodes + i0) = make_float4(v[0], v[1], v[2], v[3]);
                 Pq[0] = make_longlong2(0, 0);
                 Pq[1] = make_longlong2(0, 0);
@@ -107,11 +100,8 @@ __global__ void __launch_bounds__(256) clear_kernel(int64_t *__restrict__ grid, 
         grid[i] = 0;
 }
 
-// One thread per particle.  Over the stencil in lexicographic node order (x
-// offset outermost), with w = (wx[a]*wy[b])*wz[c] and wv_d = w*vg_d, the
-// per-axis offset sums S[d][e][o] += wv_d; then v_d = sum_o S[d][0][o] and
-// B_de = sum_o r_e[o] S[d][e][o] (in offset order), C = B*(4 n^2), x += dt*v,
-// clamp.
+// One thread per particle: the APIC gather and advection of g2p_particle,
+// reading the grid velocity of the stencil's nodes from vg.
 template <int DIM>
 __global__ void __launch_bounds__(256) g2p_kernel(int n, float nf, float dx, float last_base,
                                                   const float *__restrict__ vg, float *__restrict__ x,
@@ -121,76 +111,31 @@ __global__ void __launch_bounds__(256) g2p_kernel(int n, float nf, float dx, flo
     const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
         Axis ax[DIM];
+        float xp[DIM];
         bool ok = true;
 #pragma unroll
-        for (int e = 0; e < DIM; ++e)
-            ok = axis_stencil(x[e * np + p], nf, dx, last_base, ax[e]) && ok;
+        for (int e = 0; e < DIM; ++e) {
+            xp[e] = x[e * np + p];
+            ok = axis_stencil(xp[e], nf, dx, last_base, ax[e]) && ok;
+        }
         wave_count(!ok, &status[0]);
         if (!ok)
             continue;
-        // S[d][e][o]: sum of w * vg_d over the stencil nodes at offset o along
-        // axis e, in lexicographic node order; v and B follow from it because
-        // r_e depends on the offset along axis e only.
-        float S[DIM][DIM][3];
-#pragma unroll
-        for (int d = 0; d < DIM; ++d)
-#pragma unroll
-            for (int e = 0; e < DIM; ++e)
-#pragma unroll
-                for (int o = 0; o < 3; ++o)
-                    S[d][e][o] = 0.0f;
-        const float wx[3] = { ax[0].w0, ax[0].w1, ax[0].w2 }, rx[3] = { ax[0].r0, ax[0].r1, ax[0].r2 };
-        const float wy[3] = { ax[1].w0, ax[1].w1, ax[1].w2 }, ry[3] = { ax[1].r0, ax[1].r1, ax[1].r2 };
-        float wz[3] = { 1.0f, 0.0f, 0.0f }, rz[3] = { 0.0f, 0.0f, 0.0f };
-        int bz = 0;
-        if constexpr (DIM == 3) {
-            wz[0] = ax[2].w0; wz[1] = ax[2].w1; wz[2] = ax[2].w2;
-            rz[0] = ax[2].r0; rz[1] = ax[2].r1; rz[2] = ax[2].r2;
-            bz = ax[2].base;
-        }
-        const int nc = DIM == 3 ? 3 : 1;
-#pragma unroll
-        for (int a = 0; a < 3; ++a)
-#pragma unroll
-            for (int b = 0; b < 3; ++b)
-#pragma unroll
-                for (int c = 0; c < nc; ++c) {
-                    float w = wx[a] * wy[b];
-                    if constexpr (DIM == 3)
-                        w = w * wz[c];
-                    const int64_t node = DIM == 3
-                        ? ((int64_t)(bz + c) * n + (ax[1].base + b)) * n + (ax[0].base + a)
-                        : (int64_t)(ax[1].base + b) * n + (ax[0].base + a);
-                    const int o[3] = { a, b, c };
-#pragma unroll
-                    for (int d = 0; d < DIM; ++d) {
-                        const float wv = w * vg[d * nodes + node];
-#pragma unroll
-                        for (int e = 0; e < DIM; ++e)
-                            S[d][e][o[e]] = S[d][e][o[e]] + wv;
-                    }
-                }
-        const float *rr[3] = { rx, ry, rz };
-        float vn[DIM];
-        float B[DIM][DIM];
-#pragma unroll
-        for (int d = 0; d < DIM; ++d) {
-            vn[d] = (S[d][0][0] + S[d][0][1]) + S[d][0][2];
-#pragma unroll
-            for (int e = 0; e < DIM; ++e)
-                B[d][e] = (rr[e][0] * S[d][e][0] + rr[e][1] * S[d][e][1]) + rr[e][2] * S[d][e][2];
-        }
-        bool clamped = false;
+        const int bz = DIM == 3 ? ax[DIM - 1].base : 0;
+        auto vel = [&](int a, int b, int c, int d) {
+            const int64_t node = DIM == 3 ? ((int64_t)(bz + c) * n + (ax[1].base + b)) * n + (ax[0].base + a)
+                                          : (int64_t)(ax[1].base + b) * n + (ax[0].base + a);
+            return vg[d * nodes + node];
+        };
+        float vn[DIM], Cn[DIM * DIM], xn[DIM];
+        const bool clamped = g2p_particle<DIM>(ax, xp, vel, dt, lo, hi, cscale, vn, Cn, xn);
 #pragma unroll
         for (int d = 0; d < DIM; ++d) {
 #pragma unroll
             for (int e = 0; e < DIM; ++e)
-                C[(int64_t)(d * DIM + e) * np + p] = B[d][e] * cscale;
+                C[(int64_t)(d * DIM + e) * np + p] = Cn[d * DIM + e];
             v[d * np + p] = vn[d];
-            const float xn = x[d * np + p] + dt * vn[d];
-            const float xc = fminf(fmaxf(xn, lo), hi);
-            clamped = clamped || (xc != xn);
-            x[d * np + p] = xc;
+            x[d * np + p] = xn[d];
         }
         wave_count(clamped, &status[2]);
     }
@@ -256,6 +201,26 @@ hipError_t launch_grid_clear(int dim, int n, int64_t *grid, const BinView *bins,
         hipLaunchKernelGGL(clear_kernel, dim3(blocks_for((1 + dim) * nodes, 256)), dim3(256), 0, s, grid,
                            (int64_t)(1 + dim) * nodes);
     }
+    return hipGetLastError();
+}
+
+namespace {
+
+__global__ void __launch_bounds__(256) zero_bytes_kernel(uint8_t *__restrict__ a, int64_t count)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+        a[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_grid_clear_tiles(int dim, int n, int64_t *grid, uint8_t *tiles, hipStream_t s)
+{
+    const float g[3] = { 0.0f, 0.0f, 0.0f };
+    node_rows<0>(dim, n, tiles, grid, nullptr, 0.0f, g, 0, s);
+    const int64_t n_tiles = dim == 3 ? (int64_t)(n / kTile) * (n / kTile) * (n / kTile)
+                                     : (int64_t)(n / kTile) * (n / kTile);
+    hipLaunchKernelGGL(zero_bytes_kernel, dim3(blocks_for(n_tiles, 256)), dim3(256), 0, s, tiles, n_tiles);
     return hipGetLastError();
 }
 

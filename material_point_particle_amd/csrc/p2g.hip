@@ -113,6 +113,37 @@ __device__ __forceinline__ void atomic_add_i64(int64_t *addr, int64_t v)
     atomicAdd(reinterpret_cast<unsigned long long *>(addr), (unsigned long long)v);
 }
 
+// Every contribution of one hoisted particle to the grid, one 64-bit global
+// atomic each.
+template <int DIM>
+__device__ __forceinline__ void deposit_direct(const Hoisted<DIM> &h, int n, int64_t nodes, int64_t *__restrict__ grid)
+{
+    const int nc = DIM == 3 ? 3 : 1;
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int b = 0; b < 3; ++b)
+#pragma unroll
+            for (int c = 0; c < nc; ++c) {
+                float wmS = h.mwxy[a][b];
+                int64_t node;
+                if constexpr (DIM == 3) {
+                    wmS = wmS * h.wz[c];
+                    node = ((int64_t)(h.base[2] + c) * n + (h.base[1] + b)) * n + (h.base[0] + a);
+                } else {
+                    node = (int64_t)(h.base[1] + b) * n + (h.base[0] + a);
+                }
+                atomic_add_i64(&grid[node], (int64_t)rintf(wmS));
+#pragma unroll
+                for (int d = 0; d < DIM; ++d) {
+                    float u = h.t2[d][a][b];
+                    if constexpr (DIM == 3)
+                        u = u + h.cz[d][c];
+                    atomic_add_i64(&grid[(1 + d) * nodes + node], (int64_t)rintf(wmS * u));
+                }
+            }
+}
+
 // ---------------------------------------------------------------------------
 // Direct path: one thread per particle, 64-bit global atomics per
 // contribution.  No binning needed; the baseline the tiled path is measured
@@ -140,30 +171,7 @@ __global__ void __launch_bounds__(256) p2g_direct_kernel(Fields f, const uint32_
         wave_count(dom && !rng, &status[1]);
         if (!rng)
             continue;
-        const int nc = DIM == 3 ? 3 : 1;
-#pragma unroll
-        for (int a = 0; a < 3; ++a)
-#pragma unroll
-            for (int b = 0; b < 3; ++b)
-#pragma unroll
-                for (int c = 0; c < nc; ++c) {
-                    float wmS = h.mwxy[a][b];
-                    int64_t node;
-                    if constexpr (DIM == 3) {
-                        wmS = wmS * h.wz[c];
-                        node = ((int64_t)(h.base[2] + c) * n + (h.base[1] + b)) * n + (h.base[0] + a);
-                    } else {
-                        node = (int64_t)(h.base[1] + b) * n + (h.base[0] + a);
-                    }
-                    atomic_add_i64(&grid[node], (int64_t)rintf(wmS));
-#pragma unroll
-                    for (int d = 0; d < DIM; ++d) {
-                        float u = h.t2[d][a][b];
-                        if constexpr (DIM == 3)
-                            u = u + h.cz[d][c];
-                        atomic_add_i64(&grid[(1 + d) * nodes + node], (int64_t)rintf(wmS * u));
-                    }
-                }
+        deposit_direct<DIM>(h, n, nodes, grid);
     }
 }
 
@@ -316,6 +324,9 @@ __device__ __forceinline__ void load_keys(const uint8_t *__restrict__ keys, uint
 
 // `kw` holds the slice's keys as load_keys left them; cnt must be zero on
 // entry (all 2 kWave slots), and the call leaves it so for the next item.
+// STRAYS: a key of kWave or more marks a record outside the tile, which gets
+// no group (its entry goes to the spare entry).
+template <bool STRAYS>
 __device__ __forceinline__ uint32_t sort_item(const uint32_t kw[kKeyWords], uint32_t first, uint32_t count,
                                               uint16_t *ent, uint16_t *gpos, uint32_t *cnt, uint32_t *cgs,
                                               uint32_t *rep, int lane)
@@ -336,7 +347,9 @@ __device__ __forceinline__ uint32_t sort_item(const uint32_t kw[kKeyWords], uint
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const uint32_t s = 4u * (uint32_t)(k * kWave + lane) + (uint32_t)b - off;
-            const uint32_t key = s < count ? (kw[k] >> (8 * b)) & 0xFFu : kWave + (uint32_t)lane;
+            const uint32_t byte = (kw[k] >> (8 * b)) & 0xFFu;
+            const bool live = s < count && (!STRAYS || byte < (uint32_t)kWave);
+            const uint32_t key = live ? byte : kWave + (uint32_t)lane;
             rk[k][b] = atomicAdd(&cnt[key], 1u);
             rep[key] = s;
         }
@@ -372,10 +385,13 @@ __device__ __forceinline__ uint32_t sort_item(const uint32_t kw[kKeyWords], uint
         if (k >= rounds)
             continue;
         uint32_t g4[4];
+        bool live[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const uint32_t s = 4u * (uint32_t)(k * kWave + lane) + (uint32_t)b - off;
-            g4[b] = s < count ? cgs[(kw[k] >> (8 * b)) & 0xFFu] + rk[k][b] / kGroup : 0u;
+            const uint32_t byte = (kw[k] >> (8 * b)) & 0xFFu;
+            live[b] = s < count && (!STRAYS || byte < (uint32_t)kWave);
+            g4[b] = live[b] ? cgs[byte] + rk[k][b] / kGroup : 0u;
         }
         uint32_t p4[4];
 #pragma unroll
@@ -385,11 +401,150 @@ __device__ __forceinline__ uint32_t sort_item(const uint32_t kw[kKeyWords], uint
         for (int b = 0; b < 4; ++b) {
             const uint32_t s = 4u * (uint32_t)(k * kWave + lane) + (uint32_t)b - off;
             const uint32_t e = kGroup * p4[b] + rk[k][b] % kGroup;
-            ent[s < count ? e : kTrashEntry] = (uint16_t)s;
+            ent[live[b] ? e : kTrashEntry] = (uint16_t)s;
         }
     }
     __syncthreads();
     return groups;
+}
+
+// Range check of one binned record (x, v, C, m): the declared ranges as at
+// binning.
+template <int DIM>
+__device__ __forceinline__ bool record_in_ranges(const float *rec, RangesF r)
+{
+    bool ok = fabsf(rec[2 * DIM + DIM * DIM]) <= r.max_mass;
+#pragma unroll
+    for (int e = 0; e < DIM; ++e)
+        ok = ok && fabsf(rec[DIM + e]) <= r.max_speed;
+#pragma unroll
+    for (int q = 0; q < DIM * DIM; ++q)
+        ok = ok && fabsf(rec[2 * DIM + q]) <= r.max_affine;
+    return ok;
+}
+
+// The rows of one work item: per lane and row, the group's kGroup records
+// (entries ent, offsets from `first`), their quantised contributions summed
+// per node and channel in float64 registers and added to the node block acc
+// with one LDS atomic.  CHECK: records are range-checked here (out-of-range
+// records add nothing and are counted in status[1]).
+template <int DIM, bool CHECK>
+__device__ __forceinline__ void item_rows(const TiledArgs &a, RangesF r, uint32_t first, uint32_t rows,
+                                          uint32_t groups, const uint16_t *ent, double *acc, const int (&torg)[3],
+                                          int lane)
+{
+    using TS = TileShape<DIM>;
+    constexpr int R = rec_floats<DIM>();
+    constexpr int G = kGroup;
+    uint32_t bad = 0;
+    static_assert(kGroup == 4, "a group's entries load as one 8-byte word");
+    for (uint32_t j = 0; j < rows; ++j) {
+        // this lane's group in row j is group 64 j + lane of the item
+        if (j * kWave + (uint32_t)lane >= groups)
+            continue;
+        const uint2 w2 = *reinterpret_cast<const uint2 *>(&ent[(j * kWave + lane) * kGroup]);
+        const uint32_t e4[G] = { w2.x & 0xFFFFu, w2.x >> 16, w2.y & 0xFFFFu, w2.y >> 16 };
+        GroupHoist<DIM> h[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const float4 *src =
+                reinterpret_cast<const float4 *>(a.sorted + (int64_t)(first + (e4[k] & ~(uint32_t)kPad16)) * R);
+            float rec[R];
+#pragma unroll
+            for (int q = 0; q < R / 4; ++q) {
+                const float4 t = src[q];
+                rec[4 * q] = t.x;
+                rec[4 * q + 1] = t.y;
+                rec[4 * q + 2] = t.z;
+                rec[4 * q + 3] = t.w;
+            }
+            const bool pad = (e4[k] & kPad16) != 0;
+            if constexpr (CHECK) {
+                // the declared ranges, checked here instead of at binning:
+                // a record outside them adds nothing and is counted once
+                if (!pad && !record_in_ranges<DIM>(rec, r)) {
+                    ++bad;
+#pragma unroll
+                    for (int q = DIM; q < R; ++q)
+                        rec[q] = 0.0f;
+                }
+            }
+            if (pad)                                     // completes the cell's group: zero mass
+                rec[2 * DIM + DIM * DIM] = 0.0f;
+            group_hoist<DIM>(rec, a.nf, a.dx, a.last_base, a.S, h[k]);
+        }
+        // every record of the group is in one cell of this tile (binning's
+        // invariant); a group that breaks it is counted and skipped
+        bool ok = true;
+#pragma unroll
+        for (int e = 0; e < DIM; ++e) {
+            ok = ok && (unsigned)(h[0].base[e] - torg[e]) < (unsigned)kTile;
+#pragma unroll
+            for (int k = 1; k < G; ++k)
+                ok = ok && h[k].base[e] == h[0].base[e];
+        }
+        if (!ok) {
+            atomicAdd(&a.status[3], 1u);
+            continue;
+        }
+        int lb;
+        if constexpr (DIM == 3)
+            lb = ((h[0].base[2] - torg[2]) * TS::side + (h[0].base[1] - torg[1])) * TS::side +
+                 (h[0].base[0] - torg[0]);
+        else
+            lb = (h[0].base[1] - torg[1]) * TS::side + (h[0].base[0] - torg[0]);
+        const int nc = DIM == 3 ? 3 : 1;
+#pragma unroll
+        for (int aa = 0; aa < 3; ++aa)
+#pragma unroll
+            for (int b = 0; b < 3; ++b) {
+                float mwxy[G], t2[G][DIM];
+#pragma unroll
+                for (int k = 0; k < G; ++k) {
+                    mwxy[k] = h[k].mwx[aa] * h[k].wy[b];
+#pragma unroll
+                    for (int d = 0; d < DIM; ++d)
+                        t2[k][d] = h[k].t1[d][aa] + h[k].cy[d][b];
+                }
+#pragma unroll
+                for (int c = 0; c < nc; ++c) {
+                    const int off = DIM == 3 ? (c * TS::side + b) * TS::side + aa : b * TS::side + aa;
+                    // The node's (1+DIM) x G contributions are independent until
+                    // the per-channel sums; they are written phase by phase
+                    // (products, rounding, widening, sums) so that the chains
+                    // interleave instead of running back to back.
+                    float wmS[G], val[1 + DIM][G];
+#pragma unroll
+                    for (int k = 0; k < G; ++k) {
+                        wmS[k] = DIM == 3 ? mwxy[k] * h[k].wz[c] : mwxy[k];
+                        val[0][k] = wmS[k];
+                    }
+#pragma unroll
+                    for (int d = 0; d < DIM; ++d)
+#pragma unroll
+                        for (int k = 0; k < G; ++k) {
+                            const float u = DIM == 3 ? t2[k][d] + h[k].cz[d][c] : t2[k][d];
+                            val[1 + d][k] = wmS[k] * u;
+                        }
+                    double q[1 + DIM][G];
+#pragma unroll
+                    for (int ch = 0; ch < 1 + DIM; ++ch)
+#pragma unroll
+                        for (int k = 0; k < G; ++k)
+                            q[ch][k] = (double)rintf(val[ch][k]);
+#pragma unroll
+                    for (int ch = 0; ch < 1 + DIM; ++ch) {
+                        // exact integer adds: a pairwise tree gives the same sum
+                        const double sum = (q[ch][0] + q[ch][1]) + (q[ch][2] + q[ch][3]);
+                        atomicAdd(&acc[ch * TS::nodes + lb + off], sum);
+                    }
+                }
+            }
+    }
+    if constexpr (CHECK) {
+        if (bad != 0u)
+            atomicAdd(&a.status[1], bad);
+    }
 }
 
 template <int DIM>
@@ -397,8 +552,6 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 p2g_tiled_kernel(TiledArgs a)
 {
     using TS = TileShape<DIM>;
-    constexpr int R = rec_floats<DIM>();
-    constexpr int G = kGroup;
     constexpr int kFlush = (TS::nodes + kWave - 1) / kWave;      // node-block entries per lane
     __shared__ double acc[TS::ch * TS::nodes];
     __shared__ __align__(16) uint16_t ent[kMaxGroups * kGroup + 4];
@@ -459,105 +612,13 @@ p2g_tiled_kernel(TiledArgs a)
                 t /= (uint32_t)a.ntx;
             }
         }
-        const uint32_t groups = sort_item(kw, first, count, ent, gpos, cnt, cgs, rep, lane);
+        const uint32_t groups = sort_item<false>(kw, first, count, ent, gpos, cnt, cgs, rep, lane);
         const uint32_t rows = (groups + kWave - 1) / kWave;
         const uint32_t item_next = __builtin_amdgcn_readfirstlane(next);
         uint4 rec_next = make_uint4(0u, 0u, 0u, 0u);
         if (item_next < n_items)
             rec_next = items[item_next];
-        static_assert(kGroup == 4, "a group's entries load as one 8-byte word");
-        for (uint32_t j = 0; j < rows; ++j) {
-            // this lane's group in row j is group 64 j + lane of the item
-            if (j * kWave + (uint32_t)lane >= groups)
-                continue;
-            const uint2 w2 = *reinterpret_cast<const uint2 *>(&ent[(j * kWave + lane) * kGroup]);
-            const uint32_t e4[G] = { w2.x & 0xFFFFu, w2.x >> 16, w2.y & 0xFFFFu, w2.y >> 16 };
-            GroupHoist<DIM> h[G];
-#pragma unroll
-            for (int k = 0; k < G; ++k) {
-                const float4 *src =
-                    reinterpret_cast<const float4 *>(a.sorted + (int64_t)(first + (e4[k] & ~(uint32_t)kPad16)) * R);
-                float rec[R];
-#pragma unroll
-                for (int q = 0; q < R / 4; ++q) {
-                    const float4 t = src[q];
-                    rec[4 * q] = t.x;
-                    rec[4 * q + 1] = t.y;
-                    rec[4 * q + 2] = t.z;
-                    rec[4 * q + 3] = t.w;
-                }
-                if (e4[k] & kPad16)                          // completes the cell's group: zero mass
-                    rec[2 * DIM + DIM * DIM] = 0.0f;
-                group_hoist<DIM>(rec, a.nf, a.dx, a.last_base, a.S, h[k]);
-            }
-            // every record of the group is in one cell of this tile (binning's
-            // invariant); a group that breaks it is counted and skipped
-            bool ok = true;
-#pragma unroll
-            for (int e = 0; e < DIM; ++e) {
-                ok = ok && (unsigned)(h[0].base[e] - torg[e]) < (unsigned)kTile;
-#pragma unroll
-                for (int k = 1; k < G; ++k)
-                    ok = ok && h[k].base[e] == h[0].base[e];
-            }
-            if (!ok) {
-                atomicAdd(&a.status[3], 1u);
-                continue;
-            }
-            int lb;
-            if constexpr (DIM == 3)
-                lb = ((h[0].base[2] - torg[2]) * TS::side + (h[0].base[1] - torg[1])) * TS::side +
-                     (h[0].base[0] - torg[0]);
-            else
-                lb = (h[0].base[1] - torg[1]) * TS::side + (h[0].base[0] - torg[0]);
-            const int nc = DIM == 3 ? 3 : 1;
-#pragma unroll
-            for (int aa = 0; aa < 3; ++aa)
-#pragma unroll
-                for (int b = 0; b < 3; ++b) {
-                    float mwxy[G], t2[G][DIM];
-#pragma unroll
-                    for (int k = 0; k < G; ++k) {
-                        mwxy[k] = h[k].mwx[aa] * h[k].wy[b];
-#pragma unroll
-                        for (int d = 0; d < DIM; ++d)
-                            t2[k][d] = h[k].t1[d][aa] + h[k].cy[d][b];
-                    }
-#pragma unroll
-                    for (int c = 0; c < nc; ++c) {
-                        const int off = DIM == 3 ? (c * TS::side + b) * TS::side + aa : b * TS::side + aa;
-                        // The node's (1+DIM) x G contributions are independent until
-                        // the per-channel sums; they are written phase by phase
-                        // (products, rounding, widening, sums) so that the chains
-                        // interleave instead of running back to back.
-                        float wmS[G], val[1 + DIM][G];
-#pragma unroll
-                        for (int k = 0; k < G; ++k) {
-                            wmS[k] = DIM == 3 ? mwxy[k] * h[k].wz[c] : mwxy[k];
-                            val[0][k] = wmS[k];
-                        }
-#pragma unroll
-                        for (int d = 0; d < DIM; ++d)
-#pragma unroll
-                            for (int k = 0; k < G; ++k) {
-                                const float u = DIM == 3 ? t2[k][d] + h[k].cz[d][c] : t2[k][d];
-                                val[1 + d][k] = wmS[k] * u;
-                            }
-                        double q[1 + DIM][G];
-#pragma unroll
-                        for (int ch = 0; ch < 1 + DIM; ++ch)
-#pragma unroll
-                            for (int k = 0; k < G; ++k)
-                                q[ch][k] = (double)rintf(val[ch][k]);
-#pragma unroll
-                        for (int ch = 0; ch < 1 + DIM; ++ch) {
-                            // exact integer adds: a pairwise tree gives the same sum
-                            const double sum = (q[ch][0] + q[ch][1]) + (q[ch][2] + q[ch][3]);
-                            atomicAdd(&acc[ch * TS::nodes + lb + off], sum);
-                        }
-                    }
-                }
-        }
+        item_rows<DIM, false>(a, RangesF{ 0.0f, 0.0f, 0.0f }, first, rows, groups, ent, acc, torg, lane);
         __syncthreads();
         item = item_next;
         rec_item = rec_next;
@@ -581,6 +642,281 @@ p2g_tiled_kernel(TiledArgs a)
                     atomic_add_i64(&a.grid[ch * nodes + node], (int64_t)val);
             }
         }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused grid-to-particle and particle-to-grid per work item ("Implementation
+// -- GPU Optimization & Reference Codebases", section 2.1: one kernel per
+// tile slice loads the tile's node block with its halo, applying the grid
+// update as it loads, gathers and updates the slice's particles, and scatters
+// them into the next grid through the on-chip block).  The particle state is
+// the binned records, updated in place.  Per item:
+//  1. the grid velocity of the (kTile+4)^dim nodes from one node below the
+//     tile to six above (every node a particle of the tile can read after
+//     drifting less than a cell) is formed from grid_in with node_velocity
+//     into LDS (sharing the node block's memory);
+//  2. each record is gathered and advected (g2p_particle, the same arithmetic
+//     as the G2P kernel; a particle whose stencil leaves that window reads
+//     grid_in directly) and written back; its cell in the new position is its
+//     key, or a stray mark when it has left the tile;
+//  3. the keys are sorted on chip as in the P2G kernel and the rows deposit
+//     the updated records into the tile's node block (range checks here, not
+//     at binning); strays deposit with global atomics;
+//  4. the block is flushed to grid_out, and every node tile this item wrote
+//     is flagged in tiles_out (for the restricted clear of that grid later).
+// With grid_in NULL only steps 2 (keys), 3 and 4 run: the deposit of the
+// records as they are.
+// ---------------------------------------------------------------------------
+struct FusedArgs {
+    TiledArgs t;               // sorted: the records; grid: grid_out
+    float *records;            // the same records, written
+    const int64_t *grid_in;    // grid velocity source, or NULL for a deposit only
+    uint8_t *tiles_out;        // node-tile flags of grid_out
+    RangesF r;
+    float dt, lo, hi, cscale;
+    float gdt[3];
+    int sticky;
+};
+
+// Flags the node tiles covering nodes [lo, lo + span) per axis.
+template <int DIM>
+__device__ __forceinline__ void flag_node_tiles(uint8_t *tiles, int ntx, const int (&lo)[3], int span)
+{
+    int t0[3] = { 0, 0, 0 }, t1[3] = { 0, 0, 0 };
+#pragma unroll
+    for (int e = 0; e < DIM; ++e) {
+        t0[e] = lo[e] / kTile;
+        t1[e] = (lo[e] + span - 1) / kTile;
+        t1[e] = t1[e] < ntx - 1 ? t1[e] : ntx - 1;
+    }
+    for (int z = t0[2]; z <= (DIM == 3 ? t1[2] : 0); ++z)
+        for (int y = t0[1]; y <= t1[1]; ++y)
+            for (int x = t0[0]; x <= t1[0]; ++x)
+                tiles[((int64_t)z * ntx + y) * ntx + x] = 1;
+}
+
+template <int DIM>
+__global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+g2p2g_kernel(FusedArgs f)
+{
+    using TS = TileShape<DIM>;
+    constexpr int R = rec_floats<DIM>();
+    constexpr int W = kTile + 4;                                     // velocity window edge
+    constexpr int WN = DIM == 3 ? W * W * W : W * W;
+    constexpr int kFlush = (TS::nodes + kWave - 1) / kWave;
+    static_assert(DIM * WN * sizeof(float) <= TS::ch * TS::nodes * sizeof(double),
+                  "the velocity window fits in the node block's memory");
+    __shared__ double acc[TS::ch * TS::nodes];                      // velocity window, then the node block
+    __shared__ __align__(16) uint16_t ent[kMaxGroups * kGroup + 4];
+    __shared__ uint16_t gpos[kMaxGroups];
+    __shared__ uint32_t cnt[2 * kWave], cgs[kWave], rep[2 * kWave];
+    __shared__ __align__(4) uint8_t keys[kKeyWords * kWave * 4];
+    __shared__ uint16_t strays[slice_records<DIM>()];
+    __shared__ uint32_t n_strays;
+    static_assert(slice_records<DIM>() <= kKeyWords * kWave * 4, "a slice's keys fit the key buffer");
+    const TiledArgs &a = f.t;
+    float *vw = reinterpret_cast<float *>(acc);
+    const int lane = threadIdx.x;
+    const uint32_t n_items = a.meta[0];
+    const int n = a.n;
+    const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    int fx[kFlush], fy[kFlush], fz[kFlush];
+#pragma unroll
+    for (int m = 0; m < kFlush; ++m) {
+        const int i = lane + kWave * m;
+        fx[m] = i % TS::side;
+        fy[m] = (i / TS::side) % TS::side;
+        fz[m] = DIM == 3 ? i / (TS::side * TS::side) : 0;
+    }
+    for (int i = lane; i < TS::ch * TS::nodes; i += kWave)
+        acc[i] = 0.0;
+    cnt[lane] = 0u;
+    cnt[kWave + lane] = 0u;
+    __syncthreads();
+    const uint4 *items = reinterpret_cast<const uint4 *>(a.items);
+    for (;;) {
+        uint32_t next = 0;
+        if (lane == 0)
+            next = atomicAdd(a.cursor, 1u);
+        const uint32_t item = __builtin_amdgcn_readfirstlane(next);
+        if (item >= n_items)
+            break;
+        const uint4 it = items[item];
+        const uint32_t tile = it.x, first = it.y, count = it.z;
+        int torg[3] = { 0, 0, 0 };
+        {
+            uint32_t t = tile;
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                torg[e] = (int)(t % (uint32_t)a.ntx) * kTile;
+                t /= (uint32_t)a.ntx;
+            }
+        }
+        // 1. grid velocity of the window (its origin one node below the tile)
+        if (f.grid_in) {
+            for (int i = lane; i < WN; i += kWave) {
+                const int l[3] = { i % W, (i / W) % W, DIM == 3 ? i / (W * W) : 0 };
+                int g[3] = { 0, 0, 0 };
+                bool inside = true, wall = false;
+#pragma unroll
+                for (int e = 0; e < DIM; ++e) {
+                    g[e] = torg[e] - 1 + l[e];
+                    inside = inside && g[e] >= 0 && g[e] < n;
+                    wall = wall || g[e] < f.sticky || g[e] >= n - f.sticky;
+                }
+                const int64_t node = DIM == 3 ? ((int64_t)g[2] * n + g[1]) * n + g[0] : (int64_t)g[1] * n + g[0];
+                const int64_t M = inside ? f.grid_in[node] : 0;
+#pragma unroll
+                for (int d = 0; d < DIM; ++d) {
+                    const int64_t P = (inside && M != 0) ? f.grid_in[(1 + d) * nodes + node] : 0;
+                    vw[d * WN + i] = node_velocity(M, P, f.gdt[d], wall);
+                }
+            }
+        }
+        if (lane == 0)
+            n_strays = 0u;
+        __syncthreads();
+        // 2. gather and advect each record (with grid_in), then its key
+        uint32_t clamps = 0;
+        for (uint32_t i = (uint32_t)lane; i < count; i += kWave) {
+            float4 *src = reinterpret_cast<float4 *>(f.records + (int64_t)(first + i) * R);
+            float rec[R];
+#pragma unroll
+            for (int q = 0; q < R / 4; ++q) {
+                const float4 t = src[q];
+                rec[4 * q] = t.x;
+                rec[4 * q + 1] = t.y;
+                rec[4 * q + 2] = t.z;
+                rec[4 * q + 3] = t.w;
+            }
+            if (f.grid_in) {
+                Axis ax[DIM];
+                float xp[DIM];
+                bool win = true;
+                int lb[3] = { 0, 0, 0 };
+#pragma unroll
+                for (int e = 0; e < DIM; ++e) {
+                    xp[e] = rec[e];
+                    axis_stencil(xp[e], a.nf, a.dx, a.last_base, ax[e]);
+                    lb[e] = ax[e].base - (torg[e] - 1);
+                    win = win && lb[e] >= 0 && lb[e] <= W - 3;
+                }
+                auto vel = [&](int aa, int b, int c, int d) {
+                    if (win) {
+                        const int w = DIM == 3 ? ((lb[2] + c) * W + (lb[1] + b)) * W + (lb[0] + aa)
+                                               : (lb[1] + b) * W + (lb[0] + aa);
+                        return vw[d * WN + w];
+                    }
+                    const int g[3] = { ax[0].base + aa, ax[1].base + b, DIM == 3 ? ax[DIM - 1].base + c : 0 };
+                    const int64_t node = DIM == 3 ? ((int64_t)g[2] * n + g[1]) * n + g[0] : (int64_t)g[1] * n + g[0];
+                    bool wall = false;
+#pragma unroll
+                    for (int e = 0; e < DIM; ++e)
+                        wall = wall || g[e] < f.sticky || g[e] >= n - f.sticky;
+                    const int64_t M = f.grid_in[node];
+                    const int64_t P = M != 0 ? f.grid_in[(1 + d) * nodes + node] : 0;
+                    return node_velocity(M, P, f.gdt[d], wall);
+                };
+                float vn[DIM], Cn[DIM * DIM], xn[DIM];
+                clamps += g2p_particle<DIM>(ax, xp, vel, f.dt, f.lo, f.hi, f.cscale, vn, Cn, xn) ? 1u : 0u;
+#pragma unroll
+                for (int d = 0; d < DIM; ++d) {
+                    rec[d] = xn[d];
+                    rec[DIM + d] = vn[d];
+                }
+#pragma unroll
+                for (int q = 0; q < DIM * DIM; ++q)
+                    rec[2 * DIM + q] = Cn[q];
+#pragma unroll
+                for (int q = 0; q < R / 4; ++q)
+                    src[q] = make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
+            }
+            uint32_t l[DIM];
+            bool in_tile = true;
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                Axis ax;
+                axis_stencil(rec[e], a.nf, a.dx, a.last_base, ax);
+                const int d = ax.base - torg[e];
+                in_tile = in_tile && d >= 0 && d < kTile;
+                l[e] = (uint32_t)(d & (kTile - 1));
+            }
+            keys[i] = in_tile ? (uint8_t)tile_local<DIM>(l) : (uint8_t)0xFFu;
+            if (!in_tile)
+                strays[atomicAdd(&n_strays, 1u)] = (uint16_t)i;
+        }
+        if (clamps != 0u)
+            atomicAdd(&a.status[2], clamps);
+        // the records written above are read back below by other lanes
+        __threadfence();
+        __syncthreads();
+        if (f.grid_in) {                                             // the window becomes the node block
+            for (int i = lane; i < TS::ch * TS::nodes; i += kWave)
+                acc[i] = 0.0;
+            __syncthreads();
+        }
+        // 3. sort by the new cells and deposit
+        uint32_t kw[kKeyWords];
+        {
+            const uint32_t *kwords = reinterpret_cast<const uint32_t *>(keys);
+            const uint32_t n_words = (count + 3u) / 4u;
+#pragma unroll
+            for (int k = 0; k < kKeyWords; ++k) {
+                const uint32_t i = (uint32_t)(k * kWave + lane);
+                kw[k] = i < n_words ? kwords[i] : 0u;
+            }
+        }
+        const uint32_t groups = sort_item<true>(kw, 0u, count, ent, gpos, cnt, cgs, rep, lane);
+        const uint32_t rows = (groups + kWave - 1) / kWave;
+        item_rows<DIM, true>(a, f.r, first, rows, groups, ent, acc, torg, lane);
+        const uint32_t ns = n_strays;
+        uint32_t bad = 0;
+        for (uint32_t k = (uint32_t)lane; k < ns; k += kWave) {
+            const float *rec = a.sorted + (int64_t)(first + strays[k]) * R;
+            Particle<DIM> p;
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                p.x[e] = rec[e];
+                p.v[e] = rec[DIM + e];
+            }
+#pragma unroll
+            for (int q = 0; q < DIM * DIM; ++q)
+                p.C[q] = rec[2 * DIM + q];
+            p.m = rec[2 * DIM + DIM * DIM];
+            if (!in_ranges<DIM>(p, f.r)) {
+                ++bad;
+                continue;
+            }
+            Hoisted<DIM> h;
+            hoist<DIM>(p, a.nf, a.dx, a.last_base, a.S, h);
+            deposit_direct<DIM>(h, n, nodes, a.grid);
+            const int lo[3] = { h.base[0], h.base[1], DIM == 3 ? h.base[DIM - 1] : 0 };
+            flag_node_tiles<DIM>(f.tiles_out, a.ntx, lo, 3);
+        }
+        if (bad != 0u)
+            atomicAdd(&a.status[1], bad);
+        __syncthreads();
+        // 4. flush the node block; flag its node tiles
+#pragma unroll
+        for (int m = 0; m < kFlush; ++m) {
+            const int i = lane + kWave * m;
+            if (i >= TS::nodes)
+                continue;
+            const int gx = torg[0] + fx[m], gy = torg[1] + fy[m], gz = torg[2] + fz[m];
+            const bool in_grid = gx < n && gy < n && gz < n;
+            const int64_t node = DIM == 3 ? ((int64_t)gz * n + gy) * n + gx : (int64_t)gy * n + gx;
+#pragma unroll
+            for (int ch = 0; ch < TS::ch; ++ch) {
+                const double val = acc[ch * TS::nodes + i];
+                acc[ch * TS::nodes + i] = 0.0;
+                if (val != 0.0 && in_grid)
+                    atomic_add_i64(&a.grid[ch * nodes + node], (int64_t)val);
+            }
+        }
+        if (lane == 0)
+            flag_node_tiles<DIM>(f.tiles_out, a.ntx, torg, TS::side);
         __syncthreads();
     }
 }
@@ -694,6 +1030,57 @@ hipError_t launch_p2g_tiled(int dim, int n, int frac_bits, const BinView &b, int
         hipLaunchKernelGGL(p2g_tiled_kernel<3>, dim3((unsigned)blocks), dim3(kWave), 0, s, a);
     else
         hipLaunchKernelGGL(p2g_tiled_kernel<2>, dim3((unsigned)blocks), dim3(kWave), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_g2p2g(int dim, int n, int frac_bits, const BinView &b, RangesF r, const int64_t *grid_in,
+                        int64_t *grid_out, uint8_t *tiles_out, float dt, const float *gravity, int sticky,
+                        uint32_t *status, hipStream_t s)
+{
+    FusedArgs f;
+    TiledArgs &a = f.t;
+    a.sorted = b.sorted;
+    a.cell_key = b.cell_key;
+    a.items = b.items;
+    a.meta = b.meta;
+    a.cursor = b.meta + 3;
+    a.n = n;
+    a.ntx = n / kTile;
+    a.nf = (float)n;
+    a.dx = 1.0f / (float)n;
+    a.last_base = (float)(n - 3);
+    a.S = ldexpf(1.0f, frac_bits);
+    a.grid = grid_out;
+    a.status = status;
+    f.records = b.sorted;
+    f.grid_in = grid_in;
+    f.tiles_out = tiles_out;
+    f.r = r;
+    f.dt = dt;
+    f.lo = a.dx;
+    f.hi = (float)(n - 2) * a.dx;
+    f.cscale = 4.0f * (float)n * (float)n;
+    for (int d = 0; d < 3; ++d)
+        f.gdt[d] = d < dim ? dt * gravity[d] : 0.0f;
+    f.sticky = sticky;
+    hipLaunchKernelGGL(reset_cursor_kernel, dim3(1), dim3(1), 0, s, a.cursor);
+    int per_cu = 0;
+    hipError_t e;
+    if (dim == 3)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, g2p2g_kernel<3>, kWave, 0);
+    else
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, g2p2g_kernel<2>, kWave, 0);
+    if (e != hipSuccess)
+        return e;
+    int64_t blocks = (int64_t)device_cu_count() * (per_cu > 0 ? per_cu : 1);
+    if (blocks > b.max_items)
+        blocks = b.max_items;
+    if (blocks < 1)
+        blocks = 1;
+    if (dim == 3)
+        hipLaunchKernelGGL(g2p2g_kernel<3>, dim3((unsigned)blocks), dim3(kWave), 0, s, f);
+    else
+        hipLaunchKernelGGL(g2p2g_kernel<2>, dim3((unsigned)blocks), dim3(kWave), 0, s, f);
     return hipGetLastError();
 }
 

@@ -116,3 +116,47 @@ class Transfer:
 
     def meta(self) -> np.ndarray:
         return self.ws_u32("meta", 16).cpu().numpy().view(np.uint32)
+
+
+class ResidentSubsteps:
+    """The substep loop with the particle state kept in the binned records
+    (mpm_bin_resident, mpm_g2p2g, mpm_grid_clear_tiles, mpm_gather_records):
+    two grids used in turn, each with its node-tile flags.  After start(),
+    self.grid holds the deposit of the current state (the next substep's
+    P2G grid)."""
+
+    def __init__(self, tr: Transfer, parts: DeviceParticles, dt: float, gravity, sticky: int, device="cuda"):
+        self.tr, self.parts = tr, parts
+        self.dt, self.gravity, self.sticky = dt, list(gravity), sticky
+        dim, n = tr.dim, tr.n
+        self.grids = [tr.grid, torch.zeros_like(tr.grid)]
+        n_tiles = (n // 4) ** dim
+        self.tiles = [torch.zeros(n_tiles, dtype=torch.uint8, device=device) for _ in range(2)]
+        self.cur = 0
+
+    @property
+    def grid(self) -> torch.Tensor:
+        return self.grids[self.cur]
+
+    def start(self) -> None:
+        """Bin the particles and deposit them into the current grid (zeroed
+        here)."""
+        self.grids[self.cur].zero_()
+        self.tiles[self.cur].zero_()
+        self.rebin()
+        L.mpm_g2p2g(self.tr.desc, self.tr.ranges, self.tr.ws, self.parts.n, None, self.grids[self.cur],
+                    self.tiles[self.cur], self.dt, self.gravity, self.sticky, self.tr.status)
+
+    def rebin(self) -> None:
+        L.mpm_bin_resident(self.tr.desc, self.parts.desc(), self.tr.ws, self.tr.status)
+
+    def substep(self) -> None:
+        a, b = self.cur, 1 - self.cur
+        L.mpm_g2p2g(self.tr.desc, self.tr.ranges, self.tr.ws, self.parts.n, self.grids[a], self.grids[b],
+                    self.tiles[b], self.dt, self.gravity, self.sticky, self.tr.status)
+        L.mpm_grid_clear_tiles(self.tr.desc, self.grids[a], self.tiles[a])
+        self.cur = b
+
+    def gather(self) -> None:
+        """Write the records' x, v, C back to the particle arrays."""
+        L.mpm_gather_records(self.tr.desc, self.tr.ws, self.parts.desc())

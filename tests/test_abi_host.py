@@ -155,6 +155,26 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert isplit(3, 64, 10, A, A, A, A, None, 1000, 1000, 1000, (ct.c_void_p(4360), 1 << 30)) == L.MPM_ERR_INVALID
     need = M.mpm_isplit_workspace_bytes(3, 64, 10)
     assert isplit(3, 64, 10, A, A, A, A, None, 1000, 1000, 1000, (W[0], need - 1)) == L.MPM_ERR_WORKSPACE
+    # resident substep entries
+    g3 = (ct.c_float * 3)(0, -9.8, 0)
+    T = ct.c_void_p(1 << 16)
+    assert lib.mpm_g2p2g(ct.byref(d), ct.byref(r), ct.c_void_p(4096), 10, grid, grid, T, 1e-4, g3, 2, status,
+                         None) == L.MPM_ERR_INVALID                                    # grid_in == grid_out
+    assert lib.mpm_g2p2g(ct.byref(d), ct.byref(r), ct.c_void_p(4100), 10, None, grid, T, 1e-4, g3, 2, status,
+                         None) == L.MPM_ERR_INVALID                                    # misaligned workspace
+    assert lib.mpm_g2p2g(ct.byref(d), ct.byref(r), ct.c_void_p(4096), 10, ct.c_void_p(8192), grid, T, 1e-4, g3,
+                         100, status, None) == L.MPM_ERR_INVALID                       # sticky beyond n/2
+    assert lib.mpm_g2p2g(ct.byref(d), ct.byref(r), ct.c_void_p(4096), 10, ct.c_void_p(8192), grid, T, 1e-4, None,
+                         2, status, None) == L.MPM_ERR_INVALID                         # no gravity
+    assert lib.mpm_g2p2g(ct.byref(d), ct.byref(M.ranges(1e30, 1e30, 1e30)), ct.c_void_p(4096), 10, None, grid, T,
+                         1e-4, g3, 2, status, None) == L.MPM_ERR_OVERFLOW
+    assert lib.mpm_grid_clear_tiles(ct.byref(d), ct.c_void_p(4100), T, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_clear_tiles(None, grid, T, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_gather_records(ct.byref(d), ct.c_void_p(4096), ct.byref(L.mpm_particles(10, 4096, 4096, None,
+                                                                                           4096)),
+                                  None) == L.MPM_ERR_INVALID                           # no C
+    assert lib.mpm_bin_resident(ct.byref(d), ct.byref(p2), ct.c_void_p(4096), 16, status,
+                                None) == L.MPM_ERR_WORKSPACE
     g = (ct.c_float * 3)(0, -9.8, 0)
     assert lib.mpm_grid_update(ct.byref(d), None, grid, ct.c_void_p(4096), 1e-4, g, 100, None) == L.MPM_ERR_INVALID
     assert lib.mpm_grid_update(ct.byref(d), None, grid, ct.c_void_p(4096), 1e-4, None, 2, None) == L.MPM_ERR_INVALID

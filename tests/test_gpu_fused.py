@@ -1,0 +1,198 @@
+"""GPU parity of the resident substep (mpm_bin_resident, mpm_g2p2g,
+mpm_grid_clear_tiles, mpm_gather_records): the fused grid-to-particle and
+particle-to-grid kernel must give bit for bit the particle states and P2G
+grids of the separate steps and of the oracle's substeps.
+
+Cases: the dam-break recipe on 64^3 nodes in lockstep with the oracle (re-binned
+every 10 substeps); the full 8M-particle 256^3 dam-break against the separate
+GPU steps; fast clouds in 2D and 3D whose particles leave their tiles between
+re-binnings (the stray path) with some particles outside the declared ranges;
+the deposit-only call against mpm_p2g; and the flagged clear.
+"""
+import sys
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from mpm_inputs import WORKLOADS, build, scaled
+from mpm_inputs import generators as G
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-test]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def mpm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import material_point_particle_amd as M
+    M.lib()
+    return M
+
+
+def ranges_of(w):
+    return (w.max_mass, w.max_speed, w.max_affine)
+
+
+def assert_same(a, b, what):
+    if not np.array_equal(a, b):
+        diff = np.argwhere(a != b)
+        i = tuple(diff[0])
+        raise AssertionError(f"{what}: {len(diff)} entries differ; first at {i}: gpu {a[i]} ref {b[i]}")
+
+
+def oracle_substep(oracle_lib, w, state, ex):
+    """One oracle substep from `state`: (P2G grid, status, state after)."""
+    grid, st = oracle_lib.p2g_quadratic(w.dim, w.n, w.frac_bits, state, ranges_of(w))
+    g = grid.copy()
+    vg = oracle_lib.grid_update(w.dim, w.n, g, ex["dt"], ex["gravity"], ex["sticky"])
+    out = {k: v.copy() for k, v in state.items()}
+    oracle_lib.g2p(w.dim, w.n, vg, out, ex["dt"])
+    return grid, st, out
+
+
+def resident(mpm, w, host, ex):
+    from material_point_particle_amd.transfer import DeviceParticles, ResidentSubsteps, Transfer
+    parts = DeviceParticles(host)
+    tr = Transfer(w.dim, w.n, w.frac_bits, ranges_of(w), parts.n)
+    rs = ResidentSubsteps(tr, parts, ex["dt"], ex["gravity"], ex["sticky"])
+    return parts, tr, rs
+
+
+def test_lockstep_with_oracle_small(mpm, oracle_lib):
+    """Dam-break recipe, 2^16 particles on 64^3 nodes, 40 substeps re-binned
+    every 10: after every substep k in 5, 10, ..., 40 the gathered state and
+    the grid the resident loop holds (the P2G of that state) equal the
+    oracle's own trajectory."""
+    w = scaled(WORKLOADS["dam_3d_256"], 1 << 16, n=64)
+    ex = w.extra
+    host = build(w)
+    parts, tr, rs = resident(mpm, w, host, ex)
+    rs.start()
+    state = {k: v.copy() for k, v in host.items()}
+    grid0, _, _ = oracle_substep(oracle_lib, w, state, ex)
+    torch.cuda.synchronize()
+    assert_same(rs.grid.cpu().numpy(), grid0, "initial deposit")
+    for k in range(1, 41):
+        rs.substep()
+        _, _, state = oracle_substep(oracle_lib, w, state, ex)
+        if k % 5 == 0:
+            rs.gather()
+            torch.cuda.synchronize()
+            say("fused lockstep", k)
+            got = parts.host()
+            for key in ("x", "v", "C"):
+                assert_same(got[key], state[key], f"substep {k} {key}")
+            nxt, _, _ = oracle_substep(oracle_lib, w, state, ex)
+            assert_same(rs.grid.cpu().numpy(), nxt, f"grid after substep {k}")
+        if k % 10 == 0:
+            rs.rebin()
+    assert tr.status.cpu().numpy().view(np.uint32).tolist() == [0, 0, 0, 0]
+
+
+@pytest.mark.timeout(600)
+def test_full_size_matches_separate_steps(mpm):
+    """The 8M-particle 256^3 dam-break: 12 fused substeps (re-binned every 5)
+    against 12 substeps of binning, P2G, restricted grid update and G2P."""
+    from material_point_particle_amd.transfer import DeviceParticles, Transfer
+    w = WORKLOADS["dam_3d_256"]
+    ex = w.extra
+    host = build(w)
+    parts, tr, rs = resident(mpm, w, host, ex)
+    rs.start()
+    for k in range(1, 13):
+        rs.substep()
+        if k % 5 == 0:
+            rs.gather()
+            rs.rebin()
+    rs.gather()
+    p2 = DeviceParticles(host)
+    t2 = Transfer(w.dim, w.n, w.frac_bits, ranges_of(w), p2.n)
+    for k in range(12):
+        t2.bin(p2)
+        t2.p2g(p2, binned=True)
+        t2.grid_update(ex["dt"], ex["gravity"], ex["sticky"], active=True)
+        t2.g2p(p2, ex["dt"])
+    t2.bin(p2)
+    t2.p2g(p2, binned=True)
+    torch.cuda.synchronize()
+    say("fused full size")
+    a, b = parts.host(), p2.host()
+    for key in ("x", "v", "C"):
+        assert_same(a[key], b[key], f"{key} after 12 substeps")
+    assert_same(rs.grid.cpu().numpy(), t2.grid.cpu().numpy(), "grid of the state after 12 substeps")
+    assert tr.status.cpu().numpy().view(np.uint32).tolist() == t2.status.cpu().numpy().view(np.uint32).tolist()
+
+
+def fast_cloud(dim, n, count, seed):
+    """Particles over the middle of the grid moving a third of a cell per
+    substep, with a few beyond the declared speed and affine ranges."""
+    u = G.uniform01(seed, 1, dim * count).reshape(dim, count)
+    x = ((n * 0.25 + u * n * 0.5) / n).astype(np.float32)
+    f = G.particle_fields(seed, count, dim, (0.5, 2.0), 6.0, 2.0)
+    f["v"][0, :40] = 50.0                              # beyond max_speed
+    f["C"][0, 40:60] = 30.0                            # beyond max_affine
+    return {"x": np.ascontiguousarray(x), **f}
+
+
+@pytest.mark.parametrize("dim", [2, 3])
+def test_strays_and_range_checks_in_lockstep(mpm, oracle_lib, dim):
+    """Fast particles cross tile boundaries between re-binnings (every 12
+    substeps here), so many deposit through the stray path; particles beyond
+    the declared ranges add nothing and are counted at every deposit."""
+    n = 32 if dim == 3 else 64
+    base = WORKLOADS["dam_3d_256"] if dim == 3 else WORKLOADS["pile_2d"]
+    host = fast_cloud(dim, n, 6000 if dim == 3 else 3000, 0xFA5 + dim)
+    w = replace(scaled(base, host["m"].shape[0], n=n), frac_bits=28, max_mass=2.0, max_speed=40.0, max_affine=25.0)
+    ex = {"dt": 2e-3 / (n / 32), "gravity": (0.0, -9.8, 0.0)[:dim], "sticky": 2}
+    parts, tr, rs = resident(mpm, w, host, ex)
+    rs.start()
+    state = {k: v.copy() for k, v in host.items()}
+    _, st0, _ = oracle_substep(oracle_lib, w, state, ex)
+    total_range = int(st0[1])
+    for k in range(1, 25):
+        rs.substep()
+        _, _, state = oracle_substep(oracle_lib, w, state, ex)
+        nxt, st, _ = oracle_substep(oracle_lib, w, state, ex)
+        total_range += int(st[1])
+        if k % 4 == 0:
+            rs.gather()
+            torch.cuda.synchronize()
+            say("fused strays", dim, k)
+            got = parts.host()
+            for key in ("x", "v", "C"):
+                assert_same(got[key], state[key], f"{dim}D substep {k} {key}")
+            assert_same(rs.grid.cpu().numpy(), nxt, f"{dim}D grid after substep {k}")
+        if k % 12 == 0:
+            rs.rebin()
+    status = tr.status.cpu().numpy().view(np.uint32).tolist()
+    assert status[1] == total_range and total_range > 0
+    assert status[0] == 0 and status[3] == 0
+
+
+def test_deposit_only_matches_p2g_and_flagged_clear(mpm, oracle_lib):
+    """mpm_g2p2g with no input grid deposits the binned records as mpm_p2g
+    does (here on blob particles, dense tiles); mpm_grid_clear_tiles then
+    leaves the grid zero and the flags clear."""
+    from material_point_particle_amd.transfer import DeviceParticles, ResidentSubsteps, Transfer
+    w = scaled(WORKLOADS["blobs_3d_256"], 1 << 18)
+    host = build(w)
+    ref, _ = oracle_lib.p2g_quadratic(w.dim, w.n, w.frac_bits, host, ranges_of(w))
+    parts = DeviceParticles(host)
+    tr = Transfer(w.dim, w.n, w.frac_bits, ranges_of(w), parts.n)
+    rs = ResidentSubsteps(tr, parts, 1e-4, (0.0, -9.8, 0.0), 2)
+    rs.start()
+    torch.cuda.synchronize()
+    say("deposit only")
+    assert_same(rs.grid.cpu().numpy(), ref, "deposit-only grid")
+    flags = rs.tiles[rs.cur]
+    assert int(flags.sum()) > 0
+    import material_point_particle_amd._lib as L
+    L.mpm_grid_clear_tiles(tr.desc, rs.grid, flags)
+    torch.cuda.synchronize()
+    assert int(rs.grid.abs().sum()) == 0 and int(flags.sum()) == 0
