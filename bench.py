@@ -136,6 +136,64 @@ def measure_substeps(args, torch, w, build, DeviceParticles, Transfer):
     }
 
 
+def measure_fused(args, torch, w, build, DeviceParticles, Transfer):
+    """The dam-break substep with the particle state resident in the binned
+    records (8M particles, 256^3 nodes): one fused G2P2G kernel per substep
+    (grid update on load, gather and advection, deposit into the other grid)
+    plus the flagged clear of the grid it read, re-binned every 10 substeps
+    (gather of the records into the particle arrays and a resident binning),
+    all inside the timed region."""
+    import material_point_particle_amd._lib as L
+    from material_point_particle_amd.transfer import ResidentSubsteps
+    host = build(w)
+    ex = w.extra
+    parts = DeviceParticles(host)
+    del host
+    tr = Transfer(w.dim, w.n, w.frac_bits, (w.max_mass, w.max_speed, w.max_affine), parts.n)
+    rs = ResidentSubsteps(tr, parts, ex["dt"], ex["gravity"], ex["sticky"])
+    stream = torch.cuda.current_stream()
+    every = 10
+    rs.start()
+    for _ in range(3):
+        rs.substep()
+    torch.cuda.synchronize()
+    k = args.substeps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(k)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(k):
+        e = ev[i]
+        e[0].record(stream)
+        a, b = rs.cur, 1 - rs.cur
+        L.mpm_g2p2g(tr.desc, tr.ranges, tr.ws, parts.n, rs.grids[a], rs.grids[b], rs.tiles[b], ex["dt"],
+                    ex["gravity"], ex["sticky"], tr.status)
+        e[1].record(stream)
+        L.mpm_grid_clear_tiles(tr.desc, rs.grids[a], rs.tiles[a])
+        rs.cur = b
+        e[2].record(stream)
+        if (i + 1) % every == 0:
+            rs.gather()
+            rs.rebin()
+        e[3].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total = start.elapsed_time(stop) / k
+    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])
+    fused_ms, clear_ms = st[:, 0].mean(), st[:, 1].mean()
+    rebin_ms = st[:, 2].sum() / max(1, k // every)
+    status = tr.status.cpu().numpy().view(np.uint32).tolist()
+    log(f"fused substeps: {total:.3f} ms (g2p2g {fused_ms:.3f}, clear {clear_ms:.3f}, re-bin {rebin_ms:.3f} "
+        f"every {every})")
+    return {
+        "workload": f"{w.name}: {parts.n} particles, dam-break block, {w.n}^3 nodes, state resident in the binned "
+                    f"records, re-binned every {every} substeps",
+        "substeps": k, "ms_per_substep": round(total, 4), "particles_per_s": round(parts.n / (total * 1e-3), 1),
+        "stages_ms": {"g2p2g": round(float(fused_ms), 4), "clear": round(float(clear_ms), 4),
+                      "rebin_each": round(float(rebin_ms), 4)},
+        "status": status,
+    }
+
+
 def measure_elastic(args, torch, w, build, Transfer):
     """The elastic substep (MLS-MPM with the Neo-Hookean stress term) on the
     8M-particle jelly cube at 256^3 nodes: stressed affine matrix, binning,
@@ -268,6 +326,10 @@ def parse():
                     help="skip the elastic-substep measurement (Neo-Hookean stress term) on the jelly cube")
     ap.add_argument("--only-elastic", action="store_true",
                     help="run only the elastic-substep measurement; prints its object")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the fused-substep measurement (state resident in the binned records)")
+    ap.add_argument("--only-fused", action="store_true",
+                    help="run only the fused-substep measurement; prints its object")
     ap.add_argument("--no-isplit", action="store_true",
                     help="skip the integer-split quadratic transfer measurement")
     ap.add_argument("--only-isplit", action="store_true",
@@ -292,6 +354,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     M.lib()
+    if args.only_fused:
+        print(json.dumps({"substep_fused": measure_fused(args, torch, WORKLOADS["dam_3d_256"], build, DeviceParticles,
+                                                         Transfer)}), flush=True)
+        return
     if args.only_isplit:
         print(json.dumps({"isplit": measure_isplit(args, torch, WORKLOADS["isplit_3d_128"], build)}), flush=True)
         return
@@ -414,14 +480,20 @@ def main():
         torch.cuda.empty_cache()
         out["substep"] = measure_substeps(args, torch, WORKLOADS["dam_3d_256"], build, DeviceParticles, Transfer)
         torch.cuda.empty_cache()
-    if not args.no_elastic:
+    if not args.no_fused:
         if args.no_substep:
+            del copies, parts, tr
+            torch.cuda.empty_cache()
+        out["substep_fused"] = measure_fused(args, torch, WORKLOADS["dam_3d_256"], build, DeviceParticles, Transfer)
+        torch.cuda.empty_cache()
+    if not args.no_elastic:
+        if args.no_substep and args.no_fused:
             del copies, parts, tr
             torch.cuda.empty_cache()
         out["elastic"] = measure_elastic(args, torch, WORKLOADS["jelly_3d_256"], build, Transfer)
         torch.cuda.empty_cache()
     if not args.no_isplit:
-        if args.no_substep and args.no_elastic:
+        if args.no_substep and args.no_fused and args.no_elastic:
             del copies, parts, tr
             torch.cuda.empty_cache()
         out["isplit"] = measure_isplit(args, torch, WORKLOADS["isplit_3d_128"], build)

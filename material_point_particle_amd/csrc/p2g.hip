@@ -722,14 +722,6 @@ g2p2g_kernel(FusedArgs f)
     const uint32_t n_items = a.meta[0];
     const int n = a.n;
     const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
-    int fx[kFlush], fy[kFlush], fz[kFlush];
-#pragma unroll
-    for (int m = 0; m < kFlush; ++m) {
-        const int i = lane + kWave * m;
-        fx[m] = i % TS::side;
-        fy[m] = (i / TS::side) % TS::side;
-        fz[m] = DIM == 3 ? i / (TS::side * TS::side) : 0;
-    }
     for (int i = lane; i < TS::ch * TS::nodes; i += kWave)
         acc[i] = 0.0;
     cnt[lane] = 0u;
@@ -754,42 +746,70 @@ g2p2g_kernel(FusedArgs f)
                 t /= (uint32_t)a.ntx;
             }
         }
-        // 1. grid velocity of the window (its origin one node below the tile)
+        // 1. grid velocity of the window (its origin one node below the tile):
+        //    every lane's nodes are loaded before any is converted, so the
+        //    loads are in flight together
         if (f.grid_in) {
-            for (int i = lane; i < WN; i += kWave) {
+            constexpr int kWin = (WN + kWave - 1) / kWave;            // window nodes per lane
+            int64_t M[kWin], P[kWin][DIM];
+            bool wall[kWin];
+#pragma unroll
+            for (int m = 0; m < kWin; ++m) {
+                const int i = lane + kWave * m;
                 const int l[3] = { i % W, (i / W) % W, DIM == 3 ? i / (W * W) : 0 };
+                bool inside = i < WN;
+                wall[m] = false;
                 int g[3] = { 0, 0, 0 };
-                bool inside = true, wall = false;
 #pragma unroll
                 for (int e = 0; e < DIM; ++e) {
                     g[e] = torg[e] - 1 + l[e];
                     inside = inside && g[e] >= 0 && g[e] < n;
-                    wall = wall || g[e] < f.sticky || g[e] >= n - f.sticky;
+                    wall[m] = wall[m] || g[e] < f.sticky || g[e] >= n - f.sticky;
                 }
                 const int64_t node = DIM == 3 ? ((int64_t)g[2] * n + g[1]) * n + g[0] : (int64_t)g[1] * n + g[0];
-                const int64_t M = inside ? f.grid_in[node] : 0;
+                M[m] = inside ? f.grid_in[node] : 0;
 #pragma unroll
-                for (int d = 0; d < DIM; ++d) {
-                    const int64_t P = (inside && M != 0) ? f.grid_in[(1 + d) * nodes + node] : 0;
-                    vw[d * WN + i] = node_velocity(M, P, f.gdt[d], wall);
+                for (int d = 0; d < DIM; ++d)
+                    P[m][d] = inside ? f.grid_in[(1 + d) * nodes + node] : 0;
+            }
+#pragma unroll
+            for (int m = 0; m < kWin; ++m) {
+                const int i = lane + kWave * m;
+                if (i < WN) {
+#pragma unroll
+                    for (int d = 0; d < DIM; ++d)
+                        vw[d * WN + i] = node_velocity(M[m], P[m][d], f.gdt[d], wall[m]);
                 }
             }
         }
         if (lane == 0)
             n_strays = 0u;
         __syncthreads();
-        // 2. gather and advect each record (with grid_in), then its key
+        // 2. gather and advect each record (with grid_in), then its key; the
+        //    next record of the lane is loaded while this one is computed
         uint32_t clamps = 0;
+        float4 nxt[R / 4];
+        if ((uint32_t)lane < count) {
+            const float4 *src = reinterpret_cast<const float4 *>(f.records + (int64_t)(first + lane) * R);
+#pragma unroll
+            for (int q = 0; q < R / 4; ++q)
+                nxt[q] = src[q];
+        }
         for (uint32_t i = (uint32_t)lane; i < count; i += kWave) {
             float4 *src = reinterpret_cast<float4 *>(f.records + (int64_t)(first + i) * R);
             float rec[R];
 #pragma unroll
             for (int q = 0; q < R / 4; ++q) {
-                const float4 t = src[q];
-                rec[4 * q] = t.x;
-                rec[4 * q + 1] = t.y;
-                rec[4 * q + 2] = t.z;
-                rec[4 * q + 3] = t.w;
+                rec[4 * q] = nxt[q].x;
+                rec[4 * q + 1] = nxt[q].y;
+                rec[4 * q + 2] = nxt[q].z;
+                rec[4 * q + 3] = nxt[q].w;
+            }
+            if (i + kWave < count) {
+                const float4 *ns = reinterpret_cast<const float4 *>(f.records + (int64_t)(first + i + kWave) * R);
+#pragma unroll
+                for (int q = 0; q < R / 4; ++q)
+                    nxt[q] = ns[q];
             }
             if (f.grid_in) {
                 Axis ax[DIM];
@@ -849,8 +869,8 @@ g2p2g_kernel(FusedArgs f)
         }
         if (clamps != 0u)
             atomicAdd(&a.status[2], clamps);
-        // the records written above are read back below by other lanes
-        __threadfence();
+        // the records written above are read back below by other lanes of
+        // this workgroup: the barrier's workgroup-scope fence orders them
         __syncthreads();
         if (f.grid_in) {                                             // the window becomes the node block
             for (int i = lane; i < TS::ch * TS::nodes; i += kWave)
@@ -904,7 +924,8 @@ g2p2g_kernel(FusedArgs f)
             const int i = lane + kWave * m;
             if (i >= TS::nodes)
                 continue;
-            const int gx = torg[0] + fx[m], gy = torg[1] + fy[m], gz = torg[2] + fz[m];
+            const int gx = torg[0] + i % TS::side, gy = torg[1] + (i / TS::side) % TS::side;
+            const int gz = torg[2] + (DIM == 3 ? i / (TS::side * TS::side) : 0);
             const bool in_grid = gx < n && gy < n && gz < n;
             const int64_t node = DIM == 3 ? ((int64_t)gz * n + gy) * n + gx : (int64_t)gy * n + gx;
 #pragma unroll
