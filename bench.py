@@ -38,7 +38,8 @@ def measured_traffic():
     import re
     here = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for f in ("material_point_particle_amd/csrc/p2g.hip", "material_point_particle_amd/csrc/common.hpp"):
+    for f in ("material_point_particle_amd/csrc/p2g.hip", "material_point_particle_amd/csrc/p2g_device.hpp",
+              "material_point_particle_amd/csrc/common.hpp"):
         with open(os.path.join(here, f), "rb") as fh:
             h.update(fh.read())
     try:
