@@ -16,6 +16,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 p2g_tiled_kernel(TiledArgs a)
 {
     using TS = TileShape<DIM>;
+    constexpr int R = rec_floats<DIM>();
+    constexpr int G = kGroup;
     constexpr int kFlush = (TS::nodes + kWave - 1) / kWave;      // node-block entries per lane
     __shared__ double acc[TS::ch * TS::nodes];
     __shared__ __align__(16) uint16_t ent[kMaxGroups * kGroup + 4];
@@ -82,7 +84,102 @@ p2g_tiled_kernel(TiledArgs a)
         uint4 rec_next = make_uint4(0u, 0u, 0u, 0u);
         if (item_next < n_items)
             rec_next = items[item_next];
-        item_rows<DIM, false>(a, RangesF{ 0.0f, 0.0f, 0.0f }, first, rows, groups, ent, acc, torg, lane);
+        // The rows: the same loop as item_rows<DIM, false> in p2g_device.hpp,
+        // kept here because that function, inlined into this kernel, was
+        // scheduled differently and measured 12% slower on the blob workload.
+        static_assert(kGroup == 4, "a group's entries load as one 8-byte word");
+        for (uint32_t j = 0; j < rows; ++j) {
+            // this lane's group in row j is group 64 j + lane of the item
+            if (j * kWave + (uint32_t)lane >= groups)
+                continue;
+            const uint2 w2 = *reinterpret_cast<const uint2 *>(&ent[(j * kWave + lane) * kGroup]);
+            const uint32_t e4[G] = { w2.x & 0xFFFFu, w2.x >> 16, w2.y & 0xFFFFu, w2.y >> 16 };
+            GroupHoist<DIM> h[G];
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
+                const float4 *src =
+                    reinterpret_cast<const float4 *>(a.sorted + (int64_t)(first + (e4[k] & ~(uint32_t)kPad16)) * R);
+                float rec[R];
+#pragma unroll
+                for (int q = 0; q < R / 4; ++q) {
+                    const float4 t = src[q];
+                    rec[4 * q] = t.x;
+                    rec[4 * q + 1] = t.y;
+                    rec[4 * q + 2] = t.z;
+                    rec[4 * q + 3] = t.w;
+                }
+                if (e4[k] & kPad16)                          // completes the cell's group: zero mass
+                    rec[2 * DIM + DIM * DIM] = 0.0f;
+                group_hoist<DIM>(rec, a.nf, a.dx, a.last_base, a.S, h[k]);
+            }
+            // every record of the group is in one cell of this tile (binning's
+            // invariant); a group that breaks it is counted and skipped
+            bool ok = true;
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                ok = ok && (unsigned)(h[0].base[e] - torg[e]) < (unsigned)kTile;
+#pragma unroll
+                for (int k = 1; k < G; ++k)
+                    ok = ok && h[k].base[e] == h[0].base[e];
+            }
+            if (!ok) {
+                atomicAdd(&a.status[3], 1u);
+                continue;
+            }
+            int lb;
+            if constexpr (DIM == 3)
+                lb = ((h[0].base[2] - torg[2]) * TS::side + (h[0].base[1] - torg[1])) * TS::side +
+                     (h[0].base[0] - torg[0]);
+            else
+                lb = (h[0].base[1] - torg[1]) * TS::side + (h[0].base[0] - torg[0]);
+            const int nc = DIM == 3 ? 3 : 1;
+#pragma unroll
+            for (int aa = 0; aa < 3; ++aa)
+#pragma unroll
+                for (int b = 0; b < 3; ++b) {
+                    float mwxy[G], t2[G][DIM];
+#pragma unroll
+                    for (int k = 0; k < G; ++k) {
+                        mwxy[k] = h[k].mwx[aa] * h[k].wy[b];
+#pragma unroll
+                        for (int d = 0; d < DIM; ++d)
+                            t2[k][d] = h[k].t1[d][aa] + h[k].cy[d][b];
+                    }
+#pragma unroll
+                    for (int c = 0; c < nc; ++c) {
+                        const int off = DIM == 3 ? (c * TS::side + b) * TS::side + aa : b * TS::side + aa;
+                        // The node's (1+DIM) x G contributions are independent until
+                        // the per-channel sums; they are written phase by phase
+                        // (products, rounding, widening, sums) so that the chains
+                        // interleave instead of running back to back.
+                        float wmS[G], val[1 + DIM][G];
+#pragma unroll
+                        for (int k = 0; k < G; ++k) {
+                            wmS[k] = DIM == 3 ? mwxy[k] * h[k].wz[c] : mwxy[k];
+                            val[0][k] = wmS[k];
+                        }
+#pragma unroll
+                        for (int d = 0; d < DIM; ++d)
+#pragma unroll
+                            for (int k = 0; k < G; ++k) {
+                                const float u = DIM == 3 ? t2[k][d] + h[k].cz[d][c] : t2[k][d];
+                                val[1 + d][k] = wmS[k] * u;
+                            }
+                        double q[1 + DIM][G];
+#pragma unroll
+                        for (int ch = 0; ch < 1 + DIM; ++ch)
+#pragma unroll
+                            for (int k = 0; k < G; ++k)
+                                q[ch][k] = (double)rintf(val[ch][k]);
+#pragma unroll
+                        for (int ch = 0; ch < 1 + DIM; ++ch) {
+                            // exact integer adds: a pairwise tree gives the same sum
+                            const double sum = (q[ch][0] + q[ch][1]) + (q[ch][2] + q[ch][3]);
+                            atomicAdd(&acc[ch * TS::nodes + lb + off], sum);
+                        }
+                    }
+                }
+        }
         __syncthreads();
         item = item_next;
         rec_item = rec_next;
