@@ -12,10 +12,10 @@ namespace {
 // update as it loads, gathers and updates the slice's particles, and scatters
 // them into the next grid through the on-chip block).  The particle state is
 // the binned records, updated in place.  Per item:
-//  1. the grid velocity of the (kTile+4)^dim nodes from one node below the
-//     tile to six above (every node a particle of the tile can read after
-//     drifting less than a cell) is formed from grid_in with node_velocity
-//     into LDS (sharing the node block's memory);
+//  1. the grid velocity of the (kTile+4)^dim nodes t0-1 .. t0+6 per axis,
+//     t0 the tile's first node (every node a particle of the tile reads
+//     while it stays within a cell of the tile), is formed from grid_in with
+//     node_velocity into LDS (sharing the node block's memory);
 //  2. each record is gathered and advected (g2p_particle, the same arithmetic
 //     as the G2P kernel; a particle whose stencil leaves that window reads
 //     grid_in directly) and written back; its cell in the new position is its
