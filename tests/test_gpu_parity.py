@@ -178,7 +178,7 @@ def _cloud_in_cells(dim, n, cells_and_counts, seed):
     return {"x": np.ascontiguousarray(x.astype(np.float32)), **f}
 
 
-@pytest.mark.parametrize("layout", ["ragged_tiles", "one_dense_cell", "tile_corners"])
+@pytest.mark.parametrize("layout", ["ragged_tiles", "sparse_tiles", "one_dense_cell", "tile_corners"])
 def test_p2g_ragged_and_dense_tiles(mpm, oracle_lib, layout):
     dim, n, k = 3, 32, 32
     if layout == "ragged_tiles":
@@ -187,6 +187,18 @@ def test_p2g_ragged_and_dense_tiles(mpm, oracle_lib, layout):
         spec = [((1, 1, 1), 1), ((5, 1, 1), 63), ((9, 1, 1), 64), ((13, 2, 3), 65), ((1, 5, 1), 2047),
                 ((5, 5, 5), 2048), ((9, 9, 9), 2049), ((13, 13, 13), 4097), ((17, 1, 1), 1855),
                 ((21, 1, 1), 1856), ((25, 1, 1), 1857), ((17, 5, 1), 3713)]
+    elif layout == "sparse_tiles":
+        # 101 tiles of 1..67 particles (one row each at the bound, mostly idle
+        # lanes), a tile of 1856 + 3 (a full work item and a 3-record one) and
+        # tiles of 68 and 200 (two rows at the bound)
+        rng = np.random.default_rng(0x5A1E)
+        cells = rng.choice((n // 4) ** 3, 104, replace=False)
+        spec = []
+        for i, c in enumerate(cells):
+            t = (int(c % 8) * 4 + int(rng.integers(4)), int(c // 8 % 8) * 4 + int(rng.integers(4)),
+                 int(c // 64) * 4 + int(rng.integers(4)))
+            t = tuple(min(v, n - 3) for v in t)
+            spec.append((t, [1859, 68, 200][i - 101] if i >= 101 else int(rng.integers(1, 68))))
     elif layout == "one_dense_cell":
         spec = [((17, 17, 17), 9000)]
     else:
