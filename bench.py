@@ -13,7 +13,10 @@ Timing: HIP events recorded on the stream the library launches on (torch's
 current stream), around each stage of each timed step; `value` is particles
 per second of the whole step.  The `roofline` object is for the dominant
 kernel, using algorithmic bytes (particle records read once, touched nodes
-written once) over its average event-measured duration.  `cpu_baseline` is
+written once) over its average event-measured duration; `alu_roofline` puts
+the same kernel against the vector-ALU issue rate (the lane operations the
+fixed-order transfer needs per particle, over the same duration), which is
+what limits it.  `cpu_baseline` is
 the oracle (plain single-threaded C) timed on this host's cores over one
 step of the same workload.
 """
@@ -28,6 +31,14 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+# Vector-ALU issue peak: 256 CUs x 4 SIMDs, one 64-lane instruction per SIMD every 4 cycles (16 lanes per cycle)
+# at 2.4 GHz, in lane operations per second (float32 without packed math, float64 adds and conversions alike).
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Lane operations the fixed-order transfer needs per particle and stencil node, however it is scheduled: the
+# product w*m*S, DIM sums for u, DIM momentum products, 1 + DIM roundings and widenings to float64, and the
+# 1 + DIM exact float64 sums of groups of four (three adds per four contributions).
+def alu_ops_per_node(dim: int) -> float:
+    return 1 + dim + dim + 2 * (1 + dim) + 0.75 * (1 + dim)
 METRIC = "P2G particles/sec and achieved HBM GB/s (% of peak), 3D 16M particles, 1 GPU"
 
 
@@ -447,6 +458,11 @@ def main():
                 "bytes_per_launch": int(roof["bytes_per_launch"]), "ms_per_launch": round(roof["ms_per_launch"], 4)}
     if roof["kernel"].startswith("p2g_tiled"):
         roofline["traffic"] = measured_traffic()
+    # the same kernel against the vector-ALU issue rate, which is what limits it
+    ops = alu_ops_per_node(w.dim) * 3 ** w.dim
+    alu_tops = ops * binned / (p2g_ms * 1e-3) / 1e12
+    alu = {"bound": "alu", "achieved": round(alu_tops, 2), "peak": round(VALU_PEAK_TOPS, 2), "unit": "T lane-ops/s",
+           "frac": round(alu_tops / VALU_PEAK_TOPS, 4), "ops_per_particle": ops, "kernel": roof["kernel"]}
 
     value = w.n_particles / (ms_step * 1e-3)
     out = {
@@ -467,6 +483,7 @@ def main():
                                "binning into 4^3-cell tiles + tiled P2G",
                    "particles": w.n_particles, "nodes": w.n ** w.dim, "touched_nodes": touched},
         "roofline": roofline,
+        "alu_roofline": alu,
         "breakdown": {
             "clear_ms": round(clear_ms, 4), "bin_ms": round(bin_ms, 4), "p2g_ms": round(p2g_ms, 4),
             "p2g_particles_per_s": round(binned / (p2g_ms * 1e-3), 1), "p2g_gbs": round(p2g_gbs, 1),
