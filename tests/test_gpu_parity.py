@@ -116,7 +116,8 @@ def test_cic_split_edge_cases(mpm, oracle_lib):
 CASES = [("pile_2d", None), ("dam_3d_128", 1 << 16), ("blobs_3d_256", 1 << 18)]
 
 
-@pytest.mark.parametrize("name,count", CASES)
+# the 1M-particle dam-break on 128^3 nodes at its full size, beside the smaller cases
+@pytest.mark.parametrize("name,count", CASES + [("dam_3d_128", None)])
 @pytest.mark.parametrize("binned", [False, True])
 def test_p2g_bit_exact(mpm, oracle_lib, name, count, binned):
     w = WORKLOADS[name] if count is None else scaled(WORKLOADS[name], count)
