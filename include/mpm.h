@@ -262,16 +262,19 @@ int mpm_isplit_workspace_bytes(int32_t dim, int32_t n, int64_t np, size_t *bytes
  * tile's node block with its halo, gathers and advects the slice's
  * particles, and scatters them into the next grid through the on-chip block.
  * The state lives in the workspace between substeps; a substep reads grid k
- * and writes grid k+1 (two grid buffers used in turn, each with a byte per
- * 4^dim-node tile that flags the node tiles written into it), and the grid
- * just read is cleared afterwards.  Results are identical to the separate
+ * and writes grid k+1 (three grid buffers used in turn, each with a byte per
+ * 4^dim-node tile that flags the node tiles written into it), and zeroes grid
+ * k-1, the one read in the previous substep, once its own items are done, so
+ * no clear runs between substeps.  Results are identical to the separate
  * steps (binning, mpm_p2g, mpm_grid_update, mpm_g2p).  A loop:
  *
  *   mpm_bin_resident(ws <- particles); mpm_g2p2g(grid_in = NULL -> A, flags A)
- *   per substep: mpm_g2p2g(A -> B, flags B); mpm_grid_clear_tiles(A, flags A);
- *                swap A and B
+ *   per substep: mpm_g2p2g(A -> B, flags B, clearing C and flags C);
+ *                (A, B, C) <- (B, C, A)
  *   to re-bin (particles drift out of their tiles) or to read the state:
  *                mpm_gather_records(ws -> particles), then mpm_bin_resident
+ * (With two grids, pass grid_clear = NULL and call mpm_grid_clear_tiles on
+ * the grid just read after each substep.)
  */
 
 /* Binning as mpm_bin_particles, keeping every record as it is (no range
@@ -294,12 +297,16 @@ int mpm_bin_resident(const mpm_grid_desc *grid, const mpm_particles *particles, 
  * binning deposit with global atomics, so the result does not depend on
  * when the caller re-bins.  grid_out must be zero on entry; every node tile
  * it writes is flagged (set to 1) in tiles_out, uint8[(n/4)^dim], for
- * mpm_grid_clear_tiles.  All pointers device; grid_in and grid_out distinct.
+ * mpm_grid_clear_tiles.  grid_clear != NULL: a third grid, neither grid_in
+ * nor grid_out, whose node tiles flagged in tiles_clear (not tiles_out) are
+ * zeroed in every channel, and those flags reset, as mpm_grid_clear_tiles
+ * would (grid_clear == NULL: tiles_clear is ignored).  All pointers device.
  * Errors: MPM_ERR_INVALID, MPM_ERR_OVERFLOW (bounds for n_particles and the
  * ranges, as mpm_check_bounds), MPM_ERR_HIP. */
 int mpm_g2p2g(const mpm_grid_desc *grid, const mpm_ranges *ranges, void *ws, int64_t n_particles,
-              const int64_t *grid_in, int64_t *grid_out, uint8_t *tiles_out, float dt, const float *gravity,
-              int32_t sticky, uint32_t *status, hipStream_t stream);
+              const int64_t *grid_in, int64_t *grid_out, uint8_t *tiles_out, int64_t *grid_clear,
+              uint8_t *tiles_clear, float dt, const float *gravity, int32_t sticky, uint32_t *status,
+              hipStream_t stream);
 
 /* Zeroes every node of the node tiles flagged in tiles (uint8[(n/4)^dim]),
  * in every channel of grid, then clears the flags.  Errors: MPM_ERR_INVALID,

@@ -106,7 +106,8 @@ def lib() -> ct.CDLL:
                                        ct.c_void_p]
         L.mpm_g2p2g.restype = ct.c_int
         L.mpm_g2p2g.argtypes = [P(mpm_grid_desc), P(mpm_ranges), ct.c_void_p, ct.c_int64, ct.c_void_p, ct.c_void_p,
-                                ct.c_void_p, ct.c_float, P(ct.c_float), ct.c_int32, ct.c_void_p, ct.c_void_p]
+                                ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_float, P(ct.c_float), ct.c_int32,
+                                ct.c_void_p, ct.c_void_p]
         L.mpm_grid_clear_tiles.restype = ct.c_int
         L.mpm_grid_clear_tiles.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p]
         L.mpm_gather_records.restype = ct.c_int
@@ -217,10 +218,11 @@ def mpm_bin_resident(desc, parts: mpm_particles, ws, status, stream=None) -> Non
 
 
 def mpm_g2p2g(desc, rng: mpm_ranges, ws, n_particles: int, grid_in, grid_out, tiles_out, dt: float, gravity,
-              sticky: int, status, stream=None) -> None:
+              sticky: int, status, stream=None, grid_clear=None, tiles_clear=None) -> None:
     g = (ct.c_float * 3)(*(list(gravity) + [0.0] * (3 - len(gravity))))
     _check(lib().mpm_g2p2g(ct.byref(desc), ct.byref(rng), _ptr(ws), n_particles, _ptr(grid_in), _ptr(grid_out),
-                           _ptr(tiles_out), dt, g, sticky, _ptr(status), _stream(stream)), "mpm_g2p2g")
+                           _ptr(tiles_out), _ptr(grid_clear), _ptr(tiles_clear), dt, g, sticky, _ptr(status),
+                           _stream(stream)), "mpm_g2p2g")
 
 
 def mpm_grid_clear_tiles(desc, grid, tiles, stream=None) -> None:

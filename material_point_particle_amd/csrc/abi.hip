@@ -270,14 +270,18 @@ int mpm_bin_resident(const mpm_grid_desc *grid, const mpm_particles *particles, 
 }
 
 int mpm_g2p2g(const mpm_grid_desc *grid, const mpm_ranges *ranges, void *ws, int64_t n_particles,
-              const int64_t *grid_in, int64_t *grid_out, uint8_t *tiles_out, float dt, const float *gravity,
-              int32_t sticky, uint32_t *status, hipStream_t stream)
+              const int64_t *grid_in, int64_t *grid_out, uint8_t *tiles_out, int64_t *grid_clear,
+              uint8_t *tiles_clear, float dt, const float *gravity, int32_t sticky, uint32_t *status,
+              hipStream_t stream)
 {
     int rc;
     if ((rc = check_desc(grid)) != MPM_OK || (rc = check_ranges(ranges)) != MPM_OK)
         return rc;
     if (n_particles < 0 || n_particles > kMaxParticles || !aligned(ws, 256) || !aligned(grid_out, 8) ||
         !aligned(tiles_out, 4) || !aligned(status, 4) || (grid_in && !aligned(grid_in, 8)) || grid_in == grid_out)
+        return MPM_ERR_INVALID;
+    if (grid_clear && (!aligned(grid_clear, 8) || !aligned(tiles_clear, 4) || grid_clear == grid_out ||
+                       grid_clear == grid_in || tiles_clear == tiles_out))
         return MPM_ERR_INVALID;
     if (grid_in && (!gravity || sticky < 0 || sticky > grid->n / 2 || !(dt >= 0.0f)))
         return MPM_ERR_INVALID;
@@ -288,7 +292,8 @@ int mpm_g2p2g(const mpm_grid_desc *grid, const mpm_ranges *ranges, void *ws, int
     const float g3[3] = { gravity ? gravity[0] : 0.0f, gravity ? gravity[1] : 0.0f,
                           gravity && grid->dim == 3 ? gravity[2] : 0.0f };
     return hip_status(launch_g2p2g(grid->dim, grid->n, grid->frac_bits, bin_view(ws, l), ranges_f(ranges), grid_in,
-                                   grid_out, tiles_out, dt, g3, sticky, status, stream));
+                                   grid_out, tiles_out, grid_clear, grid_clear ? tiles_clear : nullptr, dt, g3, sticky,
+                                   status, stream));
 }
 
 int mpm_grid_clear_tiles(const mpm_grid_desc *grid, int64_t *grid_io, uint8_t *tiles, hipStream_t stream)

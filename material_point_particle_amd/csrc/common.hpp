@@ -240,8 +240,8 @@ hipError_t launch_p2g_direct(int dim, int n, int frac_bits, const Fields &p, con
 hipError_t launch_p2g_tiled(int dim, int n, int frac_bits, const BinView &b, int64_t *grid, uint32_t *status,
                             hipStream_t s);
 hipError_t launch_g2p2g(int dim, int n, int frac_bits, const BinView &b, RangesF r, const int64_t *grid_in,
-                        int64_t *grid_out, uint8_t *tiles_out, float dt, const float *gravity, int sticky,
-                        uint32_t *status, hipStream_t s);
+                        int64_t *grid_out, uint8_t *tiles_out, int64_t *grid_clear, uint8_t *tiles_clear, float dt,
+                        const float *gravity, int sticky, uint32_t *status, hipStream_t s);
 hipError_t launch_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32_t *vel,
                                 const uint32_t *order, int cells, int64_t *grid, uint32_t *status, hipStream_t s);
 hipError_t launch_p2g_isplit(int dim, int n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,

@@ -24,7 +24,10 @@ namespace {
 //     the updated records into the tile's node block (range checks here, not
 //     at binning); strays deposit with global atomics;
 //  4. the block is flushed to grid_out, and every node tile this item wrote
-//     is flagged in tiles_out (for the restricted clear of that grid later).
+//     is flagged in tiles_out (for the restricted clear of that grid later);
+//  5. (after the last item, with a third grid) the flagged node tiles of the
+//     grid read in the previous substep are zeroed, so that three grids in
+//     turn need no clear between substeps.
 // With grid_in NULL only steps 2 (keys), 3 and 4 run: the deposit of the
 // records as they are.
 // ---------------------------------------------------------------------------
@@ -33,6 +36,8 @@ struct FusedArgs {
     float *records;            // the same records, written
     const int64_t *grid_in;    // grid velocity source, or NULL for a deposit only
     uint8_t *tiles_out;        // node-tile flags of grid_out
+    int64_t *grid_clear;       // a third grid to zero (its flagged node tiles), or NULL
+    uint8_t *tiles_clear;      // its node-tile flags, reset with it
     RangesF r;
     float dt, lo, hi, cscale;
     float gdt[3];
@@ -299,13 +304,50 @@ g2p2g_kernel(FusedArgs f)
             flag_node_tiles<DIM>(f.tiles_out, a.ntx, torg, TS::side);
         __syncthreads();
     }
+    // 5. With a third grid (the one read in the previous substep): once the
+    //    item queue is empty, each workgroup zeroes the flagged node tiles of
+    //    its share of that grid's tiles and resets their flags, so that no
+    //    clear runs between substeps and the workgroups that finish first
+    //    fill the kernel's tail with it.  This kernel neither reads nor
+    //    writes that grid otherwise.
+    if (f.grid_clear) {
+        constexpr int kTileNodes = DIM == 3 ? kTile * kTile * kTile : kTile * kTile;
+        static_assert(kTileNodes <= kWave, "one lane per node of a node tile");
+        const int ntx = a.ntx;
+        const int64_t n_tiles = DIM == 3 ? (int64_t)ntx * ntx * ntx : (int64_t)ntx * ntx;
+        const int64_t share = (n_tiles + gridDim.x - 1) / gridDim.x;
+        const int64_t t_begin = (int64_t)blockIdx.x * share;
+        const int64_t t_end = t_begin + share < n_tiles ? t_begin + share : n_tiles;
+        const int lx = lane % kTile, ly = (lane / kTile) % kTile, lz = DIM == 3 ? lane / (kTile * kTile) : 0;
+        for (int64_t base = t_begin; base < t_end; base += kWave) {
+            const int64_t t = base + lane;
+            const bool flagged = t < t_end && f.tiles_clear[t] != 0;
+            uint64_t m = __ballot(flagged);
+            while (m != 0ull) {
+                int64_t tt = base + __builtin_ctzll(m);
+                m &= m - 1ull;
+                const int tx = (int)(tt % ntx);
+                tt /= ntx;
+                const int ty = (int)(tt % ntx), tz = DIM == 3 ? (int)(tt / ntx) : 0;
+                if (lane < kTileNodes) {
+                    const int gx = tx * kTile + lx, gy = ty * kTile + ly, gz = tz * kTile + lz;
+                    const int64_t node = DIM == 3 ? ((int64_t)gz * n + gy) * n + gx : (int64_t)gy * n + gx;
+#pragma unroll
+                    for (int ch = 0; ch < TS::ch; ++ch)
+                        f.grid_clear[ch * nodes + node] = 0;
+                }
+            }
+            if (flagged)
+                f.tiles_clear[t] = 0;
+        }
+    }
 }
 
 }  // namespace
 
 hipError_t launch_g2p2g(int dim, int n, int frac_bits, const BinView &b, RangesF r, const int64_t *grid_in,
-                        int64_t *grid_out, uint8_t *tiles_out, float dt, const float *gravity, int sticky,
-                        uint32_t *status, hipStream_t s)
+                        int64_t *grid_out, uint8_t *tiles_out, int64_t *grid_clear, uint8_t *tiles_clear, float dt,
+                        const float *gravity, int sticky, uint32_t *status, hipStream_t s)
 {
     FusedArgs f;
     TiledArgs &a = f.t;
@@ -325,6 +367,8 @@ hipError_t launch_g2p2g(int dim, int n, int frac_bits, const BinView &b, RangesF
     f.records = b.sorted;
     f.grid_in = grid_in;
     f.tiles_out = tiles_out;
+    f.grid_clear = grid_clear;
+    f.tiles_clear = tiles_clear;
     f.r = r;
     f.dt = dt;
     f.lo = a.dx;

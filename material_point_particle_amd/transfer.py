@@ -120,8 +120,9 @@ class Transfer:
 
 class ResidentSubsteps:
     """The substep loop with the particle state kept in the binned records
-    (mpm_bin_resident, mpm_g2p2g, mpm_grid_clear_tiles, mpm_gather_records):
-    two grids used in turn, each with its node-tile flags.  After start(),
+    (mpm_bin_resident, mpm_g2p2g, mpm_gather_records): three grids used in
+    turn, each with its node-tile flags; a substep reads grid k, deposits into
+    grid k+1 and zeroes grid k-1 in the same kernel.  After start(),
     self.grid holds the deposit of the current state (the next substep's
     P2G grid)."""
 
@@ -129,9 +130,9 @@ class ResidentSubsteps:
         self.tr, self.parts = tr, parts
         self.dt, self.gravity, self.sticky = dt, list(gravity), sticky
         dim, n = tr.dim, tr.n
-        self.grids = [tr.grid, torch.zeros_like(tr.grid)]
+        self.grids = [tr.grid, torch.zeros_like(tr.grid), torch.zeros_like(tr.grid)]
         n_tiles = (n // 4) ** dim
-        self.tiles = [torch.zeros(n_tiles, dtype=torch.uint8, device=device) for _ in range(2)]
+        self.tiles = [torch.zeros(n_tiles, dtype=torch.uint8, device=device) for _ in range(3)]
         self.cur = 0
 
     @property
@@ -150,11 +151,11 @@ class ResidentSubsteps:
     def rebin(self) -> None:
         L.mpm_bin_resident(self.tr.desc, self.parts.desc(), self.tr.ws, self.tr.status)
 
-    def substep(self) -> None:
-        a, b = self.cur, 1 - self.cur
+    def substep(self, stream=None) -> None:
+        a, b, c = self.cur, (self.cur + 1) % 3, (self.cur + 2) % 3
         L.mpm_g2p2g(self.tr.desc, self.tr.ranges, self.tr.ws, self.parts.n, self.grids[a], self.grids[b],
-                    self.tiles[b], self.dt, self.gravity, self.sticky, self.tr.status)
-        L.mpm_grid_clear_tiles(self.tr.desc, self.grids[a], self.tiles[a])
+                    self.tiles[b], self.dt, self.gravity, self.sticky, self.tr.status, stream,
+                    grid_clear=self.grids[c], tiles_clear=self.tiles[c])
         self.cur = b
 
     def gather(self) -> None:

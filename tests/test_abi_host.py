@@ -158,16 +158,22 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     # resident substep entries
     g3 = (ct.c_float * 3)(0, -9.8, 0)
     T = ct.c_void_p(1 << 16)
-    assert lib.mpm_g2p2g(ct.byref(d), ct.byref(r), ct.c_void_p(4096), 10, grid, grid, T, 1e-4, g3, 2, status,
-                         None) == L.MPM_ERR_INVALID                                    # grid_in == grid_out
-    assert lib.mpm_g2p2g(ct.byref(d), ct.byref(r), ct.c_void_p(4100), 10, None, grid, T, 1e-4, g3, 2, status,
-                         None) == L.MPM_ERR_INVALID                                    # misaligned workspace
-    assert lib.mpm_g2p2g(ct.byref(d), ct.byref(r), ct.c_void_p(4096), 10, ct.c_void_p(8192), grid, T, 1e-4, g3,
-                         100, status, None) == L.MPM_ERR_INVALID                       # sticky beyond n/2
-    assert lib.mpm_g2p2g(ct.byref(d), ct.byref(r), ct.c_void_p(4096), 10, ct.c_void_p(8192), grid, T, 1e-4, None,
-                         2, status, None) == L.MPM_ERR_INVALID                         # no gravity
-    assert lib.mpm_g2p2g(ct.byref(d), ct.byref(M.ranges(1e30, 1e30, 1e30)), ct.c_void_p(4096), 10, None, grid, T,
-                         1e-4, g3, 2, status, None) == L.MPM_ERR_OVERFLOW
+    G3, T3 = ct.c_void_p(1 << 20), ct.c_void_p(1 << 17)
+
+    def g2p2g(ws, grid_in, grid_out, tiles_out, grav=g3, sticky=2, rng=r, clear=(None, None)):
+        return lib.mpm_g2p2g(ct.byref(d), ct.byref(rng), ct.c_void_p(ws), 10, grid_in, grid_out, tiles_out,
+                             clear[0], clear[1], 1e-4, grav, sticky, status, None)
+    assert g2p2g(4096, grid, grid, T) == L.MPM_ERR_INVALID                             # grid_in == grid_out
+    assert g2p2g(4100, None, grid, T) == L.MPM_ERR_INVALID                             # misaligned workspace
+    assert g2p2g(4096, ct.c_void_p(8192), grid, T, sticky=100) == L.MPM_ERR_INVALID    # sticky beyond n/2
+    assert g2p2g(4096, ct.c_void_p(8192), grid, T, grav=None) == L.MPM_ERR_INVALID     # no gravity
+    assert g2p2g(4096, None, grid, T, rng=M.ranges(1e30, 1e30, 1e30)) == L.MPM_ERR_OVERFLOW
+    # the third grid: distinct from both others, its flags distinct from tiles_out, both aligned
+    assert g2p2g(4096, ct.c_void_p(8192), grid, T, clear=(grid, T3)) == L.MPM_ERR_INVALID
+    assert g2p2g(4096, ct.c_void_p(8192), grid, T, clear=(ct.c_void_p(8192), T3)) == L.MPM_ERR_INVALID
+    assert g2p2g(4096, ct.c_void_p(8192), grid, T, clear=(G3, T)) == L.MPM_ERR_INVALID
+    assert g2p2g(4096, ct.c_void_p(8192), grid, T, clear=(G3, None)) == L.MPM_ERR_INVALID
+    assert g2p2g(4096, ct.c_void_p(8192), grid, T, clear=(ct.c_void_p((1 << 20) + 4), T3)) == L.MPM_ERR_INVALID
     assert lib.mpm_grid_clear_tiles(ct.byref(d), ct.c_void_p(4100), T, None) == L.MPM_ERR_INVALID
     assert lib.mpm_grid_clear_tiles(None, grid, T, None) == L.MPM_ERR_INVALID
     assert lib.mpm_gather_records(ct.byref(d), ct.c_void_p(4096), ct.byref(L.mpm_particles(10, 4096, 4096, None,

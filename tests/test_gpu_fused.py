@@ -1,7 +1,8 @@
 """GPU parity of the resident substep (mpm_bin_resident, mpm_g2p2g,
 mpm_grid_clear_tiles, mpm_gather_records): the fused grid-to-particle and
 particle-to-grid kernel must give bit for bit the particle states and P2G
-grids of the separate steps and of the oracle's substeps.
+grids of the separate steps and of the oracle's substeps, with three grids
+(the kernel zeroes the one read before) and with two (a separate clear).
 
 Cases: the dam-break recipe on 64^3 nodes in lockstep with the oracle (re-binned
 every 10 substeps); the full 8M-particle 256^3 dam-break against the separate
@@ -64,11 +65,25 @@ def resident(mpm, w, host, ex):
     return parts, tr, rs
 
 
-def test_lockstep_with_oracle_small(mpm, oracle_lib):
+def two_grid_substep(rs):
+    """The same substep with two grids: no third grid passed, and the grid
+    just read cleared by mpm_grid_clear_tiles afterwards."""
+    import material_point_particle_amd._lib as L
+    a, b = rs.cur, (rs.cur + 1) % 2
+    L.mpm_g2p2g(rs.tr.desc, rs.tr.ranges, rs.tr.ws, rs.parts.n, rs.grids[a], rs.grids[b], rs.tiles[b], rs.dt,
+                rs.gravity, rs.sticky, rs.tr.status)
+    L.mpm_grid_clear_tiles(rs.tr.desc, rs.grids[a], rs.tiles[a])
+    rs.cur = b
+
+
+@pytest.mark.parametrize("grids", [3, 2])
+def test_lockstep_with_oracle_small(mpm, oracle_lib, grids):
     """Dam-break recipe, 2^16 particles on 64^3 nodes, 40 substeps re-binned
     every 10: after every substep k in 5, 10, ..., 40 the gathered state and
     the grid the resident loop holds (the P2G of that state) equal the
-    oracle's own trajectory."""
+    oracle's own trajectory.  Three grids: the grid read in the previous
+    substep is zero after each substep, flags included; two grids: the
+    separate flagged clear."""
     w = scaled(WORKLOADS["dam_3d_256"], 1 << 16, n=64)
     ex = w.extra
     host = build(w)
@@ -79,17 +94,24 @@ def test_lockstep_with_oracle_small(mpm, oracle_lib):
     torch.cuda.synchronize()
     assert_same(rs.grid.cpu().numpy(), grid0, "initial deposit")
     for k in range(1, 41):
-        rs.substep()
+        if grids == 3:
+            rs.substep()
+        else:
+            two_grid_substep(rs)
         _, _, state = oracle_substep(oracle_lib, w, state, ex)
         if k % 5 == 0:
             rs.gather()
             torch.cuda.synchronize()
-            say("fused lockstep", k)
+            say("fused lockstep", grids, k)
             got = parts.host()
             for key in ("x", "v", "C"):
                 assert_same(got[key], state[key], f"substep {k} {key}")
             nxt, _, _ = oracle_substep(oracle_lib, w, state, ex)
             assert_same(rs.grid.cpu().numpy(), nxt, f"grid after substep {k}")
+            if grids == 3 and k > 1:
+                cleared = (rs.cur + 1) % 3
+                assert int(rs.grids[cleared].abs().sum()) == 0 and int(rs.tiles[cleared].sum()) == 0
+                assert int(rs.tiles[rs.cur].sum()) > 0
         if k % 10 == 0:
             rs.rebin()
     assert tr.status.cpu().numpy().view(np.uint32).tolist() == [0, 0, 0, 0]
