@@ -5,7 +5,8 @@
  * Conventions for every entry point:
  *  - Pointers named as device pointers must point to device memory of the
  *    current HIP device; the caller owns them (the library allocates nothing
- *    and keeps no per-call state between calls).  Host pointers are read
+ *    and keeps no per-call state between calls; the one exception is the
+ *    static scratch of mpm_p2g_isplit_noalloc).  Host pointers are read
  *    before the call returns.
  *  - Work is enqueued on `stream` and the call returns without waiting; the
  *    library never synchronises the stream.  Results (and the status
@@ -51,7 +52,8 @@ typedef enum {
     MPM_ERR_OVERFLOW = -2,  /* the declared ranges could overflow the accumulators */
     MPM_ERR_DOMAIN = -3,    /* reserved: domain problems are counted on the device */
     MPM_ERR_WORKSPACE = -4, /* workspace smaller than mpm_workspace_bytes() */
-    MPM_ERR_HIP = -6        /* a HIP call or kernel launch failed */
+    MPM_ERR_HIP = -6,       /* a HIP call or kernel launch failed */
+    MPM_ERR_SCRATCH = -7    /* the input needs more than the library's static scratch holds */
 } mpm_status;
 
 /* The background grid of the quadratic-stencil transfer.  The domain is the
@@ -248,6 +250,29 @@ int mpm_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32
 int mpm_p2g_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
                    const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed, int64_t max_affine,
                    void *workspace, size_t workspace_bytes, int64_t *grid_out, uint32_t *status, hipStream_t stream);
+
+/* Bytes of the static device scratch mpm_p2g_isplit_noalloc uses (64 MiB per
+ * GPU, held from the library's load until the process ends). */
+#define MPM_ISPLIT_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+/* mpm_p2g_isplit's tiled path with its workspace taken from the library's
+ * static device scratch instead of the caller's memory: for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The call allocates nothing: it
+ * makes no hipMalloc/hipFree call and no torch allocation.  Arguments, result,
+ * status counters and errors are those of mpm_p2g_isplit with a workspace,
+ * and the grid is bit-identical to that call's.  The scratch is one array per
+ * GPU (MPM_ISPLIT_SCRATCH_BYTES); every call on a GPU reuses it and clears
+ * what must start at zero, so calls that overlap on one GPU (several streams,
+ * or host threads without ordering) race and must not be issued.  Inputs
+ * whose mpm_isplit_workspace_bytes(dim, n, np) exceeds
+ * MPM_ISPLIT_SCRATCH_BYTES are refused with MPM_ERR_SCRATCH before any launch
+ * (for example np up to about 8.3M particles on a 128^3 grid).  The first
+ * call on a device looks up that device's copy of the scratch once.
+ * Errors: those of mpm_p2g_isplit, MPM_ERR_SCRATCH. */
+int mpm_p2g_isplit_noalloc(int32_t dim, int32_t n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
+                           const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed,
+                           int64_t max_affine, int64_t *grid_out, uint32_t *status, hipStream_t stream);
 
 /* Bytes of the workspace mpm_p2g_isplit's tiled path needs for np particles
  * on n^dim nodes (tile counts and starts, each visited particle's rank and

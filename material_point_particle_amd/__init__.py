@@ -8,7 +8,7 @@ include/mpm.h); this package holds the HIP sources (csrc/), the build step
 from ._lib import (  # noqa: F401
     EXPORTS, LIB_PATH, MpmError, grid_desc, lib, mpm_bin_particles, mpm_bin_resident, mpm_check_bounds, mpm_g2p,
     mpm_g2p2g, mpm_gather_records, mpm_grid_clear_tiles, mpm_grid_update, mpm_isplit_workspace_bytes, mpm_p2g,
-    mpm_p2g_cic_split, mpm_p2g_isplit, mpm_strerror, mpm_version, mpm_workspace_bytes, mpm_workspace_layout,
+    mpm_p2g_cic_split, mpm_p2g_isplit, mpm_p2g_isplit_noalloc, mpm_strerror, mpm_version, mpm_workspace_bytes, mpm_workspace_layout,
     particles, ranges,
 )
 

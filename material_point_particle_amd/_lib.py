@@ -20,6 +20,9 @@ MPM_ERR_OVERFLOW = -2
 MPM_ERR_DOMAIN = -3
 MPM_ERR_WORKSPACE = -4
 MPM_ERR_HIP = -6
+MPM_ERR_SCRATCH = -7
+# bytes of the static device scratch of mpm_p2g_isplit_noalloc (include/mpm.h)
+MPM_ISPLIT_SCRATCH_BYTES = 64 * 1024 * 1024
 
 
 class MpmError(RuntimeError):
@@ -50,7 +53,8 @@ class mpm_ws_layout(ct.Structure):
 EXPORTS = ("mpm_version", "mpm_strerror", "mpm_check_bounds", "mpm_workspace_bytes", "mpm_workspace_layout",
            "mpm_bin_particles", "mpm_p2g", "mpm_p2g_cic_split", "mpm_p2g_isplit", "mpm_isplit_workspace_bytes",
            "mpm_grid_update", "mpm_grid_clear", "mpm_g2p", "mpm_neohookean_affine", "mpm_update_deformation",
-           "mpm_bin_resident", "mpm_g2p2g", "mpm_grid_clear_tiles", "mpm_gather_records")
+           "mpm_bin_resident", "mpm_g2p2g", "mpm_grid_clear_tiles", "mpm_gather_records",
+           "mpm_p2g_isplit_noalloc")
 
 _lib = None
 
@@ -87,6 +91,10 @@ def lib() -> ct.CDLL:
         L.mpm_p2g_isplit.argtypes = [ct.c_int32, ct.c_int32, ct.c_int64, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                      ct.c_void_p, ct.c_void_p, ct.c_int64, ct.c_int64, ct.c_int64, ct.c_void_p,
                                      ct.c_size_t, ct.c_void_p, ct.c_void_p, ct.c_void_p]
+        L.mpm_p2g_isplit_noalloc.restype = ct.c_int
+        L.mpm_p2g_isplit_noalloc.argtypes = [ct.c_int32, ct.c_int32, ct.c_int64, ct.c_void_p, ct.c_void_p,
+                                             ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int64, ct.c_int64,
+                                             ct.c_int64, ct.c_void_p, ct.c_void_p, ct.c_void_p]
         L.mpm_isplit_workspace_bytes.restype = ct.c_int
         L.mpm_isplit_workspace_bytes.argtypes = [ct.c_int32, ct.c_int32, ct.c_int64, P(ct.c_size_t)]
         L.mpm_grid_update.restype = ct.c_int
@@ -210,6 +218,15 @@ def mpm_p2g_isplit(dim: int, n: int, X, m, v, C, order, max_mass: int, max_speed
     _check(lib().mpm_p2g_isplit(dim, n, m.numel(), _ptr(X), _ptr(m), _ptr(v), _ptr(C), _ptr(order), max_mass,
                                 max_speed, max_affine, _ptr(workspace), ws_bytes, _ptr(grid), _ptr(status),
                                 _stream(stream)), "mpm_p2g_isplit")
+
+
+def mpm_p2g_isplit_noalloc(dim: int, n: int, X, m, v, C, order, max_mass: int, max_speed: int, max_affine: int,
+                           grid, status, stream=None) -> None:
+    """mpm_p2g_isplit's tiled path on the library's static device scratch
+    (no allocation by the library or by this wrapper)."""
+    _check(lib().mpm_p2g_isplit_noalloc(dim, n, m.numel(), _ptr(X), _ptr(m), _ptr(v), _ptr(C), _ptr(order), max_mass,
+                                        max_speed, max_affine, _ptr(grid), _ptr(status), _stream(stream)),
+           "mpm_p2g_isplit_noalloc")
 
 
 def mpm_bin_resident(desc, parts: mpm_particles, ws, status, stream=None) -> None:

@@ -193,6 +193,7 @@ const char *mpm_strerror(int code)
     case MPM_ERR_DOMAIN: return "particle outside the grid";
     case MPM_ERR_WORKSPACE: return "workspace too small";
     case MPM_ERR_HIP: return "HIP runtime or launch failure";
+    case MPM_ERR_SCRATCH: return "input needs more than the static scratch holds (MPM_ISPLIT_SCRATCH_BYTES)";
     default: return "unknown error";
     }
 }
@@ -366,9 +367,14 @@ int mpm_isplit_workspace_bytes(int32_t dim, int32_t n, int64_t np, size_t *bytes
     return MPM_OK;
 }
 
-int mpm_p2g_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
-                   const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed, int64_t max_affine,
-                   void *workspace, size_t workspace_bytes, int64_t *grid_out, uint32_t *status, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Arguments and bounds line of the integer-split transfer (both entry points).
+int check_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
+                 const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed, int64_t max_affine,
+                 const int64_t *grid_out, const uint32_t *status)
 {
     if ((dim != 2 && dim != 3) || n < 3 || n > 32767 || np < 0 || np > (int64_t)0xFFFFFFF0 || max_mass < 0 ||
         max_speed < 0 || max_affine < 0)
@@ -388,6 +394,20 @@ int mpm_p2g_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const i
                             ((long double)max_speed + (long double)dim * (long double)max_affine * 1.5L + 1.0L);
     if (line >= 4611686018427387904.0L || one >= 4611686018427387904.0L)
         return MPM_ERR_OVERFLOW;
+    return MPM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mpm_p2g_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
+                   const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed, int64_t max_affine,
+                   void *workspace, size_t workspace_bytes, int64_t *grid_out, uint32_t *status, hipStream_t stream)
+{
+    const int rc = check_isplit(dim, n, np, X, m, v, C, order, max_mass, max_speed, max_affine, grid_out, status);
+    if (rc != MPM_OK)
+        return rc;
     if (workspace) {
         if (!aligned(workspace, 256))
             return MPM_ERR_INVALID;
@@ -398,6 +418,25 @@ int mpm_p2g_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const i
     }
     return hip_status(launch_p2g_isplit(dim, n, np, X, m, v, C, order, max_mass, max_speed, max_affine, grid_out,
                                         status, stream));
+}
+
+int mpm_p2g_isplit_noalloc(int32_t dim, int32_t n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
+                           const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed,
+                           int64_t max_affine, int64_t *grid_out, uint32_t *status, hipStream_t stream)
+{
+    const int rc = check_isplit(dim, n, np, X, m, v, C, order, max_mass, max_speed, max_affine, grid_out, status);
+    if (rc != MPM_OK)
+        return rc;
+    if (isplit_layout(dim, n, np).total > (size_t)MPM_ISPLIT_SCRATCH_BYTES)
+        return MPM_ERR_SCRATCH;
+    if (np == 0)
+        return MPM_OK;
+    void *ws = nullptr;
+    const hipError_t e = isplit_scratch(&ws);
+    if (e != hipSuccess)
+        return MPM_ERR_HIP;
+    return hip_status(launch_p2g_isplit_tiled(dim, n, np, X, m, v, C, order, max_mass, max_speed, max_affine, ws,
+                                              grid_out, status, stream));
 }
 
 int mpm_grid_update(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, float *vg, float dt,

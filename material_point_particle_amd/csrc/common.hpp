@@ -253,6 +253,7 @@ struct IsplitLayout {      // byte offsets into the integer-split workspace
     int slot_shift;       // 2^slot_shift counters per tile
 };
 IsplitLayout isplit_layout(int dim, int n, int64_t np);
+hipError_t isplit_scratch(void **ptr);
 hipError_t launch_p2g_isplit_tiled(int dim, int n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
                                    const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed,
                                    int64_t max_affine, void *ws, int64_t *grid, uint32_t *status, hipStream_t s);

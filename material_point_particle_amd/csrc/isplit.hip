@@ -35,6 +35,8 @@
 //    block on chip with 64-bit LDS atomics and flushes it with one global
 //    atomic per non-zero node and channel, consecutive lanes on consecutive
 //    x nodes.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace mpmk {
@@ -590,6 +592,12 @@ int64_t is_blocks(int64_t work, int64_t cap_per_cu)
     return want < 1 ? 1 : (want > cap ? cap : want);
 }
 
+// The tiled path's workspace for callers that cannot allocate
+// (mpm_p2g_isplit_noalloc): a file-scope device array, one per GPU, held
+// until the process ends.  In host code `scratch` only names the symbol;
+// its device address comes from hipGetSymbolAddress (isplit_scratch below).
+__device__ __align__(256) uint8_t scratch[MPM_ISPLIT_SCRATCH_BYTES];
+
 }  // namespace
 
 IsplitLayout isplit_layout(int dim, int n, int64_t np)
@@ -687,6 +695,33 @@ hipError_t launch_p2g_isplit(int dim, int n, int64_t np, const int32_t *X, const
     else
         pick_width<2>(max_mass, max_speed, max_affine, launch, isplit_kernel<2, true>, isplit_kernel<2, false>);
     return hipGetLastError();
+}
+
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// with that device current and kept; every later call on the device reuses
+// it.  Returns the lookup's error (and leaves *ptr NULL) on failure.
+hipError_t isplit_scratch(void **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices];
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace mpmk

@@ -200,3 +200,23 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert lib.mpm_neohookean_affine(None, ct.byref(p4), *ok, None) == L.MPM_ERR_INVALID
     assert lib.mpm_update_deformation(ct.byref(d), ct.byref(p3), ct.c_void_p(4096), 1e-4, None) == L.MPM_ERR_INVALID
     assert lib.mpm_update_deformation(ct.byref(d), ct.byref(p4), None, 1e-4, None) == L.MPM_ERR_INVALID
+
+
+def test_noalloc_isplit_refuses_inputs_past_its_static_scratch():
+    """mpm_p2g_isplit_noalloc checks the workspace its input needs against the
+    static scratch before any device call; the pointers here are only aligned
+    placeholders, never dereferenced."""
+    lib = M.lib()
+    fake = ct.c_void_p(1 << 20)
+    np_ = 1 << 24
+    assert M.mpm_isplit_workspace_bytes(3, 128, np_) > L.MPM_ISPLIT_SCRATCH_BYTES
+    rc = lib.mpm_p2g_isplit_noalloc(3, 128, np_, fake, fake, fake, fake, None, 1, 1, 1, fake, fake, None)
+    assert rc == L.MPM_ERR_SCRATCH
+    assert "static scratch" in M.mpm_strerror(rc)
+    # the bounds line and argument checks come first, as in mpm_p2g_isplit
+    assert lib.mpm_p2g_isplit_noalloc(3, 128, np_, fake, fake, fake, fake, None, 1 << 40, 1 << 20, 1, fake, fake,
+                                      None) == L.MPM_ERR_OVERFLOW
+    assert lib.mpm_p2g_isplit_noalloc(4, 128, 10, fake, fake, fake, fake, None, 1, 1, 1, fake, fake,
+                                      None) == L.MPM_ERR_INVALID
+    # the largest 3D workload that fits: about 8.3M particles on 128^3
+    assert M.mpm_isplit_workspace_bytes(3, 128, 8_300_000) <= L.MPM_ISPLIT_SCRATCH_BYTES
