@@ -98,11 +98,16 @@ typedef struct {
     size_t tile_active;     /* uint8  [n_tiles] written by mpm_grid_update and mpm_grid_clear when
                                         given the bins: 1 for the node tiles that P2G from these
                                         bins can reach */
+    size_t meta;            /* uint32 [32]: [0] items, [2] binned particles, [3] work cursor,
+                                        [16..24] the binning's stamp
+                                        (grid, particle count, declared ranges, resident or
+                                        checked), which every reader of the bins compares with
+                                        its own arguments on the device.  (Offsets up to here do
+                                        not depend on the particle count.) */
     size_t items;           /* uint32 [max_items][4] work items: tile, first record, records (a
                                         slice of at most rows_per_item rows' worth of a tile's
                                         records), 0; handed out alternately the largest and
                                         smallest remaining                                 */
-    size_t meta;            /* uint32 [16]: [0] items, [2] binned particles, [3] P2G work cursor */
     size_t rank;            /* uint32 [n] rank of each particle inside its tile (internal)      */
     size_t slot;            /* uint32 [n] record index of each particle (0xFFFFFFFF: not binned) */
     size_t cell_key;        /* uint8  [n] local cell number of each record, in record order      */
@@ -135,7 +140,14 @@ const char *mpm_strerror(int code);
 int mpm_check_bounds(const mpm_grid_desc *grid, int64_t n_particles, const mpm_ranges *ranges,
                      double *log2_bound);
 
-/* Workspace size for binning n_particles on this grid (host-only). */
+/* Workspace size for binning n_particles on this grid (host-only).  The size
+ * and layout of a workspace follow from the grid and the particle count; every
+ * entry point that is handed a workspace also takes its size in bytes, refuses
+ * one that is too small for its own grid and count (MPM_ERR_WORKSPACE), and its
+ * kernels compare the stamp the binning left in the workspace with their own
+ * arguments before reading anything else (a mismatch is counted in status[3]
+ * and the call does nothing, or, for the restricted grid update and clear,
+ * falls back to every node). */
 int mpm_workspace_bytes(const mpm_grid_desc *grid, int64_t n_particles, size_t *bytes);
 
 /* Offsets of the arrays inside that workspace (host-only). */
@@ -180,18 +192,21 @@ int mpm_bin_particles(const mpm_grid_desc *grid, const mpm_particles *particles,
  * order and every scheduling.
  *   bins == NULL: one thread per particle of `particles`, 64-bit global
  *     atomics; skipped particles are counted in status[0]/status[1].
- *   bins != NULL: the workspace filled by mpm_bin_particles for these
- *     particles on this grid (particles may be NULL); one wavefront per
- *     work item (a slice of one tile's records) sorts the slice by cell in
- *     LDS, sums each 4 same-cell particles' contributions in registers,
- *     accumulates the tile's node block on chip and flushes it with one
- *     64-bit atomic per non-zero node and channel.
+ *   bins != NULL: the workspace (bins_bytes long) filled by
+ *     mpm_bin_particles for these particles on this grid with these ranges
+ *     (particles->n must be the count binned; its arrays are not read and may
+ *     be NULL); one wavefront per work item (a slice of one tile's records)
+ *     sorts the slice by cell in LDS, sums each 4 same-cell particles'
+ *     contributions in registers, accumulates the tile's node block on chip
+ *     and flushes it with one 64-bit atomic per non-zero node and channel.
+ *     A workspace whose stamp names another grid, particle count, declared
+ *     ranges or a resident binning adds nothing and is counted in status[3].
  * grid: device int64[1+dim][n]^dim, accumulated into (zero it first for a
  * fresh transfer).  The caller must have run mpm_check_bounds on `ranges`;
  * this call re-checks and refuses with MPM_ERR_OVERFLOW.
- * Errors: MPM_ERR_INVALID, MPM_ERR_OVERFLOW, MPM_ERR_HIP. */
+ * Errors: MPM_ERR_INVALID, MPM_ERR_OVERFLOW, MPM_ERR_WORKSPACE, MPM_ERR_HIP. */
 int mpm_p2g(const mpm_grid_desc *grid, const mpm_particles *particles, const mpm_ranges *ranges,
-            const void *bins, int64_t *grid_out, uint32_t *status, hipStream_t stream);
+            const void *bins, size_t bins_bytes, int64_t *grid_out, uint32_t *status, hipStream_t stream);
 
 /* Integer-split cloud-in-cell scatter in 2D ("particle to grid transfer in
  * checked integer arithmetic", sections "integers do not care about order"
@@ -325,10 +340,12 @@ int mpm_bin_resident(const mpm_grid_desc *grid, const mpm_particles *particles, 
  * mpm_grid_clear_tiles.  grid_clear != NULL: a third grid, neither grid_in
  * nor grid_out, whose node tiles flagged in tiles_clear (not tiles_out) are
  * zeroed in every channel, and those flags reset, as mpm_grid_clear_tiles
- * would (grid_clear == NULL: tiles_clear is ignored).  All pointers device.
+ * would (grid_clear == NULL: tiles_clear is ignored).  All pointers device;
+ * ws is ws_bytes long.  A workspace whose stamp names another grid or
+ * particle count does nothing and is counted in status[3].
  * Errors: MPM_ERR_INVALID, MPM_ERR_OVERFLOW (bounds for n_particles and the
- * ranges, as mpm_check_bounds), MPM_ERR_HIP. */
-int mpm_g2p2g(const mpm_grid_desc *grid, const mpm_ranges *ranges, void *ws, int64_t n_particles,
+ * ranges, as mpm_check_bounds), MPM_ERR_WORKSPACE, MPM_ERR_HIP. */
+int mpm_g2p2g(const mpm_grid_desc *grid, const mpm_ranges *ranges, void *ws, size_t ws_bytes, int64_t n_particles,
               const int64_t *grid_in, int64_t *grid_out, uint8_t *tiles_out, int64_t *grid_clear,
               uint8_t *tiles_clear, float dt, const float *gravity, int32_t sticky, uint32_t *status,
               hipStream_t stream);
@@ -340,10 +357,12 @@ int mpm_grid_clear_tiles(const mpm_grid_desc *grid, int64_t *grid_io, uint8_t *t
 
 /* Copies x, v and C of every binned particle from its record back to the
  * caller's arrays (particles->n must be the count the workspace was binned
- * with; m and particles that were not binned are left as they are).
- * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
-int mpm_gather_records(const mpm_grid_desc *grid, const void *ws, const mpm_particles *particles,
-                       hipStream_t stream);
+ * with; m and particles that were not binned are left as they are).  ws is
+ * ws_bytes long; a workspace whose stamp names another grid or particle count
+ * copies nothing and is counted in status[3].
+ * Errors: MPM_ERR_INVALID, MPM_ERR_WORKSPACE, MPM_ERR_HIP. */
+int mpm_gather_records(const mpm_grid_desc *grid, const void *ws, size_t ws_bytes, const mpm_particles *particles,
+                       uint32_t *status, hipStream_t stream);
 
 /* Grid update with consume-and-zero ("Implementation -- GPU Optimization &
  * Reference Codebases", section 1 four-phase step; section 2.1 and rule 4
@@ -353,8 +372,10 @@ int mpm_gather_records(const mpm_grid_desc *grid, const void *ws, const mpm_part
  * then v_d = v_d + (dt * g_d) (the product formed once in float32); where
  * M == 0, v = 0; nodes within `sticky` nodes of any face get v = 0; then
  * M and P are set to 0.
- * bins == NULL: every node.  bins != NULL: the workspace of the
- * mpm_bin_particles call whose P2G filled the grid (same grid descriptor);
+ * bins == NULL: every node.  bins != NULL: the workspace (bins_bytes long,
+ * at least its particle-count-independent prefix) of the mpm_bin_particles
+ * call whose P2G filled the grid (same grid descriptor; bins stamped for
+ * another grid fall back to every node);
  * only the nodes of 4^dim-node tiles that this P2G can reach (tiles whose
  * own or lower-neighbour cell tiles hold binned particles) are updated, and
  * vg elsewhere is left as it was.  Every other accumulator is already zero
@@ -364,22 +385,24 @@ int mpm_gather_records(const mpm_grid_desc *grid, const void *ws, const mpm_part
  * workspace.
  * grid: device int64[1+dim][n]^dim, read and zeroed.  vg: device
  * float[dim][n]^dim, written.  gravity: host float[dim].
- * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
-int mpm_grid_update(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, float *vg, float dt,
+ * Errors: MPM_ERR_INVALID, MPM_ERR_WORKSPACE, MPM_ERR_HIP. */
+int mpm_grid_update(const mpm_grid_desc *grid, void *bins, size_t bins_bytes, int64_t *grid_io, float *vg, float dt,
                     const float *gravity, int32_t sticky, hipStream_t stream);
 
 /* Accumulator reset before a P2G ("Implementation -- GPU Optimization &
  * Reference Codebases", section 2.1 and rule 4 of section 5: accumulators
  * must start each step at zero; sparse grids reset only the blocks in use).
  * bins == NULL: every channel of every node is set to 0.  bins != NULL: the
- * workspace of the mpm_bin_particles call whose P2G last added to this grid
- * (same grid descriptor); only the nodes of the 4^dim-node tiles that this
+ * workspace (bins_bytes long, as for mpm_grid_update) of the
+ * mpm_bin_particles call whose P2G last added to this grid (same grid
+ * descriptor; bins stamped for another grid fall back to every node); only
+ * the nodes of the 4^dim-node tiles that this
  * P2G could reach are zeroed (the set mpm_grid_update restricts itself to),
  * which zeroes the whole grid when it was zero before that P2G.  The call
  * writes the tile_active flags of the workspace.
  * grid: device int64[1+dim][n]^dim, written.
- * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
-int mpm_grid_clear(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, hipStream_t stream);
+ * Errors: MPM_ERR_INVALID, MPM_ERR_WORKSPACE, MPM_ERR_HIP. */
+int mpm_grid_clear(const mpm_grid_desc *grid, void *bins, size_t bins_bytes, int64_t *grid_io, hipStream_t stream);
 
 /* APIC grid-to-particle gather and advection ("Implementation -- GPU
  * Optimization & Reference Codebases", sections 1 and 3.1).  Per particle,

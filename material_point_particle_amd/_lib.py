@@ -44,7 +44,7 @@ class mpm_ranges(ct.Structure):
 
 
 class mpm_ws_layout(ct.Structure):
-    _fields_ = [(name, ct.c_size_t) for name in ("tile_count", "tile_start", "tile_active", "items", "meta", "rank",
+    _fields_ = [(name, ct.c_size_t) for name in ("tile_count", "tile_start", "tile_active", "meta", "items", "rank",
                                                   "slot", "cell_key", "sorted", "scan_tmp")]
     _fields_ += [(name, ct.c_int64) for name in ("n_cells", "n_tiles", "max_items", "n_fields", "rows_per_item")]
     _fields_ += [("total_bytes", ct.c_size_t)]
@@ -82,8 +82,8 @@ def lib() -> ct.CDLL:
         L.mpm_bin_particles.argtypes = [P(mpm_grid_desc), P(mpm_particles), P(mpm_ranges), ct.c_void_p, ct.c_size_t,
                                         ct.c_void_p, ct.c_void_p]
         L.mpm_p2g.restype = ct.c_int
-        L.mpm_p2g.argtypes = [P(mpm_grid_desc), P(mpm_particles), P(mpm_ranges), ct.c_void_p, ct.c_void_p,
-                              ct.c_void_p, ct.c_void_p]
+        L.mpm_p2g.argtypes = [P(mpm_grid_desc), P(mpm_particles), P(mpm_ranges), ct.c_void_p, ct.c_size_t,
+                              ct.c_void_p, ct.c_void_p, ct.c_void_p]
         L.mpm_p2g_cic_split.restype = ct.c_int
         L.mpm_p2g_cic_split.argtypes = [ct.c_int64, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int32,
                                         ct.c_int64, ct.c_int64, ct.c_void_p, ct.c_void_p, ct.c_void_p]
@@ -98,10 +98,10 @@ def lib() -> ct.CDLL:
         L.mpm_isplit_workspace_bytes.restype = ct.c_int
         L.mpm_isplit_workspace_bytes.argtypes = [ct.c_int32, ct.c_int32, ct.c_int64, P(ct.c_size_t)]
         L.mpm_grid_update.restype = ct.c_int
-        L.mpm_grid_update.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_float,
-                                      P(ct.c_float), ct.c_int32, ct.c_void_p]
+        L.mpm_grid_update.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_size_t, ct.c_void_p, ct.c_void_p,
+                                      ct.c_float, P(ct.c_float), ct.c_int32, ct.c_void_p]
         L.mpm_grid_clear.restype = ct.c_int
-        L.mpm_grid_clear.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p]
+        L.mpm_grid_clear.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_size_t, ct.c_void_p, ct.c_void_p]
         L.mpm_g2p.restype = ct.c_int
         L.mpm_g2p.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_float, ct.c_void_p, ct.c_void_p]
         L.mpm_neohookean_affine.restype = ct.c_int
@@ -113,13 +113,14 @@ def lib() -> ct.CDLL:
         L.mpm_bin_resident.argtypes = [P(mpm_grid_desc), P(mpm_particles), ct.c_void_p, ct.c_size_t, ct.c_void_p,
                                        ct.c_void_p]
         L.mpm_g2p2g.restype = ct.c_int
-        L.mpm_g2p2g.argtypes = [P(mpm_grid_desc), P(mpm_ranges), ct.c_void_p, ct.c_int64, ct.c_void_p, ct.c_void_p,
-                                ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_float, P(ct.c_float), ct.c_int32,
-                                ct.c_void_p, ct.c_void_p]
+        L.mpm_g2p2g.argtypes = [P(mpm_grid_desc), P(mpm_ranges), ct.c_void_p, ct.c_size_t, ct.c_int64, ct.c_void_p,
+                                ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_float, P(ct.c_float),
+                                ct.c_int32, ct.c_void_p, ct.c_void_p]
         L.mpm_grid_clear_tiles.restype = ct.c_int
         L.mpm_grid_clear_tiles.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p]
         L.mpm_gather_records.restype = ct.c_int
-        L.mpm_gather_records.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_void_p]
+        L.mpm_gather_records.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_size_t, P(mpm_particles), ct.c_void_p,
+                                         ct.c_void_p]
         _lib = L
     return _lib
 
@@ -133,6 +134,10 @@ def _ptr(t) -> int | None:
     if t is None:
         return None
     return t.data_ptr()
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream(stream) -> int | None:
@@ -197,8 +202,8 @@ def mpm_bin_particles(desc, parts: mpm_particles, rng: mpm_ranges, ws, status, s
 
 
 def mpm_p2g(desc, parts: mpm_particles, rng: mpm_ranges, bins, grid, status, stream=None) -> None:
-    _check(lib().mpm_p2g(ct.byref(desc), ct.byref(parts), ct.byref(rng), _ptr(bins), _ptr(grid), _ptr(status),
-                         _stream(stream)), "mpm_p2g")
+    _check(lib().mpm_p2g(ct.byref(desc), ct.byref(parts), ct.byref(rng), _ptr(bins), _nbytes(bins), _ptr(grid),
+                         _ptr(status), _stream(stream)), "mpm_p2g")
 
 
 def mpm_p2g_cic_split(X, m, vel, order, cells: int, max_mass: int, max_speed: int, grid, status, stream=None) -> None:
@@ -237,7 +242,8 @@ def mpm_bin_resident(desc, parts: mpm_particles, ws, status, stream=None) -> Non
 def mpm_g2p2g(desc, rng: mpm_ranges, ws, n_particles: int, grid_in, grid_out, tiles_out, dt: float, gravity,
               sticky: int, status, stream=None, grid_clear=None, tiles_clear=None) -> None:
     g = (ct.c_float * 3)(*(list(gravity) + [0.0] * (3 - len(gravity))))
-    _check(lib().mpm_g2p2g(ct.byref(desc), ct.byref(rng), _ptr(ws), n_particles, _ptr(grid_in), _ptr(grid_out),
+    _check(lib().mpm_g2p2g(ct.byref(desc), ct.byref(rng), _ptr(ws), _nbytes(ws), n_particles, _ptr(grid_in),
+                           _ptr(grid_out),
                            _ptr(tiles_out), _ptr(grid_clear), _ptr(tiles_clear), dt, g, sticky, _ptr(status),
                            _stream(stream)), "mpm_g2p2g")
 
@@ -247,19 +253,20 @@ def mpm_grid_clear_tiles(desc, grid, tiles, stream=None) -> None:
            "mpm_grid_clear_tiles")
 
 
-def mpm_gather_records(desc, ws, parts: mpm_particles, stream=None) -> None:
-    _check(lib().mpm_gather_records(ct.byref(desc), _ptr(ws), ct.byref(parts), _stream(stream)),
-           "mpm_gather_records")
+def mpm_gather_records(desc, ws, parts: mpm_particles, status, stream=None) -> None:
+    _check(lib().mpm_gather_records(ct.byref(desc), _ptr(ws), _nbytes(ws), ct.byref(parts), _ptr(status),
+                                    _stream(stream)), "mpm_gather_records")
 
 
 def mpm_grid_update(desc, bins, grid, vg, dt: float, gravity, sticky: int, stream=None) -> None:
     g = (ct.c_float * 3)(*(list(gravity) + [0.0] * (3 - len(gravity))))
-    _check(lib().mpm_grid_update(ct.byref(desc), _ptr(bins), _ptr(grid), _ptr(vg), dt, g, sticky, _stream(stream)),
-           "mpm_grid_update")
+    _check(lib().mpm_grid_update(ct.byref(desc), _ptr(bins), _nbytes(bins), _ptr(grid), _ptr(vg), dt, g, sticky,
+                                 _stream(stream)), "mpm_grid_update")
 
 
 def mpm_grid_clear(desc, bins, grid, stream=None) -> None:
-    _check(lib().mpm_grid_clear(ct.byref(desc), _ptr(bins), _ptr(grid), _stream(stream)), "mpm_grid_clear")
+    _check(lib().mpm_grid_clear(ct.byref(desc), _ptr(bins), _nbytes(bins), _ptr(grid), _stream(stream)),
+           "mpm_grid_clear")
 
 
 def mpm_g2p(desc, vg, parts: mpm_particles, dt: float, status, stream=None) -> None:

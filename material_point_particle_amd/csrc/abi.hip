@@ -123,9 +123,9 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     const int64_t n1 = np > 0 ? np : 1;
     o->tile_count = take(u4 * (size_t)n_tiles);
     o->tile_start = take(u4 * (size_t)(n_tiles + 1));
-    o->tile_active = take((size_t)n_tiles);          // (offsets up to here do not depend on np)
+    o->tile_active = take((size_t)n_tiles);
+    o->meta = take(u4 * kMetaWords);                 // (offsets up to here do not depend on np)
     o->items = take(u4 * 4 * (size_t)max_items);
-    o->meta = take(u4 * 16);
     o->rank = take(u4 * (size_t)n1);
     o->slot = take(u4 * (size_t)n1);
     o->cell_key = take((size_t)n1);
@@ -139,10 +139,42 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     o->total_bytes = off;
 }
 
-BinView bin_view(void *ws, const mpm_ws_layout &l)
+// Bytes of the workspace prefix whose offsets do not depend on the particle
+// count (tile arrays and meta): what the grid update and clear read.
+size_t fixed_prefix_bytes(const mpm_grid_desc *g)
+{
+    mpm_ws_layout l;
+    make_layout(g, 0, &l);
+    return l.meta + sizeof(uint32_t) * kMetaWords;
+}
+
+uint32_t float_bits(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+BinStamp make_stamp(const mpm_grid_desc *g, int64_t np, RangesF r, bool keep)
+{
+    BinStamp s;
+    s.magic = kStampMagic;
+    s.dim = (uint32_t)g->dim;
+    s.n = (uint32_t)g->n;
+    s.np_lo = (uint32_t)((uint64_t)np & 0xFFFFFFFFu);
+    s.np_hi = (uint32_t)((uint64_t)np >> 32);
+    s.max_mass = keep ? 0u : float_bits(r.max_mass);
+    s.max_speed = keep ? 0u : float_bits(r.max_speed);
+    s.max_affine = keep ? 0u : float_bits(r.max_affine);
+    s.keep = keep ? 1u : 0u;
+    return s;
+}
+
+BinView bin_view(void *ws, const mpm_ws_layout &l, const BinStamp &stamp)
 {
     char *b = (char *)ws;
     BinView v;
+    v.stamp = stamp;
     v.tile_count = (uint32_t *)(b + l.tile_count);
     v.tile_start = (uint32_t *)(b + l.tile_start);
     v.items = (uint32_t *)(b + l.items);
@@ -247,9 +279,10 @@ int mpm_bin_particles(const mpm_grid_desc *grid, const mpm_particles *particles,
     make_layout(grid, particles->n, &l);
     if (ws_bytes < l.total_bytes)
         return MPM_ERR_WORKSPACE;
-    const BinView b = bin_view(ws, l);
+    const RangesF rf = ranges_f(ranges);
+    const BinView b = bin_view(ws, l, make_stamp(grid, particles->n, rf, false));
     Fields f{ particles->x, particles->v, particles->C, particles->m, particles->n };
-    return hip_status(launch_bin(grid->dim, grid->n, f, ranges_f(ranges), b, status, stream));
+    return hip_status(launch_bin(grid->dim, grid->n, f, rf, b, status, stream));
 }
 
 int mpm_bin_resident(const mpm_grid_desc *grid, const mpm_particles *particles, void *ws, size_t ws_bytes,
@@ -264,13 +297,13 @@ int mpm_bin_resident(const mpm_grid_desc *grid, const mpm_particles *particles, 
     make_layout(grid, particles->n, &l);
     if (ws_bytes < l.total_bytes)
         return MPM_ERR_WORKSPACE;
-    const BinView b = bin_view(ws, l);
-    Fields f{ particles->x, particles->v, particles->C, particles->m, particles->n };
     const RangesF none{ 0.0f, 0.0f, 0.0f };
+    const BinView b = bin_view(ws, l, make_stamp(grid, particles->n, none, true));
+    Fields f{ particles->x, particles->v, particles->C, particles->m, particles->n };
     return hip_status(launch_bin(grid->dim, grid->n, f, none, b, status, stream, true));
 }
 
-int mpm_g2p2g(const mpm_grid_desc *grid, const mpm_ranges *ranges, void *ws, int64_t n_particles,
+int mpm_g2p2g(const mpm_grid_desc *grid, const mpm_ranges *ranges, void *ws, size_t ws_bytes, int64_t n_particles,
               const int64_t *grid_in, int64_t *grid_out, uint8_t *tiles_out, int64_t *grid_clear,
               uint8_t *tiles_clear, float dt, const float *gravity, int32_t sticky, uint32_t *status,
               hipStream_t stream)
@@ -290,9 +323,13 @@ int mpm_g2p2g(const mpm_grid_desc *grid, const mpm_ranges *ranges, void *ws, int
         return rc;
     mpm_ws_layout l;
     make_layout(grid, n_particles, &l);
+    if (ws_bytes < l.total_bytes)
+        return MPM_ERR_WORKSPACE;
     const float g3[3] = { gravity ? gravity[0] : 0.0f, gravity ? gravity[1] : 0.0f,
                           gravity && grid->dim == 3 ? gravity[2] : 0.0f };
-    return hip_status(launch_g2p2g(grid->dim, grid->n, grid->frac_bits, bin_view(ws, l), ranges_f(ranges), grid_in,
+    const RangesF rf = ranges_f(ranges);
+    const BinView b = bin_view(ws, l, make_stamp(grid, n_particles, rf, true));
+    return hip_status(launch_g2p2g(grid->dim, grid->n, grid->frac_bits, b, rf, grid_in,
                                    grid_out, tiles_out, grid_clear, grid_clear ? tiles_clear : nullptr, dt, g3, sticky,
                                    status, stream));
 }
@@ -304,21 +341,26 @@ int mpm_grid_clear_tiles(const mpm_grid_desc *grid, int64_t *grid_io, uint8_t *t
     return hip_status(launch_grid_clear_tiles(grid->dim, grid->n, grid_io, tiles, stream));
 }
 
-int mpm_gather_records(const mpm_grid_desc *grid, const void *ws, const mpm_particles *particles, hipStream_t stream)
+int mpm_gather_records(const mpm_grid_desc *grid, const void *ws, size_t ws_bytes, const mpm_particles *particles,
+                       uint32_t *status, hipStream_t stream)
 {
     int rc;
     if ((rc = check_desc(grid)) != MPM_OK || (rc = check_particles(grid, particles, true, false)) != MPM_OK)
         return rc;
-    if (!aligned(ws, 256) || (particles->n > 0 && !particles->C))
+    if (!aligned(ws, 256) || !aligned(status, 4) || (particles->n > 0 && !particles->C))
         return MPM_ERR_INVALID;
     mpm_ws_layout l;
     make_layout(grid, particles->n, &l);
-    return hip_status(launch_gather_records(grid->dim, particles->n, bin_view((void *)ws, l), particles->x,
-                                            particles->v, particles->C, stream));
+    if (ws_bytes < l.total_bytes)
+        return MPM_ERR_WORKSPACE;
+    const RangesF none{ 0.0f, 0.0f, 0.0f };
+    return hip_status(launch_gather_records(grid->dim, particles->n,
+                                            bin_view((void *)ws, l, make_stamp(grid, particles->n, none, true)),
+                                            particles->x, particles->v, particles->C, status, stream));
 }
 
 int mpm_p2g(const mpm_grid_desc *grid, const mpm_particles *particles, const mpm_ranges *ranges, const void *bins,
-            int64_t *grid_out, uint32_t *status, hipStream_t stream)
+            size_t bins_bytes, int64_t *grid_out, uint32_t *status, hipStream_t stream)
 {
     int rc;
     if ((rc = check_desc(grid)) != MPM_OK || (rc = check_ranges(ranges)) != MPM_OK ||
@@ -333,8 +375,10 @@ int mpm_p2g(const mpm_grid_desc *grid, const mpm_particles *particles, const mpm
             return MPM_ERR_INVALID;
         mpm_ws_layout l;
         make_layout(grid, particles->n, &l);
-        return hip_status(launch_p2g_tiled(grid->dim, grid->n, grid->frac_bits, bin_view((void *)bins, l), grid_out,
-                                           status, stream));
+        if (bins_bytes < l.total_bytes)
+            return MPM_ERR_WORKSPACE;
+        const BinView b = bin_view((void *)bins, l, make_stamp(grid, particles->n, ranges_f(ranges), false));
+        return hip_status(launch_p2g_tiled(grid->dim, grid->n, grid->frac_bits, b, grid_out, status, stream));
     }
     Fields f{ particles->x, particles->v, particles->C, particles->m, particles->n };
     return hip_status(launch_p2g_direct(grid->dim, grid->n, grid->frac_bits, f, nullptr, ranges_f(ranges), grid_out,
@@ -439,7 +483,7 @@ int mpm_p2g_isplit_noalloc(int32_t dim, int32_t n, int64_t np, const int32_t *X,
                                               grid_out, status, stream));
 }
 
-int mpm_grid_update(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, float *vg, float dt,
+int mpm_grid_update(const mpm_grid_desc *grid, void *bins, size_t bins_bytes, int64_t *grid_io, float *vg, float dt,
                     const float *gravity, int32_t sticky, hipStream_t stream)
 {
     if (check_desc(grid) != MPM_OK || !aligned(grid_io, 8) || !aligned(vg, 4) || !gravity || sticky < 0 ||
@@ -448,21 +492,27 @@ int mpm_grid_update(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, flo
     float g3[3] = { gravity[0], gravity[1], grid->dim == 3 ? gravity[2] : 0.0f };
     if (!bins)
         return hip_status(launch_grid_update(grid->dim, grid->n, grid_io, vg, dt, g3, sticky, nullptr, stream));
+    if (bins_bytes < fixed_prefix_bytes(grid))
+        return MPM_ERR_WORKSPACE;
     mpm_ws_layout l;
-    make_layout(grid, 0, &l);         // tile_count and tile_active come first: their offsets do not depend on n
-    const BinView v = bin_view(bins, l);
+    make_layout(grid, 0, &l);         // tile arrays and meta come first: their offsets do not depend on n
+    const RangesF none{ 0.0f, 0.0f, 0.0f };
+    const BinView v = bin_view(bins, l, make_stamp(grid, 0, none, true));
     return hip_status(launch_grid_update(grid->dim, grid->n, grid_io, vg, dt, g3, sticky, &v, stream));
 }
 
-int mpm_grid_clear(const mpm_grid_desc *grid, void *bins, int64_t *grid_io, hipStream_t stream)
+int mpm_grid_clear(const mpm_grid_desc *grid, void *bins, size_t bins_bytes, int64_t *grid_io, hipStream_t stream)
 {
     if (check_desc(grid) != MPM_OK || !aligned(grid_io, 8) || (bins && !aligned(bins, 256)))
         return MPM_ERR_INVALID;
     if (!bins)
         return hip_status(launch_grid_clear(grid->dim, grid->n, grid_io, nullptr, stream));
+    if (bins_bytes < fixed_prefix_bytes(grid))
+        return MPM_ERR_WORKSPACE;
     mpm_ws_layout l;
-    make_layout(grid, 0, &l);         // tile_count and tile_active come first: their offsets do not depend on n
-    const BinView v = bin_view(bins, l);
+    make_layout(grid, 0, &l);         // tile arrays and meta come first: their offsets do not depend on n
+    const RangesF none{ 0.0f, 0.0f, 0.0f };
+    const BinView v = bin_view(bins, l, make_stamp(grid, 0, none, true));
     return hip_status(launch_grid_clear(grid->dim, grid->n, grid_io, &v, stream));
 }
 

@@ -56,13 +56,20 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *t
     return r;
 }
 
-__global__ void fill2_u32_kernel(uint32_t *__restrict__ p, int64_t np, uint32_t *__restrict__ q, int64_t nq)
+// Zeroes the tile counts and the meta words, and writes the binning's stamp.
+__global__ void bin_reset_kernel(uint32_t *__restrict__ tile_count, int64_t n_tiles, uint32_t *__restrict__ meta,
+                                 BinStamp stamp)
 {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < np + nq; i += (int64_t)gridDim.x * blockDim.x) {
-        if (i < np)
-            p[i] = 0u;
-        else
-            q[i - np] = 0u;
+    const uint32_t *sw = reinterpret_cast<const uint32_t *>(&stamp);
+    constexpr int kStampWords = (int)(sizeof(BinStamp) / 4);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_tiles + kMetaWords;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        if (i < n_tiles) {
+            tile_count[i] = 0u;
+        } else {
+            const int w = (int)(i - n_tiles);
+            meta[w] = (w >= kMetaStamp && w < kMetaStamp + kStampWords) ? sw[w - kMetaStamp] : 0u;
+        }
     }
 }
 
@@ -528,8 +535,8 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
 {
     const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3);
     const int ntx = n / kTile;
-    hipLaunchKernelGGL(fill2_u32_kernel, dim3(blocks_for(b.n_tiles + 16, 256)), dim3(256), 0, s, b.tile_count,
-                       b.n_tiles, b.meta, (int64_t)16);
+    hipLaunchKernelGGL(bin_reset_kernel, dim3(blocks_for(b.n_tiles + kMetaWords, 256)), dim3(256), 0, s, b.tile_count,
+                       b.n_tiles, b.meta, b.stamp);
     // particles per thread of a chunk: enough chunks for two blocks per CU, at most kMaxPer
     const int64_t span = (int64_t)kBinThreads * device_cu_count() * 2;
     int64_t per = (p.n + span - 1) / span;
@@ -582,9 +589,16 @@ namespace {
 template <int DIM>
 __global__ void __launch_bounds__(256) gather_records_kernel(int64_t np, const uint32_t *__restrict__ slot,
                                                              const float *__restrict__ sorted, float *__restrict__ x,
-                                                             float *__restrict__ v, float *__restrict__ C)
+                                                             float *__restrict__ v, float *__restrict__ C,
+                                                             const uint32_t *__restrict__ meta, BinStamp stamp,
+                                                             uint32_t *__restrict__ status)
 {
     constexpr int R = rec_floats<DIM>();
+    if (!stamp_matches(meta, stamp, false)) {        // binned for another grid or count: copy nothing
+        if (blockIdx.x == 0 && threadIdx.x == 0)
+            atomicAdd(&status[3], 1u);
+        return;
+    }
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
         const uint32_t r = slot[p];
         if (r == kEmpty)
@@ -612,16 +626,17 @@ __global__ void __launch_bounds__(256) gather_records_kernel(int64_t np, const u
 
 }  // namespace
 
-hipError_t launch_gather_records(int dim, int64_t np, const BinView &b, float *x, float *v, float *C, hipStream_t s)
+hipError_t launch_gather_records(int dim, int64_t np, const BinView &b, float *x, float *v, float *C,
+                                 uint32_t *status, hipStream_t s)
 {
     if (np == 0)
         return hipSuccess;
     if (dim == 3)
         hipLaunchKernelGGL(gather_records_kernel<3>, dim3(blocks_for(np, 256)), dim3(256), 0, s, np, b.slot, b.sorted,
-                           x, v, C);
+                           x, v, C, b.meta, b.stamp, status);
     else
         hipLaunchKernelGGL(gather_records_kernel<2>, dim3(blocks_for(np, 256)), dim3(256), 0, s, np, b.slot, b.sorted,
-                           x, v, C);
+                           x, v, C, b.meta, b.stamp, status);
     return hipGetLastError();
 }
 

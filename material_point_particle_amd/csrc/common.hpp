@@ -228,11 +228,44 @@ struct Fields {           // component-major particle arrays of n particles
     int64_t n;
 };
 
+// Words of the binning workspace's meta array (uint32[kMetaWords]).  It sits
+// at an offset that does not depend on the particle count, so every entry
+// point that is handed a workspace can find it.
+constexpr int kMetaWords = 32;
+constexpr int kMetaItems = 0;        // work items
+constexpr int kMetaBinned = 2;       // binned particles
+constexpr int kMetaCursor = 3;       // work cursor of P2G and the fused substep
+constexpr int kMetaStamp = 16;       // the binning's stamp (BinStamp)
+constexpr uint32_t kStampMagic = 0x4D504D42u;
+
+// What a binning was made for: written into meta by the binning, compared by
+// every kernel that reads the bins before it reads anything else, so that a
+// workspace binned for another grid, particle count or range declaration is
+// refused on the device (status[3]) instead of being read with the wrong
+// layout or bounds.  keep: records kept as they are (the resident binning),
+// without range checks or the cell sort.
+struct BinStamp {
+    uint32_t magic, dim, n, np_lo, np_hi, max_mass, max_speed, max_affine, keep;
+};
+static_assert(sizeof(BinStamp) / 4 + kMetaStamp <= kMetaWords, "the stamp fits the meta words");
+
+// ranges: also compare the declared ranges and require a checked binning
+// (records range-checked), as the tiled P2G needs.
+__device__ __forceinline__ bool stamp_matches(const uint32_t *meta, const BinStamp &s, bool ranges)
+{
+    const uint32_t *m = meta + kMetaStamp;
+    bool ok = m[0] == s.magic && m[1] == s.dim && m[2] == s.n && m[3] == s.np_lo && m[4] == s.np_hi;
+    if (ranges)
+        ok = ok && m[5] == s.max_mass && m[6] == s.max_speed && m[7] == s.max_affine && m[8] == 0u;
+    return ok;
+}
+
 struct BinView {          // the workspace arrays, as typed device pointers
     uint32_t *tile_count, *tile_start, *items, *meta, *rank, *slot, *scan_tmp;
     uint8_t *cell_key, *tile_active;
     float *sorted;
     int64_t n_cells, n_tiles, max_items, n_fields;
+    BinStamp stamp;       // the binning this view is for (written by launch_bin, expected by readers)
 };
 
 hipError_t launch_p2g_direct(int dim, int n, int frac_bits, const Fields &p, const uint32_t *order, RangesF r,
@@ -259,7 +292,8 @@ hipError_t launch_p2g_isplit_tiled(int dim, int n, int64_t np, const int32_t *X,
                                    int64_t max_affine, void *ws, int64_t *grid, uint32_t *status, hipStream_t s);
 hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView &b, uint32_t *status,
                       hipStream_t s, bool keep = false);
-hipError_t launch_gather_records(int dim, int64_t np, const BinView &b, float *x, float *v, float *C, hipStream_t s);
+hipError_t launch_gather_records(int dim, int64_t np, const BinView &b, float *x, float *v, float *C,
+                                 uint32_t *status, hipStream_t s);
 hipError_t launch_grid_update(int dim, int n, int64_t *grid, float *vg, float dt, const float *gravity,
                               int sticky, const BinView *bins, hipStream_t s);
 hipError_t launch_grid_clear(int dim, int n, int64_t *grid, const BinView *bins, hipStream_t s);

@@ -83,7 +83,14 @@ g2p2g_kernel(FusedArgs f)
     const TiledArgs &a = f.t;
     float *vw = reinterpret_cast<float *>(acc);
     const int lane = threadIdx.x;
-    const uint32_t n_items = a.meta[0];
+    // a workspace binned for another grid or particle count: refused before
+    // anything else is read (the whole call does nothing)
+    if (!stamp_matches(a.meta, a.stamp, false)) {
+        if (blockIdx.x == 0 && lane == 0)
+            atomicAdd(&a.status[3], 1u);
+        return;
+    }
+    const uint32_t n_items = a.meta[kMetaItems];
     const int n = a.n;
     const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
     for (int i = lane; i < TS::ch * TS::nodes; i += kWave)
@@ -355,7 +362,8 @@ hipError_t launch_g2p2g(int dim, int n, int frac_bits, const BinView &b, RangesF
     a.cell_key = b.cell_key;
     a.items = b.items;
     a.meta = b.meta;
-    a.cursor = b.meta + 3;
+    a.stamp = b.stamp;
+    a.cursor = b.meta + kMetaCursor;
     a.n = n;
     a.ntx = n / kTile;
     a.nf = (float)n;

@@ -13,12 +13,21 @@ namespace {
 
 // Node tile t (the 4^dim nodes whose indices divided by 4 give t) can receive
 // deposits from the node blocks of cell tiles t - e, e in {0,1}^dim: a block
-// covers the 6 nodes from its tile's first node on each axis.
+// covers the 6 nodes from its tile's first node on each axis.  Bins whose
+// stamp names another grid mark every tile (the restricted pass becomes the
+// full one, which is always correct).
 template <int DIM>
 __global__ void __launch_bounds__(256) active_tiles_kernel(const uint32_t *__restrict__ tile_count, int ntx,
-                                                           int64_t n_tiles, uint8_t *__restrict__ active)
+                                                           int64_t n_tiles, uint8_t *__restrict__ active,
+                                                           const uint32_t *__restrict__ meta, uint32_t n)
 {
+    const uint32_t *st = meta + kMetaStamp;
+    const bool same_grid = st[0] == kStampMagic && st[1] == (uint32_t)DIM && st[2] == n;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n_tiles; t += (int64_t)gridDim.x * blockDim.x) {
+        if (!same_grid) {
+            active[t] = 1;
+            continue;
+        }
         const int tx = (int)(t % ntx), ty = (int)((t / ntx) % ntx), tz = DIM == 3 ? (int)(t / ((int64_t)ntx * ntx)) : 0;
         bool act = false;
 #pragma unroll
@@ -158,10 +167,10 @@ void mark_active(int dim, int n, const BinView *bins, hipStream_t s)
     const int ntx = n / kTile;
     if (dim == 3)
         hipLaunchKernelGGL(active_tiles_kernel<3>, dim3(blocks_for(bins->n_tiles, 256)), dim3(256), 0, s,
-                           bins->tile_count, ntx, bins->n_tiles, bins->tile_active);
+                           bins->tile_count, ntx, bins->n_tiles, bins->tile_active, bins->meta, (uint32_t)n);
     else
         hipLaunchKernelGGL(active_tiles_kernel<2>, dim3(blocks_for(bins->n_tiles, 256)), dim3(256), 0, s,
-                           bins->tile_count, ntx, bins->n_tiles, bins->tile_active);
+                           bins->tile_count, ntx, bins->n_tiles, bins->tile_active, bins->meta, (uint32_t)n);
 }
 
 template <int OP>

@@ -8,9 +8,16 @@ namespace mpmk {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Direct path: one thread per particle, 64-bit global atomics per
-// contribution.  No binning needed; the baseline the tiled path is measured
-// against and the path for unbinned particle sets.
+// Tiled path: one wavefront per work item (a slice of one tile's records),
+// items taken from a work cursor.  Per item: the slice's records sorted by
+// cell on chip into groups of four same-cell records (sort_item; a cell's last
+// group completed with pad entries read with zero mass: records are
+// range-checked at binning, so a pad's velocity and affine entries are finite
+// and its products exact zeros); per row and lane, the group's contributions
+// per stencil node and channel rounded and summed exactly in float64
+// registers, one LDS atomic per node and channel into the tile's node block;
+// then the block flushed with one 64-bit global atomic per non-zero node and
+// channel and left zeroed.
 template <int DIM>
 __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 p2g_tiled_kernel(TiledArgs a)
@@ -28,7 +35,14 @@ p2g_tiled_kernel(TiledArgs a)
     static_assert(groups_bound<DIM>(slice_records<DIM>()) <= kMaxGroups, "a slice's groups fit the entry rows");
     static_assert(cells_per_tile<DIM>() <= (uint32_t)kWave, "one lane per cell of a tile");
     const int lane = threadIdx.x;
-    const uint32_t n_items = a.meta[0];
+    // bins made for another grid, particle count or range declaration, or by
+    // the resident binning: refused before anything else is read
+    if (!stamp_matches(a.meta, a.stamp, true)) {
+        if (blockIdx.x == 0 && lane == 0)
+            atomicAdd(&a.status[3], 1u);
+        return;
+    }
+    const uint32_t n_items = a.meta[kMetaItems];
     const int64_t nodes = DIM == 3 ? (int64_t)a.n * a.n * a.n : (int64_t)a.n * a.n;
 
     // The block's local coordinates of the nodes this lane flushes (node
@@ -289,7 +303,8 @@ hipError_t launch_p2g_tiled(int dim, int n, int frac_bits, const BinView &b, int
     a.cell_key = b.cell_key;
     a.items = b.items;
     a.meta = b.meta;
-    a.cursor = b.meta + 3;
+    a.stamp = b.stamp;
+    a.cursor = b.meta + kMetaCursor;
     a.n = n;
     a.ntx = n / kTile;
     a.nf = (float)n;

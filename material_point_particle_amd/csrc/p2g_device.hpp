@@ -272,6 +272,7 @@ struct TiledArgs {
     float nf, dx, last_base, S;
     int64_t *grid;
     uint32_t *status;
+    BinStamp stamp;                        // the binning these bins must come from
 };
 
 __global__ void reset_cursor_kernel(uint32_t *cursor) { *cursor = 0u; }
@@ -469,8 +470,15 @@ __device__ __forceinline__ void item_rows(const TiledArgs &a, RangesF r, uint32_
                         rec[q] = 0.0f;
                 }
             }
-            if (pad)                                     // completes the cell's group: zero mass
-                rec[2 * DIM + DIM * DIM] = 0.0f;
+            // a pad completes the cell's group and adds nothing: its record (one
+            // of the cell's, for the cell's position) is read with zero mass,
+            // velocity and affine matrix, so its products are exact zeros even
+            // where that record holds values outside the ranges (Inf, NaN)
+            if (pad) {
+#pragma unroll
+                for (int q = DIM; q < R; ++q)
+                    rec[q] = 0.0f;
+            }
             group_hoist<DIM>(rec, a.nf, a.dx, a.last_base, a.S, h[k]);
         }
         // every record of the group is in one cell of this tile (binning's

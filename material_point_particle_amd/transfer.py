@@ -115,7 +115,7 @@ class Transfer:
         return self.ws.view(torch.int32)[off // 4: off // 4 + count]
 
     def meta(self) -> np.ndarray:
-        return self.ws_u32("meta", 16).cpu().numpy().view(np.uint32)
+        return self.ws_u32("meta", 32).cpu().numpy().view(np.uint32)
 
 
 class ResidentSubsteps:
@@ -160,4 +160,4 @@ class ResidentSubsteps:
 
     def gather(self) -> None:
         """Write the records' x, v, C back to the particle arrays."""
-        L.mpm_gather_records(self.tr.desc, self.tr.ws, self.parts.desc())
+        L.mpm_gather_records(self.tr.desc, self.tr.ws, self.parts.desc(), self.tr.status)

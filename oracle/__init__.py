@@ -33,7 +33,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp"
         subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-shared",
-                        "-Wall", "-o", tmp, _SRC, "-lm"], check=True)
+                        "-fopenmp", "-Wall", "-o", tmp, _SRC, "-lm"], check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -53,6 +53,10 @@ def lib():
         L.oracle_p2g_quadratic.restype = None
         L.oracle_p2g_quadratic.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_int64, F32P, F32P, F32P, F32P,
                                            I64P, ct.c_double, ct.c_double, ct.c_double, I64P, U32P]
+        L.oracle_p2g_quadratic_threads.restype = ct.c_int
+        L.oracle_p2g_quadratic_threads.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_int64, F32P, F32P, F32P, F32P,
+                                                   I64P, ct.c_double, ct.c_double, ct.c_double, I64P, U32P,
+                                                   ct.c_int]
         L.oracle_p2g_log2_bound.restype = ct.c_double
         L.oracle_p2g_log2_bound.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_int64,
                                             ct.c_double, ct.c_double, ct.c_double]
@@ -124,6 +128,25 @@ def p2g_quadratic(dim: int, n: int, frac_bits: int, particles: dict, ranges, ord
     lib().oracle_p2g_quadratic(dim, n, frac_bits, np_, _p(x, F32P), _p(v, F32P), _p(C, F32P), _p(m, F32P), op,
                                float(ranges[0]), float(ranges[1]), float(ranges[2]), _p(grid, I64P),
                                _p(status, U32P))
+    return grid, status
+
+
+def p2g_quadratic_threads(dim: int, n: int, frac_bits: int, particles: dict, ranges, threads: int, order=None,
+                          grid=None):
+    """The same P2G on `threads` host threads (private grids, integer-summed);
+    bit-identical to p2g_quadratic.  For the CPU baseline's all-cores leg."""
+    x, v, C, m = _soa(particles)
+    np_ = m.shape[0]
+    shape = (1 + dim,) + (n,) * dim
+    if grid is None:
+        grid = np.zeros(shape, dtype=np.int64)
+    status = np.zeros(4, dtype=np.uint32)
+    o, op = _order_ptr(order)
+    rc = lib().oracle_p2g_quadratic_threads(dim, n, frac_bits, np_, _p(x, F32P), _p(v, F32P), _p(C, F32P),
+                                            _p(m, F32P), op, float(ranges[0]), float(ranges[1]), float(ranges[2]),
+                                            _p(grid, I64P), _p(status, U32P), int(threads))
+    if rc != 0:
+        raise MemoryError("oracle_p2g_quadratic_threads: private grids could not be allocated")
     return grid, status
 
 

@@ -8,9 +8,11 @@
  * benchmark's CPU-baseline leg use it.  It shares no code with the HIP
  * library: the two are written separately from the same definitions.
  *
- * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no -ffast-math, no
- * -march=native), so every float operation is one IEEE binary32 operation
- * rounded to nearest even, in the order written below.
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -fPIC -shared (no -ffast-math,
+ * no -march=native), so every float operation is one IEEE binary32 operation
+ * rounded to nearest even, in the order written below.  OpenMP is used only
+ * by oracle_p2g_quadratic_threads (the CPU baseline's all-cores leg); every
+ * other function is single-threaded.
  *
  * Sources (pages as titled):
  *  - "particle to grid transfer in checked integer arithmetic" (integerc.dev),
@@ -343,14 +345,17 @@ static int in_ranges(int dim, int64_t np_, int64_t p, const float *v, const floa
  * status[0]; particles outside the declared ranges are skipped and counted
  * in status[1] (domain is checked first).
  */
-void oracle_p2g_quadratic(int dim, int n, int frac_bits, int64_t np_,
-                          const float *x, const float *v, const float *C, const float *m,
-                          const int64_t *order, double max_mass, double max_speed, double max_affine,
-                          int64_t *grid, uint32_t *status)
+/* The particles at positions k0 .. k1-1 of the visiting order; touched (may
+ * be NULL) gets a 1 for every 4^dim-node tile that receives a contribution. */
+static void p2g_quadratic_range(int dim, int n, int frac_bits, int64_t np_, int64_t k0, int64_t k1,
+                                const float *x, const float *v, const float *C, const float *m,
+                                const int64_t *order, double max_mass, double max_speed, double max_affine,
+                                int64_t *grid, uint32_t *status, uint8_t *touched)
 {
     const int64_t nodes = dim == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    const int nt = n / 4;
     const float S = ldexpf(1.0f, frac_bits);
-    for (int64_t k = 0; k < np_; ++k) {
+    for (int64_t k = k0; k < k1; ++k) {
         int64_t p = order ? order[k] : k;
         int base[3] = { 0, 0, 0 };
         float w[3][3] = { { 1, 0, 0 }, { 1, 0, 0 }, { 1, 0, 0 } };
@@ -368,6 +373,12 @@ void oracle_p2g_quadratic(int dim, int n, int frac_bits, int64_t np_,
         }
         const float mS = m[p] * S;
         const int nc = dim == 3 ? 3 : 1;
+        if (touched) {
+            for (int tz = base[2] / 4; tz <= (dim == 3 ? (base[2] + 2) / 4 : 0); ++tz)
+                for (int ty = base[1] / 4; ty <= (base[1] + 2) / 4; ++ty)
+                    for (int tx = base[0] / 4; tx <= (base[0] + 2) / 4; ++tx)
+                        touched[((int64_t)tz * nt + ty) * nt + tx] = 1;
+        }
         for (int a = 0; a < 3; ++a)
             for (int b = 0; b < 3; ++b)
                 for (int c = 0; c < nc; ++c) {
@@ -387,6 +398,84 @@ void oracle_p2g_quadratic(int dim, int n, int frac_bits, int64_t np_,
                     }
                 }
     }
+}
+
+void oracle_p2g_quadratic(int dim, int n, int frac_bits, int64_t np_,
+                          const float *x, const float *v, const float *C, const float *m,
+                          const int64_t *order, double max_mass, double max_speed, double max_affine,
+                          int64_t *grid, uint32_t *status)
+{
+    p2g_quadratic_range(dim, n, frac_bits, np_, 0, np_, x, v, C, m, order, max_mass, max_speed, max_affine, grid,
+                        status, NULL);
+}
+
+/*
+ * The same transfer on several host threads, for the CPU baseline's
+ * all-cores measurement (not used by any test as a reference: the tests
+ * compare it with oracle_p2g_quadratic).  The visiting order is cut into
+ * nthreads contiguous ranges; each thread accumulates its range into a
+ * private zeroed int64 grid with the arithmetic above and flags the 4^dim-node
+ * tiles it wrote; then the private grids of every flagged tile are added into
+ * `grid`, tile by tile in parallel.  Integer additions commute, so the result
+ * is bit-identical to oracle_p2g_quadratic.  Returns 0, or -1 when the private
+ * grids cannot be allocated (nothing is added then).
+ */
+int oracle_p2g_quadratic_threads(int dim, int n, int frac_bits, int64_t np_,
+                                 const float *x, const float *v, const float *C, const float *m,
+                                 const int64_t *order, double max_mass, double max_speed, double max_affine,
+                                 int64_t *grid, uint32_t *status, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    const int64_t nodes = dim == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    const int nt = n / 4;
+    const int64_t tiles = dim == 3 ? (int64_t)nt * nt * nt : (int64_t)nt * nt;
+    const int64_t words = (int64_t)(1 + dim) * nodes;
+    int64_t **priv = calloc((size_t)nthreads, sizeof(int64_t *));
+    uint8_t **flag = calloc((size_t)nthreads, sizeof(uint8_t *));
+    uint32_t *st = calloc((size_t)nthreads * 4, sizeof(uint32_t));
+    int ok = priv && flag && st;
+    for (int t = 0; ok && t < nthreads; ++t) {
+        priv[t] = calloc((size_t)words, sizeof(int64_t));
+        flag[t] = calloc((size_t)tiles, 1);
+        ok = priv[t] && flag[t];
+    }
+    if (ok) {
+#pragma omp parallel for num_threads(nthreads) schedule(static, 1)
+        for (int t = 0; t < nthreads; ++t) {
+            const int64_t k0 = np_ * t / nthreads, k1 = np_ * (t + 1) / nthreads;
+            p2g_quadratic_range(dim, n, frac_bits, np_, k0, k1, x, v, C, m, order, max_mass, max_speed, max_affine,
+                                priv[t], st + 4 * t, flag[t]);
+        }
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 64)
+        for (int64_t tile = 0; tile < tiles; ++tile) {
+            const int tx = (int)(tile % nt), ty = (int)((tile / nt) % nt), tz = dim == 3 ? (int)(tile / ((int64_t)nt * nt)) : 0;
+            for (int t = 0; t < nthreads; ++t) {
+                if (!flag[t][tile])
+                    continue;
+                for (int c = 0; c <= dim; ++c)
+                    for (int z = 0; z < (dim == 3 ? 4 : 1); ++z)
+                        for (int y = 0; y < 4; ++y)
+                            for (int xx = 0; xx < 4; ++xx) {
+                                const int64_t node = dim == 3
+                                    ? ((int64_t)(tz * 4 + z) * n + (ty * 4 + y)) * n + (tx * 4 + xx)
+                                    : (int64_t)(ty * 4 + y) * n + (tx * 4 + xx);
+                                grid[(int64_t)c * nodes + node] += priv[t][(int64_t)c * nodes + node];
+                            }
+            }
+        }
+        for (int t = 0; t < nthreads; ++t)
+            for (int i = 0; i < 4; ++i)
+                status[i] += st[4 * t + i];
+    }
+    for (int t = 0; priv && flag && t < nthreads; ++t) {
+        free(priv[t]);
+        free(flag[t]);
+    }
+    free(priv);
+    free(flag);
+    free(st);
+    return ok ? 0 : -1;
 }
 
 /*

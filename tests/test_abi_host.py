@@ -77,7 +77,7 @@ def test_workspace_layout_is_disjoint_and_aligned():
         assert lay.n_fields == {2: 12, 3: 16}[dim]     # x, v, C, m padded to a multiple of 4 floats
         spans = sorted([
             (lay.tile_count, 4 * lay.n_tiles), (lay.tile_start, 4 * (lay.n_tiles + 1)), (lay.tile_active, lay.n_tiles),
-            (lay.items, 16 * lay.max_items), (lay.meta, 64), (lay.rank, 4 * max(N, 1)), (lay.slot, 4 * max(N, 1)),
+            (lay.meta, 128), (lay.items, 16 * lay.max_items), (lay.rank, 4 * max(N, 1)), (lay.slot, 4 * max(N, 1)),
             (lay.cell_key, max(N, 1)), (lay.sorted, 4 * lay.n_fields * max(N, 1)),
             (lay.scan_tmp, 4 * (2 + lay.rows_per_item) * ((lay.n_tiles + 4095) // 4096))])
         for (a, la), (b, _) in zip(spans, spans[1:]):
@@ -112,8 +112,9 @@ def test_tile_arrays_sit_at_offsets_independent_of_the_particle_count():
         base = M.mpm_workspace_layout(d, 0)
         for N in (1, 3500, 1 << 20):
             lay = M.mpm_workspace_layout(d, N)
-            assert (lay.tile_count, lay.tile_start, lay.tile_active) == (base.tile_count, base.tile_start,
-                                                                         base.tile_active)
+            assert (lay.tile_count, lay.tile_start, lay.tile_active, lay.meta) == (
+                base.tile_count, base.tile_start, base.tile_active, base.meta)
+            assert lay.meta < lay.items
 
 
 def test_entry_points_reject_bad_arguments_before_any_launch():
@@ -123,17 +124,24 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     p = L.mpm_particles(10, None, None, None, None)
     status = ct.c_void_p(256)
     grid = ct.c_void_p(4096)
-    assert lib.mpm_p2g(ct.byref(d), ct.byref(p), ct.byref(r), None, grid, status, None) == L.MPM_ERR_INVALID
-    assert lib.mpm_p2g(None, ct.byref(p), ct.byref(r), None, grid, status, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_p2g(ct.byref(d), ct.byref(p), ct.byref(r), None, 0, grid, status, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_p2g(None, ct.byref(p), ct.byref(r), None, 0, grid, status, None) == L.MPM_ERR_INVALID
     misaligned = ct.c_void_p(4099)
     p2 = L.mpm_particles(10, 4096, 4096, 4096, 4096)
-    assert lib.mpm_p2g(ct.byref(d), ct.byref(p2), ct.byref(r), None, misaligned, status, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_p2g(ct.byref(d), ct.byref(p2), ct.byref(r), None, 0, misaligned, status, None) == L.MPM_ERR_INVALID
     assert lib.mpm_bin_particles(ct.byref(d), ct.byref(p2), ct.byref(r), ct.c_void_p(4096), 16, status,
                                  None) == L.MPM_ERR_WORKSPACE
     assert lib.mpm_bin_particles(ct.byref(d), ct.byref(p2), ct.byref(r), ct.c_void_p(4100), 1 << 30, status,
                                  None) == L.MPM_ERR_INVALID
     big = L.mpm_ranges(1e30, 1e30, 1e30)
-    assert lib.mpm_p2g(ct.byref(d), ct.byref(p2), ct.byref(big), None, grid, status, None) == L.MPM_ERR_OVERFLOW
+    assert lib.mpm_p2g(ct.byref(d), ct.byref(p2), ct.byref(big), None, 0, grid, status, None) == L.MPM_ERR_OVERFLOW
+    # a workspace too small for this grid and particle count is refused before any launch
+    need_bins = M.mpm_workspace_bytes(d, 10)
+    wsp = ct.c_void_p(1 << 20)
+    assert lib.mpm_p2g(ct.byref(d), ct.byref(p2), ct.byref(r), wsp, need_bins - 1, grid, status,
+                       None) == L.MPM_ERR_WORKSPACE
+    assert lib.mpm_p2g(ct.byref(d), ct.byref(p), ct.byref(r), ct.c_void_p((1 << 20) + 8), need_bins, grid, status,
+                       None) == L.MPM_ERR_INVALID
     assert lib.mpm_p2g_cic_split(256, None, None, None, None, 8, 1000, 1000, grid, status, None) == L.MPM_ERR_INVALID
     assert lib.mpm_p2g_cic_split(1 << 40, 4096, 4096, 4096, None, 8, 1 << 20, 1 << 20, grid, status,
                                  None) == L.MPM_ERR_INVALID
@@ -160,9 +168,10 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     T = ct.c_void_p(1 << 16)
     G3, T3 = ct.c_void_p(1 << 20), ct.c_void_p(1 << 17)
 
-    def g2p2g(ws, grid_in, grid_out, tiles_out, grav=g3, sticky=2, rng=r, clear=(None, None)):
-        return lib.mpm_g2p2g(ct.byref(d), ct.byref(rng), ct.c_void_p(ws), 10, grid_in, grid_out, tiles_out,
+    def g2p2g(ws, grid_in, grid_out, tiles_out, grav=g3, sticky=2, rng=r, clear=(None, None), ws_bytes=1 << 30):
+        return lib.mpm_g2p2g(ct.byref(d), ct.byref(rng), ct.c_void_p(ws), ws_bytes, 10, grid_in, grid_out, tiles_out,
                              clear[0], clear[1], 1e-4, grav, sticky, status, None)
+    assert g2p2g(4096, None, grid, T, ws_bytes=need_bins - 1) == L.MPM_ERR_WORKSPACE
     assert g2p2g(4096, grid, grid, T) == L.MPM_ERR_INVALID                             # grid_in == grid_out
     assert g2p2g(4100, None, grid, T) == L.MPM_ERR_INVALID                             # misaligned workspace
     assert g2p2g(4096, ct.c_void_p(8192), grid, T, sticky=100) == L.MPM_ERR_INVALID    # sticky beyond n/2
@@ -176,19 +185,29 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert g2p2g(4096, ct.c_void_p(8192), grid, T, clear=(ct.c_void_p((1 << 20) + 4), T3)) == L.MPM_ERR_INVALID
     assert lib.mpm_grid_clear_tiles(ct.byref(d), ct.c_void_p(4100), T, None) == L.MPM_ERR_INVALID
     assert lib.mpm_grid_clear_tiles(None, grid, T, None) == L.MPM_ERR_INVALID
-    assert lib.mpm_gather_records(ct.byref(d), ct.c_void_p(4096), ct.byref(L.mpm_particles(10, 4096, 4096, None,
-                                                                                           4096)),
+    assert lib.mpm_gather_records(ct.byref(d), ct.c_void_p(4096), 1 << 30,
+                                  ct.byref(L.mpm_particles(10, 4096, 4096, None, 4096)), status,
                                   None) == L.MPM_ERR_INVALID                           # no C
+    assert lib.mpm_gather_records(ct.byref(d), ct.c_void_p(4096), need_bins - 1, ct.byref(p2), status,
+                                  None) == L.MPM_ERR_WORKSPACE
     assert lib.mpm_bin_resident(ct.byref(d), ct.byref(p2), ct.c_void_p(4096), 16, status,
                                 None) == L.MPM_ERR_WORKSPACE
     g = (ct.c_float * 3)(0, -9.8, 0)
-    assert lib.mpm_grid_update(ct.byref(d), None, grid, ct.c_void_p(4096), 1e-4, g, 100, None) == L.MPM_ERR_INVALID
-    assert lib.mpm_grid_update(ct.byref(d), None, grid, ct.c_void_p(4096), 1e-4, None, 2, None) == L.MPM_ERR_INVALID
-    assert lib.mpm_grid_update(ct.byref(d), ct.c_void_p(4100), grid, ct.c_void_p(4096), 1e-4, g, 2,
+    assert lib.mpm_grid_update(ct.byref(d), None, 0, grid, ct.c_void_p(4096), 1e-4, g, 100,
                                None) == L.MPM_ERR_INVALID
-    assert lib.mpm_grid_clear(ct.byref(d), None, ct.c_void_p(4100), None) == L.MPM_ERR_INVALID
-    assert lib.mpm_grid_clear(ct.byref(d), ct.c_void_p(4100), grid, None) == L.MPM_ERR_INVALID
-    assert lib.mpm_grid_clear(None, None, grid, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_update(ct.byref(d), None, 0, grid, ct.c_void_p(4096), 1e-4, None, 2,
+                               None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_update(ct.byref(d), ct.c_void_p(4100), 1 << 30, grid, ct.c_void_p(4096), 1e-4, g, 2,
+                               None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_clear(ct.byref(d), None, 0, ct.c_void_p(4100), None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_clear(ct.byref(d), ct.c_void_p(4100), 1 << 30, grid, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_clear(None, None, 0, grid, None) == L.MPM_ERR_INVALID
+    # the restricted update and clear need the workspace's tile arrays and meta words
+    lay0 = M.mpm_workspace_layout(d, 0)
+    prefix = lay0.meta + 128
+    assert lib.mpm_grid_update(ct.byref(d), wsp, prefix - 1, grid, ct.c_void_p(4096), 1e-4, g, 2,
+                               None) == L.MPM_ERR_WORKSPACE
+    assert lib.mpm_grid_clear(ct.byref(d), wsp, prefix - 1, grid, None) == L.MPM_ERR_WORKSPACE
     p3 = L.mpm_particles(10, 4096, 4096, None, 4096)
     assert lib.mpm_g2p(ct.byref(d), ct.c_void_p(4096), ct.byref(p3), 1e-4, status, None) == L.MPM_ERR_INVALID
     p4 = L.mpm_particles(10, 4096, 4096, 4096, 4096)

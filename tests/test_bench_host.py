@@ -1,5 +1,6 @@
 """Host-side checks of bench.py that need no GPU: the one-GPU guard, the
-ALU operation count per particle, and the traffic lookup from the committed
+ALU operation count per particle by instruction class, the algorithmic byte
+count, the stage statistics, and the profile lookup from the committed
 counter summary."""
 import os
 import subprocess
@@ -20,14 +21,29 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
 
 def test_alu_operations_per_particle():
     import bench
-    # per node: w*m*S, 3 sums for u, 3 momentum products, 4 roundings, 4 widenings, 3 float64 adds
-    assert bench.alu_ops_per_node(3) * 27 == 486
-    # 2D: 1 + 2 + 2 + 3 + 3 + 2.25 per node over 9 nodes
-    assert bench.alu_ops_per_node(2) * 9 == pytest.approx(119.25)
-    assert bench.VALU_PEAK_TOPS == pytest.approx(39.3216)
+    # per node, fast class: w*m*S, 3 sums for u, 3 momentum products; slow class: 4 roundings, 4 widenings,
+    # 3 float64 adds (three per four contributions and channel)
+    fast, slow = bench.alu_ops_per_node(3)
+    assert (fast * 27, slow * 27) == (189, 297)
+    fast2, slow2 = bench.alu_ops_per_node(2)
+    assert (fast2 * 9, slow2 * 9) == (45, pytest.approx(74.25))
+    # the slow class issues one 64-lane instruction per SIMD every 4 cycles
+    assert bench.SLOW_PEAK_TOPS == pytest.approx(39.3216)
 
 
-def test_traffic_lookup_is_none_when_the_summary_is_missing(tmp_path, monkeypatch):
+def test_algorithmic_bytes_and_stage_stats():
+    import numpy as np
+
+    import bench
+    # 3D: 64 B of state (x, v, C, m) + a 4-byte index entry per particle, 32 B per touched node
+    assert bench.p2g_algorithmic_bytes(3, 10, 7) == 10 * 68 + 7 * 32
+    assert bench.p2g_algorithmic_bytes(2, 10, 7) == 10 * 40 + 7 * 24     # 2D: 36 B of state + 4
+    st = bench.stage_stats(np.arange(1, 11, dtype=float))
+    assert st["median"] == 5.5 and st["mean"] == 5.5 and st["p10"] == pytest.approx(1.9)
+    assert st["p90"] == pytest.approx(9.1)
+
+
+def test_profile_lookup_is_none_when_the_summary_is_missing(tmp_path, monkeypatch):
     import bench
     # a copy of bench.py beside no profiles/ directory finds no summary
     d = tmp_path / "repo"
@@ -36,4 +52,4 @@ def test_traffic_lookup_is_none_when_the_summary_is_missing(tmp_path, monkeypatc
         src = os.path.join(ROOT, "material_point_particle_amd", "csrc", f)
         (d / "material_point_particle_amd" / "csrc" / f).write_bytes(open(src, "rb").read())
     monkeypatch.setattr(bench.os.path, "abspath", lambda p: str(d / "bench.py"))
-    assert bench.measured_traffic() is None
+    assert bench.profile_record() is None

@@ -218,3 +218,44 @@ def test_deposit_only_matches_p2g_and_flagged_clear(mpm, oracle_lib):
     L.mpm_grid_clear_tiles(tr.desc, rs.grid, flags)
     torch.cuda.synchronize()
     assert int(rs.grid.abs().sum()) == 0 and int(flags.sum()) == 0
+
+
+def test_deposit_pads_of_out_of_range_records_add_nothing(mpm, oracle_lib):
+    """mpm_bin_resident keeps records unchecked, so a cell's pad entries (which
+    complete its last group of four and name one of the cell's records) may
+    name a record with an infinite or NaN velocity or affine entry.  Pads must
+    still add exact zeros: cells of 5 and 9 records with such entries, one cell
+    whose records are all out of range, around in-range particles; the
+    deposit-only call equals the oracle's grid and counts every out-of-range
+    record once."""
+    from material_point_particle_amd.transfer import DeviceParticles, ResidentSubsteps, Transfer
+    n, dim = 32, 3
+    cells = [((10, 10, 10), 5), ((11, 10, 10), 9), ((12, 14, 9), 5), ((20, 20, 20), 13), ((5, 6, 7), 1)]
+    xs = []
+    for (cx, cy, cz), cnt in cells:
+        u = G.uniform01(0xBAD + cx, 1, 3 * cnt).reshape(3, cnt)
+        c = np.array([cx, cy, cz], dtype=np.float64)[:, None]
+        xs.append((c + 0.5 + 0.999 * u) / n)                 # base cell = (cx, cy, cz)
+    x = np.concatenate(xs, axis=1).astype(np.float32)
+    count = x.shape[1]
+    f = G.particle_fields(0xBAD, count, dim, (0.5, 2.0), 1.0, 0.5)
+    host = {"x": np.ascontiguousarray(x), **f}
+    # cell (10,10,10): every record out of range (its pads must name one of them)
+    host["v"][0, 0:5] = np.inf
+    # cell (11,10,10): one NaN affine entry among 9 records
+    host["C"][4, 7] = np.nan
+    # cell (12,14,9): one -Inf velocity among 5
+    host["v"][2, 16] = -np.inf
+    w = replace(scaled(WORKLOADS["dam_3d_256"], count, n=n), frac_bits=28, max_mass=2.0, max_speed=8.0,
+                max_affine=4.0)
+    rng = (w.max_mass, w.max_speed, w.max_affine)
+    ref, rst = oracle_lib.p2g_quadratic(dim, n, w.frac_bits, host, rng)
+    assert int(rst[1]) == 7
+    parts = DeviceParticles(host)
+    tr = Transfer(dim, n, w.frac_bits, rng, parts.n)
+    rs = ResidentSubsteps(tr, parts, 1e-4, (0.0, -9.8, 0.0), 2)
+    say("deposit pads of out-of-range records")
+    rs.start()
+    torch.cuda.synchronize()
+    assert_same(rs.grid.cpu().numpy(), ref, "deposit with out-of-range pads")
+    assert tr.status.cpu().numpy().view(np.uint32).tolist() == rst.tolist() == [0, 7, 0, 0]

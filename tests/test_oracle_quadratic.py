@@ -313,3 +313,23 @@ def test_quantiser_rounds_to_nearest_even(oracle_lib):
                 fracs.add(val - math.floor(val))
                 assert grid[(ch,) + tuple(reversed(node))] == round(val), (node, ch, val)
         assert Fraction(1, 2) in fracs
+
+
+@pytest.mark.parametrize("threads", [1, 3, 8])
+def test_threaded_oracle_equals_single_thread(oracle_lib, threads):
+    """The CPU baseline's all-cores leg (contiguous particle ranges, private
+    grids, integer sums over the touched node tiles) gives the single-thread
+    grid bit for bit, with skipped particles counted alike."""
+    w = scaled(WORKLOADS["blobs_3d_256"], 1 << 15)
+    host = build(w)
+    host = {k: np.array(a, copy=True) for k, a in host.items()}
+    host["x"][0, :7] = 1.5                     # outside the grid
+    host["v"][1, 7:12] = 100.0                 # outside the declared ranges
+    rng = (w.max_mass, w.max_speed, w.max_affine)
+    ref, rst = oracle_lib.p2g_quadratic(w.dim, w.n, w.frac_bits, host, rng)
+    got, st = oracle_lib.p2g_quadratic_threads(w.dim, w.n, w.frac_bits, host, rng, threads)
+    assert np.array_equal(got, ref)
+    assert st.tolist() == rst.tolist() == [7, 5, 0, 0]
+    order = np.arange(w.n_particles)[::-1].copy()
+    got2, _ = oracle_lib.p2g_quadratic_threads(w.dim, w.n, w.frac_bits, host, rng, threads, order=order)
+    assert np.array_equal(got2, ref)
