@@ -478,6 +478,7 @@ def main():
     parts, tr = copies[0]
     meta = tr.meta()
     binned = int(meta[2])
+    runs, keys = int(meta[6]), int(meta[7])
     touched = int((tr.grid != 0).any(dim=0).sum().item())
     status = tr.status.cpu().numpy().view(np.uint32).tolist()
     rec_bytes = 4 * (2 * w.dim + w.dim * w.dim + 1)          # x, v, C, m
@@ -494,6 +495,8 @@ def main():
     perm = G.permutation(w.seed ^ 0x5F5F, 0x5EED, w.n_particles)
     shuffled_host = {k: np.ascontiguousarray(v[..., perm]) for k, v in host.items()}
     sh_total, sh_stage, sh_copies = run_steps(shuffled_host, args.steps, args.warmup, "timed (shuffled order)")
+    sh_meta = sh_copies[0][1].meta()
+    sh_runs, sh_keys = int(sh_meta[6]), int(sh_meta[7])
     del sh_copies, shuffled_host
     torch.cuda.empty_cache()
 
@@ -552,11 +555,14 @@ def main():
             "p2g_frac_hbm": round(p2g_gbs / HBM_PEAK_GBS, 4), "bin_gbs": round(bin_gbs, 1),
             "bin_frac_hbm": round(bin_gbs / HBM_PEAK_GBS, 4), "bin_frac_copy": round(bin_gbs / copy["gbs"], 4),
             "bin_bytes": int(bin_bytes), "p2g_bytes": int(p2g_bytes), "status": status,
+            "binning_runs": runs, "mean_run": round(binned / max(runs, 1), 1), "cell_keys_written": bool(keys),
         },
         "shuffled": {
             "order": "the same particles in a seeded random order",
             "ms_per_step": round(sh_ms, 4), "particles_per_s": round(w.n_particles / (sh_ms * 1e-3), 1),
             "ratio_to_generator_order": round(sh_ms / ms_step, 4),
+            "binning_runs": sh_runs, "mean_run": round(binned / max(sh_runs, 1), 1),
+            "cell_keys_written": bool(sh_keys),
             "stages_ms": {"reset": stage_stats(sh_stage[:, 0]), "binning": stage_stats(sh_stage[:, 1]),
                           "p2g": stage_stats(sh_stage[:, 2])},
         },

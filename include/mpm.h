@@ -99,6 +99,7 @@ typedef struct {
                                         given the bins: 1 for the node tiles that P2G from these
                                         bins can reach */
     size_t meta;            /* uint32 [32]: [0] items, [2] binned particles, [3] work cursor,
+                                        [6] runs (chunk, tile) of the count, [7] cell keys written,
                                         [16..24] the binning's stamp
                                         (grid, particle count, declared ranges, resident or
                                         checked), which every reader of the bins compares with
@@ -110,7 +111,10 @@ typedef struct {
                                         smallest remaining                                 */
     size_t rank;            /* uint32 [n] rank of each particle inside its tile (internal)      */
     size_t slot;            /* uint32 [n] record index of each particle (0xFFFFFFFF: not binned) */
-    size_t cell_key;        /* uint8  [n] local cell number of each record, in record order      */
+    size_t cell_key;        /* uint8  [n + 4] local cell number of each record, in record order, written
+                                        when meta[7] is 1 (the binning's runs averaged at least 32
+                                        records); otherwise mpm_p2g reads a record's cell from its
+                                        position */
     size_t sorted;          /* float  [n][n_fields] binned records x, v, C, m (+ padding floats),
                                         tile by tile                                       */
     size_t scan_tmp;        /* uint32 [ceil(n_tiles/4096)][2 + rows_per_item] per-block sums of the
@@ -159,10 +163,9 @@ int mpm_workspace_layout(const mpm_grid_desc *grid, int64_t n_particles, mpm_ws_
  * Codebases", section 2.1: sort + tile).  The caller's arrays are not
  * reordered (section 5 rule 2): the workspace receives the tile histogram
  * and prefix sum, each particle's record index, a binned copy of x, v, C, m
- * (64-byte records, 48 in 2D) tile by tile with each record's local cell
- * number (inside a 3D tile cells are numbered x fastest, then z, then y), and
- * the P2G work items: slices of each tile's records, which mpm_p2g sorts by
- * cell on chip.
+ * (64-byte records, 48 in 2D) tile by tile, and the P2G work items: slices
+ * of each tile's records, which mpm_p2g sorts by cell on chip (the cell of a
+ * record follows from its position).
  * Particles whose stencil leaves the grid are not binned and
  * are counted in status[0]; particles whose attributes leave the declared
  * ranges are binned as zero-mass records (they contribute nothing, exactly

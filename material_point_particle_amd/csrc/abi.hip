@@ -128,7 +128,7 @@ void make_layout(const mpm_grid_desc *g, int64_t np, mpm_ws_layout *o)
     o->items = take(u4 * 4 * (size_t)max_items);
     o->rank = take(u4 * (size_t)n1);
     o->slot = take(u4 * (size_t)n1);
-    o->cell_key = take((size_t)n1);
+    o->cell_key = take((size_t)n1 + 4);
     o->sorted = take(sizeof(float) * (size_t)(n_fields * n1));
     o->scan_tmp = take(u4 * (size_t)(kPlanStride * plan_blocks));
     o->n_cells = n_cells;

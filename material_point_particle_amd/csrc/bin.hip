@@ -13,16 +13,22 @@
 //               the chunk's particles per tile, then one global atomic per
 //               (chunk, tile) reserves the chunk's run inside the tile, so a
 //               particle's rank in its tile is its run's base plus its rank
-//               in the chunk.
+//               in the chunk.  The table has room for every tile a chunk of
+//               particles in any order touches on the workloads here, so
+//               input order changes only the number of runs.
 //   2-4. plan   each tile's first record (prefix sum of the counts) and its
 //               work items: the tile's records cut into slices of at most
 //               slice_records(), listed by size (full slices, then partial
 //               slices counting-sorted by the rows their groups need) and
 //               handed out alternately from the two ends of that list.
-//   5. scatter  the same chunks as pass 1: each particle's 64-byte record
-//               (x, v, C, m in 3D) goes to its tile's record range at its
-//               rank, with the cell's local number beside it.  A chunk's
-//               particles of one tile land in one contiguous run.
+//   5. scatter  each particle's 64-byte record (x, v, C, m in 3D) goes to
+//               its tile's record range at its rank; a chunk's particles of
+//               one tile land in one contiguous run.  When the count's runs
+//               are long (input listed region by region) the record's cell
+//               key goes beside it; when they are short (input in random
+//               order) those one-byte writes would land scattered and cost
+//               more than the records, so none are written and P2G reads a
+//               record's cell from its position (meta[kMetaKeys] says which).
 // Arrival ranks depend on scheduling, so record order inside a tile differs
 // between runs; P2G's grid does not depend on it.
 #include "common.hpp"
@@ -73,14 +79,17 @@ __global__ void bin_reset_kernel(uint32_t *__restrict__ tile_count, int64_t n_ti
     }
 }
 
-// Passes 1 and 5 visit the same chunks of kBinThreads * per consecutive
-// particles (per <= kMaxPer, chosen per launch so that every CU gets chunks),
-// one block per chunk.
+// Pass 1 visits chunks of kBinThreads * per consecutive particles (per <=
+// kMaxPer, chosen per launch so that every CU gets a chunk), one block per
+// chunk and one block per CU: its hash table takes 128 KB of LDS.  Pass 5
+// needs no chunks (it reads each particle's final rank) and visits blocks of
+// consecutive particles sized for occupancy.
 constexpr int kBinThreads = 1024;
-constexpr int kMaxPer = 32;                          // a chunk holds at most 32,768 particles
-constexpr int kHashBits = 11;
+constexpr int kMaxPer = 64;                          // a chunk holds at most 65,536 particles
+constexpr int kHashBits = 14;
 constexpr int kHashSlots = 1 << kHashBits;           // tiles per chunk counted in LDS
 constexpr int kMaxProbes = 64;
+constexpr int kScatterPer = 32;                      // particles per thread of a scatter block, at most
 constexpr uint32_t kLocalRank = 0x80000000u;         // rank_out holds (slot << 16) | rank in the chunk
 static_assert(kBinThreads * kMaxPer <= 65536, "a rank inside the chunk must fit 16 bits");
 
@@ -137,7 +146,7 @@ __global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, f
         hval[e] = 0u;
     }
     __syncthreads();
-    uint32_t binned = 0;
+    uint32_t binned = 0, runs = 0;
     const int64_t chunk = (int64_t)kBinThreads * per;
     for (int64_t c = blockIdx.x; c < chunks; c += gridDim.x) {
         const int64_t p0 = c * chunk + threadIdx.x;
@@ -178,14 +187,17 @@ __global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, f
                     }
                     v[k0 + j] = found ? kLocalRank | (h << 16) | atomicAdd(&hval[h], 1u) : atomicAdd(&tile_count[t], 1u);
                     ++binned;
+                    runs += found ? 0u : 1u;                 // a particle placed on its own is a run of one
                 }
             }
         }
         __syncthreads();
         for (int e = threadIdx.x; e < kHashSlots; e += kBinThreads) {
             const uint32_t key = hkey[e];
-            if (key != kEmpty)
+            if (key != kEmpty) {
                 hval[e] = atomicAdd(&tile_count[key], hval[e]);
+                ++runs;
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -204,10 +216,13 @@ __global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, f
     }
     // one atomic per block for the binned-particle total (a per-wave atomic on
     // one address from every wave of the grid would serialise)
-    __shared__ uint32_t total;
+    __shared__ uint32_t total, total_runs;
     (void)block_exclusive_scan<kBinThreads>(binned, &total);
-    if (threadIdx.x == 0 && total != 0u)
-        atomicAdd(&meta[2], total);
+    (void)block_exclusive_scan<kBinThreads>(runs, &total_runs);
+    if (threadIdx.x == 0 && total != 0u) {
+        atomicAdd(&meta[kMetaBinned], total);
+        atomicAdd(&meta[kMetaRuns], total_runs);
+    }
 }
 
 // Passes 2-4: the work-item plan.  Each tile's records are cut into slices
@@ -304,8 +319,9 @@ __global__ void __launch_bounds__(1024) plan_partials_kernel(uint32_t *__restric
             cbase[lane] = ftot[1] + inc - v;
         if (lane == kWave - 1) {
             *tile_start_end = ftot[0];
-            meta[0] = ftot[1] + inc;
-            meta[3] = 0u;
+            meta[kMetaItems] = ftot[1] + inc;
+            meta[kMetaCursor] = 0u;
+            meta[kMetaKeys] = (uint64_t)meta[kMetaRuns] * kKeyRunLength <= (uint64_t)meta[kMetaBinned] ? 1u : 0u;
         }
     }
     __syncthreads();
@@ -403,7 +419,7 @@ __device__ __forceinline__ uint32_t place_record(const Fields &f, RangesF r, flo
                                                  const uint32_t *__restrict__ rank_in,
                                                  const uint32_t *__restrict__ tile_start,
                                                  uint32_t *__restrict__ slot_out, uint8_t *__restrict__ cell_key,
-                                                 uint32_t *__restrict__ status)
+                                                 bool write_key, uint32_t *__restrict__ status)
 {
     constexpr int R = rec_floats<DIM>();
     uint32_t t, l;
@@ -428,7 +444,8 @@ __device__ __forceinline__ uint32_t place_record(const Fields &f, RangesF r, flo
     }
     const uint32_t pos = tile_start[t] + __builtin_nontemporal_load(&rank_in[p]);
     __builtin_nontemporal_store(pos, &slot_out[p]);
-    cell_key[pos] = (uint8_t)l;
+    if (write_key)
+        cell_key[pos] = (uint8_t)l;
     return pos;
 }
 
@@ -487,6 +504,7 @@ __global__ void __launch_bounds__(kBinThreads) bin_scatter_kernel(Fields f, Rang
                                                                    const uint32_t *__restrict__ tile_start,
                                                                    uint32_t *__restrict__ slot_out,
                                                                    uint8_t *__restrict__ cell_key,
+                                                                   const uint32_t *__restrict__ meta,
                                                                    float *__restrict__ sorted,
                                                                    uint32_t *__restrict__ status)
 {
@@ -497,6 +515,7 @@ __global__ void __launch_bounds__(kBinThreads) bin_scatter_kernel(Fields f, Rang
     const int w = threadIdx.x / kWave;
     float4 *my_stage = DIM == 3 ? stage + w * kWave * 4 : stage;
     uint32_t *my_spos = DIM == 3 ? spos + w * kWave : spos;
+    const bool write_keys = !KEEP && meta[kMetaKeys] != 0u;
     const int64_t chunk = (int64_t)kBinThreads * per;
     for (int64_t c = blockIdx.x; c < chunks; c += gridDim.x) {
         for (int k = 0; k < per; k += 2) {              // uniform trip count: every lane reaches the exchanges
@@ -510,11 +529,11 @@ __global__ void __launch_bounds__(kBinThreads) bin_scatter_kernel(Fields f, Rang
                 load_record<DIM>(f, pb, rb);
             uint32_t da = kEmpty, db = kEmpty;
             if (la)
-                da = place_record<DIM, KEEP>(f, r, nf, dx, last_base, ntx, pa, ra, rank_in, tile_start, slot_out, cell_key,
-                                       status);
+                da = place_record<DIM, KEEP>(f, r, nf, dx, last_base, ntx, pa, ra, rank_in, tile_start, slot_out,
+                                             cell_key, write_keys, status);
             if (lb)
-                db = place_record<DIM, KEEP>(f, r, nf, dx, last_base, ntx, pb, rb, rank_in, tile_start, slot_out, cell_key,
-                                       status);
+                db = place_record<DIM, KEEP>(f, r, nf, dx, last_base, ntx, pb, rb, rank_in, tile_start, slot_out,
+                                             cell_key, write_keys, status);
             write_records<DIM>(ra, da, my_stage, my_spos, sorted);
             write_records<DIM>(rb, db, my_stage, my_spos, sorted);
         }
@@ -537,12 +556,12 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
     const int ntx = n / kTile;
     hipLaunchKernelGGL(bin_reset_kernel, dim3(blocks_for(b.n_tiles + kMetaWords, 256)), dim3(256), 0, s, b.tile_count,
                        b.n_tiles, b.meta, b.stamp);
-    // particles per thread of a chunk: enough chunks for two blocks per CU, at most kMaxPer
-    const int64_t span = (int64_t)kBinThreads * device_cu_count() * 2;
+    // particles per thread of a chunk: a chunk for every CU, at most kMaxPer
+    const int64_t span = (int64_t)kBinThreads * device_cu_count();
     int64_t per = (p.n + span - 1) / span;
     per = per < 4 ? 4 : (per > kMaxPer ? kMaxPer : per);
     const int64_t chunks = (p.n + kBinThreads * per - 1) / (kBinThreads * per);
-    const unsigned cblocks = (unsigned)(chunks < (int64_t)device_cu_count() * 2 ? chunks : device_cu_count() * 2);
+    const unsigned cblocks = (unsigned)(chunks < (int64_t)device_cu_count() ? chunks : device_cu_count());
     if (chunks > 0) {
         if (dim == 3)
             hipLaunchKernelGGL(bin_tile_count_kernel<3>, dim3(cblocks), dim3(kBinThreads), 0, s, p, nf, dx, last, ntx,
@@ -568,10 +587,15 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
         hipLaunchKernelGGL(plan_final_kernel<2>, dim3((unsigned)pblocks), dim3(kPlanBlock), 0, s, b.tile_count,
                            b.n_tiles, b.scan_tmp, b.meta, b.tile_start, items);
     }
-    const unsigned sblocks = (unsigned)(chunks < (int64_t)device_cu_count() * 8 ? chunks : device_cu_count() * 8);
+    // the scatter's own blocks: two or more per CU
+    const int64_t sspan = (int64_t)kBinThreads * device_cu_count() * 2;
+    int64_t sper = (p.n + sspan - 1) / sspan;
+    sper = sper < 4 ? 4 : (sper > kScatterPer ? kScatterPer : sper);
+    const int64_t schunks = (p.n + kBinThreads * sper - 1) / (kBinThreads * sper);
+    const unsigned sblocks = (unsigned)(schunks < (int64_t)device_cu_count() * 8 ? schunks : device_cu_count() * 8);
     auto scatter = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(sblocks), dim3(kBinThreads), 0, s, p, r, nf, dx, last, ntx, chunks, (int)per,
-                           b.rank, b.tile_start, b.slot, b.cell_key, b.sorted, status);
+        hipLaunchKernelGGL(kern, dim3(sblocks), dim3(kBinThreads), 0, s, p, r, nf, dx, last, ntx, schunks, (int)sper,
+                           b.rank, b.tile_start, b.slot, b.cell_key, b.meta, b.sorted, status);
     };
     if (chunks > 0) {
         if (dim == 3)

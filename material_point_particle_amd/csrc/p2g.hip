@@ -63,18 +63,37 @@ p2g_tiled_kernel(TiledArgs a)
 
     // Lane 0 fetches the next item index as soon as an item starts; the next
     // item's record is loaded during the current item's rows and its cell keys
-    // during the current item's flush, so no round trip stalls the wave
-    // between items.
+    // (from its records' positions) during the current item's flush, so no
+    // round trip stalls the wave between items.
     const uint4 *items = reinterpret_cast<const uint4 *>(a.items);
+    auto tile_origin = [&](uint32_t tile, int (&torg)[3]) {
+#pragma unroll
+        for (int e = 0; e < DIM; ++e) {
+            torg[e] = (int)(tile % (uint32_t)a.ntx) * kTile;
+            tile /= (uint32_t)a.ntx;
+        }
+    };
     uint32_t next = 0;
     if (lane == 0)
         next = atomicAdd(a.cursor, 1u);
     uint32_t item = __builtin_amdgcn_readfirstlane(next);
+    // cell keys: from the binning's key array where it wrote one, else from
+    // the records' positions
+    const bool key_array = a.meta[kMetaKeys] != 0u;
+    auto item_keys = [&](const uint4 &it, uint32_t (&kw)[kKeyWords]) {
+        if (key_array) {
+            load_keys(a.cell_key, it.y, it.z, lane, kw);
+        } else {
+            int t0[3] = { 0, 0, 0 };
+            tile_origin(it.x, t0);
+            record_keys<DIM>(a.sorted, it.y, it.z, t0, a.nf, lane, kw);
+        }
+    };
     uint4 rec_item = make_uint4(0u, 0u, 0u, 0u);
     uint32_t kw[kKeyWords];
     if (item < n_items) {
         rec_item = items[item];
-        load_keys(a.cell_key, rec_item.y, rec_item.z, lane, kw);
+        item_keys(rec_item, kw);
     }
     for (;;) {
         if (item >= n_items)
@@ -82,16 +101,9 @@ p2g_tiled_kernel(TiledArgs a)
         if (lane == 0)
             next = atomicAdd(a.cursor, 1u);
         // item: tile, first record, records (one slice of the tile)
-        const uint32_t tile = rec_item.x, first = rec_item.y, count = rec_item.z;
+        const uint32_t first = rec_item.y, count = rec_item.z;
         int torg[3] = { 0, 0, 0 };
-        {
-            uint32_t t = tile;
-#pragma unroll
-            for (int e = 0; e < DIM; ++e) {
-                torg[e] = (int)(t % (uint32_t)a.ntx) * kTile;
-                t /= (uint32_t)a.ntx;
-            }
-        }
+        tile_origin(rec_item.x, torg);
         const uint32_t groups = sort_item<false>(kw, first, count, ent, gpos, cnt, cgs, rep, lane);
         const uint32_t rows = (groups + kWave - 1) / kWave;
         const uint32_t item_next = __builtin_amdgcn_readfirstlane(next);
@@ -198,7 +210,7 @@ p2g_tiled_kernel(TiledArgs a)
         item = item_next;
         rec_item = rec_next;
         if (item < n_items)
-            load_keys(a.cell_key, rec_item.y, rec_item.z, lane, kw);
+            item_keys(rec_item, kw);
         // Flush: every non-zero node sum goes to the grid with one 64-bit
         // atomic, and the block is left zeroed for the next item.
 #pragma unroll

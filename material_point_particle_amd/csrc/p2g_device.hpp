@@ -265,7 +265,7 @@ __device__ __forceinline__ void group_hoist(const float *rec, float nf, float dx
 
 struct TiledArgs {
     const float *sorted;
-    const uint8_t *cell_key;
+    const uint8_t *cell_key;               // the records' cell keys, when the binning wrote them
     const uint32_t *items, *meta;
     uint32_t *cursor;
     int n, ntx;
@@ -323,7 +323,46 @@ __device__ __forceinline__ void load_keys(const uint8_t *__restrict__ keys, uint
     }
 }
 
-// `kw` holds the slice's keys as load_keys left them; cnt must be zero on
+// The same packing of keys computed from the records themselves: the key of
+// slice position s is the local number (tile_local) of the base cell of
+// record first + s inside the tile whose first cell is torg, with
+// base = floor(x n - 1/2) per axis exactly as the binning computes it.  Each
+// axis offset is masked to the tile, so a key is below kWave even for a record
+// outside its tile (never in correct use; the rows check such a group and
+// count it in status[3]).  Records are read by their first 16 bytes (x).
+template <int DIM>
+__device__ __forceinline__ void record_keys(const float *__restrict__ sorted, uint32_t first, uint32_t count,
+                                            const int (&torg)[3], float nf, int lane, uint32_t kw[kKeyWords])
+{
+    constexpr int R = rec_floats<DIM>();
+    const uint32_t off = first & 3u;
+    const uint32_t n_words = (off + count + 3u) / 4u;
+    const int rounds = (int)((n_words + kWave - 1) / kWave);
+#pragma unroll
+    for (int k = 0; k < kKeyWords; ++k) {
+        kw[k] = 0u;
+        if (k >= rounds)
+            continue;
+        float4 xs[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t s = 4u * (uint32_t)(k * kWave + lane) + (uint32_t)b - off;
+            xs[b] = s < count ? *reinterpret_cast<const float4 *>(sorted + (int64_t)(first + s) * R)
+                              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float xe[3] = { xs[b].x, xs[b].y, xs[b].z };
+            uint32_t l[DIM];
+#pragma unroll
+            for (int e = 0; e < DIM; ++e)
+                l[e] = (uint32_t)((int)floorf(xe[e] * nf - 0.5f) - torg[e]) & (uint32_t)(kTile - 1);
+            kw[k] |= tile_local<DIM>(l) << (8 * b);
+        }
+    }
+}
+
+// `kw` holds the slice's keys as load_keys or record_keys left them; cnt must be zero on
 // entry (all 2 kWave slots), and the call leaves it so for the next item.
 // STRAYS: a key of kWave or more marks a record outside the tile, which gets
 // no group (its entry goes to the spare entry).

@@ -78,7 +78,7 @@ def test_workspace_layout_is_disjoint_and_aligned():
         spans = sorted([
             (lay.tile_count, 4 * lay.n_tiles), (lay.tile_start, 4 * (lay.n_tiles + 1)), (lay.tile_active, lay.n_tiles),
             (lay.meta, 128), (lay.items, 16 * lay.max_items), (lay.rank, 4 * max(N, 1)), (lay.slot, 4 * max(N, 1)),
-            (lay.cell_key, max(N, 1)), (lay.sorted, 4 * lay.n_fields * max(N, 1)),
+            (lay.cell_key, max(N, 1) + 4), (lay.sorted, 4 * lay.n_fields * max(N, 1)),
             (lay.scan_tmp, 4 * (2 + lay.rows_per_item) * ((lay.n_tiles + 4095) // 4096))])
         for (a, la), (b, _) in zip(spans, spans[1:]):
             assert a % 256 == 0 and a + la <= b

@@ -240,13 +240,23 @@ def test_p2g_empty_and_single_particle(mpm, oracle_lib):
 
 # ------------------------------------------------------------------ binning
 
-@pytest.mark.parametrize("name,count", [("pile_2d", None), ("dam_3d_128", 1 << 16), ("blobs_3d_256", 1 << 18)])
-def test_binning_matches_oracle(mpm, oracle_lib, name, count):
+@pytest.mark.parametrize("name,count,shuffled", [("pile_2d", None, False), ("dam_3d_128", 1 << 16, False),
+                                                 ("blobs_3d_256", 1 << 18, False), ("blobs_3d_256", 1 << 18, True)])
+def test_binning_matches_oracle(mpm, oracle_lib, name, count, shuffled):
+    """Tile counts, starts, records, work items and the P2G grid of the
+    binning, in generator order (long runs: the binning writes the records'
+    cell keys) and shuffled (short runs: no key array, P2G reads each record's
+    cell from its position)."""
     w = WORKLOADS[name] if count is None else scaled(WORKLOADS[name], count)
     host = build(w)
-    say("binning", w.name)
+    if shuffled:
+        perm = G.permutation(w.seed ^ 0x5F5F, 0x5EED, w.n_particles)
+        host = {k: np.ascontiguousarray(v[..., perm]) for k, v in host.items()}
+    say("binning", w.name, "shuffled" if shuffled else "generator order")
     cnt, start, order = oracle_lib.bin_particles(w.dim, w.n, w.tile, host, ranges_of(w))
-    _, _, tr = gpu_p2g(mpm, w, host, True)
+    grids, _, tr = gpu_p2g(mpm, w, host, True)
+    ref, _ = oracle_lib.p2g_quadratic(w.dim, w.n, w.frac_bits, host, ranges_of(w))
+    assert_same(grids[0], ref, f"{w.name} binned P2G")
     lay = tr.layout
     N, per = w.n_particles, 4 ** w.dim
     # the library numbers the cells of a 3D tile x fastest, then z, then y; the
@@ -269,6 +279,15 @@ def test_binning_matches_oracle(mpm, oracle_lib, name, count):
     meta = tr.meta()
     items = int(meta[0])
     assert int(meta[2]) == len(order)
+    # keys are written exactly when the count's runs average 32 records or
+    # more: the lattice-ordered dam and the pile in rows do, a shuffled input
+    # does not (the generator-ordered blobs at this size may go either way)
+    runs = int(meta[6])
+    assert int(meta[7]) == int(runs * 32 <= len(order))
+    if shuffled:
+        assert int(meta[7]) == 0
+    elif name != "blobs_3d_256":
+        assert int(meta[7]) == 1
     # record index of every binned particle: inside its tile's range, each index once
     slot_of = u32(tr.ws_u32("slot", N)).astype(np.int64)
     binned_idx = np.nonzero(slot_of != 0xFFFFFFFF)[0]
@@ -283,8 +302,14 @@ def test_binning_matches_oracle(mpm, oracle_lib, name, count):
     src = np.concatenate([host["x"], host["v"], host["C"], host["m"][None]])
     nf = src.shape[0]
     assert np.array_equal(rec[sl, :nf].T, src[:, order])
-    ck = tr.ws.view(torch.uint8)[lay.cell_key: lay.cell_key + nb].cpu().numpy().astype(np.int64)
+    # each record's cell, as P2G reads it from the record's position (float32
+    # floor(x n - 1/2) per axis, local to its tile), is the oracle's cell
+    g = np.floor(rec[:, :w.dim].astype(np.float32) * np.float32(w.n) - np.float32(0.5)).astype(np.int64) % 4
+    ck = g[:, 0] + 4 * g[:, 2] + 16 * g[:, 1] if w.dim == 3 else g[:, 0] + 4 * g[:, 1]
     assert np.array_equal(ck[sl], plocal[order])
+    if int(meta[7]):
+        written = tr.ws.view(torch.uint8)[lay.cell_key: lay.cell_key + nb].cpu().numpy().astype(np.int64)
+        assert np.array_equal(written, ck)
     # work items: each tile's records cut into slices of S records (the last one
     # shorter), handed out alternately from the large and the small end of the
     # size order (by the rows their groups need)
