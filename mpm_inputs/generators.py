@@ -10,7 +10,12 @@ pseudorandom number generators", OOPSLA 2014) used as a counter-based
 generator: draw ``i`` of a stream is the SplitMix64 output function applied to
 ``base + (i + 1) * golden``.  Every derived distribution is written out here
 (uniform from the top bits, normals by Box-Muller) instead of relying on a
-library distribution whose algorithm could change between versions.
+library distribution whose algorithm could change between versions.  The
+Box-Muller logarithm and cosine are evaluated here too (range reduction by
+exact steps, then series in float64 with only IEEE-rounded +, -, *, /), not by
+numpy's log and cos, whose vectorised versions differ in the last bit between
+host CPUs: every host draws bit-identical inputs, so stored digests of results
+on these inputs hold wherever the inputs are generated.
 """
 from __future__ import annotations
 
@@ -93,21 +98,65 @@ def uniform_int(seed: int, tag: int, n: int, lo: int, hi: int) -> np.ndarray:
     return (lo + np.floor(uniform01(seed, tag, n) * span)).astype(np.int64)
 
 
+_LN2 = 0.6931471805599453
+_HALF_PI = 1.5707963267948966
+_SQRT_HALF = 0.7071067811865476
+
+
+def _log(y: np.ndarray) -> np.ndarray:
+    """Natural logarithm of positive float64 y: y = m 2^e with m in
+    [sqrt(1/2), sqrt(2)) (frexp and the doubling are exact), then
+    ln m = 2 atanh(s) = 2 (s + s^3/3 + s^5/5 + ...), s = (m - 1)/(m + 1),
+    |s| < 0.172, summed by Horner's rule to s^27 (truncation below 1e-20)."""
+    m, e = np.frexp(y)
+    low = m < _SQRT_HALF
+    m = np.where(low, m * 2.0, m)
+    e = e - low.astype(e.dtype)
+    s = (m - 1.0) / (m + 1.0)
+    z = s * s
+    p = np.full_like(s, 1.0 / 27.0)
+    for k in range(12, -1, -1):
+        p = p * z + 1.0 / (2 * k + 1)
+    return e.astype(np.float64) * _LN2 + 2.0 * s * p
+
+
+def _cos_2pi(u: np.ndarray) -> np.ndarray:
+    """cos(2 pi u) for float64 u in [0, 1): quadrant q = floor(4u) and
+    f = 4u - q exactly (u holds 53-bit multiples of 2^-53), folded to
+    f <= 1/2 by f -> 1 - f (cos and sin swap); then the Taylor series of cos
+    and sin at phi = (pi/2) f <= pi/4, summed by Horner's rule to phi^26
+    (truncation below 1e-20)."""
+    v = u * 4.0
+    q = np.floor(v)
+    f = v - q
+    fold = f > 0.5
+    f = np.where(fold, 1.0 - f, f)
+    phi = f * _HALF_PI
+    z = phi * phi
+    c = np.ones_like(phi)
+    sn = np.ones_like(phi)
+    for k in range(13, 0, -1):                 # cos: 1 - z/2! + z^2/4! ...; sin: phi (1 - z/3! + ...)
+        c = 1.0 - z * c / ((2 * k - 1) * (2 * k))
+        sn = 1.0 - z * sn / ((2 * k) * (2 * k + 1))
+    sn = sn * phi
+    cf = np.where(fold, sn, c)                 # cos((pi/2) f) before folding
+    sf = np.where(fold, c, sn)                 # sin((pi/2) f)
+    qi = q.astype(np.int64) & 3
+    return np.where(qi == 0, cf, np.where(qi == 1, -sf, np.where(qi == 2, -cf, sf)))
+
+
 def normal(seed: int, tag: int, n: int, sigma: float, start: int = 0) -> np.ndarray:
     """float64 normal draws N(0, sigma^2) by the Box-Muller transform: draw k
     uses uniforms k of streams (2*tag+1, 2*tag+2), r = sqrt(-2 ln(1-u1)),
-    value = sigma * r * cos(2 pi u2)."""
+    value = sigma * r * cos(2 pi u2) (ln and cos as _log and _cos_2pi)."""
     b1, b2 = _base(seed, 2 * tag + 1), _base(seed, 2 * tag + 2)
 
     def fn(lo, hi):
         u1 = _u01(b1, start + lo, start + hi)
         np.subtract(1.0, u1, out=u1)          # (0, 1]
-        np.log(u1, out=u1); np.multiply(u1, -2.0, out=u1); np.sqrt(u1, out=u1)
-        u2 = _u01(b2, start + lo, start + hi)
-        np.multiply(u2, 2.0 * np.pi, out=u2); np.cos(u2, out=u2)
-        np.multiply(u1, u2, out=u1)
-        np.multiply(u1, sigma, out=u1)
-        return u1
+        r = np.sqrt(_log(u1) * -2.0)
+        c = _cos_2pi(_u01(b2, start + lo, start + hi))
+        return (r * c) * sigma
     return _parallel(n, fn, np.empty(n, dtype=np.float64))
 
 
