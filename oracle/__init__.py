@@ -57,6 +57,12 @@ def lib():
         L.oracle_p2g_quadratic_threads.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_int64, F32P, F32P, F32P, F32P,
                                                    I64P, ct.c_double, ct.c_double, ct.c_double, I64P, U32P,
                                                    ct.c_int]
+        L.oracle_pbmpm_project_elastic.restype = None
+        L.oracle_pbmpm_project_elastic.argtypes = [ct.c_int, ct.c_int64, F32P, F32P, ct.c_float, ct.c_int, U32P]
+        L.oracle_pbmpm_grid_update.restype = None
+        L.oracle_pbmpm_grid_update.argtypes = [ct.c_int, ct.c_int, I64P, F32P, ct.c_int]
+        L.oracle_pbmpm_integrate.restype = None
+        L.oracle_pbmpm_integrate.argtypes = [ct.c_int, ct.c_int, ct.c_int64, F32P, F32P, ct.c_float, F32P, U32P]
         L.oracle_p2g_log2_bound.restype = ct.c_double
         L.oracle_p2g_log2_bound.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_int64,
                                             ct.c_double, ct.c_double, ct.c_double]
@@ -229,3 +235,54 @@ def bin_particles(dim: int, n: int, tile: int, particles: dict, ranges):
                               float(ranges[0]), float(ranges[1]), float(ranges[2]), _p(count, U32P),
                               _p(start, U32P), _p(order, I64P))
     return count, start, order[:placed]
+
+
+# ------------------------------------------------------------------ PB-MPM
+
+def pbmpm_project_elastic(dim: int, F: np.ndarray, D: np.ndarray, relax: float, polar_iters: int):
+    """Elastic projection of D (float32 [dim*dim][np], updated in place) toward
+    the polar rotation of (I + D) F; returns status[4]."""
+    F = np.ascontiguousarray(F, dtype=np.float32)
+    assert D.dtype == np.float32 and D.flags.c_contiguous
+    status = np.zeros(4, dtype=np.uint32)
+    lib().oracle_pbmpm_project_elastic(dim, D.shape[-1], _p(F, F32P), _p(D, F32P), ct.c_float(relax), polar_iters,
+                                       _p(status, U32P))
+    return status
+
+
+def pbmpm_grid_update(dim: int, n: int, grid: np.ndarray, band: int):
+    """Displacement-form grid update; consumes (zeroes) grid; returns dg[dim][n]*dim."""
+    assert grid.dtype == np.int64 and grid.flags.c_contiguous
+    dg = np.zeros((dim,) + (n,) * dim, dtype=np.float32)
+    lib().oracle_pbmpm_grid_update(dim, n, _p(grid, I64P), _p(dg, F32P), band)
+    return dg
+
+
+def pbmpm_integrate(dim: int, n: int, x: np.ndarray, d: np.ndarray, dt: float, gravity):
+    """x += d (clamped, counted in status[2]), then d += g dt^2; in place; returns status[4]."""
+    assert x.dtype == np.float32 and d.dtype == np.float32 and x.flags.c_contiguous and d.flags.c_contiguous
+    g = np.zeros(3, dtype=np.float32)
+    g[:dim] = np.asarray(gravity, dtype=np.float32)[:dim]
+    status = np.zeros(4, dtype=np.uint32)
+    lib().oracle_pbmpm_integrate(dim, n, x.shape[-1], _p(x, F32P), _p(d, F32P), ct.c_float(dt), _p(g, F32P),
+                                 _p(status, U32P))
+    return status
+
+
+def pbmpm_substep(dim: int, n: int, frac_bits: int, state: dict, ranges, iterations: int, relax: float,
+                  polar_iters: int, band: int, dt: float, gravity):
+    """One PB-MPM substep of the oracle on state = {x, v (the displacement d),
+    C (the displacement gradient D), m, F}, updated in place.  Returns
+    (the P2G grid of the last iteration, status[4] summed)."""
+    status = np.zeros(4, dtype=np.int64)
+    grid = None
+    for _ in range(iterations):
+        status += pbmpm_project_elastic(dim, state["F"], state["C"], relax, polar_iters)
+        grid, st = p2g_quadratic(dim, n, frac_bits, state, ranges)
+        status += st
+        dg = pbmpm_grid_update(dim, n, grid.copy(), band)
+        status += g2p(dim, n, dg, state, 0.0)
+    status += pbmpm_integrate(dim, n, state["x"], state["v"], dt, gravity)
+    update_F(dim, state["C"], state["F"], 1.0)
+    return grid, status
+

@@ -780,3 +780,176 @@ int64_t oracle_bin(int dim, int n, int tile, int64_t np_, const float *x, const 
     free(key);
     return (int64_t)run;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Position-based MPM (PB-MPM), elastic material: the iteration loop of the  */
+/* implementation page's section 3.3.2.                                      */
+/* ------------------------------------------------------------------------ */
+/*
+ * A particle carries its displacement over the substep d (kept where the
+ * APIC transfer keeps v) and its displacement gradient D (kept where it keeps
+ * the affine matrix C, same layout), with x, m and the deformation gradient
+ * F.  Per substep, `iterations` times:
+ *   oracle_pbmpm_project_elastic   (particleUpdate: D toward the elastic target)
+ *   oracle_p2g_quadratic           (particleToGrid of m and m (d + D (x_i - x_p)),
+ *                                   with v := d and C := D; no stress term)
+ *   oracle_pbmpm_grid_update       (gridUpdate in displacement form)
+ *   oracle_g2p with dt = 0         (gridToParticle: gathers d and D = B 4 n^2;
+ *                                   x stays in place)
+ * then once: oracle_pbmpm_integrate (x += d, gravity into the next d) and
+ * oracle_update_F with dt = 1 (F <- (I + D) F).  d and D persist into the next
+ * substep (the warm start the page describes).
+ */
+
+/* Cofactor matrix of the dim x dim matrix a (so a^-T = cof / det); returns
+ * det a = (a00 cof00 + a01 cof01) + a02 cof02 (2D: a00 a11 - a01 a10). */
+static double pb_cofactor(int dim, const double a[3][3], double cof[3][3])
+{
+    if (dim == 3) {
+        cof[0][0] = a[1][1] * a[2][2] - a[1][2] * a[2][1];
+        cof[0][1] = a[1][2] * a[2][0] - a[1][0] * a[2][2];
+        cof[0][2] = a[1][0] * a[2][1] - a[1][1] * a[2][0];
+        cof[1][0] = a[0][2] * a[2][1] - a[0][1] * a[2][2];
+        cof[1][1] = a[0][0] * a[2][2] - a[0][2] * a[2][0];
+        cof[1][2] = a[0][1] * a[2][0] - a[0][0] * a[2][1];
+        cof[2][0] = a[0][1] * a[1][2] - a[0][2] * a[1][1];
+        cof[2][1] = a[0][2] * a[1][0] - a[0][0] * a[1][2];
+        cof[2][2] = a[0][0] * a[1][1] - a[0][1] * a[1][0];
+        return (a[0][0] * cof[0][0] + a[0][1] * cof[0][1]) + a[0][2] * cof[0][2];
+    }
+    cof[0][0] = a[1][1];
+    cof[0][1] = -a[1][0];
+    cof[1][0] = -a[0][1];
+    cof[1][1] = a[0][0];
+    return a[0][0] * a[1][1] - a[0][1] * a[1][0];
+}
+
+/*
+ * particleUpdate for an elastic material.  The material's target shape is a
+ * pure rotation: the polar rotation R of the trial deformation Ft = (I + D) F
+ * (the U V^T of its SVD; the page replaces the SVD by Newton's polar
+ * iteration in 3D: R <- (R + R^-T) / 2 from R = Ft, `polar_iters` steps).  The
+ * displacement gradient that reaches the target is D* = R F^-1 - I, and D
+ * relaxes toward it at rate `relax` (the page's elasticRelaxation, default 1.5,
+ * over-relaxed): D <- D + relax (D* - D).  Everything in float64 in this order,
+ * D rounded to float32 once:
+ *   Ft_de = sum_q ([d == q] + D_dq) F_qe          (q ascending)
+ *   R_de  <- (R_de + cof(R)_de / det R) * 0.5
+ *   F^-1_qe = cof(F)_eq / det F
+ *   D*_de = (sum_q R_dq F^-1_qe) - [d == e]
+ *   D_de  <- D_de + relax * (D*_de - D_de)
+ * A particle whose Ft or F has a non-positive determinant, or whose Newton
+ * iterate loses it, keeps D and is counted in status[0].
+ */
+void oracle_pbmpm_project_elastic(int dim, int64_t np_, const float *F, float *D, float relax, int polar_iters,
+                                  uint32_t *status)
+{
+    for (int64_t p = 0; p < np_; ++p) {
+        double f[3][3] = { { 0 } }, dd[3][3] = { { 0 } }, ft[3][3] = { { 0 } }, r[3][3], cof[3][3];
+        for (int d = 0; d < dim; ++d)
+            for (int e = 0; e < dim; ++e) {
+                f[d][e] = (double)F[(int64_t)(d * dim + e) * np_ + p];
+                dd[d][e] = (double)D[(int64_t)(d * dim + e) * np_ + p];
+            }
+        for (int d = 0; d < dim; ++d)
+            for (int e = 0; e < dim; ++e) {
+                double t = ((d == 0 ? 1.0 : 0.0) + dd[d][0]) * f[0][e];
+                for (int q = 1; q < dim; ++q)
+                    t = t + ((d == q ? 1.0 : 0.0) + dd[d][q]) * f[q][e];
+                ft[d][e] = t;
+            }
+        int ok = pb_cofactor(dim, ft, cof) > 0.0;
+        for (int d = 0; d < 3; ++d)
+            for (int e = 0; e < 3; ++e)
+                r[d][e] = ft[d][e];
+        for (int k = 0; ok && k < polar_iters; ++k) {
+            const double det = pb_cofactor(dim, r, cof);
+            if (!(det > 0.0)) {
+                ok = 0;
+                break;
+            }
+            for (int d = 0; d < dim; ++d)
+                for (int e = 0; e < dim; ++e)
+                    r[d][e] = (r[d][e] + cof[d][e] / det) * 0.5;
+        }
+        const double detf = ok ? pb_cofactor(dim, f, cof) : 0.0;
+        if (!ok || !(detf > 0.0)) {
+            status[ST_DOMAIN] += 1;
+            continue;
+        }
+        double finv[3][3];
+        for (int q = 0; q < dim; ++q)
+            for (int e = 0; e < dim; ++e)
+                finv[q][e] = cof[e][q] / detf;
+        for (int d = 0; d < dim; ++d)
+            for (int e = 0; e < dim; ++e) {
+                double t = r[d][0] * finv[0][e];
+                for (int q = 1; q < dim; ++q)
+                    t = t + r[d][q] * finv[q][e];
+                const double dstar = t - (d == e ? 1.0 : 0.0);
+                const int64_t i = (int64_t)(d * dim + e) * np_ + p;
+                D[i] = (float)(dd[d][e] + (double)relax * (dstar - dd[d][e]));
+            }
+    }
+}
+
+/*
+ * gridUpdate in displacement form (section 3.3.2: mass-normalise, then the
+ * guardian projects each node's displaced position back into bounds).  Per
+ * node: where M != 0, d_e = (float)((double)P_e / (double)M), then with the
+ * node's position X_e = i_e dx (exact in float32 for a power-of-two n),
+ * d_e = fminf(fmaxf(X_e + d_e, lo), hi) - X_e with lo = band dx and
+ * hi = (n - 1 - band) dx (float32, in this order); d = 0 where M == 0; then
+ * M and P are set to 0 (consume-and-zero, as the velocity-form update).
+ * No gravity here: the integrate step puts it into the next displacement.
+ */
+void oracle_pbmpm_grid_update(int dim, int n, int64_t *grid, float *dg, int band)
+{
+    const int64_t nodes = dim == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    const float dx = 1.0f / (float)n;
+    const float lo = (float)band * dx, hi = (float)(n - 1 - band) * dx;
+    for (int64_t node = 0; node < nodes; ++node) {
+        const int64_t M = grid[node];
+        const int idx[3] = { (int)(node % n), (int)((node / n) % n), dim == 3 ? (int)(node / ((int64_t)n * n)) : 0 };
+        for (int d = 0; d < dim; ++d) {
+            float v = 0.0f;
+            if (M != 0) {
+                v = (float)((double)grid[(int64_t)(1 + d) * nodes + node] / (double)M);
+                const float X = (float)idx[d] * dx;
+                v = fminf(fmaxf(X + v, lo), hi) - X;
+            }
+            dg[(int64_t)d * nodes + node] = v;
+            grid[(int64_t)(1 + d) * nodes + node] = 0;
+        }
+        grid[node] = 0;
+    }
+}
+
+/*
+ * particleIntegrate for an elastic material (section 3.3.2), without the
+ * deformation update (oracle_update_F with dt = 1 does F <- (I + D) F): per
+ * particle x_e <- x_e + d_e (float32), clamped to [dx, (n - 2) dx] with
+ * clamped particles counted in status[2] (a backstop counted, not hidden);
+ * then gravity goes into the next substep's displacement: d_e <- d_e + gdt2_e
+ * with gdt2_e = g_e * (dt * dt) formed once in float32.
+ */
+void oracle_pbmpm_integrate(int dim, int n, int64_t np_, float *x, float *d, float dt, const float *gravity,
+                            uint32_t *status)
+{
+    const float dx = 1.0f / (float)n;
+    const float lo = dx, hi = (float)(n - 2) * dx;
+    float gdt2[3];
+    for (int e = 0; e < dim; ++e)
+        gdt2[e] = gravity[e] * (dt * dt);
+    for (int64_t p = 0; p < np_; ++p) {
+        int clamped = 0;
+        for (int e = 0; e < dim; ++e) {
+            const float xa = x[(int64_t)e * np_ + p] + d[(int64_t)e * np_ + p];
+            const float xc = fminf(fmaxf(xa, lo), hi);
+            clamped |= xc != xa;
+            x[(int64_t)e * np_ + p] = xc;
+            d[(int64_t)e * np_ + p] = d[(int64_t)e * np_ + p] + gdt2[e];
+        }
+        status[ST_CLAMP] += (uint32_t)clamped;
+    }
+}
