@@ -308,6 +308,88 @@ def measure_elastic(args, torch, w, build, Transfer):
     }
 
 
+def measure_pbmpm(args, torch, w, build):
+    """The position-based MPM substep (elastic material) on the 8M-particle
+    jelly cube at 256^3: per substep 5 iterations of the elastic projection,
+    binning, P2G, displacement-form grid update and G2P gather, then the
+    integrate step and F <- (I + D) F, timed per stage with HIP events over
+    the evolving state.  Algorithmic bytes of the per-particle passes: the
+    projection reads F and D and writes D (108 B per particle), the integrate
+    step reads and writes x and d (48 B)."""
+    import material_point_particle_amd._lib as L
+    from material_point_particle_amd.transfer import ElasticParticles, PBMPMSubsteps, Transfer
+    host = build(w)
+    ex = w.extra
+    parts = ElasticParticles(host, host["F"], host["vol"])
+    del host
+    tr = Transfer(w.dim, w.n, w.frac_bits, (w.max_mass, w.max_speed, w.max_affine), parts.n)
+    loop = PBMPMSubsteps(tr, parts, ex["dt"], ex["gravity"], ex["iterations"], ex["relax"], ex["polar_iters"],
+                         ex["band"])
+    stream = torch.cuda.current_stream()
+    names = ("project", "bin", "p2g", "grid_update", "g2p")
+    steps = (lambda: L.mpm_pbmpm_project_elastic(tr.desc, parts.desc(), parts.F, loop.relax, loop.polar_iters,
+                                                 tr.status),
+             lambda: tr.bin(parts),
+             lambda: tr.p2g(parts, binned=True),
+             lambda: L.mpm_pbmpm_grid_update(tr.desc, tr.ws, tr.grid, tr.vg, loop.band),
+             lambda: tr.g2p(parts, 0.0))
+
+    def substep(ev=None):
+        for it in range(loop.iterations):
+            for i, f in enumerate(steps):
+                if ev:
+                    ev[it][i].record(stream)
+                f()
+        if ev:
+            ev[loop.iterations][0].record(stream)
+        loop.integrate()
+        if ev:
+            ev[loop.iterations][1].record(stream)
+
+    substep()
+    torch.cuda.synchronize()
+    k = max(3, args.substeps // 4)
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(loop.iterations + 1)]
+              for _ in range(k)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(k):
+        substep(events[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total = start.elapsed_time(stop) / k
+    st = np.zeros(len(names))
+    integ = 0.0
+    for ev in events:
+        for it in range(loop.iterations):
+            nxt = ev[it + 1][0]
+            marks = ev[it] + [nxt]
+            for i in range(len(names)):
+                st[i] += marks[i].elapsed_time(marks[i + 1])
+        integ += ev[loop.iterations][0].elapsed_time(ev[loop.iterations][1])
+    st /= k
+    integ /= k
+    status = tr.status.cpu().numpy().view(np.uint32).tolist()
+    log(f"pbmpm substeps: {total:.3f} ms (" + ", ".join(f"{nm} {t:.3f}" for nm, t in zip(names, st)) +
+        f", integrate {integ:.3f}; {loop.iterations} iterations)")
+
+    def gbs(b, t):
+        return round(b / (t * 1e-3) / 1e9, 1)
+
+    proj_ms = st[0] / loop.iterations
+    return {
+        "workload": f"{w.name}: {parts.n} particles, elastic cube falling onto the floor, {w.n}^3 nodes, "
+                    f"2^{w.frac_bits}, dt {ex['dt']}, {loop.iterations} iterations per substep, relaxation "
+                    f"{loop.relax}, {loop.polar_iters} Newton polar steps, guardian band {loop.band}",
+        "substeps": k, "ms_per_substep": round(total, 4), "particles_per_s": round(parts.n / (total * 1e-3), 1),
+        "stages_ms_per_substep": {nm: round(float(t), 4) for nm, t in zip(names, st)},
+        "integrate_ms": round(float(integ), 4),
+        "project": {"bytes": parts.n * 108, "ms_per_call": round(float(proj_ms), 4),
+                    "achieved_gbs": gbs(parts.n * 108, proj_ms), "bound": "alu (float64 Newton polar iteration)"},
+        "status": status,
+    }
+
+
 def measure_isplit(args, torch, w, build):
     """The integer-split quadratic APIC transfer (exact conservation) on
     1,048,576 integer particles at 128^3 nodes, one mpm_p2g_isplit call per
@@ -381,6 +463,10 @@ def parse():
                     help="skip the fused-substep measurement (state resident in the binned records)")
     ap.add_argument("--only-fused", action="store_true",
                     help="run only the fused-substep measurement; prints its object")
+    ap.add_argument("--no-pbmpm", action="store_true",
+                    help="skip the position-based MPM substep measurement on the jelly cube")
+    ap.add_argument("--only-pbmpm", action="store_true",
+                    help="run only the position-based MPM substep measurement; prints its object")
     ap.add_argument("--no-isplit", action="store_true",
                     help="skip the integer-split quadratic transfer measurement")
     ap.add_argument("--only-isplit", action="store_true",
@@ -408,6 +494,9 @@ def main():
     if args.only_fused:
         print(json.dumps({"substep_fused": measure_fused(args, torch, WORKLOADS["dam_3d_256"], build, DeviceParticles,
                                                          Transfer)}), flush=True)
+        return
+    if args.only_pbmpm:
+        print(json.dumps({"pbmpm": measure_pbmpm(args, torch, WORKLOADS["pbmpm_jelly_3d_256"], build)}), flush=True)
         return
     if args.only_isplit:
         print(json.dumps({"isplit": measure_isplit(args, torch, WORKLOADS["isplit_3d_128"], build)}), flush=True)
@@ -577,6 +666,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_elastic:
         out["elastic"] = measure_elastic(args, torch, WORKLOADS["jelly_3d_256"], build, Transfer)
+        torch.cuda.empty_cache()
+    if not args.no_pbmpm:
+        out["pbmpm"] = measure_pbmpm(args, torch, WORKLOADS["pbmpm_jelly_3d_256"], build)
         torch.cuda.empty_cache()
     if not args.no_isplit:
         out["isplit"] = measure_isplit(args, torch, WORKLOADS["isplit_3d_128"], build)

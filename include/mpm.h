@@ -452,6 +452,65 @@ int mpm_neohookean_affine(const mpm_grid_desc *grid, const mpm_particles *partic
 int mpm_update_deformation(const mpm_grid_desc *grid, const mpm_particles *particles, float *F, float dt,
                            hipStream_t stream);
 
+/* ---- Position-based MPM (PB-MPM): the iteration loop for an elastic material ----
+ *
+ * "Implementation -- GPU Optimization & Reference Codebases", section 3.3.2.
+ * A particle carries its displacement over the substep d (in particles->v)
+ * and its displacement gradient D (in particles->C, same layout), with x, m
+ * and the deformation gradient F (float[dim*dim][n], like C).  A substep:
+ *
+ *   repeat `iterations` times (the page's default 5):
+ *     mpm_pbmpm_project_elastic     D toward the elastic target
+ *     mpm_bin_particles, mpm_p2g    mass and momentum m (d + D (x_i - x_p)),
+ *                                   no stress term
+ *     mpm_pbmpm_grid_update         mass-normalise, guardian
+ *     mpm_g2p with dt = 0           gather d and D (x stays in place)
+ *   mpm_pbmpm_integrate             x += d, gravity into the next d
+ *   mpm_update_deformation, dt = 1  F <- (I + D) F
+ *
+ * d and D carry over to the next substep as its starting guess (warm start).
+ */
+
+/* particleUpdate for an elastic material: the target shape is a rotation, the
+ * polar rotation R of the trial deformation Ft = (I + D) F (Newton's iteration
+ * R <- (R + R^-T) / 2 from R = Ft, polar_iters steps, in place of an SVD); the
+ * displacement gradient reaching it is D* = R F^-1 - I, and D relaxes toward it:
+ * D <- D + relax (D* - D) (relax in [0, 2]; the page's default 1.5 over-relaxes).
+ * In float64 in this order, D rounded to float32 once:
+ *   Ft_de = sum_q ([d == q] + D_dq) F_qe, R_de <- (R_de + cof(R)_de / det R) / 2,
+ *   F^-1_qe = cof(F)_eq / det F, D*_de = sum_q R_dq F^-1_qe - [d == e],
+ *   D_de <- D_de + relax (D*_de - D_de),
+ * cof the cofactor matrix (det = (a00 cof00 + a01 cof01) + a02 cof02).
+ * Particles whose Ft, F or a Newton iterate has det <= 0 keep D and are
+ * counted in status[0].  particles: device; C (= D) read and written, x, v, m
+ * unused.  F: device float[dim*dim][n].  polar_iters in [0, 64].
+ * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
+int mpm_pbmpm_project_elastic(const mpm_grid_desc *grid, const mpm_particles *particles, const float *F, float relax,
+                              int32_t polar_iters, uint32_t *status, hipStream_t stream);
+
+/* gridUpdate in displacement form (the same section: mass-normalise, then the
+ * guardian projects each node's displaced position back into bounds).  Per
+ * node: where M != 0, d_e = (float)((double)P_e / (double)M), then with the
+ * node's position X_e = i_e dx, d_e = fminf(fmaxf(X_e + d_e, lo), hi) - X_e,
+ * lo = band dx, hi = (n - 1 - band) dx; d = 0 where M == 0; then M = P = 0.  No
+ * gravity (mpm_pbmpm_integrate puts it into the next displacement).  bins and
+ * bins_bytes as for mpm_grid_update (NULL: every node; else only the node
+ * tiles the binned P2G can reach).  grid: device int64[1+dim][n]^dim, read and
+ * zeroed.  dg: device float[dim][n]^dim, written.  band in [1, (n - 2) / 2].
+ * Errors: MPM_ERR_INVALID, MPM_ERR_WORKSPACE, MPM_ERR_HIP. */
+int mpm_pbmpm_grid_update(const mpm_grid_desc *grid, void *bins, size_t bins_bytes, int64_t *grid_io, float *dg,
+                          int32_t band, hipStream_t stream);
+
+/* particleIntegrate for an elastic material (the same section), without the
+ * deformation update (mpm_update_deformation with dt = 1): per particle
+ * x_e <- x_e + d_e (float32), clamped to [dx, (n - 2) dx] with clamped
+ * particles counted in status[2]; then d_e <- d_e + g_e * (dt * dt) (the
+ * product formed once in float32): gravity goes into the next substep's
+ * displacement.  particles: device, x and v (= d) read and written.
+ * gravity: host float[dim].  Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
+int mpm_pbmpm_integrate(const mpm_grid_desc *grid, const mpm_particles *particles, float dt, const float *gravity,
+                        uint32_t *status, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,7 +54,7 @@ EXPORTS = ("mpm_version", "mpm_strerror", "mpm_check_bounds", "mpm_workspace_byt
            "mpm_bin_particles", "mpm_p2g", "mpm_p2g_cic_split", "mpm_p2g_isplit", "mpm_isplit_workspace_bytes",
            "mpm_grid_update", "mpm_grid_clear", "mpm_g2p", "mpm_neohookean_affine", "mpm_update_deformation",
            "mpm_bin_resident", "mpm_g2p2g", "mpm_grid_clear_tiles", "mpm_gather_records",
-           "mpm_p2g_isplit_noalloc")
+           "mpm_p2g_isplit_noalloc", "mpm_pbmpm_project_elastic", "mpm_pbmpm_grid_update", "mpm_pbmpm_integrate")
 
 _lib = None
 
@@ -118,6 +118,15 @@ def lib() -> ct.CDLL:
                                 ct.c_int32, ct.c_void_p, ct.c_void_p]
         L.mpm_grid_clear_tiles.restype = ct.c_int
         L.mpm_grid_clear_tiles.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p]
+        L.mpm_pbmpm_project_elastic.restype = ct.c_int
+        L.mpm_pbmpm_project_elastic.argtypes = [P(mpm_grid_desc), P(mpm_particles), ct.c_void_p, ct.c_float, ct.c_int32,
+                                                ct.c_void_p, ct.c_void_p]
+        L.mpm_pbmpm_grid_update.restype = ct.c_int
+        L.mpm_pbmpm_grid_update.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_size_t, ct.c_void_p, ct.c_void_p,
+                                            ct.c_int32, ct.c_void_p]
+        L.mpm_pbmpm_integrate.restype = ct.c_int
+        L.mpm_pbmpm_integrate.argtypes = [P(mpm_grid_desc), P(mpm_particles), ct.c_float, P(ct.c_float), ct.c_void_p,
+                                          ct.c_void_p]
         L.mpm_gather_records.restype = ct.c_int
         L.mpm_gather_records.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_size_t, P(mpm_particles), ct.c_void_p,
                                          ct.c_void_p]
@@ -282,3 +291,21 @@ def mpm_neohookean_affine(desc, parts: mpm_particles, F, vol0, dt: float, mu: fl
 def mpm_update_deformation(desc, parts: mpm_particles, F, dt: float, stream=None) -> None:
     _check(lib().mpm_update_deformation(ct.byref(desc), ct.byref(parts), _ptr(F), dt, _stream(stream)),
            "mpm_update_deformation")
+
+
+def mpm_pbmpm_project_elastic(desc, parts: mpm_particles, F, relax: float, polar_iters: int, status,
+                              stream=None) -> None:
+    _check(lib().mpm_pbmpm_project_elastic(ct.byref(desc), ct.byref(parts), _ptr(F), relax, polar_iters, _ptr(status),
+                                           _stream(stream)), "mpm_pbmpm_project_elastic")
+
+
+def mpm_pbmpm_grid_update(desc, bins, grid, dg, band: int, stream=None) -> None:
+    _check(lib().mpm_pbmpm_grid_update(ct.byref(desc), _ptr(bins), _nbytes(bins), _ptr(grid), _ptr(dg), band,
+                                       _stream(stream)), "mpm_pbmpm_grid_update")
+
+
+def mpm_pbmpm_integrate(desc, parts: mpm_particles, dt: float, gravity, status, stream=None) -> None:
+    g = (ct.c_float * 3)(*(list(gravity) + [0.0] * (3 - len(gravity))))
+    _check(lib().mpm_pbmpm_integrate(ct.byref(desc), ct.byref(parts), dt, g, _ptr(status), _stream(stream)),
+           "mpm_pbmpm_integrate")
+

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmpm.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["abi.hip", "p2g.hip", "fused.hip", "bin.hip", "grid.hip", "stress.hip", "isplit.hip"]
+SOURCES = ["abi.hip", "p2g.hip", "fused.hip", "bin.hip", "grid.hip", "stress.hip", "isplit.hip", "pbmpm.hip"]
 ARCH = os.environ.get("MPM_OFFLOAD_ARCH", "gfx950")
 
 

@@ -541,6 +541,49 @@ int mpm_update_deformation(const mpm_grid_desc *grid, const mpm_particles *parti
     return hip_status(launch_update_F(grid->dim, particles->n, particles->C, F, dt, stream));
 }
 
+int mpm_pbmpm_project_elastic(const mpm_grid_desc *grid, const mpm_particles *particles, const float *F, float relax,
+                              int32_t polar_iters, uint32_t *status, hipStream_t stream)
+{
+    if (check_desc(grid) != MPM_OK || !particles || particles->n < 0 || particles->n > kMaxParticles)
+        return MPM_ERR_INVALID;
+    if (particles->n > 0 && (!aligned(particles->C, 4) || !aligned(F, 4)))
+        return MPM_ERR_INVALID;
+    if (!aligned(status, 4) || !(relax >= 0.0f && relax <= 2.0f) || polar_iters < 0 || polar_iters > 64)
+        return MPM_ERR_INVALID;
+    return hip_status(launch_pbmpm_project(grid->dim, particles->n, F, particles->C, relax, polar_iters, status,
+                                           stream));
+}
+
+int mpm_pbmpm_grid_update(const mpm_grid_desc *grid, void *bins, size_t bins_bytes, int64_t *grid_io, float *dg,
+                          int32_t band, hipStream_t stream)
+{
+    if (check_desc(grid) != MPM_OK || !aligned(grid_io, 8) || !aligned(dg, 4) || band < 1 ||
+        2 * band >= grid->n - 1 || (bins && !aligned(bins, 256)))
+        return MPM_ERR_INVALID;
+    if (!bins)
+        return hip_status(launch_pbmpm_grid_update(grid->dim, grid->n, grid_io, dg, band, nullptr, stream));
+    if (bins_bytes < fixed_prefix_bytes(grid))
+        return MPM_ERR_WORKSPACE;
+    mpm_ws_layout l;
+    make_layout(grid, 0, &l);
+    const RangesF none{ 0.0f, 0.0f, 0.0f };
+    const BinView v = bin_view(bins, l, make_stamp(grid, 0, none, true));
+    return hip_status(launch_pbmpm_grid_update(grid->dim, grid->n, grid_io, dg, band, &v, stream));
+}
+
+int mpm_pbmpm_integrate(const mpm_grid_desc *grid, const mpm_particles *particles, float dt, const float *gravity,
+                        uint32_t *status, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_desc(grid)) != MPM_OK || (rc = check_particles(grid, particles, true, false)) != MPM_OK)
+        return rc;
+    if (!gravity || !aligned(status, 4) || !(dt >= 0.0f))
+        return MPM_ERR_INVALID;
+    const float g3[3] = { gravity[0], gravity[1], grid->dim == 3 ? gravity[2] : 0.0f };
+    return hip_status(launch_pbmpm_integrate(grid->dim, grid->n, particles->n, particles->x, particles->v, dt, g3,
+                                             status, stream));
+}
+
 int mpm_g2p(const mpm_grid_desc *grid, const float *vg, const mpm_particles *particles, float dt, uint32_t *status,
             hipStream_t stream)
 {

@@ -314,6 +314,12 @@ hipError_t launch_neohookean_affine(int dim, int n, int64_t np, const float *F, 
 hipError_t launch_update_F(int dim, int64_t np, const float *C, float *F, float dt, hipStream_t s);
 hipError_t launch_g2p(int dim, int n, const float *vg, float *x, float *v, float *C, int64_t np, float dt,
                       uint32_t *status, hipStream_t s);
+hipError_t launch_pbmpm_project(int dim, int64_t np, const float *F, float *D, float relax, int polar_iters,
+                                uint32_t *status, hipStream_t s);
+hipError_t launch_pbmpm_grid_update(int dim, int n, int64_t *grid, float *dg, int band, const BinView *bins,
+                                    hipStream_t s);
+hipError_t launch_pbmpm_integrate(int dim, int n, int64_t np, float *x, float *d, float dt, const float *gravity,
+                                  uint32_t *status, hipStream_t s);
 
 int device_cu_count();
 

@@ -46,7 +46,13 @@ __global__ void __launch_bounds__(256) active_tiles_kernel(const uint32_t *__res
 // skipped.  OP 0 zeroes the nodes in every channel.  OP 1 is the grid update:
 // per node v_d = (float)((double)P_d / (double)M) then v_d += dt*g_d where
 // M != 0, v = 0 where M == 0 and within `sticky` nodes of a face; then
-// M = P = 0 (P is not read where the run's four M are all zero).
+// M = P = 0 (P is not read where the run's four M are all zero).  OP 2 is the
+// displacement-form update of the PB-MPM loop (the implementation page,
+// section 3.3.2: mass-normalise, then the guardian projects the node's
+// displaced position back into bounds): where M != 0, d_e = (float)((double)
+// P_e / (double)M), then with X = i_e dx, d_e = fminf(fmaxf(X + d_e, lo), hi)
+// - X, lo = band dx, hi = (n - 1 - band) dx (band passed as `sticky`); d = 0
+// where M == 0; then M = P = 0.
 template <int DIM, int OP>
 __global__ void __launch_bounds__(256) node_rows_kernel(int n, const uint8_t *__restrict__ active,
                                                         int64_t *__restrict__ grid, float *__restrict__ vg, float dt,
@@ -56,6 +62,8 @@ __global__ void __launch_bounds__(256) node_rows_kernel(int n, const uint8_t *__
     const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
     const int64_t runs = nodes / kTile;
     const float gdt[3] = { dt * g0, dt * g1, dt * g2 };
+    const float dxf = 1.0f / (float)n;
+    const float lo = (float)sticky * dxf, hi = (float)(n - 1 - sticky) * dxf;
     for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < runs; r += (int64_t)gridDim.x * blockDim.x) {
         const int64_t i0 = r * kTile;
         const int ix0 = (int)(i0 & (n - 1)), iy = (int)((i0 >> sh) & (n - 1));
@@ -90,8 +98,19 @@ __global__ void __launch_bounds__(256) node_rows_kernel(int n, const uint8_t *__
                 }
                 float v[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    v[k] = node_velocity(M[k], P[k], gdt[d], wall_row || ix0 + k < sticky || ix0 + k >= n - sticky);
+                for (int k = 0; k < 4; ++k) {
+                    if (OP == 1) {
+                        v[k] = node_velocity(M[k], P[k], gdt[d], wall_row || ix0 + k < sticky || ix0 + k >= n - sticky);
+                    } else {
+                        float dv = 0.0f;
+                        if (M[k] != 0) {
+                            dv = (float)((double)P[k] / (double)M[k]);
+                            const float X = (float)(d == 0 ? ix0 + k : (d == 1 ? iy : iz)) * dxf;
+                            dv = fminf(fmaxf(X + dv, lo), hi) - X;
+                        }
+                        v[k] = dv;
+                    }
+                }
                 *reinterpret_cast<float4 *>(vg + d * nodes + i0) = make_float4(v[0], v[1], v[2], v[3]);
                 Pq[0] = make_longlong2(0, 0);
                 Pq[1] = make_longlong2(0, 0);
@@ -196,6 +215,16 @@ hipError_t launch_grid_update(int dim, int n, int64_t *grid, float *vg, float dt
     if (bins)
         mark_active(dim, n, bins, s);
     node_rows<1>(dim, n, bins ? bins->tile_active : nullptr, grid, vg, dt, g, sticky, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_pbmpm_grid_update(int dim, int n, int64_t *grid, float *dg, int band, const BinView *bins,
+                                    hipStream_t s)
+{
+    const float g[3] = { 0.0f, 0.0f, 0.0f };
+    if (bins)
+        mark_active(dim, n, bins, s);
+    node_rows<2>(dim, n, bins ? bins->tile_active : nullptr, grid, dg, 0.0f, g, band, s);
     return hipGetLastError();
 }
 

@@ -1,0 +1,188 @@
+// pbmpm.hip -- the per-particle steps of the position-based MPM (PB-MPM)
+// iteration loop for an elastic material ("Implementation -- GPU
+// Optimization & Reference Codebases", section 3.3.2).
+//
+// A particle carries its displacement over the substep d (in the velocity
+// array) and its displacement gradient D (in the affine-matrix array, same
+// layout), with x, m and the deformation gradient F.  A substep is
+// `iterations` times { the elastic projection of D (this file), binning and
+// P2G of m and m (d + D (x_i - x_p)) (the APIC P2G with v := d, C := D; no
+// stress term), the displacement-form grid update (grid.hip, node_rows_kernel
+// OP 2) and the G2P gather of d and D (the G2P kernel with dt = 0, which
+// leaves x in place) }, then the integrate step (this file) and
+// F <- (I + D) F (stress.hip's F update with dt = 1).
+#include "common.hpp"
+
+namespace mpmk {
+namespace {
+
+// Cofactor matrix of the dim x dim matrix a (a^-T = cof / det); returns
+// det a = (a00 cof00 + a01 cof01) + a02 cof02 (2D: a00 a11 - a01 a10).
+template <int DIM>
+__device__ __forceinline__ double cofactor(const double (&a)[3][3], double (&cof)[3][3])
+{
+    if constexpr (DIM == 3) {
+        cof[0][0] = a[1][1] * a[2][2] - a[1][2] * a[2][1];
+        cof[0][1] = a[1][2] * a[2][0] - a[1][0] * a[2][2];
+        cof[0][2] = a[1][0] * a[2][1] - a[1][1] * a[2][0];
+        cof[1][0] = a[0][2] * a[2][1] - a[0][1] * a[2][2];
+        cof[1][1] = a[0][0] * a[2][2] - a[0][2] * a[2][0];
+        cof[1][2] = a[0][1] * a[2][0] - a[0][0] * a[2][1];
+        cof[2][0] = a[0][1] * a[1][2] - a[0][2] * a[1][1];
+        cof[2][1] = a[0][2] * a[1][0] - a[0][0] * a[1][2];
+        cof[2][2] = a[0][0] * a[1][1] - a[0][1] * a[1][0];
+        return (a[0][0] * cof[0][0] + a[0][1] * cof[0][1]) + a[0][2] * cof[0][2];
+    } else {
+        cof[0][0] = a[1][1];
+        cof[0][1] = -a[1][0];
+        cof[1][0] = -a[0][1];
+        cof[1][1] = a[0][0];
+        return a[0][0] * a[1][1] - a[0][1] * a[1][0];
+    }
+}
+
+// particleUpdate for an elastic material: the target shape is the polar
+// rotation R of the trial deformation Ft = (I + D) F (Newton's iteration
+// R <- (R + R^-T) / 2 from R = Ft, polar_iters steps); the displacement
+// gradient reaching it is D* = R F^-1 - I; D <- D + relax (D* - D).  Float64
+// in this order, D rounded to float32 once:
+//   Ft_de = sum_q ([d == q] + D_dq) F_qe                  (q ascending)
+//   R_de <- (R_de + cof(R)_de / det R) * 0.5
+//   F^-1_qe = cof(F)_eq / det F
+//   D*_de = (sum_q R_dq F^-1_qe) - [d == e]
+//   D_de <- D_de + relax * (D*_de - D_de)
+// A particle whose Ft or F (or a Newton iterate) has a non-positive
+// determinant keeps D and is counted in status[0].  One thread per particle.
+template <int DIM>
+__global__ void __launch_bounds__(256) pbmpm_project_kernel(int64_t np, const float *__restrict__ F,
+                                                            float *__restrict__ D, double relax, int polar_iters,
+                                                            uint32_t *__restrict__ status)
+{
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
+        double f[3][3] = {}, dd[3][3] = {}, ft[3][3] = {}, r[3][3] = {}, cof[3][3] = {};
+#pragma unroll
+        for (int d = 0; d < DIM; ++d)
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                f[d][e] = (double)F[(int64_t)(d * DIM + e) * np + p];
+                dd[d][e] = (double)D[(int64_t)(d * DIM + e) * np + p];
+            }
+#pragma unroll
+        for (int d = 0; d < DIM; ++d)
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                double t = ((d == 0 ? 1.0 : 0.0) + dd[d][0]) * f[0][e];
+#pragma unroll
+                for (int q = 1; q < DIM; ++q)
+                    t = t + ((d == q ? 1.0 : 0.0) + dd[d][q]) * f[q][e];
+                ft[d][e] = t;
+                r[d][e] = t;
+            }
+        bool ok = cofactor<DIM>(ft, cof) > 0.0;
+        for (int k = 0; k < polar_iters; ++k) {
+            if (!ok)
+                break;
+            const double det = cofactor<DIM>(r, cof);
+            if (!(det > 0.0)) {
+                ok = false;
+                break;
+            }
+#pragma unroll
+            for (int d = 0; d < DIM; ++d)
+#pragma unroll
+                for (int e = 0; e < DIM; ++e)
+                    r[d][e] = (r[d][e] + cof[d][e] / det) * 0.5;
+        }
+        const double detf = ok ? cofactor<DIM>(f, cof) : 0.0;
+        const bool counted = !ok || !(detf > 0.0);
+        wave_count(counted, &status[0]);
+        if (counted)
+            continue;
+        double finv[3][3];
+#pragma unroll
+        for (int q = 0; q < DIM; ++q)
+#pragma unroll
+            for (int e = 0; e < DIM; ++e)
+                finv[q][e] = cof[e][q] / detf;
+#pragma unroll
+        for (int d = 0; d < DIM; ++d)
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                double t = r[d][0] * finv[0][e];
+#pragma unroll
+                for (int q = 1; q < DIM; ++q)
+                    t = t + r[d][q] * finv[q][e];
+                const double dstar = t - (d == e ? 1.0 : 0.0);
+                D[(int64_t)(d * DIM + e) * np + p] = (float)(dd[d][e] + relax * (dstar - dd[d][e]));
+            }
+    }
+}
+
+// particleIntegrate for an elastic material, without the deformation update:
+// x_e <- x_e + d_e (float32) clamped to [lo, hi] = [dx, (n - 2) dx], clamped
+// particles counted in status[2]; then d_e <- d_e + gdt2_e (gravity into the
+// next substep's displacement, gdt2_e = g_e * (dt * dt) formed once on the
+// host in float32).
+template <int DIM>
+__global__ void __launch_bounds__(256) pbmpm_integrate_kernel(int64_t np, float *__restrict__ x,
+                                                              float *__restrict__ d, float lo, float hi, float gx,
+                                                              float gy, float gz, uint32_t *__restrict__ status)
+{
+    const float gdt2[3] = { gx, gy, gz };
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
+        bool clamped = false;
+#pragma unroll
+        for (int e = 0; e < DIM; ++e) {
+            const float de = d[(int64_t)e * np + p];
+            const float xa = x[(int64_t)e * np + p] + de;
+            const float xc = fminf(fmaxf(xa, lo), hi);
+            clamped = clamped || xc != xa;
+            x[(int64_t)e * np + p] = xc;
+            d[(int64_t)e * np + p] = de + gdt2[e];
+        }
+        wave_count(clamped, &status[2]);
+    }
+}
+
+int blocks_for(int64_t work, int block)
+{
+    const int64_t want = (work + block - 1) / block;
+    const int64_t cap = (int64_t)device_cu_count() * 16;
+    return (int)(want < 1 ? 1 : (want > cap ? cap : want));
+}
+
+}  // namespace
+
+hipError_t launch_pbmpm_project(int dim, int64_t np, const float *F, float *D, float relax, int polar_iters,
+                                uint32_t *status, hipStream_t s)
+{
+    if (np == 0)
+        return hipSuccess;
+    if (dim == 3)
+        hipLaunchKernelGGL(pbmpm_project_kernel<3>, dim3(blocks_for(np, 256)), dim3(256), 0, s, np, F, D,
+                           (double)relax, polar_iters, status);
+    else
+        hipLaunchKernelGGL(pbmpm_project_kernel<2>, dim3(blocks_for(np, 256)), dim3(256), 0, s, np, F, D,
+                           (double)relax, polar_iters, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_pbmpm_integrate(int dim, int n, int64_t np, float *x, float *d, float dt, const float *gravity,
+                                  uint32_t *status, hipStream_t s)
+{
+    if (np == 0)
+        return hipSuccess;
+    const float dx = 1.0f / (float)n;
+    float gdt2[3] = { 0.0f, 0.0f, 0.0f };
+    for (int e = 0; e < dim; ++e)
+        gdt2[e] = gravity[e] * (dt * dt);
+    if (dim == 3)
+        hipLaunchKernelGGL(pbmpm_integrate_kernel<3>, dim3(blocks_for(np, 256)), dim3(256), 0, s, np, x, d, dx,
+                           (float)(n - 2) * dx, gdt2[0], gdt2[1], gdt2[2], status);
+    else
+        hipLaunchKernelGGL(pbmpm_integrate_kernel<2>, dim3(blocks_for(np, 256)), dim3(256), 0, s, np, x, d, dx,
+                           (float)(n - 2) * dx, gdt2[0], gdt2[1], gdt2[2], status);
+    return hipGetLastError();
+}
+
+}  // namespace mpmk

@@ -161,3 +161,38 @@ class ResidentSubsteps:
     def gather(self) -> None:
         """Write the records' x, v, C back to the particle arrays."""
         L.mpm_gather_records(self.tr.desc, self.tr.ws, self.parts.desc(), self.tr.status)
+
+
+class PBMPMSubsteps:
+    """The position-based MPM (PB-MPM) substep of an elastic material
+    ("Implementation -- GPU Optimization & Reference Codebases", section
+    3.3.2) on ElasticParticles whose v holds the displacement d and whose C
+    holds the displacement gradient D: `iterations` times the elastic
+    projection, binning and P2G, the displacement-form grid update (into
+    tr.vg) and the G2P gather (dt = 0); then the integrate step and
+    F <- (I + D) F.  The records are re-binned every iteration, since d and D
+    change while x does not."""
+
+    def __init__(self, tr: Transfer, parts: ElasticParticles, dt: float, gravity, iterations: int = 5,
+                 relax: float = 1.5, polar_iters: int = 12, band: int = 2):
+        self.tr, self.parts = tr, parts
+        self.dt, self.gravity = dt, list(gravity)
+        self.iterations, self.relax, self.polar_iters, self.band = iterations, relax, polar_iters, band
+
+    def iteration(self) -> None:
+        tr, parts = self.tr, self.parts
+        L.mpm_pbmpm_project_elastic(tr.desc, parts.desc(), parts.F, self.relax, self.polar_iters, tr.status)
+        tr.bin(parts)
+        tr.p2g(parts, binned=True)
+        L.mpm_pbmpm_grid_update(tr.desc, tr.ws, tr.grid, tr.vg, self.band)
+        tr.g2p(parts, 0.0)
+
+    def integrate(self) -> None:
+        tr, parts = self.tr, self.parts
+        L.mpm_pbmpm_integrate(tr.desc, parts.desc(), self.dt, self.gravity, tr.status)
+        L.mpm_update_deformation(tr.desc, parts.desc(), parts.F, 1.0)
+
+    def substep(self) -> None:
+        for _ in range(self.iterations):
+            self.iteration()
+        self.integrate()

@@ -97,6 +97,22 @@ WORKLOADS = {
                "mu": 4.0e9, "lam": 4.0e9, "v0": (0.0, -3.0, 0.0)}),
     # Integer-split quadratic APIC transfer (exact conservation): integer
     # positions (2^-16 cell), masses, velocities and affine entries.
+    # PB-MPM (position-based MPM, elastic material): the jelly cubes, with the
+    # particle state in displacement form (d = v dt for the first substep,
+    # D = 0, F = I) and the iteration loop's parameters (the page's defaults: 5
+    # iterations, relaxation 1.5)
+    "pbmpm_jelly_3d_64": Workload(
+        name="pbmpm_jelly_3d_64", kind="pbmpm", dim=3, n=64, n_particles=8 * 16 ** 3, frac_bits=32,
+        placement="jelly", mass=1.0, v_sigma=0.05, c_sigma=0.0,
+        max_mass=1.0, max_speed=0.5, max_affine=4.0, seed=_seed(10),
+        extra={"dt": 2e-3, "gravity": (0.0, -9.8, 0.0), "band": 2, "iterations": 5, "relax": 1.5,
+               "polar_iters": 12, "substeps": 20, "v0": (0.0, -3.0, 0.0)}),
+    "pbmpm_jelly_3d_256": Workload(
+        name="pbmpm_jelly_3d_256", kind="pbmpm", dim=3, n=256, n_particles=8 * 100 ** 3, frac_bits=32,
+        placement="jelly", mass=1.0, v_sigma=0.05, c_sigma=0.0,
+        max_mass=1.0, max_speed=0.5, max_affine=4.0, seed=_seed(11),
+        extra={"dt": 1e-3, "gravity": (0.0, -9.8, 0.0), "band": 2, "iterations": 5, "relax": 1.5,
+               "polar_iters": 12, "substeps": 10, "v0": (0.0, -3.0, 0.0)}),
     "isplit_2d_64": Workload(
         name="isplit_2d_64", kind="isplit", dim=2, n=64, n_particles=3500, frac_bits=0,
         max_mass=1000, max_speed=1000, max_affine=1000, seed=_seed(8)),
@@ -142,4 +158,9 @@ def build(w: Workload) -> dict:
         out["vol"] = np.full(w.n_particles, dx ** 3 / 8.0, dtype=np.float32)
         out["F"] = np.ascontiguousarray(np.tile(np.eye(3, dtype=np.float32).reshape(9, 1), (1, w.n_particles)))
         out["v"] = np.ascontiguousarray(out["v"] + np.asarray(w.extra["v0"], np.float32)[:, None])
+    if w.kind == "pbmpm":
+        # displacement form: v holds the displacement over the first substep
+        # (velocity times dt), C the displacement gradient (zero at rest)
+        out["v"] = np.ascontiguousarray(out["v"] * np.float32(w.extra["dt"]))
+        out["C"] = np.zeros_like(out["C"])
     return out
