@@ -42,11 +42,19 @@ SLOW_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 FAST_PEAK_TOPS = 53.6
 
 
-# Lane operations the fixed-order transfer needs per particle and stencil node, however it is scheduled, by class:
-# fast: the product w*m*S, DIM sums for u, DIM momentum products; slow: 1 + DIM roundings, 1 + DIM widenings to
-# float64, and the 1 + DIM exact float64 sums of groups of four (three adds per four contributions).
-def alu_ops_per_node(dim: int) -> tuple[float, float]:
-    return 1 + dim + dim, 2 * (1 + dim) + 0.75 * (1 + dim)
+# Lane operations the fixed-order transfer needs per particle, however it is scheduled, by class, with every
+# product or sum that several stencil nodes share counted once.  Fast class (float32 multiply and add): per axis
+# 18 for the stencil (x*n, the -0.5, t = g - b, the three weight factors, squares and scalings, the three node
+# offsets and their scaling by dx); m*S and the weight prefix products (m S wx) wy ... (3 + 9 + 27 in 3D); per
+# velocity channel DIM products C_de r_e and the prefix sums of u (3 + 9 + 27); DIM momentum products per node.
+# Slow class: per axis floor and the base cell's conversion, and per node and channel one rounding, one widening
+# to float64 and three quarters of a float64 add (three adds per group of four contributions).
+def alu_ops_per_particle(dim: int) -> tuple[float, float]:
+    nodes = 3 ** dim
+    prefixes = sum(3 ** k for k in range(1, dim + 1))
+    fast = 18 * dim + (1 + prefixes) + dim * (3 * dim + prefixes) + dim * nodes
+    slow = 2 * dim + (2 + 0.75) * (1 + dim) * nodes
+    return fast, slow
 
 
 # Algorithmic bytes per P2G (the survey's per-unit figures): each particle's state (x, v, C, m) and its index
@@ -450,6 +458,8 @@ def parse():
     ap.add_argument("--workload", default="blobs_3d_256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="particles in the CPU-baseline sample (0: all)")
+    ap.add_argument("--no-shuffled", action="store_true",
+                    help="skip the headline step on the shuffled particle order (profiling runs)")
     ap.add_argument("--no-substep", action="store_true",
                     help="skip the full-substep measurement (binning, P2G, grid update, G2P) on the dam-break workload")
     ap.add_argument("--substeps", type=int, default=20, help="timed substeps of the full-substep measurement")
@@ -580,14 +590,26 @@ def main():
 
     # the same step on the same particles in a seeded shuffled order: binning
     # sees every chunk spread over the blobs' tiles instead of a few
-    from mpm_inputs import generators as G
-    perm = G.permutation(w.seed ^ 0x5F5F, 0x5EED, w.n_particles)
-    shuffled_host = {k: np.ascontiguousarray(v[..., perm]) for k, v in host.items()}
-    sh_total, sh_stage, sh_copies = run_steps(shuffled_host, args.steps, args.warmup, "timed (shuffled order)")
-    sh_meta = sh_copies[0][1].meta()
-    sh_runs, sh_keys = int(sh_meta[6]), int(sh_meta[7])
-    del sh_copies, shuffled_host
-    torch.cuda.empty_cache()
+    shuffled = None
+    if not args.no_shuffled:
+        from mpm_inputs import generators as G
+        perm = G.permutation(w.seed ^ 0x5F5F, 0x5EED, w.n_particles)
+        shuffled_host = {k: np.ascontiguousarray(v[..., perm]) for k, v in host.items()}
+        sh_total, sh_stage, sh_copies = run_steps(shuffled_host, args.steps, args.warmup, "timed (shuffled order)")
+        sh_meta = sh_copies[0][1].meta()
+        sh_runs, sh_keys = int(sh_meta[6]), int(sh_meta[7])
+        del sh_copies, shuffled_host
+        torch.cuda.empty_cache()
+        sh_ms = sh_total / args.steps
+        shuffled = {
+            "order": "the same particles in a seeded random order",
+            "ms_per_step": round(sh_ms, 4), "particles_per_s": round(w.n_particles / (sh_ms * 1e-3), 1),
+            "ratio_to_generator_order": round(sh_ms / ms_step, 4),
+            "binning_runs": sh_runs, "mean_run": round(binned / max(sh_runs, 1), 1),
+            "cell_keys_written": bool(sh_keys),
+            "stages_ms": {"reset": stage_stats(sh_stage[:, 0]), "binning": stage_stats(sh_stage[:, 1]),
+                          "p2g": stage_stats(sh_stage[:, 2])},
+        }
 
     copy = time_copy(torch)
     log(f"device copy: {copy['gbs']} GB/s (read + write)")
@@ -604,19 +626,17 @@ def main():
                 "copy_gbs": copy["gbs"], "frac_of_copy": round(p2g_gbs / copy["gbs"], 4),
                 "limiter": None if rec is None else rec.get("limiter")}
     # the same kernel against the vector-ALU issue rates of the instruction classes it needs
-    fast, slow = alu_ops_per_node(w.dim)
-    nodes = 3 ** w.dim
-    floor_s = binned * nodes * (fast / (FAST_PEAK_TOPS * 1e12) + slow / (SLOW_PEAK_TOPS * 1e12))
-    ops = (fast + slow) * nodes
+    fast, slow = alu_ops_per_particle(w.dim)
+    floor_s = binned * (fast / (FAST_PEAK_TOPS * 1e12) + slow / (SLOW_PEAK_TOPS * 1e12))
+    ops = fast + slow
     peak = ops * binned / floor_s / 1e12
     alu_tops = ops * binned / (p2g_ms * 1e-3) / 1e12
     alu = {"bound": "alu", "achieved": round(alu_tops, 2), "peak": round(peak, 2), "unit": "T lane-ops/s",
-           "frac": round(alu_tops / peak, 4), "ops_per_particle": {"fast": fast * nodes, "slow": slow * nodes},
+           "frac": round(alu_tops / peak, 4), "ops_per_particle": {"fast": fast, "slow": slow},
            "class_peaks_tops": {"fast": FAST_PEAK_TOPS, "slow": round(SLOW_PEAK_TOPS, 2)},
            "floor_ms": round(floor_s * 1e3, 4), "kernel": roofline["kernel"]}
 
     value = w.n_particles / (ms_step * 1e-3)
-    sh_ms = sh_total / args.steps
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -646,15 +666,7 @@ def main():
             "bin_bytes": int(bin_bytes), "p2g_bytes": int(p2g_bytes), "status": status,
             "binning_runs": runs, "mean_run": round(binned / max(runs, 1), 1), "cell_keys_written": bool(keys),
         },
-        "shuffled": {
-            "order": "the same particles in a seeded random order",
-            "ms_per_step": round(sh_ms, 4), "particles_per_s": round(w.n_particles / (sh_ms * 1e-3), 1),
-            "ratio_to_generator_order": round(sh_ms / ms_step, 4),
-            "binning_runs": sh_runs, "mean_run": round(binned / max(sh_runs, 1), 1),
-            "cell_keys_written": bool(sh_keys),
-            "stages_ms": {"reset": stage_stats(sh_stage[:, 0]), "binning": stage_stats(sh_stage[:, 1]),
-                          "p2g": stage_stats(sh_stage[:, 2])},
-        },
+        "shuffled": shuffled,
         "copy_reference": copy,
     }
 

@@ -20,13 +20,24 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
 
 
 def test_alu_operations_per_particle():
+    import itertools
+
     import bench
-    # per node, fast class: w*m*S, 3 sums for u, 3 momentum products; slow class: 4 roundings, 4 widenings,
-    # 3 float64 adds (three per four contributions and channel)
-    fast, slow = bench.alu_ops_per_node(3)
-    assert (fast * 27, slow * 27) == (189, 297)
-    fast2, slow2 = bench.alu_ops_per_node(2)
-    assert (fast2 * 9, slow2 * 9) == (45, pytest.approx(74.25))
+    # count the distinct subexpressions of the fixed-order transfer by enumerating them
+    for dim in (2, 3):
+        offs = range(3)
+        prefixes = {t for k in range(1, dim + 1) for t in itertools.product(offs, repeat=k)}
+        nodes = list(itertools.product(offs, repeat=dim))
+        weights = 18 * dim                                    # per-axis stencil setup
+        wms = 1 + len(prefixes)                               # m*S, then ((m S wx) wy) wz prefixes
+        u_products = {(e, a, o) for e in range(dim) for a in range(dim) for o in offs}   # C_ea * r_a[o]
+        u_sums = {(e, t) for e in range(dim) for t in prefixes}
+        momentum = dim * len(nodes)
+        fast, slow = bench.alu_ops_per_particle(dim)
+        assert fast == weights + wms + len(u_products) + len(u_sums) + momentum
+        per_value = 1 + 1 + 0.75                              # round, widen, 3/4 of a float64 add
+        assert slow == pytest.approx(2 * dim + per_value * (1 + dim) * len(nodes))
+    assert bench.alu_ops_per_particle(3) == (319, pytest.approx(303))
     # the slow class issues one 64-lane instruction per SIMD every 4 cycles
     assert bench.SLOW_PEAK_TOPS == pytest.approx(39.3216)
 
