@@ -539,7 +539,9 @@ void oracle_grid_update(int dim, int n, int64_t *grid, float *vg, float dt, cons
 }
 
 /*
- * APIC gather: v = sum w vg and B = sum (w vg) r^T over the stencil.  For each
+ * APIC gather: v = sum w vg and B = sum (w vg) r^T over the stencil (the
+ * definition; the grouping below regroups these same sums exactly and only
+ * fixes the float32 rounding order).  For each
  * particle, over its stencil nodes in lexicographic order (a outermost, then
  * b, then c), with w = (wx[a] * wy[b]) * wz[c]:
  *   wv_d        = w * vg_d(node)
