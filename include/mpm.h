@@ -255,8 +255,9 @@ int mpm_p2g_cic_split(int64_t n, const int32_t *X, const int32_t *m, const int32
  * on the host (MPM_ERR_OVERFLOW).
  * workspace == NULL: one thread per particle adds each share with a 64-bit
  * global atomic.  workspace != NULL (device, 256-byte aligned, at least
- * mpm_isplit_workspace_bytes): particle indices are counting-sorted into
- * 8^dim-cell tiles and each slice of up to 2048 particles of a tile
+ * mpm_isplit_workspace_bytes): the particles are counting-sorted into
+ * 8^dim-cell tiles (a 128-byte copy of each, in tile order, in the
+ * workspace) and each slice of up to 2048 particles of a tile
  * accumulates its 10^dim-node block on chip before one atomic per non-zero
  * node and channel.  Both give the same grid.  The workspace is scratch,
  * overwritten by each call; calls sharing one workspace must not overlap.
@@ -269,9 +270,9 @@ int mpm_p2g_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const i
                    const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed, int64_t max_affine,
                    void *workspace, size_t workspace_bytes, int64_t *grid_out, uint32_t *status, hipStream_t stream);
 
-/* Bytes of the static device scratch mpm_p2g_isplit_noalloc uses (64 MiB per
- * GPU, held from the library's load until the process ends). */
-#define MPM_ISPLIT_SCRATCH_BYTES (64u * 1024u * 1024u)
+/* Bytes of the static device scratch mpm_p2g_isplit_noalloc uses (256 MiB
+ * per GPU, held from the library's load until the process ends). */
+#define MPM_ISPLIT_SCRATCH_BYTES (256u * 1024u * 1024u)
 
 /* mpm_p2g_isplit's tiled path with its workspace taken from the library's
  * static device scratch instead of the caller's memory: for callers that
@@ -285,7 +286,7 @@ int mpm_p2g_isplit(int32_t dim, int32_t n, int64_t np, const int32_t *X, const i
  * or host threads without ordering) race and must not be issued.  Inputs
  * whose mpm_isplit_workspace_bytes(dim, n, np) exceeds
  * MPM_ISPLIT_SCRATCH_BYTES are refused with MPM_ERR_SCRATCH before any launch
- * (for example np up to about 8.3M particles on a 128^3 grid).  The first
+ * (for example np up to about 2M particles on a 128^3 grid).  The first
  * call on a device looks up that device's copy of the scratch once.
  * Errors: those of mpm_p2g_isplit, MPM_ERR_SCRATCH. */
 int mpm_p2g_isplit_noalloc(int32_t dim, int32_t n, int64_t np, const int32_t *X, const int64_t *m, const int64_t *v,
@@ -294,7 +295,7 @@ int mpm_p2g_isplit_noalloc(int32_t dim, int32_t n, int64_t np, const int32_t *X,
 
 /* Bytes of the workspace mpm_p2g_isplit's tiled path needs for np particles
  * on n^dim nodes (tile counts and starts, each visited particle's rank and
- * the tile-ordered particle indices).  Host only.
+ * its 128-byte tile-ordered record).  Host only.
  * Errors: MPM_ERR_INVALID. */
 int mpm_isplit_workspace_bytes(int32_t dim, int32_t n, int64_t np, size_t *bytes);
 

@@ -22,7 +22,7 @@ MPM_ERR_WORKSPACE = -4
 MPM_ERR_HIP = -6
 MPM_ERR_SCRATCH = -7
 # bytes of the static device scratch of mpm_p2g_isplit_noalloc (include/mpm.h)
-MPM_ISPLIT_SCRATCH_BYTES = 64 * 1024 * 1024
+MPM_ISPLIT_SCRATCH_BYTES = 256 * 1024 * 1024
 
 
 class MpmError(RuntimeError):

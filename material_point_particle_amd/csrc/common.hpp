@@ -291,7 +291,7 @@ hipError_t launch_p2g_isplit(int dim, int n, int64_t np, const int32_t *X, const
                              const int64_t *C, const uint32_t *order, int64_t max_mass, int64_t max_speed,
                              int64_t max_affine, int64_t *grid, uint32_t *status, hipStream_t s);
 struct IsplitLayout {      // byte offsets into the integer-split workspace
-    size_t count, start, partial, meta, rank, perm, total;
+    size_t count, start, partial, meta, rank, rec, total;
     int64_t tiles_x, tiles, entries, scan_blocks;
     int slot_shift;       // 2^slot_shift counters per tile
 };

@@ -30,7 +30,8 @@
 //  - direct: one thread per particle; its 3^dim shares of one channel are
 //    formed in registers and added with one 64-bit global atomic each
 //    (27 x 4 random atomics per particle in 3D);
-//  - tiled: a counting sort of particle indices into 8^dim-cell tiles, then
+//  - tiled: a counting sort of the particles into 8^dim-cell tiles, each
+//    visited particle copied into a 128-byte record in tile order, then
 //    one workgroup per slice of a tile accumulates the tile's 10^dim-node
 //    block on chip with 64-bit LDS atomics and flushes it with one global
 //    atomic per non-zero node and channel, consecutive lanes on consecutive
@@ -266,6 +267,19 @@ __global__ void __launch_bounds__(256) isplit_kernel(int64_t np, int n, const in
 // ---------------------------------------------------------------------------
 // Tiled path.
 // ---------------------------------------------------------------------------
+// A particle's tile-ordered copy: position and quantities in one 128-byte
+// record (one cache line), written by the scatter in tile order so that the
+// accumulating kernel streams whole lines instead of gathering 4 to 8 bytes
+// from each of the caller's 16 arrays per particle.
+struct __align__(16) IsRecord {
+    int32_t X[4];          // X[DIM..3] unused
+    int64_t m;
+    int64_t v[3];          // v[DIM..2] unused
+    int64_t C[9];          // (d, e) at d * DIM + e
+    int64_t pad;
+};
+static_assert(sizeof(IsRecord) == 128, "one record per 128-byte line");
+
 constexpr int kIsTile = 8;                 // cells per tile edge
 constexpr int kIsBlock = kIsTile + 2;      // nodes per block edge: bases t0..t0+7 reach t0..t0+9
 constexpr int kIsChunk = 2048;             // particles per work item
@@ -434,13 +448,17 @@ __global__ void __launch_bounds__(kIsThreads) is_scan_final_kernel(const uint32_
     }
 }
 
+// Each visited particle's record goes to its tile's range at its rank.
 template <int DIM>
 __global__ void __launch_bounds__(256) is_scatter_kernel(int64_t np, int n, int64_t tx, int sshift,
                                                          const int32_t *__restrict__ X,
+                                                         const int64_t *__restrict__ m,
+                                                         const int64_t *__restrict__ v,
+                                                         const int64_t *__restrict__ C,
                                                          const uint32_t *__restrict__ order,
                                                          const uint32_t *__restrict__ rank,
                                                          const uint64_t *__restrict__ start,
-                                                         uint32_t *__restrict__ perm)
+                                                         IsRecord *__restrict__ rec)
 {
     for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < np; k += (int64_t)gridDim.x * blockDim.x) {
         const uint32_t r = rank[k];
@@ -451,7 +469,23 @@ __global__ void __launch_bounds__(256) is_scatter_kernel(int64_t np, int n, int6
         AxisCoef ax[DIM];
         stencil<DIM>(X, np, p, n, base, ax);
         const int64_t e = (tile_of<DIM>(base, tx) << sshift) | ((k >> 8) & ((1ll << sshift) - 1));
-        perm[(start[e] & 0xFFFFFFFFull) + r] = (uint32_t)p;
+        IsRecord q;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            q.X[d] = d < DIM ? X[(int64_t)d * np + p] : 0;
+        q.m = m[p];
+#pragma unroll
+        for (int d = 0; d < 3; ++d)
+            q.v[d] = d < DIM ? v[(int64_t)d * np + p] : 0;
+#pragma unroll
+        for (int i = 0; i < 9; ++i)
+            q.C[i] = i < DIM * DIM ? C[(int64_t)i * np + p] : 0;
+        q.pad = 0;
+        const uint4 *src = reinterpret_cast<const uint4 *>(&q);
+        uint4 *dst = reinterpret_cast<uint4 *>(rec + (int64_t)(start[e] & 0xFFFFFFFFull) + r);
+#pragma unroll
+        for (int w = 0; w < 8; ++w)
+            dst[w] = src[w];
     }
 }
 
@@ -474,13 +508,9 @@ __device__ __forceinline__ int64_t item_tile(const uint64_t *__restrict__ start,
 
 template <int DIM, bool NARROW>
 __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n, int64_t tx, int64_t tiles, int sshift,
-                                                              const int32_t *__restrict__ X,
-                                                              const int64_t *__restrict__ m,
-                                                              const int64_t *__restrict__ v,
-                                                              const int64_t *__restrict__ C,
+                                                              const IsRecord *__restrict__ rec,
                                                               const uint32_t *__restrict__ count,
                                                               const uint64_t *__restrict__ start,
-                                                              const uint32_t *__restrict__ perm,
                                                               const uint64_t *__restrict__ meta, int64_t max_mass,
                                                               int64_t max_speed, int64_t max_affine,
                                                               int64_t *__restrict__ grid,
@@ -511,12 +541,35 @@ __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n,
             block[e] = 0ull;
         __syncthreads();
         for (int64_t j = lo + threadIdx.x; j < hi; j += kIsThreads) {
-            const int64_t p = perm[j];
+            IsRecord q;
+            {
+                const uint4 *src = reinterpret_cast<const uint4 *>(rec + j);
+                uint4 *dst = reinterpret_cast<uint4 *>(&q);
+#pragma unroll
+                for (int w = 0; w < 8; ++w)
+                    dst[w] = src[w];
+            }
             int64_t base[DIM];
             AxisCoef ax[DIM];
-            stencil<DIM>(X, np, p, n, base, ax);
-            int64_t mp, vp[DIM], cp[DIM][DIM];
-            const bool in_range = load_quantities<DIM>(m, v, C, np, p, max_mass, max_speed, max_affine, mp, vp, cp);
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                const int64_t x = q.X[e];
+                base[e] = (x - 32768) >> 16;
+                ax[e] = axis_coef(x - (base[e] << 16));
+            }
+            const int64_t mp = q.m;
+            int64_t vp[DIM], cp[DIM][DIM];
+            bool in_range = mp >= -max_mass && mp <= max_mass;
+#pragma unroll
+            for (int d = 0; d < DIM; ++d) {
+                vp[d] = q.v[d];
+                in_range &= vp[d] >= -max_speed && vp[d] <= max_speed;
+#pragma unroll
+                for (int e = 0; e < DIM; ++e) {
+                    cp[d][e] = q.C[d * DIM + e];
+                    in_range &= cp[d][e] >= -max_affine && cp[d][e] <= max_affine;
+                }
+            }
             wave_count(!in_range, &status[1]);
             if (!in_range)
                 continue;
@@ -621,7 +674,7 @@ IsplitLayout isplit_layout(int dim, int n, int64_t np)
     l.partial = take(sizeof(uint64_t) * (size_t)l.scan_blocks);
     l.meta = take(sizeof(uint64_t) * 2);
     l.rank = take(sizeof(uint32_t) * (size_t)(np > 0 ? np : 1));
-    l.perm = take(sizeof(uint32_t) * (size_t)(np > 0 ? np : 1));
+    l.rec = take(sizeof(IsRecord) * (size_t)(np > 0 ? np : 1));
     l.total = off;
     return l;
 }
@@ -639,7 +692,7 @@ hipError_t launch_p2g_isplit_tiled(int dim, int n, int64_t np, const int32_t *X,
     uint64_t *partial = reinterpret_cast<uint64_t *>(w + l.partial);
     uint64_t *meta = reinterpret_cast<uint64_t *>(w + l.meta);
     uint32_t *rank = reinterpret_cast<uint32_t *>(w + l.rank);
-    uint32_t *perm = reinterpret_cast<uint32_t *>(w + l.perm);
+    IsRecord *rec = reinterpret_cast<IsRecord *>(w + l.rec);
     const dim3 blk(kIsThreads);
     const int sh = l.slot_shift;
     hipLaunchKernelGGL(is_zero_kernel, dim3((unsigned)is_blocks(l.entries, 16)), blk, 0, s, count, l.entries);
@@ -656,24 +709,24 @@ hipError_t launch_p2g_isplit_tiled(int dim, int n, int64_t np, const int32_t *X,
     hipLaunchKernelGGL(is_scan_final_kernel, dim3((unsigned)l.scan_blocks), blk, 0, s, count, l.entries, sh, partial,
                        start);
     if (dim == 3)
-        hipLaunchKernelGGL(is_scatter_kernel<3>, dim3(pb), blk, 0, s, np, n, l.tiles_x, sh, X, order, rank, start,
-                           perm);
+        hipLaunchKernelGGL(is_scatter_kernel<3>, dim3(pb), blk, 0, s, np, n, l.tiles_x, sh, X, m, v, C, order, rank,
+                           start, rec);
     else
-        hipLaunchKernelGGL(is_scatter_kernel<2>, dim3(pb), blk, 0, s, np, n, l.tiles_x, sh, X, order, rank, start,
-                           perm);
+        hipLaunchKernelGGL(is_scatter_kernel<2>, dim3(pb), blk, 0, s, np, n, l.tiles_x, sh, X, m, v, C, order, rank,
+                           start, rec);
     // items <= tiles + np / kIsChunk; persistent workgroups stride over them
     const int64_t max_items = l.tiles + np / kIsChunk + 1;
     const int64_t cap = (int64_t)device_cu_count() * 4;
     const unsigned tb = (unsigned)(max_items < cap ? max_items : cap);
 if (dim == 3)
         pick_width<3>(max_mass, max_speed, max_affine, [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3(tb), blk, 0, s, np, n, l.tiles_x, l.tiles, sh, X, m, v, C, count, start,
-                               perm, meta, max_mass, max_speed, max_affine, grid, status);
+            hipLaunchKernelGGL(kern, dim3(tb), blk, 0, s, np, n, l.tiles_x, l.tiles, sh, rec, count, start, meta,
+                               max_mass, max_speed, max_affine, grid, status);
         }, is_tiled_kernel<3, true>, is_tiled_kernel<3, false>);
     else
         pick_width<2>(max_mass, max_speed, max_affine, [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3(tb), blk, 0, s, np, n, l.tiles_x, l.tiles, sh, X, m, v, C, count, start,
-                               perm, meta, max_mass, max_speed, max_affine, grid, status);
+            hipLaunchKernelGGL(kern, dim3(tb), blk, 0, s, np, n, l.tiles_x, l.tiles, sh, rec, count, start, meta,
+                               max_mass, max_speed, max_affine, grid, status);
         }, is_tiled_kernel<2, true>, is_tiled_kernel<2, false>);
     return hipGetLastError();
 }

@@ -87,8 +87,8 @@ def test_workspace_layout_is_disjoint_and_aligned():
 
 def test_isplit_workspace_size():
     # tile counters and starts (8^dim-cell tiles over the n - 2 base nodes per
-    # axis; up to 8 counters per tile, at most 2^22 in all), plus a rank and an
-    # index per visited particle, in 256-byte sections
+    # axis; up to 8 counters per tile, at most 2^22 in all), plus a rank and a
+    # 128-byte record per visited particle, in 256-byte sections
     def r(b):
         return (b + 255) // 256 * 256
     for dim, n, N in [(3, 128, 1 << 20), (2, 64, 3500), (3, 10, 1), (2, 2048, 0), (3, 1024, 5), (2, 32767, 7)]:
@@ -98,7 +98,7 @@ def test_isplit_workspace_size():
             slots //= 2
         e = t * slots
         blocks = (e + 1023) // 1024
-        want = r(4 * e) + r(8 * e) + r(8 * blocks) + r(16) + 2 * r(4 * max(N, 1))
+        want = r(4 * e) + r(8 * e) + r(8 * blocks) + r(16) + r(4 * max(N, 1)) + r(128 * max(N, 1))
         assert M.mpm_isplit_workspace_bytes(dim, n, N) == want
     with pytest.raises(M.MpmError):
         M.mpm_isplit_workspace_bytes(3, 2, 10)
@@ -237,5 +237,6 @@ def test_noalloc_isplit_refuses_inputs_past_its_static_scratch():
                                       None) == L.MPM_ERR_OVERFLOW
     assert lib.mpm_p2g_isplit_noalloc(4, 128, 10, fake, fake, fake, fake, None, 1, 1, 1, fake, fake,
                                       None) == L.MPM_ERR_INVALID
-    # the largest 3D workload that fits: about 8.3M particles on 128^3
-    assert M.mpm_isplit_workspace_bytes(3, 128, 8_300_000) <= L.MPM_ISPLIT_SCRATCH_BYTES
+    # the largest 3D workload that fits: about 2M particles (132 bytes each) on 128^3
+    assert M.mpm_isplit_workspace_bytes(3, 128, 2_000_000) <= L.MPM_ISPLIT_SCRATCH_BYTES
+    assert M.mpm_isplit_workspace_bytes(3, 128, 2_100_000) > L.MPM_ISPLIT_SCRATCH_BYTES

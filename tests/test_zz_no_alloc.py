@@ -94,7 +94,7 @@ def test_empty_call_and_size_refusal(mpm):
     mpm.mpm_p2g_isplit_noalloc(2, 8, e32, e64, e64, e64, None, 1, 1, 1, g, st)
     torch.cuda.synchronize()
     assert int(g.abs().sum().item()) == 0
-    # 2^24 particles on 128^3 needs more than the 64 MiB scratch: refused
+    # 2^24 particles on 128^3 needs more than the 256 MiB scratch: refused
     np_ = 1 << 24
     assert mpm.mpm_isplit_workspace_bytes(3, 128, np_) > L.MPM_ISPLIT_SCRATCH_BYTES
     # (inputs and grid sized as a real call of this shape would be)
