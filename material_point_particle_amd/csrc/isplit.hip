@@ -37,6 +37,7 @@
 //    atomic per non-zero node and channel, consecutive lanes on consecutive
 //    x nodes.
 #include <mutex>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -70,45 +71,88 @@ __device__ __forceinline__ int64_t round_shift(__int128 t)
     return fl + (int64_t)((r > half) | ((r == half) & ((uint64_t)fl & 1ull)));
 }
 
-// round-half-even(q c / 2^K) for |q| < 2^31, |c| < 2^49 and 31 < K < 50,
-// with c = c_hi 2^31 + c_lo (0 <= c_lo < 2^31): two signed 32 x 32 -> 64-bit
-// multiply-adds.  u = q c_lo + 2^(K-1) and w = q c_hi + floor(u / 2^31) give
-// q c + 2^(K-1) = 2^31 w + (u mod 2^31), so floor((q c + 2^(K-1)) / 2^K) =
-// floor(w / 2^(K-31)) (round half up); on an exact tie (both remainders zero)
-// an odd result steps down to the even neighbour.
-template <int K>
-__device__ __forceinline__ int64_t mul_round_narrow(int32_t q, int64_t c)
+// A split coefficient as two signed 32-bit words: c = hi 2^32 + lo with lo in
+// [-2^31, 2^31) (the low word read as signed, hi taking the rest).  For the
+// weights (0 <= c <= 2^32) hi is 0 or 1 and is kept as the mask -hi.
+struct NarrowCoef {
+    int32_t hi, lo;
+};
+
+template <bool WEIGHT>
+__device__ __forceinline__ NarrowCoef narrow_coef(int64_t c)
 {
-    const int32_t c_lo = (int32_t)(c & 0x7FFFFFFFll), c_hi = (int32_t)(c >> 31);
-    // the offset's value is hidden from the optimiser: with it known, the
-    // remainder test below is rewritten as a separate low-word multiply
-    int64_t half = 1ll << (K - 1);
-    asm("" : "+s"(half));
-    const int64_t u = (int64_t)q * c_lo + half;
-    const int64_t w = (int64_t)q * c_hi + (u >> 31);
-    const int64_t r = w >> (K - 31);
-    const int64_t tie = (int64_t)(((w & ((1ll << (K - 31)) - 1)) == 0) & ((u & 0x7FFFFFFFll) == 0));
-    return r - (tie & r & 1);
+    int32_t lo = (int32_t)(uint32_t)(uint64_t)c;
+    int32_t hi = (int32_t)((c - (int64_t)lo) >> 32);
+    if constexpr (WEIGHT)
+        hi = -hi;
+    // the signs the optimiser could prove (a square is non-negative) are
+    // hidden, so that each product stays one signed 32 x 32 -> 64-bit
+    // multiply-add instead of an unsigned one with sign corrections
+    asm("" : "+v"(lo), "+v"(hi));
+    return NarrowCoef{ hi, lo };
 }
 
-// Split q along one axis: KIND 0 with the weights, KIND 1 with the first
-// moments.  NARROW: |q| < 2^31 (guaranteed by the declared ranges), products
-// from two 32-bit multiply-adds; otherwise full 128-bit products.
-template <int KIND, bool NARROW>
+struct NarrowAxis {
+    NarrowCoef w0, w2, u0, u2;
+};
+
+__device__ __forceinline__ NarrowAxis narrow_axis(const AxisCoef &c)
+{
+    return NarrowAxis{ narrow_coef<true>(c.w0), narrow_coef<true>(c.w2), narrow_coef<false>(c.u0),
+                       narrow_coef<false>(c.u2) };
+}
+
+// round-half-even(q c / 2^K) for |q| < 2^29, |c| < 2^49 and K = 33 (the
+// weights, 0 <= c <= 2^32) or 49 (the first moments), as a 32-bit result:
+// u = q lo + 2^(K-1) (a signed 32 x 32 -> 64-bit multiply-add) and
+// V = q hi + floor(u / 2^32) give q c + 2^(K-1) = 2^32 V + (u mod 2^32), so
+// the quotient rounded half up is floor(V / 2^(K-32)); the sum is an exact
+// tie when u mod 2^32 and V mod 2^(K-32) are both zero, and then an odd
+// quotient steps down to the even neighbour (its lowest bit cleared).  For
+// K = 33, |V| <= 2^29 + 1 and q hi is q or 0, so V takes two 32-bit
+// operations; for K = 49 it is a second multiply-add.
+template <int K>
+__device__ __forceinline__ int32_t round_share(int32_t q, NarrowCoef c)
+{
+    // the offset's value is hidden from the optimiser: with it known, the
+    // tie test below is rewritten as a separate low-word multiply
+    int64_t half = 1ll << (K - 1);
+    asm("" : "+s"(half));
+    const int64_t u = (int64_t)q * c.lo + half;
+    const uint32_t u_lo = (uint32_t)(uint64_t)u;
+    if constexpr (K == 33) {
+        const int32_t V = (q & c.hi) + (int32_t)(u >> 32);
+        const int32_t r = V >> 1;
+        return (((uint32_t)V & 1u) | u_lo) == 0u ? (r & ~1) : r;
+    } else {
+        const int64_t V = (int64_t)q * c.hi + (u >> 32);
+        const int32_t r = (int32_t)(V >> (K - 32));
+        const uint32_t rem = ((uint32_t)(uint64_t)V & ((1u << (K - 32)) - 1u)) | u_lo;
+        return rem == 0u ? (r & ~1) : r;
+    }
+}
+
+// The one-axis split of the narrow path: q and its shares in 32 bits.
+template <int KIND>
+__device__ __forceinline__ void split_narrow(int32_t q, const NarrowAxis &c, int32_t s[3])
+{
+    if constexpr (KIND == 0) {
+        s[0] = round_share<33>(q, c.w0);
+        s[2] = round_share<33>(q, c.w2);
+        s[1] = q - (s[0] + s[2]);
+    } else {
+        s[0] = round_share<49>(q, c.u0);
+        s[2] = round_share<49>(q, c.u2);
+        s[1] = -(s[0] + s[2]);
+    }
+}
+
+// Split q along one axis (the wide path): KIND 0 with the weights, KIND 1
+// with the first moments; the products formed exactly in 128 bits.
+template <int KIND>
 __device__ __forceinline__ void split1(int64_t q, const AxisCoef &c, int64_t s[3])
 {
-    if constexpr (NARROW) {
-        const int32_t q32 = (int32_t)q;
-        if constexpr (KIND == 0) {
-            s[0] = mul_round_narrow<33>(q32, c.w0);
-            s[2] = mul_round_narrow<33>(q32, c.w2);
-            s[1] = q - s[0] - s[2];
-        } else {
-            s[0] = mul_round_narrow<49>(q32, c.u0);
-            s[2] = mul_round_narrow<49>(q32, c.u2);
-            s[1] = -s[0] - s[2];
-        }
-    } else if constexpr (KIND == 0) {
+    if constexpr (KIND == 0) {
         s[0] = round_shift<33>((__int128)q * c.w0);
         s[2] = round_shift<33>((__int128)q * c.w2);
         s[1] = q - s[0] - s[2];
@@ -120,21 +164,31 @@ __device__ __forceinline__ void split1(int64_t q, const AxisCoef &c, int64_t s[3
 }
 
 // acc[(a * 3 + b) * 3 + c] (2D: acc[a * 3 + b]) += the tensor split of q,
-// along x with KX, then y with KY, then z with KZ.
-template <int DIM, bool NARROW, int KX, int KY, int KZ>
-__device__ __forceinline__ void tensor_add(int64_t q, const AxisCoef (&ax)[DIM], int64_t (&acc)[DIM == 3 ? 27 : 9])
+// along x with KX, then y with KY, then z with KZ: 64-bit values with
+// 128-bit products (Axis = AxisCoef) or 32-bit values (Axis = NarrowAxis).
+template <int KIND, class T, class Axis>
+__device__ __forceinline__ void split_any(T q, const Axis &c, T s[3])
 {
-    int64_t sx[3];
-    split1<KX, NARROW>(q, ax[0], sx);
+    if constexpr (sizeof(T) == 4)
+        split_narrow<KIND>(q, c, s);
+    else
+        split1<KIND>(q, c, s);
+}
+
+template <int DIM, int KX, int KY, int KZ, class T, class Axis>
+__device__ __forceinline__ void tensor_add(T q, const Axis (&ax)[DIM], T (&acc)[DIM == 3 ? 27 : 9])
+{
+    T sx[3];
+    split_any<KX>(q, ax[0], sx);
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
-        int64_t sy[3];
-        split1<KY, NARROW>(sx[a], ax[1], sy);
+        T sy[3];
+        split_any<KY>(sx[a], ax[1], sy);
 #pragma unroll
         for (int b = 0; b < 3; ++b) {
             if constexpr (DIM == 3) {
-                int64_t sz[3];
-                split1<KZ, NARROW>(sy[b], ax[2], sz);
+                T sz[3];
+                split_any<KZ>(sy[b], ax[2], sz);
 #pragma unroll
                 for (int c = 0; c < 3; ++c)
                     acc[(a * 3 + b) * 3 + c] += sz[c];
@@ -145,8 +199,8 @@ __device__ __forceinline__ void tensor_add(int64_t q, const AxisCoef (&ax)[DIM],
     }
 }
 
-template <int DIM>
-__device__ __forceinline__ void flush(int64_t *g, const int64_t (&acc)[DIM == 3 ? 27 : 9], const int64_t (&base)[DIM],
+template <int DIM, class T>
+__device__ __forceinline__ void flush(int64_t *g, const T (&acc)[DIM == 3 ? 27 : 9], const int64_t (&base)[DIM],
                                       int64_t n)
 {
 #pragma unroll
@@ -155,7 +209,8 @@ __device__ __forceinline__ void flush(int64_t *g, const int64_t (&acc)[DIM == 3 
         for (int b = 0; b < 3; ++b)
 #pragma unroll
             for (int c = 0; c < (DIM == 3 ? 3 : 1); ++c) {
-                int64_t node, s;
+                int64_t node;
+                T s;
                 if constexpr (DIM == 3) {
                     node = ((base[2] + c) * n + (base[1] + b)) * n + (base[0] + a);
                     s = acc[(a * 3 + b) * 3 + c];
@@ -164,7 +219,7 @@ __device__ __forceinline__ void flush(int64_t *g, const int64_t (&acc)[DIM == 3 
                     s = acc[a * 3 + b];
                 }
                 if (s != 0)
-                    atomicAdd(reinterpret_cast<unsigned long long *>(&g[node]), (unsigned long long)s);
+                    atomicAdd(reinterpret_cast<unsigned long long *>(&g[node]), (unsigned long long)(int64_t)s);
             }
 }
 
@@ -208,28 +263,41 @@ __device__ __forceinline__ bool load_quantities(const int64_t *__restrict__ m, c
 }
 
 // All channels of one particle: sink(channel, acc) receives the 3^dim shares
-// of each channel in turn.
+// of each channel in turn.  NARROW: every quantity m, m v_d, m C_de is below
+// 2^28 in magnitude (the declared ranges guarantee it), so every share and
+// every node's sum of up to four tensors' shares fits in 32 bits.
 template <int DIM, bool NARROW, class Sink>
 __device__ __forceinline__ void particle_shares(const AxisCoef (&ax)[DIM], int64_t mp, const int64_t (&vp)[DIM],
                                                 const int64_t (&cp)[DIM][DIM], Sink &&sink)
 {
     constexpr int K = DIM == 3 ? 27 : 9;
-    int64_t acc[K];
+    using T = typename std::conditional<NARROW, int32_t, int64_t>::type;
+    using Axis = typename std::conditional<NARROW, NarrowAxis, AxisCoef>::type;
+    Axis c[DIM];
+#pragma unroll
+    for (int e = 0; e < DIM; ++e) {
+        if constexpr (NARROW)
+            c[e] = narrow_axis(ax[e]);
+        else
+            c[e] = ax[e];
+    }
+    T acc[K];
 #pragma unroll
     for (int i = 0; i < K; ++i)
         acc[i] = 0;
-    tensor_add<DIM, NARROW, 0, 0, 0>(mp, ax, acc);
+    tensor_add<DIM, 0, 0, 0>((T)mp, c, acc);
     sink(0, acc);
 #pragma unroll 1
     for (int d = 0; d < DIM; ++d) {
 #pragma unroll
         for (int i = 0; i < K; ++i)
             acc[i] = 0;
-        tensor_add<DIM, NARROW, 0, 0, 0>(mp * vp[d], ax, acc);
-        tensor_add<DIM, NARROW, 1, 0, 0>(mp * cp[d][0], ax, acc);
-        tensor_add<DIM, NARROW, 0, 1, 0>(mp * cp[d][1], ax, acc);
+        // (narrow: the products are below 2^28, so 32-bit multiplies are exact)
+        tensor_add<DIM, 0, 0, 0>((T)mp * (T)vp[d], c, acc);
+        tensor_add<DIM, 1, 0, 0>((T)mp * (T)cp[d][0], c, acc);
+        tensor_add<DIM, 0, 1, 0>((T)mp * (T)cp[d][1], c, acc);
         if constexpr (DIM == 3)
-            tensor_add<DIM, NARROW, 0, 0, 1>(mp * cp[d][2], ax, acc);
+            tensor_add<DIM, 0, 0, 1>((T)mp * (T)cp[d][2], c, acc);
         sink(1 + d, acc);
     }
 }
@@ -258,7 +326,7 @@ __global__ void __launch_bounds__(256) isplit_kernel(int64_t np, int n, const in
         wave_count(inside && !in_range, &status[1]);
         if (!inside || !in_range)
             continue;
-        particle_shares<DIM, NARROW>(ax, mp, vp, cp, [&](int ch, const int64_t(&acc)[DIM == 3 ? 27 : 9]) {
+        particle_shares<DIM, NARROW>(ax, mp, vp, cp, [&](int ch, const auto &acc) {
             flush<DIM>(grid + ch * nodes, acc, base, n);
         });
     }
@@ -577,7 +645,7 @@ __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n,
 #pragma unroll
             for (int e = 0; e < DIM; ++e)
                 lb[e] = (int)(base[e] - origin[e]);
-            particle_shares<DIM, NARROW>(ax, mp, vp, cp, [&](int ch, const int64_t(&acc)[DIM == 3 ? 27 : 9]) {
+            particle_shares<DIM, NARROW>(ax, mp, vp, cp, [&](int ch, const auto &acc) {
 #pragma unroll
                 for (int a = 0; a < 3; ++a)
 #pragma unroll
@@ -585,7 +653,7 @@ __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n,
 #pragma unroll
                         for (int c = 0; c < (DIM == 3 ? 3 : 1); ++c) {
                             int idx;
-                            int64_t sh;
+                            int64_t sh;      // a 32-bit share widened with its sign
                             if constexpr (DIM == 3) {
                                 idx = ((ch * B + lb[2] + c) * B + lb[1] + b) * B + lb[0] + a;
                                 sh = acc[(a * 3 + b) * 3 + c];
@@ -626,17 +694,22 @@ __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n,
     }
 }
 
-// Narrow splits need every split quantity below 2^31 in magnitude: the first
-// splits take m, m v_d and m C_de, and each split's shares exceed its
-// quantity by at most one, so max_mass * max(1, max_speed, max_affine) + 3
-// below 2^31 suffices (particles beyond the declared ranges are skipped).
+// The narrow path needs every split quantity m, m v_d, m C_de below 2^28 in
+// magnitude: max_mass * max(1, max_speed, max_affine) < 2^28 (particles
+// beyond the declared ranges are skipped).  A share of q is then at most
+// 1.25 |q| + 3 in magnitude (a first-moment split's outer shares are at most
+// 3/4 and 1/2 of q, rounded, the middle one their negated sum; a weight
+// split's shares at most q + 1 each), and a node's sum over the four tensors
+// of a momentum channel at most 4.75 * 2^28 + 12 < 2^31: 32-bit values and
+// sums throughout, and products of 29 by 49 bits in two 32 x 32 -> 64-bit
+// multiply-adds.
 template <int DIM, class Launch, class K>
 void pick_width(int64_t max_mass, int64_t max_speed, int64_t max_affine, Launch &&launch, K narrow, K wide)
 {
     int64_t f = max_speed > max_affine ? max_speed : max_affine;
     f = f > 1 ? f : 1;
-    const __int128 q = (__int128)max_mass * f + 3;
-    launch(q < ((__int128)1 << 31) ? narrow : wide);
+    const __int128 q = (__int128)max_mass * f;
+    launch(q < ((__int128)1 << 28) ? narrow : wide);
 }
 
 int64_t is_blocks(int64_t work, int64_t cap_per_cu)

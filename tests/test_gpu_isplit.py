@@ -85,11 +85,12 @@ def test_3d_wide_ranges_ragged_bit_exact(mpm, oracle_lib, path):
 
 @pytest.mark.parametrize("path", PATHS)
 def test_narrow_limit_signs_and_ties(mpm, oracle_lib, path):
-    """Declared maxima at the edge of the 32-bit product path (46,340 each:
-    m v up to 2^31 - 88,048), values at the extremes with both signs
-    (negative masses included), positions on ties and nodes; and the same
-    cloud with maxima one step wider, which takes the 128-bit path."""
-    lim = 46340
+    """Declared maxima at the edge of the 32-bit path (16,383 each: m v up to
+    2^28 - 32,767, shares and node sums in 32 bits), values at the extremes
+    with both signs (negative masses included), positions on ties and nodes;
+    and the same cloud with maxima one step wider (m v up to 2^28), which
+    takes the 128-bit path."""
+    lim = 16383
     h = G.integer_cloud_quadratic(0x6A, 9001, 24, 3, lim, lim, lim)
     rng = np.random.default_rng(5)
     for key in ("m", "v", "C"):
