@@ -335,10 +335,12 @@ __global__ void __launch_bounds__(256) isplit_kernel(int64_t np, int n, const in
 // ---------------------------------------------------------------------------
 // Tiled path.
 // ---------------------------------------------------------------------------
-// A particle's tile-ordered copy: position and quantities in one 128-byte
-// record (one cache line), written by the scatter in tile order so that the
-// accumulating kernel streams whole lines instead of gathering 4 to 8 bytes
-// from each of the caller's 16 arrays per particle.
+// A particle's tile-ordered copy: position and quantities in one record,
+// written by the scatter in tile order so that the accumulating kernel
+// streams whole lines instead of gathering 4 to 8 bytes from each of the
+// caller's 16 arrays per particle.  The wide path keeps 64-bit quantities in
+// 128 bytes (one cache line); the narrow path, whose quantities the scatter
+// has range-checked (so they fit in 32 bits), 32-bit ones in 64 bytes.
 struct __align__(16) IsRecord {
     int32_t X[4];          // X[DIM..3] unused
     int64_t m;
@@ -347,6 +349,17 @@ struct __align__(16) IsRecord {
     int64_t pad;
 };
 static_assert(sizeof(IsRecord) == 128, "one record per 128-byte line");
+
+struct __align__(16) IsRecord32 {
+    int32_t X[3];          // X[DIM..2] unused
+    int32_t m;
+    int32_t v[3];          // v[DIM..2] unused
+    int32_t C[9];          // (d, e) at d * DIM + e
+};
+static_assert(sizeof(IsRecord32) == 64, "two records per 128-byte line");
+
+template <bool NARROW>
+using IsRec = typename std::conditional<NARROW, IsRecord32, IsRecord>::type;
 
 constexpr int kIsTile = 8;                 // cells per tile edge
 constexpr int kIsBlock = kIsTile + 2;      // nodes per block edge: bases t0..t0+7 reach t0..t0+9
@@ -517,7 +530,10 @@ __global__ void __launch_bounds__(kIsThreads) is_scan_final_kernel(const uint32_
 }
 
 // Each visited particle's record goes to its tile's range at its rank.
-template <int DIM>
+// NARROW: the declared ranges are checked here (a particle outside them is
+// counted in status[1] and its record carries zero mass, velocity and affine
+// matrix, so it adds nothing), and the quantities are stored in 32 bits.
+template <int DIM, bool NARROW>
 __global__ void __launch_bounds__(256) is_scatter_kernel(int64_t np, int n, int64_t tx, int sshift,
                                                          const int32_t *__restrict__ X,
                                                          const int64_t *__restrict__ m,
@@ -525,34 +541,59 @@ __global__ void __launch_bounds__(256) is_scatter_kernel(int64_t np, int n, int6
                                                          const int64_t *__restrict__ C,
                                                          const uint32_t *__restrict__ order,
                                                          const uint32_t *__restrict__ rank,
-                                                         const uint64_t *__restrict__ start,
-                                                         IsRecord *__restrict__ rec)
+                                                         const uint64_t *__restrict__ start, int64_t max_mass,
+                                                         int64_t max_speed, int64_t max_affine,
+                                                         IsRec<NARROW> *__restrict__ rec,
+                                                         uint32_t *__restrict__ status)
 {
     for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < np; k += (int64_t)gridDim.x * blockDim.x) {
         const uint32_t r = rank[k];
-        if (r == ~0u)
-            continue;
+        const bool visit = r != ~0u;
         const int64_t p = order ? (int64_t)order[k] : k;
         int64_t base[DIM];
         AxisCoef ax[DIM];
-        stencil<DIM>(X, np, p, n, base, ax);
+        if (visit)
+            stencil<DIM>(X, np, p, n, base, ax);
+        IsRec<NARROW> q;
+        if (visit) {
+#pragma unroll
+            for (int d = 0; d < (NARROW ? 3 : 4); ++d)
+                q.X[d] = d < DIM ? X[(int64_t)d * np + p] : 0;
+        }
+        if constexpr (NARROW) {
+            int64_t mp = 0, vp[DIM], cp[DIM][DIM];
+            bool in_range = true;
+            if (visit)
+                in_range = load_quantities<DIM>(m, v, C, np, p, max_mass, max_speed, max_affine, mp, vp, cp);
+            wave_count(visit && !in_range, &status[1]);
+            if (!visit)
+                continue;
+            q.m = in_range ? (int32_t)mp : 0;
+#pragma unroll
+            for (int d = 0; d < 3; ++d)
+                q.v[d] = d < DIM && in_range ? (int32_t)vp[d < DIM ? d : 0] : 0;
+#pragma unroll
+            for (int i = 0; i < 9; ++i)
+                q.C[i] = i < DIM * DIM && in_range ? (int32_t)cp[(i < DIM * DIM ? i : 0) / DIM][(i < DIM * DIM ? i : 0) % DIM]
+                                                   : 0;
+        } else {
+            if (!visit)
+                continue;
+            q.m = m[p];
+#pragma unroll
+            for (int d = 0; d < 3; ++d)
+                q.v[d] = d < DIM ? v[(int64_t)d * np + p] : 0;
+#pragma unroll
+            for (int i = 0; i < 9; ++i)
+                q.C[i] = i < DIM * DIM ? C[(int64_t)i * np + p] : 0;
+            q.pad = 0;
+        }
         const int64_t e = (tile_of<DIM>(base, tx) << sshift) | ((k >> 8) & ((1ll << sshift) - 1));
-        IsRecord q;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-            q.X[d] = d < DIM ? X[(int64_t)d * np + p] : 0;
-        q.m = m[p];
-#pragma unroll
-        for (int d = 0; d < 3; ++d)
-            q.v[d] = d < DIM ? v[(int64_t)d * np + p] : 0;
-#pragma unroll
-        for (int i = 0; i < 9; ++i)
-            q.C[i] = i < DIM * DIM ? C[(int64_t)i * np + p] : 0;
-        q.pad = 0;
+        constexpr int W = (int)(sizeof(IsRec<NARROW>) / 16);
         const uint4 *src = reinterpret_cast<const uint4 *>(&q);
         uint4 *dst = reinterpret_cast<uint4 *>(rec + (int64_t)(start[e] & 0xFFFFFFFFull) + r);
 #pragma unroll
-        for (int w = 0; w < 8; ++w)
+        for (int w = 0; w < W; ++w)
             dst[w] = src[w];
     }
 }
@@ -576,7 +617,7 @@ __device__ __forceinline__ int64_t item_tile(const uint64_t *__restrict__ start,
 
 template <int DIM, bool NARROW>
 __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n, int64_t tx, int64_t tiles, int sshift,
-                                                              const IsRecord *__restrict__ rec,
+                                                              const IsRec<NARROW> *__restrict__ rec,
                                                               const uint32_t *__restrict__ count,
                                                               const uint64_t *__restrict__ start,
                                                               const uint64_t *__restrict__ meta, int64_t max_mass,
@@ -609,12 +650,13 @@ __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n,
             block[e] = 0ull;
         __syncthreads();
         for (int64_t j = lo + threadIdx.x; j < hi; j += kIsThreads) {
-            IsRecord q;
+            IsRec<NARROW> q;
             {
+                constexpr int W = (int)(sizeof(IsRec<NARROW>) / 16);
                 const uint4 *src = reinterpret_cast<const uint4 *>(rec + j);
                 uint4 *dst = reinterpret_cast<uint4 *>(&q);
 #pragma unroll
-                for (int w = 0; w < 8; ++w)
+                for (int w = 0; w < W; ++w)
                     dst[w] = src[w];
             }
             int64_t base[DIM];
@@ -638,9 +680,11 @@ __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n,
                     in_range &= cp[d][e] >= -max_affine && cp[d][e] <= max_affine;
                 }
             }
-            wave_count(!in_range, &status[1]);
-            if (!in_range)
-                continue;
+            if constexpr (!NARROW) {         // (narrow: checked by the scatter)
+                wave_count(!in_range, &status[1]);
+                if (!in_range)
+                    continue;
+            }
             int lb[DIM];
 #pragma unroll
             for (int e = 0; e < DIM; ++e)
@@ -703,13 +747,11 @@ __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n,
 // of a momentum channel at most 4.75 * 2^28 + 12 < 2^31: 32-bit values and
 // sums throughout, and products of 29 by 49 bits in two 32 x 32 -> 64-bit
 // multiply-adds.
-template <int DIM, class Launch, class K>
-void pick_width(int64_t max_mass, int64_t max_speed, int64_t max_affine, Launch &&launch, K narrow, K wide)
+bool narrow_ranges(int64_t max_mass, int64_t max_speed, int64_t max_affine)
 {
     int64_t f = max_speed > max_affine ? max_speed : max_affine;
     f = f > 1 ? f : 1;
-    const __int128 q = (__int128)max_mass * f;
-    launch(q < ((__int128)1 << 28) ? narrow : wide);
+    return (__int128)max_mass * f < ((__int128)1 << 28);
 }
 
 int64_t is_blocks(int64_t work, int64_t cap_per_cu)
@@ -765,7 +807,6 @@ hipError_t launch_p2g_isplit_tiled(int dim, int n, int64_t np, const int32_t *X,
     uint64_t *partial = reinterpret_cast<uint64_t *>(w + l.partial);
     uint64_t *meta = reinterpret_cast<uint64_t *>(w + l.meta);
     uint32_t *rank = reinterpret_cast<uint32_t *>(w + l.rank);
-    IsRecord *rec = reinterpret_cast<IsRecord *>(w + l.rec);
     const dim3 blk(kIsThreads);
     const int sh = l.slot_shift;
     hipLaunchKernelGGL(is_zero_kernel, dim3((unsigned)is_blocks(l.entries, 16)), blk, 0, s, count, l.entries);
@@ -781,26 +822,29 @@ hipError_t launch_p2g_isplit_tiled(int dim, int n, int64_t np, const int32_t *X,
     hipLaunchKernelGGL(is_scan_top_kernel, dim3(1), blk, 0, s, partial, l.scan_blocks, meta);
     hipLaunchKernelGGL(is_scan_final_kernel, dim3((unsigned)l.scan_blocks), blk, 0, s, count, l.entries, sh, partial,
                        start);
+    const bool narrow = narrow_ranges(max_mass, max_speed, max_affine);
+    auto scatter = [&](auto kern, auto *records) {
+        hipLaunchKernelGGL(kern, dim3(pb), blk, 0, s, np, n, l.tiles_x, sh, X, m, v, C, order, rank, start, max_mass,
+                           max_speed, max_affine, records, status);
+    };
+    IsRecord *rec = reinterpret_cast<IsRecord *>(w + l.rec);
+    IsRecord32 *rec32 = reinterpret_cast<IsRecord32 *>(w + l.rec);
     if (dim == 3)
-        hipLaunchKernelGGL(is_scatter_kernel<3>, dim3(pb), blk, 0, s, np, n, l.tiles_x, sh, X, m, v, C, order, rank,
-                           start, rec);
+        narrow ? scatter(is_scatter_kernel<3, true>, rec32) : scatter(is_scatter_kernel<3, false>, rec);
     else
-        hipLaunchKernelGGL(is_scatter_kernel<2>, dim3(pb), blk, 0, s, np, n, l.tiles_x, sh, X, m, v, C, order, rank,
-                           start, rec);
+        narrow ? scatter(is_scatter_kernel<2, true>, rec32) : scatter(is_scatter_kernel<2, false>, rec);
     // items <= tiles + np / kIsChunk; persistent workgroups stride over them
     const int64_t max_items = l.tiles + np / kIsChunk + 1;
     const int64_t cap = (int64_t)device_cu_count() * 4;
     const unsigned tb = (unsigned)(max_items < cap ? max_items : cap);
-if (dim == 3)
-        pick_width<3>(max_mass, max_speed, max_affine, [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3(tb), blk, 0, s, np, n, l.tiles_x, l.tiles, sh, rec, count, start, meta,
-                               max_mass, max_speed, max_affine, grid, status);
-        }, is_tiled_kernel<3, true>, is_tiled_kernel<3, false>);
+auto tiled = [&](auto kern, auto *records) {
+        hipLaunchKernelGGL(kern, dim3(tb), blk, 0, s, np, n, l.tiles_x, l.tiles, sh, records, count, start, meta,
+                           max_mass, max_speed, max_affine, grid, status);
+    };
+    if (dim == 3)
+        narrow ? tiled(is_tiled_kernel<3, true>, rec32) : tiled(is_tiled_kernel<3, false>, rec);
     else
-        pick_width<2>(max_mass, max_speed, max_affine, [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3(tb), blk, 0, s, np, n, l.tiles_x, l.tiles, sh, rec, count, start, meta,
-                               max_mass, max_speed, max_affine, grid, status);
-        }, is_tiled_kernel<2, true>, is_tiled_kernel<2, false>);
+        narrow ? tiled(is_tiled_kernel<2, true>, rec32) : tiled(is_tiled_kernel<2, false>, rec);
     return hipGetLastError();
 }
 
@@ -816,10 +860,11 @@ hipError_t launch_p2g_isplit(int dim, int n, int64_t np, const int32_t *X, const
         hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, np, n, X, m, v, C, order, max_mass, max_speed,
                            max_affine, grid, status);
     };
+    const bool narrow = narrow_ranges(max_mass, max_speed, max_affine);
     if (dim == 3)
-        pick_width<3>(max_mass, max_speed, max_affine, launch, isplit_kernel<3, true>, isplit_kernel<3, false>);
+        narrow ? launch(isplit_kernel<3, true>) : launch(isplit_kernel<3, false>);
     else
-        pick_width<2>(max_mass, max_speed, max_affine, launch, isplit_kernel<2, true>, isplit_kernel<2, false>);
+        narrow ? launch(isplit_kernel<2, true>) : launch(isplit_kernel<2, false>);
     return hipGetLastError();
 }
 

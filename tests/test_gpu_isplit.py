@@ -159,8 +159,13 @@ def test_boundaries_skips_and_accumulation(mpm, oracle_lib, dim, path):
     h["m"][200] = 501                                     # over max_mass
     h["v"][0, 201] = -501                                 # over max_speed
     h["C"][dim * dim - 1, 202] = 501                      # over max_affine
+    # far beyond 32 bits (the narrow path stores range-checked 32-bit values,
+    # so these must be refused before they are narrowed, not wrapped)
+    h["m"][203] = (1 << 40) + 7
+    h["v"][dim - 1, 204] = -(1 << 33)
+    h["C"][0, 205] = (1 << 32) + 100                      # wraps to 100 in 32 bits
     ok = inside.copy()
-    ok[[200, 201, 202]] = False
+    ok[[200, 201, 202, 203, 204, 205]] = False
     prior = np.arange(np.prod((1 + dim,) + (n,) * dim), dtype=np.int64).reshape((1 + dim,) + (n,) * dim) * 7 - 11
     say("isplit boundaries", dim, path)
     g, st = run_gpu(mpm, dim, n, h, (500, 500, 500), grid=prior, path=path)
@@ -168,7 +173,7 @@ def test_boundaries_skips_and_accumulation(mpm, oracle_lib, dim, path):
     ref, rst = oracle_lib.p2g_isplit(dim, n, sub, grid=prior.copy())
     assert np.array_equal(g, ref)
     assert rst.tolist() == [0, 0, 0, 0]
-    assert st.tolist() == [2, 3, 0, 0]
+    assert st.tolist() == [2, 6, 0, 0]
 
 
 def test_one_tile_many_items_and_sparse_tiles(mpm, oracle_lib):
