@@ -67,20 +67,25 @@ def p2g_algorithmic_bytes(dim: int, particles: int, touched: int) -> int:
 METRIC = "P2G particles/sec and achieved HBM GB/s (% of peak), 3D 16M particles, 1 GPU"
 
 
-def profile_record():
-    """The machine-readable record of the committed rocprofv3 summary of the P2G
-    kernel (calibrated HBM bytes per launch, counter-derived limiter), or None
-    when the kernel sources changed since the counters were taken."""
+P2G_SOURCES = ("material_point_particle_amd/csrc/p2g.hip", "material_point_particle_amd/csrc/p2g_device.hpp",
+               "material_point_particle_amd/csrc/common.hpp")
+ISPLIT_SOURCES = ("material_point_particle_amd/csrc/isplit.hip", "material_point_particle_amd/csrc/common.hpp")
+
+
+def profile_record(name: str = "p2g_tiled_blobs_3d_256", sources: tuple = P2G_SOURCES):
+    """The machine-readable record of a committed rocprofv3 summary (the last
+    JSON block of profiles/<name>.md: counter-derived bytes, instruction
+    counts, limiter), or None when the kernel's sources changed since the
+    counters were taken (their SHA-256 no longer matches the record's)."""
     import hashlib
     import re
     here = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for f in ("material_point_particle_amd/csrc/p2g.hip", "material_point_particle_amd/csrc/p2g_device.hpp",
-              "material_point_particle_amd/csrc/common.hpp"):
+    for f in sources:
         with open(os.path.join(here, f), "rb") as fh:
             h.update(fh.read())
     try:
-        text = open(os.path.join(here, "profiles", "p2g_tiled_blobs_3d_256.md")).read()
+        text = open(os.path.join(here, "profiles", name + ".md")).read()
         rec = json.loads(re.findall(r"```json\n(.*?)\n```", text, re.S)[-1])
     except (OSError, IndexError, ValueError):
         return None
@@ -438,12 +443,30 @@ def measure_isplit(args, torch, w, build):
     ms_d = timed(None, 5)
     atomics = np_ * 27 * (1 + w.dim)
     rd = np_ * 116
+    # the accumulating kernel against the VALU issue rate: its issued lane-ops
+    # per particle and its own duration come from the committed counter
+    # record (null once its sources change); the rounded products per second
+    # of the whole call are measured here
+    splits = (1 + w.dim * (1 + w.dim)) * sum(3 ** k_ for k_ in range(w.dim))
+    rec = profile_record("isplit_tiled_isplit_3d_128", ISPLIT_SOURCES)
+    alu = {"bound": "alu", "kernel": "is_tiled_kernel<3, true>", "unit": "T lane-ops/s",
+           "peak": round(SLOW_PEAK_TOPS, 2),
+           "peak_basis": "one 64-lane VALU instruction per SIMD every 4 cycles (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz)",
+           "splits_per_particle": splits, "rounded_products_per_particle": 2 * splits,
+           "rounded_products_per_s_whole_call": round(2 * splits * np_ / (ms_t * 1e-3), 1),
+           "achieved": None, "frac": None, "lane_ops_per_particle": None, "kernel_ms": None, "valu_busy": None}
+    if rec is not None:
+        achieved = rec["valu_lane_ops_per_particle"] * np_ / (rec["kernel_us"] * 1e-6) / 1e12
+        alu.update({"achieved": round(achieved, 2), "frac": round(achieved / SLOW_PEAK_TOPS, 4),
+                    "lane_ops_per_particle": rec["valu_lane_ops_per_particle"],
+                    "kernel_ms": round(rec["kernel_us"] * 1e-3, 4), "valu_busy": rec["valu_busy"]})
     log(f"isplit: tiled {ms_t:.3f} ms, direct {ms_d:.3f} ms per call ({np_ / (ms_t * 1e-3) / 1e9:.2f} G particles/s)")
     return {
         "workload": f"{w.name}: {np_} integer particles uniform over {w.n}^3 nodes, |m|,|v|,|C| <= "
                     f"{rng[0]}, 2^-16 cell positions",
         "calls": k, "ms_per_call": round(ms_t, 4), "particles_per_s": round(np_ / (ms_t * 1e-3), 1),
         "read_bytes_per_call": rd, "read_gbs": round(rd / (ms_t * 1e-3) / 1e9, 1),
+        "alu_roofline": alu,
         "direct": {"ms_per_call": round(ms_d, 4), "particles_per_s": round(np_ / (ms_d * 1e-3), 1),
                    "atomics_per_call": atomics, "atomics_per_s": round(atomics / (ms_d * 1e-3), 1)},
         "status": status.cpu().numpy().view(np.uint32).tolist(),
