@@ -8,7 +8,7 @@
 // work item on chip.
 //
 // Passes (all on the caller's stream, no host synchronisation):
-//   1. count    blocks of up to 65,536 consecutive particles (a chunk): each
+//   1. count    blocks of up to 32,768 consecutive particles (a chunk): each
 //               particle's base cell gives its tile; an LDS hash table counts
 //               the chunk's particles per tile, then one global atomic per
 //               (chunk, tile) reserves the chunk's run inside the tile, so a
@@ -79,13 +79,15 @@ __global__ void bin_reset_kernel(uint32_t *__restrict__ tile_count, int64_t n_ti
     }
 }
 
-// Pass 1 visits chunks of kBinThreads * per consecutive particles (per <=
-// kMaxPer, chosen per launch so that every CU gets a chunk), one block per
-// chunk and one block per CU: its hash table takes 128 KB of LDS.  Pass 5
+// Pass 1 visits chunks of kBinThreads * PER consecutive particles (PER a
+// power of two from 4 to kMaxPer, chosen per launch so that every CU gets a
+// chunk, and a template argument so that each thread's PER ranks stay in
+// registers), one block per chunk and one block per CU: its hash table takes
+// 128 KB of LDS.  Pass 5
 // needs no chunks (it reads each particle's final rank) and visits blocks of
 // consecutive particles sized for occupancy.
 constexpr int kBinThreads = 1024;
-constexpr int kMaxPer = 64;                          // a chunk holds at most 65,536 particles
+constexpr int kMaxPer = 32;                          // a chunk holds at most 32,768 particles
 constexpr int kHashBits = 14;
 constexpr int kHashSlots = 1 << kHashBits;           // tiles per chunk counted in LDS
 constexpr int kMaxProbes = 64;
@@ -131,9 +133,9 @@ __device__ __forceinline__ bool particle_cell(const float *x, float nf, float dx
 // contiguous run for pass 5 to write.  Inside a run the records keep their
 // arrival order, so records written close together in time are neighbours in
 // memory.
-template <int DIM>
+template <int DIM, int PER>
 __global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, float nf, float dx, float last_base,
-                                                                      int ntx, int64_t chunks, int per,
+                                                                      int ntx, int64_t chunks,
                                                                       uint32_t *__restrict__ tile_count,
                                                                       uint32_t *__restrict__ rank_out,
                                                                       uint32_t *__restrict__ status,
@@ -147,29 +149,28 @@ __global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, f
     }
     __syncthreads();
     uint32_t binned = 0, runs = 0;
-    const int64_t chunk = (int64_t)kBinThreads * per;
+    static_assert(PER % 4 == 0 && PER <= kMaxPer, "particles per thread");
+    const int64_t chunk = (int64_t)kBinThreads * PER;
     for (int64_t c = blockIdx.x; c < chunks; c += gridDim.x) {
         const int64_t p0 = c * chunk + threadIdx.x;
         // per particle k of this thread: kLocalRank | slot << 16 | rank in the
         // chunk, a final rank, or 0 when not binned; kept in registers until the
         // chunk's runs are placed
-        uint32_t v[kMaxPer];
+        uint32_t v[PER];
 #pragma unroll
-        for (int k0 = 0; k0 < kMaxPer; k0 += 4) {
-            if (k0 >= per)
-                break;
+        for (int k0 = 0; k0 < PER; k0 += 4) {
             float xs[4][DIM];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t p = p0 + (int64_t)(k0 + j) * kBinThreads;
 #pragma unroll
                 for (int e = 0; e < DIM; ++e)
-                    xs[j][e] = (k0 + j < per && p < f.n) ? f.x[e * f.n + p] : 0.0f;
+                    xs[j][e] = p < f.n ? f.x[e * f.n + p] : 0.0f;
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t p = p0 + (int64_t)(k0 + j) * kBinThreads;
-                const bool live = k0 + j < per && p < f.n;
+                const bool live = p < f.n;
                 uint32_t t = 0, l = 0;
                 const bool dom = live && particle_cell<DIM>(xs[j], nf, dx, last_base, ntx, t, l);
                 wave_count(live && !dom, &status[0]);
@@ -201,11 +202,10 @@ __global__ void __launch_bounds__(kBinThreads) bin_tile_count_kernel(Fields f, f
         }
         __syncthreads();
 #pragma unroll
-        for (int k = 0; k < kMaxPer; ++k) {
+        for (int k = 0; k < PER; ++k) {
             const int64_t p = p0 + (int64_t)k * kBinThreads;
-            if (k >= per || p >= f.n)
-                break;
-            rank_out[p] = (v[k] & kLocalRank) ? hval[(v[k] >> 16) & (kHashSlots - 1)] + (v[k] & 0xFFFFu) : v[k];
+            if (p < f.n)
+                rank_out[p] = (v[k] & kLocalRank) ? hval[(v[k] >> 16) & (kHashSlots - 1)] + (v[k] & 0xFFFFu) : v[k];
         }
         __syncthreads();
         for (int e = threadIdx.x; e < kHashSlots; e += kBinThreads) {
@@ -556,19 +556,36 @@ hipError_t launch_bin(int dim, int n, const Fields &p, RangesF r, const BinView 
     const int ntx = n / kTile;
     hipLaunchKernelGGL(bin_reset_kernel, dim3(blocks_for(b.n_tiles + kMetaWords, 256)), dim3(256), 0, s, b.tile_count,
                        b.n_tiles, b.meta, b.stamp);
-    // particles per thread of a chunk: a chunk for every CU, at most kMaxPer
+    // particles per thread of a chunk: the smallest power of two from 4 to
+    // kMaxPer that gives no more chunks than CUs (or kMaxPer)
     const int64_t span = (int64_t)kBinThreads * device_cu_count();
-    int64_t per = (p.n + span - 1) / span;
-    per = per < 4 ? 4 : (per > kMaxPer ? kMaxPer : per);
+    int per = 4;
+    while (per < kMaxPer && (int64_t)per * span < p.n)
+        per *= 2;
     const int64_t chunks = (p.n + kBinThreads * per - 1) / (kBinThreads * per);
     const unsigned cblocks = (unsigned)(chunks < (int64_t)device_cu_count() ? chunks : device_cu_count());
+    auto count = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(cblocks), dim3(kBinThreads), 0, s, p, nf, dx, last, ntx, chunks, b.tile_count,
+                           b.rank, status, b.meta);
+    };
     if (chunks > 0) {
-        if (dim == 3)
-            hipLaunchKernelGGL(bin_tile_count_kernel<3>, dim3(cblocks), dim3(kBinThreads), 0, s, p, nf, dx, last, ntx,
-                               chunks, (int)per, b.tile_count, b.rank, status, b.meta);
-        else
-            hipLaunchKernelGGL(bin_tile_count_kernel<2>, dim3(cblocks), dim3(kBinThreads), 0, s, p, nf, dx, last, ntx,
-                               chunks, (int)per, b.tile_count, b.rank, status, b.meta);
+        if (dim == 3) {
+            switch (per) {
+            case 4: count(bin_tile_count_kernel<3, 4>); break;
+            case 8: count(bin_tile_count_kernel<3, 8>); break;
+            case 16: count(bin_tile_count_kernel<3, 16>); break;
+            case 32: count(bin_tile_count_kernel<3, 32>); break;
+            default: count(bin_tile_count_kernel<3, kMaxPer>); break;
+            }
+        } else {
+            switch (per) {
+            case 4: count(bin_tile_count_kernel<2, 4>); break;
+            case 8: count(bin_tile_count_kernel<2, 8>); break;
+            case 16: count(bin_tile_count_kernel<2, 16>); break;
+            case 32: count(bin_tile_count_kernel<2, 32>); break;
+            default: count(bin_tile_count_kernel<2, kMaxPer>); break;
+            }
+        }
     }
     const int64_t pblocks = (b.n_tiles + kPlanTiles - 1) / kPlanTiles;
     uint4 *items = reinterpret_cast<uint4 *>(b.items);
