@@ -144,7 +144,11 @@ const char *mpm_strerror(int code);
 int mpm_check_bounds(const mpm_grid_desc *grid, int64_t n_particles, const mpm_ranges *ranges,
                      double *log2_bound);
 
-/* Workspace size for binning n_particles on this grid (host-only).  The size
+/* Workspace size for binning n_particles on this grid (host-only): the
+ * histogram, prefix sum and scattered copy of the counting sort ("Particle
+ * worlds, part 3", steps 3-4) and the per-tile index the implementation page
+ * builds each substep ("Implementation -- GPU Optimization & Reference
+ * Codebases", section 2.1).  The size
  * and layout of a workspace follow from the grid and the particle count; every
  * entry point that is handed a workspace also takes its size in bytes, refuses
  * one that is too small for its own grid and count (MPM_ERR_WORKSPACE), and its
@@ -154,7 +158,8 @@ int mpm_check_bounds(const mpm_grid_desc *grid, int64_t n_particles, const mpm_r
  * falls back to every node). */
 int mpm_workspace_bytes(const mpm_grid_desc *grid, int64_t n_particles, size_t *bytes);
 
-/* Offsets of the arrays inside that workspace (host-only). */
+/* Offsets of the arrays inside that workspace (host-only; the arrays are
+ * those of mpm_ws_layout above, for the same passages). */
 int mpm_workspace_layout(const mpm_grid_desc *grid, int64_t n_particles, mpm_ws_layout *layout);
 
 /* Counting sort of the particles into tiles of 4^dim cells by the stencil's
