@@ -181,6 +181,43 @@ def test_jelly_substeps_in_lockstep(mpm, oracle_lib):
     assert u32(tr.status).tolist()[3] == 0
 
 
+def test_square_2d_substeps_in_lockstep(mpm, oracle_lib):
+    """The 2D loop: a 24 x 24-cell elastic square at 4 particles per cell
+    (jittered 2 x 2 sub-lattice) thrown down and sideways onto the floor of a
+    64^2 grid, 12 substeps of 5 iterations, the guardian engaging; after every
+    substep x, d, D and F bit-identical to the oracle's own trajectory."""
+    from material_point_particle_amd import _lib as L
+    from material_point_particle_amd.transfer import ElasticParticles, PBMPMSubsteps, Transfer
+    n, frac, dt, band, iters, relax, polar = 64, 32, 2e-3, 2, 5, 1.5, 12
+    cells = np.stack(np.meshgrid(np.arange(20, 44), np.arange(3, 27), indexing="ij"), 0).reshape(2, -1)
+    sub = np.stack(np.meshgrid([0.25, 0.75], [0.25, 0.75], indexing="ij"), 0).reshape(2, -1)
+    pos = (cells[:, :, None] + sub[:, None, :]).reshape(2, -1)
+    k = pos.shape[1]
+    jit = 0.2 * (G.uniform01(0x2D, 1, 2 * k).reshape(2, k) - 0.5)
+    x = ((pos + jit) / n).astype(np.float32)
+    v0 = np.array([0.4, -3.0])[:, None] + 0.05 * (G.uniform01(0x2D, 2, 2 * k).reshape(2, k) - 0.5)
+    host = {"x": np.ascontiguousarray(x), "v": np.ascontiguousarray((v0 * dt).astype(np.float32)),
+            "C": np.zeros((4, k), np.float32), "m": np.ones(k, np.float32)}
+    F = np.ascontiguousarray(np.tile(np.eye(2, dtype=np.float32).reshape(4, 1), (1, k)))
+    rng = (1.0, 0.5, 4.0)
+    grav = (0.0, -9.8)
+    parts = ElasticParticles(host, F, np.full(k, 1.0 / (4 * n * n), np.float32))
+    tr = Transfer(2, n, frac, rng, parts.n)
+    loop = PBMPMSubsteps(tr, parts, dt, grav, iters, relax, polar, band)
+    state = {key: np.ascontiguousarray(a.copy()) for key, a in host.items()}
+    state["F"] = F.copy()
+    for step in range(1, 13):
+        loop.substep()
+        oracle_lib.pbmpm_substep(2, n, frac, state, rng, iters, relax, polar, band, dt, grav)
+        torch.cuda.synchronize()
+        got = parts.host()
+        say("pbmpm 2D lockstep substep", step)
+        for key in ("x", "v", "C", "F"):
+            assert_same(got[key], state[key], f"2D substep {step} {key}")
+    assert float(state["x"][1].min()) < 3.0 / n                 # it reached the floor
+    assert u32(tr.status).tolist()[0] == 0 and u32(tr.status).tolist()[3] == 0
+
+
 @pytest.mark.timeout(900)
 def test_full_size_jelly_substep(mpm, oracle_lib):
     """One substep (5 iterations) of the 8M-particle jelly cube at 256^3: the
