@@ -156,31 +156,18 @@ g2p2g_kernel(FusedArgs f)
         if (lane == 0)
             n_strays = 0u;
         __syncthreads();
-        // 2. gather and advect each record (with grid_in), then its key; the
-        //    next record of the lane is loaded while this one is computed
+        // 2. gather and advect each record (with grid_in), then its key
         uint32_t clamps = 0;
-        float4 nxt[R / 4];
-        if ((uint32_t)lane < count) {
-            const float4 *src = reinterpret_cast<const float4 *>(f.records + (int64_t)(first + lane) * R);
-#pragma unroll
-            for (int q = 0; q < R / 4; ++q)
-                nxt[q] = src[q];
-        }
         for (uint32_t i = (uint32_t)lane; i < count; i += kWave) {
             float4 *src = reinterpret_cast<float4 *>(f.records + (int64_t)(first + i) * R);
             float rec[R];
 #pragma unroll
             for (int q = 0; q < R / 4; ++q) {
-                rec[4 * q] = nxt[q].x;
-                rec[4 * q + 1] = nxt[q].y;
-                rec[4 * q + 2] = nxt[q].z;
-                rec[4 * q + 3] = nxt[q].w;
-            }
-            if (i + kWave < count) {
-                const float4 *ns = reinterpret_cast<const float4 *>(f.records + (int64_t)(first + i + kWave) * R);
-#pragma unroll
-                for (int q = 0; q < R / 4; ++q)
-                    nxt[q] = ns[q];
+                const float4 t = src[q];
+                rec[4 * q] = t.x;
+                rec[4 * q + 1] = t.y;
+                rec[4 * q + 2] = t.z;
+                rec[4 * q + 3] = t.w;
             }
             if (f.grid_in) {
                 Axis ax[DIM];
