@@ -208,21 +208,24 @@ def measure_substeps(args, torch, w, build, DeviceParticles, Transfer):
     }
 
 
-def measure_fused(args, torch, w, build, DeviceParticles, Transfer):
+def measure_fused(args, torch, w, build, DeviceParticles, Transfer, split=False):
     """The dam-break substep with the particle state resident in the binned
-    records (8M particles, 256^3 nodes): one fused G2P2G kernel per substep
+    records (8M particles, 256^3 nodes), re-binned every 10 substeps (gather
+    of the records into the particle arrays and a resident binning), all
+    inside the timed region.  The fused form: one G2P2G kernel per substep
     (grid update on load, gather and advection, deposit into the next of
-    three grids, and the clear of the grid read in the previous substep),
-    re-binned every 10 substeps (gather of the records into the particle
-    arrays and a resident binning), all inside the timed region."""
+    three grids, and the clear of the grid read in the previous substep).
+    split: three launches per substep over two grids (grid update of the node
+    tiles the last deposit flagged, consuming them; G2P over the records in
+    place; the deposit), each timed with events."""
+    from material_point_particle_amd.transfer import ResidentSubsteps, SplitResidentSubsteps
     import material_point_particle_amd._lib as L
-    from material_point_particle_amd.transfer import ResidentSubsteps
     host = build(w)
     ex = w.extra
     parts = DeviceParticles(host)
     del host
     tr = Transfer(w.dim, w.n, w.frac_bits, (w.max_mass, w.max_speed, w.max_affine), parts.n)
-    rs = ResidentSubsteps(tr, parts, ex["dt"], ex["gravity"], ex["sticky"])
+    rs = (SplitResidentSubsteps if split else ResidentSubsteps)(tr, parts, ex["dt"], ex["gravity"], ex["sticky"])
     stream = torch.cuda.current_stream()
     every = 10
     rs.start()
@@ -230,32 +233,51 @@ def measure_fused(args, torch, w, build, DeviceParticles, Transfer):
         rs.substep()
     torch.cuda.synchronize()
     k = args.substeps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(k)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(k)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(k):
         e = ev[i]
         e[0].record(stream)
-        rs.substep(stream)
-        e[1].record(stream)
+        if split:
+            a, b = rs.cur, 1 - rs.cur
+            L.mpm_grid_update_tiles(tr.desc, rs.grids[a], rs.tiles[a], tr.vg, rs.dt, rs.gravity, rs.sticky, stream)
+            e[1].record(stream)
+            L.mpm_g2p_records(tr.desc, tr.ws, parts.n, tr.vg, rs.dt, tr.status, stream)
+            e[2].record(stream)
+            L.mpm_g2p2g(tr.desc, tr.ranges, tr.ws, parts.n, None, rs.grids[b], rs.tiles[b], rs.dt, rs.gravity,
+                        rs.sticky, tr.status, stream)
+            rs.cur = b
+        else:
+            rs.substep(stream)
+            e[1].record(stream)
+            e[2].record(stream)
+        e[3].record(stream)
         if (i + 1) % every == 0:
             rs.gather()
             rs.rebin()
-        e[2].record(stream)
+        e[4].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
     total = start.elapsed_time(stop) / k
-    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(2)] for e in ev])
-    fused_ms = st[:, 0].mean()
-    rebin_ms = st[:, 1].sum() / max(1, k // every)
+    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])
+    rebin_ms = st[:, 3].sum() / max(1, k // every)
     status = tr.status.cpu().numpy().view(np.uint32).tolist()
-    log(f"fused substeps: {total:.3f} ms (g2p2g with the third grid's clear {fused_ms:.3f}, re-bin {rebin_ms:.3f} "
-        f"every {every})")
+    if split:
+        stages = {"grid_update_tiles": round(float(st[:, 0].mean()), 4), "g2p_records": round(float(st[:, 1].mean()), 4),
+                  "deposit": round(float(st[:, 2].mean()), 4), "rebin_each": round(float(rebin_ms), 4)}
+        log(f"split resident substeps: {total:.3f} ms (grid update {stages['grid_update_tiles']:.3f}, g2p over the "
+            f"records {stages['g2p_records']:.3f}, deposit {stages['deposit']:.3f}, re-bin {rebin_ms:.3f} every {every})")
+    else:
+        stages = {"g2p2g": round(float(st[:, 0].mean()), 4), "rebin_each": round(float(rebin_ms), 4)}
+        log(f"fused substeps: {total:.3f} ms (g2p2g with the third grid's clear {stages['g2p2g']:.3f}, re-bin "
+            f"{rebin_ms:.3f} every {every})")
     return {
         "workload": f"{w.name}: {parts.n} particles, dam-break block, {w.n}^3 nodes, state resident in the binned "
-                    f"records, re-binned every {every} substeps",
+                    f"records, re-binned every {every} substeps" + (", three launches per substep over two grids"
+                                                                    if split else ", one fused kernel per substep"),
         "substeps": k, "ms_per_substep": round(total, 4), "particles_per_s": round(parts.n / (total * 1e-3), 1),
-        "stages_ms": {"g2p2g": round(float(fused_ms), 4), "rebin_each": round(float(rebin_ms), 4)},
+        "stages_ms": stages,
         "status": status,
     }
 
@@ -496,6 +518,10 @@ def parse():
                     help="skip the fused-substep measurement (state resident in the binned records)")
     ap.add_argument("--only-fused", action="store_true",
                     help="run only the fused-substep measurement; prints its object")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip the split resident substep (grid update of flagged tiles, G2P over records, deposit)")
+    ap.add_argument("--only-split", action="store_true",
+                    help="run only the split resident substep measurement; prints its object")
     ap.add_argument("--no-pbmpm", action="store_true",
                     help="skip the position-based MPM substep measurement on the jelly cube")
     ap.add_argument("--only-pbmpm", action="store_true",
@@ -527,6 +553,10 @@ def main():
     if args.only_fused:
         print(json.dumps({"substep_fused": measure_fused(args, torch, WORKLOADS["dam_3d_256"], build, DeviceParticles,
                                                          Transfer)}), flush=True)
+        return
+    if args.only_split:
+        print(json.dumps({"substep_split": measure_fused(args, torch, WORKLOADS["dam_3d_256"], build, DeviceParticles,
+                                                         Transfer, split=True)}), flush=True)
         return
     if args.only_pbmpm:
         print(json.dumps({"pbmpm": measure_pbmpm(args, torch, WORKLOADS["pbmpm_jelly_3d_256"], build)}), flush=True)
@@ -698,6 +728,10 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_fused:
         out["substep_fused"] = measure_fused(args, torch, WORKLOADS["dam_3d_256"], build, DeviceParticles, Transfer)
+        torch.cuda.empty_cache()
+    if not args.no_split:
+        out["substep_split"] = measure_fused(args, torch, WORKLOADS["dam_3d_256"], build, DeviceParticles, Transfer,
+                                             split=True)
         torch.cuda.empty_cache()
     if not args.no_elastic:
         out["elastic"] = measure_elastic(args, torch, WORKLOADS["jelly_3d_256"], build, Transfer)

@@ -364,6 +364,38 @@ int mpm_g2p2g(const mpm_grid_desc *grid, const mpm_ranges *ranges, void *ws, siz
  * MPM_ERR_HIP. */
 int mpm_grid_clear_tiles(const mpm_grid_desc *grid, int64_t *grid_io, uint8_t *tiles, hipStream_t stream);
 
+/* The resident substep split in three launches instead of the fused kernel's
+ * one ("Implementation -- GPU Optimization & Reference Codebases", section
+ * 2.1: the transfer cycle over the binned state; the node tiles a deposit
+ * wrote are the ones the next update touches):
+ *
+ *   mpm_bin_resident(ws <- particles); mpm_g2p2g(grid_in = NULL -> A, flags A)
+ *   per substep: mpm_grid_update_tiles(A, flags A -> vg)      (A zeroed)
+ *                mpm_g2p_records(vg, records in place)
+ *                mpm_g2p2g(grid_in = NULL -> B, flags B)      (the deposit)
+ *                (A, B) <- (B, A)
+ *
+ * Results are identical to the fused kernel's and to the separate steps'.
+ * Two grids suffice: the update consumes the grid it reads. */
+
+/* Grid update of the node tiles flagged in tiles (uint8[(n/4)^dim], as
+ * mpm_g2p2g writes them): at every node of a flagged tile, v = P/M + dt g
+ * (M != 0), 0 where M == 0 and on the sticky walls, into vg; M and P set to
+ * zero; then every flag reset.  Nodes of unflagged tiles are not touched
+ * (their vg stays as it was).  Same arithmetic as mpm_grid_update.  All
+ * pointers device.  Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
+int mpm_grid_update_tiles(const mpm_grid_desc *grid, int64_t *grid_io, uint8_t *tiles, float *vg, float dt,
+                          const float *gravity, int32_t sticky, hipStream_t stream);
+
+/* The APIC gather and advection (as mpm_g2p: vg read, clamps counted in
+ * status[2]) of every record of a resident binning of n_particles, written
+ * back into the record in place (x, v, C; m kept), records visited in tile
+ * order.  ws: device, ws_bytes long; a workspace whose stamp names another
+ * grid or particle count does nothing and is counted in status[3].
+ * Errors: MPM_ERR_INVALID, MPM_ERR_WORKSPACE, MPM_ERR_HIP. */
+int mpm_g2p_records(const mpm_grid_desc *grid, void *ws, size_t ws_bytes, int64_t n_particles, const float *vg,
+                    float dt, uint32_t *status, hipStream_t stream);
+
 /* Copies x, v and C of every binned particle from its record back to the
  * caller's arrays (particles->n must be the count the workspace was binned
  * with; m and particles that were not binned are left as they are).  ws is

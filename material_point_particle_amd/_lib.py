@@ -54,7 +54,8 @@ EXPORTS = ("mpm_version", "mpm_strerror", "mpm_check_bounds", "mpm_workspace_byt
            "mpm_bin_particles", "mpm_p2g", "mpm_p2g_cic_split", "mpm_p2g_isplit", "mpm_isplit_workspace_bytes",
            "mpm_grid_update", "mpm_grid_clear", "mpm_g2p", "mpm_neohookean_affine", "mpm_update_deformation",
            "mpm_bin_resident", "mpm_g2p2g", "mpm_grid_clear_tiles", "mpm_gather_records",
-           "mpm_p2g_isplit_noalloc", "mpm_pbmpm_project_elastic", "mpm_pbmpm_grid_update", "mpm_pbmpm_integrate")
+           "mpm_p2g_isplit_noalloc", "mpm_pbmpm_project_elastic", "mpm_pbmpm_grid_update", "mpm_pbmpm_integrate",
+           "mpm_grid_update_tiles", "mpm_g2p_records")
 
 _lib = None
 
@@ -127,6 +128,12 @@ def lib() -> ct.CDLL:
         L.mpm_pbmpm_integrate.restype = ct.c_int
         L.mpm_pbmpm_integrate.argtypes = [P(mpm_grid_desc), P(mpm_particles), ct.c_float, P(ct.c_float), ct.c_void_p,
                                           ct.c_void_p]
+        L.mpm_grid_update_tiles.restype = ct.c_int
+        L.mpm_grid_update_tiles.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_float,
+                                            P(ct.c_float), ct.c_int32, ct.c_void_p]
+        L.mpm_g2p_records.restype = ct.c_int
+        L.mpm_g2p_records.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_size_t, ct.c_int64, ct.c_void_p, ct.c_float,
+                                      ct.c_void_p, ct.c_void_p]
         L.mpm_gather_records.restype = ct.c_int
         L.mpm_gather_records.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_size_t, P(mpm_particles), ct.c_void_p,
                                          ct.c_void_p]
@@ -260,6 +267,17 @@ def mpm_g2p2g(desc, rng: mpm_ranges, ws, n_particles: int, grid_in, grid_out, ti
 def mpm_grid_clear_tiles(desc, grid, tiles, stream=None) -> None:
     _check(lib().mpm_grid_clear_tiles(ct.byref(desc), _ptr(grid), _ptr(tiles), _stream(stream)),
            "mpm_grid_clear_tiles")
+
+
+def mpm_grid_update_tiles(desc, grid, tiles, vg, dt: float, gravity, sticky: int, stream=None) -> None:
+    g = (ct.c_float * 3)(*(list(gravity) + [0.0] * (3 - len(gravity))))
+    _check(lib().mpm_grid_update_tiles(ct.byref(desc), _ptr(grid), _ptr(tiles), _ptr(vg), dt, g, sticky,
+                                       _stream(stream)), "mpm_grid_update_tiles")
+
+
+def mpm_g2p_records(desc, ws, n_particles: int, vg, dt: float, status, stream=None) -> None:
+    _check(lib().mpm_g2p_records(ct.byref(desc), _ptr(ws), _nbytes(ws), n_particles, _ptr(vg), dt, _ptr(status),
+                                 _stream(stream)), "mpm_g2p_records")
 
 
 def mpm_gather_records(desc, ws, parts: mpm_particles, status, stream=None) -> None:

@@ -5,7 +5,7 @@
 
 #include <atomic>
 
-#include "common.hpp"
+#include "resident.hpp"
 
 namespace mpmk {
 
@@ -339,6 +339,33 @@ int mpm_grid_clear_tiles(const mpm_grid_desc *grid, int64_t *grid_io, uint8_t *t
     if (check_desc(grid) != MPM_OK || !aligned(grid_io, 8) || !aligned(tiles, 4))
         return MPM_ERR_INVALID;
     return hip_status(launch_grid_clear_tiles(grid->dim, grid->n, grid_io, tiles, stream));
+}
+
+int mpm_grid_update_tiles(const mpm_grid_desc *grid, int64_t *grid_io, uint8_t *tiles, float *vg, float dt,
+                          const float *gravity, int32_t sticky, hipStream_t stream)
+{
+    if (check_desc(grid) != MPM_OK || !aligned(grid_io, 8) || !aligned(tiles, 4) || !aligned(vg, 4) || !gravity ||
+        sticky < 0 || sticky > grid->n / 2 || !(dt >= 0.0f))
+        return MPM_ERR_INVALID;
+    return hip_status(launch_grid_update_tiles(grid->dim, grid->n, grid_io, tiles, vg, dt, gravity, sticky, stream));
+}
+
+int mpm_g2p_records(const mpm_grid_desc *grid, void *ws, size_t ws_bytes, int64_t n_particles, const float *vg,
+                    float dt, uint32_t *status, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_desc(grid)) != MPM_OK)
+        return rc;
+    if (n_particles < 0 || n_particles > kMaxParticles || !aligned(ws, 256) || !aligned(vg, 4) ||
+        !aligned(status, 4) || !(dt >= 0.0f))
+        return MPM_ERR_INVALID;
+    mpm_ws_layout l;
+    make_layout(grid, n_particles, &l);
+    if (ws_bytes < l.total_bytes)
+        return MPM_ERR_WORKSPACE;
+    const RangesF none{ 0.0f, 0.0f, 0.0f };
+    return hip_status(launch_g2p_records(grid->dim, grid->n, bin_view(ws, l, make_stamp(grid, n_particles, none, true)),
+                                         vg, dt, status, stream));
 }
 
 int mpm_gather_records(const mpm_grid_desc *grid, const void *ws, size_t ws_bytes, const mpm_particles *particles,

@@ -6,7 +6,7 @@
 // it in place and no separate clear pass exists), rule 1 (the fixed-point sums
 // are converted once, in the grid update) and rule 7 (gravity is applied by the
 // solver to the grid velocity).
-#include "common.hpp"
+#include "resident.hpp"
 
 namespace mpmk {
 namespace {
@@ -169,6 +169,109 @@ __global__ void __launch_bounds__(256) g2p_kernel(int n, float nf, float dx, flo
     }
 }
 
+// The resident substep's gather ("Implementation -- GPU Optimization &
+// Reference Codebases", section 2.1, the state kept in the binned records):
+// the APIC gather and advection of g2p_particle from vg (the same arithmetic
+// as g2p_kernel) for every record, in tile order, x, v and C written back
+// into the record in place, m kept.  Records come from a resident binning, so
+// every one is inside the grid when binned, and the clamp keeps it there.
+// A block takes 256 consecutive records at a time and moves them through LDS
+// in 16-byte pieces, so that each global load and store instruction covers
+// 16 whole records (1 KB) instead of one piece of 64 records spread over
+// 4 KB; each lane then works on one record.  Piece q of record r sits in
+// slot (q + r) mod 4 of the record's 64 bytes in LDS, so that the lanes'
+// record-wise accesses fall in distinct banks.
+template <int DIM>
+__global__ void __launch_bounds__(256) g2p_records_kernel(int n, float nf, float dx, float last_base,
+                                                          const float *__restrict__ vg, float *__restrict__ records,
+                                                          const uint32_t *__restrict__ meta, BinStamp stamp,
+                                                          float dt, float lo, float hi, float cscale,
+                                                          uint32_t *__restrict__ status)
+{
+    constexpr int R = rec_floats<DIM>();
+    constexpr int Q = R / 4;                           // 16-byte pieces per record
+    __shared__ float4 stage[256 * Q];
+    if (!stamp_matches(meta, stamp, false)) {        // binned for another grid or count: touch nothing
+        if (blockIdx.x == 0 && threadIdx.x == 0)
+            atomicAdd(&status[3], 1u);
+        return;
+    }
+    const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    const int64_t n_rec = meta[kMetaBinned];
+    const int t = threadIdx.x;
+    float4 *rec4 = reinterpret_cast<float4 *>(records);
+    for (int64_t base = (int64_t)blockIdx.x * 256; base < n_rec; base += (int64_t)gridDim.x * 256) {
+        // the block's records into LDS: consecutive threads on consecutive pieces
+#pragma unroll
+        for (int k = 0; k < Q; ++k) {
+            const int idx = k * 256 + t, r = idx / Q, q = idx % Q;
+            if (base + r < n_rec)
+                stage[r * Q + (q + r) % Q] = rec4[(base + r) * Q + q];
+        }
+        __syncthreads();
+        const bool live = base + t < n_rec;
+        // only x (the first piece) is read here; the gather replaces v and C,
+        // and m is copied over when the record is written back
+        const float4 p0 = stage[t * Q + t % Q];
+        const float x0[3] = { p0.x, p0.y, p0.z };
+        Axis ax[DIM];
+        float xp[DIM];
+        bool ok = live;
+#pragma unroll
+        for (int e = 0; e < DIM; ++e) {
+            xp[e] = x0[e];
+            ok = axis_stencil(xp[e], nf, dx, last_base, ax[e]) && ok;
+        }
+        wave_count(live && !ok, &status[0]);
+        bool clamped = false;
+        if (ok) {
+            const int bz = DIM == 3 ? ax[DIM - 1].base : 0;
+            auto vel = [&](int a, int b, int c, int d) {
+                const int64_t node = DIM == 3 ? ((int64_t)(bz + c) * n + (ax[1].base + b)) * n + (ax[0].base + a)
+                                              : (int64_t)(ax[1].base + b) * n + (ax[0].base + a);
+                return vg[d * nodes + node];
+            };
+            float vn[DIM], Cn[DIM * DIM], xn[DIM];
+            clamped = g2p_particle<DIM>(ax, xp, vel, dt, lo, hi, cscale, vn, Cn, xn);
+            constexpr int M = 2 * DIM + DIM * DIM;        // m's float in the record
+            float rec[R];
+#pragma unroll
+            for (int d = 0; d < DIM; ++d) {
+                rec[d] = xn[d];
+                rec[DIM + d] = vn[d];
+            }
+#pragma unroll
+            for (int q = 0; q < DIM * DIM; ++q)
+                rec[2 * DIM + q] = Cn[q];
+            const float4 pm = stage[t * Q + (M / 4 + t) % Q];
+            rec[M] = (M % 4 == 0) ? pm.x : (M % 4 == 1) ? pm.y : (M % 4 == 2) ? pm.z : pm.w;
+#pragma unroll
+            for (int q = M + 1; q < R; ++q)
+                rec[q] = 0.0f;
+            // the pieces past m's hold only padding and are left as they are
+#pragma unroll
+            for (int q = 0; q <= M / 4; ++q)
+                stage[t * Q + (q + t) % Q] = make_float4(rec[4 * q], rec[4 * q + 1], rec[4 * q + 2], rec[4 * q + 3]);
+        }
+        wave_count(clamped, &status[2]);
+        __syncthreads();
+        // and back: a record left untouched (outside the grid) is written back as it was
+#pragma unroll
+        for (int k = 0; k < Q; ++k) {
+            const int idx = k * 256 + t, r = idx / Q, q = idx % Q;
+            if (base + r < n_rec)
+                rec4[(base + r) * Q + q] = stage[r * Q + (q + r) % Q];
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void __launch_bounds__(256) clear_words_kernel(uint32_t *__restrict__ w, int64_t count)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+        w[i] = 0u;
+}
+
 int blocks_for(int64_t work, int block)
 {
     const int64_t want = (work + block - 1) / block;
@@ -259,6 +362,40 @@ hipError_t launch_grid_clear_tiles(int dim, int n, int64_t *grid, uint8_t *tiles
     const int64_t n_tiles = dim == 3 ? (int64_t)(n / kTile) * (n / kTile) * (n / kTile)
                                      : (int64_t)(n / kTile) * (n / kTile);
     hipLaunchKernelGGL(zero_bytes_kernel, dim3(blocks_for(n_tiles, 256)), dim3(256), 0, s, tiles, n_tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_grid_update_tiles(int dim, int n, int64_t *grid, uint8_t *tiles, float *vg, float dt,
+                                    const float *gravity, int sticky, hipStream_t s)
+{
+    const float g[3] = { gravity[0], gravity[1], dim == 3 ? gravity[2] : 0.0f };
+    node_rows<1>(dim, n, tiles, grid, vg, dt, g, sticky, s);
+    // the flags are consumed with the nodes: one byte per 4^dim-node tile,
+    // (n/4)^dim of them, a multiple of four for every n the grid accepts
+    const int64_t ntx = n / kTile;
+    const int64_t words = (dim == 3 ? ntx * ntx * ntx : ntx * ntx) / 4;
+    hipLaunchKernelGGL(clear_words_kernel, dim3(blocks_for(words, 256)), dim3(256), 0, s,
+                       reinterpret_cast<uint32_t *>(tiles), words);
+    return hipGetLastError();
+}
+
+hipError_t launch_g2p_records(int dim, int n, const BinView &b, const float *vg, float dt, uint32_t *status,
+                              hipStream_t s)
+{
+    const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3);
+    const float lo = dx, hi = (float)(n - 2) * dx;
+    const float cscale = 4.0f * (float)n * (float)n;
+    // the record count is read on the device; enough threads for every
+    // particle the workspace was sized for
+    const int64_t np = (int64_t)b.stamp.np_lo | ((int64_t)b.stamp.np_hi << 32);
+    if (np == 0)
+        return hipSuccess;
+    if (dim == 3)
+        hipLaunchKernelGGL(g2p_records_kernel<3>, dim3(blocks_for(np, 256)), dim3(256), 0, s, n, nf, dx, last, vg,
+                           b.sorted, b.meta, b.stamp, dt, lo, hi, cscale, status);
+    else
+        hipLaunchKernelGGL(g2p_records_kernel<2>, dim3(blocks_for(np, 256)), dim3(256), 0, s, n, nf, dx, last, vg,
+                           b.sorted, b.meta, b.stamp, dt, lo, hi, cscale, status);
     return hipGetLastError();
 }
 

@@ -163,6 +163,28 @@ class ResidentSubsteps:
         L.mpm_gather_records(self.tr.desc, self.tr.ws, self.parts.desc(), self.tr.status)
 
 
+class SplitResidentSubsteps(ResidentSubsteps):
+    """The resident-state substep in three launches instead of the fused
+    kernel: the grid update of the node tiles the last deposit flagged
+    (consuming that grid and its flags), the G2P gather over the records in
+    place, and the fused kernel's deposit-only launch into the other grid.
+    Two grids in turn; results identical to ResidentSubsteps'."""
+
+    def __init__(self, tr: Transfer, parts: DeviceParticles, dt: float, gravity, sticky: int, device="cuda"):
+        super().__init__(tr, parts, dt, gravity, sticky, device)
+        self.grids, self.tiles = self.grids[:2], self.tiles[:2]
+
+    def substep(self, stream=None) -> None:
+        a, b = self.cur, 1 - self.cur
+        tr = self.tr
+        L.mpm_grid_update_tiles(tr.desc, self.grids[a], self.tiles[a], tr.vg, self.dt, self.gravity, self.sticky,
+                                stream)
+        L.mpm_g2p_records(tr.desc, tr.ws, self.parts.n, tr.vg, self.dt, tr.status, stream)
+        L.mpm_g2p2g(tr.desc, tr.ranges, tr.ws, self.parts.n, None, self.grids[b], self.tiles[b], self.dt,
+                    self.gravity, self.sticky, tr.status, stream)
+        self.cur = b
+
+
 class PBMPMSubsteps:
     """The position-based MPM (PB-MPM) substep of an elastic material
     ("Implementation -- GPU Optimization & Reference Codebases", section

@@ -185,6 +185,22 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert g2p2g(4096, ct.c_void_p(8192), grid, T, clear=(ct.c_void_p((1 << 20) + 4), T3)) == L.MPM_ERR_INVALID
     assert lib.mpm_grid_clear_tiles(ct.byref(d), ct.c_void_p(4100), T, None) == L.MPM_ERR_INVALID
     assert lib.mpm_grid_clear_tiles(None, grid, T, None) == L.MPM_ERR_INVALID
+    # the split resident substep's entries
+    VG = ct.c_void_p(1 << 21)
+    assert lib.mpm_grid_update_tiles(ct.byref(d), grid, T, VG, 1e-4, g3, 100, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_update_tiles(ct.byref(d), grid, T, VG, 1e-4, None, 2, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_update_tiles(ct.byref(d), grid, ct.c_void_p((1 << 16) + 2), VG, 1e-4, g3, 2,
+                                     None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_update_tiles(ct.byref(d), grid, T, VG, -1.0, g3, 2, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_grid_update_tiles(None, grid, T, VG, 1e-4, g3, 2, None) == L.MPM_ERR_INVALID
+    assert lib.mpm_g2p_records(ct.byref(d), ct.c_void_p(4096), need_bins - 1, 10, VG, 1e-4, status,
+                               None) == L.MPM_ERR_WORKSPACE
+    assert lib.mpm_g2p_records(ct.byref(d), ct.c_void_p(4100), 1 << 30, 10, VG, 1e-4, status,
+                               None) == L.MPM_ERR_INVALID
+    assert lib.mpm_g2p_records(ct.byref(d), ct.c_void_p(4096), 1 << 30, -1, VG, 1e-4, status,
+                               None) == L.MPM_ERR_INVALID
+    assert lib.mpm_g2p_records(ct.byref(d), ct.c_void_p(4096), 1 << 30, 10, VG, float("nan"), status,
+                               None) == L.MPM_ERR_INVALID
     assert lib.mpm_gather_records(ct.byref(d), ct.c_void_p(4096), 1 << 30,
                                   ct.byref(L.mpm_particles(10, 4096, 4096, None, 4096)), status,
                                   None) == L.MPM_ERR_INVALID                           # no C

@@ -57,11 +57,16 @@ def oracle_substep(oracle_lib, w, state, ex):
     return grid, st, out
 
 
-def resident(mpm, w, host, ex):
-    from material_point_particle_amd.transfer import DeviceParticles, ResidentSubsteps, Transfer
+def resident(mpm, w, host, ex, split=False):
+    """The resident loop: the fused kernel (three grids), or split in three
+    launches (grid update of the flagged tiles, G2P over the records, the
+    deposit) over two grids."""
+    from material_point_particle_amd.transfer import (DeviceParticles, ResidentSubsteps, SplitResidentSubsteps,
+                                                      Transfer)
     parts = DeviceParticles(host)
     tr = Transfer(w.dim, w.n, w.frac_bits, ranges_of(w), parts.n)
-    rs = ResidentSubsteps(tr, parts, ex["dt"], ex["gravity"], ex["sticky"])
+    cls = SplitResidentSubsteps if split else ResidentSubsteps
+    rs = cls(tr, parts, ex["dt"], ex["gravity"], ex["sticky"])
     return parts, tr, rs
 
 
@@ -76,28 +81,29 @@ def two_grid_substep(rs):
     rs.cur = b
 
 
-@pytest.mark.parametrize("grids", [3, 2])
+@pytest.mark.parametrize("grids", [3, 2, "split"])
 def test_lockstep_with_oracle_small(mpm, oracle_lib, grids):
     """Dam-break recipe, 2^16 particles on 64^3 nodes, 40 substeps re-binned
     every 10: after every substep k in 5, 10, ..., 40 the gathered state and
     the grid the resident loop holds (the P2G of that state) equal the
     oracle's own trajectory.  Three grids: the grid read in the previous
     substep is zero after each substep, flags included; two grids: the
-    separate flagged clear."""
+    separate flagged clear; split: the grid update of the flagged tiles, G2P
+    over the records and the deposit, the grid read zero afterwards."""
     w = scaled(WORKLOADS["dam_3d_256"], 1 << 16, n=64)
     ex = w.extra
     host = build(w)
-    parts, tr, rs = resident(mpm, w, host, ex)
+    parts, tr, rs = resident(mpm, w, host, ex, split=grids == "split")
     rs.start()
     state = {k: v.copy() for k, v in host.items()}
     grid0, _, _ = oracle_substep(oracle_lib, w, state, ex)
     torch.cuda.synchronize()
     assert_same(rs.grid.cpu().numpy(), grid0, "initial deposit")
     for k in range(1, 41):
-        if grids == 3:
-            rs.substep()
-        else:
+        if grids == 2:
             two_grid_substep(rs)
+        else:
+            rs.substep()
         _, _, state = oracle_substep(oracle_lib, w, state, ex)
         if k % 5 == 0:
             rs.gather()
@@ -112,20 +118,26 @@ def test_lockstep_with_oracle_small(mpm, oracle_lib, grids):
                 cleared = (rs.cur + 1) % 3
                 assert int(rs.grids[cleared].abs().sum()) == 0 and int(rs.tiles[cleared].sum()) == 0
                 assert int(rs.tiles[rs.cur].sum()) > 0
+            if grids == "split":
+                read = 1 - rs.cur
+                assert int(rs.grids[read].abs().sum()) == 0 and int(rs.tiles[read].sum()) == 0
+                assert int(rs.tiles[rs.cur].sum()) > 0
         if k % 10 == 0:
             rs.rebin()
     assert tr.status.cpu().numpy().view(np.uint32).tolist() == [0, 0, 0, 0]
 
 
 @pytest.mark.timeout(600)
-def test_full_size_matches_separate_steps(mpm):
-    """The 8M-particle 256^3 dam-break: 12 fused substeps (re-binned every 5)
-    against 12 substeps of binning, P2G, restricted grid update and G2P."""
+@pytest.mark.parametrize("split", [False, True])
+def test_full_size_matches_separate_steps(mpm, split):
+    """The 8M-particle 256^3 dam-break: 12 resident substeps (fused kernel, or
+    split in three launches; re-binned every 5) against 12 substeps of
+    binning, P2G, restricted grid update and G2P."""
     from material_point_particle_amd.transfer import DeviceParticles, Transfer
     w = WORKLOADS["dam_3d_256"]
     ex = w.extra
     host = build(w)
-    parts, tr, rs = resident(mpm, w, host, ex)
+    parts, tr, rs = resident(mpm, w, host, ex, split=split)
     rs.start()
     for k in range(1, 13):
         rs.substep()
@@ -143,7 +155,7 @@ def test_full_size_matches_separate_steps(mpm):
     t2.bin(p2)
     t2.p2g(p2, binned=True)
     torch.cuda.synchronize()
-    say("fused full size")
+    say("resident full size", "split" if split else "fused")
     a, b = parts.host(), p2.host()
     for key in ("x", "v", "C"):
         assert_same(a[key], b[key], f"{key} after 12 substeps")
@@ -162,8 +174,9 @@ def fast_cloud(dim, n, count, seed):
     return {"x": np.ascontiguousarray(x), **f}
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("dim", [2, 3])
-def test_strays_and_range_checks_in_lockstep(mpm, oracle_lib, dim):
+def test_strays_and_range_checks_in_lockstep(mpm, oracle_lib, dim, split):
     """Fast particles cross tile boundaries between re-binnings (every 12
     substeps here), so many deposit through the stray path; particles beyond
     the declared ranges add nothing and are counted at every deposit."""
@@ -172,7 +185,7 @@ def test_strays_and_range_checks_in_lockstep(mpm, oracle_lib, dim):
     host = fast_cloud(dim, n, 6000 if dim == 3 else 3000, 0xFA5 + dim)
     w = replace(scaled(base, host["m"].shape[0], n=n), frac_bits=28, max_mass=2.0, max_speed=40.0, max_affine=25.0)
     ex = {"dt": 2e-3 / (n / 32), "gravity": (0.0, -9.8, 0.0)[:dim], "sticky": 2}
-    parts, tr, rs = resident(mpm, w, host, ex)
+    parts, tr, rs = resident(mpm, w, host, ex, split=split)
     rs.start()
     state = {k: v.copy() for k, v in host.items()}
     _, st0, _ = oracle_substep(oracle_lib, w, state, ex)
@@ -185,7 +198,7 @@ def test_strays_and_range_checks_in_lockstep(mpm, oracle_lib, dim):
         if k % 4 == 0:
             rs.gather()
             torch.cuda.synchronize()
-            say("fused strays", dim, k)
+            say("resident strays", dim, "split" if split else "fused", k)
             got = parts.host()
             for key in ("x", "v", "C"):
                 assert_same(got[key], state[key], f"{dim}D substep {k} {key}")
