@@ -498,8 +498,8 @@ def measure_isplit(args, torch, w, build):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="blobs_3d_256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="particles in the CPU-baseline sample (0: all)")
@@ -754,24 +754,37 @@ def main():
         n_s = args.cpu_sample or w.n_particles
         sample = {k: np.ascontiguousarray(v[..., :n_s]) for k, v in host.items() if k in ("x", "v", "C", "m")}
         threads = min(16, len(os.sched_getaffinity(0)))
-        log(f"cpu baseline on {n_s} particles: 1 thread, then {threads}")
-        t = time.perf_counter()
-        g1, s1 = oracle.p2g_quadratic(w.dim, w.n, w.frac_bits, sample, rng)
-        dt1 = time.perf_counter() - t
-        t = time.perf_counter()
-        gt, st = oracle.p2g_quadratic_threads(w.dim, w.n, w.frac_bits, sample, rng, threads)
-        dtt = time.perf_counter() - t
-        same = bool(np.array_equal(g1, gt) and s1.tolist() == st.tolist())
-        del g1, gt
-        if not same:
-            raise SystemExit("bench.py: the threaded oracle's grid differs from the single-thread oracle's")
+        runs = 3
+        log(f"cpu baseline on {n_s} particles: 1 thread, then {threads}, {runs} runs each")
+        t1, tt = [], []
+        for _ in range(runs):
+            t = time.perf_counter()
+            g1, s1 = oracle.p2g_quadratic(w.dim, w.n, w.frac_bits, sample, rng)
+            t1.append(time.perf_counter() - t)
+            t = time.perf_counter()
+            gt, st = oracle.p2g_quadratic_threads(w.dim, w.n, w.frac_bits, sample, rng, threads)
+            tt.append(time.perf_counter() - t)
+            same = bool(np.array_equal(g1, gt) and s1.tolist() == st.tolist())
+            del g1, gt
+            if not same:
+                raise SystemExit("bench.py: the threaded oracle's grid differs from the single-thread oracle's")
+        dt1, dtt = float(np.median(t1)), float(np.median(tt))
+        cpu_model = None
+        try:
+            with open("/proc/cpuinfo") as fh:
+                cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+        except OSError:
+            pass
+        gpu_rate = binned / (p2g_ms * 1e-3)
         out["cpu_baseline"] = {"value": round(n_s / dtt, 1), "unit": "particles/s", "cores": threads,
                                "kind": "oracle",
                                "sample": f"the oracle's P2G over the first {n_s} particles of {w.name} on {threads} "
-                                         f"host threads (private int64 grids, integer-summed), {dtt:.2f}s; grid "
-                                         "bit-identical to the one-thread oracle's",
+                                         f"host threads (private int64 grids, integer-summed), median of {runs} runs "
+                                         f"{dtt:.2f}s; grid bit-identical to the one-thread oracle's",
                                "single_core": {"value": round(n_s / dt1, 1), "unit": "particles/s", "cores": 1,
                                                "seconds": round(dt1, 3)},
+                               "gpu_p2g_over_cpu": round(gpu_rate / (n_s / dtt), 1),
+                               "host_cpu": cpu_model,
                                "host_cpus": os.cpu_count(), "host_cpus_usable": len(os.sched_getaffinity(0))}
     print(json.dumps(out), flush=True)
 
