@@ -31,7 +31,8 @@
 //    formed in registers and added with one 64-bit global atomic each
 //    (27 x 4 random atomics per particle in 3D);
 //  - tiled: a counting sort of the particles into 8^dim-cell tiles, each
-//    visited particle copied into a 128-byte record in tile order, then
+//    visited particle copied into a record in tile order (128 bytes; 64 in
+//    the narrow path, whose quantities fit in 32 bits), then
 //    one workgroup per slice of a tile accumulates the tile's 10^dim-node
 //    block on chip with 64-bit LDS atomics and flushes it with one global
 //    atomic per non-zero node and channel, consecutive lanes on consecutive
@@ -71,79 +72,161 @@ __device__ __forceinline__ int64_t round_shift(__int128 t)
     return fl + (int64_t)((r > half) | ((r == half) & ((uint64_t)fl & 1ull)));
 }
 
-// A split coefficient as two signed 32-bit words: c = hi 2^32 + lo with lo in
-// [-2^31, 2^31) (the low word read as signed, hi taking the rest).  For the
-// weights (0 <= c <= 2^32) hi is 0 or 1 and is kept as the mask -hi.
+// The narrow path (every split quantity below 2^28 in magnitude) forms each
+// rounded product from 32 x 32 -> 64-bit multiply-adds, with the shares
+// kept in 32 bits and biased so that they stay non-negative.  Every value
+// entering a split along axis e carries the bias B_e = 3^(dim - e) b
+// (b = 2^27 + 2^23 + 1, odd) and every share leaving it B_(e+1) (the last
+// axis' shares b).  A share is at most 3/4 |q| + 1 in magnitude (a weight is
+// at most 3/4, a first moment at most 1/4 in magnitude, and a near share adds
+// the two roundings of the outer ones), so the values entering every axis'
+// splits stay below 2^28 + 2 < 2 b in magnitude, and 27 b + 2^28 < 2^32:
+// every biased value lies in [0, 2^32).  Because B_e = 3 B_(e+1), the near share of a
+// weight split is q - s_0 - s_2 on the biased values as it is on the plain
+// ones, and a first-moment split's is 3 B_(e+1) - s_0 - s_2.  A node's
+// channel sum starts at minus the bias of the shares it will receive, so it
+// ends at the plain sum (32-bit arithmetic modulo 2^32, whose result fits).
+//
+// A weight product (0 <= c <= 2^32) is one unsigned multiply-add: with
+// q = q' - B_e, u = q' (c mod 2^32) + k with k = (1 + 2 B_(e+1)) 2^32 - B_e c
+// is q c + 2^32 + 2 B_(e+1) 2^32 (half the divisor, then a shift of the high
+// word) once q' is added to its high word where c = 2^32 (a weight of
+// exactly one half, the only one whose low word is not c; such a weight
+// exists only for a particle half a cell from a node, so that addition is
+// made only in the wavefronts that hold one).  The high word is
+// V' = V + 2 B_(e+1), V that of q c + 2^32: V / 2 rounds half up, and a tie
+// (low word 0, V even) whose rounded-up quotient is odd (V = 2 mod 4, that
+// is V' = 0 mod 4, B_(e+1) being odd) steps down by one.  The biased share
+// (V' - tie) / 2 is formed as (V' - 1 + min(t, 1)) / 2 with
+// t = (V' mod 4) | low word, zero exactly at such a tie.
+constexpr uint32_t kShareBias = (1u << 27) + (1u << 23) + 1u;
+
+template <int DIM, int E>
+constexpr uint32_t axis_bias()
+{
+    uint32_t b = kShareBias;
+    for (int i = E; i < DIM; ++i)
+        b *= 3u;
+    return b;
+}
+
+struct BiasedCoef {
+    uint32_t c;       // the weight's low word
+    uint32_t half;    // all ones for c = 2^32, else 0
+    uint64_t k;
+};
+
+// A first moment (|c| < 2^49) as two signed 32-bit words: c = hi 2^32 + lo
+// with lo in [-2^31, 2^31) (the low word read as signed, hi taking the rest).
 struct NarrowCoef {
     int32_t hi, lo;
 };
 
-template <bool WEIGHT>
+struct BiasedAxis {
+    BiasedCoef w0, w2;
+    NarrowCoef u0, u2;
+};
+
+template <int DIM, int E>
+__device__ __forceinline__ BiasedCoef biased_coef(int64_t c)
+{
+    constexpr uint64_t bin = axis_bias<DIM, E>(), bout = axis_bias<DIM, E + 1>();
+    const uint64_t k = ((1ull + 2ull * bout) << 32) - bin * (uint64_t)c;
+    return BiasedCoef{ (uint32_t)(uint64_t)c, (c >> 32) != 0 ? ~0u : 0u, k };
+}
+
 __device__ __forceinline__ NarrowCoef narrow_coef(int64_t c)
 {
     int32_t lo = (int32_t)(uint32_t)(uint64_t)c;
     int32_t hi = (int32_t)((c - (int64_t)lo) >> 32);
-    if constexpr (WEIGHT)
-        hi = -hi;
-    // the signs the optimiser could prove (a square is non-negative) are
-    // hidden, so that each product stays one signed 32 x 32 -> 64-bit
-    // multiply-add instead of an unsigned one with sign corrections
+    // signs the optimiser could prove are hidden, so that each product stays
+    // one signed 32 x 32 -> 64-bit multiply-add
     asm("" : "+v"(lo), "+v"(hi));
     return NarrowCoef{ hi, lo };
 }
 
-struct NarrowAxis {
-    NarrowCoef w0, w2, u0, u2;
-};
-
-__device__ __forceinline__ NarrowAxis narrow_axis(const AxisCoef &c)
+template <int DIM, int E>
+__device__ __forceinline__ BiasedAxis biased_axis(const AxisCoef &c)
 {
-    return NarrowAxis{ narrow_coef<true>(c.w0), narrow_coef<true>(c.w2), narrow_coef<false>(c.u0),
-                       narrow_coef<false>(c.u2) };
+    return BiasedAxis{ biased_coef<DIM, E>(c.w0), biased_coef<DIM, E>(c.w2), narrow_coef(c.u0),
+                       narrow_coef(c.u2) };
 }
 
-// round-half-even(q c / 2^K) for |q| < 2^29, |c| < 2^49 and K = 33 (the
-// weights, 0 <= c <= 2^32) or 49 (the first moments), as a 32-bit result:
-// u = q lo + 2^(K-1) (a signed 32 x 32 -> 64-bit multiply-add) and
-// V = q hi + floor(u / 2^32) give q c + 2^(K-1) = 2^32 V + (u mod 2^32), so
-// the quotient rounded half up is floor(V / 2^(K-32)); the sum is an exact
-// tie when u mod 2^32 and V mod 2^(K-32) are both zero, and then an odd
-// quotient steps down to the even neighbour (its lowest bit cleared).  For
-// K = 33, |V| <= 2^29 + 1 and q hi is q or 0, so V takes two 32-bit
-// operations; for K = 49 it is a second multiply-add.
-template <int K>
-__device__ __forceinline__ int32_t round_share(int32_t q, NarrowCoef c)
+// HALF: the wavefront holds a weight of exactly one half (only w_0 can be).
+template <bool HALF>
+__device__ __forceinline__ uint32_t biased_weight_share(uint32_t q, BiasedCoef w)
 {
-    // the offset's value is hidden from the optimiser: with it known, the
-    // tie test below is rewritten as a separate low-word multiply
-    int64_t half = 1ll << (K - 1);
+    const uint64_t u = (uint64_t)q * w.c + w.k;
+    uint32_t hi = (uint32_t)(u >> 32);
+    if constexpr (HALF)
+        hi += q & w.half;
+    const uint32_t t = (hi & 3u) | (uint32_t)u;
+    return (hi - 1u + (t < 1u ? t : 1u)) >> 1;
+}
+
+// round-half-even(q c / 2^49) + BOUT for a plain q and a first moment c: with
+// u = q lo + 2^48 + 2^49 and V' = q hi + floor(u / 2^32) (two signed
+// multiply-adds), q c + 2^48 + 2^49 = 2^32 V' + (u mod 2^32) and V' = V + 2^17
+// with V that of q c + 2^48; V' / 2^17 - 1 is the quotient rounded half up,
+// and a tie (low word 0, V' = 0 mod 2^18: the rounded-up quotient odd) steps
+// down: V' / 2^17 + BOUT - 2 + min(t, 1) with t zero exactly then.
+template <uint32_t BOUT>
+__device__ __forceinline__ uint32_t biased_moment_share(int32_t q, NarrowCoef c)
+{
+    // the offset's value is hidden from the optimiser, which would otherwise
+    // rewrite the tie test as a separate low-word multiply
+    int64_t half = 3ll << 48;
     asm("" : "+s"(half));
     const int64_t u = (int64_t)q * c.lo + half;
     const uint32_t u_lo = (uint32_t)(uint64_t)u;
-    if constexpr (K == 33) {
-        const int32_t V = (q & c.hi) + (int32_t)(u >> 32);
-        const int32_t r = V >> 1;
-        return (((uint32_t)V & 1u) | u_lo) == 0u ? (r & ~1) : r;
+    const int64_t V = (int64_t)q * c.hi + (u >> 32);
+    const uint32_t r = (uint32_t)(uint64_t)(V >> 17);
+    const uint32_t t = ((uint32_t)(uint64_t)V & 0x3FFFFu) | u_lo;
+    return r + (BOUT - 2u) + (t < 1u ? t : 1u);
+}
+
+// The one-axis split of the narrow path: KIND 0 with the weights, KIND 1
+// with the first moments; q biased by BIN, its shares by BOUT.
+template <int KIND, uint32_t BIN, uint32_t BOUT, bool HALF>
+__device__ __forceinline__ void split_biased(uint32_t q, const BiasedAxis &c, uint32_t s[3])
+{
+    if constexpr (KIND == 0) {
+        s[0] = biased_weight_share<HALF>(q, c.w0);
+        s[2] = biased_weight_share<false>(q, c.w2);
+        s[1] = q - s[0] - s[2];
     } else {
-        const int64_t V = (int64_t)q * c.hi + (u >> 32);
-        const int32_t r = (int32_t)(V >> (K - 32));
-        const uint32_t rem = ((uint32_t)(uint64_t)V & ((1u << (K - 32)) - 1u)) | u_lo;
-        return rem == 0u ? (r & ~1) : r;
+        const int32_t plain = (int32_t)(q - BIN);
+        s[0] = biased_moment_share<BOUT>(plain, c.u0);
+        s[2] = biased_moment_share<BOUT>(plain, c.u2);
+        s[1] = 3u * BOUT - s[0] - s[2];
     }
 }
 
-// The one-axis split of the narrow path: q and its shares in 32 bits.
-template <int KIND>
-__device__ __forceinline__ void split_narrow(int32_t q, const NarrowAxis &c, int32_t s[3])
+// acc[(a * 3 + b) * 3 + c] (2D: acc[a * 3 + b]) += the biased tensor split
+// of the plain q, along x with KX, then y with KY, then z with KZ.
+template <int DIM, int KX, int KY, int KZ, bool HALF>
+__device__ __forceinline__ void tensor_add_biased(int32_t q, const BiasedAxis (&ax)[DIM],
+                                                  uint32_t (&acc)[DIM == 3 ? 27 : 9])
 {
-    if constexpr (KIND == 0) {
-        s[0] = round_share<33>(q, c.w0);
-        s[2] = round_share<33>(q, c.w2);
-        s[1] = q - (s[0] + s[2]);
-    } else {
-        s[0] = round_share<49>(q, c.u0);
-        s[2] = round_share<49>(q, c.u2);
-        s[1] = -(s[0] + s[2]);
+    constexpr uint32_t b0 = axis_bias<DIM, 0>(), b1 = axis_bias<DIM, 1>(), b2 = axis_bias<DIM, 2>();
+    uint32_t sx[3];
+    split_biased<KX, b0, b1, HALF>((uint32_t)q + b0, ax[0], sx);
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        uint32_t sy[3];
+        split_biased<KY, b1, b2, HALF>(sx[a], ax[1], sy);
+#pragma unroll
+        for (int b = 0; b < 3; ++b) {
+            if constexpr (DIM == 3) {
+                uint32_t sz[3];
+                split_biased<KZ, b2, axis_bias<DIM, 3>(), HALF>(sy[b], ax[2], sz);
+#pragma unroll
+                for (int c = 0; c < 3; ++c)
+                    acc[(a * 3 + b) * 3 + c] += sz[c];
+            } else {
+                acc[a * 3 + b] += sy[b];
+            }
+        }
     }
 }
 
@@ -164,31 +247,21 @@ __device__ __forceinline__ void split1(int64_t q, const AxisCoef &c, int64_t s[3
 }
 
 // acc[(a * 3 + b) * 3 + c] (2D: acc[a * 3 + b]) += the tensor split of q,
-// along x with KX, then y with KY, then z with KZ: 64-bit values with
-// 128-bit products (Axis = AxisCoef) or 32-bit values (Axis = NarrowAxis).
-template <int KIND, class T, class Axis>
-__device__ __forceinline__ void split_any(T q, const Axis &c, T s[3])
+// along x with KX, then y with KY, then z with KZ, with 128-bit products.
+template <int DIM, int KX, int KY, int KZ>
+__device__ __forceinline__ void tensor_add(int64_t q, const AxisCoef (&ax)[DIM], int64_t (&acc)[DIM == 3 ? 27 : 9])
 {
-    if constexpr (sizeof(T) == 4)
-        split_narrow<KIND>(q, c, s);
-    else
-        split1<KIND>(q, c, s);
-}
-
-template <int DIM, int KX, int KY, int KZ, class T, class Axis>
-__device__ __forceinline__ void tensor_add(T q, const Axis (&ax)[DIM], T (&acc)[DIM == 3 ? 27 : 9])
-{
-    T sx[3];
-    split_any<KX>(q, ax[0], sx);
+    int64_t sx[3];
+    split1<KX>(q, ax[0], sx);
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
-        T sy[3];
-        split_any<KY>(sx[a], ax[1], sy);
+        int64_t sy[3];
+        split1<KY>(sx[a], ax[1], sy);
 #pragma unroll
         for (int b = 0; b < 3; ++b) {
             if constexpr (DIM == 3) {
-                T sz[3];
-                split_any<KZ>(sy[b], ax[2], sz);
+                int64_t sz[3];
+                split1<KZ>(sy[b], ax[2], sz);
 #pragma unroll
                 for (int c = 0; c < 3; ++c)
                     acc[(a * 3 + b) * 3 + c] += sz[c];
@@ -265,40 +338,81 @@ __device__ __forceinline__ bool load_quantities(const int64_t *__restrict__ m, c
 // All channels of one particle: sink(channel, acc) receives the 3^dim shares
 // of each channel in turn.  NARROW: every quantity m, m v_d, m C_de is below
 // 2^28 in magnitude (the declared ranges guarantee it), so every share and
-// every node's sum of up to four tensors' shares fits in 32 bits.
+// every node's sum of up to four tensors' shares fits in 32 bits, and the
+// biased 32-bit splits apply; otherwise 64-bit shares and 128-bit products.
+template <int DIM, bool HALF, class Sink>
+__device__ __forceinline__ void particle_shares_narrow(const AxisCoef (&ax)[DIM], int64_t mp,
+                                                       const int64_t (&vp)[DIM], const int64_t (&cp)[DIM][DIM],
+                                                       Sink &sink)
+{
+    constexpr int K = DIM == 3 ? 27 : 9;
+    BiasedAxis c[DIM];
+    c[0] = biased_axis<DIM, 0>(ax[0]);
+    c[1] = biased_axis<DIM, 1>(ax[1]);
+    if constexpr (DIM == 3)
+        c[2] = biased_axis<DIM, 2>(ax[2]);
+    uint32_t acc[K];
+    int32_t out[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+        acc[i] = 0u - kShareBias;
+    tensor_add_biased<DIM, 0, 0, 0, HALF>((int32_t)mp, c, acc);
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+        out[i] = (int32_t)acc[i];
+    sink(0, out);
+#pragma unroll 1
+    for (int d = 0; d < DIM; ++d) {
+#pragma unroll
+        for (int i = 0; i < K; ++i)
+            acc[i] = 0u - (uint32_t)(1 + DIM) * kShareBias;
+        // the products are below 2^28, so 32-bit multiplies are exact
+        const int32_t m32 = (int32_t)mp;
+        tensor_add_biased<DIM, 0, 0, 0, HALF>(m32 * (int32_t)vp[d], c, acc);
+        tensor_add_biased<DIM, 1, 0, 0, HALF>(m32 * (int32_t)cp[d][0], c, acc);
+        tensor_add_biased<DIM, 0, 1, 0, HALF>(m32 * (int32_t)cp[d][1], c, acc);
+        if constexpr (DIM == 3)
+            tensor_add_biased<DIM, 0, 0, 1, HALF>(m32 * (int32_t)cp[d][2], c, acc);
+#pragma unroll
+        for (int i = 0; i < K; ++i)
+            out[i] = (int32_t)acc[i];
+        sink(1 + d, out);
+    }
+}
+
 template <int DIM, bool NARROW, class Sink>
 __device__ __forceinline__ void particle_shares(const AxisCoef (&ax)[DIM], int64_t mp, const int64_t (&vp)[DIM],
                                                 const int64_t (&cp)[DIM][DIM], Sink &&sink)
 {
     constexpr int K = DIM == 3 ? 27 : 9;
-    using T = typename std::conditional<NARROW, int32_t, int64_t>::type;
-    using Axis = typename std::conditional<NARROW, NarrowAxis, AxisCoef>::type;
-    Axis c[DIM];
+    if constexpr (NARROW) {
+        bool half = false;
 #pragma unroll
-    for (int e = 0; e < DIM; ++e) {
-        if constexpr (NARROW)
-            c[e] = narrow_axis(ax[e]);
+        for (int e = 0; e < DIM; ++e)
+            half |= (ax[e].w0 >> 32) != 0;
+        if (__builtin_amdgcn_ballot_w64(half) != 0ull)
+            particle_shares_narrow<DIM, true>(ax, mp, vp, cp, sink);
         else
-            c[e] = ax[e];
-    }
-    T acc[K];
-#pragma unroll
-    for (int i = 0; i < K; ++i)
-        acc[i] = 0;
-    tensor_add<DIM, 0, 0, 0>((T)mp, c, acc);
-    sink(0, acc);
-#pragma unroll 1
-    for (int d = 0; d < DIM; ++d) {
+            particle_shares_narrow<DIM, false>(ax, mp, vp, cp, sink);
+    } else {
+        int64_t acc[K];
 #pragma unroll
         for (int i = 0; i < K; ++i)
             acc[i] = 0;
-        // (narrow: the products are below 2^28, so 32-bit multiplies are exact)
-        tensor_add<DIM, 0, 0, 0>((T)mp * (T)vp[d], c, acc);
-        tensor_add<DIM, 1, 0, 0>((T)mp * (T)cp[d][0], c, acc);
-        tensor_add<DIM, 0, 1, 0>((T)mp * (T)cp[d][1], c, acc);
-        if constexpr (DIM == 3)
-            tensor_add<DIM, 0, 0, 1>((T)mp * (T)cp[d][2], c, acc);
-        sink(1 + d, acc);
+        tensor_add<DIM, 0, 0, 0>(mp, ax, acc);
+        sink(0, acc);
+#pragma unroll 1
+        for (int d = 0; d < DIM; ++d) {
+#pragma unroll
+            for (int i = 0; i < K; ++i)
+                acc[i] = 0;
+            tensor_add<DIM, 0, 0, 0>(mp * vp[d], ax, acc);
+            tensor_add<DIM, 1, 0, 0>(mp * cp[d][0], ax, acc);
+            tensor_add<DIM, 0, 1, 0>(mp * cp[d][1], ax, acc);
+            if constexpr (DIM == 3)
+                tensor_add<DIM, 0, 0, 1>(mp * cp[d][2], ax, acc);
+            sink(1 + d, acc);
+        }
     }
 }
 
@@ -615,6 +729,8 @@ __device__ __forceinline__ int64_t item_tile(const uint64_t *__restrict__ start,
     return lo;
 }
 
+typedef __attribute__((address_space(3))) unsigned long long lds_u64;
+
 template <int DIM, bool NARROW>
 __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n, int64_t tx, int64_t tiles, int sshift,
                                                               const IsRec<NARROW> *__restrict__ rec,
@@ -690,23 +806,31 @@ __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n,
             for (int e = 0; e < DIM; ++e)
                 lb[e] = (int)(base[e] - origin[e]);
             particle_shares<DIM, NARROW>(ax, mp, vp, cp, [&](int ch, const auto &acc) {
+                // the stencil's first node in the block, formed once: its 27
+                // (9) nodes are fixed offsets from it, which the LDS atomics
+                // carry as immediates (left to itself the compiler rebuilds
+                // the address inside every conditional add)
+                lds_u64 *nb = (lds_u64 *)&block[DIM == 3 ? ((ch * B + lb[DIM - 1]) * B + lb[1]) * B + lb[0]
+                                                         : (ch * B + lb[1]) * B + lb[0]];
+                asm volatile("" : "+v"(nb));
 #pragma unroll
                 for (int a = 0; a < 3; ++a)
 #pragma unroll
                     for (int b = 0; b < 3; ++b)
 #pragma unroll
                         for (int c = 0; c < (DIM == 3 ? 3 : 1); ++c) {
-                            int idx;
+                            int off;
                             int64_t sh;      // a 32-bit share widened with its sign
                             if constexpr (DIM == 3) {
-                                idx = ((ch * B + lb[2] + c) * B + lb[1] + b) * B + lb[0] + a;
+                                off = (c * B + b) * B + a;
                                 sh = acc[(a * 3 + b) * 3 + c];
                             } else {
-                                idx = (ch * B + lb[1] + b) * B + lb[0] + a;
+                                off = b * B + a;
                                 sh = acc[a * 3 + b];
                             }
                             if (sh != 0)
-                                atomicAdd(&block[idx], (unsigned long long)sh);
+                                __hip_atomic_fetch_add(nb + off, (unsigned long long)sh, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_WORKGROUP);
                         }
             });
         }
@@ -741,12 +865,12 @@ __global__ void __launch_bounds__(kIsThreads) is_tiled_kernel(int64_t np, int n,
 // The narrow path needs every split quantity m, m v_d, m C_de below 2^28 in
 // magnitude: max_mass * max(1, max_speed, max_affine) < 2^28 (particles
 // beyond the declared ranges are skipped).  A share of q is then at most
-// 1.25 |q| + 3 in magnitude (a first-moment split's outer shares are at most
-// 3/4 and 1/2 of q, rounded, the middle one their negated sum; a weight
-// split's shares at most q + 1 each), and a node's sum over the four tensors
-// of a momentum channel at most 4.75 * 2^28 + 12 < 2^31: 32-bit values and
-// sums throughout, and products of 29 by 49 bits in two 32 x 32 -> 64-bit
-// multiply-adds.
+// 3/4 |q| + 1 in magnitude (the weights are at most 3/4, the first moments
+// at most 1/4 in magnitude, and a near share adds the two roundings of the
+// outer ones), so the values entering each axis' splits stay below 2^28 + 2
+// and a node's sum over the four tensors of a momentum channel below
+// 4 (2^28 + 3) < 2^31: 32-bit values and sums throughout, and products of
+// 29 by 49 bits in two 32 x 32 -> 64-bit multiply-adds.
 bool narrow_ranges(int64_t max_mass, int64_t max_speed, int64_t max_affine)
 {
     int64_t f = max_speed > max_affine ? max_speed : max_affine;

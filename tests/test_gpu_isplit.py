@@ -100,6 +100,10 @@ def test_narrow_limit_signs_and_ties(mpm, oracle_lib, path):
     h["m"][::7] *= -1
     h["X"][0, :500] = (h["X"][0, :500] & ~0xFFFF) | 0x8000           # ties on x
     h["X"][1, 500:1000] &= ~0xFFFF                                    # on nodes in y
+    # half a cell from a node in y or z (a weight of exactly one half) for a
+    # few particles scattered among the others
+    h["X"][1, 1000::97] = (h["X"][1, 1000::97] & ~0xFFFF) | 0x8000
+    h["X"][2, 1001::89] = (h["X"][2, 1001::89] & ~0xFFFF) | 0x8000
     assert int(np.abs(h["m"]).max()) == lim
     ref, rst = oracle_lib.p2g_isplit(3, 24, h)
     assert rst.tolist() == [0, 0, 0, 0]
