@@ -490,6 +490,22 @@ int mpm_neohookean_affine(const mpm_grid_desc *grid, const mpm_particles *partic
 int mpm_update_deformation(const mpm_grid_desc *grid, const mpm_particles *particles, float *F, float dt,
                            hipStream_t stream);
 
+/* The two per-particle passes of the same part of the guide that sit between
+ * one substep's G2P and the next substep's binning, in one pass: F is updated
+ * exactly as mpm_update_deformation does, then C_out receives C' exactly as
+ * mpm_neohookean_affine computes it from the updated F and the particles' C
+ * (the same float32 and float64 operations in the same order, so the results
+ * are bit-identical to those two calls in sequence; C, F, m and vol0 are read
+ * once).  dt is the substep's time step, used for both.
+ * particles: device; C and m read.  F: device float[dim*dim][n], read and
+ * written.  vol0: device float[n].  C_out: device float[dim*dim][n], written
+ * (may alias neither C nor F).  status[0] counts particles whose updated F
+ * has det <= 0 (their C' = C).
+ * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
+int mpm_update_deformation_stress(const mpm_grid_desc *grid, const mpm_particles *particles, float *F,
+                                  const float *vol0, float dt, float mu, float lambda, float *C_out, uint32_t *status,
+                                  hipStream_t stream);
+
 /* ---- Position-based MPM (PB-MPM): the iteration loop for an elastic material ----
  *
  * "Implementation -- GPU Optimization & Reference Codebases", section 3.3.2.

@@ -55,7 +55,7 @@ EXPORTS = ("mpm_version", "mpm_strerror", "mpm_check_bounds", "mpm_workspace_byt
            "mpm_grid_update", "mpm_grid_clear", "mpm_g2p", "mpm_neohookean_affine", "mpm_update_deformation",
            "mpm_bin_resident", "mpm_g2p2g", "mpm_grid_clear_tiles", "mpm_gather_records",
            "mpm_p2g_isplit_noalloc", "mpm_pbmpm_project_elastic", "mpm_pbmpm_grid_update", "mpm_pbmpm_integrate",
-           "mpm_grid_update_tiles", "mpm_g2p_records")
+           "mpm_grid_update_tiles", "mpm_g2p_records", "mpm_update_deformation_stress")
 
 _lib = None
 
@@ -110,6 +110,10 @@ def lib() -> ct.CDLL:
                                             ct.c_float, ct.c_float, ct.c_void_p, ct.c_void_p, ct.c_void_p]
         L.mpm_update_deformation.restype = ct.c_int
         L.mpm_update_deformation.argtypes = [P(mpm_grid_desc), P(mpm_particles), ct.c_void_p, ct.c_float, ct.c_void_p]
+        L.mpm_update_deformation_stress.restype = ct.c_int
+        L.mpm_update_deformation_stress.argtypes = [P(mpm_grid_desc), P(mpm_particles), ct.c_void_p, ct.c_void_p,
+                                                    ct.c_float, ct.c_float, ct.c_float, ct.c_void_p, ct.c_void_p,
+                                                    ct.c_void_p]
         L.mpm_bin_resident.restype = ct.c_int
         L.mpm_bin_resident.argtypes = [P(mpm_grid_desc), P(mpm_particles), ct.c_void_p, ct.c_size_t, ct.c_void_p,
                                        ct.c_void_p]
@@ -309,6 +313,13 @@ def mpm_neohookean_affine(desc, parts: mpm_particles, F, vol0, dt: float, mu: fl
 def mpm_update_deformation(desc, parts: mpm_particles, F, dt: float, stream=None) -> None:
     _check(lib().mpm_update_deformation(ct.byref(desc), ct.byref(parts), _ptr(F), dt, _stream(stream)),
            "mpm_update_deformation")
+
+
+def mpm_update_deformation_stress(desc, parts: mpm_particles, F, vol0, dt: float, mu: float, lam: float, C_out,
+                                  status, stream=None) -> None:
+    _check(lib().mpm_update_deformation_stress(ct.byref(desc), ct.byref(parts), _ptr(F), _ptr(vol0), dt, mu, lam,
+                                               _ptr(C_out), _ptr(status), _stream(stream)),
+           "mpm_update_deformation_stress")
 
 
 def mpm_pbmpm_project_elastic(desc, parts: mpm_particles, F, relax: float, polar_iters: int, status,

@@ -6,6 +6,7 @@
 #include <atomic>
 
 #include "resident.hpp"
+#include "stress.hpp"
 
 namespace mpmk {
 
@@ -566,6 +567,23 @@ int mpm_update_deformation(const mpm_grid_desc *grid, const mpm_particles *parti
     if (particles->n > 0 && (!particles->C || !F || !aligned(particles->C, 4) || !aligned(F, 4)))
         return MPM_ERR_INVALID;
     return hip_status(launch_update_F(grid->dim, particles->n, particles->C, F, dt, stream));
+}
+
+int mpm_update_deformation_stress(const mpm_grid_desc *grid, const mpm_particles *particles, float *F,
+                                  const float *vol0, float dt, float mu, float lambda, float *C_out, uint32_t *status,
+                                  hipStream_t stream)
+{
+    if (check_desc(grid) != MPM_OK || !particles || particles->n < 0 || particles->n > kMaxParticles)
+        return MPM_ERR_INVALID;
+    const int64_t np = particles->n;
+    if (np > 0 && (!particles->C || !particles->m || !F || !vol0 || !C_out || !aligned(particles->C, 4) ||
+                   !aligned(particles->m, 4) || !aligned(F, 4) || !aligned(vol0, 4) || !aligned(C_out, 4) ||
+                   C_out == particles->C || C_out == F))
+        return MPM_ERR_INVALID;
+    if (!aligned(status, 4) || !(dt >= 0.0f) || !(mu >= 0.0f) || !(lambda >= 0.0f))
+        return MPM_ERR_INVALID;
+    return hip_status(launch_update_F_stress(grid->dim, grid->n, np, particles->C, F, particles->m, vol0, dt, mu,
+                                             lambda, C_out, status, stream));
 }
 
 int mpm_pbmpm_project_elastic(const mpm_grid_desc *grid, const mpm_particles *particles, const float *F, float relax,

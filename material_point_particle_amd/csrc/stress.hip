@@ -14,11 +14,122 @@
 //
 // Both passes are one thread per particle over component-major arrays
 // (coalesced); they are HBM-bound.  The stress is formed in float64 in a fixed
-// order and each C' entry is rounded to float32 once.
-#include "common.hpp"
+// order and each C' entry is rounded to float32 once.  In a substep loop the
+// F update and the next substep's C' can run as one pass (the same
+// arithmetic, C and F read once).
+#include "stress.hpp"
 
 namespace mpmk {
 namespace {
+
+// C' of one particle from its F (float32, as stored) and C: the Neo-Hookean
+// stress formed in float64 in a fixed order, each entry rounded to float32
+// once.  Returns true when det F <= 0 (C' = C, counted by the caller).
+template <int DIM>
+__device__ __forceinline__ bool stressed_affine(const float (&fs)[DIM][DIM], const float (&c)[DIM][DIM], float mp,
+                                                float vol, double scale, float dt, float mu, float lambda,
+                                                float (&out)[DIM][DIM])
+{
+    double f[DIM][DIM], cof[DIM][DIM];
+#pragma unroll
+    for (int d = 0; d < DIM; ++d)
+#pragma unroll
+        for (int e = 0; e < DIM; ++e)
+            f[d][e] = (double)fs[d][e];
+    double J;
+    if constexpr (DIM == 3) {
+        cof[0][0] = f[1][1] * f[2][2] - f[1][2] * f[2][1];
+        cof[0][1] = f[1][2] * f[2][0] - f[1][0] * f[2][2];
+        cof[0][2] = f[1][0] * f[2][1] - f[1][1] * f[2][0];
+        cof[1][0] = f[0][2] * f[2][1] - f[0][1] * f[2][2];
+        cof[1][1] = f[0][0] * f[2][2] - f[0][2] * f[2][0];
+        cof[1][2] = f[0][1] * f[2][0] - f[0][0] * f[2][1];
+        cof[2][0] = f[0][1] * f[1][2] - f[0][2] * f[1][1];
+        cof[2][1] = f[0][2] * f[1][0] - f[0][0] * f[1][2];
+        cof[2][2] = f[0][0] * f[1][1] - f[0][1] * f[1][0];
+        J = (f[0][0] * cof[0][0] + f[0][1] * cof[0][1]) + f[0][2] * cof[0][2];
+    } else {
+        cof[0][0] = f[1][1];
+        cof[0][1] = -f[1][0];
+        cof[1][0] = -f[0][1];
+        cof[1][1] = f[0][0];
+        J = f[0][0] * f[1][1] - f[0][1] * f[1][0];
+    }
+    const bool inverted = !(J > 0.0);
+#pragma unroll
+    for (int d = 0; d < DIM; ++d)
+#pragma unroll
+        for (int e = 0; e < DIM; ++e)
+            out[d][e] = c[d][e];
+    if (!inverted && mp != 0.0f) {
+        const double llj = (double)lambda * log(J);
+        double P[DIM][DIM];
+#pragma unroll
+        for (int d = 0; d < DIM; ++d)
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                const double fit = cof[d][e] / J;                   // (F^-T)_de
+                P[d][e] = (double)mu * (f[d][e] - fit) + llj * fit;
+            }
+        const double k = (((double)dt * (double)vol) * scale) / (double)mp;
+#pragma unroll
+        for (int d = 0; d < DIM; ++d)
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                double tau = 0.0;                                   // (P F^T)_de
+#pragma unroll
+                for (int q = 0; q < DIM; ++q)
+                    tau = tau + P[d][q] * f[e][q];
+                out[d][e] = (float)((double)c[d][e] - k * tau);
+            }
+    }
+    return inverted;
+}
+
+// F <- (I + dt C) F of one particle: G_dq = [d == q] + dt C_dq,
+// F'_de = sum_q G_dq F_qe in order q = 0, 1, 2, all float32.
+template <int DIM>
+__device__ __forceinline__ void updated_F(const float (&c)[DIM][DIM], float dt, float (&f)[DIM][DIM])
+{
+    float G[DIM][DIM], g[DIM][DIM];
+#pragma unroll
+    for (int d = 0; d < DIM; ++d)
+#pragma unroll
+        for (int q = 0; q < DIM; ++q) {
+            G[d][q] = (d == q ? 1.0f : 0.0f) + dt * c[d][q];
+            g[d][q] = f[d][q];
+        }
+#pragma unroll
+    for (int d = 0; d < DIM; ++d)
+#pragma unroll
+        for (int e = 0; e < DIM; ++e) {
+            float t = G[d][0] * g[0][e];
+#pragma unroll
+            for (int q = 1; q < DIM; ++q)
+                t = t + G[d][q] * g[q][e];
+            f[d][e] = t;
+        }
+}
+
+template <int DIM>
+__device__ __forceinline__ void load_mat(const float *__restrict__ a, int64_t np, int64_t p, float (&m)[DIM][DIM])
+{
+#pragma unroll
+    for (int d = 0; d < DIM; ++d)
+#pragma unroll
+        for (int e = 0; e < DIM; ++e)
+            m[d][e] = a[(int64_t)(d * DIM + e) * np + p];
+}
+
+template <int DIM>
+__device__ __forceinline__ void store_mat(float *__restrict__ a, int64_t np, int64_t p, const float (&m)[DIM][DIM])
+{
+#pragma unroll
+    for (int d = 0; d < DIM; ++d)
+#pragma unroll
+        for (int e = 0; e < DIM; ++e)
+            a[(int64_t)(d * DIM + e) * np + p] = m[d][e];
+}
 
 template <int DIM>
 __global__ void __launch_bounds__(256) neohookean_affine_kernel(int64_t np, double scale, const float *__restrict__ F,
@@ -29,98 +140,47 @@ __global__ void __launch_bounds__(256) neohookean_affine_kernel(int64_t np, doub
                                                                 uint32_t *__restrict__ status)
 {
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
-        double f[DIM][DIM], cof[DIM][DIM];
-        float c[DIM][DIM];
-#pragma unroll
-        for (int d = 0; d < DIM; ++d)
-#pragma unroll
-            for (int e = 0; e < DIM; ++e) {
-                f[d][e] = (double)F[(int64_t)(d * DIM + e) * np + p];
-                c[d][e] = C[(int64_t)(d * DIM + e) * np + p];
-            }
-        double J;
-        if constexpr (DIM == 3) {
-            cof[0][0] = f[1][1] * f[2][2] - f[1][2] * f[2][1];
-            cof[0][1] = f[1][2] * f[2][0] - f[1][0] * f[2][2];
-            cof[0][2] = f[1][0] * f[2][1] - f[1][1] * f[2][0];
-            cof[1][0] = f[0][2] * f[2][1] - f[0][1] * f[2][2];
-            cof[1][1] = f[0][0] * f[2][2] - f[0][2] * f[2][0];
-            cof[1][2] = f[0][1] * f[2][0] - f[0][0] * f[2][1];
-            cof[2][0] = f[0][1] * f[1][2] - f[0][2] * f[1][1];
-            cof[2][1] = f[0][2] * f[1][0] - f[0][0] * f[1][2];
-            cof[2][2] = f[0][0] * f[1][1] - f[0][1] * f[1][0];
-            J = (f[0][0] * cof[0][0] + f[0][1] * cof[0][1]) + f[0][2] * cof[0][2];
-        } else {
-            cof[0][0] = f[1][1];
-            cof[0][1] = -f[1][0];
-            cof[1][0] = -f[0][1];
-            cof[1][1] = f[0][0];
-            J = f[0][0] * f[1][1] - f[0][1] * f[1][0];
-        }
-        const bool inverted = !(J > 0.0);
+        float f[DIM][DIM], c[DIM][DIM], out[DIM][DIM];
+        load_mat<DIM>(F, np, p, f);
+        load_mat<DIM>(C, np, p, c);
+        const bool inverted = stressed_affine<DIM>(f, c, m[p], vol0[p], scale, dt, mu, lambda, out);
         wave_count(inverted, &status[0]);
-        float out[DIM][DIM];
-#pragma unroll
-        for (int d = 0; d < DIM; ++d)
-#pragma unroll
-            for (int e = 0; e < DIM; ++e)
-                out[d][e] = c[d][e];
-        const float mp = m[p];
-        if (!inverted && mp != 0.0f) {
-            const double llj = (double)lambda * log(J);
-            double P[DIM][DIM];
-#pragma unroll
-            for (int d = 0; d < DIM; ++d)
-#pragma unroll
-                for (int e = 0; e < DIM; ++e) {
-                    const double fit = cof[d][e] / J;                   // (F^-T)_de
-                    P[d][e] = (double)mu * (f[d][e] - fit) + llj * fit;
-                }
-            const double k = (((double)dt * (double)vol0[p]) * scale) / (double)mp;
-#pragma unroll
-            for (int d = 0; d < DIM; ++d)
-#pragma unroll
-                for (int e = 0; e < DIM; ++e) {
-                    double tau = 0.0;                                   // (P F^T)_de
-#pragma unroll
-                    for (int q = 0; q < DIM; ++q)
-                        tau = tau + P[d][q] * f[e][q];
-                    out[d][e] = (float)((double)c[d][e] - k * tau);
-                }
-        }
-#pragma unroll
-        for (int d = 0; d < DIM; ++d)
-#pragma unroll
-            for (int e = 0; e < DIM; ++e)
-                Cout[(int64_t)(d * DIM + e) * np + p] = out[d][e];
+        store_mat<DIM>(Cout, np, p, out);
     }
 }
 
-// F <- (I + dt C) F: G_dq = [d == q] + dt C_dq, F'_de = sum_q G_dq F_qe in
-// order q = 0, 1, 2, all float32.
 template <int DIM>
 __global__ void __launch_bounds__(256) update_F_kernel(int64_t np, const float *__restrict__ C, float *__restrict__ F,
                                                        float dt)
 {
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
-        float G[DIM][DIM], f[DIM][DIM];
-#pragma unroll
-        for (int d = 0; d < DIM; ++d)
-#pragma unroll
-            for (int q = 0; q < DIM; ++q) {
-                G[d][q] = (d == q ? 1.0f : 0.0f) + dt * C[(int64_t)(d * DIM + q) * np + p];
-                f[d][q] = F[(int64_t)(d * DIM + q) * np + p];
-            }
-#pragma unroll
-        for (int d = 0; d < DIM; ++d)
-#pragma unroll
-            for (int e = 0; e < DIM; ++e) {
-                float t = G[d][0] * f[0][e];
-#pragma unroll
-                for (int q = 1; q < DIM; ++q)
-                    t = t + G[d][q] * f[q][e];
-                F[(int64_t)(d * DIM + e) * np + p] = t;
-            }
+        float f[DIM][DIM], c[DIM][DIM];
+        load_mat<DIM>(C, np, p, c);
+        load_mat<DIM>(F, np, p, f);
+        updated_F<DIM>(c, dt, f);
+        store_mat<DIM>(F, np, p, f);
+    }
+}
+
+// The two passes of one particle in one: F updated with the new C, then C'
+// of the next substep from the updated F and the same C (C, F, m and vol0
+// read once; F and C' written).
+template <int DIM>
+__global__ void __launch_bounds__(256) update_F_stress_kernel(int64_t np, double scale, const float *__restrict__ C,
+                                                              float *__restrict__ F, const float *__restrict__ m,
+                                                              const float *__restrict__ vol0, float dt, float mu,
+                                                              float lambda, float *__restrict__ Cout,
+                                                              uint32_t *__restrict__ status)
+{
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
+        float f[DIM][DIM], c[DIM][DIM], out[DIM][DIM];
+        load_mat<DIM>(C, np, p, c);
+        load_mat<DIM>(F, np, p, f);
+        updated_F<DIM>(c, dt, f);
+        store_mat<DIM>(F, np, p, f);
+        const bool inverted = stressed_affine<DIM>(f, c, m[p], vol0[p], scale, dt, mu, lambda, out);
+        wave_count(inverted, &status[0]);
+        store_mat<DIM>(Cout, np, p, out);
     }
 }
 
@@ -145,6 +205,22 @@ hipError_t launch_neohookean_affine(int dim, int n, int64_t np, const float *F, 
                            vol0, dt, mu, lambda, Cout, status);
     else
         hipLaunchKernelGGL(neohookean_affine_kernel<2>, dim3(stress_blocks(np)), dim3(256), 0, s, np, scale, F, C, m,
+                           vol0, dt, mu, lambda, Cout, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_update_F_stress(int dim, int n, int64_t np, const float *C, float *F, const float *m,
+                                  const float *vol0, float dt, float mu, float lambda, float *Cout, uint32_t *status,
+                                  hipStream_t s)
+{
+    if (np == 0)
+        return hipSuccess;
+    const double scale = 4.0 * (double)n * (double)n;
+    if (dim == 3)
+        hipLaunchKernelGGL(update_F_stress_kernel<3>, dim3(stress_blocks(np)), dim3(256), 0, s, np, scale, C, F, m,
+                           vol0, dt, mu, lambda, Cout, status);
+    else
+        hipLaunchKernelGGL(update_F_stress_kernel<2>, dim3(stress_blocks(np)), dim3(256), 0, s, np, scale, C, F, m,
                            vol0, dt, mu, lambda, Cout, status);
     return hipGetLastError();
 }

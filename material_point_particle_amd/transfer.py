@@ -54,6 +54,10 @@ class ElasticParticles(DeviceParticles):
     def update_F(self, tr: "Transfer", dt: float) -> None:
         L.mpm_update_deformation(tr.desc, self.desc(), self.F, dt)
 
+    def update_F_stress(self, tr: "Transfer", dt: float, mu: float, lam: float) -> None:
+        """update_F, then stress() for the next substep, in one pass."""
+        L.mpm_update_deformation_stress(tr.desc, self.desc(), self.F, self.vol0, dt, mu, lam, self.C_aff, tr.status)
+
     def host(self) -> dict:
         h = super().host()
         h["F"] = self.F.cpu().numpy()

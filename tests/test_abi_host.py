@@ -235,6 +235,16 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert lib.mpm_neohookean_affine(None, ct.byref(p4), *ok, None) == L.MPM_ERR_INVALID
     assert lib.mpm_update_deformation(ct.byref(d), ct.byref(p3), ct.c_void_p(4096), 1e-4, None) == L.MPM_ERR_INVALID
     assert lib.mpm_update_deformation(ct.byref(d), ct.byref(p4), None, 1e-4, None) == L.MPM_ERR_INVALID
+    # F, vol0, dt, mu, lambda, C_out, status: one fault per call
+    okf = (ct.c_void_p(8192), ct.c_void_p(12288), 1e-4, 1e5, 1e5, ct.c_void_p(16384), status)
+    fused = lib.mpm_update_deformation_stress
+    assert fused(ct.byref(d), ct.byref(p3), *okf, None) == L.MPM_ERR_INVALID                       # no C
+    assert fused(ct.byref(d), ct.byref(p4), None, *okf[1:], None) == L.MPM_ERR_INVALID             # no F
+    assert fused(ct.byref(d), ct.byref(p4), ct.c_void_p(8194), *okf[1:], None) == L.MPM_ERR_INVALID
+    assert fused(ct.byref(d), ct.byref(p4), *okf[:4], -1.0, *okf[5:], None) == L.MPM_ERR_INVALID
+    assert fused(ct.byref(d), ct.byref(p4), *okf[:5], ct.c_void_p(4096), status, None) == L.MPM_ERR_INVALID  # C' = C
+    assert fused(ct.byref(d), ct.byref(p4), *okf[:5], ct.c_void_p(8192), status, None) == L.MPM_ERR_INVALID  # C' = F
+    assert fused(None, ct.byref(p4), *okf, None) == L.MPM_ERR_INVALID
 
 
 def test_noalloc_isplit_refuses_inputs_past_its_static_scratch():

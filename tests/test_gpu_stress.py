@@ -99,12 +99,51 @@ def test_update_F_bit_exact(mpm, oracle_lib, dim):
     assert np.array_equal(parts.F.cpu().numpy(), ref)
 
 
-def test_elastic_substeps_match_oracle(mpm, oracle_lib):
+@pytest.mark.parametrize("dim", [2, 3])
+def test_fused_update_and_stress_equals_the_two_calls(mpm, oracle_lib, dim):
+    """mpm_update_deformation_stress against mpm_update_deformation followed
+    by mpm_neohookean_affine on the same inputs: F and C' bit-identical, the
+    same status count; against the oracle, F bit-exact and C' within one
+    float32 ulp (float64 log).  Some particles are inverted after the update
+    (det F <= 0 keeps C), some massless."""
+    from material_point_particle_amd.transfer import ElasticParticles, Transfer
+    np_ = 70_001
+    host, F, vol0 = random_solid(dim, np_, 41 + dim, inverted=23)
+    host["C"] *= 30.0                            # large enough that dt C moves F visibly
+    dt, mu, lam = 2e-3, 2.0e8, 3.0e8
+    n = 64
+    say("fused F update and stress", dim, np_)
+    sep = ElasticParticles(host, F, vol0)
+    fus = ElasticParticles(host, F, vol0)
+    tr_s = Transfer(dim, n, 24, (2.0, 10.0, 1e6), np_)
+    tr_f = Transfer(dim, n, 24, (2.0, 10.0, 1e6), np_)
+    sep.update_F(tr_s, dt)
+    sep.stress(tr_s, dt, mu, lam)
+    fus.update_F_stress(tr_f, dt, mu, lam)
+    torch.cuda.synchronize()
+    F_sep, F_fus = sep.F.cpu().numpy(), fus.F.cpu().numpy()
+    c_sep, c_fus = sep.C_aff.cpu().numpy(), fus.C_aff.cpu().numpy()
+    assert np.array_equal(F_fus.view(np.uint32), F_sep.view(np.uint32))
+    assert np.array_equal(c_fus.view(np.uint32), c_sep.view(np.uint32))
+    st = tr_f.status.cpu().numpy().view(np.uint32).tolist()
+    assert st == tr_s.status.cpu().numpy().view(np.uint32).tolist() and st[0] >= 23
+    F_ref = F.copy()
+    oracle_lib.update_F(dim, host["C"], F_ref, dt)
+    assert np.array_equal(F_fus, F_ref)
+    ref, ref_st = oracle_lib.neohookean_affine(dim, n, host, F_ref, vol0, dt, mu, lam)
+    assert_close_ulp(c_fus, ref, "C'")
+    assert ref_st.tolist() == st
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_elastic_substeps_match_oracle(mpm, oracle_lib, fused):
     """An elastic cube thrown at the floor (32,768 particles, 64^3 nodes): the
     substep stress -> bin -> P2G (with C') -> restricted grid update -> G2P ->
-    F update on the GPU.  At every 10th substep the oracle recomputes that
-    substep from the GPU's state before it: C' within one ulp (float64 log);
-    given the GPU's C', the P2G grid, the particle state and F bit-exact."""
+    F update on the GPU (fused: the F update and the next substep's stress in
+    one call after G2P, the first substep's stress on its own).  At every 10th
+    substep the oracle recomputes that substep from the GPU's state before it:
+    C' within one ulp (float64 log); given the GPU's C', the P2G grid, the
+    particle state and F bit-exact."""
     from material_point_particle_amd.transfer import ElasticParticles, Transfer
     w = WORKLOADS["jelly_3d_64"]
     ex = w.extra
@@ -118,7 +157,8 @@ def test_elastic_substeps_match_oracle(mpm, oracle_lib):
         if check:
             torch.cuda.synchronize()
             before = parts.host()
-        parts.stress(tr, ex["dt"], ex["mu"], ex["lam"])
+        if not fused or k == 1:
+            parts.stress(tr, ex["dt"], ex["mu"], ex["lam"])
         tr.bin(parts.affine())
         tr.p2g(parts.affine(), binned=True)
         if check:
@@ -127,12 +167,15 @@ def test_elastic_substeps_match_oracle(mpm, oracle_lib):
             grid = tr.grid.cpu().numpy()
         tr.grid_update(ex["dt"], ex["gravity"], ex["sticky"], active=True)
         tr.g2p(parts, ex["dt"])
-        parts.update_F(tr, ex["dt"])
+        if fused:
+            parts.update_F_stress(tr, ex["dt"], ex["mu"], ex["lam"])
+        else:
+            parts.update_F(tr, ex["dt"])
         if not check:
             continue
         torch.cuda.synchronize()
         after = parts.host()
-        say("elastic substep", k)
+        say("elastic substep", k, "fused" if fused else "")
         ref_c, _ = oracle_lib.neohookean_affine(3, w.n, before, before["F"], host["vol"], ex["dt"], ex["mu"],
                                                 ex["lam"])
         assert_close_ulp(c_aff, ref_c, f"C' at substep {k}")
@@ -158,9 +201,11 @@ def test_elastic_substeps_match_oracle(mpm, oracle_lib):
 @pytest.mark.timeout(900)
 def test_elastic_full_size_checked_substeps(mpm, oracle_lib):
     """The benchmark's elastic workload at full size (8M-particle jelly cube,
-    256^3 nodes): 12 substeps on the GPU; substeps 6 and 12 are recomputed by
-    the oracle from the GPU state before them: C' within one float32 ulp, and
-    given the GPU's C', the P2G grid, the particles and F bit-exact."""
+    256^3 nodes) in the benchmark's loop (the F update fused with the next
+    substep's stress): 12 substeps on the GPU; substeps 6 and 12 are
+    recomputed by the oracle from the GPU state before them: C' within one
+    float32 ulp, and given the GPU's C', the P2G grid, the particles and F
+    bit-exact."""
     from material_point_particle_amd.transfer import ElasticParticles, Transfer
     w = WORKLOADS["jelly_3d_256"]
     ex = w.extra
@@ -175,7 +220,8 @@ def test_elastic_full_size_checked_substeps(mpm, oracle_lib):
         if check:
             torch.cuda.synchronize()
             before = parts.host()
-        parts.stress(tr, ex["dt"], ex["mu"], ex["lam"])
+        if k == 1:
+            parts.stress(tr, ex["dt"], ex["mu"], ex["lam"])
         tr.bin(parts.affine())
         tr.p2g(parts.affine(), binned=True)
         if check:
@@ -184,7 +230,7 @@ def test_elastic_full_size_checked_substeps(mpm, oracle_lib):
             grid = tr.grid.cpu().numpy()
         tr.grid_update(ex["dt"], ex["gravity"], ex["sticky"], active=True)
         tr.g2p(parts, ex["dt"])
-        parts.update_F(tr, ex["dt"])
+        parts.update_F_stress(tr, ex["dt"], ex["mu"], ex["lam"])
         if not check:
             continue
         torch.cuda.synchronize()
