@@ -29,6 +29,8 @@ def test_library_exports_every_declared_entry_point():
     for name in names:
         assert hasattr(lib, name), name
         assert ct.cast(getattr(lib, name), ct.c_void_p).value
+        # and the package's binding carries a wrapper of the same name
+        assert callable(getattr(M, name, None)), name
 
 
 def test_version_and_errors():
