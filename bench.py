@@ -344,12 +344,13 @@ def measure_elastic(args, torch, w, build, Transfer):
 
 def measure_pbmpm(args, torch, w, build):
     """The position-based MPM substep (elastic material) on the 8M-particle
-    jelly cube at 256^3: per substep 5 iterations of the elastic projection,
-    binning, P2G, displacement-form grid update and G2P gather, then the
-    integrate step and F <- (I + D) F, timed per stage with HIP events over
-    the evolving state.  Algorithmic bytes of the per-particle passes: the
-    projection reads F and D and writes D (108 B per particle), the integrate
-    step reads and writes x and d (48 B)."""
+    jelly cube at 256^3: per substep 5 iterations of binning, P2G,
+    displacement-form grid update and G2P gather, each iteration opened by
+    the elastic projection (the first on its own, the others in the previous
+    iteration's gather pass, mpm_pbmpm_g2p_project), then the integrate step
+    and F <- (I + D) F, timed per stage with HIP events over the evolving
+    state.  The projection is float64 ALU work (108 B per particle: F and D
+    read, D written); the integrate step reads and writes x and d (48 B)."""
     import material_point_particle_amd._lib as L
     from material_point_particle_amd.transfer import ElasticParticles, PBMPMSubsteps, Transfer
     host = build(w)
@@ -360,31 +361,33 @@ def measure_pbmpm(args, torch, w, build):
     loop = PBMPMSubsteps(tr, parts, ex["dt"], ex["gravity"], ex["iterations"], ex["relax"], ex["polar_iters"],
                          ex["band"])
     stream = torch.cuda.current_stream()
-    names = ("project", "bin", "p2g", "grid_update", "g2p")
-    steps = (lambda: L.mpm_pbmpm_project_elastic(tr.desc, parts.desc(), parts.F, loop.relax, loop.polar_iters,
-                                                 tr.status),
-             lambda: tr.bin(parts),
-             lambda: tr.p2g(parts, binned=True),
-             lambda: L.mpm_pbmpm_grid_update(tr.desc, tr.ws, tr.grid, tr.vg, loop.band),
-             lambda: tr.g2p(parts, 0.0))
+    names = ("project", "bin", "p2g", "grid_update", "g2p_project", "g2p")
+    calls = {"project": loop.project,
+             "bin": lambda: tr.bin(parts),
+             "p2g": lambda: tr.p2g(parts, binned=True),
+             "grid_update": lambda: L.mpm_pbmpm_grid_update(tr.desc, tr.ws, tr.grid, tr.vg, loop.band),
+             "g2p_project": loop.gather_project,
+             "g2p": lambda: tr.g2p(parts, 0.0)}
+    last = loop.iterations - 1
+    order = ["project"]
+    for it in range(loop.iterations):
+        order += ["bin", "p2g", "grid_update", "g2p_project" if it < last else "g2p"]
 
     def substep(ev=None):
-        for it in range(loop.iterations):
-            for i, f in enumerate(steps):
-                if ev:
-                    ev[it][i].record(stream)
-                f()
+        for i, nm in enumerate(order):
+            if ev:
+                ev[i].record(stream)
+            calls[nm]()
         if ev:
-            ev[loop.iterations][0].record(stream)
+            ev[len(order)].record(stream)
         loop.integrate()
         if ev:
-            ev[loop.iterations][1].record(stream)
+            ev[len(order) + 1].record(stream)
 
     substep()
     torch.cuda.synchronize()
     k = max(3, args.substeps // 4)
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(loop.iterations + 1)]
-              for _ in range(k)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 2)] for _ in range(k)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(k):
@@ -392,34 +395,32 @@ def measure_pbmpm(args, torch, w, build):
     stop.record(stream)
     torch.cuda.synchronize()
     total = start.elapsed_time(stop) / k
-    st = np.zeros(len(names))
+    st = dict.fromkeys(names, 0.0)
     integ = 0.0
     for ev in events:
-        for it in range(loop.iterations):
-            nxt = ev[it + 1][0]
-            marks = ev[it] + [nxt]
-            for i in range(len(names)):
-                st[i] += marks[i].elapsed_time(marks[i + 1])
-        integ += ev[loop.iterations][0].elapsed_time(ev[loop.iterations][1])
-    st /= k
+        for i, nm in enumerate(order):
+            st[nm] += ev[i].elapsed_time(ev[i + 1])
+        integ += ev[len(order)].elapsed_time(ev[len(order) + 1])
+    st = {nm: t / k for nm, t in st.items()}
     integ /= k
     status = tr.status.cpu().numpy().view(np.uint32).tolist()
-    log(f"pbmpm substeps: {total:.3f} ms (" + ", ".join(f"{nm} {t:.3f}" for nm, t in zip(names, st)) +
+    log(f"pbmpm substeps: {total:.3f} ms (" + ", ".join(f"{nm} {t:.3f}" for nm, t in st.items()) +
         f", integrate {integ:.3f}; {loop.iterations} iterations)")
 
     def gbs(b, t):
         return round(b / (t * 1e-3) / 1e9, 1)
 
-    proj_ms = st[0] / loop.iterations
+    proj_ms = st["project"]
     return {
         "workload": f"{w.name}: {parts.n} particles, elastic cube falling onto the floor, {w.n}^3 nodes, "
                     f"2^{w.frac_bits}, dt {ex['dt']}, {loop.iterations} iterations per substep, relaxation "
                     f"{loop.relax}, {loop.polar_iters} Newton polar steps, guardian band {loop.band}",
         "substeps": k, "ms_per_substep": round(total, 4), "particles_per_s": round(parts.n / (total * 1e-3), 1),
-        "stages_ms_per_substep": {nm: round(float(t), 4) for nm, t in zip(names, st)},
+        "stages_ms_per_substep": {nm: round(float(t), 4) for nm, t in st.items()},
         "integrate_ms": round(float(integ), 4),
         "project": {"bytes": parts.n * 108, "ms_per_call": round(float(proj_ms), 4),
                     "achieved_gbs": gbs(parts.n * 108, proj_ms), "bound": "alu (float64 Newton polar iteration)"},
+        "g2p_project_ms_per_call": round(float(st["g2p_project"]) / last, 4) if last > 0 else None,
         "status": status,
     }
 

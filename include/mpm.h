@@ -523,6 +523,8 @@ int mpm_update_deformation_stress(const mpm_grid_desc *grid, const mpm_particles
  *   mpm_update_deformation, dt = 1  F <- (I + D) F
  *
  * d and D carry over to the next substep as its starting guess (warm start).
+ * Every iteration's G2P but the last may run together with the next
+ * iteration's projection (mpm_pbmpm_g2p_project), the same results in one pass.
  */
 
 /* particleUpdate for an elastic material: the target shape is a rotation, the
@@ -541,6 +543,24 @@ int mpm_update_deformation_stress(const mpm_grid_desc *grid, const mpm_particles
  * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
 int mpm_pbmpm_project_elastic(const mpm_grid_desc *grid, const mpm_particles *particles, const float *F, float relax,
                               int32_t polar_iters, uint32_t *status, hipStream_t stream);
+
+/* The loop's G2P gather of one iteration and the elastic projection that
+ * opens the next, in one pass: exactly mpm_g2p with dt = 0 (d and D gathered
+ * from dg, x kept and clamped as there) followed by mpm_pbmpm_project_elastic
+ * on the D it gathered (or on the stored D of a particle outside the grid,
+ * which the gather skips); the same operations in the same order, so the
+ * results and the status counts are bit-identical to those two calls in
+ * sequence.  A substep then runs mpm_pbmpm_project_elastic once before its
+ * first iteration and this call after every iteration but the last, whose
+ * G2P is mpm_g2p.
+ * dg: device float[dim][nodes], the displacement grid of mpm_pbmpm_grid_update.
+ * particles: device; x read (and clamped), v (d) written, C (D) read and
+ * written.  F: device float[dim*dim][n].  relax in [0, 2], polar_iters in
+ * [0, 64].  status[0] counts particles outside the grid and refused
+ * projections, status[2] clamps.
+ * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
+int mpm_pbmpm_g2p_project(const mpm_grid_desc *grid, const float *dg, const mpm_particles *particles, const float *F,
+                          float relax, int32_t polar_iters, uint32_t *status, hipStream_t stream);
 
 /* gridUpdate in displacement form (the same section: mass-normalise, then the
  * guardian projects each node's displaced position back into bounds).  Per

@@ -55,7 +55,8 @@ EXPORTS = ("mpm_version", "mpm_strerror", "mpm_check_bounds", "mpm_workspace_byt
            "mpm_grid_update", "mpm_grid_clear", "mpm_g2p", "mpm_neohookean_affine", "mpm_update_deformation",
            "mpm_bin_resident", "mpm_g2p2g", "mpm_grid_clear_tiles", "mpm_gather_records",
            "mpm_p2g_isplit_noalloc", "mpm_pbmpm_project_elastic", "mpm_pbmpm_grid_update", "mpm_pbmpm_integrate",
-           "mpm_grid_update_tiles", "mpm_g2p_records", "mpm_update_deformation_stress")
+           "mpm_grid_update_tiles", "mpm_g2p_records", "mpm_update_deformation_stress",
+           "mpm_pbmpm_g2p_project")
 
 _lib = None
 
@@ -123,6 +124,9 @@ def lib() -> ct.CDLL:
                                 ct.c_int32, ct.c_void_p, ct.c_void_p]
         L.mpm_grid_clear_tiles.restype = ct.c_int
         L.mpm_grid_clear_tiles.argtypes = [P(mpm_grid_desc), ct.c_void_p, ct.c_void_p, ct.c_void_p]
+        L.mpm_pbmpm_g2p_project.restype = ct.c_int
+        L.mpm_pbmpm_g2p_project.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_void_p, ct.c_float,
+                                            ct.c_int32, ct.c_void_p, ct.c_void_p]
         L.mpm_pbmpm_project_elastic.restype = ct.c_int
         L.mpm_pbmpm_project_elastic.argtypes = [P(mpm_grid_desc), P(mpm_particles), ct.c_void_p, ct.c_float, ct.c_int32,
                                                 ct.c_void_p, ct.c_void_p]
@@ -320,6 +324,12 @@ def mpm_update_deformation_stress(desc, parts: mpm_particles, F, vol0, dt: float
     _check(lib().mpm_update_deformation_stress(ct.byref(desc), ct.byref(parts), _ptr(F), _ptr(vol0), dt, mu, lam,
                                                _ptr(C_out), _ptr(status), _stream(stream)),
            "mpm_update_deformation_stress")
+
+
+def mpm_pbmpm_g2p_project(desc, dg, parts: mpm_particles, F, relax: float, polar_iters: int, status,
+                          stream=None) -> None:
+    _check(lib().mpm_pbmpm_g2p_project(ct.byref(desc), _ptr(dg), ct.byref(parts), _ptr(F), relax, polar_iters,
+                                       _ptr(status), _stream(stream)), "mpm_pbmpm_g2p_project")
 
 
 def mpm_pbmpm_project_elastic(desc, parts: mpm_particles, F, relax: float, polar_iters: int, status,

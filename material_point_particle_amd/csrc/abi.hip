@@ -6,6 +6,7 @@
 #include <atomic>
 
 #include "resident.hpp"
+#include "pbmpm_device.hpp"
 #include "stress.hpp"
 
 namespace mpmk {
@@ -597,6 +598,20 @@ int mpm_pbmpm_project_elastic(const mpm_grid_desc *grid, const mpm_particles *pa
         return MPM_ERR_INVALID;
     return hip_status(launch_pbmpm_project(grid->dim, particles->n, F, particles->C, relax, polar_iters, status,
                                            stream));
+}
+
+int mpm_pbmpm_g2p_project(const mpm_grid_desc *grid, const float *dg, const mpm_particles *particles, const float *F,
+                          float relax, int32_t polar_iters, uint32_t *status, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_desc(grid)) != MPM_OK || (rc = check_particles(grid, particles, true, false)) != MPM_OK)
+        return rc;
+    if (!aligned(dg, 4) || !aligned(status, 4) || (particles->n > 0 && (!aligned(particles->C, 4) || !aligned(F, 4))))
+        return MPM_ERR_INVALID;
+    if (!(relax >= 0.0f && relax <= 2.0f) || polar_iters < 0 || polar_iters > 64)
+        return MPM_ERR_INVALID;
+    return hip_status(launch_pbmpm_g2p_project(grid->dim, grid->n, dg, particles->x, particles->v, particles->C,
+                                               particles->n, F, relax, polar_iters, status, stream));
 }
 
 int mpm_pbmpm_grid_update(const mpm_grid_desc *grid, void *bins, size_t bins_bytes, int64_t *grid_io, float *dg,

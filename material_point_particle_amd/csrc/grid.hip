@@ -6,6 +6,7 @@
 // it in place and no separate clear pass exists), rule 1 (the fixed-point sums
 // are converted once, in the grid update) and rule 7 (gravity is applied by the
 // solver to the grid velocity).
+#include "pbmpm_device.hpp"
 #include "resident.hpp"
 
 namespace mpmk {
@@ -166,6 +167,66 @@ __global__ void __launch_bounds__(256) g2p_kernel(int n, float nf, float dx, flo
             x[d * np + p] = xn[d];
         }
         wave_count(clamped, &status[2]);
+    }
+}
+
+// The PB-MPM loop's G2P gather (dt = 0: d and D from the displacement grid,
+// x kept) and the next iteration's elastic projection of D in one pass: per
+// particle exactly g2p_kernel's arithmetic and then pbmpm_project_kernel's on
+// the D it produced (or on the stored D for a particle outside the grid,
+// which the gather skips), so memory ends as after the two kernels in
+// sequence; D is written once, projected or (when the projection refuses the
+// particle) as gathered.
+template <int DIM>
+__global__ void __launch_bounds__(256) g2p_project_kernel(int n, float nf, float dx, float last_base,
+                                                          const float *__restrict__ dg, float *__restrict__ x,
+                                                          float *__restrict__ d, float *__restrict__ D, int64_t np,
+                                                          float lo, float hi, float cscale,
+                                                          const float *__restrict__ F, double relax,
+                                                          int polar_iters, uint32_t *__restrict__ status)
+{
+    const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
+        Axis ax[DIM];
+        float xp[DIM];
+        bool ok = true;
+#pragma unroll
+        for (int e = 0; e < DIM; ++e) {
+            xp[e] = x[e * np + p];
+            ok = axis_stencil(xp[e], nf, dx, last_base, ax[e]) && ok;
+        }
+        wave_count(!ok, &status[0]);
+        float Dn[DIM * DIM];
+        bool clamped = false;
+        if (ok) {
+            const int bz = DIM == 3 ? ax[DIM - 1].base : 0;
+            auto disp = [&](int a, int b, int c, int k) {
+                const int64_t node = DIM == 3 ? ((int64_t)(bz + c) * n + (ax[1].base + b)) * n + (ax[0].base + a)
+                                              : (int64_t)(ax[1].base + b) * n + (ax[0].base + a);
+                return dg[k * nodes + node];
+            };
+            float dn[DIM], xn[DIM];
+            clamped = g2p_particle<DIM>(ax, xp, disp, 0.0f, lo, hi, cscale, dn, Dn, xn);
+#pragma unroll
+            for (int k = 0; k < DIM; ++k) {
+                d[k * np + p] = dn[k];
+                x[k * np + p] = xn[k];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < DIM * DIM; ++q)
+                Dn[q] = D[(int64_t)q * np + p];
+        }
+        wave_count(clamped, &status[2]);
+        const bool projected = pbmpm_project_particle<DIM>(
+            [&](int q) { return F[(int64_t)q * np + p]; }, Dn, relax, polar_iters,
+            [&](int q, float val) { D[(int64_t)q * np + p] = val; });
+        wave_count(!projected, &status[0]);
+        if (ok && !projected) {                      // the gathered D stays
+#pragma unroll
+            for (int q = 0; q < DIM * DIM; ++q)
+                D[(int64_t)q * np + p] = Dn[q];
+        }
     }
 }
 
@@ -396,6 +457,23 @@ hipError_t launch_g2p_records(int dim, int n, const BinView &b, const float *vg,
     else
         hipLaunchKernelGGL(g2p_records_kernel<2>, dim3(blocks_for(np, 256)), dim3(256), 0, s, n, nf, dx, last, vg,
                            b.sorted, b.meta, b.stamp, dt, lo, hi, cscale, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_pbmpm_g2p_project(int dim, int n, const float *dg, float *x, float *d, float *D, int64_t np,
+                                    const float *F, float relax, int polar_iters, uint32_t *status, hipStream_t s)
+{
+    if (np == 0)
+        return hipSuccess;
+    const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3);
+    const float lo = dx, hi = (float)(n - 2) * dx;
+    const float cscale = 4.0f * (float)n * (float)n;
+    if (dim == 3)
+        hipLaunchKernelGGL(g2p_project_kernel<3>, dim3(blocks_for(np, 256)), dim3(256), 0, s, n, nf, dx, last, dg, x, d,
+                           D, np, lo, hi, cscale, F, (double)relax, polar_iters, status);
+    else
+        hipLaunchKernelGGL(g2p_project_kernel<2>, dim3(blocks_for(np, 256)), dim3(256), 0, s, n, nf, dx, last, dg, x, d,
+                           D, np, lo, hi, cscale, F, (double)relax, polar_iters, status);
     return hipGetLastError();
 }
 

@@ -10,111 +10,31 @@
 // stress term), the displacement-form grid update (grid.hip, node_rows_kernel
 // OP 2) and the G2P gather of d and D (the G2P kernel with dt = 0, which
 // leaves x in place) }, then the integrate step (this file) and
-// F <- (I + D) F (stress.hip's F update with dt = 1).
-#include "common.hpp"
+// F <- (I + D) F (stress.hip's F update with dt = 1).  The per-particle
+// projection lives in pbmpm_device.hpp, so that grid.hip's gather can run the
+// next iteration's projection in the same pass.
+#include "pbmpm_device.hpp"
 
 namespace mpmk {
 namespace {
 
-// Cofactor matrix of the dim x dim matrix a (a^-T = cof / det); returns
-// det a = (a00 cof00 + a01 cof01) + a02 cof02 (2D: a00 a11 - a01 a10).
-template <int DIM>
-__device__ __forceinline__ double cofactor(const double (&a)[3][3], double (&cof)[3][3])
-{
-    if constexpr (DIM == 3) {
-        cof[0][0] = a[1][1] * a[2][2] - a[1][2] * a[2][1];
-        cof[0][1] = a[1][2] * a[2][0] - a[1][0] * a[2][2];
-        cof[0][2] = a[1][0] * a[2][1] - a[1][1] * a[2][0];
-        cof[1][0] = a[0][2] * a[2][1] - a[0][1] * a[2][2];
-        cof[1][1] = a[0][0] * a[2][2] - a[0][2] * a[2][0];
-        cof[1][2] = a[0][1] * a[2][0] - a[0][0] * a[2][1];
-        cof[2][0] = a[0][1] * a[1][2] - a[0][2] * a[1][1];
-        cof[2][1] = a[0][2] * a[1][0] - a[0][0] * a[1][2];
-        cof[2][2] = a[0][0] * a[1][1] - a[0][1] * a[1][0];
-        return (a[0][0] * cof[0][0] + a[0][1] * cof[0][1]) + a[0][2] * cof[0][2];
-    } else {
-        cof[0][0] = a[1][1];
-        cof[0][1] = -a[1][0];
-        cof[1][0] = -a[0][1];
-        cof[1][1] = a[0][0];
-        return a[0][0] * a[1][1] - a[0][1] * a[1][0];
-    }
-}
-
-// particleUpdate for an elastic material: the target shape is the polar
-// rotation R of the trial deformation Ft = (I + D) F (Newton's iteration
-// R <- (R + R^-T) / 2 from R = Ft, polar_iters steps); the displacement
-// gradient reaching it is D* = R F^-1 - I; D <- D + relax (D* - D).  Float64
-// in this order, D rounded to float32 once:
-//   Ft_de = sum_q ([d == q] + D_dq) F_qe                  (q ascending)
-//   R_de <- (R_de + cof(R)_de / det R) * 0.5
-//   F^-1_qe = cof(F)_eq / det F
-//   D*_de = (sum_q R_dq F^-1_qe) - [d == e]
-//   D_de <- D_de + relax * (D*_de - D_de)
-// A particle whose Ft or F (or a Newton iterate) has a non-positive
-// determinant keeps D and is counted in status[0].  One thread per particle.
+// particleUpdate for an elastic material (pbmpm_project_particle): a
+// particle whose Ft or F (or a Newton iterate) has a non-positive determinant
+// keeps D and is counted in status[0].  One thread per particle.
 template <int DIM>
 __global__ void __launch_bounds__(256) pbmpm_project_kernel(int64_t np, const float *__restrict__ F,
                                                             float *__restrict__ D, double relax, int polar_iters,
                                                             uint32_t *__restrict__ status)
 {
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
-        double f[3][3] = {}, dd[3][3] = {}, ft[3][3] = {}, r[3][3] = {}, cof[3][3] = {};
+        float ds[DIM * DIM];
 #pragma unroll
-        for (int d = 0; d < DIM; ++d)
-#pragma unroll
-            for (int e = 0; e < DIM; ++e) {
-                f[d][e] = (double)F[(int64_t)(d * DIM + e) * np + p];
-                dd[d][e] = (double)D[(int64_t)(d * DIM + e) * np + p];
-            }
-#pragma unroll
-        for (int d = 0; d < DIM; ++d)
-#pragma unroll
-            for (int e = 0; e < DIM; ++e) {
-                double t = ((d == 0 ? 1.0 : 0.0) + dd[d][0]) * f[0][e];
-#pragma unroll
-                for (int q = 1; q < DIM; ++q)
-                    t = t + ((d == q ? 1.0 : 0.0) + dd[d][q]) * f[q][e];
-                ft[d][e] = t;
-                r[d][e] = t;
-            }
-        bool ok = cofactor<DIM>(ft, cof) > 0.0;
-        for (int k = 0; k < polar_iters; ++k) {
-            if (!ok)
-                break;
-            const double det = cofactor<DIM>(r, cof);
-            if (!(det > 0.0)) {
-                ok = false;
-                break;
-            }
-#pragma unroll
-            for (int d = 0; d < DIM; ++d)
-#pragma unroll
-                for (int e = 0; e < DIM; ++e)
-                    r[d][e] = (r[d][e] + cof[d][e] / det) * 0.5;
-        }
-        const double detf = ok ? cofactor<DIM>(f, cof) : 0.0;
-        const bool counted = !ok || !(detf > 0.0);
-        wave_count(counted, &status[0]);
-        if (counted)
-            continue;
-        double finv[3][3];
-#pragma unroll
-        for (int q = 0; q < DIM; ++q)
-#pragma unroll
-            for (int e = 0; e < DIM; ++e)
-                finv[q][e] = cof[e][q] / detf;
-#pragma unroll
-        for (int d = 0; d < DIM; ++d)
-#pragma unroll
-            for (int e = 0; e < DIM; ++e) {
-                double t = r[d][0] * finv[0][e];
-#pragma unroll
-                for (int q = 1; q < DIM; ++q)
-                    t = t + r[d][q] * finv[q][e];
-                const double dstar = t - (d == e ? 1.0 : 0.0);
-                D[(int64_t)(d * DIM + e) * np + p] = (float)(dd[d][e] + relax * (dstar - dd[d][e]));
-            }
+        for (int q = 0; q < DIM * DIM; ++q)
+            ds[q] = D[(int64_t)q * np + p];
+        const bool ok = pbmpm_project_particle<DIM>(
+            [&](int q) { return F[(int64_t)q * np + p]; }, ds, relax, polar_iters,
+            [&](int q, float val) { D[(int64_t)q * np + p] = val; });
+        wave_count(!ok, &status[0]);
     }
 }
 

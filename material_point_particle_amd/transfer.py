@@ -200,18 +200,32 @@ class PBMPMSubsteps:
     change while x does not."""
 
     def __init__(self, tr: Transfer, parts: ElasticParticles, dt: float, gravity, iterations: int = 5,
-                 relax: float = 1.5, polar_iters: int = 12, band: int = 2):
+                 relax: float = 1.5, polar_iters: int = 12, band: int = 2, fused: bool = True):
         self.tr, self.parts = tr, parts
         self.dt, self.gravity = dt, list(gravity)
         self.iterations, self.relax, self.polar_iters, self.band = iterations, relax, polar_iters, band
+        self.fused = fused
 
-    def iteration(self) -> None:
+    def project(self) -> None:
         tr, parts = self.tr, self.parts
         L.mpm_pbmpm_project_elastic(tr.desc, parts.desc(), parts.F, self.relax, self.polar_iters, tr.status)
+
+    def deposit(self) -> None:
+        """Binning, P2G and the displacement-form grid update of one iteration."""
+        tr, parts = self.tr, self.parts
         tr.bin(parts)
         tr.p2g(parts, binned=True)
         L.mpm_pbmpm_grid_update(tr.desc, tr.ws, tr.grid, tr.vg, self.band)
-        tr.g2p(parts, 0.0)
+
+    def gather_project(self) -> None:
+        """This iteration's G2P and the next iteration's projection in one pass."""
+        tr, parts = self.tr, self.parts
+        L.mpm_pbmpm_g2p_project(tr.desc, tr.vg, parts.desc(), parts.F, self.relax, self.polar_iters, tr.status)
+
+    def iteration(self) -> None:
+        self.project()
+        self.deposit()
+        self.tr.g2p(self.parts, 0.0)
 
     def integrate(self) -> None:
         tr, parts = self.tr, self.parts
@@ -219,6 +233,18 @@ class PBMPMSubsteps:
         L.mpm_update_deformation(tr.desc, parts.desc(), parts.F, 1.0)
 
     def substep(self) -> None:
-        for _ in range(self.iterations):
-            self.iteration()
+        """fused: the first projection on its own, then every iteration's G2P
+        but the last together with the next projection; else the separate
+        calls.  Both give the same bits."""
+        if self.fused:
+            self.project()
+            for it in range(self.iterations):
+                self.deposit()
+                if it + 1 < self.iterations:
+                    self.gather_project()
+                else:
+                    self.tr.g2p(self.parts, 0.0)
+        else:
+            for _ in range(self.iterations):
+                self.iteration()
         self.integrate()

@@ -247,6 +247,15 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert fused(ct.byref(d), ct.byref(p4), *okf[:5], ct.c_void_p(4096), status, None) == L.MPM_ERR_INVALID  # C' = C
     assert fused(ct.byref(d), ct.byref(p4), *okf[:5], ct.c_void_p(8192), status, None) == L.MPM_ERR_INVALID  # C' = F
     assert fused(None, ct.byref(p4), *okf, None) == L.MPM_ERR_INVALID
+    # PB-MPM gather with the next projection: dg, particles, F, relax, iterations, status
+    gp = lib.mpm_pbmpm_g2p_project
+    dg = ct.c_void_p(20480)
+    assert gp(ct.byref(d), None, ct.byref(p4), ct.c_void_p(8192), 1.5, 12, status, None) == L.MPM_ERR_INVALID
+    assert gp(ct.byref(d), dg, ct.byref(p3), ct.c_void_p(8192), 1.5, 12, status, None) == L.MPM_ERR_INVALID  # no C
+    assert gp(ct.byref(d), dg, ct.byref(p4), None, 1.5, 12, status, None) == L.MPM_ERR_INVALID               # no F
+    assert gp(ct.byref(d), dg, ct.byref(p4), ct.c_void_p(8192), 2.5, 12, status, None) == L.MPM_ERR_INVALID
+    assert gp(ct.byref(d), dg, ct.byref(p4), ct.c_void_p(8192), 1.5, 65, status, None) == L.MPM_ERR_INVALID
+    assert gp(None, dg, ct.byref(p4), ct.c_void_p(8192), 1.5, 12, status, None) == L.MPM_ERR_INVALID
 
 
 def test_noalloc_isplit_refuses_inputs_past_its_static_scratch():

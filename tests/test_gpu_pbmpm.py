@@ -140,11 +140,13 @@ def oracle_state(host):
     return {k: np.ascontiguousarray(host[k].copy()) for k in ("x", "v", "C", "m", "F")}
 
 
-def test_jelly_substeps_in_lockstep(mpm, oracle_lib):
+@pytest.mark.parametrize("fused", [False, True])
+def test_jelly_substeps_in_lockstep(mpm, oracle_lib, fused):
     """20 substeps of 5 iterations of the 32,768-particle jelly cube falling
     onto the floor (the guardian engages): after every substep x, d, D and F
     are bit-identical to the oracle's own trajectory, and so is the last
-    iteration's P2G grid at every 5th substep."""
+    iteration's P2G grid at every 5th substep.  fused: every iteration's G2P
+    but the last runs with the next projection (mpm_pbmpm_g2p_project)."""
     w = WORKLOADS["pbmpm_jelly_3d_64"]
     ex = w.extra
     host = build(w)
@@ -155,16 +157,23 @@ def test_jelly_substeps_in_lockstep(mpm, oracle_lib):
     from material_point_particle_amd import _lib as L
     for k in range(1, ex["substeps"] + 1):
         grid_gpu = None
+        last = ex["iterations"] - 1
         for it in range(ex["iterations"]):
-            # loop.iteration(), with the P2G grid of the substep's last iteration kept before the
+            # loop.substep(), with the P2G grid of the substep's last iteration kept before the
             # grid update consumes it
-            L.mpm_pbmpm_project_elastic(tr.desc, parts.desc(), parts.F, ex["relax"], ex["polar_iters"], tr.status)
+            if not fused or it == 0:
+                L.mpm_pbmpm_project_elastic(tr.desc, parts.desc(), parts.F, ex["relax"], ex["polar_iters"],
+                                            tr.status)
             tr.bin(parts)
             tr.p2g(parts, binned=True)
-            if it == ex["iterations"] - 1 and k % 5 == 0:
+            if it == last and k % 5 == 0:
                 grid_gpu = tr.grid.cpu().numpy()
             L.mpm_pbmpm_grid_update(tr.desc, tr.ws, tr.grid, tr.vg, ex["band"])
-            tr.g2p(parts, 0.0)
+            if fused and it < last:
+                L.mpm_pbmpm_g2p_project(tr.desc, tr.vg, parts.desc(), parts.F, ex["relax"], ex["polar_iters"],
+                                        tr.status)
+            else:
+                tr.g2p(parts, 0.0)
         loop.integrate()
         grid, st = oracle_lib.pbmpm_substep(3, w.n, w.frac_bits, state, rng, ex["iterations"], ex["relax"],
                                             ex["polar_iters"], ex["band"], ex["dt"], ex["gravity"])
@@ -179,6 +188,47 @@ def test_jelly_substeps_in_lockstep(mpm, oracle_lib):
     # the cube reached the floor: particles pushed back by the guardian, none clamped by the backstop
     assert float(state["x"][1].min()) < 3.0 / w.n
     assert u32(tr.status).tolist()[3] == 0
+
+
+@pytest.mark.parametrize("dim", [2, 3])
+def test_g2p_project_equals_the_two_calls(mpm, dim):
+    """mpm_pbmpm_g2p_project against mpm_g2p (dt = 0) followed by
+    mpm_pbmpm_project_elastic, on a displacement grid of random values: x, d,
+    D and the status counts bit-identical.  Some particles sit outside the
+    grid (the gather skips them, the projection still runs on their stored D),
+    some at the clamp bounds, some have an inverted F (the projection keeps
+    their gathered D)."""
+    from material_point_particle_amd import _lib as L
+    n, k = (64 if dim == 2 else 32), 50_001
+    rng = np.random.default_rng(60 + dim)
+    x = rng.uniform(1.0 / n, (n - 2.0) / n, (dim, k)).astype(np.float32)
+    x[0, :40] = 0.2 / n                          # base -1 on x: outside the grid
+    x[dim - 1, 40:80] = (n - 1.2) / n            # base n - 2 on the last axis: outside
+    x[0, 80:120] = 0.9 / n                       # inside the grid, below the clamp bound dx
+    d = (0.01 * rng.standard_normal((dim, k))).astype(np.float32)
+    D = (0.05 * rng.standard_normal((dim * dim, k))).astype(np.float32)
+    F = (np.eye(dim).reshape(dim * dim, 1) + 0.1 * rng.standard_normal((dim * dim, k))).astype(np.float32)
+    F[0, 120:160] = -3.0                          # det F < 0 for most of these
+    dg = (0.002 * rng.standard_normal((dim,) + (n,) * dim)).astype(np.float32)
+    desc = L.grid_desc(dim, n, 32)
+    out = []
+    for fused in (False, True):
+        xd, dd, Dd = (torch.from_numpy(a.copy()).cuda() for a in (x, d, D))
+        Fd, dgd = torch.from_numpy(F).cuda(), torch.from_numpy(dg).cuda()
+        st = torch.zeros(4, dtype=torch.int32, device="cuda")
+        parts = L.particles(k, xd, dd, Dd, None)
+        if fused:
+            L.mpm_pbmpm_g2p_project(desc, dgd, parts, Fd, 1.5, 12, st)
+        else:
+            L.mpm_g2p(desc, dgd, parts, 0.0, st)
+            L.mpm_pbmpm_project_elastic(desc, parts, Fd, 1.5, 12, st)
+        torch.cuda.synchronize()
+        out.append([a.cpu().numpy() for a in (xd, dd, Dd)] + [u32(st).tolist()])
+    say("g2p + projection, one pass", dim, out[1][3])
+    for a, b, what in zip(out[0][:3], out[1][:3], ("x", "d", "D")):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), what
+    assert out[0][3] == out[1][3]
+    assert out[1][3][0] >= 80 + 20 and out[1][3][2] > 0       # skipped, refused and clamped particles
 
 
 def test_square_2d_substeps_in_lockstep(mpm, oracle_lib):
