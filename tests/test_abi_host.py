@@ -277,3 +277,18 @@ def test_noalloc_isplit_refuses_inputs_past_its_static_scratch():
     # the largest 3D workload that fits: about 2M particles (132 bytes each) on 128^3
     assert M.mpm_isplit_workspace_bytes(3, 128, 2_000_000) <= L.MPM_ISPLIT_SCRATCH_BYTES
     assert M.mpm_isplit_workspace_bytes(3, 128, 2_100_000) > L.MPM_ISPLIT_SCRATCH_BYTES
+
+
+def test_empty_calls_of_the_one_pass_entry_points_return_before_any_launch():
+    """With no particles, the one-pass calls validate their descriptors and
+    return MPM_OK without a device call (the pointers are aligned
+    placeholders, never dereferenced), as the calls they combine do."""
+    lib = M.lib()
+    d = L.grid_desc(3, 32, 28)
+    p0 = L.mpm_particles(0, None, None, None, None)
+    fake = ct.c_void_p(4096)
+    assert lib.mpm_update_deformation_stress(ct.byref(d), ct.byref(p0), None, None, 1e-4, 1e5, 1e5, None, fake,
+                                             None) == L.MPM_OK
+    assert lib.mpm_pbmpm_g2p_project(ct.byref(d), fake, ct.byref(p0), None, 1.5, 12, fake, None) == L.MPM_OK
+    assert lib.mpm_update_deformation(ct.byref(d), ct.byref(p0), None, 1e-4, None) == L.MPM_OK
+
