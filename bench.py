@@ -344,13 +344,16 @@ def measure_elastic(args, torch, w, build, Transfer):
 
 def measure_pbmpm(args, torch, w, build):
     """The position-based MPM substep (elastic material) on the 8M-particle
-    jelly cube at 256^3: per substep 5 iterations of binning, P2G,
-    displacement-form grid update and G2P gather, each iteration opened by
-    the elastic projection (the first on its own, the others in the previous
-    iteration's gather pass, mpm_pbmpm_g2p_project), then the integrate step
-    and F <- (I + D) F, timed per stage with HIP events over the evolving
-    state.  The projection is float64 ALU work (108 B per particle: F and D
-    read, D written); the integrate step reads and writes x and d (48 B)."""
+    jelly cube at 256^3: per substep 5 iterations of P2G, displacement-form
+    grid update and G2P gather, each iteration opened by the elastic
+    projection (the first on its own, the others in the previous iteration's
+    gather pass), then the integrate step and F <- (I + D) F, timed per stage
+    with HIP events over the evolving state.  The particles are binned once per
+    substep, after the first projection; every gather but the last rewrites
+    their binned records (mpm_pbmpm_g2p_project_records).  The same loop
+    re-binning every iteration (mpm_pbmpm_g2p_project) is timed after it, from
+    the same starting state, for comparison.  The projection is float64 ALU work (108 B per particle: F and
+    D read, D written); the integrate step reads and writes x and d (48 B)."""
     import material_point_particle_amd._lib as L
     from material_point_particle_amd.transfer import ElasticParticles, PBMPMSubsteps, Transfer
     host = build(w)
@@ -369,9 +372,16 @@ def measure_pbmpm(args, torch, w, build):
              "g2p_project": loop.gather_project,
              "g2p": lambda: tr.g2p(parts, 0.0)}
     last = loop.iterations - 1
-    order = ["project"]
-    for it in range(loop.iterations):
-        order += ["bin", "p2g", "grid_update", "g2p_project" if it < last else "g2p"]
+
+    def stage_order():
+        order = ["project"]
+        for it in range(loop.iterations):
+            if it == 0 or not loop.records:
+                order.append("bin")
+            order += ["p2g", "grid_update", "g2p_project" if it < last else "g2p"]
+        return order
+
+    order = stage_order()
 
     def substep(ev=None):
         for i, nm in enumerate(order):
@@ -384,28 +394,43 @@ def measure_pbmpm(args, torch, w, build):
         if ev:
             ev[len(order) + 1].record(stream)
 
-    substep()
-    torch.cuda.synchronize()
+    def timed(k):
+        """k substeps after one untimed: the mean substep and per-stage times."""
+        substep()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 2)] for _ in range(k)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(k):
+            substep(events[i])
+        stop.record(stream)
+        torch.cuda.synchronize()
+        st = dict.fromkeys(names, 0.0)
+        integ = 0.0
+        for ev in events:
+            for i, nm in enumerate(order):
+                st[nm] += ev[i].elapsed_time(ev[i + 1])
+            integ += ev[len(order)].elapsed_time(ev[len(order) + 1])
+        return start.elapsed_time(stop) / k, {nm: t / k for nm, t in st.items()}, integ / k
+
     k = max(3, args.substeps // 4)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 2)] for _ in range(k)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(k):
-        substep(events[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total = start.elapsed_time(stop) / k
-    st = dict.fromkeys(names, 0.0)
-    integ = 0.0
-    for ev in events:
-        for i, nm in enumerate(order):
-            st[nm] += ev[i].elapsed_time(ev[i + 1])
-        integ += ev[len(order)].elapsed_time(ev[len(order) + 1])
-    st = {nm: t / k for nm, t in st.items()}
-    integ /= k
+    start_state = [t.clone() for t in (parts.x, parts.v, parts.C, parts.F)]
+    total, st, integ = timed(k)
     status = tr.status.cpu().numpy().view(np.uint32).tolist()
     log(f"pbmpm substeps: {total:.3f} ms (" + ", ".join(f"{nm} {t:.3f}" for nm, t in st.items()) +
-        f", integrate {integ:.3f}; {loop.iterations} iterations)")
+        f", integrate {integ:.3f}; {loop.iterations} iterations, {order.count('bin')} binning)")
+    # the same loop re-binning every iteration, from the same state
+    total_rebin, st_rebin = None, {}
+    if not getattr(args, "no_pbmpm_rebin", False):
+        for t, t0 in zip((parts.x, parts.v, parts.C, parts.F), start_state):
+            t.copy_(t0)
+        loop.records = False
+        order = stage_order()
+        total_rebin, st_rebin, _ = timed(k)
+        loop.records = True
+        log(f"pbmpm substeps re-binning every iteration: {total_rebin:.3f} ms (" +
+            ", ".join(f"{nm} {t:.3f}" for nm, t in st_rebin.items()) + ")")
+    del start_state
 
     def gbs(b, t):
         return round(b / (t * 1e-3) / 1e9, 1)
@@ -421,6 +446,9 @@ def measure_pbmpm(args, torch, w, build):
         "project": {"bytes": parts.n * 108, "ms_per_call": round(float(proj_ms), 4),
                     "achieved_gbs": gbs(parts.n * 108, proj_ms), "bound": "alu (float64 Newton polar iteration)"},
         "g2p_project_ms_per_call": round(float(st["g2p_project"]) / last, 4) if last > 0 else None,
+        "binnings_per_substep": 1,
+        "ms_per_substep_rebinning_every_iteration": round(total_rebin, 4) if total_rebin else None,
+        "stages_ms_per_substep_rebinning_every_iteration": {nm: round(float(t), 4) for nm, t in st_rebin.items()},
         "status": status,
     }
 
@@ -526,6 +554,8 @@ def parse():
                     help="skip the position-based MPM substep measurement on the jelly cube")
     ap.add_argument("--only-pbmpm", action="store_true",
                     help="run only the position-based MPM substep measurement; prints its object")
+    ap.add_argument("--no-pbmpm-rebin", action="store_true",
+                    help="skip the PB-MPM comparison loop that re-bins every iteration (profiling runs)")
     ap.add_argument("--no-isplit", action="store_true",
                     help="skip the integer-split quadratic transfer measurement")
     ap.add_argument("--only-isplit", action="store_true",

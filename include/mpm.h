@@ -562,6 +562,28 @@ int mpm_pbmpm_project_elastic(const mpm_grid_desc *grid, const mpm_particles *pa
 int mpm_pbmpm_g2p_project(const mpm_grid_desc *grid, const float *dg, const mpm_particles *particles, const float *F,
                           float relax, int32_t polar_iters, uint32_t *status, hipStream_t stream);
 
+/* mpm_pbmpm_g2p_project, and then each particle's record in ws rewritten from
+ * its new state exactly as mpm_bin_particles writes it (x, v = d, C = D, m;
+ * v, C and m zeroed and counted in status[1] when outside the ranges), so that
+ * the next iteration's mpm_p2g runs on the same binning: the particles' x
+ * moves only by the gather's clamp to [dx, (n - 2) dx], which keeps each one in
+ * its cell (x n is exact for a power-of-two n, and the clamp maps x n in
+ * [1/2, 1) to 1 and in (n - 2, n - 3/2) to n - 2, each with its stencil base),
+ * so the tiles, work items and slots stay valid.  The P2G grid is then
+ * bit-identical to the one after a fresh binning (its integer sums do not
+ * depend on the records' order inside a tile).  A substep bins once, after its
+ * first projection, and calls this after every iteration but the last.
+ * ws, ws_bytes: the workspace of mpm_bin_particles on these particles with the
+ * same grid and ranges, binned since x last changed outside these calls; a
+ * workspace binned for another grid, particle count or ranges is refused on
+ * the device (nothing is written, status[3] incremented).  particles: as for
+ * mpm_pbmpm_g2p_project, and m read.  Other arguments and status counts as for
+ * mpm_pbmpm_g2p_project.
+ * Errors: MPM_ERR_INVALID, MPM_ERR_OVERFLOW, MPM_ERR_WORKSPACE, MPM_ERR_HIP. */
+int mpm_pbmpm_g2p_project_records(const mpm_grid_desc *grid, const float *dg, const mpm_particles *particles,
+                                  const float *F, float relax, int32_t polar_iters, const mpm_ranges *ranges, void *ws,
+                                  size_t ws_bytes, uint32_t *status, hipStream_t stream);
+
 /* gridUpdate in displacement form (the same section: mass-normalise, then the
  * guardian projects each node's displaced position back into bounds).  Per
  * node: where M != 0, d_e = (float)((double)P_e / (double)M), then with the

@@ -614,6 +614,32 @@ int mpm_pbmpm_g2p_project(const mpm_grid_desc *grid, const float *dg, const mpm_
                                                particles->n, F, relax, polar_iters, status, stream));
 }
 
+int mpm_pbmpm_g2p_project_records(const mpm_grid_desc *grid, const float *dg, const mpm_particles *particles,
+                                  const float *F, float relax, int32_t polar_iters, const mpm_ranges *ranges, void *ws,
+                                  size_t ws_bytes, uint32_t *status, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_desc(grid)) != MPM_OK || (rc = check_ranges(ranges)) != MPM_OK ||
+        (rc = check_particles(grid, particles, true, true)) != MPM_OK)
+        return rc;
+    if (!aligned(dg, 4) || !aligned(status, 4) || !aligned(ws, 256) ||
+        (particles->n > 0 && (!aligned(particles->C, 4) || !aligned(F, 4))))
+        return MPM_ERR_INVALID;
+    if (!(relax >= 0.0f && relax <= 2.0f) || polar_iters < 0 || polar_iters > 64)
+        return MPM_ERR_INVALID;
+    if ((rc = mpm_check_bounds(grid, particles->n, ranges, nullptr)) != MPM_OK)
+        return rc;
+    mpm_ws_layout l;
+    make_layout(grid, particles->n, &l);
+    if (ws_bytes < l.total_bytes)
+        return MPM_ERR_WORKSPACE;
+    const RangesF rf = ranges_f(ranges);
+    const BinView b = bin_view(ws, l, make_stamp(grid, particles->n, rf, false));
+    return hip_status(launch_pbmpm_g2p_project(grid->dim, grid->n, dg, particles->x, particles->v, particles->C,
+                                               particles->n, F, relax, polar_iters, status, stream, &b, rf,
+                                               particles->m));
+}
+
 int mpm_pbmpm_grid_update(const mpm_grid_desc *grid, void *bins, size_t bins_bytes, int64_t *grid_io, float *dg,
                           int32_t band, hipStream_t stream)
 {

@@ -170,6 +170,52 @@ __global__ void __launch_bounds__(256) g2p_kernel(int n, float nf, float dx, flo
     }
 }
 
+// A binned record written with the widest aligned stores: 3D records are
+// x0 x1 x2 v0 | v1 v2 C0 C1 | C2..C5 | C6 C7 C8 m, 2D ones x0 x1 v0 v1 |
+// C0..C3 | m 0 0 0.  keep false: v, C and m are written as zeros (x always
+// as given), as the binning writes a record outside the ranges.
+template <int DIM>
+__device__ __forceinline__ void record_head(float *rec, const float (&x)[DIM], const float (&v)[DIM], bool keep)
+{
+    if constexpr (DIM == 3) {
+        *reinterpret_cast<float4 *>(rec) = make_float4(x[0], x[1], x[2], keep ? v[0] : 0.0f);
+        *reinterpret_cast<float2 *>(rec + 4) = make_float2(keep ? v[1] : 0.0f, keep ? v[2] : 0.0f);
+    } else {
+        *reinterpret_cast<float4 *>(rec) = make_float4(x[0], x[1], keep ? v[0] : 0.0f, keep ? v[1] : 0.0f);
+    }
+}
+
+template <int DIM>
+__device__ __forceinline__ void record_tail(float *rec, const float (&C)[DIM * DIM], float m, bool keep)
+{
+    float c[DIM * DIM];
+#pragma unroll
+    for (int q = 0; q < DIM * DIM; ++q)
+        c[q] = keep ? C[q] : 0.0f;
+    const float mk = keep ? m : 0.0f;
+    if constexpr (DIM == 3) {
+        *reinterpret_cast<float2 *>(rec + 6) = make_float2(c[0], c[1]);
+        *reinterpret_cast<float4 *>(rec + 8) = make_float4(c[2], c[3], c[4], c[5]);
+        *reinterpret_cast<float4 *>(rec + 12) = make_float4(c[6], c[7], c[8], mk);
+    } else {
+        *reinterpret_cast<float4 *>(rec + 4) = make_float4(c[0], c[1], c[2], c[3]);
+        *reinterpret_cast<float4 *>(rec + 8) = make_float4(mk, 0.0f, 0.0f, 0.0f);
+    }
+}
+
+static_assert(rec_floats<3>() == 16 && rec_floats<2>() == 12, "the record layouts written above");
+
+// The binned records a PB-MPM gather rewrites (REFRESH), from a checked
+// binning of the same particles with the same ranges.
+struct RecordRefresh {
+    const uint32_t *slot;     // each particle's record, or kEmpty (outside the grid)
+    float *records;
+    const uint32_t *meta;
+    BinStamp stamp;
+    RangesF r;
+    const float *m;
+};
+
 // The PB-MPM loop's G2P gather (dt = 0: d and D from the displacement grid,
 // x kept) and the next iteration's elastic projection of D in one pass: per
 // particle exactly g2p_kernel's arithmetic and then pbmpm_project_kernel's on
@@ -177,14 +223,33 @@ __global__ void __launch_bounds__(256) g2p_kernel(int n, float nf, float dx, flo
 // which the gather skips), so memory ends as after the two kernels in
 // sequence; D is written once, projected or (when the projection refuses the
 // particle) as gathered.
-template <int DIM>
+// REFRESH: each particle's binned record is then rewritten from its new state
+// exactly as the binning's scatter writes it (x, v = d, C = D, m; v, C and m
+// zeroed and counted in status[1] when out of the declared ranges).  The
+// gather moves x only by its clamp to [dx, (n - 2) dx] (dt = 0, and the
+// gathered d is finite: the grid update bounds every node's displacement),
+// and the clamp keeps every particle's stencil base: with g = x n exact (n a
+// power of two), the base floor(g - 1/2) of a particle inside the grid is 0
+// for g in [1/2, 1), which the clamp maps to 1, and n - 3 for g in
+// (n - 2, n - 3/2), which it maps to n - 2, both with the same base.  So each
+// record stays in its tile and cell, and the next P2G can run on the same
+// binning.
+template <int DIM, bool REFRESH>
 __global__ void __launch_bounds__(256) g2p_project_kernel(int n, float nf, float dx, float last_base,
                                                           const float *__restrict__ dg, float *__restrict__ x,
                                                           float *__restrict__ d, float *__restrict__ D, int64_t np,
                                                           float lo, float hi, float cscale,
                                                           const float *__restrict__ F, double relax,
-                                                          int polar_iters, uint32_t *__restrict__ status)
+                                                          int polar_iters, uint32_t *__restrict__ status,
+                                                          RecordRefresh rr)
 {
+    if constexpr (REFRESH) {
+        if (!stamp_matches(rr.meta, rr.stamp, true)) {   // binned for another grid, count or ranges
+            if (blockIdx.x == 0 && threadIdx.x == 0)
+                atomicAdd(&status[3], 1u);
+            return;
+        }
+    }
     const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
         Axis ax[DIM];
@@ -226,6 +291,36 @@ __global__ void __launch_bounds__(256) g2p_project_kernel(int n, float nf, float
 #pragma unroll
             for (int q = 0; q < DIM * DIM; ++q)
                 D[(int64_t)q * np + p] = Dn[q];
+        }
+    }
+    if constexpr (REFRESH) {
+        // The records, in a pass of their own over this thread's particles (so
+        // that the gather and the projection keep their registers): each from
+        // the x, d, D this thread has just written and m, with the binning's
+        // range check.
+        for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np;
+             p += (int64_t)gridDim.x * blockDim.x) {
+            const uint32_t slot = rr.slot[p];
+            if (slot == kEmpty)
+                continue;
+            float xr[DIM], dr[DIM], Dr[DIM * DIM];
+            const float mr = rr.m[p];
+            bool rng = fabsf(mr) <= rr.r.max_mass;
+#pragma unroll
+            for (int e = 0; e < DIM; ++e) {
+                xr[e] = x[e * np + p];
+                dr[e] = d[e * np + p];
+                rng = rng && fabsf(dr[e]) <= rr.r.max_speed;
+            }
+#pragma unroll
+            for (int q = 0; q < DIM * DIM; ++q) {
+                Dr[q] = D[(int64_t)q * np + p];
+                rng = rng && fabsf(Dr[q]) <= rr.r.max_affine;
+            }
+            float *rec = rr.records + (int64_t)slot * rec_floats<DIM>();
+            record_head<DIM>(rec, xr, dr, rng);
+            record_tail<DIM>(rec, Dr, mr, rng);
+            wave_count(!rng, &status[1]);
         }
     }
 }
@@ -461,19 +556,39 @@ hipError_t launch_g2p_records(int dim, int n, const BinView &b, const float *vg,
 }
 
 hipError_t launch_pbmpm_g2p_project(int dim, int n, const float *dg, float *x, float *d, float *D, int64_t np,
-                                    const float *F, float relax, int polar_iters, uint32_t *status, hipStream_t s)
+                                    const float *F, float relax, int polar_iters, uint32_t *status, hipStream_t s,
+                                    const BinView *bins, RangesF r, const float *m)
 {
     if (np == 0)
         return hipSuccess;
     const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3);
     const float lo = dx, hi = (float)(n - 2) * dx;
     const float cscale = 4.0f * (float)n * (float)n;
-    if (dim == 3)
-        hipLaunchKernelGGL(g2p_project_kernel<3>, dim3(blocks_for(np, 256)), dim3(256), 0, s, n, nf, dx, last, dg, x, d,
-                           D, np, lo, hi, cscale, F, (double)relax, polar_iters, status);
-    else
-        hipLaunchKernelGGL(g2p_project_kernel<2>, dim3(blocks_for(np, 256)), dim3(256), 0, s, n, nf, dx, last, dg, x, d,
-                           D, np, lo, hi, cscale, F, (double)relax, polar_iters, status);
+    RecordRefresh rr{};
+    if (bins) {
+        rr.slot = bins->slot;
+        rr.records = bins->sorted;
+        rr.meta = bins->meta;
+        rr.stamp = bins->stamp;
+        rr.r = r;
+        rr.m = m;
+    }
+    const dim3 grid(blocks_for(np, 256)), block(256);
+    if (dim == 3) {
+        if (bins)
+            hipLaunchKernelGGL((g2p_project_kernel<3, true>), grid, block, 0, s, n, nf, dx, last, dg, x, d, D, np, lo,
+                               hi, cscale, F, (double)relax, polar_iters, status, rr);
+        else
+            hipLaunchKernelGGL((g2p_project_kernel<3, false>), grid, block, 0, s, n, nf, dx, last, dg, x, d, D, np, lo,
+                               hi, cscale, F, (double)relax, polar_iters, status, rr);
+    } else {
+        if (bins)
+            hipLaunchKernelGGL((g2p_project_kernel<2, true>), grid, block, 0, s, n, nf, dx, last, dg, x, d, D, np, lo,
+                               hi, cscale, F, (double)relax, polar_iters, status, rr);
+        else
+            hipLaunchKernelGGL((g2p_project_kernel<2, false>), grid, block, 0, s, n, nf, dx, last, dg, x, d, D, np, lo,
+                               hi, cscale, F, (double)relax, polar_iters, status, rr);
+    }
     return hipGetLastError();
 }
 

@@ -111,7 +111,11 @@ __device__ __forceinline__ bool pbmpm_project_particle(LoadF &&loadF, const floa
 
 // The G2P gather with dt = 0 (d and D from the displacement grid dg, x kept)
 // followed by the projection above, one pass (grid.hip).
+// bins: a checked binning of these particles whose records the gather
+// rewrites from the new state (with the binning's ranges r and the masses m),
+// or NULL.
 hipError_t launch_pbmpm_g2p_project(int dim, int n, const float *dg, float *x, float *d, float *D, int64_t np,
-                                    const float *F, float relax, int polar_iters, uint32_t *status, hipStream_t s);
+                                    const float *F, float relax, int polar_iters, uint32_t *status, hipStream_t s,
+                                    const BinView *bins = nullptr, RangesF r = RangesF{}, const float *m = nullptr);
 
 }  // namespace mpmk

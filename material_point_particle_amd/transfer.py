@@ -196,31 +196,43 @@ class PBMPMSubsteps:
     holds the displacement gradient D: `iterations` times the elastic
     projection, binning and P2G, the displacement-form grid update (into
     tr.vg) and the G2P gather (dt = 0); then the integrate step and
-    F <- (I + D) F.  The records are re-binned every iteration, since d and D
-    change while x does not."""
+    F <- (I + D) F.  d and D change every iteration while x does not (beyond
+    the gather's clamp, which keeps each particle in its cell): with
+    `records` the particles are binned once per substep and every gather but
+    the last rewrites their binned records; without it every iteration
+    re-bins."""
 
     def __init__(self, tr: Transfer, parts: ElasticParticles, dt: float, gravity, iterations: int = 5,
-                 relax: float = 1.5, polar_iters: int = 12, band: int = 2, fused: bool = True):
+                 relax: float = 1.5, polar_iters: int = 12, band: int = 2, fused: bool = True,
+                 records: bool = True):
         self.tr, self.parts = tr, parts
         self.dt, self.gravity = dt, list(gravity)
         self.iterations, self.relax, self.polar_iters, self.band = iterations, relax, polar_iters, band
         self.fused = fused
+        self.records = fused and records
 
     def project(self) -> None:
         tr, parts = self.tr, self.parts
         L.mpm_pbmpm_project_elastic(tr.desc, parts.desc(), parts.F, self.relax, self.polar_iters, tr.status)
 
-    def deposit(self) -> None:
-        """Binning, P2G and the displacement-form grid update of one iteration."""
+    def deposit(self, rebin: bool = True) -> None:
+        """Binning (unless the records are current), P2G and the
+        displacement-form grid update of one iteration."""
         tr, parts = self.tr, self.parts
-        tr.bin(parts)
+        if rebin:
+            tr.bin(parts)
         tr.p2g(parts, binned=True)
         L.mpm_pbmpm_grid_update(tr.desc, tr.ws, tr.grid, tr.vg, self.band)
 
     def gather_project(self) -> None:
-        """This iteration's G2P and the next iteration's projection in one pass."""
+        """This iteration's G2P and the next iteration's projection in one
+        pass (with `records`, the binned records rewritten too)."""
         tr, parts = self.tr, self.parts
-        L.mpm_pbmpm_g2p_project(tr.desc, tr.vg, parts.desc(), parts.F, self.relax, self.polar_iters, tr.status)
+        if self.records:
+            L.mpm_pbmpm_g2p_project_records(tr.desc, tr.vg, parts.desc(), parts.F, self.relax, self.polar_iters,
+                                            tr.ranges, tr.ws, tr.status)
+        else:
+            L.mpm_pbmpm_g2p_project(tr.desc, tr.vg, parts.desc(), parts.F, self.relax, self.polar_iters, tr.status)
 
     def iteration(self) -> None:
         self.project()
@@ -234,12 +246,13 @@ class PBMPMSubsteps:
 
     def substep(self) -> None:
         """fused: the first projection on its own, then every iteration's G2P
-        but the last together with the next projection; else the separate
-        calls.  Both give the same bits."""
+        but the last together with the next projection (with `records`, one
+        binning per substep); else the separate calls.  All give the same
+        bits."""
         if self.fused:
             self.project()
             for it in range(self.iterations):
-                self.deposit()
+                self.deposit(rebin=it == 0 or not self.records)
                 if it + 1 < self.iterations:
                     self.gather_project()
                 else:

@@ -256,6 +256,26 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert gp(ct.byref(d), dg, ct.byref(p4), ct.c_void_p(8192), 2.5, 12, status, None) == L.MPM_ERR_INVALID
     assert gp(ct.byref(d), dg, ct.byref(p4), ct.c_void_p(8192), 1.5, 65, status, None) == L.MPM_ERR_INVALID
     assert gp(None, dg, ct.byref(p4), ct.c_void_p(8192), 1.5, 12, status, None) == L.MPM_ERR_INVALID
+    # the same with the binned records rewritten: also ranges, masses and the binning's workspace
+    gpr = lib.mpm_pbmpm_g2p_project_records
+    F8 = ct.c_void_p(8192)
+    wsr = (ct.byref(r), wsp, need_bins, status)
+    nom = L.mpm_particles(10, 4096, 4096, 4096, None)
+    assert gpr(ct.byref(d), dg, ct.byref(p3), F8, 1.5, 12, *wsr, None) == L.MPM_ERR_INVALID          # no C
+    assert gpr(ct.byref(d), dg, ct.byref(nom), F8, 1.5, 12, *wsr, None) == L.MPM_ERR_INVALID         # no m
+    assert gpr(ct.byref(d), dg, ct.byref(p4), None, 1.5, 12, *wsr, None) == L.MPM_ERR_INVALID        # no F
+    assert gpr(ct.byref(d), dg, ct.byref(p4), F8, 2.5, 12, *wsr, None) == L.MPM_ERR_INVALID
+    assert gpr(ct.byref(d), dg, ct.byref(p4), F8, 1.5, -1, *wsr, None) == L.MPM_ERR_INVALID
+    assert gpr(ct.byref(d), dg, ct.byref(p4), F8, 1.5, 12, None, *wsr[1:], None) == L.MPM_ERR_INVALID
+    assert gpr(ct.byref(d), dg, ct.byref(p4), F8, 1.5, 12, ct.byref(L.mpm_ranges(-1.0, 1.0, 1.0)), *wsr[1:],
+               None) == L.MPM_ERR_INVALID
+    assert gpr(ct.byref(d), dg, ct.byref(p4), F8, 1.5, 12, ct.byref(big), *wsr[1:], None) == L.MPM_ERR_OVERFLOW
+    assert gpr(ct.byref(d), dg, ct.byref(p4), F8, 1.5, 12, ct.byref(r), None, need_bins, status,
+               None) == L.MPM_ERR_INVALID
+    assert gpr(ct.byref(d), dg, ct.byref(p4), F8, 1.5, 12, ct.byref(r), ct.c_void_p((1 << 20) + 8), need_bins,
+               status, None) == L.MPM_ERR_INVALID
+    assert gpr(ct.byref(d), dg, ct.byref(p4), F8, 1.5, 12, ct.byref(r), wsp, need_bins - 1, status,
+               None) == L.MPM_ERR_WORKSPACE
 
 
 def test_noalloc_isplit_refuses_inputs_past_its_static_scratch():
@@ -290,5 +310,8 @@ def test_empty_calls_of_the_one_pass_entry_points_return_before_any_launch():
     assert lib.mpm_update_deformation_stress(ct.byref(d), ct.byref(p0), None, None, 1e-4, 1e5, 1e5, None, fake,
                                              None) == L.MPM_OK
     assert lib.mpm_pbmpm_g2p_project(ct.byref(d), fake, ct.byref(p0), None, 1.5, 12, fake, None) == L.MPM_OK
+    r = L.mpm_ranges(1.0, 1.0, 1.0)
+    assert lib.mpm_pbmpm_g2p_project_records(ct.byref(d), fake, ct.byref(p0), None, 1.5, 12, ct.byref(r), fake,
+                                             M.mpm_workspace_bytes(d, 0), fake, None) == L.MPM_OK
     assert lib.mpm_update_deformation(ct.byref(d), ct.byref(p0), None, 1e-4, None) == L.MPM_OK
 

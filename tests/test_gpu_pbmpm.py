@@ -140,13 +140,15 @@ def oracle_state(host):
     return {k: np.ascontiguousarray(host[k].copy()) for k in ("x", "v", "C", "m", "F")}
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_jelly_substeps_in_lockstep(mpm, oracle_lib, fused):
+@pytest.mark.parametrize("form", ["separate", "fused", "records"])
+def test_jelly_substeps_in_lockstep(mpm, oracle_lib, form):
     """20 substeps of 5 iterations of the 32,768-particle jelly cube falling
     onto the floor (the guardian engages): after every substep x, d, D and F
     are bit-identical to the oracle's own trajectory, and so is the last
     iteration's P2G grid at every 5th substep.  fused: every iteration's G2P
-    but the last runs with the next projection (mpm_pbmpm_g2p_project)."""
+    but the last runs with the next projection (mpm_pbmpm_g2p_project);
+    records: likewise, rewriting the binned records
+    (mpm_pbmpm_g2p_project_records), so the substep bins only once."""
     w = WORKLOADS["pbmpm_jelly_3d_64"]
     ex = w.extra
     host = build(w)
@@ -161,15 +163,19 @@ def test_jelly_substeps_in_lockstep(mpm, oracle_lib, fused):
         for it in range(ex["iterations"]):
             # loop.substep(), with the P2G grid of the substep's last iteration kept before the
             # grid update consumes it
-            if not fused or it == 0:
+            if form == "separate" or it == 0:
                 L.mpm_pbmpm_project_elastic(tr.desc, parts.desc(), parts.F, ex["relax"], ex["polar_iters"],
                                             tr.status)
-            tr.bin(parts)
+            if form != "records" or it == 0:
+                tr.bin(parts)
             tr.p2g(parts, binned=True)
             if it == last and k % 5 == 0:
                 grid_gpu = tr.grid.cpu().numpy()
             L.mpm_pbmpm_grid_update(tr.desc, tr.ws, tr.grid, tr.vg, ex["band"])
-            if fused and it < last:
+            if form == "records" and it < last:
+                L.mpm_pbmpm_g2p_project_records(tr.desc, tr.vg, parts.desc(), parts.F, ex["relax"],
+                                                ex["polar_iters"], tr.ranges, tr.ws, tr.status)
+            elif form == "fused" and it < last:
                 L.mpm_pbmpm_g2p_project(tr.desc, tr.vg, parts.desc(), parts.F, ex["relax"], ex["polar_iters"],
                                         tr.status)
             else:
@@ -229,6 +235,105 @@ def test_g2p_project_equals_the_two_calls(mpm, dim):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), what
     assert out[0][3] == out[1][3]
     assert out[1][3][0] >= 80 + 20 and out[1][3][2] > 0       # skipped, refused and clamped particles
+
+
+@pytest.mark.parametrize("dim", [2, 3])
+def test_g2p_project_records_rewrites_the_binning(mpm, dim):
+    """mpm_pbmpm_g2p_project_records on particles binned beforehand, on a
+    displacement grid of random values: x, d, D and the status counts of
+    mpm_pbmpm_g2p_project bit for bit; every binned record equal, bit for bit,
+    to the record the binning's scatter makes from the new state (x, d, D, m;
+    d, D and m zeroed where outside the ranges, which status[1] counts); the
+    next P2G on these records bit-identical to a P2G after a fresh binning.
+    Particles outside the grid (no record), at the clamp bounds, with an
+    inverted F, and outside each of the three ranges before or after the
+    gather are included.  A call with other ranges than the binning's is
+    refused on the device: status[3] counts it and nothing is written."""
+    from material_point_particle_amd import _lib as L
+    from material_point_particle_amd.transfer import DeviceParticles, Transfer
+    n, k = (64 if dim == 2 else 32), 40_003
+    rng = np.random.default_rng(70 + dim)
+    ranges = (2.0, 0.05, 0.4)
+    x = rng.uniform(1.0 / n, (n - 2.0) / n, (dim, k)).astype(np.float32)
+    x[0, :40] = 0.2 / n                          # outside the grid
+    x[0, 40:80] = 0.9 / n                        # inside, below the clamp bound dx
+    x[dim - 1, 80:120] = (n - 1.7) / n           # inside, above the clamp bound (n - 2) dx
+    d = (0.01 * rng.standard_normal((dim, k))).astype(np.float32)
+    d[0, 120:140] = 0.3                          # d out of range at binning (the gather replaces it)
+    D = (0.05 * rng.standard_normal((dim * dim, k))).astype(np.float32)
+    D[1, 140:160] = 3.0                          # out of range at binning
+    m = rng.uniform(0.5, 1.5, k).astype(np.float32)
+    m[160:170] = 5.0                             # out of the mass range for good
+    F = (np.eye(dim).reshape(dim * dim, 1) + 0.1 * rng.standard_normal((dim * dim, k))).astype(np.float32)
+    F[0, 170:210] = -3.0                         # det F < 0 for most: the gathered D stays
+    dg = (0.002 * rng.standard_normal((dim,) + (n,) * dim)).astype(np.float32)
+    dg[0, 5:9] = 0.2                             # some gathered d out of range
+    host = {"x": x, "v": d, "C": D, "m": m}
+    desc = L.grid_desc(dim, n, 32)
+    dgd, Fd = dev(dg), dev(F)
+
+    ref = DeviceParticles({kk: a.copy() for kk, a in host.items()})
+    st_ref = torch.zeros(4, dtype=torch.int32, device="cuda")
+    L.mpm_pbmpm_g2p_project(desc, dgd, ref.desc(), Fd, 1.5, 12, st_ref)
+
+    parts = DeviceParticles({kk: a.copy() for kk, a in host.items()})
+    tr = Transfer(dim, n, 32, ranges, k)
+    tr.bin(parts)
+    torch.cuda.synchronize()
+    st_bin = u32(tr.status).copy()
+    tr.status.zero_()
+    L.mpm_pbmpm_g2p_project_records(desc, dgd, parts.desc(), Fd, 1.5, 12, tr.ranges, tr.ws, tr.status)
+    torch.cuda.synchronize()
+    st = u32(tr.status).tolist()
+    got, want = parts.host(), ref.host()
+    for key in ("x", "v", "C"):
+        assert np.array_equal(got[key].view(np.uint32), want[key].view(np.uint32)), key
+    assert st[0] == u32(st_ref)[0] and st[2] == u32(st_ref)[2] and st[3] == 0
+    assert st[0] >= 40 and st[2] > 0
+
+    # the records against the scatter's rule, from the new state
+    lay = tr.layout
+    R = lay.n_fields
+    slot = u32(tr.ws_u32("slot", k)).astype(np.int64)
+    has = slot != 0xFFFFFFFF
+    assert int(has.sum()) == k - 40 and not has[:40].any()
+    recs = tr.ws.view(torch.float32)[lay.sorted // 4: lay.sorted // 4 + R * (int(slot[has].max()) + 1)]
+    recs = recs.view(-1, R).cpu().numpy()
+    xs, ds, Ds = got["x"], got["v"], got["C"]
+    rm, rv, ra = (np.float32(r) for r in ranges)
+    inr = (np.abs(m) <= rm) & (np.abs(ds) <= rv).all(0) & (np.abs(Ds) <= ra).all(0)
+    exp = np.zeros((k, R), np.float32)
+    exp[:, :dim] = xs.T
+    exp[:, dim:2 * dim] = ds.T
+    exp[:, 2 * dim:2 * dim + dim * dim] = Ds.T
+    exp[:, 2 * dim + dim * dim] = m
+    exp[~inr, dim:] = 0.0
+    assert np.array_equal(recs[slot[has]].view(np.uint32), exp[has].view(np.uint32))
+    assert st[1] == int((has & ~inr).sum()) and st[1] > 0
+    assert st_bin[1] == int((has & ~((np.abs(m) <= rm) & (np.abs(d) <= rv).all(0)
+                                     & (np.abs(D) <= ra).all(0))).sum())
+    say("g2p + projection + records", dim, st, "out of range", int((has & ~inr).sum()))
+
+    # the next P2G: refreshed records against a fresh binning of the new state
+    g1 = tr.p2g(parts, binned=True).clone()
+    tr2 = Transfer(dim, n, 32, ranges, k)
+    tr2.bin(parts)
+    g2 = tr2.p2g(parts, binned=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g1, g2)
+    assert u32(tr.status)[3] == 0 and u32(tr2.status)[3] == 0
+
+    # other ranges than the binning's: refused on the device, nothing written
+    tr.bin(parts)
+    torch.cuda.synchronize()
+    before = [t.clone() for t in (parts.x, parts.v, parts.C, tr.ws)]
+    tr.status.zero_()
+    L.mpm_pbmpm_g2p_project_records(desc, dgd, parts.desc(), Fd, 1.5, 12, L.ranges(2.0, 0.06, 0.4), tr.ws,
+                                    tr.status)
+    torch.cuda.synchronize()
+    assert u32(tr.status).tolist() == [0, 0, 0, 1]
+    for a, b in zip(before, (parts.x, parts.v, parts.C, tr.ws)):
+        assert torch.equal(a, b)
 
 
 def test_square_2d_substeps_in_lockstep(mpm, oracle_lib):
