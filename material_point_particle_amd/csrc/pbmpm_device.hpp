@@ -33,6 +33,47 @@ __device__ __forceinline__ double pbmpm_cofactor(const double (&a)[3][3], double
     }
 }
 
+// Quotients a / b of several numerators over one positive denominator b,
+// each bit-identical to the correctly rounded float64 division that the
+// compiler emits for a / b.  That division scales both operands when their
+// exponents are extreme, takes the hardware reciprocal of the (scaled)
+// denominator and refines it with two Newton steps, multiplies the numerator
+// by it, corrects the product once with its exact FMA residual, and fixes up
+// special values.  Inside the range that div_safe accepts no scaling and no
+// fix-up happens (no operand, reciprocal or quotient is denormal, zero,
+// infinite or near overflow, and the exponents differ by far less than the
+// 768 at which the denominator is scaled), so the reciprocal and its two
+// refinements depend on b alone and are formed once for all numerators; each
+// quotient then costs a multiply and two FMAs instead of the whole sequence.
+// The final correction is written as -fma(-e, r, -q), the same rounding as
+// fma(e, r, q), so that a -0 numerator gives -0 as the division does.
+__device__ __forceinline__ double recip_refined(double b)
+{
+    double r = __builtin_amdgcn_rcp(b);
+    double t = __builtin_fma(-b, r, 1.0);
+    r = __builtin_fma(r, t, r);
+    t = __builtin_fma(-b, r, 1.0);
+    return __builtin_fma(r, t, r);
+}
+
+__device__ __forceinline__ double div_refined(double a, double b, double rb)
+{
+    const double q = a * rb;
+    const double e = __builtin_fma(-b, q, a);
+    return -__builtin_fma(-e, rb, -q);
+}
+
+// The operands for which div_refined equals a / b: a denominator in
+// [2^-100, 2^100] and numerators that are zero or in [2^-700, 2^200] in
+// magnitude (quotients then in [2^-800, 2^300]).
+// (Bitwise, not short-circuit, operators: the tests are compares, not branches.)
+__device__ __forceinline__ bool div_denominator_safe(double b) { return (b >= 0x1p-100) & (b <= 0x1p100); }
+__device__ __forceinline__ bool div_numerator_safe(double a)
+{
+    const double m = fabs(a);
+    return (a == 0.0) | ((m >= 0x1p-700) & (m <= 0x1p200));
+}
+
 // particleUpdate for an elastic material: the target shape is the polar
 // rotation R of the trial deformation Ft = (I + D) F (Newton's iteration
 // R <- (R + R^-T) / 2 from R = Ft, polar_iters steps); the displacement
@@ -47,7 +88,8 @@ __device__ __forceinline__ double pbmpm_cofactor(const double (&a)[3][3], double
 // q = d * DIM + e); the new D goes out through store(q, value), entry by
 // entry as it is formed (so that no second copy of it stays live).  Returns
 // false, with nothing stored, when Ft, F or a Newton iterate has a
-// non-positive determinant.
+// non-positive determinant.  The divisions by det R and det F run through
+// div_refined where div_safe allows (the same bits as the division).
 template <int DIM, class LoadF, class Store>
 __device__ __forceinline__ bool pbmpm_project_particle(LoadF &&loadF, const float (&D)[DIM * DIM], double relax,
                                                        int polar_iters, Store &&store)
@@ -80,21 +122,51 @@ __device__ __forceinline__ bool pbmpm_project_particle(LoadF &&loadF, const floa
             ok = false;
             break;
         }
+        bool fast = div_denominator_safe(det);
 #pragma unroll
         for (int d = 0; d < DIM; ++d)
 #pragma unroll
             for (int e = 0; e < DIM; ++e)
-                r[d][e] = (r[d][e] + cof[d][e] / det) * 0.5;
+                fast = fast & div_numerator_safe(cof[d][e]);
+        if (fast) {
+            const double rdet = recip_refined(det);
+#pragma unroll
+            for (int d = 0; d < DIM; ++d)
+#pragma unroll
+                for (int e = 0; e < DIM; ++e)
+                    r[d][e] = (r[d][e] + div_refined(cof[d][e], det, rdet)) * 0.5;
+        } else {
+#pragma unroll
+            for (int d = 0; d < DIM; ++d)
+#pragma unroll
+                for (int e = 0; e < DIM; ++e)
+                    r[d][e] = (r[d][e] + cof[d][e] / det) * 0.5;
+        }
     }
     const double detf = ok ? pbmpm_cofactor<DIM>(f, cof) : 0.0;
     if (!ok || !(detf > 0.0))
         return false;
     double finv[3][3];
+    bool fast = div_denominator_safe(detf);
 #pragma unroll
     for (int q = 0; q < DIM; ++q)
 #pragma unroll
         for (int e = 0; e < DIM; ++e)
-            finv[q][e] = cof[e][q] / detf;
+            fast = fast & div_numerator_safe(cof[e][q]);
+    if (fast) {
+        const double rdet = recip_refined(detf);
+#pragma unroll
+        for (int q = 0; q < DIM; ++q)
+#pragma unroll
+            for (int e = 0; e < DIM; ++e)
+                finv[q][e] = div_refined(cof[e][q], detf, rdet);
+    } else {
+#pragma unroll
+        for (int q = 0; q < DIM; ++q)
+#pragma unroll
+            for (int e = 0; e < DIM; ++e)
+                finv[q][e] = cof[e][q] / detf;
+    }
 #pragma unroll
     for (int d = 0; d < DIM; ++d)
 #pragma unroll
