@@ -114,33 +114,33 @@ __device__ __forceinline__ bool pbmpm_project_particle(LoadF &&loadF, const floa
             r[d][e] = t;
         }
     bool ok = pbmpm_cofactor<DIM>(ft, cof) > 0.0;
+    // A lane whose iterate turns singular stops updating R (and returns
+    // false); the loop has no early exit, so R needs no copy per step.
     for (int k = 0; k < polar_iters; ++k) {
-        if (!ok)
-            break;
-        const double det = pbmpm_cofactor<DIM>(r, cof);
-        if (!(det > 0.0)) {
-            ok = false;
-            break;
-        }
-        bool fast = div_denominator_safe(det);
-#pragma unroll
-        for (int d = 0; d < DIM; ++d)
-#pragma unroll
-            for (int e = 0; e < DIM; ++e)
-                fast = fast & div_numerator_safe(cof[d][e]);
-        if (fast) {
-            const double rdet = recip_refined(det);
+        if (ok) {
+            const double det = pbmpm_cofactor<DIM>(r, cof);
+            bool fast = div_denominator_safe(det);
 #pragma unroll
             for (int d = 0; d < DIM; ++d)
 #pragma unroll
                 for (int e = 0; e < DIM; ++e)
-                    r[d][e] = (r[d][e] + div_refined(cof[d][e], det, rdet)) * 0.5;
-        } else {
+                    fast = fast & div_numerator_safe(cof[d][e]);
+            if (!(det > 0.0)) {
+                ok = false;
+            } else if (fast) {
+                const double rdet = recip_refined(det);
 #pragma unroll
-            for (int d = 0; d < DIM; ++d)
+                for (int d = 0; d < DIM; ++d)
 #pragma unroll
-                for (int e = 0; e < DIM; ++e)
-                    r[d][e] = (r[d][e] + cof[d][e] / det) * 0.5;
+                    for (int e = 0; e < DIM; ++e)
+                        r[d][e] = (r[d][e] + div_refined(cof[d][e], det, rdet)) * 0.5;
+            } else {
+#pragma unroll
+                for (int d = 0; d < DIM; ++d)
+#pragma unroll
+                    for (int e = 0; e < DIM; ++e)
+                        r[d][e] = (r[d][e] + cof[d][e] / det) * 0.5;
+            }
         }
     }
     const double detf = ok ? pbmpm_cofactor<DIM>(f, cof) : 0.0;
