@@ -119,7 +119,8 @@ __device__ __forceinline__ bool pbmpm_project_particle(LoadF &&loadF, const floa
     for (int k = 0; k < polar_iters; ++k) {
         if (ok) {
             const double det = pbmpm_cofactor<DIM>(r, cof);
-            bool fast = div_denominator_safe(det);
+            const double det2 = det + det;               // exact
+            bool fast = div_denominator_safe(det2);
 #pragma unroll
             for (int d = 0; d < DIM; ++d)
 #pragma unroll
@@ -128,12 +129,16 @@ __device__ __forceinline__ bool pbmpm_project_particle(LoadF &&loadF, const floa
             if (!(det > 0.0)) {
                 ok = false;
             } else if (fast) {
-                const double rdet = recip_refined(det);
+                // RN(RN(R + q) / 2) with q = RN(cof / det) is RN(R / 2 +
+                // RN(cof / (2 det))), one FMA: halving commutes with rounding
+                // in the normal range, and here q/2 is 0 or at least 2^-801 in
+                // magnitude, so neither side rounds into the subnormals.
+                const double rdet2 = recip_refined(det2);
 #pragma unroll
                 for (int d = 0; d < DIM; ++d)
 #pragma unroll
                     for (int e = 0; e < DIM; ++e)
-                        r[d][e] = (r[d][e] + div_refined(cof[d][e], det, rdet)) * 0.5;
+                        r[d][e] = __builtin_fma(r[d][e], 0.5, div_refined(cof[d][e], det2, rdet2));
             } else {
 #pragma unroll
                 for (int d = 0; d < DIM; ++d)
