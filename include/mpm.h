@@ -506,6 +506,23 @@ int mpm_update_deformation_stress(const mpm_grid_desc *grid, const mpm_particles
                                   const float *vol0, float dt, float mu, float lambda, float *C_out, uint32_t *status,
                                   hipStream_t stream);
 
+/* The elastic substep's G2P and the pass after it, in one launch: exactly
+ * mpm_g2p (the gather and advection from vg, with dt) followed by
+ * mpm_update_deformation_stress (F updated with the new C, then C_out = C' of
+ * the next substep from the updated F), the same operations in the same
+ * order, so the results and the status counts are bit-identical to those two
+ * calls in sequence.  The gather runs over the particles first and the second
+ * pass reads back the C it wrote.
+ * vg: device float[dim][nodes].  particles: device; x, v, C read and written,
+ * m read.  F: device float[dim*dim][n], read and written.  vol0: device
+ * float[n].  C_out: device float[dim*dim][n], written (may alias neither C nor
+ * F).  status[0] counts particles outside the grid and particles whose
+ * updated F has det <= 0, status[2] clamped particles.
+ * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
+int mpm_g2p_update_deformation_stress(const mpm_grid_desc *grid, const float *vg, const mpm_particles *particles,
+                                      float dt, float *F, const float *vol0, float mu, float lambda, float *C_out,
+                                      uint32_t *status, hipStream_t stream);
+
 /* ---- Position-based MPM (PB-MPM): the iteration loop for an elastic material ----
  *
  * "Implementation -- GPU Optimization & Reference Codebases", section 3.3.2.

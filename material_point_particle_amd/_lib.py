@@ -56,7 +56,7 @@ EXPORTS = ("mpm_version", "mpm_strerror", "mpm_check_bounds", "mpm_workspace_byt
            "mpm_bin_resident", "mpm_g2p2g", "mpm_grid_clear_tiles", "mpm_gather_records",
            "mpm_p2g_isplit_noalloc", "mpm_pbmpm_project_elastic", "mpm_pbmpm_grid_update", "mpm_pbmpm_integrate",
            "mpm_grid_update_tiles", "mpm_g2p_records", "mpm_update_deformation_stress",
-           "mpm_pbmpm_g2p_project", "mpm_pbmpm_g2p_project_records")
+           "mpm_pbmpm_g2p_project", "mpm_pbmpm_g2p_project_records", "mpm_g2p_update_deformation_stress")
 
 _lib = None
 
@@ -127,6 +127,10 @@ def lib() -> ct.CDLL:
         L.mpm_pbmpm_g2p_project.restype = ct.c_int
         L.mpm_pbmpm_g2p_project.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_void_p, ct.c_float,
                                             ct.c_int32, ct.c_void_p, ct.c_void_p]
+        L.mpm_g2p_update_deformation_stress.restype = ct.c_int
+        L.mpm_g2p_update_deformation_stress.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_float,
+                                                        ct.c_void_p, ct.c_void_p, ct.c_float, ct.c_float, ct.c_void_p,
+                                                        ct.c_void_p, ct.c_void_p]
         L.mpm_pbmpm_g2p_project_records.restype = ct.c_int
         L.mpm_pbmpm_g2p_project_records.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_void_p,
                                                     ct.c_float, ct.c_int32, P(mpm_ranges), ct.c_void_p, ct.c_size_t,
@@ -334,6 +338,13 @@ def mpm_pbmpm_g2p_project(desc, dg, parts: mpm_particles, F, relax: float, polar
                           stream=None) -> None:
     _check(lib().mpm_pbmpm_g2p_project(ct.byref(desc), _ptr(dg), ct.byref(parts), _ptr(F), relax, polar_iters,
                                        _ptr(status), _stream(stream)), "mpm_pbmpm_g2p_project")
+
+
+def mpm_g2p_update_deformation_stress(desc, vg, parts: mpm_particles, dt: float, F, vol0, mu: float, lam: float,
+                                      C_out, status, stream=None) -> None:
+    _check(lib().mpm_g2p_update_deformation_stress(ct.byref(desc), _ptr(vg), ct.byref(parts), dt, _ptr(F), _ptr(vol0),
+                                                   mu, lam, _ptr(C_out), _ptr(status), _stream(stream)),
+           "mpm_g2p_update_deformation_stress")
 
 
 def mpm_pbmpm_g2p_project_records(desc, dg, parts: mpm_particles, F, relax: float, polar_iters: int,

@@ -587,6 +587,25 @@ int mpm_update_deformation_stress(const mpm_grid_desc *grid, const mpm_particles
                                              lambda, C_out, status, stream));
 }
 
+int mpm_g2p_update_deformation_stress(const mpm_grid_desc *grid, const float *vg, const mpm_particles *particles,
+                                      float dt, float *F, const float *vol0, float mu, float lambda, float *C_out,
+                                      uint32_t *status, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_desc(grid)) != MPM_OK || (rc = check_particles(grid, particles, true, true)) != MPM_OK)
+        return rc;
+    const int64_t np = particles->n;
+    if (!aligned(vg, 4) || !aligned(status, 4))
+        return MPM_ERR_INVALID;
+    if (np > 0 && (!particles->C || !F || !vol0 || !C_out || !aligned(particles->C, 4) || !aligned(F, 4) ||
+                   !aligned(vol0, 4) || !aligned(C_out, 4) || C_out == particles->C || C_out == F))
+        return MPM_ERR_INVALID;
+    if (!(dt >= 0.0f) || !(mu >= 0.0f) || !(lambda >= 0.0f))
+        return MPM_ERR_INVALID;
+    return hip_status(launch_g2p_stress(grid->dim, grid->n, vg, particles->x, particles->v, particles->C, np, dt, F,
+                                        particles->m, vol0, mu, lambda, C_out, status, stream));
+}
+
 int mpm_pbmpm_project_elastic(const mpm_grid_desc *grid, const mpm_particles *particles, const float *F, float relax,
                               int32_t polar_iters, uint32_t *status, hipStream_t stream)
 {

@@ -8,6 +8,7 @@
 // solver to the grid velocity).
 #include "pbmpm_device.hpp"
 #include "resident.hpp"
+#include "stress.hpp"
 
 namespace mpmk {
 namespace {
@@ -129,8 +130,47 @@ __global__ void __launch_bounds__(256) clear_kernel(int64_t *__restrict__ grid, 
         grid[i] = 0;
 }
 
-// One thread per particle: the APIC gather and advection of g2p_particle,
-// reading the grid velocity of the stencil's nodes from vg.
+// The APIC gather and advection of g2p_particle for particle p, reading the
+// grid velocity of the stencil's nodes from vg (nodes per component plane);
+// particles outside the grid are counted in status[0] and left as they are,
+// clamped ones in status[2].
+template <int DIM>
+__device__ __forceinline__ void g2p_one(int64_t p, int n, int64_t nodes, float nf, float dx, float last_base,
+                                        const float *__restrict__ vg, float *__restrict__ x, float *__restrict__ v,
+                                        float *__restrict__ C, int64_t np, float dt, float lo, float hi, float cscale,
+                                        uint32_t *__restrict__ status)
+{
+    Axis ax[DIM];
+    float xp[DIM];
+    bool ok = true;
+#pragma unroll
+    for (int e = 0; e < DIM; ++e) {
+        xp[e] = x[e * np + p];
+        ok = axis_stencil(xp[e], nf, dx, last_base, ax[e]) && ok;
+    }
+    wave_count(!ok, &status[0]);
+    if (!ok)
+        return;
+    const int bz = DIM == 3 ? ax[DIM - 1].base : 0;
+    auto vel = [&](int a, int b, int c, int d) {
+        const int64_t node = DIM == 3 ? ((int64_t)(bz + c) * n + (ax[1].base + b)) * n + (ax[0].base + a)
+                                      : (int64_t)(ax[1].base + b) * n + (ax[0].base + a);
+        return vg[d * nodes + node];
+    };
+    float vn[DIM], Cn[DIM * DIM], xn[DIM];
+    const bool clamped = g2p_particle<DIM>(ax, xp, vel, dt, lo, hi, cscale, vn, Cn, xn);
+#pragma unroll
+    for (int d = 0; d < DIM; ++d) {
+#pragma unroll
+        for (int e = 0; e < DIM; ++e)
+            C[(int64_t)(d * DIM + e) * np + p] = Cn[d * DIM + e];
+        v[d * np + p] = vn[d];
+        x[d * np + p] = xn[d];
+    }
+    wave_count(clamped, &status[2]);
+}
+
+// One thread per particle: g2p_one.
 template <int DIM>
 __global__ void __launch_bounds__(256) g2p_kernel(int n, float nf, float dx, float last_base,
                                                   const float *__restrict__ vg, float *__restrict__ x,
@@ -138,35 +178,40 @@ __global__ void __launch_bounds__(256) g2p_kernel(int n, float nf, float dx, flo
                                                   float lo, float hi, float cscale, uint32_t *__restrict__ status)
 {
     const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x)
+        g2p_one<DIM>(p, n, nodes, nf, dx, last_base, vg, x, v, C, np, dt, lo, hi, cscale, status);
+}
+
+// The elastic substep's G2P and then the F update with the next substep's
+// stressed affine matrix (update_F_stress_kernel's arithmetic), in one
+// launch: the gather runs over the thread's particles first, then a second
+// loop over the same particles reads back the C just written, with F, m and
+// vol0, and writes F and C'.  Memory ends as after the two kernels in
+// sequence.  The two loops keep the gather's registers (the two bodies in one
+// loop need 144 and leave 3 waves per SIMD), and waves in the load-bound
+// gather run beside waves in the streaming second loop.
+template <int DIM>
+__global__ void __launch_bounds__(256) g2p_stress_kernel(int n, float nf, float dx, float last_base,
+                                                         const float *__restrict__ vg, float *__restrict__ x,
+                                                         float *__restrict__ v, float *__restrict__ C, int64_t np,
+                                                         float dt, float lo, float hi, float cscale,
+                                                         uint32_t *__restrict__ status, double scale,
+                                                         float *__restrict__ F, const float *__restrict__ m,
+                                                         const float *__restrict__ vol0, float mu, float lambda,
+                                                         float *__restrict__ Cout)
+{
+    const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x)
+        g2p_one<DIM>(p, n, nodes, nf, dx, last_base, vg, x, v, C, np, dt, lo, hi, cscale, status);
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
-        Axis ax[DIM];
-        float xp[DIM];
-        bool ok = true;
-#pragma unroll
-        for (int e = 0; e < DIM; ++e) {
-            xp[e] = x[e * np + p];
-            ok = axis_stencil(xp[e], nf, dx, last_base, ax[e]) && ok;
-        }
-        wave_count(!ok, &status[0]);
-        if (!ok)
-            continue;
-        const int bz = DIM == 3 ? ax[DIM - 1].base : 0;
-        auto vel = [&](int a, int b, int c, int d) {
-            const int64_t node = DIM == 3 ? ((int64_t)(bz + c) * n + (ax[1].base + b)) * n + (ax[0].base + a)
-                                          : (int64_t)(ax[1].base + b) * n + (ax[0].base + a);
-            return vg[d * nodes + node];
-        };
-        float vn[DIM], Cn[DIM * DIM], xn[DIM];
-        const bool clamped = g2p_particle<DIM>(ax, xp, vel, dt, lo, hi, cscale, vn, Cn, xn);
-#pragma unroll
-        for (int d = 0; d < DIM; ++d) {
-#pragma unroll
-            for (int e = 0; e < DIM; ++e)
-                C[(int64_t)(d * DIM + e) * np + p] = Cn[d * DIM + e];
-            v[d * np + p] = vn[d];
-            x[d * np + p] = xn[d];
-        }
-        wave_count(clamped, &status[2]);
+        float f[DIM][DIM], c[DIM][DIM], out[DIM][DIM];
+        load_mat<DIM>(C, np, p, c);
+        load_mat<DIM>(F, np, p, f);
+        updated_F<DIM>(c, dt, f);
+        store_mat<DIM>(F, np, p, f);
+        const bool inverted = stressed_affine<DIM>(f, c, m[p], vol0[p], scale, dt, mu, lambda, out);
+        wave_count(inverted, &status[0]);
+        store_mat<DIM>(Cout, np, p, out);
     }
 }
 
@@ -435,6 +480,16 @@ int blocks_for(int64_t work, int block)
     return (int)(want < 1 ? 1 : (want > cap ? cap : want));
 }
 
+// One thread per particle (grid of at most 2^24 blocks for the particle
+// counts accepted here): for the kernels whose second loop reads back what
+// the first wrote for the same particle, so that the read follows the write
+// closely and finds it in the cache.
+unsigned blocks_one_each(int64_t np)
+{
+    const int64_t want = (np + 255) / 256;
+    return (unsigned)(want < 1 ? 1 : want);
+}
+
 }  // namespace
 
 namespace {
@@ -573,7 +628,7 @@ hipError_t launch_pbmpm_g2p_project(int dim, int n, const float *dg, float *x, f
         rr.r = r;
         rr.m = m;
     }
-    const dim3 grid(blocks_for(np, 256)), block(256);
+    const dim3 grid(bins ? blocks_one_each(np) : (unsigned)blocks_for(np, 256)), block(256);
     if (dim == 3) {
         if (bins)
             hipLaunchKernelGGL((g2p_project_kernel<3, true>), grid, block, 0, s, n, nf, dx, last, dg, x, d, D, np, lo,
@@ -589,6 +644,25 @@ hipError_t launch_pbmpm_g2p_project(int dim, int n, const float *dg, float *x, f
             hipLaunchKernelGGL((g2p_project_kernel<2, false>), grid, block, 0, s, n, nf, dx, last, dg, x, d, D, np, lo,
                                hi, cscale, F, (double)relax, polar_iters, status, rr);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_g2p_stress(int dim, int n, const float *vg, float *x, float *v, float *C, int64_t np, float dt,
+                             float *F, const float *m, const float *vol0, float mu, float lambda, float *Cout,
+                             uint32_t *status, hipStream_t s)
+{
+    if (np == 0)
+        return hipSuccess;
+    const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3);
+    const float lo = dx, hi = (float)(n - 2) * dx;
+    const float cscale = 4.0f * (float)n * (float)n;
+    const double scale = 4.0 * (double)n * (double)n;
+    if (dim == 3)
+        hipLaunchKernelGGL(g2p_stress_kernel<3>, dim3(blocks_one_each(np)), dim3(256), 0, s, n, nf, dx, last, vg, x,
+                           v, C, np, dt, lo, hi, cscale, status, scale, F, m, vol0, mu, lambda, Cout);
+    else
+        hipLaunchKernelGGL(g2p_stress_kernel<2>, dim3(blocks_one_each(np)), dim3(256), 0, s, n, nf, dx, last, vg, x,
+                           v, C, np, dt, lo, hi, cscale, status, scale, F, m, vol0, mu, lambda, Cout);
     return hipGetLastError();
 }
 

@@ -58,6 +58,11 @@ class ElasticParticles(DeviceParticles):
         """update_F, then stress() for the next substep, in one pass."""
         L.mpm_update_deformation_stress(tr.desc, self.desc(), self.F, self.vol0, dt, mu, lam, self.C_aff, tr.status)
 
+    def g2p_update_F_stress(self, tr: "Transfer", dt: float, mu: float, lam: float) -> None:
+        """tr.g2p(self, dt), then update_F_stress, in one launch."""
+        L.mpm_g2p_update_deformation_stress(tr.desc, tr.vg, self.desc(), dt, self.F, self.vol0, mu, lam, self.C_aff,
+                                            tr.status)
+
     def host(self) -> dict:
         h = super().host()
         h["F"] = self.F.cpu().numpy()

@@ -247,6 +247,22 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert fused(ct.byref(d), ct.byref(p4), *okf[:5], ct.c_void_p(4096), status, None) == L.MPM_ERR_INVALID  # C' = C
     assert fused(ct.byref(d), ct.byref(p4), *okf[:5], ct.c_void_p(8192), status, None) == L.MPM_ERR_INVALID  # C' = F
     assert fused(None, ct.byref(p4), *okf, None) == L.MPM_ERR_INVALID
+    # G2P with the F update and stress in one launch: vg, particles, dt, F, vol0, mu, lambda, C_out, status
+    g2s = lib.mpm_g2p_update_deformation_stress
+    VG8 = ct.c_void_p(20480)
+    ok2 = (ct.c_void_p(8192), ct.c_void_p(12288), 1e5, 1e5, ct.c_void_p(16384), status)
+    assert g2s(ct.byref(d), VG8, ct.byref(p3), 1e-4, *ok2, None) == L.MPM_ERR_INVALID               # no C
+    assert g2s(ct.byref(d), VG8, ct.byref(L.mpm_particles(10, 4096, 4096, 4096, None)), 1e-4, *ok2,
+               None) == L.MPM_ERR_INVALID                                                        # no m
+    assert g2s(ct.byref(d), None, ct.byref(p4), 1e-4, *ok2, None) == L.MPM_ERR_INVALID              # no vg
+    assert g2s(ct.byref(d), VG8, ct.byref(p4), 1e-4, None, *ok2[1:], None) == L.MPM_ERR_INVALID     # no F
+    assert g2s(ct.byref(d), VG8, ct.byref(p4), -1e-4, *ok2, None) == L.MPM_ERR_INVALID
+    assert g2s(ct.byref(d), VG8, ct.byref(p4), 1e-4, *ok2[:2], -1.0, *ok2[3:], None) == L.MPM_ERR_INVALID
+    assert g2s(ct.byref(d), VG8, ct.byref(p4), 1e-4, *ok2[:4], ct.c_void_p(4096), status,
+               None) == L.MPM_ERR_INVALID                                                        # C' = C
+    assert g2s(ct.byref(d), VG8, ct.byref(p4), 1e-4, *ok2[:4], ct.c_void_p(8192), status,
+               None) == L.MPM_ERR_INVALID                                                        # C' = F
+    assert g2s(None, VG8, ct.byref(p4), 1e-4, *ok2, None) == L.MPM_ERR_INVALID
     # PB-MPM gather with the next projection: dg, particles, F, relax, iterations, status
     gp = lib.mpm_pbmpm_g2p_project
     dg = ct.c_void_p(20480)
@@ -314,4 +330,6 @@ def test_empty_calls_of_the_one_pass_entry_points_return_before_any_launch():
     assert lib.mpm_pbmpm_g2p_project_records(ct.byref(d), fake, ct.byref(p0), None, 1.5, 12, ct.byref(r), fake,
                                              M.mpm_workspace_bytes(d, 0), fake, None) == L.MPM_OK
     assert lib.mpm_update_deformation(ct.byref(d), ct.byref(p0), None, 1e-4, None) == L.MPM_OK
+    assert lib.mpm_g2p_update_deformation_stress(ct.byref(d), fake, ct.byref(p0), 1e-4, None, None, 1e5, 1e5, None,
+                                                 fake, None) == L.MPM_OK
 

@@ -135,12 +135,53 @@ def test_fused_update_and_stress_equals_the_two_calls(mpm, oracle_lib, dim):
     assert ref_st.tolist() == st
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_elastic_substeps_match_oracle(mpm, oracle_lib, fused):
+@pytest.mark.parametrize("dim", [2, 3])
+def test_g2p_update_stress_equals_the_two_calls(mpm, dim):
+    """mpm_g2p_update_deformation_stress against mpm_g2p followed by
+    mpm_update_deformation_stress on the same inputs and a grid velocity of
+    random values: x, v, C, F and C' bit-identical, the same status counts.
+    Some particles sit outside the grid (the gather leaves them, the F update
+    still runs on their C), some at the clamp bounds, some are inverted after
+    the update, some massless."""
+    from material_point_particle_amd import _lib as L
+    from material_point_particle_amd.transfer import ElasticParticles, Transfer
+    np_, n = 60_001, (64 if dim == 2 else 32)
+    host, F, vol0 = random_solid(dim, np_, 77 + dim, inverted=31)
+    rng = np.random.default_rng(90 + dim)
+    host["x"] = rng.uniform(1.0 / n, (n - 2.0) / n, (dim, np_)).astype(np.float32)
+    host["x"][0, 31:70] = 0.2 / n                           # outside the grid
+    host["x"][dim - 1, 70:110] = (n - 1.7) / n              # inside, above the clamp bound
+    host["C"] *= 30.0
+    vg = (0.5 * rng.standard_normal((dim,) + (n,) * dim)).astype(np.float32)
+    dt, mu, lam = 2e-3, 2.0e8, 3.0e8
+    out = []
+    for one in (False, True):
+        parts = ElasticParticles(host, F, vol0)
+        tr = Transfer(dim, n, 24, (2.0, 10.0, 1e6), np_)
+        tr.vg.copy_(torch.from_numpy(vg))
+        if one:
+            parts.g2p_update_F_stress(tr, dt, mu, lam)
+        else:
+            tr.g2p(parts, dt)
+            parts.update_F_stress(tr, dt, mu, lam)
+        torch.cuda.synchronize()
+        out.append([t.cpu().numpy().view(np.uint32) for t in (parts.x, parts.v, parts.C, parts.F, parts.C_aff)]
+                   + [tr.status.cpu().numpy().view(np.uint32).tolist()])
+    say("G2P with the F update and stress, one launch", dim, out[1][5])
+    for a, b, what in zip(out[0][:5], out[1][:5], ("x", "v", "C", "F", "C'")):
+        assert np.array_equal(a, b), what
+    assert out[0][5] == out[1][5]
+    st = out[1][5]
+    assert st[0] >= 39 + 31 and st[2] > 0                  # outside, inverted; clamped
+
+
+@pytest.mark.parametrize("form", ["separate", "fused", "one_launch"])
+def test_elastic_substeps_match_oracle(mpm, oracle_lib, form):
     """An elastic cube thrown at the floor (32,768 particles, 64^3 nodes): the
     substep stress -> bin -> P2G (with C') -> restricted grid update -> G2P ->
     F update on the GPU (fused: the F update and the next substep's stress in
-    one call after G2P, the first substep's stress on its own).  At every 10th
+    one call after G2P, the first substep's stress on its own; one_launch: G2P
+    and that call as one, mpm_g2p_update_deformation_stress).  At every 10th
     substep the oracle recomputes that substep from the GPU's state before it:
     C' within one ulp (float64 log); given the GPU's C', the P2G grid, the
     particle state and F bit-exact."""
@@ -157,7 +198,7 @@ def test_elastic_substeps_match_oracle(mpm, oracle_lib, fused):
         if check:
             torch.cuda.synchronize()
             before = parts.host()
-        if not fused or k == 1:
+        if form == "separate" or k == 1:
             parts.stress(tr, ex["dt"], ex["mu"], ex["lam"])
         tr.bin(parts.affine())
         tr.p2g(parts.affine(), binned=True)
@@ -166,16 +207,19 @@ def test_elastic_substeps_match_oracle(mpm, oracle_lib, fused):
             c_aff = parts.C_aff.cpu().numpy()
             grid = tr.grid.cpu().numpy()
         tr.grid_update(ex["dt"], ex["gravity"], ex["sticky"], active=True)
-        tr.g2p(parts, ex["dt"])
-        if fused:
-            parts.update_F_stress(tr, ex["dt"], ex["mu"], ex["lam"])
+        if form == "one_launch":
+            parts.g2p_update_F_stress(tr, ex["dt"], ex["mu"], ex["lam"])
         else:
-            parts.update_F(tr, ex["dt"])
+            tr.g2p(parts, ex["dt"])
+            if form == "fused":
+                parts.update_F_stress(tr, ex["dt"], ex["mu"], ex["lam"])
+            else:
+                parts.update_F(tr, ex["dt"])
         if not check:
             continue
         torch.cuda.synchronize()
         after = parts.host()
-        say("elastic substep", k, "fused" if fused else "")
+        say("elastic substep", k, form)
         ref_c, _ = oracle_lib.neohookean_affine(3, w.n, before, before["F"], host["vol"], ex["dt"], ex["mu"],
                                                 ex["lam"])
         assert_close_ulp(c_aff, ref_c, f"C' at substep {k}")
@@ -201,8 +245,8 @@ def test_elastic_substeps_match_oracle(mpm, oracle_lib, fused):
 @pytest.mark.timeout(900)
 def test_elastic_full_size_checked_substeps(mpm, oracle_lib):
     """The benchmark's elastic workload at full size (8M-particle jelly cube,
-    256^3 nodes) in the benchmark's loop (the F update fused with the next
-    substep's stress): 12 substeps on the GPU; substeps 6 and 12 are
+    256^3 nodes) in the benchmark's loop (G2P, the F update and the next
+    substep's stress in one launch): 12 substeps on the GPU; substeps 6 and 12 are
     recomputed by the oracle from the GPU state before them: C' within one
     float32 ulp, and given the GPU's C', the P2G grid, the particles and F
     bit-exact."""
@@ -229,8 +273,7 @@ def test_elastic_full_size_checked_substeps(mpm, oracle_lib):
             c_aff = parts.C_aff.cpu().numpy()
             grid = tr.grid.cpu().numpy()
         tr.grid_update(ex["dt"], ex["gravity"], ex["sticky"], active=True)
-        tr.g2p(parts, ex["dt"])
-        parts.update_F_stress(tr, ex["dt"], ex["mu"], ex["lam"])
+        parts.g2p_update_F_stress(tr, ex["dt"], ex["mu"], ex["lam"])
         if not check:
             continue
         torch.cuda.synchronize()
