@@ -481,9 +481,9 @@ int blocks_for(int64_t work, int block)
 }
 
 // One thread per particle (grid of at most 2^24 blocks for the particle
-// counts accepted here): for the kernels whose second loop reads back what
-// the first wrote for the same particle, so that the read follows the write
-// closely and finds it in the cache.
+// counts accepted here): for G2P, and for the kernels whose second loop
+// reads back what the first wrote for the same particle, so that the read
+// follows the write closely and finds it in the cache.
 unsigned blocks_one_each(int64_t np)
 {
     const int64_t want = (np + 255) / 256;
@@ -674,11 +674,12 @@ hipError_t launch_g2p(int dim, int n, const float *vg, float *x, float *v, float
     const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3);
     const float lo = dx, hi = (float)(n - 2) * dx;
     const float cscale = 4.0f * (float)n * (float)n;
+    // one thread per particle: 0.220 against 0.230 ms with a capped grid (8M particles)
     if (dim == 3)
-        hipLaunchKernelGGL(g2p_kernel<3>, dim3(blocks_for(np, 256)), dim3(256), 0, s, n, nf, dx, last, vg, x, v, C, np,
+        hipLaunchKernelGGL(g2p_kernel<3>, dim3(blocks_one_each(np)), dim3(256), 0, s, n, nf, dx, last, vg, x, v, C, np,
                            dt, lo, hi, cscale, status);
     else
-        hipLaunchKernelGGL(g2p_kernel<2>, dim3(blocks_for(np, 256)), dim3(256), 0, s, n, nf, dx, last, vg, x, v, C, np,
+        hipLaunchKernelGGL(g2p_kernel<2>, dim3(blocks_one_each(np)), dim3(256), 0, s, n, nf, dx, last, vg, x, v, C, np,
                            dt, lo, hi, cscale, status);
     return hipGetLastError();
 }

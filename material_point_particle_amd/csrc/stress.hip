@@ -75,11 +75,13 @@ __global__ void __launch_bounds__(256) update_F_stress_kernel(int64_t np, double
     }
 }
 
+// One thread per particle (measured faster than a grid of 16 blocks per CU
+// striding over several: 0.246 against 0.266 ms for the F update with stress
+// on 8M particles).
 int stress_blocks(int64_t np)
 {
     const int64_t want = (np + 255) / 256;
-    const int64_t cap = (int64_t)device_cu_count() * 16;
-    return (int)(want < 1 ? 1 : (want > cap ? cap : want));
+    return (int)(want < 1 ? 1 : want);
 }
 
 }  // namespace
