@@ -379,13 +379,14 @@ def measure_pbmpm(args, torch, w, build):
     loop = PBMPMSubsteps(tr, parts, ex["dt"], ex["gravity"], ex["iterations"], ex["relax"], ex["polar_iters"],
                          ex["band"])
     stream = torch.cuda.current_stream()
-    names = ("project", "bin", "p2g", "grid_update", "g2p_project", "g2p")
+    names = ("project", "bin", "p2g", "grid_update", "g2p_project", "g2p", "g2p_integrate")
     calls = {"project": loop.project,
              "bin": lambda: tr.bin(parts),
              "p2g": lambda: tr.p2g(parts, binned=True),
              "grid_update": lambda: L.mpm_pbmpm_grid_update(tr.desc, tr.ws, tr.grid, tr.vg, loop.band),
              "g2p_project": loop.gather_project,
-             "g2p": lambda: tr.g2p(parts, 0.0)}
+             "g2p": lambda: tr.g2p(parts, 0.0),
+             "g2p_integrate": loop.gather_integrate}
     last = loop.iterations - 1
 
     def stage_order():
@@ -393,7 +394,8 @@ def measure_pbmpm(args, torch, w, build):
         for it in range(loop.iterations):
             if it == 0 or not loop.records:
                 order.append("bin")
-            order += ["p2g", "grid_update", "g2p_project" if it < last else "g2p"]
+            order += ["p2g", "grid_update"]
+            order.append("g2p_project" if it < last else ("g2p_integrate" if loop.records else "g2p"))
         return order
 
     order = stage_order()
@@ -405,7 +407,8 @@ def measure_pbmpm(args, torch, w, build):
             calls[nm]()
         if ev:
             ev[len(order)].record(stream)
-        loop.integrate()
+        if order[-1] != "g2p_integrate":
+            loop.integrate()
         if ev:
             ev[len(order) + 1].record(stream)
 
@@ -426,7 +429,7 @@ def measure_pbmpm(args, torch, w, build):
             for i, nm in enumerate(order):
                 st[nm] += ev[i].elapsed_time(ev[i + 1])
             integ += ev[len(order)].elapsed_time(ev[len(order) + 1])
-        return start.elapsed_time(stop) / k, {nm: t / k for nm, t in st.items()}, integ / k
+        return start.elapsed_time(stop) / k, {nm: t / k for nm, t in st.items() if nm in order}, integ / k
 
     k = max(3, args.substeps // 4)
     start_state = [t.clone() for t in (parts.x, parts.v, parts.C, parts.F)]

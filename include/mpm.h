@@ -541,7 +541,9 @@ int mpm_g2p_update_deformation_stress(const mpm_grid_desc *grid, const float *vg
  *
  * d and D carry over to the next substep as its starting guess (warm start).
  * Every iteration's G2P but the last may run together with the next
- * iteration's projection (mpm_pbmpm_g2p_project), the same results in one pass.
+ * iteration's projection (mpm_pbmpm_g2p_project, or _records to skip the
+ * re-binning), and the last with the integrate step and the F update
+ * (mpm_pbmpm_g2p_integrate), the same results in fewer passes.
  */
 
 /* particleUpdate for an elastic material: the target shape is a rotation, the
@@ -600,6 +602,21 @@ int mpm_pbmpm_g2p_project(const mpm_grid_desc *grid, const float *dg, const mpm_
 int mpm_pbmpm_g2p_project_records(const mpm_grid_desc *grid, const float *dg, const mpm_particles *particles,
                                   const float *F, float relax, int32_t polar_iters, const mpm_ranges *ranges, void *ws,
                                   size_t ws_bytes, uint32_t *status, hipStream_t stream);
+
+/* The loop's last G2P gather and the end of the substep in one launch:
+ * exactly mpm_g2p with dt = 0 on dg (d and D gathered, x kept and clamped),
+ * then mpm_pbmpm_integrate (x += d clamped, d += g dt^2) and
+ * mpm_update_deformation with dt = 1 (F <- (I + D) F), the same operations in
+ * the same order, so the results and the status counts are bit-identical to
+ * those three calls in sequence.  A substep then ends with this call in place
+ * of its last mpm_g2p.
+ * dg: device float[dim][nodes].  particles: device; x, v (d) and C (D) read
+ * and written.  F: device float[dim*dim][n], read and written.  gravity: host
+ * float[dim].  status[0] counts particles outside the grid, status[2] clamps
+ * (by the gather and by the integrate step).
+ * Errors: MPM_ERR_INVALID, MPM_ERR_HIP. */
+int mpm_pbmpm_g2p_integrate(const mpm_grid_desc *grid, const float *dg, const mpm_particles *particles, float *F,
+                            float dt, const float *gravity, uint32_t *status, hipStream_t stream);
 
 /* gridUpdate in displacement form (the same section: mass-normalise, then the
  * guardian projects each node's displaced position back into bounds).  Per

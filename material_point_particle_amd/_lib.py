@@ -56,7 +56,8 @@ EXPORTS = ("mpm_version", "mpm_strerror", "mpm_check_bounds", "mpm_workspace_byt
            "mpm_bin_resident", "mpm_g2p2g", "mpm_grid_clear_tiles", "mpm_gather_records",
            "mpm_p2g_isplit_noalloc", "mpm_pbmpm_project_elastic", "mpm_pbmpm_grid_update", "mpm_pbmpm_integrate",
            "mpm_grid_update_tiles", "mpm_g2p_records", "mpm_update_deformation_stress",
-           "mpm_pbmpm_g2p_project", "mpm_pbmpm_g2p_project_records", "mpm_g2p_update_deformation_stress")
+           "mpm_pbmpm_g2p_project", "mpm_pbmpm_g2p_project_records", "mpm_g2p_update_deformation_stress",
+           "mpm_pbmpm_g2p_integrate")
 
 _lib = None
 
@@ -131,6 +132,9 @@ def lib() -> ct.CDLL:
         L.mpm_g2p_update_deformation_stress.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_float,
                                                         ct.c_void_p, ct.c_void_p, ct.c_float, ct.c_float, ct.c_void_p,
                                                         ct.c_void_p, ct.c_void_p]
+        L.mpm_pbmpm_g2p_integrate.restype = ct.c_int
+        L.mpm_pbmpm_g2p_integrate.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_void_p, ct.c_float,
+                                              P(ct.c_float), ct.c_void_p, ct.c_void_p]
         L.mpm_pbmpm_g2p_project_records.restype = ct.c_int
         L.mpm_pbmpm_g2p_project_records.argtypes = [P(mpm_grid_desc), ct.c_void_p, P(mpm_particles), ct.c_void_p,
                                                     ct.c_float, ct.c_int32, P(mpm_ranges), ct.c_void_p, ct.c_size_t,
@@ -352,6 +356,12 @@ def mpm_pbmpm_g2p_project_records(desc, dg, parts: mpm_particles, F, relax: floa
     _check(lib().mpm_pbmpm_g2p_project_records(ct.byref(desc), _ptr(dg), ct.byref(parts), _ptr(F), relax,
                                                polar_iters, ct.byref(rng), _ptr(ws), _nbytes(ws), _ptr(status),
                                                _stream(stream)), "mpm_pbmpm_g2p_project_records")
+
+
+def mpm_pbmpm_g2p_integrate(desc, dg, parts: mpm_particles, F, dt: float, gravity, status, stream=None) -> None:
+    g = (ct.c_float * 3)(*(list(gravity) + [0.0] * (3 - len(gravity))))
+    _check(lib().mpm_pbmpm_g2p_integrate(ct.byref(desc), _ptr(dg), ct.byref(parts), _ptr(F), dt, g, _ptr(status),
+                                         _stream(stream)), "mpm_pbmpm_g2p_integrate")
 
 
 def mpm_pbmpm_project_elastic(desc, parts: mpm_particles, F, relax: float, polar_iters: int, status,

@@ -676,6 +676,21 @@ int mpm_pbmpm_grid_update(const mpm_grid_desc *grid, void *bins, size_t bins_byt
     return hip_status(launch_pbmpm_grid_update(grid->dim, grid->n, grid_io, dg, band, &v, stream));
 }
 
+int mpm_pbmpm_g2p_integrate(const mpm_grid_desc *grid, const float *dg, const mpm_particles *particles, float *F,
+                            float dt, const float *gravity, uint32_t *status, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_desc(grid)) != MPM_OK || (rc = check_particles(grid, particles, true, false)) != MPM_OK)
+        return rc;
+    if (!aligned(dg, 4) || !aligned(status, 4) || !gravity || !(dt >= 0.0f))
+        return MPM_ERR_INVALID;
+    if (particles->n > 0 && (!particles->C || !aligned(particles->C, 4) || !aligned(F, 4)))
+        return MPM_ERR_INVALID;
+    const float g3[3] = { gravity[0], gravity[1], grid->dim == 3 ? gravity[2] : 0.0f };
+    return hip_status(launch_pbmpm_g2p_integrate(grid->dim, grid->n, dg, particles->x, particles->v, particles->C,
+                                                 particles->n, F, dt, g3, status, stream));
+}
+
 int mpm_pbmpm_integrate(const mpm_grid_desc *grid, const mpm_particles *particles, float dt, const float *gravity,
                         uint32_t *status, hipStream_t stream)
 {

@@ -250,6 +250,34 @@ __device__ __forceinline__ void record_tail(float *rec, const float (&C)[DIM * D
 
 static_assert(rec_floats<3>() == 16 && rec_floats<2>() == 12, "the record layouts written above");
 
+// The PB-MPM loop's last gather and the end of the substep in one launch: the
+// G2P gather with dt = 0 (g2p_one: d and D from the displacement grid, x
+// kept and clamped) over the thread's particles (one per thread), then a
+// second loop over the same particles with the integrate step
+// (pbmpm_integrate_particle) and F <- (I + D) F (update_F_kernel's arithmetic
+// with dt = 1), reading back the x, d and D just written.  Memory and the
+// status counts end as after the three kernels in sequence.
+template <int DIM>
+__global__ void __launch_bounds__(256) g2p_integrate_kernel(int n, float nf, float dx, float last_base,
+                                                            const float *__restrict__ dg, float *__restrict__ x,
+                                                            float *__restrict__ d, float *__restrict__ D, int64_t np,
+                                                            float lo, float hi, float cscale, float *__restrict__ F,
+                                                            float gx, float gy, float gz, uint32_t *__restrict__ status)
+{
+    const int64_t nodes = DIM == 3 ? (int64_t)n * n * n : (int64_t)n * n;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x)
+        g2p_one<DIM>(p, n, nodes, nf, dx, last_base, dg, x, d, D, np, 0.0f, lo, hi, cscale, status);
+    const float gdt2[3] = { gx, gy, gz };
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
+        wave_count(pbmpm_integrate_particle<DIM>(p, np, x, d, lo, hi, gdt2), &status[2]);
+        float f[DIM][DIM], c[DIM][DIM];
+        load_mat<DIM>(D, np, p, c);
+        load_mat<DIM>(F, np, p, f);
+        updated_F<DIM>(c, 1.0f, f);
+        store_mat<DIM>(F, np, p, f);
+    }
+}
+
 // The binned records a PB-MPM gather rewrites (REFRESH), from a checked
 // binning of the same particles with the same ranges.
 struct RecordRefresh {
@@ -644,6 +672,26 @@ hipError_t launch_pbmpm_g2p_project(int dim, int n, const float *dg, float *x, f
             hipLaunchKernelGGL((g2p_project_kernel<2, false>), grid, block, 0, s, n, nf, dx, last, dg, x, d, D, np, lo,
                                hi, cscale, F, (double)relax, polar_iters, status, rr);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_pbmpm_g2p_integrate(int dim, int n, const float *dg, float *x, float *d, float *D, int64_t np,
+                                      float *F, float dt, const float *gravity, uint32_t *status, hipStream_t s)
+{
+    if (np == 0)
+        return hipSuccess;
+    const float nf = (float)n, dx = 1.0f / (float)n, last = (float)(n - 3);
+    const float lo = dx, hi = (float)(n - 2) * dx;
+    const float cscale = 4.0f * (float)n * (float)n;
+    float gdt2[3] = { 0.0f, 0.0f, 0.0f };
+    for (int e = 0; e < dim; ++e)
+        gdt2[e] = gravity[e] * (dt * dt);
+    if (dim == 3)
+        hipLaunchKernelGGL(g2p_integrate_kernel<3>, dim3(blocks_one_each(np)), dim3(256), 0, s, n, nf, dx, last, dg, x,
+                           d, D, np, lo, hi, cscale, F, gdt2[0], gdt2[1], gdt2[2], status);
+    else
+        hipLaunchKernelGGL(g2p_integrate_kernel<2>, dim3(blocks_one_each(np)), dim3(256), 0, s, n, nf, dx, last, dg, x,
+                           d, D, np, lo, hi, cscale, F, gdt2[0], gdt2[1], gdt2[2], status);
     return hipGetLastError();
 }
 

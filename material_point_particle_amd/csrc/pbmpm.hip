@@ -38,30 +38,16 @@ __global__ void __launch_bounds__(256) pbmpm_project_kernel(int64_t np, const fl
     }
 }
 
-// particleIntegrate for an elastic material, without the deformation update:
-// x_e <- x_e + d_e (float32) clamped to [lo, hi] = [dx, (n - 2) dx], clamped
-// particles counted in status[2]; then d_e <- d_e + gdt2_e (gravity into the
-// next substep's displacement, gdt2_e = g_e * (dt * dt) formed once on the
-// host in float32).
+// particleIntegrate for an elastic material, without the deformation update
+// (pbmpm_integrate_particle); clamped particles counted in status[2].
 template <int DIM>
 __global__ void __launch_bounds__(256) pbmpm_integrate_kernel(int64_t np, float *__restrict__ x,
                                                               float *__restrict__ d, float lo, float hi, float gx,
                                                               float gy, float gz, uint32_t *__restrict__ status)
 {
     const float gdt2[3] = { gx, gy, gz };
-    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x) {
-        bool clamped = false;
-#pragma unroll
-        for (int e = 0; e < DIM; ++e) {
-            const float de = d[(int64_t)e * np + p];
-            const float xa = x[(int64_t)e * np + p] + de;
-            const float xc = fminf(fmaxf(xa, lo), hi);
-            clamped = clamped || xc != xa;
-            x[(int64_t)e * np + p] = xc;
-            d[(int64_t)e * np + p] = de + gdt2[e];
-        }
-        wave_count(clamped, &status[2]);
-    }
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < np; p += (int64_t)gridDim.x * blockDim.x)
+        wave_count(pbmpm_integrate_particle<DIM>(p, np, x, d, lo, hi, gdt2), &status[2]);
 }
 
 // One thread per particle (the per-particle passes here measured no slower,

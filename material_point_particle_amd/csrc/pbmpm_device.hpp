@@ -186,11 +186,39 @@ __device__ __forceinline__ bool pbmpm_project_particle(LoadF &&loadF, const floa
     return true;
 }
 
+// particleIntegrate for one particle, without the deformation update:
+// x_e <- x_e + d_e (float32) clamped to [lo, hi] = [dx, (n - 2) dx]; then
+// d_e <- d_e + gdt2_e (gravity into the next substep's displacement, gdt2_e =
+// g_e * (dt * dt) formed once on the host in float32).  Returns whether a
+// coordinate was clamped.
+template <int DIM>
+__device__ __forceinline__ bool pbmpm_integrate_particle(int64_t p, int64_t np, float *__restrict__ x,
+                                                         float *__restrict__ d, float lo, float hi,
+                                                         const float (&gdt2)[3])
+{
+    bool clamped = false;
+#pragma unroll
+    for (int e = 0; e < DIM; ++e) {
+        const float de = d[(int64_t)e * np + p];
+        const float xa = x[(int64_t)e * np + p] + de;
+        const float xc = fminf(fmaxf(xa, lo), hi);
+        clamped = clamped || xc != xa;
+        x[(int64_t)e * np + p] = xc;
+        d[(int64_t)e * np + p] = de + gdt2[e];
+    }
+    return clamped;
+}
+
 // The G2P gather with dt = 0 (d and D from the displacement grid dg, x kept)
 // followed by the projection above, one pass (grid.hip).
 // bins: a checked binning of these particles whose records the gather
 // rewrites from the new state (with the binning's ranges r and the masses m),
 // or NULL.
+// The loop's last G2P gather (dt = 0), then per particle the integrate step
+// and F <- (I + D) F, one launch (grid.hip).
+hipError_t launch_pbmpm_g2p_integrate(int dim, int n, const float *dg, float *x, float *d, float *D, int64_t np,
+                                      float *F, float dt, const float *gravity, uint32_t *status, hipStream_t s);
+
 hipError_t launch_pbmpm_g2p_project(int dim, int n, const float *dg, float *x, float *d, float *D, int64_t np,
                                     const float *F, float relax, int polar_iters, uint32_t *status, hipStream_t s,
                                     const BinView *bins = nullptr, RangesF r = RangesF{}, const float *m = nullptr);

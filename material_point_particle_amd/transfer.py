@@ -249,17 +249,25 @@ class PBMPMSubsteps:
         L.mpm_pbmpm_integrate(tr.desc, parts.desc(), self.dt, self.gravity, tr.status)
         L.mpm_update_deformation(tr.desc, parts.desc(), parts.F, 1.0)
 
+    def gather_integrate(self) -> None:
+        """The last iteration's G2P, then integrate(), in one launch."""
+        tr, parts = self.tr, self.parts
+        L.mpm_pbmpm_g2p_integrate(tr.desc, tr.vg, parts.desc(), parts.F, self.dt, self.gravity, tr.status)
+
     def substep(self) -> None:
         """fused: the first projection on its own, then every iteration's G2P
         but the last together with the next projection (with `records`, one
-        binning per substep); else the separate calls.  All give the same
-        bits."""
+        binning per substep, and the last G2P with the integrate step and the F
+        update); else the separate calls.  All give the same bits."""
         if self.fused:
             self.project()
             for it in range(self.iterations):
                 self.deposit(rebin=it == 0 or not self.records)
                 if it + 1 < self.iterations:
                     self.gather_project()
+                elif self.records:
+                    self.gather_integrate()
+                    return
                 else:
                     self.tr.g2p(self.parts, 0.0)
         else:

@@ -272,6 +272,15 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert gp(ct.byref(d), dg, ct.byref(p4), ct.c_void_p(8192), 2.5, 12, status, None) == L.MPM_ERR_INVALID
     assert gp(ct.byref(d), dg, ct.byref(p4), ct.c_void_p(8192), 1.5, 65, status, None) == L.MPM_ERR_INVALID
     assert gp(None, dg, ct.byref(p4), ct.c_void_p(8192), 1.5, 12, status, None) == L.MPM_ERR_INVALID
+    # the loop's last gather with the integrate step and the F update: dg, particles, F, dt, gravity, status
+    gi = lib.mpm_pbmpm_g2p_integrate
+    gv = (ct.c_float * 3)(0.0, -9.8, 0.0)
+    assert gi(ct.byref(d), dg, ct.byref(p3), ct.c_void_p(8192), 1e-3, gv, status, None) == L.MPM_ERR_INVALID  # no C
+    assert gi(ct.byref(d), dg, ct.byref(p4), None, 1e-3, gv, status, None) == L.MPM_ERR_INVALID             # no F
+    assert gi(ct.byref(d), None, ct.byref(p4), ct.c_void_p(8192), 1e-3, gv, status, None) == L.MPM_ERR_INVALID
+    assert gi(ct.byref(d), dg, ct.byref(p4), ct.c_void_p(8192), 1e-3, None, status, None) == L.MPM_ERR_INVALID
+    assert gi(ct.byref(d), dg, ct.byref(p4), ct.c_void_p(8192), -1e-3, gv, status, None) == L.MPM_ERR_INVALID
+    assert gi(None, dg, ct.byref(p4), ct.c_void_p(8192), 1e-3, gv, status, None) == L.MPM_ERR_INVALID
     # the same with the binned records rewritten: also ranges, masses and the binning's workspace
     gpr = lib.mpm_pbmpm_g2p_project_records
     F8 = ct.c_void_p(8192)
@@ -332,4 +341,6 @@ def test_empty_calls_of_the_one_pass_entry_points_return_before_any_launch():
     assert lib.mpm_update_deformation(ct.byref(d), ct.byref(p0), None, 1e-4, None) == L.MPM_OK
     assert lib.mpm_g2p_update_deformation_stress(ct.byref(d), fake, ct.byref(p0), 1e-4, None, None, 1e5, 1e5, None,
                                                  fake, None) == L.MPM_OK
+    assert lib.mpm_pbmpm_g2p_integrate(ct.byref(d), fake, ct.byref(p0), None, 1e-3,
+                                       (ct.c_float * 3)(0.0, -9.8, 0.0), fake, None) == L.MPM_OK
 

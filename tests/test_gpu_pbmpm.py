@@ -190,7 +190,9 @@ def test_jelly_substeps_in_lockstep(mpm, oracle_lib, form):
     iteration's P2G grid at every 5th substep.  fused: every iteration's G2P
     but the last runs with the next projection (mpm_pbmpm_g2p_project);
     records: likewise, rewriting the binned records
-    (mpm_pbmpm_g2p_project_records), so the substep bins only once."""
+    (mpm_pbmpm_g2p_project_records), so the substep bins only once, and the
+    last G2P with the integrate step and the F update
+    (mpm_pbmpm_g2p_integrate)."""
     w = WORKLOADS["pbmpm_jelly_3d_64"]
     ex = w.extra
     host = build(w)
@@ -217,12 +219,15 @@ def test_jelly_substeps_in_lockstep(mpm, oracle_lib, form):
             if form == "records" and it < last:
                 L.mpm_pbmpm_g2p_project_records(tr.desc, tr.vg, parts.desc(), parts.F, ex["relax"],
                                                 ex["polar_iters"], tr.ranges, tr.ws, tr.status)
+            elif form == "records":
+                L.mpm_pbmpm_g2p_integrate(tr.desc, tr.vg, parts.desc(), parts.F, ex["dt"], ex["gravity"], tr.status)
             elif form == "fused" and it < last:
                 L.mpm_pbmpm_g2p_project(tr.desc, tr.vg, parts.desc(), parts.F, ex["relax"], ex["polar_iters"],
                                         tr.status)
             else:
                 tr.g2p(parts, 0.0)
-        loop.integrate()
+        if form != "records":
+            loop.integrate()
         grid, st = oracle_lib.pbmpm_substep(3, w.n, w.frac_bits, state, rng, ex["iterations"], ex["relax"],
                                             ex["polar_iters"], ex["band"], ex["dt"], ex["gravity"])
         total += st
@@ -376,6 +381,47 @@ def test_g2p_project_records_rewrites_the_binning(mpm, dim):
     assert u32(tr.status).tolist() == [0, 0, 0, 1]
     for a, b in zip(before, (parts.x, parts.v, parts.C, tr.ws)):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dim", [2, 3])
+def test_g2p_integrate_equals_the_three_calls(mpm, dim):
+    """mpm_pbmpm_g2p_integrate against mpm_g2p (dt = 0), mpm_pbmpm_integrate
+    and mpm_update_deformation (dt = 1) on a displacement grid of random
+    values: x, d, D, F and the status counts bit-identical.  Some particles
+    sit outside the grid (the gather leaves them; the integrate step and the F
+    update still run on them), some below and above the clamp bounds."""
+    from material_point_particle_amd import _lib as L
+    n, k = (64 if dim == 2 else 32), 50_003
+    rng = np.random.default_rng(80 + dim)
+    x = rng.uniform(1.0 / n, (n - 2.0) / n, (dim, k)).astype(np.float32)
+    x[0, :40] = 0.2 / n
+    x[0, 40:80] = 0.9 / n
+    x[dim - 1, 80:120] = (n - 1.7) / n
+    d = (0.01 * rng.standard_normal((dim, k))).astype(np.float32)
+    D = (0.05 * rng.standard_normal((dim * dim, k))).astype(np.float32)
+    F = (np.eye(dim).reshape(dim * dim, 1) + 0.1 * rng.standard_normal((dim * dim, k))).astype(np.float32)
+    dg = (0.02 * rng.standard_normal((dim,) + (n,) * dim)).astype(np.float32)
+    grav = (0.0, -9.8, 0.0)[:dim]
+    desc = L.grid_desc(dim, n, 32)
+    out = []
+    for one in (False, True):
+        xd, dd, Dd, Fd = (torch.from_numpy(a.copy()).cuda() for a in (x, d, D, F))
+        dgd = torch.from_numpy(dg).cuda()
+        st = torch.zeros(4, dtype=torch.int32, device="cuda")
+        parts = L.particles(k, xd, dd, Dd, None)
+        if one:
+            L.mpm_pbmpm_g2p_integrate(desc, dgd, parts, Fd, 2e-3, grav, st)
+        else:
+            L.mpm_g2p(desc, dgd, parts, 0.0, st)
+            L.mpm_pbmpm_integrate(desc, parts, 2e-3, grav, st)
+            L.mpm_update_deformation(desc, parts, Fd, 1.0)
+        torch.cuda.synchronize()
+        out.append([a.cpu().numpy() for a in (xd, dd, Dd, Fd)] + [u32(st).tolist()])
+    say("g2p + integrate + F update, one launch", dim, out[1][4])
+    for a, b, what in zip(out[0][:4], out[1][:4], ("x", "d", "D", "F")):
+        assert_same(b, a, what)
+    assert out[0][4] == out[1][4]
+    assert out[1][4][0] >= 40 and out[1][4][2] > 0
 
 
 def test_square_2d_substeps_in_lockstep(mpm, oracle_lib):
