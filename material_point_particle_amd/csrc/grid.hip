@@ -1,4 +1,5 @@
-// grid.hip -- grid update (consume-and-zero) and APIC grid-to-particle gather.
+// grid.hip -- grid update (consume-and-zero) and APIC grid-to-particle gather,
+// with the gathers that run the next per-particle step in the same launch.
 //
 // "Implementation -- GPU Optimization & Reference Codebases": section 1 (the
 // four-phase step; G2P is a contention-free gather), section 2.1 and rule 4 of
@@ -6,6 +7,16 @@
 // it in place and no separate clear pass exists), rule 1 (the fixed-point sums
 // are converted once, in the grid update) and rule 7 (gravity is applied by the
 // solver to the grid velocity).
+//
+// Kernels: the grid updates (velocity form, PB-MPM displacement form, clears,
+// restricted to reachable or flagged node tiles); G2P over the caller's
+// arrays (g2p_kernel); G2P followed, for the same particles, by the elastic
+// substep's F update and stress (g2p_stress_kernel), by the PB-MPM projection
+// of the next iteration with or without rewriting the binned records
+// (g2p_project_kernel), or by the PB-MPM integrate step and F update
+// (g2p_integrate_kernel); and G2P over the binned records in place
+// (g2p_records_kernel).  Each combined kernel computes exactly what its parts
+// compute, through the same device functions.
 #include "pbmpm_device.hpp"
 #include "resident.hpp"
 #include "stress.hpp"
